@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet layer on one MI355X.
+
+One step = one pass of the whole hot path on resident HBM inputs:
+  * a chunked prefill of one 4096-token sequence (HK=16 query/key heads, HV=32
+    value heads, d=128, bf16 q/k/v/out, fp32 gates and state, chunk 64, zero
+    initial state, final state written), and
+  * one decode step for a batch of 64 sequences against resident fp32 states
+    (bf16 q/k/v/gates/out).
+value = (4096 + 64) tokens per step / step time (tokens/s per layer); the
+prefill and decode parts are also reported on their own.
+
+Inputs are synthetic (gdn_synth). Several copies of every buffer set are
+rotated through so that each step reads its state and inputs from HBM rather
+than from the 256 MB Infinity Cache left warm by the previous step.
+
+Timing: HIP events on the stream the library launches on (torch's current
+stream), around exactly --steps steps after --warmup untimed steps, with
+torch.cuda.synchronize() on both sides. A second pass of the same steps
+brackets every kernel launch with the library's own event pairs
+(gdn_timing_start/stop) to get each kernel's mean duration for the roofline.
+
+Output: one JSON line (see the "roofline" and "cpu_baseline" objects).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HK, HV, D, CHUNK = 16, 32, 128, 64
+T_PREFILL, B_DECODE = 4096, 64
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "GDN layer tokens/s (prefill T=4K; decode B=64) + % MFMA / % HBM peak"
+
+
+def scan_flops_per_token(hv=HV, dk=D, dv=D, c=CHUNK):
+    """Algorithmic MFMA flops of the chunk-recurrent scan kernel per token:
+    per value head K S^T, Q S^T, K^T (delta U) (each 2*dk*dv per token) and
+    T Y, P U (each 2*C*dv per token)."""
+    return hv * (6 * dk * dv + 4 * c * dv)
+
+
+def prep_flops_per_token(hk=HK, dk=D, c=CHUNK):
+    """Algorithmic MFMA flops of the chunk-preparation kernel per token:
+    K K^T and Q K^T per query/key head (2*C*dk each)."""
+    return hk * 4 * c * dk
+
+
+def decode_bytes_per_step(b=B_DECODE, hk=HK, hv=HV, dk=D, dv=D):
+    """Algorithmic HBM bytes of one decode step: the fp32 state read and
+    written once, bf16 q, k (per q/k head), v, gates and output."""
+    return b * hv * dv * dk * 4 * 2 + b * (2 * hk * dk + hv * dv) * 2 + b * hv * 2 * 2 + b * hv * dv * 2
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_deltanet_linear_02_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from committed counter runs, if they were taken on
+    the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def to_device(x: np.ndarray, dtype: str, dev):
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(dev)
+
+
+def device_inputs(inp, dev):
+    import torch
+    return dict(q=to_device(inp.q, inp.io_dtype, dev), k=to_device(inp.k, inp.io_dtype, dev),
+                v=to_device(inp.v, inp.io_dtype, dev), g=to_device(inp.g, inp.gate_dtype, dev),
+                beta=to_device(inp.beta, inp.gate_dtype, dev),
+                cu_seqlens=torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev))
+
+
+def cpu_baseline(threads: int):
+    """The fp64 oracle on the host cores: the full 4096-token prefill (all 32
+    value heads) plus one decode step at batch 64."""
+    import gdn_synth as gs
+    import oracle
+    inp = gs.workload("prefill")
+    w = inp.widened()
+    t0 = time.perf_counter()
+    oracle.scan(w["q"], w["k"], w["v"], w["g"], w["beta"], w["cu_seqlens"], threads=threads)
+    t_pre = time.perf_counter() - t0
+    dec = gs.workload("decode", batch=B_DECODE)
+    wd = dec.widened()
+    s0 = gs.decode_state(B_DECODE, HV, D, D, seed=gs.SEED_BASE + 101).astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.decode_step(wd["q"], wd["k"], wd["v"], wd["g"], wd["beta"], s0, threads=threads)
+    t_dec = time.perf_counter() - t0
+    return {
+        "value": (T_PREFILL + B_DECODE) / (t_pre + t_dec), "unit": "tokens/s", "cores": threads,
+        "kind": "oracle",
+        "sample": f"one full step: prefill T={T_PREFILL} (all {HV} value heads) + decode B={B_DECODE}, "
+                  f"fp64 token scan in C; prefill {t_pre:.2f} s, decode {t_dec * 1e3:.1f} ms",
+        "prefill_tokens_per_s": T_PREFILL / t_pre,
+        "decode_tokens_per_s": B_DECODE / t_dec,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=4, help="buffer sets rotated through (cold caches)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this layer's path is built and measured on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gdn_synth as gs
+    import gated_deltanet_linear_02_amd as gdn
+
+    if torch.cuda.device_count() < 1:
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] generating inputs", file=sys.stderr, flush=True)
+
+    pre = gs.workload("prefill")
+    dec = gs.workload("decode", batch=B_DECODE)
+    s_dec = gs.decode_state(B_DECODE, HV, D, D, seed=gs.SEED_BASE + 101)
+
+    P = device_inputs(pre, dev)
+    Dd = device_inputs(dec, dev)
+    ws_bytes = gdn.prefill_workspace_size(1, T_PREFILL, HK, HV, D, D, CHUNK, torch.bfloat16)
+    sets = []
+    for i in range(args.copies):
+        sets.append(dict(
+            q=P["q"].clone(), k=P["k"].clone(), v=P["v"].clone(), g=P["g"].clone(),
+            beta=P["beta"].clone(), cu=P["cu_seqlens"].clone(),
+            out=torch.empty((T_PREFILL, HV, D), dtype=torch.bfloat16, device=dev),
+            fin=torch.empty((1, HV, D, D), dtype=torch.float32, device=dev),
+            ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev),
+            dq=Dd["q"].clone(), dk=Dd["k"].clone(), dv=Dd["v"].clone(), dg=Dd["g"].clone(),
+            db=Dd["beta"].clone(), state=torch.from_numpy(s_dec).to(dev),
+            dout=torch.empty((B_DECODE, HV, D), dtype=torch.bfloat16, device=dev),
+        ))
+
+    def step(s):
+        gdn.prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu"], chunk=CHUNK,
+                    final_state=s["fin"], out=s["out"], workspace=s["ws"])
+        gdn.decode_step(s["dq"], s["dk"], s["dv"], s["dg"], s["db"], s["state"], out=s["dout"])
+
+    # Sanity check only (parity against the oracle is the tests' job): one
+    # step must write finite outputs and states.
+    step(sets[0])
+    torch.cuda.synchronize()
+    s0 = sets[0]
+    if not all(bool(torch.isfinite(s0[x]).all()) for x in ("out", "fin", "dout", "state")):
+        print(json.dumps({"metric": METRIC, "error": "non-finite output"}))
+        sys.exit(1)
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        step(sets[i % args.copies])
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly --steps steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(sets[i % args.copies])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # ---- per-kernel pass (same steps, each launch bracketed by events)
+    gdn.timing_start(8 * args.steps)
+    for i in range(args.steps):
+        step(sets[i % args.copies])
+    kt = gdn.timing_stop()
+    torch.cuda.synchronize()
+
+    # prefill-only and decode-only rates
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(n):
+            fn(sets[i % args.copies])
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    ms_pre = timed(lambda s: gdn.prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu"], chunk=CHUNK,
+                                         final_state=s["fin"], out=s["out"], workspace=s["ws"]), args.steps)
+    ms_dec = timed(lambda s: gdn.decode_step(s["dq"], s["dk"], s["dv"], s["dg"], s["db"], s["state"],
+                                             out=s["dout"]), args.steps)
+
+    scan_ms = kt["scan"]["mean_ms"]
+    prep_ms = kt["prep"]["mean_ms"]
+    dec_ms = kt["decode"]["mean_ms"]
+    scan_flops = scan_flops_per_token() * T_PREFILL
+    prep_flops = prep_flops_per_token() * T_PREFILL
+    scan_tflops = scan_flops / (scan_ms * 1e-3) / 1e12
+    dec_bytes = decode_bytes_per_step()
+    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+
+    roof = {"bound": "mfma", "kernel": "gdn_scan_kernel", "achieved": scan_tflops,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": scan_tflops / PEAK_BF16_TFLOPS,
+            "traffic": measured_traffic("gdn_scan_kernel"),
+            "algorithmic_per_launch": scan_flops, "mean_launch_ms": scan_ms}
+    roof_dec = {"bound": "hbm", "kernel": "gdn_decode_kernel", "achieved": dec_gbs, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": dec_gbs / PEAK_HBM_GBS,
+                "traffic": measured_traffic("gdn_decode_kernel"),
+                "algorithmic_per_launch": dec_bytes, "mean_launch_ms": dec_ms}
+    prefill_all_flops = scan_flops + prep_flops
+    res = {
+        "metric": METRIC,
+        "value": (T_PREFILL + B_DECODE) / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"GDN layer step: prefill 1x{T_PREFILL} tokens + decode batch {B_DECODE}; "
+                               f"HK={HK}, HV={HV}, d={D}, chunk {CHUNK}; bf16 q/k/v/out, fp32 gates/state",
+                   "prefill_tokens": T_PREFILL, "decode_batch": B_DECODE, "parallelism": "single GPU",
+                   "buffer_copies": args.copies},
+        "roofline": roof,
+        "roofline_decode": roof_dec,
+        "prefill": {"tokens_per_s": T_PREFILL / (ms_pre * 1e-3), "ms": ms_pre,
+                    "mfma_frac_all_kernels": prefill_all_flops / (ms_pre * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                    "kernel_ms": {"schedule": kt["schedule"]["mean_ms"], "prep": prep_ms, "scan": scan_ms}},
+        "decode": {"tokens_per_s": B_DECODE / (ms_dec * 1e-3), "ms": ms_dec, "kernel_ms": dec_ms,
+                   "hbm_frac": dec_gbs / PEAK_HBM_GBS},
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        try:
+            ncpu = len(os.sched_getaffinity(0))
+        except AttributeError:
+            ncpu = os.cpu_count() or 1
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(max(1, min(16, ncpu)))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

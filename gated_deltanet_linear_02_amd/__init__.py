@@ -1,0 +1,197 @@
+"""Gated DeltaNet layer on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libgdn.so`` (the C ABI in ``include/gdn.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only marshals torch tensors (device memory) and the current HIP stream into
+the C calls, and turns status codes into exceptions. If the library has not
+been built, importing works but every call raises.
+
+Entry points (same names as the C ABI, without the ``gdn_`` prefix):
+    prefill(q, k, v, g, beta, cu_seqlens, ...)  -> (out, final_state)
+    decode_step(q, k, v, g, beta, state, ...)   -> out
+    prefill_workspace_size(...)
+    timing_start(max_launches) / timing_stop()  -> per-kernel launch times
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Dict, Optional, Tuple
+
+import torch
+
+__all__ = [
+    "GdnError", "lib_path", "load", "prefill", "decode_step", "prefill_workspace_size",
+    "timing_start", "timing_stop", "abi_version", "KERNEL_KINDS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libgdn.so")
+_lib = None
+_lock = threading.Lock()
+
+GDN_BF16, GDN_F32 = 0, 1
+KERNEL_KINDS = ("schedule", "prep", "scan", "decode")
+
+STATUS = {
+    0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
+    4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP", 6: "GDN_ERR_ALIAS",
+}
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libgdn.so (built by ``python -m gated_deltanet_linear_02_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with "
+                "`python -m gated_deltanet_linear_02_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        L.gdn_abi_version.restype = i32
+        L.gdn_abi_version.argtypes = []
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_status_string.argtypes = [i32]
+        L.gdn_prefill_workspace_size.restype = sz
+        L.gdn_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32]
+        L.gdn_prefill.restype = i32
+        L.gdn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
+                                  f32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.gdn_decode_step.restype = i32
+        L.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32,
+                                      vp, vp, i32, vp, vp]
+        L.gdn_timing_start.restype = i32
+        L.gdn_timing_start.argtypes = [i32]
+        L.gdn_timing_stop.restype = i32
+        L.gdn_timing_stop.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(f32), i32]
+        _lib = L
+        return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load().gdn_status_string(status).decode()
+        raise GdnError(status, msg)
+
+
+def abi_version() -> int:
+    return int(load().gdn_abi_version())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return GDN_BF16
+    if t == torch.float32:
+        return GDN_F32
+    raise TypeError(f"unsupported dtype {t} (bfloat16 or float32)")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libgdn must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(device: torch.device, stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream or None
+
+
+def prefill_workspace_size(num_seqs: int, total_tokens: int, hk: int, hv: int, dk: int, dv: int,
+                           chunk: int, io_dtype: torch.dtype) -> int:
+    return int(load().gdn_prefill_workspace_size(num_seqs, total_tokens, hk, hv, dk, dv, chunk,
+                                                 _dtype_code(io_dtype)))
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+            cu_seqlens: torch.Tensor, *, chunk: int = 64, scale: float = 1.0,
+            initial_state: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            write_final_state: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked prefill over packed sequences (``gdn_prefill``).
+
+    q, k [T, hk, dk]; v [T, hv, dv] (bf16 or fp32, one dtype); g, beta [T, hv]
+    (bf16 or fp32); cu_seqlens int32 [N + 1] on the device; states fp32
+    [N, hv, dv, dk]. ``final_state`` may be ``initial_state`` (in place).
+    Missing out / final_state / workspace are allocated with torch.
+    """
+    T, hk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    N = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    io = _dtype_code(q.dtype)
+    gate = _dtype_code(g.dtype)
+    dev = q.device
+    if out is None:
+        out = torch.empty((T, hv, dv), dtype=q.dtype, device=dev)
+    if final_state is None and write_final_state:
+        final_state = torch.empty((N, hv, dv, dk), dtype=torch.float32, device=dev)
+    need = prefill_workspace_size(N, T, hk, hv, dk, dv, chunk, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    status = load().gdn_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
+        hk, hv, dk, dv, chunk, float(scale), io, gate,
+        _ptr(initial_state), _ptr(final_state), _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    _check(status)
+    return out, final_state
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                state: torch.Tensor, *, scale: float = 1.0, state_slots: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One token per sequence against resident fp32 states, updated in place
+    (``gdn_decode_step``). q, k [B, hk, dk]; v [B, hv, dv]; g, beta [B, hv];
+    state [slots, hv, dv, dk]; state_slots int32 [B] on the device or None."""
+    B, hk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    if state.dtype != torch.float32:
+        raise TypeError("state must be float32")
+    if state_slots is not None and state_slots.dtype != torch.int32:
+        raise TypeError("state_slots must be int32")
+    if out is None:
+        out = torch.empty((B, hv, dv), dtype=q.dtype, device=q.device)
+    status = load().gdn_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), B, hk, hv, dk, dv, float(scale),
+        _dtype_code(q.dtype), _dtype_code(g.dtype), _ptr(state), _ptr(state_slots),
+        state.shape[0], _ptr(out), _stream(q.device, stream))
+    _check(status)
+    return out
+
+
+def timing_start(max_launches: int) -> None:
+    """Bracket the library's next ``max_launches`` kernel launches with HIP events."""
+    _check(load().gdn_timing_start(max_launches))
+
+
+def timing_stop() -> Dict[str, Dict[str, float]]:
+    """Wait for the timed launches; per kernel kind: launch count, total and mean ms."""
+    n = len(KERNEL_KINDS)
+    counts = (ctypes.c_int32 * n)()
+    ms = (ctypes.c_float * n)()
+    _check(load().gdn_timing_stop(counts, ms, n))
+    res = {}
+    for i, name in enumerate(KERNEL_KINDS):
+        c = int(counts[i])
+        res[name] = {"count": c, "total_ms": float(ms[i]), "mean_ms": float(ms[i]) / c if c else 0.0}
+    return res

@@ -1,0 +1,258 @@
+// gdn_api.hip -- the C ABI of libgdn.so (declared in include/gdn.h).
+//
+// Host side only: argument checks (all before any HIP call), workspace
+// carving, dispatch to the kernel launchers, and optional per-kernel event
+// timing. Nothing here allocates device memory.
+#include "gdn.h"
+#include "gdn_launch.hpp"
+
+#include <mutex>
+#include <new>
+#include <vector>
+
+namespace gdn {
+
+// ----------------------------------------------------------------- timing
+
+namespace {
+struct TimingState {
+    std::mutex mu;
+    bool active = false;
+    int max_launches = 0;
+    int used = 0;
+    bool open = false;
+    std::vector<hipEvent_t> events;  // 2 per launch
+    std::vector<int> kinds;
+};
+TimingState &timing() {
+    static TimingState t;
+    return t;
+}
+}  // namespace
+
+void timing_begin(KernelKind kind, hipStream_t st) {
+    TimingState &T = timing();
+    std::lock_guard<std::mutex> lk(T.mu);
+    if (!T.active || T.used >= T.max_launches) return;
+    if (hipEventRecord(T.events[2 * T.used], st) != hipSuccess) return;
+    T.kinds[T.used] = kind;
+    T.open = true;
+}
+
+void timing_end(KernelKind kind, hipStream_t st) {
+    TimingState &T = timing();
+    std::lock_guard<std::mutex> lk(T.mu);
+    if (!T.active || !T.open || T.kinds[T.used] != kind) return;
+    T.open = false;
+    if (hipEventRecord(T.events[2 * T.used + 1], st) != hipSuccess) return;
+    ++T.used;
+}
+
+// ----------------------------------------------------------------- checks
+
+static bool valid_head(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+static bool valid_chunk(int32_t c) { return c == 16 || c == 32 || c == 64; }
+static bool valid_dtype(int32_t t) { return t == GDN_BF16 || t == GDN_F32; }
+static size_t dtype_bytes(int32_t t) { return t == GDN_BF16 ? 2 : 4; }
+
+struct Range {
+    uintptr_t lo, hi;
+};
+static Range span(const void *p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + bytes};
+}
+static bool overlaps(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi || a.lo == 0 || b.lo == 0) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" {
+
+int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char *gdn_status_string(int32_t status) {
+    switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL_ARG: return "a required pointer argument is NULL";
+    case GDN_ERR_BAD_SHAPE: return "invalid sizes (negative, zero where not allowed, or hv not a multiple of hk)";
+    case GDN_ERR_UNSUPPORTED: return "head size, chunk size or dtype not supported by this build";
+    case GDN_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than gdn_prefill_workspace_size()";
+    case GDN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case GDN_ERR_ALIAS: return "output buffer overlaps an input buffer";
+    default: return "unknown status";
+    }
+}
+
+static int32_t check_prefill_shape(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
+                                   int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype,
+                                   int32_t gate_dtype) {
+    if (num_seqs < 1 || total_tokens < 0 || total_tokens > INT32_MAX || hk < 1 || hv < 1 || hv % hk != 0)
+        return GDN_ERR_BAD_SHAPE;
+    if (!valid_head(dk) || dv != dk || !valid_chunk(chunk) || !valid_dtype(io_dtype) ||
+        !valid_dtype(gate_dtype) || hk > 65535)
+        return GDN_ERR_UNSUPPORTED;
+    const PrefillLayout L = prefill_layout(num_seqs, total_tokens, hv, chunk, dtype_bytes(io_dtype));
+    const int64_t scan_grid = (((int64_t)num_seqs * hk + 7) / 8) * (hv / hk) * (dv / 16) * 8;
+    if (L.max_chunks > INT32_MAX || scan_grid > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
+                                  int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype) {
+    if (check_prefill_shape(num_seqs, total_tokens, hk, hv, dk, dv, chunk, io_dtype, GDN_F32) != GDN_OK)
+        return 0;
+    return prefill_layout(num_seqs, total_tokens, hv, chunk, dtype_bytes(io_dtype)).total;
+}
+
+int32_t gdn_prefill(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                    const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                    int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
+                    float scale, int32_t io_dtype, int32_t gate_dtype,
+                    const float *initial_state, float *final_state, void *out,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    const int32_t sc = check_prefill_shape(num_seqs, total_tokens, hk, hv, dk, dv, chunk, io_dtype, gate_dtype);
+    if (sc != GDN_OK) return sc;
+    if (!cu_seqlens) return GDN_ERR_NULL_ARG;
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL_ARG;
+
+    const size_t eb = dtype_bytes(io_dtype), gb = dtype_bytes(gate_dtype);
+    const PrefillLayout L = prefill_layout(num_seqs, total_tokens, hv, chunk, eb);
+    if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
+        return GDN_ERR_WORKSPACE;
+
+    const size_t T = (size_t)total_tokens;
+    const size_t state_bytes = (size_t)num_seqs * hv * dv * dk * sizeof(float);
+    const Range r_out = span(out, T * hv * dv * eb);
+    const Range inputs[] = {span(q, T * hk * dk * eb), span(k, T * hk * dk * eb), span(v, T * hv * dv * eb),
+                            span(g, T * hv * gb), span(beta, T * hv * gb),
+                            span(cu_seqlens, sizeof(int32_t) * (num_seqs + 1)),
+                            span(initial_state, state_bytes), span(final_state, state_bytes),
+                            span(workspace, L.total)};
+    for (const Range &r : inputs)
+        if (overlaps(r_out, r)) return GDN_ERR_ALIAS;
+    // The final state may be the initial state, but must not overlap any
+    // other buffer.
+    const Range r_fin = span(final_state, state_bytes);
+    for (int i = 0; i < 6; ++i)
+        if (overlaps(r_fin, inputs[i])) return GDN_ERR_ALIAS;
+    if (overlaps(r_fin, span(workspace, L.total))) return GDN_ERR_ALIAS;
+    if (final_state && initial_state && final_state != initial_state &&
+        overlaps(r_fin, span(initial_state, state_bytes)))
+        return GDN_ERR_ALIAS;
+
+    PrefillArgs A;
+    A.q = q; A.k = k; A.v = v; A.g = g; A.beta = beta;
+    A.cu = cu_seqlens; A.num_seqs = num_seqs; A.total_tokens = total_tokens;
+    A.hk = hk; A.hv = hv; A.d = dk; A.chunk = chunk; A.scale = scale;
+    A.io_bf16 = io_dtype == GDN_BF16; A.gate_bf16 = gate_dtype == GDN_BF16;
+    A.s0 = initial_state; A.s_final = final_state; A.out = out;
+    A.ws = static_cast<char *>(workspace); A.lay = L;
+    try {
+        return launch_prefill(A, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
+}
+
+int32_t gdn_decode_step(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                        int32_t batch, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float scale,
+                        int32_t io_dtype, int32_t gate_dtype, float *state, const int32_t *state_slots,
+                        int32_t num_slots, void *out, void *stream) {
+    if (batch < 0 || hk < 1 || hv < 1 || hv % hk != 0 || num_slots < 0) return GDN_ERR_BAD_SHAPE;
+    if (!valid_head(dk) || dv != dk || !valid_dtype(io_dtype) || !valid_dtype(gate_dtype))
+        return GDN_ERR_UNSUPPORTED;
+    if (batch == 0) return GDN_OK;
+    if ((int64_t)batch * hv > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    if (!state_slots && num_slots < batch) return GDN_ERR_BAD_SHAPE;
+    if (!q || !k || !v || !g || !beta || !state || !out) return GDN_ERR_NULL_ARG;
+
+    const size_t eb = dtype_bytes(io_dtype), gb = dtype_bytes(gate_dtype), B = (size_t)batch;
+    const Range r_out = span(out, B * hv * dv * eb);
+    const Range r_state = span(state, (size_t)num_slots * hv * dv * dk * sizeof(float));
+    const Range inputs[] = {span(q, B * hk * dk * eb), span(k, B * hk * dk * eb), span(v, B * hv * dv * eb),
+                            span(g, B * hv * gb), span(beta, B * hv * gb),
+                            span(state_slots, B * sizeof(int32_t)), r_state};
+    for (const Range &r : inputs)
+        if (overlaps(r_out, r)) return GDN_ERR_ALIAS;
+    for (int i = 0; i < 6; ++i)
+        if (overlaps(r_state, inputs[i])) return GDN_ERR_ALIAS;
+
+    DecodeArgs A;
+    A.q = q; A.k = k; A.v = v; A.g = g; A.beta = beta;
+    A.state = state; A.slots = state_slots; A.num_slots = num_slots; A.out = out;
+    A.batch = batch; A.hk = hk; A.hv = hv; A.d = dk; A.scale = scale;
+    A.io_bf16 = io_dtype == GDN_BF16; A.gate_bf16 = gate_dtype == GDN_BF16;
+    try {
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        timing_begin(kDecode, st);
+        const hipError_t e = launch_decode(A, st);
+        timing_end(kDecode, st);
+        return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
+}
+
+int32_t gdn_timing_start(int32_t max_launches) {
+    if (max_launches < 1) return GDN_ERR_BAD_SHAPE;
+    TimingState &T = timing();
+    std::lock_guard<std::mutex> lk(T.mu);
+    try {
+        for (hipEvent_t e : T.events) (void)hipEventDestroy(e);
+        T.events.assign(2 * (size_t)max_launches, nullptr);
+        T.kinds.assign((size_t)max_launches, -1);
+        for (hipEvent_t &e : T.events) {
+            if (hipEventCreate(&e) != hipSuccess) {
+                e = nullptr;
+                T.active = false;
+                return GDN_ERR_HIP;
+            }
+        }
+    } catch (...) {
+        T.active = false;
+        return GDN_ERR_HIP;
+    }
+    T.max_launches = max_launches;
+    T.used = 0;
+    T.open = false;
+    T.active = true;
+    return GDN_OK;
+}
+
+int32_t gdn_timing_stop(int32_t *counts, float *total_ms, int32_t n_kinds) {
+    TimingState &T = timing();
+    std::lock_guard<std::mutex> lk(T.mu);
+    if (!T.active) return GDN_ERR_BAD_SHAPE;
+    T.active = false;
+    int32_t status = GDN_OK;
+    for (int32_t i = 0; i < n_kinds; ++i) {
+        if (counts) counts[i] = 0;
+        if (total_ms) total_ms[i] = 0.f;
+    }
+    for (int i = 0; i < T.used; ++i) {
+        float ms = 0.f;
+        if (hipEventSynchronize(T.events[2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&ms, T.events[2 * i], T.events[2 * i + 1]) != hipSuccess) {
+            status = GDN_ERR_HIP;
+            continue;
+        }
+        const int kd = T.kinds[i];
+        if (kd >= 0 && kd < n_kinds) {
+            if (counts) counts[kd] += 1;
+            if (total_ms) total_ms[kd] += ms;
+        }
+    }
+    for (hipEvent_t e : T.events)
+        if (e) (void)hipEventDestroy(e);
+    T.events.clear();
+    T.kinds.clear();
+    T.used = 0;
+    return status;
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// gdn_launch.hpp -- internal host-side interface between the C ABI
+// (gdn_api.hip) and the kernel launchers. Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+enum KernelKind { kSchedule = 0, kPrep = 1, kScan = 2, kDecode = 3, kKinds = 4 };
+
+// Event bracketing of launches (see gdn_timing_start in gdn.h).
+void timing_begin(KernelKind kind, hipStream_t st);
+void timing_end(KernelKind kind, hipStream_t st);
+
+struct DecodeArgs {
+    const void *q, *k, *v, *g, *beta;
+    float *state;
+    const int32_t *slots;
+    int32_t num_slots;
+    void *out;
+    int32_t batch, hk, hv, d;
+    float scale;
+    bool io_bf16, gate_bf16;
+};
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
+
+// Workspace of one prefill call, carved from the caller's buffer. Sizes are
+// upper bounds known on the host: a sequence of length L has ceil(L/C)
+// chunks, so N sequences over T tokens have at most ceil(T/C) + N chunks.
+struct PrefillLayout {
+    int64_t max_chunks;
+    size_t off_bounds, off_seq_chunk0, off_order;   // int32 [N+1], [N+1], [N]
+    size_t off_chunk_seq, off_chunk_tok0, off_counters;            // int32 [max_chunks], [4]
+    size_t off_tmat, off_pmat;   // E [max_chunks][hv][C][C]
+    size_t off_gates;            // float4 [max_chunks][hv][C]
+    size_t off_gammac;           // float [max_chunks][hv]
+    size_t total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t hv,
+                                    int64_t chunk, size_t elem_bytes) {
+    PrefillLayout L;
+    L.max_chunks = (total_tokens + chunk - 1) / chunk + num_seqs;
+    size_t o = 0;
+    auto take = [&o](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+    L.off_bounds = take(sizeof(int32_t) * (size_t)(num_seqs + 1));
+    L.off_seq_chunk0 = take(sizeof(int32_t) * (size_t)(num_seqs + 1));
+    L.off_order = take(sizeof(int32_t) * (size_t)num_seqs);
+    L.off_chunk_seq = take(sizeof(int32_t) * (size_t)L.max_chunks);
+    L.off_chunk_tok0 = take(sizeof(int32_t) * (size_t)L.max_chunks);
+    L.off_counters = take(sizeof(int32_t) * 4);
+    const size_t per_mat = (size_t)L.max_chunks * (size_t)hv * (size_t)(chunk * chunk) * elem_bytes;
+    L.off_tmat = take(per_mat);
+    L.off_pmat = take(per_mat);
+    L.off_gates = take((size_t)L.max_chunks * (size_t)hv * (size_t)chunk * 16);
+    L.off_gammac = take((size_t)L.max_chunks * (size_t)hv * sizeof(float));
+    L.total = o;
+    return L;
+}
+
+struct PrefillArgs {
+    const void *q, *k, *v, *g, *beta;
+    const int32_t *cu;
+    int32_t num_seqs;
+    int64_t total_tokens;
+    int32_t hk, hv, d, chunk;
+    float scale;
+    bool io_bf16, gate_bf16;
+    const float *s0;
+    float *s_final;
+    void *out;
+    char *ws;
+    PrefillLayout lay;
+};
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st);
+
+}  // namespace gdn

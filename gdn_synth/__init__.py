@@ -43,13 +43,14 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     whose rounding overflows become +-inf, as IEEE rounding requires.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    rounded = ((u + 0x7FFF + lsb) >> 16).astype(np.uint32)
-    is_nan = np.isnan(x)
+    u = x.view(np.uint32)
+    # Only NaN bit patterns can wrap around in 32 bits; they are replaced below.
+    with np.errstate(over="ignore"):
+        rounded = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
     out = rounded.astype(np.uint16)
+    is_nan = np.isnan(x)
     if is_nan.any():
-        out = np.where(is_nan, ((u >> 16) | 0x0040).astype(np.uint16), out)
+        out = np.where(is_nan, ((u >> np.uint32(16)) | np.uint32(0x0040)).astype(np.uint16), out)
     return out
 
 

@@ -1,0 +1,158 @@
+/*
+ * gdn.h -- C ABI of libgdn.so: the Gated DeltaNet recurrent layer on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer keeps, per sequence and value head, a fixed-size fp32 matrix state
+ * S (dv x dk). For every token a learned gate decides how much of S to keep
+ * and a delta update writes the token in ("Optimiser l'inference sur appareil
+ * pour Apple Silicon", section "Qwen cree trois formes de charges de travail
+ * distinctes"). The gated delta rule computed here:
+ *
+ *     a_t = exp(g_t)
+ *     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T
+ *     o_t = scale * S_t q_t
+ *
+ * Prefill evaluates it chunk by chunk (the reorganisation into blocks that
+ * exposes matrix products, same section); decode advances one token per
+ * sequence against resident states. State and gates stay fp32 because the
+ * rounding of sequential updates accumulates ("Maintenir l'etat recurrent sur
+ * la puce"); a long prompt can be split into fragments whose final state is
+ * the next fragment's initial state ("Limiter la memoire temporaire grace au
+ * decoupage des prompts").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer to row-major, contiguous memory
+ *   that the caller owns. The library allocates no device memory per call and
+ *   keeps no pointer after a call returns.
+ * - Layouts, with T = total tokens, N = sequences, B = decode batch:
+ *       q, k            [T][hk][dk]         (decode: [B][hk][dk])
+ *       v, out          [T][hv][dv]         (decode: [B][hv][dv])
+ *       g, beta         [T][hv]             (decode: [B][hv])
+ *       states          [N or slots][hv][dv][dk] fp32; element [i][j] is
+ *                       S[i][j], i over values, j over keys.
+ *   Value head h reads query/key head h / (hv / hk): consecutive value heads
+ *   share one query/key head.
+ * - g is the log of the decay (a = exp(g)); it must be finite. beta is used
+ *   as given (normally in [0, 1]).
+ * - io_dtype applies to q, k, v and out; gate_dtype to g and beta.
+ * - `stream` is a hipStream_t (NULL = the null stream). Calls enqueue work on
+ *   it and return without synchronising; device-side faults surface at the
+ *   caller's next synchronisation.
+ * - Argument errors are detected on the host before anything is enqueued and
+ *   reported as a status code; no C++ exception or abort crosses the ABI.
+ *   After a launch, a HIP launch error is reported as GDN_ERR_HIP.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL_ARG = 1,    /* a required pointer is NULL */
+    GDN_ERR_BAD_SHAPE = 2,   /* negative size, hv % hk != 0, ... */
+    GDN_ERR_UNSUPPORTED = 3, /* head size, chunk or dtype outside the built set */
+    GDN_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
+    GDN_ERR_HIP = 5,         /* a HIP runtime call or launch failed */
+    GDN_ERR_ALIAS = 6        /* out overlaps an input */
+} gdn_status;
+
+typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+
+/* Version of this ABI (GDN_ABI_VERSION of the built library). */
+int32_t gdn_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *gdn_status_string(int32_t status);
+
+/*
+ * Bytes of device workspace gdn_prefill needs for these sizes. Depends only
+ * on host-known sizes (never on the contents of cu_seqlens). Returns 0 for
+ * arguments gdn_prefill would reject.
+ */
+size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
+                                  int32_t hk, int32_t hv, int32_t dk, int32_t dv,
+                                  int32_t chunk, int32_t io_dtype);
+
+/*
+ * Chunked prefill over N packed variable-length sequences.
+ *
+ * cu_seqlens   int32 [N + 1] DEVICE array of token offsets: sequence n owns
+ *              tokens [cu_seqlens[n], cu_seqlens[n+1]). It is read only on the
+ *              device. Offsets are clamped into [0, total_tokens] and made
+ *              non-decreasing there, so a malformed array cannot cause an
+ *              out-of-bounds access (its results are then unspecified).
+ *              Zero-length sequences are allowed: their final state equals
+ *              their initial state.
+ * chunk        tokens per chunk: 16, 32 or 64. The result does not depend on
+ *              it beyond rounding.
+ * dk, dv       16, 32, 64 or 128 each.
+ * scale        multiplies every output (1.0 for the plain rule).
+ * initial_state  fp32 [N][hv][dv][dk], or NULL for zero states.
+ * final_state    fp32 [N][hv][dv][dk], or NULL to skip writing it. It may be
+ *                the same pointer as initial_state (updated in place).
+ * out          [T][hv][dv] in io_dtype; must not overlap q, k, v, g, beta,
+ *              cu_seqlens or the states (GDN_ERR_ALIAS).
+ * workspace    device scratch of at least gdn_prefill_workspace_size(...)
+ *              bytes, 256-byte aligned; contents need not be initialised and
+ *              are meaningless afterwards. Calls on different streams need
+ *              different workspaces.
+ */
+int32_t gdn_prefill(const void *q, const void *k, const void *v,
+                    const void *g, const void *beta,
+                    const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                    int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
+                    float scale, int32_t io_dtype, int32_t gate_dtype,
+                    const float *initial_state, float *final_state, void *out,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step: one new token for each of `batch` sequences, updating
+ * their resident fp32 states in place.
+ *
+ * state        fp32 [num_slots][hv][dv][dk], read and written in place.
+ * state_slots  int32 [batch] DEVICE array: sequence b uses state slot
+ *              state_slots[b]; NULL means slot b (then num_slots >= batch is
+ *              required). A slot outside [0, num_slots) makes the kernel skip
+ *              that sequence: its state is untouched and its output row is
+ *              written as zeros. Two sequences of one call must not share a
+ *              slot.
+ * dk, dv       16, 32, 64 or 128 each.
+ * out          [batch][hv][dv] in io_dtype; must not overlap the inputs.
+ */
+int32_t gdn_decode_step(const void *q, const void *k, const void *v,
+                        const void *g, const void *beta,
+                        int32_t batch, int32_t hk, int32_t hv, int32_t dk, int32_t dv,
+                        float scale, int32_t io_dtype, int32_t gate_dtype,
+                        float *state, const int32_t *state_slots, int32_t num_slots,
+                        void *out, void *stream);
+
+/*
+ * Per-kernel timing (a profiling aid, not needed for computation).
+ *
+ * gdn_timing_start(max_launches) makes the library bracket each of its next
+ * kernel launches (up to max_launches) with a pair of HIP events recorded on
+ * the stream the kernel is launched on. gdn_timing_stop() waits for those
+ * events, writes for each kernel kind k < n_kinds the number of launches
+ * timed (counts[k]) and their summed duration in milliseconds (total_ms[k]),
+ * releases the events and stops timing. Kinds: 0 = varlen schedule,
+ * 1 = chunk preparation, 2 = chunk-recurrent scan, 3 = decode step.
+ * Not thread-safe with concurrent gdn_* calls from other host threads.
+ */
+#define GDN_KERNEL_KINDS 4
+int32_t gdn_timing_start(int32_t max_launches);
+int32_t gdn_timing_stop(int32_t *counts, float *total_ms, int32_t n_kinds);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

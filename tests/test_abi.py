@@ -1,0 +1,157 @@
+"""The C ABI on the host: symbols, sizes and argument checks (no GPU needed).
+
+Every call here is rejected by host-side validation before any HIP call is
+made, so it runs on machines without a GPU. Fake device pointers are plain
+non-zero integers; the library never dereferences them on the host.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_linear_02_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, NULL_ARG, BAD_SHAPE, UNSUPPORTED, WORKSPACE, HIP, ALIAS = range(7)
+BF16, F32 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.lib_path()):
+        from gated_deltanet_linear_02_amd import build
+        build.build()
+    return gdn.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert {"gdn_prefill", "gdn_decode_step", "gdn_prefill_workspace_size",
+            "gdn_status_string", "gdn_abi_version"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in gdn.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert gdn.abi_version() == 1
+    for s in range(7):
+        assert lib.gdn_status_string(s)
+    assert b"unknown" in lib.gdn_status_string(99)
+
+
+def _ws(n=1, T=4096, hk=16, hv=32, d=128, c=64, io=BF16):
+    return gdn.load().gdn_prefill_workspace_size(n, T, hk, hv, d, d, c, io)
+
+
+def test_workspace_size(lib):
+    w = _ws()
+    # T, P per (chunk, value head) in bf16, gates 16 B per token-head
+    chunks = 4096 // 64 + 1
+    assert w >= chunks * 32 * (2 * 64 * 64 * 2 + 64 * 16)
+    assert w < chunks * 32 * (2 * 64 * 64 * 2 + 64 * 16) + 64 * 1024
+    assert _ws(io=F32) > w
+    assert _ws(T=0) > 0
+    # rejected shapes give 0
+    assert _ws(hk=3, hv=32) == 0
+    assert _ws(d=96) == 0
+    assert _ws(c=48) == 0
+    assert _ws(n=0) == 0
+
+
+FAKE = 0x7F0000000000
+
+# The checks below pass fake device pointers and expect host-side rejection.
+# On a machine with a GPU a validation bug would launch a kernel on them, so
+# they only run where no GPU is visible.
+no_gpu = pytest.mark.skipif(
+    __import__("torch").cuda.device_count() > 0,
+    reason="fake-pointer validation tests run only on hosts without a GPU")
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30),
+             beta=FAKE + (4 << 30), cu=FAKE + (5 << 30), n=1, T=128, hk=2, hv=4, dk=64, dv=64,
+             chunk=64, scale=1.0, io=BF16, gate=F32, s0=None, sf=None, out=FAKE + (6 << 30),
+             ws=FAKE + (7 << 30), ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.gdn_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["n"], a["T"],
+                           a["hk"], a["hv"], a["dk"], a["dv"], a["chunk"], a["scale"], a["io"],
+                           a["gate"], a["s0"], a["sf"], a["out"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@no_gpu
+def test_prefill_argument_checks(lib):
+    assert _prefill(lib, q=None) == NULL_ARG
+    assert _prefill(lib, cu=None) == NULL_ARG
+    assert _prefill(lib, out=None) == NULL_ARG
+    assert _prefill(lib, hk=3, hv=4) == BAD_SHAPE
+    assert _prefill(lib, n=0) == BAD_SHAPE
+    assert _prefill(lib, T=-1) == BAD_SHAPE
+    assert _prefill(lib, T=1 << 33) == BAD_SHAPE
+    assert _prefill(lib, dk=96, dv=96) == UNSUPPORTED
+    assert _prefill(lib, dk=64, dv=128) == UNSUPPORTED
+    assert _prefill(lib, chunk=128) == UNSUPPORTED
+    assert _prefill(lib, io=7) == UNSUPPORTED
+    assert _prefill(lib, gate=2) == UNSUPPORTED
+    assert _prefill(lib, ws=None) == WORKSPACE
+    assert _prefill(lib, ws_bytes=100) == WORKSPACE
+    assert _prefill(lib, ws=FAKE + (7 << 30) + 16) == WORKSPACE  # misaligned
+    # out overlapping an input
+    assert _prefill(lib, out=FAKE + 64) == ALIAS
+    assert _prefill(lib, out=FAKE + (4 << 30) + 8) == ALIAS
+    # final state overlapping q
+    assert _prefill(lib, sf=FAKE + 128) == ALIAS
+    # in-place final == initial state is allowed by validation (it would launch
+    # next, so it is not called here); overlapping but different is not
+    assert _prefill(lib, s0=FAKE + (8 << 30), sf=FAKE + (8 << 30) + 4) == ALIAS
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30),
+             beta=FAKE + (4 << 30), B=64, hk=16, hv=32, dk=128, dv=128, scale=1.0, io=BF16,
+             gate=BF16, state=FAKE + (5 << 30), slots=None, num_slots=64,
+             out=FAKE + (9 << 30), stream=None)
+    a.update(kw)
+    return lib.gdn_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["B"], a["hk"], a["hv"],
+                               a["dk"], a["dv"], a["scale"], a["io"], a["gate"], a["state"],
+                               a["slots"], a["num_slots"], a["out"], a["stream"])
+
+
+@no_gpu
+def test_decode_argument_checks(lib):
+    assert _decode(lib, B=0) == OK  # nothing to do, nothing launched
+    assert _decode(lib, state=None) == NULL_ARG
+    assert _decode(lib, v=None) == NULL_ARG
+    assert _decode(lib, B=-1) == BAD_SHAPE
+    assert _decode(lib, hk=5) == BAD_SHAPE
+    assert _decode(lib, num_slots=10) == BAD_SHAPE  # identity slots need num_slots >= batch
+    assert _decode(lib, dk=48, dv=48) == UNSUPPORTED
+    assert _decode(lib, io=3) == UNSUPPORTED
+    assert _decode(lib, out=FAKE + 100) == ALIAS
+    assert _decode(lib, out=FAKE + (5 << 30) + 4096) == ALIAS  # out inside the state
+    assert _decode(lib, state=FAKE + (2 << 30) + 64) == ALIAS  # state over v
+
+
+def test_timing_stop_without_start(lib):
+    assert lib.gdn_timing_stop(None, None, 0) == BAD_SHAPE
+    assert lib.gdn_timing_start(0) == BAD_SHAPE
+
+
+def test_binding_raises_on_missing_library(tmp_path, monkeypatch):
+    import importlib
+    mod = importlib.reload(gdn)
+    monkeypatch.setattr(mod, "_LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(mod, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        mod.load()
+    importlib.reload(gdn)

@@ -1,0 +1,127 @@
+"""Decode step on the GPU against the fp64 oracle (one token per sequence).
+
+Workload: 16 query/key heads shared by 32 value heads, d = 128, fp32 states
+~ N(0, 0.02^2), q/k/v/gates drawn by gdn_synth; batch 1..64.
+Bars: bf16 outputs <= 2e-2 (max abs error / max |ref|); the state update is
+fp32 arithmetic on the same inputs, so states are held to 1e-4 in both
+modes; fp32 I/O mode holds outputs to 1e-4 too.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gdn_synth as gs
+import gated_deltanet_linear_02_amd as gdn
+import oracle
+from gpu_util import TOL_F32, device_inputs, note, rel_err, requires_gpu, to_f64, tol
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _decode_case(batch, io_dtype, seed_off=0, d=128, hk=16, hv=32, scale=1.0):
+    inp = gs.make_inputs([1] * batch, hk, hv, d, d, seed=gs.SEED_BASE + 1 + seed_off,
+                         io_dtype=io_dtype, gate_dtype=io_dtype)
+    s0 = gs.decode_state(batch, hv, d, d, seed=gs.SEED_BASE + 101 + seed_off)
+    return inp, s0
+
+
+@pytest.mark.parametrize("io_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("batch", [1, 2, 7, 64])
+def test_decode_matches_oracle(batch, io_dtype):
+    inp, s0 = _decode_case(batch, io_dtype)
+    note(f"decode batch={batch} io={io_dtype}")
+    d = device_inputs(inp)
+    state = torch.from_numpy(s0).cuda()
+    out = torch.full((batch, 32, 128), float("nan"), dtype=d["q"].dtype, device="cuda")
+    gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, out=out)
+    torch.cuda.synchronize()
+    w = inp.widened()
+    o_ref, s_ref = oracle.decode_step(w["q"], w["k"], w["v"], w["g"], w["beta"], s0.astype(np.float64))
+    o = to_f64(out)
+    assert np.isfinite(o).all()
+    assert rel_err(o, o_ref) <= tol(io_dtype)
+    assert rel_err(to_f64(state), s_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("d", [16, 32, 64])
+def test_decode_other_head_sizes(d):
+    inp, s0 = _decode_case(5, "f32", seed_off=3, d=d, hk=2, hv=4, scale=0.5)
+    note(f"decode d={d}")
+    dd = device_inputs(inp)
+    state = torch.from_numpy(s0).cuda()
+    out = gdn.decode_step(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], state, scale=0.5)
+    torch.cuda.synchronize()
+    w = inp.widened()
+    o_ref, s_ref = oracle.decode_step(w["q"], w["k"], w["v"], w["g"], w["beta"], s0.astype(np.float64),
+                                      scale=0.5)
+    assert rel_err(to_f64(out), o_ref) <= TOL_F32
+    assert rel_err(to_f64(state), s_ref) <= TOL_F32
+
+
+def test_decode_state_slots():
+    """Indirect slots: sequence b updates slot[b]; slot -1 is skipped (zeros out,
+    state untouched); untouched slots keep their bits."""
+    batch, slots_n = 6, 10
+    inp, _ = _decode_case(batch, "bf16", seed_off=5)
+    pool = gs.decode_state(slots_n, 32, 128, 128, seed=gs.SEED_BASE + 77)
+    slots = np.array([7, 2, -1, 0, 9, 4], dtype=np.int32)
+    note("decode state_slots")
+    d = device_inputs(inp)
+    state = torch.from_numpy(pool).cuda()
+    out = gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state,
+                          state_slots=torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    w = inp.widened()
+    o_ref, s_ref = oracle.decode_step(w["q"], w["k"], w["v"], w["g"], w["beta"],
+                                      pool[np.maximum(slots, 0)].astype(np.float64))
+    got = to_f64(state)
+    o = to_f64(out)
+    for b, s in enumerate(slots):
+        if s < 0:
+            assert np.all(o[b] == 0)
+            continue
+        assert rel_err(o[b], o_ref[b]) <= 2e-2
+        assert rel_err(got[s], s_ref[b]) <= TOL_F32
+    for s in set(range(slots_n)) - set(int(x) for x in slots):
+        assert np.array_equal(got[s], pool[s].astype(np.float64))
+
+
+def test_decode_is_deterministic():
+    inp, s0 = _decode_case(64, "bf16", seed_off=9)
+    note("decode determinism")
+    d = device_inputs(inp)
+    res = []
+    for _ in range(2):
+        st = torch.from_numpy(s0).cuda()
+        o = gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], st)
+        torch.cuda.synchronize()
+        res.append((o.view(torch.int16).cpu().numpy(), st.cpu().numpy()))
+    assert np.array_equal(res[0][0], res[1][0])
+    assert np.array_equal(res[0][1], res[1][1])
+
+
+def test_decode_retrieval_exact_in_bf16():
+    """b = 1, a = 1, standard-basis keys, zero state: writing v at key e_j and
+    querying e_j returns v bit for bit (every product is exact)."""
+    B, hk, hv, d = 4, 2, 4, 128
+    q = np.zeros((B, hk, d), np.float64)
+    k = np.zeros((B, hk, d), np.float64)
+    for b in range(B):
+        for kh in range(hk):
+            j = (5 * b + 3 * kh) % d
+            q[b, kh, j] = k[b, kh, j] = 1.0
+    rng = np.random.default_rng(0)
+    v = rng.standard_normal((B, hv, d))
+    inp = gs.GdnInputs(q=gs.to_storage(q, "bf16"), k=gs.to_storage(k, "bf16"),
+                       v=gs.to_storage(v, "bf16"), g=gs.to_storage(np.zeros((B, hv)), "bf16"),
+                       beta=gs.to_storage(np.ones((B, hv)), "bf16"),
+                       cu_seqlens=np.arange(B + 1, dtype=np.int32), initial_state=None,
+                       hk=hk, hv=hv, dk=d, dv=d, io_dtype="bf16", gate_dtype="bf16")
+    s0 = np.zeros((B, hv, d, d), np.float32)
+    note("decode retrieval")
+    dd = device_inputs(inp)
+    out = gdn.decode_step(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], torch.from_numpy(s0).cuda())
+    torch.cuda.synchronize()
+    vb = gs.widen(inp.v, "bf16")
+    assert np.array_equal(to_f64(out), vb)
