@@ -96,9 +96,9 @@ static int32_t check_prefill_shape(int32_t num_seqs, int64_t total_tokens, int32
     if (!valid_head(dk) || dv != dk || !valid_chunk(chunk) || !valid_dtype(io_dtype) ||
         !valid_dtype(gate_dtype) || hk > 65535)
         return GDN_ERR_UNSUPPORTED;
-    const PrefillLayout L = prefill_layout(num_seqs, total_tokens, hv, chunk, dtype_bytes(io_dtype));
+    const PrefillLayout L = prefill_layout(num_seqs, total_tokens, hk, hv, dk, chunk, dtype_bytes(io_dtype));
     const int64_t scan_grid = (((int64_t)num_seqs * hk + 7) / 8) * (hv / hk) * (dv / 16) * 8;
-    if (L.max_chunks > INT32_MAX || scan_grid > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    if (scan_grid > INT32_MAX || L.max_chunks > INT32_MAX) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
 
@@ -106,7 +106,7 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_
                                   int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype) {
     if (check_prefill_shape(num_seqs, total_tokens, hk, hv, dk, dv, chunk, io_dtype, GDN_F32) != GDN_OK)
         return 0;
-    return prefill_layout(num_seqs, total_tokens, hv, chunk, dtype_bytes(io_dtype)).total;
+    return prefill_layout(num_seqs, total_tokens, hk, hv, dk, chunk, dtype_bytes(io_dtype)).total;
 }
 
 int32_t gdn_prefill(const void *q, const void *k, const void *v, const void *g, const void *beta,
@@ -121,7 +121,7 @@ int32_t gdn_prefill(const void *q, const void *k, const void *v, const void *g, 
     if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL_ARG;
 
     const size_t eb = dtype_bytes(io_dtype), gb = dtype_bytes(gate_dtype);
-    const PrefillLayout L = prefill_layout(num_seqs, total_tokens, hv, chunk, eb);
+    const PrefillLayout L = prefill_layout(num_seqs, total_tokens, hk, hv, dk, chunk, eb);
     if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
         return GDN_ERR_WORKSPACE;
 

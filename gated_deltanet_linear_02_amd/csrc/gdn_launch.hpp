@@ -34,7 +34,10 @@ struct PrefillLayout {
     int64_t max_chunks;
     size_t off_bounds, off_seq_chunk0, off_order;   // int32 [N+1], [N+1], [N]
     size_t off_chunk_seq, off_chunk_tok0, off_counters;            // int32 [max_chunks], [4]
-    size_t off_tmat, off_pmat;   // E [max_chunks][hv][C][C]
+    // Operands of the scan, each in MFMA fragment order (C*C or C*dk
+    // elements per chunk and head):
+    size_t off_tmat, off_pmat;      // E, per (chunk, value head)
+    size_t off_kmat, off_qmat, off_ktmat;  // E, per (chunk, query/key head)
     size_t off_gates;            // float4 [max_chunks][hv][C]
     size_t off_gammac;           // float [max_chunks][hv]
     size_t total;
@@ -42,8 +45,8 @@ struct PrefillLayout {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-inline PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t hv,
-                                    int64_t chunk, size_t elem_bytes) {
+inline PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
+                                    int64_t dk, int64_t chunk, size_t elem_bytes) {
     PrefillLayout L;
     L.max_chunks = (total_tokens + chunk - 1) / chunk + num_seqs;
     size_t o = 0;
@@ -57,6 +60,10 @@ inline PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int6
     const size_t per_mat = (size_t)L.max_chunks * (size_t)hv * (size_t)(chunk * chunk) * elem_bytes;
     L.off_tmat = take(per_mat);
     L.off_pmat = take(per_mat);
+    const size_t per_kq = (size_t)L.max_chunks * (size_t)hk * (size_t)(dk * chunk) * elem_bytes;
+    L.off_kmat = take(per_kq);
+    L.off_qmat = take(per_kq);
+    L.off_ktmat = take(per_kq);
     L.off_gates = take((size_t)L.max_chunks * (size_t)hv * (size_t)chunk * 16);
     L.off_gammac = take((size_t)L.max_chunks * (size_t)hv * sizeof(float));
     L.total = o;
