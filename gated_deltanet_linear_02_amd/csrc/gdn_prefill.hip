@@ -406,7 +406,8 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
 // the chunk (for X = K S0^T, Q S0^T, Y, U = T Y and the output) and the
 // key tiles mt = w, w+4, .. of the state slice (for its update). Every MFMA
 // A operand (K, Q, T, P, K^T) is one contiguous fragment load from the
-// workspace, issued two chunks ahead into registers; LDS only carries the
+// workspace, issued two chunks ahead into one of three register stages
+// (bf16; fp32 fragments are four times larger and use one); LDS only carries the
 // small per-chunk exchanges between waves (the state's operand copy, Y, U,
 // diag(delta) U, the gates and the output tile).
 
@@ -536,7 +537,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int LDK = L::LDK, LDC = L::LDC;
     constexpr int RT = WS::RT, MT = WS::MT, NRW = WS::NRW, NMW = WS::NMW;
     constexpr int KBD = WS::KBD, KBC = WS::KBC;
-    constexpr bool kTwoStages = IsBf16<E>::value;  // fp32 fragments are 4x larger
+    constexpr bool kThreeStages = IsBf16<E>::value;  // fp32 fragments are 4x larger
 
     extern __shared__ __align__(16) char smem[];
     E *sS = reinterpret_cast<E *>(smem + L::off_S);
@@ -584,16 +585,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     }
 
-    WS st0, st1;
+    WS st0, st1, st2;
     auto issue = [&](WS &st, int c) {
         st.load(v, tmat, pmat, kmat, qmat, ktmat, gates, gammac, start + c * C, min(C, len - c * C), c0 + c,
                 hk, kh, hv, h, col0, wave, lane);
     };
 
-    // One chunk. The gate vectors of chunk c are in sG[c & 1] when it starts.
-    // With stage_next, nxt holds chunk c + 1, whose gates are staged before
-    // the last barrier.
-    auto body = [&](WS &st, WS &nxt, int c, auto stage_next) {
+    // One chunk c with its operands in `st`. The gate vectors of chunk c are
+    // in sG[c & 1] when it starts.
+    //   kThree: `fut` (which held chunk c - 1) is refilled with chunk c + 2 at
+    //           the start, so each load has two chunk-times to land; `nxt`
+    //           holds chunk c + 1, whose gates are staged before the last
+    //           barrier.
+    //   otherwise (one stage): `st` is refilled with chunk c + 1 at the end.
+    auto body = [&](WS &st, WS &nxt, WS &fut, int c, auto three) {
+        constexpr bool kThree = decltype(three)::value;
+        if constexpr (kThree) issue(fut, min(c + 2, nch - 1));  // past the end: reload the last chunk (ignored)
         const int tok0 = start + c * C;
         const int clen = min(C, len - c * C);
         // This wave's gate rows, read once before any LDS store of this chunk
@@ -681,34 +688,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 store_acc_t<E>(sS, LDK, 16 * mt, 0, lane, acc);
             }
         }
-        if constexpr (decltype(stage_next)::value) nxt.put_gates(sG + ((c + 1) & 1) * C, wave, lane);
+        if constexpr (kThree) nxt.put_gates(sG + ((c + 1) & 1) * C, wave, lane);
         __syncthreads();
 
-        // Refill this stage for the chunk it serves next (past the end the
-        // last chunk is loaded again and ignored, so the load is
-        // unconditional), then write this chunk's output tile; sO is only
-        // rewritten after two more barriers.
-        issue(st, min(c + (kTwoStages ? 2 : 1), nch - 1));
+        if constexpr (!kThree) issue(st, min(c + 1, nch - 1));
+        // this chunk's output tile; sO is only rewritten after two more barriers
         flush_out<E, C, R>(sO, out, tok0, clen, hv, h, DV, col0, tid);
     };
 
     if (nch > 0) {
         issue(st0, 0);
-        if constexpr (kTwoStages) {
+        if constexpr (kThreeStages) {
             issue(st1, min(1, nch - 1));
             st0.put_gates(sG, wave, lane);
             __syncthreads();
             int c = 0;
-            for (; c + 1 < nch; c += 2) {
-                body(st0, st1, c, std::true_type());
-                body(st1, st0, c + 1, std::true_type());
+            for (; c + 2 < nch; c += 3) {
+                body(st0, st1, st2, c, std::true_type());
+                body(st1, st2, st0, c + 1, std::true_type());
+                body(st2, st0, st1, c + 2, std::true_type());
             }
-            if (c < nch) body(st0, st1, c, std::false_type());
+            if (c < nch) body(st0, st1, st2, c, std::true_type());
+            if (c + 1 < nch) body(st1, st2, st0, c + 1, std::true_type());
         } else {
             for (int c = 0; c < nch; ++c) {
                 st0.put_gates(sG + (c & 1) * C, wave, lane);
                 __syncthreads();
-                body(st0, st1, c, std::false_type());
+                body(st0, st0, st0, c, std::false_type());
             }
         }
     }
