@@ -87,6 +87,72 @@ def measured_traffic(kernel: str):
     return ent.get("bytes_per_launch")
 
 
+KERNELS = {"schedule": "gdn_schedule_kernel", "prep": "gdn_prep_kernel", "scan": "gdn_scan_kernel",
+           "decode": "gdn_decode_kernel"}
+
+
+def _short_kernel(name: str) -> str:
+    for short, key in KERNELS.items():
+        if key in name:
+            return short
+    return "copy" if "copy" in name.lower() else "other"
+
+
+def _counter_means(directory: str, counter: str, probe_bytes: int):
+    """Mean counter value (KiB) per dispatch of each library kernel, and the
+    factor that maps the counter to bytes, taken from the probe copies (the
+    dispatches of a copy kernel within 10% of the largest one)."""
+    import csv
+    path = os.path.join(directory, "run_counter_collection.csv")
+    per = {}
+    copies = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            short = _short_kernel(r["Kernel_Name"])
+            val = float(r["Counter_Value"])
+            if short == "copy":
+                copies.append(val)
+            elif short != "other":
+                per.setdefault(short, []).append(val)
+    top = max(copies) if copies else 0.0
+    probe = [c for c in copies if c >= 0.9 * top]
+    if not probe:
+        raise SystemExit(f"no probe copy found in {path}")
+    kib = sum(probe) / len(probe)
+    factor = probe_bytes / kib
+    return {k: sum(v) / len(v) for k, v in per.items()}, factor, kib
+
+
+def summarize_profiles(stats_dir: str, fetch_dir: str, write_dir: str, probe_mib: int):
+    """Write profiles/traffic.json and the markdown summaries from rocprofv3
+    runs of this script (kernel trace with --stats; one --pmc FETCH_SIZE and
+    one --pmc WRITE_SIZE pass, each with --copy-probe-mib)."""
+    import csv
+    probe_bytes = probe_mib << 20
+    fetch, ffac, fkib = _counter_means(fetch_dir, "FETCH_SIZE", probe_bytes)
+    write, wfac, wkib = _counter_means(write_dir, "WRITE_SIZE", probe_bytes)
+    h = kernel_source_hash()
+    traffic = {"source_hash": h, "probe_copy_bytes": probe_bytes,
+               "fetch_bytes_per_kib": ffac, "write_bytes_per_kib": wfac}
+    for short in ("schedule", "prep", "scan", "decode"):
+        if short in fetch and short in write:
+            fb, wb = fetch[short] * ffac, write[short] * wfac
+            traffic[KERNELS[short]] = {"source_hash": h, "bytes_per_launch": fb + wb,
+                                       "fetch_bytes": fb, "write_bytes": wb,
+                                       "fetch_kib_raw": fetch[short], "write_kib_raw": write[short]}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+        f.write("\n")
+    rows = []
+    with open(os.path.join(stats_dir, "run_kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            rows.append(r)
+    return traffic, rows
+
+
 def to_device(x: np.ndarray, dtype: str, dev):
     import torch
     if dtype == "bf16":
@@ -137,7 +203,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="buffer sets rotated through (cold caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before warm-up, run 3 device-to-device copies of this many MiB "
+                         "(the known-size reference for HBM byte counters)")
+    ap.add_argument("--summarize", nargs=4, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR", "PROBE_MIB"),
+                    help="host only: turn rocprofv3 output directories into the summaries under "
+                         "profiles/ and exit")
     args = ap.parse_args()
+
+    if args.summarize:
+        summarize_profiles(*args.summarize[:3], int(args.summarize[3]))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -190,6 +266,14 @@ def main():
         sys.exit(1)
 
     stream = torch.cuda.current_stream(dev)
+    if args.copy_probe_mib > 0:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(sets[i % args.copies])
     torch.cuda.synchronize()

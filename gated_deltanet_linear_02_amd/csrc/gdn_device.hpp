@@ -83,6 +83,43 @@ __device__ __forceinline__ typename M::Frag load_frag(const E *base, int ld, int
     return *reinterpret_cast<const typename M::Frag *>(p);
 }
 
+// Accumulator order of a contraction index. An accumulator tile gives each
+// lane 4 consecutive elements of one row (columns 4 (l/16) + r of a 16-wide
+// tile). Fragments in accumulator order take their KPL elements in those
+// runs: slot e of lane group g of fragment kb holds contraction index
+// acc_k(kb, g, e). Because the MFMA sums over k in any order as long as A
+// and B agree, a product whose operands both use this order is the same
+// product; it lets one product's accumulators be stored, or read back from
+// LDS, as the next product's fragments without a transpose.
+template <typename MM> __device__ __forceinline__ int acc_k(int kb, int g, int e) {
+    if constexpr (MM::KPL == 1) return 16 * (kb >> 2) + 4 * g + (kb & 3);
+    else return kb * MM::KW + 16 * (e >> 2) + 4 * g + (e & 3);
+}
+// The 16-wide tile and the slot within the lane's run of acc_k(kb, g, e).
+template <typename MM> __device__ __forceinline__ constexpr int acc_tile(int kb, int e) {
+    return MM::KPL == 1 ? (kb >> 2) : (kb * MM::KW) / 16 + (e >> 2);
+}
+template <typename MM> __device__ __forceinline__ constexpr int acc_slot(int kb, int e) {
+    return MM::KPL == 1 ? (kb & 3) : (e & 3);
+}
+
+// Fragment of a row-major [rows][ld] LDS array in accumulator order: row
+// r0 + l%16, contraction elements acc_k(kb, l/16, .).
+template <typename M, typename E>
+__device__ __forceinline__ typename M::Frag load_frag_acc(const E *base, int ld, int r0, int kb, int lane) {
+    const int g = lane >> 4;
+    const E *row = base + (r0 + (lane & 15)) * ld;
+    if constexpr (M::KPL == 1) {
+        return row[16 * (kb >> 2) + 4 * g + (kb & 3)];
+    } else if constexpr (M::KPL == 4) {
+        return *reinterpret_cast<const bf16x4 *>(row + kb * 16 + 4 * g);
+    } else {
+        const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(row + kb * 32 + 4 * g);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(row + kb * 32 + 16 + 4 * g);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
+
 // Write an accumulator tile transposed: element D[m0 + 4g + i][n0 + n] goes to
 // dst[(n0 + n) * ld + m0 + 4g + i] (4 contiguous elements per lane).
 template <typename E> __device__ __forceinline__ void store_acc_t(E *dst, int ld, int m0, int n0, int lane, f32x4 v);

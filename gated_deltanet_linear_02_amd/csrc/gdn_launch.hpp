@@ -36,10 +36,10 @@ struct PrefillLayout {
     size_t off_chunk_seq, off_chunk_tok0, off_counters;            // int32 [max_chunks], [4]
     // Operands of the scan, each in MFMA fragment order (C*C or C*dk
     // elements per chunk and head):
-    size_t off_tmat, off_pmat;      // E, per (chunk, value head)
-    size_t off_kmat, off_qmat, off_ktmat;  // E, per (chunk, query/key head)
-    size_t off_gates;            // float4 [max_chunks][hv][C]
-    size_t off_gammac;           // float [max_chunks][hv]
+    size_t off_tbmat, off_pmat, off_wmat;  // E, per (chunk, value head)
+    size_t off_qmat, off_ktmat;            // E, per (chunk, query/key head)
+    size_t off_sgam, off_delta;            // float [max_chunks][hv][C]
+    size_t off_gammac;                     // float [max_chunks][hv]
     size_t total;
 };
 
@@ -58,13 +58,14 @@ inline PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int6
     L.off_chunk_tok0 = take(sizeof(int32_t) * (size_t)L.max_chunks);
     L.off_counters = take(sizeof(int32_t) * 4);
     const size_t per_mat = (size_t)L.max_chunks * (size_t)hv * (size_t)(chunk * chunk) * elem_bytes;
-    L.off_tmat = take(per_mat);
+    L.off_tbmat = take(per_mat);
     L.off_pmat = take(per_mat);
+    L.off_wmat = take((size_t)L.max_chunks * (size_t)hv * (size_t)(dk * chunk) * elem_bytes);
     const size_t per_kq = (size_t)L.max_chunks * (size_t)hk * (size_t)(dk * chunk) * elem_bytes;
-    L.off_kmat = take(per_kq);
     L.off_qmat = take(per_kq);
     L.off_ktmat = take(per_kq);
-    L.off_gates = take((size_t)L.max_chunks * (size_t)hv * (size_t)chunk * 16);
+    L.off_sgam = take((size_t)L.max_chunks * (size_t)hv * (size_t)chunk * sizeof(float));
+    L.off_delta = take((size_t)L.max_chunks * (size_t)hv * (size_t)chunk * sizeof(float));
     L.off_gammac = take((size_t)L.max_chunks * (size_t)hv * sizeof(float));
     L.total = o;
     return L;

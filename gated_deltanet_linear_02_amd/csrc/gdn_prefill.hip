@@ -138,23 +138,30 @@ __global__ __launch_bounds__(kSchedThreads) void gdn_schedule_kernel(
 // 2. Chunk preparation
 // ---------------------------------------------------------------------------
 //
-// One workgroup per (chunk, value head). It computes the chunk's gate
-// vectors, A and P from K K^T and Q K^T (MFMA), and T = (I + A)^-1 by blocks
-// of 16:
+// One workgroup per (chunk, query/key head). It computes K K^T and Q K^T on
+// MFMA once, keeps them in registers, and then for each value head of the
+// group applies that head's gates and builds the per-head operands of the
+// scan:
+//   Tb = T diag(b),   W = T diag(b gamma) K   (so that U = Tb V - W S0^T),
+//   P,  the gate vectors scale*gamma and delta = exp(c_C - c), and gamma_C,
+// with T = (I + A)^-1 by blocks of 16:
 //   diagonal blocks    (I + A_bb)^-1 by forward substitution, one wave each;
 //   blocks below       T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj, one wave per
 //                      block column j, on fp32 MFMA,
-// which is (I + A) T = I written blockwise. All operands the scan needs are
-// written in MFMA fragment order (see frag_off), so that every fragment the
-// scan loads is one contiguous run: T and P per value head, and (by the first
-// value head of each query/key head) K, Q and K^T.
+// which is (I + A) T = I written blockwise. Q and K^T (shared by the value
+// heads of the group) are written once.
+//
+// Every operand goes to the workspace in MFMA fragment order (frag_off), so
+// that each fragment the scan loads is one contiguous 1 KB run, and with its
+// contraction index in accumulator order (acc_k), so that accumulator tiles
+// become fragments without a transpose.
 
 template <typename E> struct IsBf16 { static constexpr bool value = false; };
 template <> struct IsBf16<bf16> { static constexpr bool value = true; };
 
 // Element offset of lane `lane`'s part of fragment f in fragment order: a
-// matrix A [M][K] is stored as fragments f = rt * (K / KW) + kb, each holding
-// for lane l the KPL elements A[16 rt + l%16][kb KW + KPL (l/16) + j].
+// matrix [M][K] is stored as fragments f = rt * (K / KW) + kb, each holding
+// KPL elements per lane for rows 16 rt + l%16.
 template <typename MM> __device__ __forceinline__ size_t frag_off(int f, int lane) {
     return ((size_t)f * 64 + lane) * MM::KPL;
 }
@@ -164,19 +171,17 @@ struct PrepSmem {
     static constexpr int PE = Pad<E>::value;
     static constexpr int LDK = DK + PE;  // staged K and Q rows (E)
     static constexpr int LDC = C + 4;    // fp32 C x C arrays, 16-byte aligned rows
-    // Region X: K and Q tiles (phases 1-3), then A and T (phase 4).
+    // K and Q tiles (phases 1-4), then A and T (per value head).
     static constexpr size_t off_K = 0;
     static constexpr size_t off_Q = off_K + (size_t)C * LDK * sizeof(E);
     static constexpr size_t kq_end = off_Q + (size_t)C * LDK * sizeof(E);
     static constexpr size_t off_A = 0;
     static constexpr size_t off_T = off_A + (size_t)C * LDC * sizeof(float);
     static constexpr size_t at_end = off_T + (size_t)C * LDC * sizeof(float);
-    // Region Y: raw K K^T and Q K^T.
-    static constexpr size_t off_G = ((kq_end > at_end ? kq_end : at_end) + 15) & ~(size_t)15;
-    static constexpr size_t off_P0 = off_G + (size_t)C * LDC * sizeof(float);
-    static constexpr size_t off_c = off_P0 + (size_t)C * LDC * sizeof(float);
+    static constexpr size_t off_c = ((kq_end > at_end ? kq_end : at_end) + 15) & ~(size_t)15;
     static constexpr size_t off_b = off_c + (size_t)C * sizeof(float);
-    static constexpr size_t bytes = off_b + (size_t)C * sizeof(float);
+    static constexpr size_t off_bg = off_b + (size_t)C * sizeof(float);
+    static constexpr size_t bytes = off_bg + (size_t)C * sizeof(float);
 };
 
 template <typename M> __device__ __forceinline__ typename M::Frag zero_frag() {
@@ -193,6 +198,11 @@ template <typename M> __device__ __forceinline__ typename M::Frag zero_frag() {
 template <typename G> __device__ __forceinline__ float gate_load(const G *p, size_t i) {
     return static_cast<float>(p[i]);
 }
+
+// 2^x on the hardware instruction (arguments here are <= 0 for decaying
+// gates; results below the fp32 range flush to 0).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float kLog2e = 1.4426950408889634f;
 
 // acc += X[xr.., xc..] (16x16) * Y[yr.., yc..] (16x16), fp32 LDS operands
 // with row stride ld, on v_mfma_f32_16x16x4_f32.
@@ -216,27 +226,30 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
     const G *__restrict__ gate_g, const G *__restrict__ gate_b,
     const int32_t *__restrict__ bounds, const int32_t *__restrict__ chunk_seq,
     const int32_t *__restrict__ chunk_tok0, const int32_t *__restrict__ counters,
-    E *__restrict__ tmat, E *__restrict__ pmat, E *__restrict__ kmat, E *__restrict__ qmat,
-    E *__restrict__ ktmat, f32x4 *__restrict__ gates, float *__restrict__ gammac,
+    E *__restrict__ tbmat, E *__restrict__ pmat, E *__restrict__ wmat, E *__restrict__ qmat,
+    E *__restrict__ ktmat, float *__restrict__ sgam, float *__restrict__ delta, float *__restrict__ gammac,
     int32_t hk, int32_t hv, float scale)
 {
     typedef PrepSmem<E, C, DK> L;
-    typedef Mma<E, DK> MD;
-    typedef Mma<E, C> MC;
+    typedef Mma<E, DK> MD;  // contractions over keys
+    typedef Mma<E, C> MC;   // contractions over the tokens of a chunk
     constexpr int NB = C / 16, MT = DK / 16;
     constexpr int KBD = DK / MD::KW, KBC = C / MC::KW;
     constexpr int LDK = L::LDK, LDC = L::LDC;
     constexpr int EPV = 16 / sizeof(E), VPR = DK / EPV;
+    // Key tiles are handled in groups that make up whole W fragments: two
+    // for the 32-deep bf16 MFMA, one otherwise.
+    constexpr int DG = MD::KW >= 32 ? 2 : 1;
+    constexpr int NDG = MT / DG, NDGW = (NDG + 3) / 4;
 
     extern __shared__ __align__(16) char smem[];
     E *sK = reinterpret_cast<E *>(smem + L::off_K);
     E *sQ = reinterpret_cast<E *>(smem + L::off_Q);
     float *sA = reinterpret_cast<float *>(smem + L::off_A);
     float *sT = reinterpret_cast<float *>(smem + L::off_T);
-    float *sGk = reinterpret_cast<float *>(smem + L::off_G);
-    float *sP0 = reinterpret_cast<float *>(smem + L::off_P0);
-    float *sc = reinterpret_cast<float *>(smem + L::off_c);
-    float *sb = reinterpret_cast<float *>(smem + L::off_b);
+    float *sc = reinterpret_cast<float *>(smem + L::off_c);    // c_t log2(e)
+    float *sb = reinterpret_cast<float *>(smem + L::off_b);    // b_t
+    float *sbg = reinterpret_cast<float *>(smem + L::off_bg);  // b_t gamma_t
 
     const int ci = blockIdx.x, kh = blockIdx.y;
     if (ci >= counters[0]) return;
@@ -258,46 +271,77 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
     }
     __syncthreads();
 
-    // ---- 2. K, Q and K^T in fragment order for the scan
+    // ---- 2. Q fragments (keys in accumulator order)
     for (int f = wave; f < NB * KBD; f += 4) {
         const int rt = f / KBD, kb = f - rt * KBD;
-        *reinterpret_cast<typename MD::Frag *>(kmat + kq0 + frag_off<MD>(f, lane)) =
-            load_frag<MD>(sK, LDK, 16 * rt, kb * MD::KW, lane);
         *reinterpret_cast<typename MD::Frag *>(qmat + kq0 + frag_off<MD>(f, lane)) =
-            load_frag<MD>(sQ, LDK, 16 * rt, kb * MD::KW, lane);
-    }
-    for (int f = wave; f < MT * KBC; f += 4) {
-        const int mt = f / KBC, kb = f - mt * KBC;
-        typename MC::Frag fr;
-#pragma unroll
-        for (int e = 0; e < MC::KPL; ++e)  // K^T[m][t] = K[t][m]
-            frag_set<MC>(fr, e, to_f32(sK[(kb * MC::KW + MC::KPL * g4 + e) * LDK + 16 * mt + ln]));
-        *reinterpret_cast<typename MC::Frag *>(ktmat + kq0 + frag_off<MC>(f, lane)) = fr;
+            load_frag_acc<MD>(sQ, LDK, 16 * rt, kb, lane);
     }
 
-    // ---- 3. Raw K K^T and Q K^T on the lower-triangular 16x16 tiles
-    constexpr int NT = NB * (NB + 1) / 2;
-    for (int t = wave; t < 2 * NT; t += 4) {
-        const int which = t / NT;  // 0: Gram, 1: scores
-        int tt = t - which * NT, ti = 0;
-        while ((ti + 1) * (ti + 2) / 2 <= tt) ++ti;
-        const int tj = tt - ti * (ti + 1) / 2;
-        const E *Am = which ? sQ : sK;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // ---- 3. K^T fragments (tokens in accumulator order) of this wave's key
+    //         groups; kept in registers as the A operand of W
+    typename MC::Frag ktr[NDGW][DG][KBC];
 #pragma unroll
-        for (int kb = 0; kb < KBD; ++kb)
-            acc = MD::mma(load_frag<MD>(Am, LDK, 16 * ti, kb * MD::KW, lane),
-                          load_frag<MD>(sK, LDK, 16 * tj, kb * MD::KW, lane), acc);
-        float *dst = which ? sP0 : sGk;
+    for (int gi = 0; gi < NDGW; ++gi) {
+        const int dg = wave + 4 * gi;
+        if (dg < NDG) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(16 * ti + 4 * g4 + r) * LDC + 16 * tj + ln] = acc[r];
+            for (int t = 0; t < DG; ++t) {
+                const int mt = dg * DG + t;
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb) {
+                    typename MC::Frag fr;
+#pragma unroll
+                    for (int e = 0; e < MC::KPL; ++e)  // K^T[m][j] = K[j][m]
+                        frag_set<MC>(fr, e, to_f32(sK[acc_k<MC>(kb, g4, e) * LDK + 16 * mt + ln]));
+                    *reinterpret_cast<typename MC::Frag *>(ktmat + kq0 + frag_off<MC>(mt * KBC + kb, lane)) = fr;
+                    ktr[gi][t][kb] = fr;
+                }
+            }
+        }
     }
-    __syncthreads();
 
-    // ---- 4. Per value head of the group
+    // ---- 4. K K^T (waves 0, 1) and Q K^T (waves 2, 3) on the tiles at or
+    //         below the diagonal, computed as K_j K_i^T and K_j Q_i^T so that
+    //         lane l holds row 16 ti + l%16, columns 16 tj + 4 (l/16) + r.
+    //         Each wave owns up to two row tiles (paired for balance).
+    const bool score_wave = wave >= 2;
+    const int par = wave & 1;
+    int rows[2];
+    bool rv[2];
+    if constexpr (NB == 4) {
+        rows[0] = par ? 1 : 0;
+        rows[1] = par ? 2 : 3;
+        rv[0] = rv[1] = true;
+    } else {
+        rows[0] = par;
+        rv[0] = par < NB;
+        rows[1] = 0;
+        rv[1] = false;
+    }
+    f32x4 til[2][NB];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int tj = 0; tj < NB; ++tj) {
+            til[s][tj] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (rv[s] && tj <= rows[s]) {
+                const E *Bm = score_wave ? sQ : sK;
+#pragma unroll
+                for (int kb = 0; kb < KBD; ++kb)
+                    til[s][tj] = MD::mma(load_frag<MD>(sK, LDK, 16 * tj, kb * MD::KW, lane),
+                                         load_frag<MD>(Bm, LDK, 16 * rows[s], kb * MD::KW, lane), til[s][tj]);
+            }
+        }
+    }
+    __syncthreads();  // the K / Q region becomes A / T
+
+    // ---- 5. Per value head of the group
     for (int hh = 0; hh < group; ++hh) {
         const int h = kh * group + hh;
-        const size_t mat0 = ((size_t)ci * hv + h) * (size_t)(C * C);
+        const size_t ch = (size_t)ci * hv + h;
+        const size_t mat0 = ch * (size_t)(C * C);
+        const size_t w0 = ch * (size_t)(C * DK);
 
         // gate prefix sums c_t = g_1 + ... + g_t (C <= 64: one wave); rows past
         // the end of the sequence act as a = 1, b = 0
@@ -310,36 +354,52 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
                 const float y = __shfl_up(x, off);
                 if (lane >= off) x += y;
             }
+            const float last = __shfl(x, C - 1);
             if (lane < C) {
-                sc[lane] = x;
+                const float gam = exp2_hw(x * kLog2e);
+                sc[lane] = x * kLog2e;
                 sb[lane] = bv;
+                sbg[lane] = bv * gam;
+                sgam[ch * C + lane] = scale * gam;
+                delta[ch * C + lane] = exp2_hw((last - x) * kLog2e);
+                if (lane == C - 1) gammac[ch] = exp2_hw(last * kLog2e);
             }
         }
         __syncthreads();
-        if (tid < C) {
-            const float last = sc[C - 1];
-            const float gam = expf(sc[tid]);
-            gates[((size_t)ci * hv + h) * C + tid] =
-                f32x4{scale * gam, sb[tid], sb[tid] * gam, expf(last - sc[tid])};
-            if (tid == 0) gammac[(size_t)ci * hv + h] = expf(last);
-        }
 
-        // A = strict_lower(b_i exp(c_i - c_j) (K K^T)_ij) into LDS
-        for (int e = tid; e < C * C; e += 256) {
-            const int i = e / C, j = e - i * C;
-            sA[i * LDC + j] = j < i ? sb[i] * expf(sc[i] - sc[j]) * sGk[i * LDC + j] : 0.f;
-        }
-        // P = lower(scale exp(c_i - c_j) (Q K^T)_ij), straight to fragment order
-        for (int f = wave; f < NB * KBC; f += 4) {
-            const int rt = f / KBC, kb = f - rt * KBC;
-            const int i = 16 * rt + ln;
-            typename MC::Frag fr;
+        // A = strict_lower(b_i exp(c_i - c_j) (K K^T)_ij) into LDS (waves 0, 1);
+        // P = lower(scale exp(c_i - c_j) (Q K^T)_ij) to fragments (waves 2, 3)
 #pragma unroll
-            for (int e = 0; e < MC::KPL; ++e) {
-                const int j = kb * MC::KW + MC::KPL * g4 + e;
-                frag_set<MC>(fr, e, j <= i ? scale * expf(sc[i] - sc[j]) * sP0[i * LDC + j] : 0.f);
+        for (int s = 0; s < 2; ++s) {
+            if (!rv[s]) continue;
+            const int ti = rows[s];
+            const int i = 16 * ti + ln;
+            const float cI = sc[i];
+            const float mI = score_wave ? scale : sb[i];
+            f32x4 val[NB];
+#pragma unroll
+            for (int tj = 0; tj < NB; ++tj) {
+                val[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (tj <= ti) {
+                    const f32x4 cJ = *reinterpret_cast<const f32x4 *>(sc + 16 * tj + 4 * g4);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 16 * tj + 4 * g4 + r;
+                        const bool keep = score_wave ? j <= i : j < i;
+                        val[tj][r] = keep ? mI * exp2_hw(cI - cJ[r]) * til[s][tj][r] : 0.f;
+                    }
+                    if (!score_wave) *reinterpret_cast<f32x4 *>(sA + i * LDC + 16 * tj + 4 * g4) = val[tj];
+                }
             }
-            *reinterpret_cast<typename MC::Frag *>(pmat + mat0 + frag_off<MC>(f, lane)) = fr;
+            if (score_wave) {
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb) {
+                    typename MC::Frag fr;
+#pragma unroll
+                    for (int e = 0; e < MC::KPL; ++e) frag_set<MC>(fr, e, val[acc_tile<MC>(kb, e)][acc_slot<MC>(kb, e)]);
+                    *reinterpret_cast<typename MC::Frag *>(pmat + mat0 + frag_off<MC>(ti * KBC + kb, lane)) = fr;
+                }
+            }
         }
         __syncthreads();
 
@@ -383,18 +443,58 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
         }
         __syncthreads();
 
-        // T in fragment order (blocks above the diagonal are zero)
+        // Tb = T diag(b) in fragments (blocks above the diagonal are zero)
         for (int f = wave; f < NB * KBC; f += 4) {
             const int rt = f / KBC, kb = f - rt * KBC;
             const int i = 16 * rt + ln;
             typename MC::Frag fr;
 #pragma unroll
             for (int e = 0; e < MC::KPL; ++e) {
-                const int j = kb * MC::KW + MC::KPL * g4 + e;
-                frag_set<MC>(fr, e, (j >> 4) <= rt ? sT[i * LDC + j] : 0.f);
+                const int j = acc_k<MC>(kb, g4, e);
+                frag_set<MC>(fr, e, (j >> 4) <= rt ? sT[i * LDC + j] * sb[j] : 0.f);
             }
-            *reinterpret_cast<typename MC::Frag *>(tmat + mat0 + frag_off<MC>(f, lane)) = fr;
+            *reinterpret_cast<typename MC::Frag *>(tbmat + mat0 + frag_off<MC>(f, lane)) = fr;
         }
+
+        // -W = -T diag(b gamma) K: per key group and token tile, K^T (registers)
+        // times (T diag(b gamma))^T read from LDS; the accumulators (lane: token
+        // 16 ti + l%16, keys 16 mt + 4 (l/16) + r) are W's fragments with keys
+        // in accumulator order.
+#pragma unroll
+        for (int gi = 0; gi < NDGW; ++gi) {
+            const int dg = wave + 4 * gi;
+            if (dg >= NDG) continue;
+            for (int ti = 0; ti < NB; ++ti) {
+                const int i = 16 * ti + ln;
+                typename MC::Frag bfr[KBC];
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb) {
+#pragma unroll
+                    for (int e = 0; e < MC::KPL; ++e) {
+                        const int j = acc_k<MC>(kb, g4, e);
+                        frag_set<MC>(bfr[kb], e, (j >> 4) <= ti ? sT[i * LDC + j] * sbg[j] : 0.f);
+                    }
+                }
+                f32x4 w[DG];
+#pragma unroll
+                for (int t = 0; t < DG; ++t) {
+                    w[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < KBC; ++kb) w[t] = MC::mma(ktr[gi][t][kb], bfr[kb], w[t]);
+                }
+                if constexpr (MD::KPL == 1) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        wmat[w0 + frag_off<MD>(ti * KBD + 4 * dg + r, lane)] = -w[0][r];
+                } else {
+                    typename MD::Frag fr;
+#pragma unroll
+                    for (int e = 0; e < MD::KPL; ++e) frag_set<MD>(fr, e, -w[e >> 2][e & 3]);
+                    *reinterpret_cast<typename MD::Frag *>(wmat + w0 + frag_off<MD>(ti * KBD + dg, lane)) = fr;
+                }
+            }
+        }
+        __syncthreads();  // sc, sb, sbg, A and T are rewritten for the next value head
     }
 }
 
@@ -403,13 +503,19 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
 // ---------------------------------------------------------------------------
 //
 // Four waves per workgroup. Wave w owns the token tiles rt = w, w+4, .. of
-// the chunk (for X = K S0^T, Q S0^T, Y, U = T Y and the output) and the
-// key tiles mt = w, w+4, .. of the state slice (for its update). Every MFMA
-// A operand (K, Q, T, P, K^T) is one contiguous fragment load from the
-// workspace, issued two chunks ahead into one of three register stages
-// (bf16; fp32 fragments are four times larger and use one); LDS only carries the
-// small per-chunk exchanges between waves (the state's operand copy, Y, U,
-// diag(delta) U, the gates and the output tile).
+// the chunk (U and the output rows) and the key tiles mt = w, w+4, .. of the
+// state slice (its update). Per chunk, with S0 the slice at the chunk start:
+//   phase 1   U = Tb V - W S0^T and O1^T = S0 Q^T (B operands S0 and V from
+//             LDS); U and diag(delta) U go to LDS;
+//   barrier
+//   phase 2   O^T = O1^T diag(scale gamma) + U^T P^T, stored from registers;
+//             S^T = gamma_C S0^T + K^T diag(delta) U, its operand copy to LDS;
+//             the next chunk's V rows to LDS;
+//   barrier.
+// Every A operand (Tb, W, Q, P, K^T) and the gate vectors are single
+// contiguous loads from the workspace, issued two chunks ahead into one of
+// three register stages (bf16; fp32 fragments are four times larger and use
+// one stage).
 
 constexpr int kSliceRows = 16;
 
@@ -419,111 +525,95 @@ struct ScanSmem {
     static constexpr int R = kSliceRows;
     static constexpr int LDK = DK + PE;  // rows of length DK
     static constexpr int LDC = C + PE;   // rows of length C
-    static constexpr size_t off_S = 0;                                   // [R][LDK]
-    static constexpr size_t off_Yt = off_S + (size_t)R * LDK * sizeof(E);  // [R][LDC]
-    static constexpr size_t off_Ut = off_Yt + (size_t)R * LDC * sizeof(E);
-    static constexpr size_t off_DUt = off_Ut + (size_t)R * LDC * sizeof(E);
-    static constexpr size_t off_O = off_DUt + (size_t)R * LDC * sizeof(E);  // [C][R]
-    static constexpr size_t off_G = (off_O + (size_t)C * R * sizeof(E) + 15) & ~(size_t)15;  // [2][C] f32x4
-    static constexpr size_t bytes = off_G + 2 * (size_t)C * 16;
+    static constexpr size_t off_S = 0;                                     // [R][LDK] S (value row, key)
+    static constexpr size_t off_Ut = off_S + (size_t)R * LDK * sizeof(E);  // [R][LDC] U^T
+    static constexpr size_t off_DUt = off_Ut + (size_t)R * LDC * sizeof(E);  // [R][LDC] (diag(delta) U)^T
+    static constexpr size_t off_Vt = off_DUt + (size_t)R * LDC * sizeof(E);  // [2][R][LDC] V^T
+    static constexpr size_t bytes = off_Vt + 2 * (size_t)R * LDC * sizeof(E);
 };
+
+template <typename E> struct Vec4;
+template <> struct Vec4<bf16> { typedef bf16x4 type; };
+template <> struct Vec4<float> { typedef f32x4 type; };
 
 // One wave's operands for one chunk, in registers.
 template <typename E, int C, int DK>
 struct WaveStage {
     typedef Mma<E, DK> MD;  // contractions over keys
     typedef Mma<E, C> MC;   // contractions over the tokens of a chunk
+    typedef typename Vec4<E>::type E4;
     static constexpr int RT = C / 16, MT = DK / 16;
     static constexpr int NRW = (RT + 3) / 4, NMW = (MT + 3) / 4;  // tiles per wave
     static constexpr int KBD = DK / MD::KW, KBC = C / MC::KW;
 
-    f32x4 gate;  // gate vector of token row min(lane, C - 1)
-    typename MD::Frag kf[NRW][KBD], qf[NRW][KBD];
+    typename MD::Frag wf[NRW][KBD], qf[NRW][KBD];
     typename MC::Frag tf[NRW][KBC], pf[NRW][KBC], ktf[NMW][KBC];
-    E vv[NRW][4];
-    float gc;
+    E4 vr[NRW];    // V[16 rt + l/4][4 (l%4) ..]
+    f32x4 dl[NRW]; // delta of tokens 16 rt + 4 (l/16) + i
+    float sg[NRW]; // scale gamma of token 16 rt + l%16
+    float gc;      // gamma_C
 
     // All loads are unconditional (tiles and rows clamped into range) so that
     // the compiler counts outstanding loads exactly across the loop; rows past
-    // the end of the sequence are masked where they are used. The gate load
-    // comes first: it is the first one waited for.
-    __device__ __forceinline__ void load(const E *__restrict__ v, const E *__restrict__ tmat,
-                                         const E *__restrict__ pmat, const E *__restrict__ kmat,
+    // the end of the sequence are masked where they are used. Three parts, in
+    // the order a chunk consumes them (part 0: V and phase-1 operands; part 1:
+    // phase-2 output operands; part 2: the state update's), so that the scan
+    // can spread them over a chunk's phases.
+    template <int Part>
+    __device__ __forceinline__ void load(const E *__restrict__ v, const E *__restrict__ tbmat,
+                                         const E *__restrict__ pmat, const E *__restrict__ wmat,
                                          const E *__restrict__ qmat, const E *__restrict__ ktmat,
-                                         const f32x4 *__restrict__ gates, const float *__restrict__ gammac,
-                                         int tok0, int clen, int ci, int hk, int kh, int hv, int h, int col0,
-                                         int wave, int lane) {
-        const int g4 = lane >> 4, ln = lane & 15;
-        const size_t ci_h = (size_t)ci * hv + h;
-        const size_t mat0 = ci_h * (size_t)(C * C);
+                                         const float *__restrict__ sgam, const float *__restrict__ delta,
+                                         const float *__restrict__ gammac, int tok0, int clen, int ci, int hk,
+                                         int kh, int hv, int h, int col0, int wave, int lane) {
+        const size_t ch = (size_t)ci * hv + h;
+        const size_t mat0 = ch * (size_t)(C * C);
+        const size_t w0 = ch * (size_t)(C * DK);
         const size_t kq0 = ((size_t)ci * hk + kh) * (size_t)(C * DK);
-        gate = gates[ci_h * C + min(lane, C - 1)];
 #pragma unroll
         for (int r = 0; r < NRW; ++r) {
             const int rt = min(wave + 4 * r, RT - 1);
+            if constexpr (Part == 0) {
+                const int vrow = min(16 * rt + (lane >> 2), clen - 1);
+                vr[r] = *reinterpret_cast<const E4 *>(v + ((size_t)(tok0 + vrow) * hv + h) * DK + col0 + 4 * (lane & 3));
 #pragma unroll
-            for (int kb = 0; kb < KBD; ++kb) {
-                kf[r][kb] = *reinterpret_cast<const typename MD::Frag *>(kmat + kq0 + frag_off<MD>(rt * KBD + kb, lane));
-                qf[r][kb] = *reinterpret_cast<const typename MD::Frag *>(qmat + kq0 + frag_off<MD>(rt * KBD + kb, lane));
-            }
+                for (int kb = 0; kb < KBC; ++kb)
+                    tf[r][kb] = *reinterpret_cast<const typename MC::Frag *>(tbmat + mat0 + frag_off<MC>(rt * KBC + kb, lane));
 #pragma unroll
-            for (int kb = 0; kb < KBC; ++kb) {
-                tf[r][kb] = *reinterpret_cast<const typename MC::Frag *>(tmat + mat0 + frag_off<MC>(rt * KBC + kb, lane));
-                pf[r][kb] = *reinterpret_cast<const typename MC::Frag *>(pmat + mat0 + frag_off<MC>(rt * KBC + kb, lane));
-            }
+                for (int kb = 0; kb < KBD; ++kb)
+                    wf[r][kb] = *reinterpret_cast<const typename MD::Frag *>(wmat + w0 + frag_off<MD>(rt * KBD + kb, lane));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int vrow = min(16 * rt + 4 * g4 + i, clen - 1);
-                vv[r][i] = v[((size_t)(tok0 + vrow) * hv + h) * DK + col0 + ln];
+                for (int kb = 0; kb < KBD; ++kb)
+                    qf[r][kb] = *reinterpret_cast<const typename MD::Frag *>(qmat + kq0 + frag_off<MD>(rt * KBD + kb, lane));
+                dl[r] = *reinterpret_cast<const f32x4 *>(delta + ch * C + 16 * rt + 4 * (lane >> 4));
+            } else if constexpr (Part == 1) {
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb)
+                    pf[r][kb] = *reinterpret_cast<const typename MC::Frag *>(pmat + mat0 + frag_off<MC>(rt * KBC + kb, lane));
+                sg[r] = sgam[ch * C + 16 * rt + (lane & 15)];
             }
         }
+        if constexpr (Part == 2) {
 #pragma unroll
-        for (int j = 0; j < NMW; ++j) {
-            const int mt = min(wave + 4 * j, MT - 1);
+            for (int j = 0; j < NMW; ++j) {
+                const int mt = min(wave + 4 * j, MT - 1);
 #pragma unroll
-            for (int kb = 0; kb < KBC; ++kb)
-                ktf[j][kb] = *reinterpret_cast<const typename MC::Frag *>(ktmat + kq0 + frag_off<MC>(mt * KBC + kb, lane));
+                for (int kb = 0; kb < KBC; ++kb)
+                    ktf[j][kb] = *reinterpret_cast<const typename MC::Frag *>(ktmat + kq0 + frag_off<MC>(mt * KBC + kb, lane));
+            }
+            gc = gammac[ch];
         }
-        gc = gammac[ci_h];
-    }
-
-    // This wave's share (rows 16 w .. 16 w + 15) of the gate vectors into LDS.
-    __device__ __forceinline__ void put_gates(f32x4 *sG, int wave, int lane) const {
-        if (lane >= 16 * wave && lane < 16 * wave + 16 && lane < C) sG[lane] = gate;
     }
 };
-
-// Write the staged output tile of one chunk ([C][R] in LDS) with 16-byte
-// stores; rows at or beyond clen are skipped.
-template <typename E, int C, int R>
-__device__ __forceinline__ void flush_out(const E *sO, E *__restrict__ out, int tok0, int clen, int hv, int h,
-                                          int dv, int col0, int tid) {
-    constexpr int EPV = 16 / sizeof(E);
-    constexpr int VPRO = R / EPV;
-    constexpr int NO = C * VPRO;
-#pragma unroll
-    for (int it = 0; it < (NO + 255) / 256; ++it) {
-        const int id = tid + 256 * it;
-        if (NO % 256 == 0 || id < NO) {
-            const int r = id / VPRO, cv = id - r * VPRO;
-            if (r < clen)
-                st16(out + ((size_t)(tok0 + r) * hv + h) * dv + col0 + cv * EPV, ld16(sO + r * R + cv * EPV));
-        }
-    }
-}
-
-template <typename M> __device__ __forceinline__ typename M::Frag mask_frag(typename M::Frag f, bool keep) {
-    return keep ? f : zero_frag<M>();
-}
 
 template <typename E, int C, int DK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gdn_scan_kernel(
     const E *__restrict__ v,
     const int32_t *__restrict__ bounds, const int32_t *__restrict__ seq_chunk0,
     const int32_t *__restrict__ order,
-    const E *__restrict__ tmat, const E *__restrict__ pmat, const E *__restrict__ kmat,
+    const E *__restrict__ tbmat, const E *__restrict__ pmat, const E *__restrict__ wmat,
     const E *__restrict__ qmat, const E *__restrict__ ktmat,
-    const f32x4 *__restrict__ gates, const float *__restrict__ gammac,
+    const float *__restrict__ sgam, const float *__restrict__ delta, const float *__restrict__ gammac,
     const float *__restrict__ s0, float *__restrict__ sfin, E *__restrict__ out,
     int32_t num_seqs, int32_t hk, int32_t hv)
 {
@@ -531,6 +621,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     typedef WaveStage<E, C, DK> WS;
     typedef typename WS::MD MD;
     typedef typename WS::MC MC;
+    typedef typename WS::E4 E4;
     constexpr int R = kSliceRows;
     constexpr int DV = DK;
     constexpr int NS = DV / R;  // value-row slices per head
@@ -541,11 +632,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     extern __shared__ __align__(16) char smem[];
     E *sS = reinterpret_cast<E *>(smem + L::off_S);
-    E *sYt = reinterpret_cast<E *>(smem + L::off_Yt);
     E *sUt = reinterpret_cast<E *>(smem + L::off_Ut);
     E *sDUt = reinterpret_cast<E *>(smem + L::off_DUt);
-    E *sO = reinterpret_cast<E *>(smem + L::off_O);
-    f32x4 *sG = reinterpret_cast<f32x4 *>(smem + L::off_G);
+    E *sVt = reinterpret_cast<E *>(smem + L::off_Vt);
 
     // Workgroup -> (sequence rank, query/key head, value head in group, slice).
     // Dispatch places workgroup b on XCD b % 8; all value heads and slices
@@ -585,95 +674,98 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     }
 
-    WS st0, st1, st2;
-    auto issue = [&](WS &st, int c) {
-        st.load(v, tmat, pmat, kmat, qmat, ktmat, gates, gammac, start + c * C, min(C, len - c * C), c0 + c,
-                hk, kh, hv, h, col0, wave, lane);
+    auto issue_part = [&](WS &st, int c, auto part) {
+        st.template load<decltype(part)::value>(v, tbmat, pmat, wmat, qmat, ktmat, sgam, delta, gammac,
+                                                start + c * C, min(C, len - c * C), c0 + c, hk, kh, hv, h, col0,
+                                                wave, lane);
     };
-
-    // One chunk c with its operands in `st`. The gate vectors of chunk c are
-    // in sG[c & 1] when it starts.
-    //   kThree: `fut` (which held chunk c - 1) is refilled with chunk c + 2 at
-    //           the start, so each load has two chunk-times to land; `nxt`
-    //           holds chunk c + 1, whose gates are staged before the last
-    //           barrier.
-    //   otherwise (one stage): `st` is refilled with chunk c + 1 at the end.
-    auto body = [&](WS &st, WS &nxt, WS &fut, int c, auto three) {
-        constexpr bool kThree = decltype(three)::value;
-        if constexpr (kThree) issue(fut, min(c + 2, nch - 1));  // past the end: reload the last chunk (ignored)
-        const int tok0 = start + c * C;
-        const int clen = min(C, len - c * C);
-        // This wave's gate rows, read once before any LDS store of this chunk
-        // (later reads would be ordered behind those stores).
-        f32x4 gr[NRW][4];
+    auto issue = [&](WS &st, int c) {
+        issue_part(st, c, std::integral_constant<int, 0>());
+        issue_part(st, c, std::integral_constant<int, 1>());
+        issue_part(st, c, std::integral_constant<int, 2>());
+    };
+    // This wave's V rows of a chunk into sVt[buf] (transposed: [value][token]).
+    auto put_v = [&](const E4 (&vr)[NRW], int buf) {
 #pragma unroll
         for (int r = 0; r < NRW; ++r) {
-            const int rt = min(wave + 4 * r, RT - 1);
+            const int rt = wave + 4 * r;
+            if (rt < RT) {
+                E *dst = sVt + buf * (R * LDC) + 16 * rt + (lane >> 2);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) gr[r][i] = sG[(c & 1) * C + 16 * rt + 4 * g4 + i];
+                for (int i = 0; i < 4; ++i) dst[(4 * (lane & 3) + i) * LDC] = vr[r][i];
+            }
         }
+    };
 
-        // ---- X = K S0^T, O1 = Q S0^T, Y = diag(b) V - diag(b gamma) X
+    // One chunk c with its operands in `st`; sVt[c & 1] holds its V rows.
+    //   kThree: `fut` (which held chunk c - 1) is refilled with chunk c + 2,
+    //           one part per phase, so each load has about two chunk-times to
+    //           land; `nxt` holds chunk c + 1, whose V rows are staged in
+    //           phase 2.
+    //   otherwise (one stage): chunk c + 1's V rows are loaded at the start
+    //           and `st` is refilled with chunk c + 1 at the end.
+    auto body = [&](WS &st, WS &nxt, WS &fut, int c, auto three) {
+        constexpr bool kThree = decltype(three)::value;
+        const int cf = min(c + 2, nch - 1);  // past the end: reload the last chunk (ignored)
+        E4 vn[NRW];
+        if constexpr (kThree) {
+            issue_part(fut, cf, std::integral_constant<int, 0>());
+        } else {
+            const int cn = min(c + 1, nch - 1);
+            const int tokn = start + cn * C, clenn = min(C, len - cn * C);
+#pragma unroll
+            for (int r = 0; r < NRW; ++r) {
+                const int rt = min(wave + 4 * r, RT - 1);
+                const int vrow = min(16 * rt + (lane >> 2), clenn - 1);
+                vn[r] = *reinterpret_cast<const E4 *>(v + ((size_t)(tokn + vrow) * hv + h) * DK + col0 + 4 * (lane & 3));
+            }
+        }
+        const int tok0 = start + c * C;
+        const int clen = min(C, len - c * C);
+
+        // ---- phase 1: U = Tb V - W S0^T (W is stored negated), O1^T = S0 Q^T
+        typename MD::Frag sf[KBD];
+        typename MC::Frag vf[KBC];
+#pragma unroll
+        for (int kb = 0; kb < KBD; ++kb) sf[kb] = load_frag_acc<MD>(sS, LDK, 0, kb, lane);
+#pragma unroll
+        for (int kb = 0; kb < KBC; ++kb) vf[kb] = load_frag_acc<MC>(sVt + (c & 1) * (R * LDC), LDC, 0, kb, lane);
         f32x4 o1[NRW];
 #pragma unroll
         for (int r = 0; r < NRW; ++r) {
             const int rt = wave + 4 * r;
             o1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (rt < RT) {
-                f32x4 x = {0.f, 0.f, 0.f, 0.f};
+                // Two accumulators: the token and key contractions may use
+                // MFMAs of different shapes (d = 16), which must not be
+                // chained through one accumulator.
+                f32x4 ut = {0.f, 0.f, 0.f, 0.f}, uk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb) ut = MC::mma(st.tf[r][kb], vf[kb], ut);
 #pragma unroll
                 for (int kb = 0; kb < KBD; ++kb) {
-                    const typename MD::Frag bs = load_frag<MD>(sS, LDK, 0, kb * MD::KW, lane);
-                    x = MD::mma(st.kf[r][kb], bs, x);
-                    o1[r] = MD::mma(st.qf[r][kb], bs, o1[r]);
+                    uk = MD::mma(st.wf[r][kb], sf[kb], uk);
+                    o1[r] = MD::mma(sf[kb], st.qf[r][kb], o1[r]);
                 }
-                f32x4 y;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * rt + 4 * g4 + i;
-                    y[i] = gr[r][i][1] * (row < clen ? to_f32(st.vv[r][i]) : 0.f) - gr[r][i][2] * x[i];
-                }
-                store_acc_t<E>(sYt, LDC, 16 * rt, 0, lane, y);
-            }
-        }
-        __syncthreads();
-
-        // ---- U = T Y; diag(delta) U
-#pragma unroll
-        for (int r = 0; r < NRW; ++r) {
-            const int rt = wave + 4 * r;
-            if (rt < RT) {
-                f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < KBC; ++kb)
-                    u = MC::mma(st.tf[r][kb], load_frag<MC>(sYt, LDC, 0, kb * MC::KW, lane), u);
+                const f32x4 u = ut + uk;
                 store_acc_t<E>(sUt, LDC, 16 * rt, 0, lane, u);
                 f32x4 du;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) du[i] = gr[r][i][3] * u[i];
+                for (int i = 0; i < 4; ++i) du[i] = st.dl[r][i] * u[i];
                 store_acc_t<E>(sDUt, LDC, 16 * rt, 0, lane, du);
             }
         }
         __syncthreads();
+        if constexpr (kThree) issue_part(fut, cf, std::integral_constant<int, 1>());
 
-        // ---- O = diag(scale gamma) Q S0^T + P U, staged in LDS
+        // ---- phase 2
+        typename MC::Frag uf[KBC], duf[KBC];
 #pragma unroll
-        for (int r = 0; r < NRW; ++r) {
-            const int rt = wave + 4 * r;
-            if (rt < RT) {
-                f32x4 o2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < KBC; ++kb)
-                    o2 = MC::mma(st.pf[r][kb], load_frag<MC>(sUt, LDC, 0, kb * MC::KW, lane), o2);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * rt + 4 * g4 + i;
-                    sO[row * R + ln] = from_f32<E>(gr[r][i][0] * o1[r][i] + o2[i]);
-                }
-            }
+        for (int kb = 0; kb < KBC; ++kb) {
+            uf[kb] = load_frag_acc<MC>(sUt, LDC, 0, kb, lane);
+            duf[kb] = load_frag_acc<MC>(sDUt, LDC, 0, kb, lane);
         }
-
-        // ---- S^T <- gamma_C S^T + K^T (diag(delta) U)
+        // S^T <- gamma_C S^T + K^T (diag(delta) U)
 #pragma unroll
         for (int j = 0; j < NMW; ++j) {
             const int mt = wave + 4 * j;
@@ -682,25 +774,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[i] *= st.gc;
 #pragma unroll
-                for (int kb = 0; kb < KBC; ++kb)
-                    acc = MC::mma(st.ktf[j][kb], load_frag<MC>(sDUt, LDC, 0, kb * MC::KW, lane), acc);
+                for (int kb = 0; kb < KBC; ++kb) acc = MC::mma(st.ktf[j][kb], duf[kb], acc);
                 sacc[j] = acc;
                 store_acc_t<E>(sS, LDK, 16 * mt, 0, lane, acc);
             }
         }
-        if constexpr (kThree) nxt.put_gates(sG + ((c + 1) & 1) * C, wave, lane);
+        // O^T = O1^T diag(scale gamma) + U^T P^T; lane: token 16 rt + l%16,
+        // value columns 4 (l/16) .. + 3
+#pragma unroll
+        for (int r = 0; r < NRW; ++r) {
+            const int rt = wave + 4 * r;
+            if (rt < RT) {
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb) o = MC::mma(uf[kb], st.pf[r][kb], o);
+                const int row = 16 * rt + ln;
+                if (row < clen) {
+                    E4 w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(st.sg[r] * o1[r][i] + o[i]);
+                    *reinterpret_cast<E4 *>(out + ((size_t)(tok0 + row) * hv + h) * DV + col0 + 4 * g4) = w;
+                }
+            }
+        }
+        if constexpr (kThree) {
+            put_v(nxt.vr, (c + 1) & 1);
+            issue_part(fut, cf, std::integral_constant<int, 2>());
+        } else {
+            put_v(vn, (c + 1) & 1);
+        }
         __syncthreads();
-
         if constexpr (!kThree) issue(st, min(c + 1, nch - 1));
-        // this chunk's output tile; sO is only rewritten after two more barriers
-        flush_out<E, C, R>(sO, out, tok0, clen, hv, h, DV, col0, tid);
     };
 
+    WS st0, st1, st2;
     if (nch > 0) {
         issue(st0, 0);
         if constexpr (kThreeStages) {
             issue(st1, min(1, nch - 1));
-            st0.put_gates(sG, wave, lane);
+            put_v(st0.vr, 0);
             __syncthreads();
             int c = 0;
             for (; c + 2 < nch; c += 3) {
@@ -711,11 +823,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             if (c < nch) body(st0, st1, st2, c, std::true_type());
             if (c + 1 < nch) body(st1, st2, st0, c + 1, std::true_type());
         } else {
-            for (int c = 0; c < nch; ++c) {
-                st0.put_gates(sG + (c & 1) * C, wave, lane);
-                __syncthreads();
-                body(st0, st0, st0, c, std::false_type());
-            }
+            put_v(st0.vr, 0);
+            __syncthreads();
+            for (int c = 0; c < nch; ++c) body(st0, st0, st0, c, std::false_type());
         }
     }
 
@@ -728,6 +838,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     }
 }
+
 
 // ---------------------------------------------------------------------------
 // Launch
@@ -752,12 +863,13 @@ static hipError_t launch_prefill_t(const PrefillArgs &A, hipStream_t st) {
     int32_t *chunk_seq = reinterpret_cast<int32_t *>(ws + Y.off_chunk_seq);
     int32_t *chunk_tok0 = reinterpret_cast<int32_t *>(ws + Y.off_chunk_tok0);
     int32_t *counters = reinterpret_cast<int32_t *>(ws + Y.off_counters);
-    E *tmat = reinterpret_cast<E *>(ws + Y.off_tmat);
+    E *tbmat = reinterpret_cast<E *>(ws + Y.off_tbmat);
     E *pmat = reinterpret_cast<E *>(ws + Y.off_pmat);
-    E *kmat = reinterpret_cast<E *>(ws + Y.off_kmat);
+    E *wmat = reinterpret_cast<E *>(ws + Y.off_wmat);
     E *qmat = reinterpret_cast<E *>(ws + Y.off_qmat);
     E *ktmat = reinterpret_cast<E *>(ws + Y.off_ktmat);
-    f32x4 *gates = reinterpret_cast<f32x4 *>(ws + Y.off_gates);
+    float *sgam = reinterpret_cast<float *>(ws + Y.off_sgam);
+    float *delta = reinterpret_cast<float *>(ws + Y.off_delta);
     float *gammac = reinterpret_cast<float *>(ws + Y.off_gammac);
 
     timing_begin(kSchedule, st);
@@ -775,8 +887,8 @@ static hipError_t launch_prefill_t(const PrefillArgs &A, hipStream_t st) {
     timing_begin(kPrep, st);
     hipLaunchKernelGGL(prep, dim3((unsigned)Y.max_chunks, (unsigned)A.hk), dim3(256), PL::bytes, st,
                        (const E *)A.q, (const E *)A.k, (const G *)A.g, (const G *)A.beta,
-                       bounds, chunk_seq, chunk_tok0, counters, tmat, pmat, kmat, qmat, ktmat, gates, gammac,
-                       A.hk, A.hv, A.scale);
+                       bounds, chunk_seq, chunk_tok0, counters, tbmat, pmat, wmat, qmat, ktmat, sgam, delta,
+                       gammac, A.hk, A.hv, A.scale);
     timing_end(kPrep, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
@@ -789,8 +901,8 @@ static hipError_t launch_prefill_t(const PrefillArgs &A, hipStream_t st) {
     const int64_t grid = ((groups + 7) / 8) * per_kh * 8;
     timing_begin(kScan, st);
     hipLaunchKernelGGL(scan, dim3((unsigned)grid), dim3(256), SL::bytes, st,
-                       (const E *)A.v, bounds, seq_chunk0, order, tmat, pmat, kmat, qmat, ktmat, gates, gammac,
-                       A.s0, A.s_final, (E *)A.out, A.num_seqs, A.hk, A.hv);
+                       (const E *)A.v, bounds, seq_chunk0, order, tbmat, pmat, wmat, qmat, ktmat, sgam, delta,
+                       gammac, A.s0, A.s_final, (E *)A.out, A.num_seqs, A.hk, A.hv);
     timing_end(kScan, st);
     return hipGetLastError();
 }

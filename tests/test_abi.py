@@ -55,10 +55,11 @@ def _ws(n=1, T=4096, hk=16, hv=32, d=128, c=64, io=BF16):
 
 def test_workspace_size(lib):
     w = _ws()
-    # per chunk: T and P per value head (bf16 C x C), K, Q and K^T per
-    # query/key head (bf16 C x d), gates 16 B per token and value head
-    chunks = 4096 // 64 + 1
-    need = chunks * (32 * (2 * 64 * 64 * 2 + 64 * 16 + 4) + 16 * 3 * 64 * 128 * 2)
+    # per chunk: Tb and P (bf16 C x C) and W (bf16 C x d) per value head, Q
+    # and K^T per query/key head (bf16 C x d), scale*gamma and delta (fp32
+    # per token) and gamma_C (fp32) per value head
+    chunks = (4096 + 63) // 64 + 1
+    need = chunks * (32 * (2 * 64 * 64 * 2 + 64 * 128 * 2 + 2 * 64 * 4 + 4) + 16 * 2 * 64 * 128 * 2)
     assert need <= w < need + 64 * 1024
     assert _ws(io=F32) > w
     assert _ws(T=0) > 0
