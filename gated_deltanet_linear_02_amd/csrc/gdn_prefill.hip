@@ -502,22 +502,25 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
 // 3. Chunk-recurrent scan over one (sequence, value head, 16 value rows)
 // ---------------------------------------------------------------------------
 //
-// Four waves per workgroup. Wave w owns the token tiles rt = w, w+4, .. of
-// the chunk (U and the output rows) and the key tiles mt = w, w+4, .. of the
-// state slice (its update). Per chunk, with S0 the slice at the chunk start:
-//   phase 1   U = Tb V - W S0^T and O1^T = S0 Q^T (B operands S0 and V from
-//             LDS); U and diag(delta) U go to LDS;
-//   barrier
-//   phase 2   O^T = O1^T diag(scale gamma) + U^T P^T, stored from registers;
-//             S^T = gamma_C S0^T + K^T diag(delta) U, its operand copy to LDS;
-//             the next chunk's V rows to LDS;
-//   barrier.
-// Every A operand (Tb, W, Q, P, K^T) and the gate vectors are single
-// contiguous loads from the workspace, issued two chunks ahead into one of
-// three register stages (bf16; fp32 fragments are four times larger and use
-// one stage).
+// Eight waves per workgroup, two per SIMD, in two roles. With S0 the slice at
+// a chunk's start and q = wave % 4:
+//   recurrence waves (0-3)  phase 1: U = Tb V - W S0^T on token tile q, then
+//                           U and diag(delta) U to LDS;
+//                           phase 2: S^T = gamma_C S0^T + K^T diag(delta) U on
+//                           key tiles q, q+4, .., operand copy of S to LDS;
+//   output waves (4-7)      phase 1: O1^T = S0 Q^T on token tile q;
+//                           phase 2: O^T = O1^T diag(scale gamma) + U^T P^T,
+//                           stored from registers; the next chunk's V rows to
+//                           LDS.
+// One barrier ends each phase. Only the recurrence waves are on the chain
+// from one chunk's state to the next; the output waves' work fills the other
+// wave slot of each SIMD. Every A operand (Tb, W, K^T; Q, P) and the gate
+// vectors are single contiguous loads from the workspace, issued three
+// (recurrence) or four (output) chunks ahead into register stages used round
+// robin (bf16; fp32 fragments are four times larger and use one stage).
 
 constexpr int kSliceRows = 16;
+constexpr int kScanThreads = 512;
 
 template <typename E, int C, int DK>
 struct ScanSmem {
@@ -525,8 +528,8 @@ struct ScanSmem {
     static constexpr int R = kSliceRows;
     static constexpr int LDK = DK + PE;  // rows of length DK
     static constexpr int LDC = C + PE;   // rows of length C
-    static constexpr size_t off_S = 0;                                     // [R][LDK] S (value row, key)
-    static constexpr size_t off_Ut = off_S + (size_t)R * LDK * sizeof(E);  // [R][LDC] U^T
+    static constexpr size_t off_S = 0;                                       // [R][LDK] S (value row, key)
+    static constexpr size_t off_Ut = off_S + (size_t)R * LDK * sizeof(E);    // [R][LDC] U^T
     static constexpr size_t off_DUt = off_Ut + (size_t)R * LDC * sizeof(E);  // [R][LDC] (diag(delta) U)^T
     static constexpr size_t off_Vt = off_DUt + (size_t)R * LDC * sizeof(E);  // [2][R][LDC] V^T
     static constexpr size_t bytes = off_Vt + 2 * (size_t)R * LDC * sizeof(E);
@@ -536,78 +539,112 @@ template <typename E> struct Vec4;
 template <> struct Vec4<bf16> { typedef bf16x4 type; };
 template <> struct Vec4<float> { typedef f32x4 type; };
 
-// One wave's operands for one chunk, in registers.
+// Where one chunk's operands live in the workspace, for one workgroup.
+struct ChunkRef {
+    int tok0, clen;  // first token, tokens in the chunk
+    size_t ch;       // chunk * hv + value head
+    size_t kq;       // (chunk * hk + query/key head)
+};
+
 template <typename E, int C, int DK>
-struct WaveStage {
+struct ScanShape {
     typedef Mma<E, DK> MD;  // contractions over keys
     typedef Mma<E, C> MC;   // contractions over the tokens of a chunk
     typedef typename Vec4<E>::type E4;
     static constexpr int RT = C / 16, MT = DK / 16;
-    static constexpr int NRW = (RT + 3) / 4, NMW = (MT + 3) / 4;  // tiles per wave
+    static constexpr int NMW = (MT + 3) / 4;  // key tiles per recurrence wave
     static constexpr int KBD = DK / MD::KW, KBC = C / MC::KW;
+};
 
-    typename MD::Frag wf[NRW][KBD], qf[NRW][KBD];
-    typename MC::Frag tf[NRW][KBC], pf[NRW][KBC], ktf[NMW][KBC];
-    E4 vr[NRW];    // V[16 rt + l/4][4 (l%4) ..]
-    f32x4 dl[NRW]; // delta of tokens 16 rt + 4 (l/16) + i
-    float sg[NRW]; // scale gamma of token 16 rt + l%16
-    float gc;      // gamma_C
+// A recurrence wave's operands for one chunk. Loads are unconditional (tiles
+// and rows clamped into range) so that the compiler counts outstanding loads
+// exactly across the loop; rows past the end of a sequence are masked where
+// they are used.
+template <typename E, int C, int DK>
+struct RStage {
+    typedef ScanShape<E, C, DK> S;
+    typename S::MD::Frag wf[S::KBD];
+    typename S::MC::Frag tf[S::KBC], ktf[S::NMW][S::KBC];
+    f32x4 dl;   // delta of tokens 16 q + 4 (l/16) + i
+    float gc;   // gamma_C
 
-    // All loads are unconditional (tiles and rows clamped into range) so that
-    // the compiler counts outstanding loads exactly across the loop; rows past
-    // the end of the sequence are masked where they are used. Three parts, in
-    // the order a chunk consumes them (part 0: V and phase-1 operands; part 1:
-    // phase-2 output operands; part 2: the state update's), so that the scan
-    // can spread them over a chunk's phases.
-    template <int Part>
-    __device__ __forceinline__ void load(const E *__restrict__ v, const E *__restrict__ tbmat,
-                                         const E *__restrict__ pmat, const E *__restrict__ wmat,
-                                         const E *__restrict__ qmat, const E *__restrict__ ktmat,
-                                         const float *__restrict__ sgam, const float *__restrict__ delta,
-                                         const float *__restrict__ gammac, int tok0, int clen, int ci, int hk,
-                                         int kh, int hv, int h, int col0, int wave, int lane) {
-        const size_t ch = (size_t)ci * hv + h;
-        const size_t mat0 = ch * (size_t)(C * C);
-        const size_t w0 = ch * (size_t)(C * DK);
-        const size_t kq0 = ((size_t)ci * hk + kh) * (size_t)(C * DK);
+    __device__ __forceinline__ void load(const E *__restrict__ tbmat, const E *__restrict__ wmat,
+                                         const E *__restrict__ ktmat, const float *__restrict__ delta,
+                                         const float *__restrict__ gammac, const ChunkRef &r, int q, int lane) {
+        const int rt = min(q, S::RT - 1);
+        const size_t mat0 = r.ch * (size_t)(C * C), w0 = r.ch * (size_t)(C * DK), kq0 = r.kq * (size_t)(C * DK);
 #pragma unroll
-        for (int r = 0; r < NRW; ++r) {
-            const int rt = min(wave + 4 * r, RT - 1);
-            if constexpr (Part == 0) {
-                const int vrow = min(16 * rt + (lane >> 2), clen - 1);
-                vr[r] = *reinterpret_cast<const E4 *>(v + ((size_t)(tok0 + vrow) * hv + h) * DK + col0 + 4 * (lane & 3));
+        for (int kb = 0; kb < S::KBC; ++kb)
+            tf[kb] = *reinterpret_cast<const typename S::MC::Frag *>(tbmat + mat0 + frag_off<typename S::MC>(rt * S::KBC + kb, lane));
 #pragma unroll
-                for (int kb = 0; kb < KBC; ++kb)
-                    tf[r][kb] = *reinterpret_cast<const typename MC::Frag *>(tbmat + mat0 + frag_off<MC>(rt * KBC + kb, lane));
+        for (int kb = 0; kb < S::KBD; ++kb)
+            wf[kb] = *reinterpret_cast<const typename S::MD::Frag *>(wmat + w0 + frag_off<typename S::MD>(rt * S::KBD + kb, lane));
+        dl = *reinterpret_cast<const f32x4 *>(delta + r.ch * C + 16 * rt + 4 * (lane >> 4));
 #pragma unroll
-                for (int kb = 0; kb < KBD; ++kb)
-                    wf[r][kb] = *reinterpret_cast<const typename MD::Frag *>(wmat + w0 + frag_off<MD>(rt * KBD + kb, lane));
+        for (int j = 0; j < S::NMW; ++j) {
+            const int mt = min(q + 4 * j, S::MT - 1);
 #pragma unroll
-                for (int kb = 0; kb < KBD; ++kb)
-                    qf[r][kb] = *reinterpret_cast<const typename MD::Frag *>(qmat + kq0 + frag_off<MD>(rt * KBD + kb, lane));
-                dl[r] = *reinterpret_cast<const f32x4 *>(delta + ch * C + 16 * rt + 4 * (lane >> 4));
-            } else if constexpr (Part == 1) {
-#pragma unroll
-                for (int kb = 0; kb < KBC; ++kb)
-                    pf[r][kb] = *reinterpret_cast<const typename MC::Frag *>(pmat + mat0 + frag_off<MC>(rt * KBC + kb, lane));
-                sg[r] = sgam[ch * C + 16 * rt + (lane & 15)];
-            }
+            for (int kb = 0; kb < S::KBC; ++kb)
+                ktf[j][kb] = *reinterpret_cast<const typename S::MC::Frag *>(ktmat + kq0 + frag_off<typename S::MC>(mt * S::KBC + kb, lane));
         }
-        if constexpr (Part == 2) {
-#pragma unroll
-            for (int j = 0; j < NMW; ++j) {
-                const int mt = min(wave + 4 * j, MT - 1);
-#pragma unroll
-                for (int kb = 0; kb < KBC; ++kb)
-                    ktf[j][kb] = *reinterpret_cast<const typename MC::Frag *>(ktmat + kq0 + frag_off<MC>(mt * KBC + kb, lane));
-            }
-            gc = gammac[ch];
-        }
+        gc = gammac[r.ch];
     }
 };
 
+// An output wave's operands for one chunk (and that chunk's V rows, which
+// the wave stages one chunk earlier).
 template <typename E, int C, int DK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gdn_scan_kernel(
+struct OStage {
+    typedef ScanShape<E, C, DK> S;
+    typename S::MD::Frag qf[S::KBD];
+    typename S::MC::Frag pf[S::KBC];
+    typename S::E4 vr;  // V[16 q + l/4][4 (l%4) ..]
+    float sg;           // scale gamma of token 16 q + l%16
+
+    __device__ __forceinline__ void load(const E *__restrict__ v, const E *__restrict__ pmat,
+                                         const E *__restrict__ qmat, const float *__restrict__ sgam,
+                                         const ChunkRef &r, int hv, int h, int col0, int q, int lane) {
+        const int rt = min(q, S::RT - 1);
+        const size_t mat0 = r.ch * (size_t)(C * C), kq0 = r.kq * (size_t)(C * DK);
+        const int vrow = min(16 * rt + (lane >> 2), r.clen - 1);
+        vr = *reinterpret_cast<const typename S::E4 *>(v + ((size_t)(r.tok0 + vrow) * hv + h) * DK + col0 + 4 * (lane & 3));
+#pragma unroll
+        for (int kb = 0; kb < S::KBD; ++kb)
+            qf[kb] = *reinterpret_cast<const typename S::MD::Frag *>(qmat + kq0 + frag_off<typename S::MD>(rt * S::KBD + kb, lane));
+#pragma unroll
+        for (int kb = 0; kb < S::KBC; ++kb)
+            pf[kb] = *reinterpret_cast<const typename S::MC::Frag *>(pmat + mat0 + frag_off<typename S::MC>(rt * S::KBC + kb, lane));
+        sg = sgam[r.ch * C + 16 * rt + (lane & 15)];
+    }
+};
+
+// Runs body(st, nxt, fut, c, three) for chunks c = 0 .. nch-1 over N register
+// stages used round robin: chunk c sits in st[c % N], `nxt` holds chunk c + 1
+// and `fut` (which held chunk c - 1) is refilled with chunk c + N - 1. The
+// loop is unrolled by N so that every stage index is a compile-time
+// constant (the stages stay in registers). st[0 .. N-2] must hold chunks
+// 0 .. N-2 on entry.
+template <int N, int I = 0, typename St, typename Body>
+__device__ __forceinline__ void pipeline_step(St (&st)[N], int c, Body &body) {
+    body(st[I], st[(I + 1) % N], st[(I + N - 1) % N], c + I, std::true_type());
+    if constexpr (I + 1 < N) pipeline_step<N, I + 1>(st, c, body);
+}
+template <int N, int I = 0, typename St, typename Body>
+__device__ __forceinline__ void pipeline_tail(St (&st)[N], int c, int nch, Body &body) {
+    if constexpr (I + 1 < N) {
+        if (c + I < nch) body(st[I], st[(I + 1) % N], st[(I + N - 1) % N], c + I, std::true_type());
+        pipeline_tail<N, I + 1>(st, c, nch, body);
+    }
+}
+template <int N, typename St, typename Body>
+__device__ __forceinline__ void run_pipeline(St (&st)[N], int nch, Body &body) {
+    int c = 0;
+    for (; c + N - 1 < nch; c += N) pipeline_step<N>(st, c, body);
+    pipeline_tail<N>(st, c, nch, body);
+}
+
+template <typename E, int C, int DK>
+__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdn_scan_kernel(
     const E *__restrict__ v,
     const int32_t *__restrict__ bounds, const int32_t *__restrict__ seq_chunk0,
     const int32_t *__restrict__ order,
@@ -618,17 +655,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int32_t num_seqs, int32_t hk, int32_t hv)
 {
     typedef ScanSmem<E, C, DK> L;
-    typedef WaveStage<E, C, DK> WS;
-    typedef typename WS::MD MD;
-    typedef typename WS::MC MC;
-    typedef typename WS::E4 E4;
+    typedef ScanShape<E, C, DK> SH;
+    typedef typename SH::MD MD;
+    typedef typename SH::MC MC;
+    typedef typename SH::E4 E4;
+    typedef RStage<E, C, DK> RS;
+    typedef OStage<E, C, DK> OS;
     constexpr int R = kSliceRows;
     constexpr int DV = DK;
     constexpr int NS = DV / R;  // value-row slices per head
     constexpr int LDK = L::LDK, LDC = L::LDC;
-    constexpr int RT = WS::RT, MT = WS::MT, NRW = WS::NRW, NMW = WS::NMW;
-    constexpr int KBD = WS::KBD, KBC = WS::KBC;
-    constexpr bool kThreeStages = IsBf16<E>::value;  // fp32 fragments are 4x larger
+    constexpr int RT = SH::RT, MT = SH::MT, NMW = SH::NMW;
+    constexpr int KBD = SH::KBD, KBC = SH::KBC;
+    // Register stages per role (bf16); fp32 fragments are 4x larger and use one.
+    constexpr bool kPipelined = IsBf16<E>::value;
+    constexpr int kRStages = 4, kOStages = 5;
 
     extern __shared__ __align__(16) char smem[];
     E *sS = reinterpret_cast<E *>(smem + L::off_S);
@@ -653,6 +694,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int n = order[rank];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q = wave & 3;
+    const bool recurrence = wave < 4;
     const int g4 = lane >> 4, ln = lane & 15;
     const int start = bounds[n];
     const int len = bounds[n + 1] - start;
@@ -660,185 +703,175 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int c0 = seq_chunk0[n];
     const size_t state0 = ((size_t)n * hv + h) * (size_t)(DV * DK);
 
-    // fp32 master copy of this wave's S^T tiles (key tiles mt); operand copy
-    // (S[value][key]) in LDS.
-    f32x4 sacc[NMW];
-#pragma unroll
-    for (int j = 0; j < NMW; ++j) {
-        const int mt = wave + 4 * j;
-        sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (mt < MT) {
-            if (s0)
-                sacc[j] = *reinterpret_cast<const f32x4 *>(s0 + state0 + (size_t)(col0 + ln) * DK + 16 * mt + 4 * g4);
-            store_acc_t<E>(sS, LDK, 16 * mt, 0, lane, sacc[j]);
-        }
-    }
-
-    auto issue_part = [&](WS &st, int c, auto part) {
-        st.template load<decltype(part)::value>(v, tbmat, pmat, wmat, qmat, ktmat, sgam, delta, gammac,
-                                                start + c * C, min(C, len - c * C), c0 + c, hk, kh, hv, h, col0,
-                                                wave, lane);
-    };
-    auto issue = [&](WS &st, int c) {
-        issue_part(st, c, std::integral_constant<int, 0>());
-        issue_part(st, c, std::integral_constant<int, 1>());
-        issue_part(st, c, std::integral_constant<int, 2>());
-    };
-    // This wave's V rows of a chunk into sVt[buf] (transposed: [value][token]).
-    auto put_v = [&](const E4 (&vr)[NRW], int buf) {
-#pragma unroll
-        for (int r = 0; r < NRW; ++r) {
-            const int rt = wave + 4 * r;
-            if (rt < RT) {
-                E *dst = sVt + buf * (R * LDC) + 16 * rt + (lane >> 2);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dst[(4 * (lane & 3) + i) * LDC] = vr[r][i];
-            }
-        }
+    auto chunk = [&](int c) {
+        ChunkRef r;
+        r.tok0 = start + c * C;
+        r.clen = min(C, len - c * C);
+        r.ch = (size_t)(c0 + c) * hv + h;
+        r.kq = (size_t)(c0 + c) * hk + kh;
+        return r;
     };
 
-    // One chunk c with its operands in `st`; sVt[c & 1] holds its V rows.
-    //   kThree: `fut` (which held chunk c - 1) is refilled with chunk c + 2,
-    //           one part per phase, so each load has about two chunk-times to
-    //           land; `nxt` holds chunk c + 1, whose V rows are staged in
-    //           phase 2.
-    //   otherwise (one stage): chunk c + 1's V rows are loaded at the start
-    //           and `st` is refilled with chunk c + 1 at the end.
-    auto body = [&](WS &st, WS &nxt, WS &fut, int c, auto three) {
-        constexpr bool kThree = decltype(three)::value;
-        const int cf = min(c + 2, nch - 1);  // past the end: reload the last chunk (ignored)
-        E4 vn[NRW];
-        if constexpr (kThree) {
-            issue_part(fut, cf, std::integral_constant<int, 0>());
-        } else {
-            const int cn = min(c + 1, nch - 1);
-            const int tokn = start + cn * C, clenn = min(C, len - cn * C);
-#pragma unroll
-            for (int r = 0; r < NRW; ++r) {
-                const int rt = min(wave + 4 * r, RT - 1);
-                const int vrow = min(16 * rt + (lane >> 2), clenn - 1);
-                vn[r] = *reinterpret_cast<const E4 *>(v + ((size_t)(tokn + vrow) * hv + h) * DK + col0 + 4 * (lane & 3));
-            }
-        }
-        const int tok0 = start + c * C;
-        const int clen = min(C, len - c * C);
-
-        // ---- phase 1: U = Tb V - W S0^T (W is stored negated), O1^T = S0 Q^T
-        typename MD::Frag sf[KBD];
-        typename MC::Frag vf[KBC];
-#pragma unroll
-        for (int kb = 0; kb < KBD; ++kb) sf[kb] = load_frag_acc<MD>(sS, LDK, 0, kb, lane);
-#pragma unroll
-        for (int kb = 0; kb < KBC; ++kb) vf[kb] = load_frag_acc<MC>(sVt + (c & 1) * (R * LDC), LDC, 0, kb, lane);
-        f32x4 o1[NRW];
-#pragma unroll
-        for (int r = 0; r < NRW; ++r) {
-            const int rt = wave + 4 * r;
-            o1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (rt < RT) {
-                // Two accumulators: the token and key contractions may use
-                // MFMAs of different shapes (d = 16), which must not be
-                // chained through one accumulator.
-                f32x4 ut = {0.f, 0.f, 0.f, 0.f}, uk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < KBC; ++kb) ut = MC::mma(st.tf[r][kb], vf[kb], ut);
-#pragma unroll
-                for (int kb = 0; kb < KBD; ++kb) {
-                    uk = MD::mma(st.wf[r][kb], sf[kb], uk);
-                    o1[r] = MD::mma(sf[kb], st.qf[r][kb], o1[r]);
-                }
-                const f32x4 u = ut + uk;
-                store_acc_t<E>(sUt, LDC, 16 * rt, 0, lane, u);
-                f32x4 du;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) du[i] = st.dl[r][i] * u[i];
-                store_acc_t<E>(sDUt, LDC, 16 * rt, 0, lane, du);
-            }
-        }
-        __syncthreads();
-        if constexpr (kThree) issue_part(fut, cf, std::integral_constant<int, 1>());
-
-        // ---- phase 2
-        typename MC::Frag uf[KBC], duf[KBC];
-#pragma unroll
-        for (int kb = 0; kb < KBC; ++kb) {
-            uf[kb] = load_frag_acc<MC>(sUt, LDC, 0, kb, lane);
-            duf[kb] = load_frag_acc<MC>(sDUt, LDC, 0, kb, lane);
-        }
-        // S^T <- gamma_C S^T + K^T (diag(delta) U)
+    if (recurrence) {
+        // fp32 master copy of this wave's S^T tiles (key tiles q + 4 j);
+        // operand copy (S[value][key]) in LDS.
+        f32x4 sacc[NMW];
 #pragma unroll
         for (int j = 0; j < NMW; ++j) {
-            const int mt = wave + 4 * j;
+            const int mt = q + 4 * j;
+            sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (mt < MT) {
-                f32x4 acc = sacc[j];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] *= st.gc;
-#pragma unroll
-                for (int kb = 0; kb < KBC; ++kb) acc = MC::mma(st.ktf[j][kb], duf[kb], acc);
-                sacc[j] = acc;
-                store_acc_t<E>(sS, LDK, 16 * mt, 0, lane, acc);
+                if (s0)
+                    sacc[j] = *reinterpret_cast<const f32x4 *>(s0 + state0 + (size_t)(col0 + ln) * DK + 16 * mt + 4 * g4);
+                store_acc_t<E>(sS, LDK, 16 * mt, 0, lane, sacc[j]);
             }
         }
-        // O^T = O1^T diag(scale gamma) + U^T P^T; lane: token 16 rt + l%16,
-        // value columns 4 (l/16) .. + 3
+        __syncthreads();  // S0 and chunk 0's V rows staged
+
+        auto body = [&](RS &st, RS &, RS &fut, int c, auto three) {
+            constexpr bool kThree = decltype(three)::value;
+            if constexpr (kThree) fut.load(tbmat, wmat, ktmat, delta, gammac, chunk(min(c + kRStages - 1, nch - 1)), q, lane);
+            // ---- phase 1: U = Tb V - W S0^T (W is stored negated). Token and
+            // key contractions accumulate separately: with d = 16 they use
+            // MFMAs of different shapes, which must not be chained through
+            // one accumulator; two key chains shorten the dependency.
+            if (q < RT) {
+                typename MC::Frag vf[KBC];
+                typename MD::Frag sf[KBD];
 #pragma unroll
-        for (int r = 0; r < NRW; ++r) {
-            const int rt = wave + 4 * r;
-            if (rt < RT) {
+                for (int kb = 0; kb < KBC; ++kb) vf[kb] = load_frag_acc<MC>(sVt + (c & 1) * (R * LDC), LDC, 0, kb, lane);
+#pragma unroll
+                for (int kb = 0; kb < KBD; ++kb) sf[kb] = load_frag_acc<MD>(sS, LDK, 0, kb, lane);
+                f32x4 ut = {0.f, 0.f, 0.f, 0.f}, uk0 = {0.f, 0.f, 0.f, 0.f}, uk1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb) ut = MC::mma(st.tf[kb], vf[kb], ut);
+#pragma unroll
+                for (int kb = 0; kb < KBD; ++kb) {
+                    if (kb & 1) uk1 = MD::mma(st.wf[kb], sf[kb], uk1);
+                    else uk0 = MD::mma(st.wf[kb], sf[kb], uk0);
+                }
+                const f32x4 u = ut + uk0 + uk1;
+                store_acc_t<E>(sUt, LDC, 16 * q, 0, lane, u);
+                f32x4 du;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) du[i] = st.dl[i] * u[i];
+                store_acc_t<E>(sDUt, LDC, 16 * q, 0, lane, du);
+            }
+            __syncthreads();
+            // ---- phase 2: S^T <- gamma_C S^T + K^T (diag(delta) U)
+            typename MC::Frag duf[KBC];
+#pragma unroll
+            for (int kb = 0; kb < KBC; ++kb) duf[kb] = load_frag_acc<MC>(sDUt, LDC, 0, kb, lane);
+#pragma unroll
+            for (int j = 0; j < NMW; ++j) {
+                const int mt = q + 4 * j;
+                if (mt < MT) {
+                    f32x4 acc = sacc[j];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i] *= st.gc;
+#pragma unroll
+                    for (int kb = 0; kb < KBC; ++kb) acc = MC::mma(st.ktf[j][kb], duf[kb], acc);
+                    sacc[j] = acc;
+                    store_acc_t<E>(sS, LDK, 16 * mt, 0, lane, acc);
+                }
+            }
+            __syncthreads();
+            if constexpr (!kThree) st.load(tbmat, wmat, ktmat, delta, gammac, chunk(min(c + 1, nch - 1)), q, lane);
+        };
+
+        if (nch > 0) {
+            if constexpr (kPipelined) {
+                RS st[kRStages];
+#pragma unroll
+                for (int i = 0; i + 1 < kRStages; ++i)
+                    st[i].load(tbmat, wmat, ktmat, delta, gammac, chunk(min(i, nch - 1)), q, lane);
+                run_pipeline<kRStages>(st, nch, body);
+            } else {
+                RS st0;
+                st0.load(tbmat, wmat, ktmat, delta, gammac, chunk(0), q, lane);
+                for (int c = 0; c < nch; ++c) body(st0, st0, st0, c, std::false_type());
+            }
+        }
+
+        if (sfin) {
+#pragma unroll
+            for (int j = 0; j < NMW; ++j) {
+                const int mt = q + 4 * j;
+                if (mt < MT)
+                    *reinterpret_cast<f32x4 *>(sfin + state0 + (size_t)(col0 + ln) * DK + 16 * mt + 4 * g4) = sacc[j];
+            }
+        }
+    } else {
+        // This wave's V rows of a chunk into sVt[buf] (transposed: [value][token]).
+        auto put_v = [&](const E4 &vr, int buf) {
+            if (q < RT) {
+                E *dst = sVt + buf * (R * LDC) + 16 * q + (lane >> 2);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[(4 * (lane & 3) + i) * LDC] = vr[i];
+            }
+        };
+        OS st[kPipelined ? kOStages : 1];
+        if (nch > 0) {
+            st[0].load(v, pmat, qmat, sgam, chunk(0), hv, h, col0, q, lane);
+            put_v(st[0].vr, 0);
+        }
+        __syncthreads();  // S0 and chunk 0's V rows staged
+
+        // One chunk c with its operands in `st`; `nxt` holds chunk c + 1
+        // (pipelined: its V rows are staged here; `fut` is refilled with
+        // chunk c + kOStages - 1). One stage: chunk c + 1's V rows are loaded
+        // at the start and `st` is refilled with chunk c + 1 at the end.
+        auto body = [&](OS &st, OS &nxt, OS &fut, int c, auto three) {
+            constexpr bool kThree = decltype(three)::value;
+            E4 vn;
+            if constexpr (kThree) {
+                fut.load(v, pmat, qmat, sgam, chunk(min(c + kOStages - 1, nch - 1)), hv, h, col0, q, lane);
+            } else {
+                const ChunkRef rn = chunk(min(c + 1, nch - 1));
+                const int vrow = min(16 * min(q, RT - 1) + (lane >> 2), rn.clen - 1);
+                vn = *reinterpret_cast<const E4 *>(v + ((size_t)(rn.tok0 + vrow) * hv + h) * DK + col0 + 4 * (lane & 3));
+            }
+            // ---- phase 1: O1^T = S0 Q^T
+            f32x4 o1 = {0.f, 0.f, 0.f, 0.f};
+            if (q < RT) {
+#pragma unroll
+                for (int kb = 0; kb < KBD; ++kb) o1 = MD::mma(load_frag_acc<MD>(sS, LDK, 0, kb, lane), st.qf[kb], o1);
+            }
+            __syncthreads();
+            // ---- phase 2: O^T = O1^T diag(scale gamma) + U^T P^T; lane: token
+            // 16 q + l%16, value columns 4 (l/16) .. + 3
+            const int tok0 = start + c * C;
+            const int clen = min(C, len - c * C);
+            if (q < RT) {
                 f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < KBC; ++kb) o = MC::mma(uf[kb], st.pf[r][kb], o);
-                const int row = 16 * rt + ln;
+                for (int kb = 0; kb < KBC; ++kb) o = MC::mma(load_frag_acc<MC>(sUt, LDC, 0, kb, lane), st.pf[kb], o);
+                const int row = 16 * q + ln;
                 if (row < clen) {
                     E4 w;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(st.sg[r] * o1[r][i] + o[i]);
+                    for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(st.sg * o1[i] + o[i]);
                     *reinterpret_cast<E4 *>(out + ((size_t)(tok0 + row) * hv + h) * DV + col0 + 4 * g4) = w;
                 }
             }
-        }
-        if constexpr (kThree) {
-            put_v(nxt.vr, (c + 1) & 1);
-            issue_part(fut, cf, std::integral_constant<int, 2>());
-        } else {
-            put_v(vn, (c + 1) & 1);
-        }
-        __syncthreads();
-        if constexpr (!kThree) issue(st, min(c + 1, nch - 1));
-    };
-
-    WS st0, st1, st2;
-    if (nch > 0) {
-        issue(st0, 0);
-        if constexpr (kThreeStages) {
-            issue(st1, min(1, nch - 1));
-            put_v(st0.vr, 0);
+            if constexpr (kThree) put_v(nxt.vr, (c + 1) & 1);
+            else put_v(vn, (c + 1) & 1);
             __syncthreads();
-            int c = 0;
-            for (; c + 2 < nch; c += 3) {
-                body(st0, st1, st2, c, std::true_type());
-                body(st1, st2, st0, c + 1, std::true_type());
-                body(st2, st0, st1, c + 2, std::true_type());
-            }
-            if (c < nch) body(st0, st1, st2, c, std::true_type());
-            if (c + 1 < nch) body(st1, st2, st0, c + 1, std::true_type());
-        } else {
-            put_v(st0.vr, 0);
-            __syncthreads();
-            for (int c = 0; c < nch; ++c) body(st0, st0, st0, c, std::false_type());
-        }
-    }
+            if constexpr (!kThree) st.load(v, pmat, qmat, sgam, chunk(min(c + 1, nch - 1)), hv, h, col0, q, lane);
+        };
 
-    if (sfin) {
+        if (nch > 0) {
+            if constexpr (kPipelined) {
 #pragma unroll
-        for (int j = 0; j < NMW; ++j) {
-            const int mt = wave + 4 * j;
-            if (mt < MT)
-                *reinterpret_cast<f32x4 *>(sfin + state0 + (size_t)(col0 + ln) * DK + 16 * mt + 4 * g4) = sacc[j];
+                for (int i = 1; i + 1 < kOStages; ++i)
+                    st[i].load(v, pmat, qmat, sgam, chunk(min(i, nch - 1)), hv, h, col0, q, lane);
+                run_pipeline<kOStages>(st, nch, body);
+            } else {
+                for (int c = 0; c < nch; ++c) body(st[0], st[0], st[0], c, std::false_type());
+            }
         }
     }
 }
-
 
 // ---------------------------------------------------------------------------
 // Launch
@@ -900,7 +933,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &A, hipStream_t st) {
     const int64_t groups = (int64_t)A.num_seqs * A.hk;
     const int64_t grid = ((groups + 7) / 8) * per_kh * 8;
     timing_begin(kScan, st);
-    hipLaunchKernelGGL(scan, dim3((unsigned)grid), dim3(256), SL::bytes, st,
+    hipLaunchKernelGGL(scan, dim3((unsigned)grid), dim3(kScanThreads), SL::bytes, st,
                        (const E *)A.v, bounds, seq_chunk0, order, tbmat, pmat, wmat, qmat, ktmat, sgam, delta,
                        gammac, A.s0, A.s_final, (E *)A.out, A.num_seqs, A.hk, A.hv);
     timing_end(kScan, st);
