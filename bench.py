@@ -150,6 +150,51 @@ def summarize_profiles(stats_dir: str, fetch_dir: str, write_dir: str, probe_mib
     with open(os.path.join(stats_dir, "run_kernel_stats.csv")) as f:
         for r in csv.DictReader(f):
             rows.append(r)
+    lines = [
+        "# Kernel time and HBM traffic: prefill 1x4096 + decode batch 64 (HK=16, HV=32, d=128, C=64, bf16)",
+        "",
+        "Made by (from the repository root; OUT is any scratch directory):",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp",
+        "rocprofv3 --kernel-trace --stats -d OUT/stats -o run --output-format csv -- "
+        "python3 REPO/bench.py --no-cpu-baseline",
+        "rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run --output-format csv -- "
+        f"python3 REPO/bench.py --no-cpu-baseline --steps 5 --warmup 2 --copy-probe-mib {probe_mib}",
+        "rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run --output-format csv -- "
+        f"python3 REPO/bench.py --no-cpu-baseline --steps 5 --warmup 2 --copy-probe-mib {probe_mib}",
+        f"cd REPO && python3 bench.py --summarize OUT/stats OUT/fetch OUT/write {probe_mib}",
+        "```",
+        "",
+        f"Kernel sources hash: `{h}` (bench.py reports traffic only while the sources match).",
+        "",
+        "## Kernel durations (rocprofv3 --kernel-trace --stats)",
+        "",
+        "| kernel | calls | mean us | min us | max us |",
+        "|---|---|---|---|---|",
+    ]
+    for r in rows:
+        short = _short_kernel(r["Name"])
+        if short in KERNELS:
+            lines.append(f"| {KERNELS[short]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += [
+        "",
+        "## HBM bytes per launch (FETCH_SIZE, WRITE_SIZE; scaled by a plain copy)",
+        "",
+        f"A {probe_mib} MiB device-to-device copy in the same runs reads {fkib:.0f} FETCH_SIZE units and "
+        f"{wkib:.0f} WRITE_SIZE units: {ffac:.1f} and {wfac:.1f} bytes per unit.",
+        "",
+        "| kernel | fetched MB | written MB | total MB |",
+        "|---|---|---|---|",
+    ]
+    for short in ("schedule", "prep", "scan", "decode"):
+        ent = traffic.get(KERNELS[short])
+        if ent:
+            lines.append(f"| {KERNELS[short]} | {ent['fetch_bytes'] / 1e6:.1f} | {ent['write_bytes'] / 1e6:.1f} | "
+                         f"{ent['bytes_per_launch'] / 1e6:.1f} |")
+    with open(os.path.join(ROOT, "profiles", "gdn_kernels_prefill4096_decode64.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
     return traffic, rows
 
 
