@@ -181,8 +181,33 @@ struct PrepSmem {
     static constexpr size_t off_c = ((kq_end > at_end ? kq_end : at_end) + 15) & ~(size_t)15;
     static constexpr size_t off_b = off_c + (size_t)C * sizeof(float);
     static constexpr size_t off_bg = off_b + (size_t)C * sizeof(float);
-    static constexpr size_t bytes = off_bg + (size_t)C * sizeof(float);
+    // Chunk location when the kernel schedules itself: sequence ends and
+    // lengths (256 each), 4 wave partials and 4 results.
+    static constexpr size_t off_loc = off_bg + (size_t)C * sizeof(float);
+    static constexpr size_t bytes = off_loc + (2 * 256 + 8) * sizeof(int);
 };
+
+// Up to this many sequences the chunk-preparation kernel locates its own
+// chunk from cu_seqlens (and publishes the scan's tables), so no separate
+// schedule launch is needed.
+constexpr int kFoldMaxSeqs = 256;
+
+// Inclusive scan (sum, or max) over a 256-thread workgroup: shuffle scans
+// within each wave, then the wave totals through LDS (s_part[4]).
+__device__ __forceinline__ int wg256_scan_incl(int x, bool use_max, int *s_part) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x = use_max ? max(x, y) : x + y;
+    }
+    if (lane == 63) s_part[wave] = x;
+    __syncthreads();
+    int carry = use_max ? INT32_MIN : 0;
+    for (int w = 0; w < wave; ++w) carry = use_max ? max(carry, s_part[w]) : carry + s_part[w];
+    __syncthreads();  // s_part is reused by the next scan
+    return use_max ? max(x, carry) : x + carry;
+}
 
 template <typename M> __device__ __forceinline__ typename M::Frag zero_frag() {
     typename M::Frag z;
@@ -224,8 +249,10 @@ template <typename E, typename G, int C, int DK>
 __global__ __launch_bounds__(256) void gdn_prep_kernel(
     const E *__restrict__ q, const E *__restrict__ k,
     const G *__restrict__ gate_g, const G *__restrict__ gate_b,
-    const int32_t *__restrict__ bounds, const int32_t *__restrict__ chunk_seq,
-    const int32_t *__restrict__ chunk_tok0, const int32_t *__restrict__ counters,
+    const int32_t *__restrict__ cu, int32_t num_seqs, int32_t total_tokens,
+    int32_t *__restrict__ bounds, int32_t *__restrict__ seq_chunk0, int32_t *__restrict__ order,
+    const int32_t *__restrict__ chunk_seq, const int32_t *__restrict__ chunk_tok0,
+    const int32_t *__restrict__ counters,
     E *__restrict__ tbmat, E *__restrict__ pmat, E *__restrict__ wmat, E *__restrict__ qmat,
     E *__restrict__ ktmat, float *__restrict__ sgam, float *__restrict__ delta, float *__restrict__ gammac,
     int32_t hk, int32_t hv, float scale)
@@ -252,13 +279,61 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
     float *sbg = reinterpret_cast<float *>(smem + L::off_bg);  // b_t gamma_t
 
     const int ci = blockIdx.x, kh = blockIdx.y;
-    if (ci >= counters[0]) return;
     const int group = hv / hk;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g4 = lane >> 4, ln = lane & 15;
-    const int n = chunk_seq[ci];
-    const int t0 = chunk_tok0[ci];
-    const int len = min(C, bounds[n + 1] - t0);
+    int t0, len;
+    if (cu != nullptr) {
+        // ---- 0. Locate this chunk (num_seqs <= 256): thread j owns sequence j.
+        //         Bounds are cu clamped into [0, T] and made non-decreasing, so a
+        //         malformed cu_seqlens cannot send any access out of range.
+        int *s_end = reinterpret_cast<int *>(smem + L::off_loc);
+        int *s_len = s_end + 256;
+        int *s_part = s_len + 256;
+        int *s_res = s_part + 4;
+        const int j = tid;
+        const int b0 = min(max(cu[0], 0), total_tokens);
+        const int e = j < num_seqs ? max(min(max(cu[j + 1], 0), total_tokens), b0) : b0;
+        const int hi = wg256_scan_incl(e, true, s_part);  // end of sequence j
+        s_end[j] = hi;
+        __syncthreads();
+        const int lo = j == 0 ? b0 : s_end[j - 1];
+        const int lenj = j < num_seqs ? hi - lo : 0;
+        const int nchj = (lenj + C - 1) / C;
+        const int first = wg256_scan_incl(nchj, false, s_part) - nchj;
+        if (j < num_seqs && ci >= first && ci < first + nchj) {
+            s_res[0] = lo + (ci - first) * C;
+            s_res[1] = hi;
+        }
+        if (j == 255) s_res[2] = first + nchj;  // chunks in total
+        if (ci == 0 && kh == 0) {
+            // the scan's tables: bounds, first chunk per sequence, longest first
+            s_len[j] = lenj;
+            if (j == 0) bounds[0] = b0;
+            if (j < num_seqs) {
+                bounds[j + 1] = hi;
+                seq_chunk0[j] = first;
+            }
+            if (j == 255) seq_chunk0[num_seqs] = first + nchj;
+        }
+        __syncthreads();
+        if (ci == 0 && kh == 0 && j < num_seqs) {
+            int rank = 0;
+            for (int m = 0; m < num_seqs; ++m) {
+                const int lm = s_len[m];
+                rank += (lm > lenj) || (lm == lenj && m < j);
+            }
+            order[rank] = j;
+        }
+        if (ci >= s_res[2]) return;
+        t0 = s_res[0];
+        len = min(C, s_res[1] - t0);
+    } else {
+        if (ci >= counters[0]) return;
+        const int n = chunk_seq[ci];
+        t0 = chunk_tok0[ci];
+        len = min(C, bounds[n + 1] - t0);
+    }
     const size_t kq0 = ((size_t)ci * hk + kh) * (size_t)(C * DK);
     const size_t ld = (size_t)hk * DK;
 
@@ -905,13 +980,17 @@ static hipError_t launch_prefill_t(const PrefillArgs &A, hipStream_t st) {
     float *delta = reinterpret_cast<float *>(ws + Y.off_delta);
     float *gammac = reinterpret_cast<float *>(ws + Y.off_gammac);
 
-    timing_begin(kSchedule, st);
-    hipLaunchKernelGGL(gdn_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, st,
-                       A.cu, A.num_seqs, (int32_t)A.total_tokens, A.chunk,
-                       bounds, seq_chunk0, order, chunk_seq, chunk_tok0, counters);
-    timing_end(kSchedule, st);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // Up to kFoldMaxSeqs sequences the preparation kernel schedules itself.
+    const bool fold = A.num_seqs <= kFoldMaxSeqs;
+    hipError_t e = hipSuccess;
+    if (!fold) {
+        timing_begin(kSchedule, st);
+        hipLaunchKernelGGL(gdn_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, st,
+                           A.cu, A.num_seqs, (int32_t)A.total_tokens, A.chunk,
+                           bounds, seq_chunk0, order, chunk_seq, chunk_tok0, counters);
+        timing_end(kSchedule, st);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
 
     typedef PrepSmem<E, C, D> PL;
     static std::atomic<bool> prep_ok{false};
@@ -920,7 +999,8 @@ static hipError_t launch_prefill_t(const PrefillArgs &A, hipStream_t st) {
     timing_begin(kPrep, st);
     hipLaunchKernelGGL(prep, dim3((unsigned)Y.max_chunks, (unsigned)A.hk), dim3(256), PL::bytes, st,
                        (const E *)A.q, (const E *)A.k, (const G *)A.g, (const G *)A.beta,
-                       bounds, chunk_seq, chunk_tok0, counters, tbmat, pmat, wmat, qmat, ktmat, sgam, delta,
+                       fold ? A.cu : nullptr, A.num_seqs, (int32_t)A.total_tokens, bounds, seq_chunk0, order,
+                       chunk_seq, chunk_tok0, counters, tbmat, pmat, wmat, qmat, ktmat, sgam, delta,
                        gammac, A.hk, A.hv, A.scale);
     timing_end(kPrep, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -236,6 +236,24 @@ def test_deterministic_and_in_place_state():
     assert torch.equal(f3, f4) and torch.equal(o3.view(torch.int16), o4.view(torch.int16))
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("n_seqs", [256, 300])
+def test_many_short_sequences(n_seqs, io):
+    """Many ragged sequences, some empty, with initial states. Up to 256 the
+    preparation kernel locates its chunks itself; past that a separate
+    schedule kernel builds the chunk table. Both must agree with the oracle."""
+    lens = gs.varlen_lengths(n_seqs, 0, 40, seed=gs.SEED_BASE + 77)
+    inp = gs.make_inputs(lens, 2, 4, 32, 32, seed=gs.SEED_BASE + 78, io_dtype=io, gate_dtype="f32",
+                         init_state=True)
+    note(f"prefill many sequences N={n_seqs} io={io}")
+    o, f = run_prefill(inp, chunk=16)
+    _check(inp, o, f, label=f"N={n_seqs}")
+    empty = [i for i, n in enumerate(lens) if n == 0]
+    assert empty, "the draw should include empty sequences"
+    for i in empty:
+        assert np.array_equal(to_f64(f)[i], inp.initial_state[i].astype(np.float64))
+
+
 def test_malformed_cu_seqlens_is_clamped():
     """Offsets past the end or decreasing are clamped on the device: no fault,
     and well-formed sequences before them are still right."""
