@@ -15,11 +15,15 @@
 //     o  = scale (a sq + kq u)          ( = scale S_new q )
 //     S_new = a S + u k^T               ( = a S (I - b k k^T) + b v k^T )
 //
-// Mapping: one 256-thread workgroup per (b, h). A state row (dk fp32) is
-// split over LPR = dk/16 consecutive lanes; each lane holds 16 elements of the
-// row as four 16-byte pieces at columns 4*lr + 4*LPR*m (m = 0..3), so that
-// for each of the four loads the LPR lanes of a row read 16*LPR contiguous
-// bytes. Row dot products finish with log2(LPR) butterfly shuffles.
+// Mapping: the rows of one (b, h) state are independent, so they are split
+// over several 256-thread workgroups of ROWS rows each: small workgroups keep
+// more of them in flight, which is what an in-place read-then-write stream
+// needs to approach the HBM rate. A state row (dk fp32) is split over
+// LPR = dk/8 consecutive lanes; lane lr holds 8 elements of the row as two
+// 16-byte pieces at columns 4*lr + 4*LPR*m (m = 0, 1), so that for each load
+// the LPR lanes of a row read 16*LPR contiguous bytes. Row dot products finish
+// with log2(LPR) butterfly shuffles. Each workgroup recomputes k.q (dk
+// products), which is negligible.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -36,6 +40,13 @@ template <> __device__ __forceinline__ void load4<bf16>(const bf16 *p, float *ds
     dst[2] = static_cast<float>(x[2]); dst[3] = static_cast<float>(x[3]);
 }
 
+template <int DK, int DV> struct DecodeShape {
+    static constexpr int EPL = 8;                  // state elements per lane
+    static constexpr int LPR = DK / EPL;           // lanes per state row
+    static constexpr int ROWS = 256 / LPR;         // rows per workgroup
+    static constexpr int SLICES = (DV + ROWS - 1) / ROWS;  // workgroups per (b, h)
+};
+
 template <typename E, typename G, int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_decode_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
@@ -43,95 +54,79 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(
     float *__restrict__ state, const int32_t *__restrict__ slots, int32_t num_slots,
     E *__restrict__ out, int32_t hk, int32_t hv, float scale)
 {
-    constexpr int LPR = DK / 16;              // lanes per state row
-    constexpr int ROWS = 256 / LPR;           // rows per pass of the workgroup
-    constexpr int PASSES = (DV + ROWS - 1) / ROWS;
+    typedef DecodeShape<DK, DV> SH;
+    constexpr int LPR = SH::LPR, ROWS = SH::ROWS, SLICES = SH::SLICES;
 
-    const int bh = blockIdx.x;
+    const int bhs = blockIdx.x;
+    const int bh = bhs / SLICES;
+    const int row0 = (bhs - bh * SLICES) * ROWS;
     const int b = bh / hv;
     const int h = bh - b * hv;
     const int kh = h / (hv / hk);
     const int tid = threadIdx.x;
     const int lr = tid % LPR;
-    const int rp = tid / LPR;
+    const int row = row0 + tid / LPR;
+    const bool live = row < DV;
 
     const int slot = slots ? slots[b] : b;
     E *o_row = out + ((size_t)b * hv + h) * DV;
     if (slot < 0 || slot >= num_slots) {
-        for (int i = tid; i < DV; i += 256) o_row[i] = from_f32<E>(0.0f);
+        if (live && lr == 0) o_row[row] = from_f32<E>(0.0f);
         return;
     }
     float *S = state + ((size_t)slot * hv + h) * (size_t)(DV * DK);
 
-    // State rows first: the bulk of the bytes, all loads in flight at once.
-    f32x4 s[PASSES][4];
+    // State row pieces first: the bulk of the bytes, all loads in flight.
+    f32x4 s[2];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-        const int row = p * ROWS + rp;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            if (row < DV)
-                s[p][m] = __builtin_nontemporal_load(
-                    reinterpret_cast<const f32x4 *>(S + (size_t)row * DK + 4 * lr + 4 * LPR * m));
-            else
-                s[p][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
+    for (int m = 0; m < 2; ++m)
+        s[m] = live ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)row * DK + 4 * lr + 4 * LPR * m))
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
 
-    float kk[16], qq[16];
+    float kk[8], qq[8];
     const E *kp = k + ((size_t)b * hk + kh) * DK;
     const E *qp = q + ((size_t)b * hk + kh) * DK;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < 2; ++m) {
         load4<E>(kp + 4 * lr + 4 * LPR * m, kk + 4 * m);
         load4<E>(qp + 4 * lr + 4 * LPR * m, qq + 4 * m);
     }
     const float a = expf(static_cast<float>(gate_g[(size_t)b * hv + h]));
     const float beta = static_cast<float>(gate_b[(size_t)b * hv + h]);
+    const float vv = live ? static_cast<float>(v[((size_t)b * hv + h) * DV + row]) : 0.f;
 
-    float kq = 0.f;
+    float kq = 0.f, sk = 0.f, sq = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) kq += kk[j] * qq[j];
+    for (int m = 0; m < 2; ++m) {
 #pragma unroll
-    for (int off = 1; off < LPR; off <<= 1) kq += __shfl_xor(kq, off);
-
-    const E *vp = v + ((size_t)b * hv + h) * DV;
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-        const int row = p * ROWS + rp;
-        float sk = 0.f, sq = 0.f;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sk += s[p][m][e] * kk[4 * m + e];
-                sq += s[p][m][e] * qq[4 * m + e];
-            }
+        for (int e = 0; e < 4; ++e) {
+            kq += kk[4 * m + e] * qq[4 * m + e];
+            sk += s[m][e] * kk[4 * m + e];
+            sq += s[m][e] * qq[4 * m + e];
         }
+    }
 #pragma unroll
-        for (int off = 1; off < LPR; off <<= 1) {
-            sk += __shfl_xor(sk, off);
-            sq += __shfl_xor(sq, off);
-        }
-        if (row < DV) {
-            const float vv = static_cast<float>(vp[row]);
-            const float u = beta * (vv - a * sk);
-            if (lr == 0) o_row[row] = from_f32<E>(scale * (a * sq + kq * u));
+    for (int off = 1; off < LPR; off <<= 1) {
+        kq += __shfl_xor(kq, off);
+        sk += __shfl_xor(sk, off);
+        sq += __shfl_xor(sq, off);
+    }
+    if (live) {
+        const float u = beta * (vv - a * sk);
+        if (lr == 0) o_row[row] = from_f32<E>(scale * (a * sq + kq * u));
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                f32x4 w;
+        for (int m = 0; m < 2; ++m) {
+            f32x4 w;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = a * s[p][m][e] + u * kk[4 * m + e];
-                __builtin_nontemporal_store(
-                    w, reinterpret_cast<f32x4 *>(S + (size_t)row * DK + 4 * lr + 4 * LPR * m));
-            }
+            for (int e = 0; e < 4; ++e) w[e] = a * s[m][e] + u * kk[4 * m + e];
+            __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(S + (size_t)row * DK + 4 * lr + 4 * LPR * m));
         }
     }
 }
 
 template <typename E, typename G, int D>
 static hipError_t launch_decode_t(const DecodeArgs &A, hipStream_t st) {
-    const dim3 grid((unsigned)A.batch * (unsigned)A.hv), block(256);
+    const dim3 grid((unsigned)A.batch * (unsigned)A.hv * (unsigned)DecodeShape<D, D>::SLICES), block(256);
     hipLaunchKernelGGL((gdn_decode_kernel<E, G, D, D>), grid, block, 0, st,
                        (const E *)A.q, (const E *)A.k, (const E *)A.v,
                        (const G *)A.g, (const G *)A.beta, A.state, A.slots, A.num_slots,
