@@ -245,8 +245,20 @@ template <typename MM> __device__ __forceinline__ void frag_set(typename MM::Fra
     if constexpr (MM::KPL == 1) f = x; else f[e] = static_cast<bf16>(x);
 }
 
+// The 16x16 tiles at or below the diagonal of a C x C product (NB = C/16
+// row tiles) owned by the waves of parity PAR: with NB = 4, row tiles {0, 3}
+// and {1, 2} (five tiles each, balanced); with NB <= 2, row tile PAR. Slot
+// first(r) + tj holds tile (row(r), tj), tj <= row(r). Everything is
+// compile-time so that the tiles stay in registers.
+template <int NB, int PAR> struct TileSet {
+    static constexpr int NR = NB == 4 ? 2 : (PAR < NB ? 1 : 0);  // owned row tiles
+    static constexpr int row(int r) { return NB == 4 ? (PAR == 0 ? (r == 0 ? 0 : 3) : (r == 0 ? 1 : 2)) : PAR; }
+    static constexpr int first(int r) { return r == 0 ? 0 : row(0) + 1; }
+    static constexpr int N = NR == 0 ? 0 : (NR == 1 ? row(0) + 1 : row(0) + row(1) + 2);
+};
+
 template <typename E, typename G, int C, int DK>
-__global__ __launch_bounds__(256) void gdn_prep_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::value ? 4 : 2, IsBf16<E>::value ? 4 : 2))) void gdn_prep_kernel(
     const E *__restrict__ q, const E *__restrict__ k,
     const G *__restrict__ gate_g, const G *__restrict__ gate_b,
     const int32_t *__restrict__ cu, int32_t num_seqs, int32_t total_tokens,
@@ -337,6 +349,20 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
     const size_t kq0 = ((size_t)ci * hk + kh) * (size_t)(C * DK);
     const size_t ld = (size_t)hk * DK;
 
+    // Gate inputs of the group's value heads (up to kGatePrefetch of them),
+    // issued now so that their latency hides under the K and Q staging.
+    constexpr int kGatePrefetch = 2;
+    float gx_pre[kGatePrefetch], gb_pre[kGatePrefetch];
+    if (wave == 0) {
+        const bool valid = lane < len;
+#pragma unroll
+        for (int hh = 0; hh < kGatePrefetch; ++hh) {
+            const size_t gi = (size_t)(t0 + (valid ? lane : 0)) * hv + kh * group + min(hh, group - 1);
+            gx_pre[hh] = gate_load(gate_g, gi);
+            gb_pre[hh] = gate_load(gate_b, gi);
+        }
+    }
+
     // ---- 1. K and Q rows into LDS (zero past the end of the sequence)
     for (int i = tid; i < C * VPR; i += 256) {
         const int r = i / VPR, cv = i - r * VPR;
@@ -379,36 +405,30 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
     // ---- 4. K K^T (waves 0, 1) and Q K^T (waves 2, 3) on the tiles at or
     //         below the diagonal, computed as K_j K_i^T and K_j Q_i^T so that
     //         lane l holds row 16 ti + l%16, columns 16 tj + 4 (l/16) + r.
-    //         Each wave owns up to two row tiles (paired for balance).
+    //         The tiles of the wave's TileSet stay in registers.
     const bool score_wave = wave >= 2;
     const int par = wave & 1;
-    int rows[2];
-    bool rv[2];
-    if constexpr (NB == 4) {
-        rows[0] = par ? 1 : 0;
-        rows[1] = par ? 2 : 3;
-        rv[0] = rv[1] = true;
-    } else {
-        rows[0] = par;
-        rv[0] = par < NB;
-        rows[1] = 0;
-        rv[1] = false;
-    }
-    f32x4 til[2][NB];
+    constexpr int NTS = TileSet<NB, 0>::N > TileSet<NB, 1>::N ? TileSet<NB, 0>::N : TileSet<NB, 1>::N;
+    f32x4 til[NTS > 0 ? NTS : 1];
+    auto gram = [&](auto parc) {
+        typedef TileSet<NB, decltype(parc)::value> TS;
+        const E *Bm = score_wave ? sQ : sK;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+        for (int r = 0; r < TS::NR; ++r) {
+            const int ti = TS::row(r);
 #pragma unroll
-        for (int tj = 0; tj < NB; ++tj) {
-            til[s][tj] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (rv[s] && tj <= rows[s]) {
-                const E *Bm = score_wave ? sQ : sK;
+            for (int tj = 0; tj <= TS::row(r); ++tj) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < KBD; ++kb)
-                    til[s][tj] = MD::mma(load_frag<MD>(sK, LDK, 16 * tj, kb * MD::KW, lane),
-                                         load_frag<MD>(Bm, LDK, 16 * rows[s], kb * MD::KW, lane), til[s][tj]);
+                    acc = MD::mma(load_frag<MD>(sK, LDK, 16 * tj, kb * MD::KW, lane),
+                                  load_frag<MD>(Bm, LDK, 16 * ti, kb * MD::KW, lane), acc);
+                til[TS::first(r) + tj] = acc;
             }
         }
-    }
+    };
+    if (par) gram(std::integral_constant<int, 1>());
+    else gram(std::integral_constant<int, 0>());
     __syncthreads();  // the K / Q region becomes A / T
 
     // ---- 5. Per value head of the group
@@ -422,8 +442,20 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
         // the end of the sequence act as a = 1, b = 0
         if (wave == 0) {
             const bool valid = lane < len;
-            float x = valid ? gate_load(gate_g, (size_t)(t0 + lane) * hv + h) : 0.f;
-            const float bv = valid ? gate_load(gate_b, (size_t)(t0 + lane) * hv + h) : 0.f;
+            float x = 0.f, bv = 0.f;
+            if (hh < kGatePrefetch) {
+#pragma unroll
+                for (int i = 0; i < kGatePrefetch; ++i) {
+                    if (i == hh) {
+                        x = gx_pre[i];
+                        bv = gb_pre[i];
+                    }
+                }
+            } else {
+                x = gate_load(gate_g, (size_t)(t0 + (valid ? lane : 0)) * hv + h);
+                bv = gate_load(gate_b, (size_t)(t0 + (valid ? lane : 0)) * hv + h);
+            }
+            if (!valid) x = bv = 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(x, off);
@@ -444,38 +476,44 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
 
         // A = strict_lower(b_i exp(c_i - c_j) (K K^T)_ij) into LDS (waves 0, 1);
         // P = lower(scale exp(c_i - c_j) (Q K^T)_ij) to fragments (waves 2, 3)
+        auto decay = [&](auto parc) {
+            typedef TileSet<NB, decltype(parc)::value> TS;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            if (!rv[s]) continue;
-            const int ti = rows[s];
-            const int i = 16 * ti + ln;
-            const float cI = sc[i];
-            const float mI = score_wave ? scale : sb[i];
-            f32x4 val[NB];
+            for (int r = 0; r < TS::NR; ++r) {
+                const int ti = TS::row(r);
+                const int i = 16 * ti + ln;
+                const float cI = sc[i];
+                const float mI = score_wave ? scale : sb[i];
+                f32x4 val[NB];
 #pragma unroll
-            for (int tj = 0; tj < NB; ++tj) {
-                val[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (tj <= ti) {
-                    const f32x4 cJ = *reinterpret_cast<const f32x4 *>(sc + 16 * tj + 4 * g4);
+                for (int tj = 0; tj < NB; ++tj) {
+                    val[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (tj <= TS::row(r)) {
+                        const f32x4 cJ = *reinterpret_cast<const f32x4 *>(sc + 16 * tj + 4 * g4);
+                        const f32x4 t = til[TS::first(r) + (tj <= TS::row(r) ? tj : 0)];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = 16 * tj + 4 * g4 + r;
-                        const bool keep = score_wave ? j <= i : j < i;
-                        val[tj][r] = keep ? mI * exp2_hw(cI - cJ[r]) * til[s][tj][r] : 0.f;
+                        for (int e = 0; e < 4; ++e) {
+                            const int j = 16 * tj + 4 * g4 + e;
+                            const bool keep = score_wave ? j <= i : j < i;
+                            val[tj][e] = keep ? mI * exp2_hw(cI - cJ[e]) * t[e] : 0.f;
+                        }
+                        if (!score_wave) *reinterpret_cast<f32x4 *>(sA + i * LDC + 16 * tj + 4 * g4) = val[tj];
                     }
-                    if (!score_wave) *reinterpret_cast<f32x4 *>(sA + i * LDC + 16 * tj + 4 * g4) = val[tj];
+                }
+                if (score_wave) {
+#pragma unroll
+                    for (int kb = 0; kb < KBC; ++kb) {
+                        typename MC::Frag fr;
+#pragma unroll
+                        for (int e = 0; e < MC::KPL; ++e)
+                            frag_set<MC>(fr, e, val[acc_tile<MC>(kb, e)][acc_slot<MC>(kb, e)]);
+                        *reinterpret_cast<typename MC::Frag *>(pmat + mat0 + frag_off<MC>(ti * KBC + kb, lane)) = fr;
+                    }
                 }
             }
-            if (score_wave) {
-#pragma unroll
-                for (int kb = 0; kb < KBC; ++kb) {
-                    typename MC::Frag fr;
-#pragma unroll
-                    for (int e = 0; e < MC::KPL; ++e) frag_set<MC>(fr, e, val[acc_tile<MC>(kb, e)][acc_slot<MC>(kb, e)]);
-                    *reinterpret_cast<typename MC::Frag *>(pmat + mat0 + frag_off<MC>(ti * KBC + kb, lane)) = fr;
-                }
-            }
-        }
+        };
+        if (par) decay(std::integral_constant<int, 1>());
+        else decay(std::integral_constant<int, 0>());
         __syncthreads();
 
         // diagonal blocks: wave b inverts (I + A_bb) by right-looking forward
