@@ -713,6 +713,7 @@ struct OStage {
     typename S::MC::Frag pf[S::KBC];
     typename S::E4 vr;  // V[16 q + l/4][4 (l%4) ..]
     float sg;           // scale gamma of token 16 q + l%16
+    int tch[2] = {0, 0};  // L2 touches issued with this stage (consumed when it is refilled)
 
     __device__ __forceinline__ void load(const E *__restrict__ v, const E *__restrict__ pmat,
                                          const E *__restrict__ qmat, const float *__restrict__ sgam,
@@ -755,6 +756,18 @@ __device__ __forceinline__ void run_pipeline(St (&st)[N], int nch, Body &body) {
     for (; c + N - 1 < nch; c += N) pipeline_step<N>(st, c, body);
     pipeline_tail<N>(st, c, nch, body);
 }
+
+// Pulls one 1 KB run into the L2 ahead of use: each lane loads one dword at
+// a 16-byte stride, so the wave touches all eight 128-byte lines of the run.
+// The value is only kept alive (see keep_alive) and consumed several chunks
+// later, so nobody waits for it.
+__device__ __forceinline__ int l2_touch(const void *run, int lane) {
+    return *reinterpret_cast<const int *>(reinterpret_cast<const char *>(run) + 16 * lane);
+}
+__device__ __forceinline__ void keep_alive(int x) { asm volatile("" ::"v"(x)); }
+
+// Chunks ahead of the scan at which its operands are pulled into L2.
+constexpr int kTouchAhead = 8;
 
 template <typename E, int C, int DK>
 __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdn_scan_kernel(
@@ -923,6 +936,44 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                 for (int i = 0; i < 4; ++i) dst[(4 * (lane & 3) + i) * LDC] = vr[i];
             }
         };
+        // One chunk's operands of this query/key head (Q, K^T, and Tb, P, W of
+        // each value head of the group) as 1 KB runs, shared out over the
+        // output waves of the group's workgroups: each wave pulls two runs of
+        // the chunk kTouchAhead ahead into L2, so that the 16 workgroups that
+        // read them find them there instead of each waiting on memory.
+        constexpr int kRunQ = (int)((size_t)C * DK * sizeof(E) / 1024);
+        constexpr int kRunM = (int)((size_t)C * C * sizeof(E) / 1024);
+        constexpr bool kTouch = kPipelined && (size_t)C * DK * sizeof(E) % 1024 == 0 &&
+                                (size_t)C * C * sizeof(E) % 1024 == 0;
+        auto touch = [&](OS &st, int cc) {
+            if constexpr (kTouch) {
+                keep_alive(st.tch[0]);
+                keep_alive(st.tch[1]);
+                const size_t kq = (size_t)(c0 + cc) * hk + kh;
+                const size_t ch0 = (size_t)(c0 + cc) * hv + (size_t)kh * group;
+                const int per_head = 2 * kRunM + kRunQ;
+                const int nruns = 2 * kRunQ + group * per_head;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    int r = ((within * 4 + q) * 2 + i) % nruns;
+                    const E *run;
+                    if (r < kRunQ) {
+                        run = qmat + kq * (size_t)(C * DK) + (size_t)r * (1024 / sizeof(E));
+                    } else if (r < 2 * kRunQ) {
+                        run = ktmat + kq * (size_t)(C * DK) + (size_t)(r - kRunQ) * (1024 / sizeof(E));
+                    } else {
+                        r -= 2 * kRunQ;
+                        const int hh = r / per_head;
+                        r -= hh * per_head;
+                        const size_t chh = ch0 + hh;
+                        if (r < kRunM) run = tbmat + chh * (size_t)(C * C) + (size_t)r * (1024 / sizeof(E));
+                        else if (r < 2 * kRunM) run = pmat + chh * (size_t)(C * C) + (size_t)(r - kRunM) * (1024 / sizeof(E));
+                        else run = wmat + chh * (size_t)(C * DK) + (size_t)(r - 2 * kRunM) * (1024 / sizeof(E));
+                    }
+                    st.tch[i] = l2_touch(run, lane);
+                }
+            }
+        };
         OS st[kPipelined ? kOStages : 1];
         if (nch > 0) {
             st[0].load(v, pmat, qmat, sgam, chunk(0), hv, h, col0, q, lane);
@@ -938,6 +989,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             constexpr bool kThree = decltype(three)::value;
             E4 vn;
             if constexpr (kThree) {
+                touch(fut, min(c + kTouchAhead, nch - 1));
                 fut.load(v, pmat, qmat, sgam, chunk(min(c + kOStages - 1, nch - 1)), hv, h, col0, q, lane);
             } else {
                 const ChunkRef rn = chunk(min(c + 1, nch - 1));
