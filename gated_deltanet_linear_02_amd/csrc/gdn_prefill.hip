@@ -645,7 +645,9 @@ struct ScanSmem {
     static constexpr size_t off_Ut = off_S + (size_t)R * LDK * sizeof(E);    // [R][LDC] U^T
     static constexpr size_t off_DUt = off_Ut + (size_t)R * LDC * sizeof(E);  // [R][LDC] (diag(delta) U)^T
     static constexpr size_t off_Vt = off_DUt + (size_t)R * LDC * sizeof(E);  // [2][R][LDC] V^T
-    static constexpr size_t bytes = off_Vt + 2 * (size_t)R * LDC * sizeof(E);
+    static constexpr size_t off_Dl = (off_Vt + 2 * (size_t)R * LDC * sizeof(E) + 15) & ~(size_t)15;  // [2][C] delta
+    static constexpr size_t off_Sg = off_Dl + 2 * (size_t)C * sizeof(float);  // [2][C] scale gamma
+    static constexpr size_t bytes = off_Sg + 2 * (size_t)C * sizeof(float);
 };
 
 template <typename E> struct Vec4;
@@ -678,12 +680,11 @@ struct RStage {
     typedef ScanShape<E, C, DK> S;
     typename S::MD::Frag wf[S::KBD];
     typename S::MC::Frag tf[S::KBC], ktf[S::NMW][S::KBC];
-    f32x4 dl;   // delta of tokens 16 q + 4 (l/16) + i
     float gc;   // gamma_C
 
     __device__ __forceinline__ void load(const E *__restrict__ tbmat, const E *__restrict__ wmat,
-                                         const E *__restrict__ ktmat, const float *__restrict__ delta,
-                                         const float *__restrict__ gammac, const ChunkRef &r, int q, int lane) {
+                                         const E *__restrict__ ktmat, const float *__restrict__ gammac,
+                                         const ChunkRef &r, int q, int lane) {
         const int rt = min(q, S::RT - 1);
         const size_t mat0 = r.ch * (size_t)(C * C), w0 = r.ch * (size_t)(C * DK), kq0 = r.kq * (size_t)(C * DK);
 #pragma unroll
@@ -692,7 +693,6 @@ struct RStage {
 #pragma unroll
         for (int kb = 0; kb < S::KBD; ++kb)
             wf[kb] = *reinterpret_cast<const typename S::MD::Frag *>(wmat + w0 + frag_off<typename S::MD>(rt * S::KBD + kb, lane));
-        dl = *reinterpret_cast<const f32x4 *>(delta + r.ch * C + 16 * rt + 4 * (lane >> 4));
 #pragma unroll
         for (int j = 0; j < S::NMW; ++j) {
             const int mt = min(q + 4 * j, S::MT - 1);
@@ -711,24 +711,24 @@ struct OStage {
     typedef ScanShape<E, C, DK> S;
     typename S::MD::Frag qf[S::KBD];
     typename S::MC::Frag pf[S::KBC];
-    typename S::E4 vr;  // V[16 q + l/4][4 (l%4) ..]
-    float sg;           // scale gamma of token 16 q + l%16
-    int tch[2] = {0, 0};  // L2 touches issued with this stage (consumed when it is refilled)
+    typename S::E4 vr;  // fp32: V[16 q + l/4][4 (l%4) ..]
+    f32x4 aux = {0.f, 0.f, 0.f, 0.f};  // auxiliary load (see the output role of the scan)
 
     __device__ __forceinline__ void load(const E *__restrict__ v, const E *__restrict__ pmat,
-                                         const E *__restrict__ qmat, const float *__restrict__ sgam,
-                                         const ChunkRef &r, int hv, int h, int col0, int q, int lane) {
+                                         const E *__restrict__ qmat, const ChunkRef &r, int hv, int h,
+                                         int col0, int q, int lane) {
         const int rt = min(q, S::RT - 1);
         const size_t mat0 = r.ch * (size_t)(C * C), kq0 = r.kq * (size_t)(C * DK);
-        const int vrow = min(16 * rt + (lane >> 2), r.clen - 1);
-        vr = *reinterpret_cast<const typename S::E4 *>(v + ((size_t)(r.tok0 + vrow) * hv + h) * DK + col0 + 4 * (lane & 3));
+        if constexpr (!IsBf16<E>::value) {  // bf16: V comes through the auxiliary loads
+            const int vrow = min(16 * rt + (lane >> 2), r.clen - 1);
+            vr = *reinterpret_cast<const typename S::E4 *>(v + ((size_t)(r.tok0 + vrow) * hv + h) * DK + col0 + 4 * (lane & 3));
+        }
 #pragma unroll
         for (int kb = 0; kb < S::KBD; ++kb)
             qf[kb] = *reinterpret_cast<const typename S::MD::Frag *>(qmat + kq0 + frag_off<typename S::MD>(rt * S::KBD + kb, lane));
 #pragma unroll
         for (int kb = 0; kb < S::KBC; ++kb)
             pf[kb] = *reinterpret_cast<const typename S::MC::Frag *>(pmat + mat0 + frag_off<typename S::MC>(rt * S::KBC + kb, lane));
-        sg = sgam[r.ch * C + 16 * rt + (lane & 15)];
     }
 };
 
@@ -757,14 +757,8 @@ __device__ __forceinline__ void run_pipeline(St (&st)[N], int nch, Body &body) {
     pipeline_tail<N>(st, c, nch, body);
 }
 
-// Pulls one 1 KB run into the L2 ahead of use: each lane loads one dword at
-// a 16-byte stride, so the wave touches all eight 128-byte lines of the run.
-// The value is only kept alive (see keep_alive) and consumed several chunks
-// later, so nobody waits for it.
-__device__ __forceinline__ int l2_touch(const void *run, int lane) {
-    return *reinterpret_cast<const int *>(reinterpret_cast<const char *>(run) + 16 * lane);
-}
-__device__ __forceinline__ void keep_alive(int x) { asm volatile("" ::"v"(x)); }
+// Keeps a loaded value alive without using it (the load of an L2 touch).
+__device__ __forceinline__ void keep_alive(float x) { asm volatile("" ::"v"(x)); }
 
 // Chunks ahead of the scan at which its operands are pulled into L2.
 constexpr int kTouchAhead = 8;
@@ -802,6 +796,8 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
     E *sUt = reinterpret_cast<E *>(smem + L::off_Ut);
     E *sDUt = reinterpret_cast<E *>(smem + L::off_DUt);
     E *sVt = reinterpret_cast<E *>(smem + L::off_Vt);
+    float *sDl = reinterpret_cast<float *>(smem + L::off_Dl);
+    float *sSg = reinterpret_cast<float *>(smem + L::off_Sg);
 
     // Workgroup -> (sequence rank, query/key head, value head in group, slice).
     // Dispatch places workgroup b on XCD b % 8; all value heads and slices
@@ -819,7 +815,9 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
     const int col0 = (within % NS) * R;
     const int n = order[rank];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // readfirstlane: the wave index is uniform across the wave, and saying so
+    // makes role and wave branches scalar.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = wave & 3;
     const bool recurrence = wave < 4;
     const int g4 = lane >> 4, ln = lane & 15;
@@ -856,7 +854,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
 
         auto body = [&](RS &st, RS &, RS &fut, int c, auto three) {
             constexpr bool kThree = decltype(three)::value;
-            if constexpr (kThree) fut.load(tbmat, wmat, ktmat, delta, gammac, chunk(min(c + kRStages - 1, nch - 1)), q, lane);
+            if constexpr (kThree) fut.load(tbmat, wmat, ktmat, gammac, chunk(min(c + kRStages - 1, nch - 1)), q, lane);
             // ---- phase 1: U = Tb V - W S0^T (W is stored negated). Token and
             // key contractions accumulate separately: with d = 16 they use
             // MFMAs of different shapes, which must not be chained through
@@ -877,10 +875,11 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                     else uk0 = MD::mma(st.wf[kb], sf[kb], uk0);
                 }
                 const f32x4 u = ut + uk0 + uk1;
+                const f32x4 dl = *reinterpret_cast<const f32x4 *>(sDl + (c & 1) * C + 16 * q + 4 * g4);
                 store_acc_t<E>(sUt, LDC, 16 * q, 0, lane, u);
                 f32x4 du;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) du[i] = st.dl[i] * u[i];
+                for (int i = 0; i < 4; ++i) du[i] = dl[i] * u[i];
                 store_acc_t<E>(sDUt, LDC, 16 * q, 0, lane, du);
             }
             __syncthreads();
@@ -902,7 +901,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                 }
             }
             __syncthreads();
-            if constexpr (!kThree) st.load(tbmat, wmat, ktmat, delta, gammac, chunk(min(c + 1, nch - 1)), q, lane);
+            if constexpr (!kThree) st.load(tbmat, wmat, ktmat, gammac, chunk(min(c + 1, nch - 1)), q, lane);
         };
 
         if (nch > 0) {
@@ -910,11 +909,11 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                 RS st[kRStages];
 #pragma unroll
                 for (int i = 0; i + 1 < kRStages; ++i)
-                    st[i].load(tbmat, wmat, ktmat, delta, gammac, chunk(min(i, nch - 1)), q, lane);
+                    st[i].load(tbmat, wmat, ktmat, gammac, chunk(min(i, nch - 1)), q, lane);
                 run_pipeline<kRStages>(st, nch, body);
             } else {
                 RS st0;
-                st0.load(tbmat, wmat, ktmat, delta, gammac, chunk(0), q, lane);
+                st0.load(tbmat, wmat, ktmat, gammac, chunk(0), q, lane);
                 for (int c = 0; c < nch; ++c) body(st0, st0, st0, c, std::false_type());
             }
         }
@@ -928,56 +927,97 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             }
         }
     } else {
-        // This wave's V rows of a chunk into sVt[buf] (transposed: [value][token]).
-        auto put_v = [&](const E4 &vr, int buf) {
-            if (q < RT) {
+        // Besides its Q and P fragments, each output wave issues one auxiliary
+        // 16-byte-per-lane load per chunk (bf16):
+        //   wave 0     the chunk's gate vectors (delta for the recurrence
+        //              waves, scale gamma for the outputs), staged in LDS;
+        //   wave 1     an L2 touch of the chunk kTouchAhead ahead: the 16
+        //              workgroups of the query/key head split that chunk's
+        //              operands (Q, K^T, and Tb, P, W of each value head of
+        //              the group; 128-byte lines) 64 lines each, one line per
+        //              lane, so that the workgroups' own loads later hit L2;
+        //              the value is only kept alive until the stage is
+        //              refilled;
+        //   waves 2-3  the chunk's V rows 32 (q - 2) .. + 31 (8 values per
+        //              lane), staged in LDS.
+        // Memory instructions, not bytes, bound the scan, so these small
+        // loads are folded into as few instructions as possible. The fp32
+        // path (one stage) loads V per wave and the gate vectors in every wave.
+        constexpr int kRunQ = (int)((size_t)C * DK * sizeof(E) / 1024);
+        constexpr int kRunM = (int)((size_t)C * C * sizeof(E) / 1024);
+        constexpr bool kTouch = kPipelined && (size_t)C * DK * sizeof(E) % 1024 == 0 &&
+                                (size_t)C * C * sizeof(E) % 1024 == 0;
+        auto gate_ptr = [&](const ChunkRef &r) {
+            // lanes [0, C/4): delta, 4 tokens each; [C/4, C/2): scale gamma
+            const int l = min(lane, C / 2 - 1);
+            return reinterpret_cast<const f32x4 *>(l < C / 4 ? delta + r.ch * C + 4 * l
+                                                             : sgam + r.ch * C + 4 * (l - C / 4));
+        };
+        auto touch_ptr = [&](int cc) {
+            const size_t kq = (size_t)(c0 + cc) * hk + kh;
+            const size_t ch0 = (size_t)(c0 + cc) * hv + (size_t)kh * group;
+            const int per_head = 2 * kRunM + kRunQ;
+            const int nlines = 8 * (2 * kRunQ + group * per_head);
+            const int line = (within * 64 + lane) % nlines;
+            int r = line >> 3;
+            const size_t off = (size_t)(line & 7) * (128 / sizeof(E));
+            const E *run;
+            if (r < kRunQ) {
+                run = qmat + kq * (size_t)(C * DK) + (size_t)r * (1024 / sizeof(E));
+            } else if (r < 2 * kRunQ) {
+                run = ktmat + kq * (size_t)(C * DK) + (size_t)(r - kRunQ) * (1024 / sizeof(E));
+            } else {
+                r -= 2 * kRunQ;
+                const int hh = r / per_head;
+                r -= hh * per_head;
+                const size_t chh = ch0 + hh;
+                if (r < kRunM) run = tbmat + chh * (size_t)(C * C) + (size_t)r * (1024 / sizeof(E));
+                else if (r < 2 * kRunM) run = pmat + chh * (size_t)(C * C) + (size_t)(r - kRunM) * (1024 / sizeof(E));
+                else run = wmat + chh * (size_t)(C * DK) + (size_t)(r - 2 * kRunM) * (1024 / sizeof(E));
+            }
+            return reinterpret_cast<const f32x4 *>(run + off);
+        };
+        auto aux_ptr = [&](int c_aux, int c_touch) {
+            const ChunkRef r = chunk(c_aux);
+            if (!kPipelined || q == 0) return gate_ptr(r);
+            if (q == 1) return kTouch ? touch_ptr(c_touch) : gate_ptr(r);
+            const int vrow = min(32 * (q - 2) + (lane >> 1), r.clen - 1);
+            return reinterpret_cast<const f32x4 *>(v + ((size_t)(r.tok0 + vrow) * hv + h) * DK + col0 + 8 * (lane & 1));
+        };
+        // The load is unconditional; only its address depends on the wave.
+        auto load_aux = [&](OS &st, int c_aux, int c_touch) {
+            keep_alive(st.aux[0]);  // wave 1: the touch issued when this stage was last filled
+            st.aux = *aux_ptr(c_aux, c_touch);
+        };
+        // A chunk's staged inputs into LDS buffer `buf`: the gate vectors
+        // (wave 0) and, bf16, the V rows (waves 2, 3) from the auxiliary load;
+        // fp32, each wave's V rows.
+        auto put_chunk = [&](const OS &st, const E4 &vr, int buf) {
+            if (q == 0 && lane < C / 2) {
+                float *dst = lane < C / 4 ? sDl + buf * C + 4 * lane : sSg + buf * C + 4 * (lane - C / 4);
+                *reinterpret_cast<f32x4 *>(dst) = st.aux;
+            }
+            if constexpr (kPipelined) {
+                if (q >= 2) {
+                    const int t = 32 * (q - 2) + (lane >> 1);
+                    if (t < C) {
+                        const bf16x8 x = __builtin_bit_cast(bf16x8, st.aux);
+                        E *dst = sVt + buf * (R * LDC) + t;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) dst[(8 * (lane & 1) + i) * LDC] = x[i];
+                    }
+                }
+            } else if (q < RT) {
                 E *dst = sVt + buf * (R * LDC) + 16 * q + (lane >> 2);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dst[(4 * (lane & 3) + i) * LDC] = vr[i];
             }
         };
-        // One chunk's operands of this query/key head (Q, K^T, and Tb, P, W of
-        // each value head of the group) as 1 KB runs, shared out over the
-        // output waves of the group's workgroups: each wave pulls two runs of
-        // the chunk kTouchAhead ahead into L2, so that the 16 workgroups that
-        // read them find them there instead of each waiting on memory.
-        constexpr int kRunQ = (int)((size_t)C * DK * sizeof(E) / 1024);
-        constexpr int kRunM = (int)((size_t)C * C * sizeof(E) / 1024);
-        constexpr bool kTouch = kPipelined && (size_t)C * DK * sizeof(E) % 1024 == 0 &&
-                                (size_t)C * C * sizeof(E) % 1024 == 0;
-        auto touch = [&](OS &st, int cc) {
-            if constexpr (kTouch) {
-                keep_alive(st.tch[0]);
-                keep_alive(st.tch[1]);
-                const size_t kq = (size_t)(c0 + cc) * hk + kh;
-                const size_t ch0 = (size_t)(c0 + cc) * hv + (size_t)kh * group;
-                const int per_head = 2 * kRunM + kRunQ;
-                const int nruns = 2 * kRunQ + group * per_head;
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    int r = ((within * 4 + q) * 2 + i) % nruns;
-                    const E *run;
-                    if (r < kRunQ) {
-                        run = qmat + kq * (size_t)(C * DK) + (size_t)r * (1024 / sizeof(E));
-                    } else if (r < 2 * kRunQ) {
-                        run = ktmat + kq * (size_t)(C * DK) + (size_t)(r - kRunQ) * (1024 / sizeof(E));
-                    } else {
-                        r -= 2 * kRunQ;
-                        const int hh = r / per_head;
-                        r -= hh * per_head;
-                        const size_t chh = ch0 + hh;
-                        if (r < kRunM) run = tbmat + chh * (size_t)(C * C) + (size_t)r * (1024 / sizeof(E));
-                        else if (r < 2 * kRunM) run = pmat + chh * (size_t)(C * C) + (size_t)(r - kRunM) * (1024 / sizeof(E));
-                        else run = wmat + chh * (size_t)(C * DK) + (size_t)(r - 2 * kRunM) * (1024 / sizeof(E));
-                    }
-                    st.tch[i] = l2_touch(run, lane);
-                }
-            }
-        };
         OS st[kPipelined ? kOStages : 1];
         if (nch > 0) {
-            st[0].load(v, pmat, qmat, sgam, chunk(0), hv, h, col0, q, lane);
-            put_v(st[0].vr, 0);
+            st[0].load(v, pmat, qmat, chunk(0), hv, h, col0, q, lane);
+            load_aux(st[0], 0, min(kTouchAhead, nch - 1));
+            put_chunk(st[0], st[0].vr, 0);
         }
         __syncthreads();  // S0 and chunk 0's V rows staged
 
@@ -988,13 +1028,16 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         auto body = [&](OS &st, OS &nxt, OS &fut, int c, auto three) {
             constexpr bool kThree = decltype(three)::value;
             E4 vn;
+            OS gn;  // one stage: chunk c + 1's gate vectors (its aux)
             if constexpr (kThree) {
-                touch(fut, min(c + kTouchAhead, nch - 1));
-                fut.load(v, pmat, qmat, sgam, chunk(min(c + kOStages - 1, nch - 1)), hv, h, col0, q, lane);
+                const int cf = min(c + kOStages - 1, nch - 1);
+                load_aux(fut, cf, min(c + kTouchAhead, nch - 1));
+                fut.load(v, pmat, qmat, chunk(cf), hv, h, col0, q, lane);
             } else {
                 const ChunkRef rn = chunk(min(c + 1, nch - 1));
                 const int vrow = min(16 * min(q, RT - 1) + (lane >> 2), rn.clen - 1);
                 vn = *reinterpret_cast<const E4 *>(v + ((size_t)(rn.tok0 + vrow) * hv + h) * DK + col0 + 4 * (lane & 3));
+                gn.aux = *gate_ptr(rn);
             }
             // ---- phase 1: O1^T = S0 Q^T
             f32x4 o1 = {0.f, 0.f, 0.f, 0.f};
@@ -1012,24 +1055,27 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
                 for (int kb = 0; kb < KBC; ++kb) o = MC::mma(load_frag_acc<MC>(sUt, LDC, 0, kb, lane), st.pf[kb], o);
                 const int row = 16 * q + ln;
+                const float sg = sSg[(c & 1) * C + row];
                 if (row < clen) {
                     E4 w;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(st.sg * o1[i] + o[i]);
+                    for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(sg * o1[i] + o[i]);
                     *reinterpret_cast<E4 *>(out + ((size_t)(tok0 + row) * hv + h) * DV + col0 + 4 * g4) = w;
                 }
             }
-            if constexpr (kThree) put_v(nxt.vr, (c + 1) & 1);
-            else put_v(vn, (c + 1) & 1);
+            if constexpr (kThree) put_chunk(nxt, nxt.vr, (c + 1) & 1);
+            else put_chunk(gn, vn, (c + 1) & 1);
             __syncthreads();
-            if constexpr (!kThree) st.load(v, pmat, qmat, sgam, chunk(min(c + 1, nch - 1)), hv, h, col0, q, lane);
+            if constexpr (!kThree) st.load(v, pmat, qmat, chunk(min(c + 1, nch - 1)), hv, h, col0, q, lane);
         };
 
         if (nch > 0) {
             if constexpr (kPipelined) {
 #pragma unroll
-                for (int i = 1; i + 1 < kOStages; ++i)
-                    st[i].load(v, pmat, qmat, sgam, chunk(min(i, nch - 1)), hv, h, col0, q, lane);
+                for (int i = 1; i + 1 < kOStages; ++i) {
+                    st[i].load(v, pmat, qmat, chunk(min(i, nch - 1)), hv, h, col0, q, lane);
+                    load_aux(st[i], min(i, nch - 1), min(i + kTouchAhead, nch - 1));
+                }
                 run_pipeline<kOStages>(st, nch, body);
             } else {
                 for (int c = 0; c < nch; ++c) body(st[0], st[0], st[0], c, std::false_type());
