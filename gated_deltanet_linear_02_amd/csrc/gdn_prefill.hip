@@ -854,7 +854,6 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
 
         auto body = [&](RS &st, RS &, RS &fut, int c, auto three) {
             constexpr bool kThree = decltype(three)::value;
-            if constexpr (kThree) fut.load(tbmat, wmat, ktmat, gammac, chunk(min(c + kRStages - 1, nch - 1)), q, lane);
             // ---- phase 1: U = Tb V - W S0^T (W is stored negated). Token and
             // key contractions accumulate separately: with d = 16 they use
             // MFMAs of different shapes, which must not be chained through
@@ -884,6 +883,10 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             }
             __syncthreads();
             // ---- phase 2: S^T <- gamma_C S^T + K^T (diag(delta) U)
+            // The prefetch is issued here rather than at the chunk start: phase 1
+            // bounds the chunk through these waves, phase 2 through the output
+            // waves, so a load queue that is full costs less here.
+            if constexpr (kThree) fut.load(tbmat, wmat, ktmat, gammac, chunk(min(c + kRStages - 1, nch - 1)), q, lane);
             typename MC::Frag duf[KBC];
 #pragma unroll
             for (int kb = 0; kb < KBC; ++kb) duf[kb] = load_frag_acc<MC>(sDUt, LDC, 0, kb, lane);
@@ -1039,6 +1042,11 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                 vn = *reinterpret_cast<const E4 *>(v + ((size_t)(rn.tok0 + vrow) * hv + h) * DK + col0 + 4 * (lane & 3));
                 gn.aux = *gate_ptr(rn);
             }
+            // The next chunk's V rows and gate vectors go to LDS now, while
+            // this wave would wait for the recurrence waves anyway (their
+            // buffers were last read before the previous barrier).
+            if constexpr (kThree) put_chunk(nxt, nxt.vr, (c + 1) & 1);
+            else put_chunk(gn, vn, (c + 1) & 1);
             // ---- phase 1: O1^T = S0 Q^T
             f32x4 o1 = {0.f, 0.f, 0.f, 0.f};
             if (q < RT) {
@@ -1063,8 +1071,6 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                     *reinterpret_cast<E4 *>(out + ((size_t)(tok0 + row) * hv + h) * DV + col0 + 4 * g4) = w;
                 }
             }
-            if constexpr (kThree) put_chunk(nxt, nxt.vr, (c + 1) & 1);
-            else put_chunk(gn, vn, (c + 1) & 1);
             __syncthreads();
             if constexpr (!kThree) st.load(v, pmat, qmat, chunk(min(c + 1, nch - 1)), hv, h, col0, q, lane);
         };
