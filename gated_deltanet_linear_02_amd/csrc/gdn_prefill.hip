@@ -971,7 +971,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                 run = ktmat + kq * (size_t)(C * DK) + (size_t)(r - kRunQ) * (1024 / sizeof(E));
             } else {
                 r -= 2 * kRunQ;
-                const int hh = r / per_head;
+                const int hh = r / (per_head > 0 ? per_head : 1);
                 r -= hh * per_head;
                 const size_t chh = ch0 + hh;
                 if (r < kRunM) run = tbmat + chh * (size_t)(C * C) + (size_t)r * (1024 / sizeof(E));
