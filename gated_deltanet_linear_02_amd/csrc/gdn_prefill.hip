@@ -700,7 +700,13 @@ struct RStage {
             for (int kb = 0; kb < S::KBC; ++kb)
                 ktf[j][kb] = *reinterpret_cast<const typename S::MC::Frag *>(ktmat + kq0 + frag_off<typename S::MC>(mt * S::KBC + kb, lane));
         }
-        gc = gammac[r.ch];
+        // A vector load, so that it completes in order with the stage's
+        // fragments (vmcnt). As a scalar load (the compiler's choice for a
+        // uniform address) it shares lgkmcnt with the LDS reads of the chain,
+        // whose waits then also wait for it.
+        int z;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+        gc = gammac[r.ch + z];
     }
 };
 
