@@ -20,7 +20,6 @@ struct TimingState {
     bool active = false;
     int max_launches = 0;
     int used = 0;
-    bool open = false;
     std::vector<hipEvent_t> events;  // 2 per launch
     std::vector<int> kinds;
 };
@@ -30,22 +29,16 @@ TimingState &timing() {
 }
 }  // namespace
 
-void timing_begin(KernelKind kind, hipStream_t st) {
+TimingEvents timing_claim(KernelKind kind) {
     TimingState &T = timing();
     std::lock_guard<std::mutex> lk(T.mu);
-    if (!T.active || T.used >= T.max_launches) return;
-    if (hipEventRecord(T.events[2 * T.used], st) != hipSuccess) return;
+    TimingEvents ev;
+    if (!T.active || T.used >= T.max_launches) return ev;
+    ev.start = T.events[2 * T.used];
+    ev.stop = T.events[2 * T.used + 1];
     T.kinds[T.used] = kind;
-    T.open = true;
-}
-
-void timing_end(KernelKind kind, hipStream_t st) {
-    TimingState &T = timing();
-    std::lock_guard<std::mutex> lk(T.mu);
-    if (!T.active || !T.open || T.kinds[T.used] != kind) return;
-    T.open = false;
-    if (hipEventRecord(T.events[2 * T.used + 1], st) != hipSuccess) return;
     ++T.used;
+    return ev;
 }
 
 // ----------------------------------------------------------------- checks
@@ -189,9 +182,7 @@ int32_t gdn_decode_step(const void *q, const void *k, const void *v, const void 
     A.io_bf16 = io_dtype == GDN_BF16; A.gate_bf16 = gate_dtype == GDN_BF16;
     try {
         const hipStream_t st = static_cast<hipStream_t>(stream);
-        timing_begin(kDecode, st);
         const hipError_t e = launch_decode(A, st);
-        timing_end(kDecode, st);
         return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
     } catch (...) {
         return GDN_ERR_HIP;
@@ -219,7 +210,6 @@ int32_t gdn_timing_start(int32_t max_launches) {
     }
     T.max_launches = max_launches;
     T.used = 0;
-    T.open = false;
     T.active = true;
     return GDN_OK;
 }

@@ -127,11 +127,10 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(
 template <typename E, typename G, int D>
 static hipError_t launch_decode_t(const DecodeArgs &A, hipStream_t st) {
     const dim3 grid((unsigned)A.batch * (unsigned)A.hv * (unsigned)DecodeShape<D, D>::SLICES), block(256);
-    hipLaunchKernelGGL((gdn_decode_kernel<E, G, D, D>), grid, block, 0, st,
-                       (const E *)A.q, (const E *)A.k, (const E *)A.v,
-                       (const G *)A.g, (const G *)A.beta, A.state, A.slots, A.num_slots,
-                       (E *)A.out, A.hk, A.hv, A.scale);
-    return hipGetLastError();
+    return launch_kernel(kDecode, gdn_decode_kernel<E, G, D, D>, grid, block, 0, st,
+                         (const E *)A.q, (const E *)A.k, (const E *)A.v,
+                         (const G *)A.g, (const G *)A.beta, A.state, A.slots, A.num_slots,
+                         (E *)A.out, A.hk, A.hv, A.scale);
 }
 
 template <typename E, typename G>

@@ -120,23 +120,52 @@ __device__ __forceinline__ typename M::Frag load_frag_acc(const E *base, int ld,
     }
 }
 
-// Write an accumulator tile transposed: element D[m0 + 4g + i][n0 + n] goes to
-// dst[(n0 + n) * ld + m0 + 4g + i] (4 contiguous elements per lane).
-template <typename E> __device__ __forceinline__ void store_acc_t(E *dst, int ld, int m0, int n0, int lane, f32x4 v);
-
-template <>
-__device__ __forceinline__ void store_acc_t<bf16>(bf16 *dst, int ld, int m0, int n0, int lane, f32x4 v) {
+// Four accumulator values to 4 contiguous elements.
+template <typename E> __device__ __forceinline__ void store4(E *p, f32x4 v);
+template <> __device__ __forceinline__ void store4<bf16>(bf16 *p, f32x4 v) {
     bf16x4 w;
     w[0] = static_cast<bf16>(v[0]);
     w[1] = static_cast<bf16>(v[1]);
     w[2] = static_cast<bf16>(v[2]);
     w[3] = static_cast<bf16>(v[3]);
-    *reinterpret_cast<bf16x4 *>(dst + (n0 + (lane & 15)) * ld + m0 + 4 * (lane >> 4)) = w;
+    *reinterpret_cast<bf16x4 *>(p) = w;
+}
+template <> __device__ __forceinline__ void store4<float>(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
+
+// Write an accumulator tile transposed: element D[m0 + 4g + i][n0 + n] goes to
+// dst[(n0 + n) * ld + m0 + 4g + i] (4 contiguous elements per lane).
+template <typename E> __device__ __forceinline__ void store_acc_t(E *dst, int ld, int m0, int n0, int lane, f32x4 v) {
+    store4<E>(dst + (n0 + (lane & 15)) * ld + m0 + 4 * (lane >> 4), v);
 }
 
-template <>
-__device__ __forceinline__ void store_acc_t<float>(float *dst, int ld, int m0, int n0, int lane, f32x4 v) {
-    *reinterpret_cast<f32x4 *>(dst + (n0 + (lane & 15)) * ld + m0 + 4 * (lane >> 4)) = v;
+// Fragment-contiguous LDS rows. In rows that are read back as 32-deep
+// accumulator-order fragments (KPL = 8), contraction index k is stored at
+// lds_pos(k): within each 32-element block the eight indices one lane reads,
+// acc_k(kb, g, 0..7), sit at 8 g .. 8 g + 7, so that a fragment is one 16-byte
+// LDS read instead of two 8-byte ones (16-byte reads move about 1.7 times the
+// bytes per cycle). The four indices an accumulator tile gives a lane
+// (4 g .. 4 g + 3 of a 16-wide tile) stay contiguous, so stores are 8 bytes.
+// Other fragment shapes keep the natural order.
+template <typename MM> __device__ __forceinline__ constexpr int lds_pos(int k) {
+    if constexpr (MM::KPL == 8) return (k & ~31) | ((k & 12) << 1) | ((k & 16) >> 2) | (k & 3);
+    else return k;
+}
+
+// store_acc_t into rows laid out by lds_pos<MM> (m0 is a multiple of 16):
+// element D[m0 + 4g + i][n0 + n] goes to dst[(n0 + n) * ld + lds_pos(m0 + 4g) + i].
+template <typename MM, typename E>
+__device__ __forceinline__ void store_acc_p(E *dst, int ld, int m0, int n0, int lane, f32x4 v) {
+    store4<E>(dst + (n0 + (lane & 15)) * ld + lds_pos<MM>(m0 + 4 * (lane >> 4)), v);
+}
+
+// load_frag_acc from rows laid out by lds_pos<M>.
+template <typename M, typename E>
+__device__ __forceinline__ typename M::Frag load_frag_p(const E *base, int ld, int r0, int kb, int lane) {
+    if constexpr (M::KPL == 8) {
+        return *reinterpret_cast<const bf16x8 *>(base + (r0 + (lane & 15)) * ld + kb * 32 + 8 * (lane >> 4));
+    } else {
+        return load_frag_acc<M>(base, ld, r0, kb, lane);
+    }
 }
 
 // 16-byte vector of elements (8 bf16 or 4 fp32) for global <-> LDS staging.

@@ -2,6 +2,7 @@
 // (gdn_api.hip) and the kernel launchers. Not installed, not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -10,9 +11,23 @@ namespace gdn {
 
 enum KernelKind { kSchedule = 0, kPrep = 1, kScan = 2, kDecode = 3, kKinds = 4 };
 
-// Event bracketing of launches (see gdn_timing_start in gdn.h).
-void timing_begin(KernelKind kind, hipStream_t st);
-void timing_end(KernelKind kind, hipStream_t st);
+// Per-kernel timing (see gdn_timing_start in gdn.h): while it is active,
+// each launch claims a pair of events that the dispatch itself stamps with
+// the kernel's start and end, so that they time the kernel alone (no marker
+// packets around it); otherwise both are null.
+struct TimingEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+TimingEvents timing_claim(KernelKind kind);
+
+// Launches `kernel` on `st`, timed as `kind` while timing is active.
+template <typename F, typename... Args>
+hipError_t launch_kernel(KernelKind kind, F kernel, dim3 grid, dim3 block, size_t smem, hipStream_t st,
+                         Args... args) {
+    const TimingEvents ev = timing_claim(kind);
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)smem, st, ev.start, ev.stop, 0u, args...);
+    return hipGetLastError();
+}
 
 struct DecodeArgs {
     const void *q, *k, *v, *g, *beta;

@@ -641,6 +641,7 @@ struct ScanSmem {
     static constexpr int R = kSliceRows;
     static constexpr int LDK = DK + PE;  // rows of length DK
     static constexpr int LDC = C + PE;   // rows of length C
+    // Rows in fragment-contiguous order (lds_pos: keys for MD, tokens for MC).
     static constexpr size_t off_S = 0;                                       // [R][LDK] S (value row, key)
     static constexpr size_t off_Ut = off_S + (size_t)R * LDK * sizeof(E);    // [R][LDC] U^T
     static constexpr size_t off_DUt = off_Ut + (size_t)R * LDC * sizeof(E);  // [R][LDC] (diag(delta) U)^T
@@ -853,7 +854,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             if (mt < MT) {
                 if (s0)
                     sacc[j] = *reinterpret_cast<const f32x4 *>(s0 + state0 + (size_t)(col0 + ln) * DK + 16 * mt + 4 * g4);
-                store_acc_t<E>(sS, LDK, 16 * mt, 0, lane, sacc[j]);
+                store_acc_p<MD>(sS, LDK, 16 * mt, 0, lane, sacc[j]);
             }
         }
         __syncthreads();  // S0 and chunk 0's V rows staged
@@ -868,9 +869,9 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                 typename MC::Frag vf[KBC];
                 typename MD::Frag sf[KBD];
 #pragma unroll
-                for (int kb = 0; kb < KBC; ++kb) vf[kb] = load_frag_acc<MC>(sVt + (c & 1) * (R * LDC), LDC, 0, kb, lane);
+                for (int kb = 0; kb < KBC; ++kb) vf[kb] = load_frag_p<MC>(sVt + (c & 1) * (R * LDC), LDC, 0, kb, lane);
 #pragma unroll
-                for (int kb = 0; kb < KBD; ++kb) sf[kb] = load_frag_acc<MD>(sS, LDK, 0, kb, lane);
+                for (int kb = 0; kb < KBD; ++kb) sf[kb] = load_frag_p<MD>(sS, LDK, 0, kb, lane);
                 f32x4 ut = {0.f, 0.f, 0.f, 0.f}, uk0 = {0.f, 0.f, 0.f, 0.f}, uk1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < KBC; ++kb) ut = MC::mma(st.tf[kb], vf[kb], ut);
@@ -881,11 +882,11 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                 }
                 const f32x4 u = ut + uk0 + uk1;
                 const f32x4 dl = *reinterpret_cast<const f32x4 *>(sDl + (c & 1) * C + 16 * q + 4 * g4);
-                store_acc_t<E>(sUt, LDC, 16 * q, 0, lane, u);
+                store_acc_p<MC>(sUt, LDC, 16 * q, 0, lane, u);
                 f32x4 du;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) du[i] = dl[i] * u[i];
-                store_acc_t<E>(sDUt, LDC, 16 * q, 0, lane, du);
+                store_acc_p<MC>(sDUt, LDC, 16 * q, 0, lane, du);
             }
             __syncthreads();
             // ---- phase 2: S^T <- gamma_C S^T + K^T (diag(delta) U)
@@ -895,7 +896,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             if constexpr (kThree) fut.load(tbmat, wmat, ktmat, gammac, chunk(min(c + kRStages - 1, nch - 1)), q, lane);
             typename MC::Frag duf[KBC];
 #pragma unroll
-            for (int kb = 0; kb < KBC; ++kb) duf[kb] = load_frag_acc<MC>(sDUt, LDC, 0, kb, lane);
+            for (int kb = 0; kb < KBC; ++kb) duf[kb] = load_frag_p<MC>(sDUt, LDC, 0, kb, lane);
 #pragma unroll
             for (int j = 0; j < NMW; ++j) {
                 const int mt = q + 4 * j;
@@ -906,7 +907,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
                     for (int kb = 0; kb < KBC; ++kb) acc = MC::mma(st.ktf[j][kb], duf[kb], acc);
                     sacc[j] = acc;
-                    store_acc_t<E>(sS, LDK, 16 * mt, 0, lane, acc);
+                    store_acc_p<MD>(sS, LDK, 16 * mt, 0, lane, acc);
                 }
             }
             __syncthreads();
@@ -1011,13 +1012,13 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                     const int t = 32 * (q - 2) + (lane >> 1);
                     if (t < C) {
                         const bf16x8 x = __builtin_bit_cast(bf16x8, st.aux);
-                        E *dst = sVt + buf * (R * LDC) + t;
+                        E *dst = sVt + buf * (R * LDC) + lds_pos<MC>(t);
 #pragma unroll
                         for (int i = 0; i < 8; ++i) dst[(8 * (lane & 1) + i) * LDC] = x[i];
                     }
                 }
             } else if (q < RT) {
-                E *dst = sVt + buf * (R * LDC) + 16 * q + (lane >> 2);
+                E *dst = sVt + buf * (R * LDC) + lds_pos<MC>(16 * q + (lane >> 2));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dst[(4 * (lane & 3) + i) * LDC] = vr[i];
             }
@@ -1057,7 +1058,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             f32x4 o1 = {0.f, 0.f, 0.f, 0.f};
             if (q < RT) {
 #pragma unroll
-                for (int kb = 0; kb < KBD; ++kb) o1 = MD::mma(load_frag_acc<MD>(sS, LDK, 0, kb, lane), st.qf[kb], o1);
+                for (int kb = 0; kb < KBD; ++kb) o1 = MD::mma(load_frag_p<MD>(sS, LDK, 0, kb, lane), st.qf[kb], o1);
             }
             __syncthreads();
             // ---- phase 2: O^T = O1^T diag(scale gamma) + U^T P^T; lane: token
@@ -1067,7 +1068,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             if (q < RT) {
                 f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < KBC; ++kb) o = MC::mma(load_frag_acc<MC>(sUt, LDC, 0, kb, lane), st.pf[kb], o);
+                for (int kb = 0; kb < KBC; ++kb) o = MC::mma(load_frag_p<MC>(sUt, LDC, 0, kb, lane), st.pf[kb], o);
                 const int row = 16 * q + ln;
                 const float sg = sSg[(c & 1) * C + row];
                 if (row < clen) {
@@ -1132,26 +1133,22 @@ static hipError_t launch_prefill_t(const PrefillArgs &A, hipStream_t st) {
     const bool fold = A.num_seqs <= kFoldMaxSeqs;
     hipError_t e = hipSuccess;
     if (!fold) {
-        timing_begin(kSchedule, st);
-        hipLaunchKernelGGL(gdn_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, st,
-                           A.cu, A.num_seqs, (int32_t)A.total_tokens, A.chunk,
-                           bounds, seq_chunk0, order, chunk_seq, chunk_tok0, counters);
-        timing_end(kSchedule, st);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        e = launch_kernel(kSchedule, gdn_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, st,
+                          A.cu, A.num_seqs, (int32_t)A.total_tokens, A.chunk,
+                          bounds, seq_chunk0, order, chunk_seq, chunk_tok0, counters);
+        if (e != hipSuccess) return e;
     }
 
     typedef PrepSmem<E, C, D> PL;
     static std::atomic<bool> prep_ok{false};
     auto prep = gdn_prep_kernel<E, G, C, D>;
     if ((e = allow_smem(prep, PL::bytes, prep_ok)) != hipSuccess) return e;
-    timing_begin(kPrep, st);
-    hipLaunchKernelGGL(prep, dim3((unsigned)Y.max_chunks, (unsigned)A.hk), dim3(256), PL::bytes, st,
-                       (const E *)A.q, (const E *)A.k, (const G *)A.g, (const G *)A.beta,
-                       fold ? A.cu : nullptr, A.num_seqs, (int32_t)A.total_tokens, bounds, seq_chunk0, order,
-                       chunk_seq, chunk_tok0, counters, tbmat, pmat, wmat, qmat, ktmat, sgam, delta,
-                       gammac, A.hk, A.hv, A.scale);
-    timing_end(kPrep, st);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = launch_kernel(kPrep, prep, dim3((unsigned)Y.max_chunks, (unsigned)A.hk), dim3(256), PL::bytes, st,
+                      (const E *)A.q, (const E *)A.k, (const G *)A.g, (const G *)A.beta,
+                      fold ? A.cu : nullptr, A.num_seqs, (int32_t)A.total_tokens, bounds, seq_chunk0, order,
+                      (const int32_t *)chunk_seq, (const int32_t *)chunk_tok0, (const int32_t *)counters,
+                      tbmat, pmat, wmat, qmat, ktmat, sgam, delta, gammac, A.hk, A.hv, A.scale);
+    if (e != hipSuccess) return e;
 
     typedef ScanSmem<E, C, D> SL;
     static std::atomic<bool> scan_ok{false};
@@ -1160,12 +1157,11 @@ static hipError_t launch_prefill_t(const PrefillArgs &A, hipStream_t st) {
     const int64_t per_kh = (int64_t)(A.hv / A.hk) * (D / kSliceRows);
     const int64_t groups = (int64_t)A.num_seqs * A.hk;
     const int64_t grid = ((groups + 7) / 8) * per_kh * 8;
-    timing_begin(kScan, st);
-    hipLaunchKernelGGL(scan, dim3((unsigned)grid), dim3(kScanThreads), SL::bytes, st,
-                       (const E *)A.v, bounds, seq_chunk0, order, tbmat, pmat, wmat, qmat, ktmat, sgam, delta,
-                       gammac, A.s0, A.s_final, (E *)A.out, A.num_seqs, A.hk, A.hv);
-    timing_end(kScan, st);
-    return hipGetLastError();
+    return launch_kernel(kScan, scan, dim3((unsigned)grid), dim3(kScanThreads), SL::bytes, st,
+                         (const E *)A.v, (const int32_t *)bounds, (const int32_t *)seq_chunk0,
+                         (const int32_t *)order, (const E *)tbmat, (const E *)pmat, (const E *)wmat,
+                         (const E *)qmat, (const E *)ktmat, (const float *)sgam, (const float *)delta,
+                         (const float *)gammac, A.s0, A.s_final, (E *)A.out, A.num_seqs, A.hk, A.hv);
 }
 
 template <typename E, typename G, int C>
