@@ -53,12 +53,16 @@ struct PrefillLayout {
     // elements per chunk and head):
     size_t off_tbmat, off_pmat, off_wmat;  // E, per (chunk, value head)
     size_t off_qmat, off_ktmat;            // E, per (chunk, query/key head)
-    size_t off_sgam, off_delta;            // float [max_chunks][hv][C]
-    size_t off_gammac;                     // float [max_chunks][hv]
+    size_t off_gates;                      // float [max_chunks][hv][gate_record(C)]
     size_t total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Floats per (chunk, value head) gate record: delta = exp(c_C - c_t) at
+// [0, C), scale * gamma_t at [C, 2C), gamma_C at 2C, then 3 floats of
+// padding, so that the record is read as C/2 + 1 aligned 16-byte pieces.
+constexpr int64_t gate_record(int64_t chunk) { return 2 * chunk + 4; }
 
 inline PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
                                     int64_t dk, int64_t chunk, size_t elem_bytes) {
@@ -79,9 +83,7 @@ inline PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int6
     const size_t per_kq = (size_t)L.max_chunks * (size_t)hk * (size_t)(dk * chunk) * elem_bytes;
     L.off_qmat = take(per_kq);
     L.off_ktmat = take(per_kq);
-    L.off_sgam = take((size_t)L.max_chunks * (size_t)hv * (size_t)chunk * sizeof(float));
-    L.off_delta = take((size_t)L.max_chunks * (size_t)hv * (size_t)chunk * sizeof(float));
-    L.off_gammac = take((size_t)L.max_chunks * (size_t)hv * sizeof(float));
+    L.off_gates = take((size_t)L.max_chunks * (size_t)hv * (size_t)gate_record(chunk) * sizeof(float));
     L.total = o;
     return L;
 }

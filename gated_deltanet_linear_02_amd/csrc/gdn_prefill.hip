@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kSchedThreads) void gdn_schedule_kernel(
 // group applies that head's gates and builds the per-head operands of the
 // scan:
 //   Tb = T diag(b),   W = T diag(b gamma) K   (so that U = Tb V - W S0^T),
-//   P,  the gate vectors scale*gamma and delta = exp(c_C - c), and gamma_C,
+//   P,  and the gate record (delta = exp(c_C - c), scale*gamma, gamma_C),
 // with T = (I + A)^-1 by blocks of 16:
 //   diagonal blocks    (I + A_bb)^-1 by forward substitution, one wave each;
 //   blocks below       T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj, one wave per
@@ -164,6 +164,17 @@ template <> struct IsBf16<bf16> { static constexpr bool value = true; };
 // KPL elements per lane for rows 16 rt + l%16.
 template <typename MM> __device__ __forceinline__ size_t frag_off(int f, int lane) {
     return ((size_t)f * 64 + lane) * MM::KPL;
+}
+
+// Tb = T diag(b) and P are lower triangular, so in row tile rt (rows
+// 16 rt .. 16 rt + 15) the contraction blocks kb with kb * KW >= 16 (rt + 1)
+// are zero. The scan reads only blocks kb < tri_read_blocks(rt) of a tile and
+// the preparation kernel writes only those: the row tiles whose nonzero
+// blocks are as few as in row tile 0 skip the rest (C = 64 bf16: tiles 0
+// and 1 read one of two blocks); other tiles read all blocks, zero or not.
+template <typename MC, int C> __host__ __device__ constexpr int tri_read_blocks(int rt) {
+    return (16 * (rt + 1) + MC::KW - 1) / MC::KW == (16 + MC::KW - 1) / MC::KW ? (16 + MC::KW - 1) / MC::KW
+                                                                               : C / MC::KW;
 }
 
 template <typename E, int C, int DK>
@@ -266,8 +277,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
     const int32_t *__restrict__ chunk_seq, const int32_t *__restrict__ chunk_tok0,
     const int32_t *__restrict__ counters,
     E *__restrict__ tbmat, E *__restrict__ pmat, E *__restrict__ wmat, E *__restrict__ qmat,
-    E *__restrict__ ktmat, float *__restrict__ sgam, float *__restrict__ delta, float *__restrict__ gammac,
-    int32_t hk, int32_t hv, float scale)
+    E *__restrict__ ktmat, float *__restrict__ gates, int32_t hk, int32_t hv, float scale)
 {
     typedef PrepSmem<E, C, DK> L;
     typedef Mma<E, DK> MD;  // contractions over keys
@@ -467,9 +477,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
                 sc[lane] = x * kLog2e;
                 sb[lane] = bv;
                 sbg[lane] = bv * gam;
-                sgam[ch * C + lane] = scale * gam;
-                delta[ch * C + lane] = exp2_hw((last - x) * kLog2e);
-                if (lane == C - 1) gammac[ch] = exp2_hw(last * kLog2e);
+                float *rec = gates + ch * (size_t)gate_record(C);
+                rec[lane] = exp2_hw((last - x) * kLog2e);
+                rec[C + lane] = scale * gam;
+                if (lane == C - 1) rec[2 * C] = exp2_hw(last * kLog2e);
             }
         }
         __syncthreads();
@@ -503,6 +514,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
                 if (score_wave) {
 #pragma unroll
                     for (int kb = 0; kb < KBC; ++kb) {
+                        if (kb >= tri_read_blocks<MC, C>(ti)) continue;  // zero, never read
                         typename MC::Frag fr;
 #pragma unroll
                         for (int e = 0; e < MC::KPL; ++e)
@@ -556,9 +568,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
         }
         __syncthreads();
 
-        // Tb = T diag(b) in fragments (blocks above the diagonal are zero)
+        // Tb = T diag(b) in fragments (blocks above the diagonal are zero;
+        // those the scan does not read are not written)
         for (int f = wave; f < NB * KBC; f += 4) {
             const int rt = f / KBC, kb = f - rt * KBC;
+            if (kb >= tri_read_blocks<MC, C>(rt)) continue;
             const int i = 16 * rt + ln;
             typename MC::Frag fr;
 #pragma unroll
@@ -648,7 +662,8 @@ struct ScanSmem {
     static constexpr size_t off_Vt = off_DUt + (size_t)R * LDC * sizeof(E);  // [2][R][LDC] V^T
     static constexpr size_t off_Dl = (off_Vt + 2 * (size_t)R * LDC * sizeof(E) + 15) & ~(size_t)15;  // [2][C] delta
     static constexpr size_t off_Sg = off_Dl + 2 * (size_t)C * sizeof(float);  // [2][C] scale gamma
-    static constexpr size_t bytes = off_Sg + 2 * (size_t)C * sizeof(float);
+    static constexpr size_t off_Gc = off_Sg + 2 * (size_t)C * sizeof(float);  // [2][4] gamma_C (first of 4)
+    static constexpr size_t bytes = off_Gc + 8 * sizeof(float);
 };
 
 template <typename E> struct Vec4;
@@ -676,20 +691,18 @@ struct ScanShape {
 // and rows clamped into range) so that the compiler counts outstanding loads
 // exactly across the loop; rows past the end of a sequence are masked where
 // they are used.
-template <typename E, int C, int DK>
+template <typename E, int C, int DK, int NT>
 struct RStage {
     typedef ScanShape<E, C, DK> S;
     typename S::MD::Frag wf[S::KBD];
-    typename S::MC::Frag tf[S::KBC], ktf[S::NMW][S::KBC];
-    float gc;   // gamma_C
+    typename S::MC::Frag tf[NT], ktf[S::NMW][S::KBC];  // Tb: the NT blocks read (tri_read_blocks)
 
     __device__ __forceinline__ void load(const E *__restrict__ tbmat, const E *__restrict__ wmat,
-                                         const E *__restrict__ ktmat, const float *__restrict__ gammac,
-                                         const ChunkRef &r, int q, int lane) {
+                                         const E *__restrict__ ktmat, const ChunkRef &r, int q, int lane) {
         const int rt = min(q, S::RT - 1);
         const size_t mat0 = r.ch * (size_t)(C * C), w0 = r.ch * (size_t)(C * DK), kq0 = r.kq * (size_t)(C * DK);
 #pragma unroll
-        for (int kb = 0; kb < S::KBC; ++kb)
+        for (int kb = 0; kb < NT; ++kb)
             tf[kb] = *reinterpret_cast<const typename S::MC::Frag *>(tbmat + mat0 + frag_off<typename S::MC>(rt * S::KBC + kb, lane));
 #pragma unroll
         for (int kb = 0; kb < S::KBD; ++kb)
@@ -701,23 +714,16 @@ struct RStage {
             for (int kb = 0; kb < S::KBC; ++kb)
                 ktf[j][kb] = *reinterpret_cast<const typename S::MC::Frag *>(ktmat + kq0 + frag_off<typename S::MC>(mt * S::KBC + kb, lane));
         }
-        // A vector load, so that it completes in order with the stage's
-        // fragments (vmcnt). As a scalar load (the compiler's choice for a
-        // uniform address) it shares lgkmcnt with the LDS reads of the chain,
-        // whose waits then also wait for it.
-        int z;
-        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-        gc = gammac[r.ch + z];
     }
 };
 
 // An output wave's operands for one chunk (and that chunk's V rows, which
 // the wave stages one chunk earlier).
-template <typename E, int C, int DK>
+template <typename E, int C, int DK, int NT>
 struct OStage {
     typedef ScanShape<E, C, DK> S;
     typename S::MD::Frag qf[S::KBD];
-    typename S::MC::Frag pf[S::KBC];
+    typename S::MC::Frag pf[NT];  // P: the NT blocks read (tri_read_blocks)
     typename S::E4 vr;  // fp32: V[16 q + l/4][4 (l%4) ..]
     f32x4 aux = {0.f, 0.f, 0.f, 0.f};  // auxiliary load (see the output role of the scan)
 
@@ -734,7 +740,7 @@ struct OStage {
         for (int kb = 0; kb < S::KBD; ++kb)
             qf[kb] = *reinterpret_cast<const typename S::MD::Frag *>(qmat + kq0 + frag_off<typename S::MD>(rt * S::KBD + kb, lane));
 #pragma unroll
-        for (int kb = 0; kb < S::KBC; ++kb)
+        for (int kb = 0; kb < NT; ++kb)
             pf[kb] = *reinterpret_cast<const typename S::MC::Frag *>(pmat + mat0 + frag_off<typename S::MC>(rt * S::KBC + kb, lane));
     }
 };
@@ -777,7 +783,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
     const int32_t *__restrict__ order,
     const E *__restrict__ tbmat, const E *__restrict__ pmat, const E *__restrict__ wmat,
     const E *__restrict__ qmat, const E *__restrict__ ktmat,
-    const float *__restrict__ sgam, const float *__restrict__ delta, const float *__restrict__ gammac,
+    const float *__restrict__ gates,
     const float *__restrict__ s0, float *__restrict__ sfin, E *__restrict__ out,
     int32_t num_seqs, int32_t hk, int32_t hv)
 {
@@ -786,8 +792,6 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
     typedef typename SH::MD MD;
     typedef typename SH::MC MC;
     typedef typename SH::E4 E4;
-    typedef RStage<E, C, DK> RS;
-    typedef OStage<E, C, DK> OS;
     constexpr int R = kSliceRows;
     constexpr int DV = DK;
     constexpr int NS = DV / R;  // value-row slices per head
@@ -805,6 +809,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
     E *sVt = reinterpret_cast<E *>(smem + L::off_Vt);
     float *sDl = reinterpret_cast<float *>(smem + L::off_Dl);
     float *sSg = reinterpret_cast<float *>(smem + L::off_Sg);
+    float *sGc = reinterpret_cast<float *>(smem + L::off_Gc);
 
     // Workgroup -> (sequence rank, query/key head, value head in group, slice).
     // Dispatch places workgroup b on XCD b % 8; all value heads and slices
@@ -843,7 +848,22 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         return r;
     };
 
-    if (recurrence) {
+    // Each role runs as one of two instantiations, by the number NT of Tb or P
+    // blocks its token tile reads (tri_read_blocks), so that every load count
+    // in its loop is a compile-time constant.
+    constexpr int kNtLo = tri_read_blocks<MC, C>(0);
+    auto by_tile = [&](auto &&role) {
+        if constexpr (kNtLo == KBC) {
+            role(std::integral_constant<int, KBC>());
+        } else {
+            if (tri_read_blocks<MC, C>(min(q, RT - 1)) == kNtLo) role(std::integral_constant<int, kNtLo>());
+            else role(std::integral_constant<int, KBC>());
+        }
+    };
+
+    if (recurrence) by_tile([&](auto ntc) {
+        constexpr int NT = decltype(ntc)::value;
+        typedef RStage<E, C, DK, NT> RS;
         // fp32 master copy of this wave's S^T tiles (key tiles q + 4 j);
         // operand copy (S[value][key]) in LDS.
         f32x4 sacc[NMW];
@@ -866,15 +886,15 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             // MFMAs of different shapes, which must not be chained through
             // one accumulator; two key chains shorten the dependency.
             if (q < RT) {
-                typename MC::Frag vf[KBC];
+                typename MC::Frag vf[NT];
                 typename MD::Frag sf[KBD];
 #pragma unroll
-                for (int kb = 0; kb < KBC; ++kb) vf[kb] = load_frag_p<MC>(sVt + (c & 1) * (R * LDC), LDC, 0, kb, lane);
+                for (int kb = 0; kb < NT; ++kb) vf[kb] = load_frag_p<MC>(sVt + (c & 1) * (R * LDC), LDC, 0, kb, lane);
 #pragma unroll
                 for (int kb = 0; kb < KBD; ++kb) sf[kb] = load_frag_p<MD>(sS, LDK, 0, kb, lane);
                 f32x4 ut = {0.f, 0.f, 0.f, 0.f}, uk0 = {0.f, 0.f, 0.f, 0.f}, uk1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < KBC; ++kb) ut = MC::mma(st.tf[kb], vf[kb], ut);
+                for (int kb = 0; kb < NT; ++kb) ut = MC::mma(st.tf[kb], vf[kb], ut);
 #pragma unroll
                 for (int kb = 0; kb < KBD; ++kb) {
                     if (kb & 1) uk1 = MD::mma(st.wf[kb], sf[kb], uk1);
@@ -893,17 +913,18 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             // The prefetch is issued here rather than at the chunk start: phase 1
             // bounds the chunk through these waves, phase 2 through the output
             // waves, so a load queue that is full costs less here.
-            if constexpr (kThree) fut.load(tbmat, wmat, ktmat, gammac, chunk(min(c + kRStages - 1, nch - 1)), q, lane);
+            if constexpr (kThree) fut.load(tbmat, wmat, ktmat, chunk(min(c + kRStages - 1, nch - 1)), q, lane);
             typename MC::Frag duf[KBC];
 #pragma unroll
             for (int kb = 0; kb < KBC; ++kb) duf[kb] = load_frag_p<MC>(sDUt, LDC, 0, kb, lane);
+            const float gc = sGc[4 * (c & 1)];
 #pragma unroll
             for (int j = 0; j < NMW; ++j) {
                 const int mt = q + 4 * j;
                 if (mt < MT) {
                     f32x4 acc = sacc[j];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[i] *= st.gc;
+                    for (int i = 0; i < 4; ++i) acc[i] *= gc;
 #pragma unroll
                     for (int kb = 0; kb < KBC; ++kb) acc = MC::mma(st.ktf[j][kb], duf[kb], acc);
                     sacc[j] = acc;
@@ -911,7 +932,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                 }
             }
             __syncthreads();
-            if constexpr (!kThree) st.load(tbmat, wmat, ktmat, gammac, chunk(min(c + 1, nch - 1)), q, lane);
+            if constexpr (!kThree) st.load(tbmat, wmat, ktmat, chunk(min(c + 1, nch - 1)), q, lane);
         };
 
         if (nch > 0) {
@@ -919,11 +940,11 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                 RS st[kRStages];
 #pragma unroll
                 for (int i = 0; i + 1 < kRStages; ++i)
-                    st[i].load(tbmat, wmat, ktmat, gammac, chunk(min(i, nch - 1)), q, lane);
+                    st[i].load(tbmat, wmat, ktmat, chunk(min(i, nch - 1)), q, lane);
                 run_pipeline<kRStages>(st, nch, body);
             } else {
                 RS st0;
-                st0.load(tbmat, wmat, ktmat, gammac, chunk(0), q, lane);
+                st0.load(tbmat, wmat, ktmat, chunk(0), q, lane);
                 for (int c = 0; c < nch; ++c) body(st0, st0, st0, c, std::false_type());
             }
         }
@@ -936,11 +957,15 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                     *reinterpret_cast<f32x4 *>(sfin + state0 + (size_t)(col0 + ln) * DK + 16 * mt + 4 * g4) = sacc[j];
             }
         }
-    } else {
+    });
+    else by_tile([&](auto ntc) {
+        constexpr int NT = decltype(ntc)::value;
+        typedef OStage<E, C, DK, NT> OS;
         // Besides its Q and P fragments, each output wave issues one auxiliary
         // 16-byte-per-lane load per chunk (bf16):
-        //   wave 0     the chunk's gate vectors (delta for the recurrence
-        //              waves, scale gamma for the outputs), staged in LDS;
+        //   wave 0     the chunk's gate record (delta and gamma_C for the
+        //              recurrence waves, scale gamma for the outputs),
+        //              staged in LDS;
         //   wave 1     an L2 touch of the chunk kTouchAhead ahead: the 16
         //              workgroups of the query/key head split that chunk's
         //              operands (Q, K^T, and Tb, P, W of each value head of
@@ -952,16 +977,15 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         //              lane), staged in LDS.
         // Memory instructions, not bytes, bound the scan, so these small
         // loads are folded into as few instructions as possible. The fp32
-        // path (one stage) loads V per wave and the gate vectors in every wave.
+        // path (one stage) loads V per wave and the gate record in every wave.
         constexpr int kRunQ = (int)((size_t)C * DK * sizeof(E) / 1024);
         constexpr int kRunM = (int)((size_t)C * C * sizeof(E) / 1024);
         constexpr bool kTouch = kPipelined && (size_t)C * DK * sizeof(E) % 1024 == 0 &&
                                 (size_t)C * C * sizeof(E) % 1024 == 0;
         auto gate_ptr = [&](const ChunkRef &r) {
-            // lanes [0, C/4): delta, 4 tokens each; [C/4, C/2): scale gamma
-            const int l = min(lane, C / 2 - 1);
-            return reinterpret_cast<const f32x4 *>(l < C / 4 ? delta + r.ch * C + 4 * l
-                                                             : sgam + r.ch * C + 4 * (l - C / 4));
+            // the chunk's gate record, 4 floats per lane: lanes [0, C/4)
+            // delta, [C/4, C/2) scale gamma, C/2 gamma_C
+            return reinterpret_cast<const f32x4 *>(gates + r.ch * (size_t)gate_record(C) + 4 * min(lane, C / 2));
         };
         auto touch_ptr = [&](int cc) {
             const size_t kq = (size_t)(c0 + cc) * hk + kh;
@@ -1003,9 +1027,13 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         // (wave 0) and, bf16, the V rows (waves 2, 3) from the auxiliary load;
         // fp32, each wave's V rows.
         auto put_chunk = [&](const OS &st, const E4 &vr, int buf) {
-            if (q == 0 && lane < C / 2) {
-                float *dst = lane < C / 4 ? sDl + buf * C + 4 * lane : sSg + buf * C + 4 * (lane - C / 4);
-                *reinterpret_cast<f32x4 *>(dst) = st.aux;
+            if (q == 0 && lane <= C / 2) {
+                if (lane < C / 2) {
+                    float *dst = lane < C / 4 ? sDl + buf * C + 4 * lane : sSg + buf * C + 4 * (lane - C / 4);
+                    *reinterpret_cast<f32x4 *>(dst) = st.aux;
+                } else {
+                    sGc[4 * buf] = st.aux[0];
+                }
             }
             if constexpr (kPipelined) {
                 if (q >= 2) {
@@ -1068,7 +1096,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             if (q < RT) {
                 f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < KBC; ++kb) o = MC::mma(load_frag_p<MC>(sUt, LDC, 0, kb, lane), st.pf[kb], o);
+                for (int kb = 0; kb < NT; ++kb) o = MC::mma(load_frag_p<MC>(sUt, LDC, 0, kb, lane), st.pf[kb], o);
                 const int row = 16 * q + ln;
                 const float sg = sSg[(c & 1) * C + row];
                 if (row < clen) {
@@ -1094,7 +1122,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                 for (int c = 0; c < nch; ++c) body(st[0], st[0], st[0], c, std::false_type());
             }
         }
-    }
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -1125,9 +1153,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &A, hipStream_t st) {
     E *wmat = reinterpret_cast<E *>(ws + Y.off_wmat);
     E *qmat = reinterpret_cast<E *>(ws + Y.off_qmat);
     E *ktmat = reinterpret_cast<E *>(ws + Y.off_ktmat);
-    float *sgam = reinterpret_cast<float *>(ws + Y.off_sgam);
-    float *delta = reinterpret_cast<float *>(ws + Y.off_delta);
-    float *gammac = reinterpret_cast<float *>(ws + Y.off_gammac);
+    float *gates = reinterpret_cast<float *>(ws + Y.off_gates);
 
     // Up to kFoldMaxSeqs sequences the preparation kernel schedules itself.
     const bool fold = A.num_seqs <= kFoldMaxSeqs;
@@ -1147,7 +1173,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &A, hipStream_t st) {
                       (const E *)A.q, (const E *)A.k, (const G *)A.g, (const G *)A.beta,
                       fold ? A.cu : nullptr, A.num_seqs, (int32_t)A.total_tokens, bounds, seq_chunk0, order,
                       (const int32_t *)chunk_seq, (const int32_t *)chunk_tok0, (const int32_t *)counters,
-                      tbmat, pmat, wmat, qmat, ktmat, sgam, delta, gammac, A.hk, A.hv, A.scale);
+                      tbmat, pmat, wmat, qmat, ktmat, gates, A.hk, A.hv, A.scale);
     if (e != hipSuccess) return e;
 
     typedef ScanSmem<E, C, D> SL;
@@ -1160,8 +1186,8 @@ static hipError_t launch_prefill_t(const PrefillArgs &A, hipStream_t st) {
     return launch_kernel(kScan, scan, dim3((unsigned)grid), dim3(kScanThreads), SL::bytes, st,
                          (const E *)A.v, (const int32_t *)bounds, (const int32_t *)seq_chunk0,
                          (const int32_t *)order, (const E *)tbmat, (const E *)pmat, (const E *)wmat,
-                         (const E *)qmat, (const E *)ktmat, (const float *)sgam, (const float *)delta,
-                         (const float *)gammac, A.s0, A.s_final, (E *)A.out, A.num_seqs, A.hk, A.hv);
+                         (const E *)qmat, (const E *)ktmat, (const float *)gates, A.s0, A.s_final,
+                         (E *)A.out, A.num_seqs, A.hk, A.hv);
 }
 
 template <typename E, typename G, int C>

@@ -56,10 +56,10 @@ def _ws(n=1, T=4096, hk=16, hv=32, d=128, c=64, io=BF16):
 def test_workspace_size(lib):
     w = _ws()
     # per chunk: Tb and P (bf16 C x C) and W (bf16 C x d) per value head, Q
-    # and K^T per query/key head (bf16 C x d), scale*gamma and delta (fp32
-    # per token) and gamma_C (fp32) per value head
+    # and K^T per query/key head (bf16 C x d), and per value head a gate
+    # record of 2C + 4 fp32 (delta and scale*gamma per token, gamma_C, padding)
     chunks = (4096 + 63) // 64 + 1
-    need = chunks * (32 * (2 * 64 * 64 * 2 + 64 * 128 * 2 + 2 * 64 * 4 + 4) + 16 * 2 * 64 * 128 * 2)
+    need = chunks * (32 * (2 * 64 * 64 * 2 + 64 * 128 * 2 + (2 * 64 + 4) * 4) + 16 * 2 * 64 * 128 * 2)
     assert need <= w < need + 64 * 1024
     assert _ws(io=F32) > w
     assert _ws(T=0) > 0
