@@ -304,6 +304,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
     const int group = hv / hk;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g4 = lane >> 4, ln = lane & 15;
+    const size_t ld = (size_t)hk * DK;
+
+    // The inputs of a chunk starting at token tb: its K and Q rows (16 bytes
+    // per thread and pass) and, wave 0, the gate inputs of its tokens for up
+    // to kGatePrefetch value heads of the group. Rows are clamped into
+    // [0, T); rows past the chunk are masked where they are used. All loads
+    // are issued before any is waited for.
+    constexpr int NIT = (C * VPR + 255) / 256;
+    constexpr int kGatePrefetch = 2;
+    Vec16 kr[NIT], qr[NIT];
+    float gx_pre[kGatePrefetch], gb_pre[kGatePrefetch];
+    auto load_inputs = [&](int tb) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int i = min(tid + 256 * it, C * VPR - 1);
+            const int r = i / VPR, cv = i - r * VPR;
+            const size_t src = (size_t)min(tb + r, total_tokens - 1) * ld + (size_t)kh * DK + cv * EPV;
+            kr[it] = ld16(k + src);
+            qr[it] = ld16(q + src);
+        }
+        if (wave == 0) {
+            const size_t t = (size_t)min(tb + lane, total_tokens - 1);
+#pragma unroll
+            for (int hh = 0; hh < kGatePrefetch; ++hh) {
+                const size_t gi = t * hv + kh * group + min(hh, group - 1);
+                gx_pre[hh] = gate_load(gate_g, gi);
+                gb_pre[hh] = gate_load(gate_b, gi);
+            }
+        }
+    };
+    // Most prefills are one sequence from token 0, where chunk ci starts at
+    // token ci * C. The inputs are loaded for that guess before the chunk is
+    // located, so that their latency overlaps the locating; they are loaded
+    // again if the guess turns out wrong.
+    const int t_guess = ci * C;
+    const bool guessed = t_guess < total_tokens;
+    if (guessed) load_inputs(t_guess);
+
     int t0, len;
     if (cu != nullptr) {
         // ---- 0. Locate this chunk (num_seqs <= 256): thread j owns sequence j.
@@ -357,28 +395,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
         len = min(C, bounds[n + 1] - t0);
     }
     const size_t kq0 = ((size_t)ci * hk + kh) * (size_t)(C * DK);
-    const size_t ld = (size_t)hk * DK;
-
-    // Gate inputs of the group's value heads (up to kGatePrefetch of them),
-    // issued now so that their latency hides under the K and Q staging.
-    constexpr int kGatePrefetch = 2;
-    float gx_pre[kGatePrefetch], gb_pre[kGatePrefetch];
-    if (wave == 0) {
-        const bool valid = lane < len;
-#pragma unroll
-        for (int hh = 0; hh < kGatePrefetch; ++hh) {
-            const size_t gi = (size_t)(t0 + (valid ? lane : 0)) * hv + kh * group + min(hh, group - 1);
-            gx_pre[hh] = gate_load(gate_g, gi);
-            gb_pre[hh] = gate_load(gate_b, gi);
-        }
-    }
+    if (!guessed || t0 != t_guess) load_inputs(t0);
 
     // ---- 1. K and Q rows into LDS (zero past the end of the sequence)
-    for (int i = tid; i < C * VPR; i += 256) {
-        const int r = i / VPR, cv = i - r * VPR;
-        const size_t src = (size_t)(t0 + r) * ld + (size_t)kh * DK + cv * EPV;
-        st16(sK + r * LDK + cv * EPV, r < len ? ld16(k + src) : zero16());
-        st16(sQ + r * LDK + cv * EPV, r < len ? ld16(q + src) : zero16());
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int i = tid + 256 * it;
+        if (i < C * VPR) {
+            const int r = i / VPR, cv = i - r * VPR;
+            st16(sK + r * LDK + cv * EPV, r < len ? kr[it] : zero16());
+            st16(sQ + r * LDK + cv * EPV, r < len ? qr[it] : zero16());
+        }
     }
     __syncthreads();
 
