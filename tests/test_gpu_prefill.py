@@ -267,3 +267,38 @@ def test_malformed_cu_seqlens_is_clamped():
     o_ref, f_ref = oracle_ref(inp)
     assert rel_err(to_f64(o)[:50], o_ref[:50]) <= TOL_F32
     assert rel_err(to_f64(f)[0], f_ref[0]) <= TOL_F32
+
+
+def test_all_sequences_empty():
+    """T = 0: every sequence is empty, so no chunk exists. The preparation
+    kernel must not read q or k (there are none), and each final state is its
+    initial state."""
+    inp = gs.make_inputs([0, 0, 0], 2, 4, 32, 32, seed=41, io_dtype="bf16", init_state=True)
+    note("prefill with every sequence empty")
+    o, f = run_prefill(inp, chunk=64)
+    assert o.shape[0] == 0
+    assert np.array_equal(to_f64(f), inp.initial_state.astype(np.float64))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_first_sequence_not_at_token_zero(io):
+    """cu_seqlens[0] > 0: the packed buffer holds tokens before the first
+    sequence. No chunk then starts at chunk_index * C, so the preparation
+    kernel's early loads (made for that common layout) are all discarded and
+    reloaded; results must match the oracle on the sequences proper."""
+    inp = gs.make_inputs([5, 70, 33], 2, 4, 32, 32, seed=43, io_dtype=io, gate_dtype="f32",
+                         init_state=True)
+    d = device_inputs(inp)
+    cu = d["cu_seqlens"][1:].contiguous()  # sequences 1 and 2 only; tokens 0..4 are not in any
+    note(f"prefill with cu_seqlens[0] = 5 io={io}")
+    out_dtype = torch.bfloat16 if io == "bf16" else torch.float32
+    out = torch.full((inp.total_tokens, 4, 32), float("nan"), dtype=out_dtype, device="cuda")
+    o, f = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, chunk=16,
+                       initial_state=d["initial_state"][1:].contiguous(), out=out)
+    torch.cuda.synchronize()
+    o_ref, f_ref = oracle_ref(inp)
+    eo = rel_err(to_f64(o)[5:], o_ref[5:])
+    ef = rel_err(to_f64(f), f_ref[1:])
+    print(f"[parity] cu0=5 io={io} out_err={eo:.3e} state_err={ef:.3e}", flush=True)
+    assert eo <= tol(io) and ef <= tol(io)
+    assert torch.isnan(o[:5].float()).all(), "tokens before the first sequence must not be written"
