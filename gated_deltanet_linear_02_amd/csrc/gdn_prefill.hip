@@ -662,16 +662,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
 //                           U and diag(delta) U to LDS;
 //                           phase 2: S^T = gamma_C S0^T + K^T diag(delta) U on
 //                           key tiles q, q+4, .., operand copy of S to LDS;
-//   output waves (4-7)      phase 1: O1^T = S0 Q^T on token tile q;
+//   output waves (4-7)      phase 1: the next chunk's gate record and V rows
+//                           to LDS; O1^T = S0 Q^T on token tile q;
 //                           phase 2: O^T = O1^T diag(scale gamma) + U^T P^T,
-//                           stored from registers; the next chunk's V rows to
-//                           LDS.
+//                           stored from registers.
 // One barrier ends each phase. Only the recurrence waves are on the chain
 // from one chunk's state to the next; the output waves' work fills the other
-// wave slot of each SIMD. Every A operand (Tb, W, K^T; Q, P) and the gate
-// vectors are single contiguous loads from the workspace, issued three
-// (recurrence) or four (output) chunks ahead into register stages used round
-// robin (bf16; fp32 fragments are four times larger and use one stage).
+// wave slot of each SIMD. Every A operand (Tb, W, K^T; Q, P) is read from the
+// workspace as contiguous 1 KB fragments and the gate record with one load,
+// issued three (recurrence) or four (output) chunks ahead into register
+// stages used round robin (bf16; fp32 fragments are four times larger and
+// use one stage). The chunk step is about as long as the CU takes to accept
+// its vector-memory instructions, so their number per chunk is kept small.
 
 constexpr int kSliceRows = 16;
 constexpr int kScanThreads = 512;

@@ -138,9 +138,11 @@ int32_t gdn_decode_step(const void *q, const void *k, const void *v,
 /*
  * Per-kernel timing (a profiling aid, not needed for computation).
  *
- * gdn_timing_start(max_launches) makes the library bracket each of its next
- * kernel launches (up to max_launches) with a pair of HIP events recorded on
- * the stream the kernel is launched on. gdn_timing_stop() waits for those
+ * gdn_timing_start(max_launches) makes the library time each of its next
+ * kernel launches (up to max_launches) with a pair of HIP events that the
+ * kernel's own dispatch on its stream stamps with the kernel's start and end
+ * (hipExtLaunchKernelGGL), so that they cover the kernel alone, as a kernel
+ * trace does. gdn_timing_stop() waits for those
  * events, writes for each kernel kind k < n_kinds the number of launches
  * timed (counts[k]) and their summed duration in milliseconds (total_ms[k]),
  * releases the events and stops timing. Kinds: 0 = varlen schedule,
