@@ -241,6 +241,67 @@ def cpu_baseline(threads: int):
     }
 
 
+# Short prefills: (sequences, tokens each). One sequence around the crossover,
+# and multi-token steps over a decode-sized batch.
+SHORT_SHAPES = ((1, 16), (1, 48), (1, 64), (1, 128), (8, 4), (64, 1), (64, 4), (64, 16))
+
+
+def short_prefill_sweep(dev, copies, steps):
+    """Token-by-token (chunk 1) vs chunked (chunk 64) prefill on short
+    prompts and multi-token steps, HK=16, HV=32, d=128, bf16, nonzero initial
+    states; one JSON line per shape. The token scan moves the fp32 state
+    once in and once out like a decode step, so its rate is also given
+    against the HBM peak (algorithmic bytes / kernel time)."""
+    import torch
+    import gdn_synth as gs
+    import gated_deltanet_linear_02_amd as gdn
+    for N, k in SHORT_SHAPES:
+        T = N * k
+        inp = gs.make_inputs([k] * N, HK, HV, D, D, seed=gs.SEED_BASE + 300 + T, io_dtype="bf16",
+                             gate_dtype="bf16", init_state=True)
+        sets = []
+        for _ in range(copies):
+            d = device_inputs(inp, dev)
+            d["s0"] = torch.from_numpy(inp.initial_state).to(dev)
+            d["out"] = torch.empty((T, HV, D), dtype=torch.bfloat16, device=dev)
+            d["fin"] = torch.empty((N, HV, D, D), dtype=torch.float32, device=dev)
+            d["ws"] = torch.empty(gdn.prefill_workspace_size(N, T, HK, HV, D, D, CHUNK, torch.bfloat16),
+                                  dtype=torch.uint8, device=dev)
+            sets.append(d)
+        res = {}
+        for c in (1, CHUNK):
+            def run(d):
+                gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=c,
+                            initial_state=d["s0"], final_state=d["fin"], out=d["out"], workspace=d["ws"])
+            for i in range(3):
+                run(sets[i % copies])
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(steps):
+                run(sets[i % copies])
+            e1.record()
+            torch.cuda.synchronize()
+            res[c] = e0.elapsed_time(e1) / steps
+            if c == 1:
+                gdn.timing_start(steps)
+                for i in range(steps):
+                    run(sets[i % copies])
+                res["kernel"] = gdn.timing_stop()["token_scan"]["mean_ms"]
+        state_bytes = N * HV * D * D * 4 * 2
+        io_bytes = T * (2 * HK * D + 2 * HV * D) * 2 + T * HV * 2 * 2
+        gbs = (state_bytes + io_bytes) / (res["kernel"] * 1e-3) / 1e9
+        auto = "token_scan" if (T <= 64 or T <= 16 * N) else "chunked"
+        print(json.dumps({
+            "mode": "short-prefill", "num_seqs": N, "tokens_per_seq": k, "total_tokens": T,
+            "token_scan_ms": res[1], "chunked_ms": res[CHUNK], "chunk0_picks": auto,
+            "token_scan_speedup": res[CHUNK] / res[1],
+            "token_scan_kernel_ms": res["kernel"], "token_scan_gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+            "dtype": "bf16", "data": "synthetic", "buffer_copies": copies,
+            "config": {"workload": f"{N} sequence(s) x {k} tokens, HK={HK}, HV={HV}, d={D}"},
+        }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,6 +309,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="buffer sets rotated through (cold caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--short-prefill", action="store_true",
+                    help="instead of the main line: token-by-token vs chunked prefill on short prompts "
+                         "and multi-token steps, one JSON line per shape")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, run 3 device-to-device copies of this many MiB "
                          "(the known-size reference for HBM byte counters)")
@@ -274,6 +338,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.short_prefill:
+        short_prefill_sweep(dev, args.copies, min(args.steps, 30))
+        return
     print("[bench] generating inputs", file=sys.stderr, flush=True)
 
     pre = gs.workload("prefill")

@@ -33,7 +33,7 @@ _lib = None
 _lock = threading.Lock()
 
 GDN_BF16, GDN_F32 = 0, 1
-KERNEL_KINDS = ("schedule", "prep", "scan", "decode")
+KERNEL_KINDS = ("schedule", "prep", "scan", "decode", "token_scan")
 
 STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
@@ -122,15 +122,17 @@ def prefill_workspace_size(num_seqs: int, total_tokens: int, hk: int, hv: int, d
 
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
-            cu_seqlens: torch.Tensor, *, chunk: int = 64, scale: float = 1.0,
+            cu_seqlens: torch.Tensor, *, chunk: int = 0, scale: float = 1.0,
             initial_state: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
             write_final_state: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunked prefill over packed sequences (``gdn_prefill``).
+    """Prefill over packed sequences (``gdn_prefill``).
 
     q, k [T, hk, dk]; v [T, hv, dv] (bf16 or fp32, one dtype); g, beta [T, hv]
     (bf16 or fp32); cu_seqlens int32 [N + 1] on the device; states fp32
     [N, hv, dv, dk]. ``final_state`` may be ``initial_state`` (in place).
+    ``chunk``: 16, 32 or 64 (chunked), 1 (token by token) or 0 (token by
+    token when T <= max(64, 16 N), else chunks of 64).
     Missing out / final_state / workspace are allocated with torch.
     """
     T, hk, dk = q.shape

@@ -44,7 +44,13 @@ TimingEvents timing_claim(KernelKind kind) {
 // ----------------------------------------------------------------- checks
 
 static bool valid_head(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
-static bool valid_chunk(int32_t c) { return c == 16 || c == 32 || c == 64; }
+static bool valid_chunk(int32_t c) { return c == 0 || c == 1 || c == 16 || c == 32 || c == 64; }
+
+// The chunk size gdn_prefill uses: 1 (token by token) or 16, 32, 64.
+static int32_t effective_chunk(int32_t chunk, int32_t num_seqs, int64_t total_tokens) {
+    if (chunk != 0) return chunk;
+    return prefer_token_scan(num_seqs, total_tokens) ? 1 : 64;
+}
 static bool valid_dtype(int32_t t) { return t == GDN_BF16 || t == GDN_F32; }
 static size_t dtype_bytes(int32_t t) { return t == GDN_BF16 ? 2 : 4; }
 
@@ -89,17 +95,31 @@ static int32_t check_prefill_shape(int32_t num_seqs, int64_t total_tokens, int32
     if (!valid_head(dk) || dv != dk || !valid_chunk(chunk) || !valid_dtype(io_dtype) ||
         !valid_dtype(gate_dtype) || hk > 65535)
         return GDN_ERR_UNSUPPORTED;
-    const PrefillLayout L = prefill_layout(num_seqs, total_tokens, hk, hv, dk, chunk, dtype_bytes(io_dtype));
+    if (effective_chunk(chunk, num_seqs, total_tokens) == 1) {
+        // token scan: one workgroup per (sequence, value head, row slice)
+        return (int64_t)num_seqs * hv * dv > INT32_MAX ? GDN_ERR_UNSUPPORTED : GDN_OK;
+    }
+    const PrefillLayout L = prefill_layout(num_seqs, total_tokens, hk, hv, dk,
+                                           effective_chunk(chunk, num_seqs, total_tokens), dtype_bytes(io_dtype));
     const int64_t scan_grid = (((int64_t)num_seqs * hk + 7) / 8) * (hv / hk) * (dv / 16) * 8;
     if (scan_grid > INT32_MAX || L.max_chunks > INT32_MAX) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
+}
+
+// Workspace bytes of the method gdn_prefill uses (the token scan needs none;
+// 256 are reported so that a size of 0 keeps meaning "rejected").
+static size_t prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
+                                      int32_t dk, int32_t chunk, int32_t io_dtype) {
+    const int32_t c = effective_chunk(chunk, num_seqs, total_tokens);
+    if (c == 1) return 256;
+    return prefill_layout(num_seqs, total_tokens, hk, hv, dk, c, dtype_bytes(io_dtype)).total;
 }
 
 size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
                                   int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype) {
     if (check_prefill_shape(num_seqs, total_tokens, hk, hv, dk, dv, chunk, io_dtype, GDN_F32) != GDN_OK)
         return 0;
-    return prefill_layout(num_seqs, total_tokens, hk, hv, dk, chunk, dtype_bytes(io_dtype)).total;
+    return prefill_workspace_bytes(num_seqs, total_tokens, hk, hv, dk, chunk, io_dtype);
 }
 
 int32_t gdn_prefill(const void *q, const void *k, const void *v, const void *g, const void *beta,
@@ -114,8 +134,10 @@ int32_t gdn_prefill(const void *q, const void *k, const void *v, const void *g, 
     if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL_ARG;
 
     const size_t eb = dtype_bytes(io_dtype), gb = dtype_bytes(gate_dtype);
-    const PrefillLayout L = prefill_layout(num_seqs, total_tokens, hk, hv, dk, chunk, eb);
-    if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    const int32_t c = effective_chunk(chunk, num_seqs, total_tokens);
+    // The token scan uses no workspace: its buffer is not checked or touched.
+    const PrefillLayout L = c == 1 ? PrefillLayout{} : prefill_layout(num_seqs, total_tokens, hk, hv, dk, c, eb);
+    if (c != 1 && (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255)))
         return GDN_ERR_WORKSPACE;
 
     const size_t T = (size_t)total_tokens;
@@ -141,12 +163,13 @@ int32_t gdn_prefill(const void *q, const void *k, const void *v, const void *g, 
     PrefillArgs A;
     A.q = q; A.k = k; A.v = v; A.g = g; A.beta = beta;
     A.cu = cu_seqlens; A.num_seqs = num_seqs; A.total_tokens = total_tokens;
-    A.hk = hk; A.hv = hv; A.d = dk; A.chunk = chunk; A.scale = scale;
+    A.hk = hk; A.hv = hv; A.d = dk; A.chunk = c; A.scale = scale;
     A.io_bf16 = io_dtype == GDN_BF16; A.gate_bf16 = gate_dtype == GDN_BF16;
     A.s0 = initial_state; A.s_final = final_state; A.out = out;
     A.ws = static_cast<char *>(workspace); A.lay = L;
     try {
-        return launch_prefill(A, static_cast<hipStream_t>(stream)) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        return (c == 1 ? launch_token_scan(A, st) : launch_prefill(A, st)) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
     } catch (...) {
         return GDN_ERR_HIP;
     }

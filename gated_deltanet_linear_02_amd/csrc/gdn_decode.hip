@@ -151,4 +151,266 @@ hipError_t launch_decode(const DecodeArgs &A, hipStream_t st) {
     return A.gate_bf16 ? launch_decode_d<float, bf16>(A, st) : launch_decode_d<float, float>(A, st);
 }
 
+// ---------------------------------------------------------------------------
+// Token-by-token prefill (chunk = 1)
+// ---------------------------------------------------------------------------
+//
+// The recurrence evaluated one token at a time, the first of the two
+// evaluations the pages name ("Qwen cree trois formes de charges de travail
+// distinctes"): it exposes no matrix products, but it has no fixed costs
+// either (no preparation pass, no workspace), so short prompts and
+// multi-token steps finish sooner than through the chunked form. A workgroup
+// holds ROWS rows of one (sequence, value head) state in registers and
+// applies the decode update for every token of the sequence in order,
+// writing each token's output and, at the end, the final state. Row sums use
+// DPP within the LPR lanes of a row. Vector-memory instructions bound it, as
+// they bound the chunked scan: per token a wave loads only its 16-byte pieces
+// of k and q (kNext tokens ahead); gates and v come in one load per lane for
+// 64 tokens at a time and are broadcast with readlane.
+
+// Sum of x over the LPR consecutive lanes of a row (LPR = 2, 4, 8 or 16; rows
+// aligned to LPR). Each step adds the value of a partner lane from a group
+// whose lanes all hold the same partial sum: quads by xor 1 and xor 2, then
+// half-rows by mirroring within 8 lanes, then rows by mirroring within 16.
+template <int Ctrl> __device__ __forceinline__ float dpp_mov(float y) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, y), Ctrl, 0xf, 0xf, false));
+}
+template <int LPR> __device__ __forceinline__ float row_sum(float x) {
+    static_assert(LPR == 2 || LPR == 4 || LPR == 8 || LPR == 16, "row width");
+    x += dpp_mov<0xB1>(x);                         // quad_perm [1, 0, 3, 2]: lane ^ 1
+    if constexpr (LPR >= 4) x += dpp_mov<0x4E>(x);   // quad_perm [2, 3, 0, 1]: lane ^ 2
+    if constexpr (LPR >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror: lane i <- 7 - i
+    if constexpr (LPR >= 16) x += dpp_mov<0x140>(x); // row_mirror: lane i <- 15 - i
+    return x;
+}
+
+// A lane's 8 consecutive elements of one token's k or q, as loaded.
+template <typename E> struct Vec8;
+template <> struct Vec8<bf16> {
+    bf16x8 x;
+    __device__ __forceinline__ void load(const bf16 *p) { x = *reinterpret_cast<const bf16x8 *>(p); }
+    __device__ __forceinline__ float operator[](int i) const { return static_cast<float>(x[i]); }
+};
+template <> struct Vec8<float> {
+    f32x4 x[2];
+    __device__ __forceinline__ void load(const float *p) {
+        x[0] = *reinterpret_cast<const f32x4 *>(p);
+        x[1] = *reinterpret_cast<const f32x4 *>(p + 4);
+    }
+    __device__ __forceinline__ float operator[](int i) const { return x[i >> 2][i & 3]; }
+};
+
+// A workgroup covers ROWS rows of one (sequence, value head) state; a row's
+// DK elements are spread over LPR = DK / 8 consecutive lanes, 8 consecutive
+// elements each, so that a lane's part of k or q is one 16-byte load (bf16).
+template <int DK, int DV> struct TokenScanShape {
+    static constexpr int LPR = DK / 8;
+    static constexpr int ROWS = 256 / LPR;
+    static constexpr int RPW = 64 / LPR;  // rows per wave
+    static constexpr int SLICES = (DV + ROWS - 1) / ROWS;
+};
+
+template <typename E, typename G, int DK, int DV>
+__global__ __launch_bounds__(256) void gdn_token_scan_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
+    const G *__restrict__ gate_g, const G *__restrict__ gate_b,
+    const int32_t *__restrict__ cu, int32_t num_seqs, int32_t total_tokens,
+    const float *__restrict__ s0, float *__restrict__ sfin, E *__restrict__ out,
+    int32_t hk, int32_t hv, float scale)
+{
+    typedef TokenScanShape<DK, DV> SH;
+    constexpr int LPR = SH::LPR, ROWS = SH::ROWS, RPW = SH::RPW, SLICES = SH::SLICES;
+    constexpr int kNext = 3;  // tokens whose k and q are in flight ahead of the one applied
+
+    const int bhs = blockIdx.x;
+    const int bh = bhs / SLICES;
+    const int row0 = (bhs - bh * SLICES) * ROWS;
+    const int n = bh / hv;
+    const int h = bh - n * hv;
+    const int kh = h / (hv / hk);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int lr = tid % LPR;
+    const int row = row0 + tid / LPR;
+    const int wrow0 = row0 + (tid >> 6) * RPW;  // first row of this wave
+    const bool live = row < DV;
+
+    // The state rows first: they do not depend on the sequence's bounds, so
+    // their latency overlaps that of cu_seqlens.
+    const size_t state0 = ((size_t)n * hv + h) * (size_t)(DV * DK) + (size_t)row * DK + 8 * lr;
+    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if (s0 && live) {
+        s[0] = *reinterpret_cast<const f32x4 *>(s0 + state0);
+        s[1] = *reinterpret_cast<const f32x4 *>(s0 + state0 + 4);
+    }
+
+    // Sequence n's tokens [lo, hi): offsets clamped into [0, T] and made
+    // non-decreasing, as on the chunked path. Each wave reduces the maxima
+    // itself (strided over the lanes, then a butterfly).
+    auto clampT = [&](int x) { return min(max(x, 0), total_tokens); };
+    const int b0 = clampT(cu[0]);
+    int hi = b0, lo = b0;
+    for (int j = lane; j <= n; j += 64) {
+        const int e = clampT(cu[j + 1]);
+        hi = max(hi, e);
+        if (j < n) lo = max(lo, e);
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        hi = max(hi, __shfl_xor(hi, off));
+        lo = max(lo, __shfl_xor(lo, off));
+    }
+    // uniform across the wave; saying so keeps the token loop's branches scalar
+    hi = __builtin_amdgcn_readfirstlane(hi);
+    lo = __builtin_amdgcn_readfirstlane(lo);
+
+    // Per block of 64 tokens, lane l loads token tb + l's gates and, for each
+    // of the wave's RPW rows, its v; a token's values are then read with
+    // readlane. Loads are unconditional (tokens clamped into [lo, hi)) so that
+    // the compiler counts outstanding loads exactly.
+    struct Block {
+        G g, b;
+        E vr[RPW];
+    };
+    auto load_block = [&](Block &bl, int tb) {
+        const int t = min(tb + lane, hi - 1);
+        bl.g = gate_g[(size_t)t * hv + h];
+        bl.b = gate_b[(size_t)t * hv + h];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) bl.vr[r] = v[((size_t)t * hv + h) * DV + min(wrow0 + r, DV - 1)];
+    };
+    auto lane_f = [](float x, int i) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), i));
+    };
+    const int myr = lane / LPR;  // this lane's row within the wave
+
+    struct KQ {
+        Vec8<E> k, q;
+    };
+    auto load_kq = [&](KQ &x, int t) {
+        const size_t tk = ((size_t)t * hk + kh) * DK + 8 * lr;
+        x.k.load(k + tk);
+        x.q.load(q + tk);
+    };
+    auto apply = [&](const KQ &x, float a, float beta, float vv, int t) {
+        float kk[8], qq[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kk[e] = x.k[e];
+            qq[e] = x.q[e];
+        }
+        float kq = 0.f, sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kq += kk[e] * qq[e];
+            sk += s[e >> 2][e & 3] * kk[e];
+            sq += s[e >> 2][e & 3] * qq[e];
+        }
+        kq = row_sum<LPR>(kq);
+        sk = row_sum<LPR>(sk);
+        sq = row_sum<LPR>(sq);
+        const float u = beta * (vv - a * sk);
+        if (live && lr == 0) out[((size_t)t * hv + h) * DV + row] = from_f32<E>(scale * (a * sq + kq * u));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e >> 2][e & 3] = a * s[e >> 2][e & 3] + u * kk[e];
+    };
+
+    // Sequences of up to kShort tokens (multi-token steps): each token's
+    // inputs loaded directly, all before the first is applied, with a load
+    // count fixed per length; the 64-token blocks and the prefetch ring would
+    // load mostly duplicates here.
+    constexpr int kShort = 4;
+    auto short_run = [&](auto lc) {
+        constexpr int L = decltype(lc)::value;
+        KQ in[L];
+        float ga[L], gb[L], gv[L];
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            const int t = lo + i;
+            load_kq(in[i], t);
+            ga[i] = static_cast<float>(gate_g[(size_t)t * hv + h]);
+            gb[i] = static_cast<float>(gate_b[(size_t)t * hv + h]);
+            gv[i] = static_cast<float>(v[((size_t)t * hv + h) * DV + min(row, DV - 1)]);
+        }
+#pragma unroll
+        for (int i = 0; i < L; ++i) apply(in[i], expf(ga[i]), gb[i], gv[i], lo + i);
+    };
+    const int len = hi - lo;
+    if (len > 0 && len <= kShort) {
+        if (len == 1) short_run(std::integral_constant<int, 1>());
+        else if (len == 2) short_run(std::integral_constant<int, 2>());
+        else if (len == 3) short_run(std::integral_constant<int, 3>());
+        else short_run(std::integral_constant<int, 4>());
+    } else if (len > kShort) {
+        constexpr int R = kNext + 1;
+        KQ in[R];
+        Block cur, nxt;
+        load_block(cur, lo);
+        __builtin_amdgcn_sched_barrier(0);
+        // In stage order: the loop's waits assume stage 0 was issued first.
+#pragma unroll
+        for (int i = 0; i < kNext; ++i) {
+            load_kq(in[i], min(lo + i, hi - 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int tb = lo; tb < hi; tb += 64) {
+            load_block(nxt, min(tb + 64, hi - 1));
+            // this block's gates and v as floats, per lane
+            float ga = 0.f, gb = 0.f, gv[RPW];
+            ga = expf(static_cast<float>(cur.g));
+            gb = static_cast<float>(cur.b);
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) gv[r] = static_cast<float>(cur.vr[r]);
+            // 64 tokens (16 groups of R = 4), stage u % R holding token t + u
+            for (int t = tb; t < min(tb + 64, hi); t += R) {
+#pragma unroll
+                for (int u = 0; u < R; ++u) {
+                    load_kq(in[(u + kNext) % R], min(t + u + kNext, hi - 1));
+                    if (t + u < hi) {
+                        const int i = t + u - tb;
+                        float vv = lane_f(gv[0], i);
+#pragma unroll
+                        for (int r = 1; r < RPW; ++r) {
+                            const float vr = lane_f(gv[r], i);
+                            vv = myr == r ? vr : vv;
+                        }
+                        apply(in[u], lane_f(ga, i), lane_f(gb, i), vv, t + u);
+                    }
+                }
+            }
+            cur = nxt;
+        }
+    }
+
+    if (sfin && live) {
+        *reinterpret_cast<f32x4 *>(sfin + state0) = s[0];
+        *reinterpret_cast<f32x4 *>(sfin + state0 + 4) = s[1];
+    }
+}
+
+template <typename E, typename G, int D>
+static hipError_t launch_token_scan_t(const PrefillArgs &A, hipStream_t st) {
+    const dim3 grid((unsigned)A.num_seqs * (unsigned)A.hv * (unsigned)TokenScanShape<D, D>::SLICES), block(256);
+    return launch_kernel(kTokenScan, gdn_token_scan_kernel<E, G, D, D>, grid, block, 0, st,
+                         (const E *)A.q, (const E *)A.k, (const E *)A.v, (const G *)A.g, (const G *)A.beta,
+                         A.cu, A.num_seqs, (int32_t)A.total_tokens, A.s0, A.s_final, (E *)A.out,
+                         A.hk, A.hv, A.scale);
+}
+
+template <typename E, typename G>
+static hipError_t launch_token_scan_d(const PrefillArgs &A, hipStream_t st) {
+    switch (A.d) {
+    case 16: return launch_token_scan_t<E, G, 16>(A, st);
+    case 32: return launch_token_scan_t<E, G, 32>(A, st);
+    case 64: return launch_token_scan_t<E, G, 64>(A, st);
+    case 128: return launch_token_scan_t<E, G, 128>(A, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_token_scan(const PrefillArgs &A, hipStream_t st) {
+    if (A.io_bf16)
+        return A.gate_bf16 ? launch_token_scan_d<bf16, bf16>(A, st) : launch_token_scan_d<bf16, float>(A, st);
+    return A.gate_bf16 ? launch_token_scan_d<float, bf16>(A, st) : launch_token_scan_d<float, float>(A, st);
+}
+
 }  // namespace gdn

@@ -9,7 +9,7 @@
 
 namespace gdn {
 
-enum KernelKind { kSchedule = 0, kPrep = 1, kScan = 2, kDecode = 3, kKinds = 4 };
+enum KernelKind { kSchedule = 0, kPrep = 1, kScan = 2, kDecode = 3, kTokenScan = 4, kKinds = 5 };
 
 // Per-kernel timing (see gdn_timing_start in gdn.h): while it is active,
 // each launch claims a pair of events that the dispatch itself stamps with
@@ -103,6 +103,22 @@ struct PrefillArgs {
     PrefillLayout lay;
 };
 
+// Chunked prefill (chunk 16, 32 or 64): preparation and scan kernels.
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st);
+// Token-by-token prefill (chunk 1): one kernel, no workspace.
+hipError_t launch_token_scan(const PrefillArgs &a, hipStream_t st);
+
+// gdn_prefill with chunk 0 evaluates token by token when
+// total_tokens <= max(kTokenScanTokens, kTokenScanPerSeq * num_seqs), else in
+// chunks of 64. Measured at HK=16, HV=32, d=128: one sequence breaks even at
+// about 56 tokens, while 64 sequences of 1 to 8 tokens run 2.3 to 4 times
+// faster token by token (the chunked path's fixed cost per sequence
+// dominates). The host does not know the lengths; even one sequence holding
+// all 16 N tokens stays within the chunked path's time.
+constexpr int64_t kTokenScanTokens = 64;
+constexpr int64_t kTokenScanPerSeq = 16;
+inline bool prefer_token_scan(int64_t num_seqs, int64_t total_tokens) {
+    return total_tokens <= kTokenScanTokens || total_tokens <= kTokenScanPerSeq * num_seqs;
+}
 
 }  // namespace gdn

@@ -92,8 +92,13 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
  *              out-of-bounds access (its results are then unspecified).
  *              Zero-length sequences are allowed: their final state equals
  *              their initial state.
- * chunk        tokens per chunk: 16, 32 or 64. The result does not depend on
- *              it beyond rounding.
+ * chunk        how the recurrence is evaluated. 16, 32 or 64: in chunks of that
+ *              many tokens (the WY form: a preparation kernel, then the
+ *              chunk-recurrent scan). 1: token by token, the state rows held
+ *              in registers (one kernel, no workspace), which is faster for
+ *              short prompts and multi-token steps. 0: 1 when total_tokens
+ *              <= max(64, 16 * num_seqs), else 64. The result does not depend
+ *              on it beyond rounding.
  * dk, dv       16, 32, 64 or 128 each.
  * scale        multiplies every output (1.0 for the plain rule).
  * initial_state  fp32 [N][hv][dv][dk], or NULL for zero states.
@@ -104,7 +109,8 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
  * workspace    device scratch of at least gdn_prefill_workspace_size(...)
  *              bytes, 256-byte aligned; contents need not be initialised and
  *              are meaningless afterwards. Calls on different streams need
- *              different workspaces.
+ *              different workspaces. Token by token (chunk 1, or chunk 0
+ *              choosing it) uses none; it may then be NULL.
  */
 int32_t gdn_prefill(const void *q, const void *k, const void *v,
                     const void *g, const void *beta,
@@ -146,10 +152,11 @@ int32_t gdn_decode_step(const void *q, const void *k, const void *v,
  * events, writes for each kernel kind k < n_kinds the number of launches
  * timed (counts[k]) and their summed duration in milliseconds (total_ms[k]),
  * releases the events and stops timing. Kinds: 0 = varlen schedule,
- * 1 = chunk preparation, 2 = chunk-recurrent scan, 3 = decode step.
+ * 1 = chunk preparation, 2 = chunk-recurrent scan, 3 = decode step,
+ * 4 = token-by-token prefill.
  * Not thread-safe with concurrent gdn_* calls from other host threads.
  */
-#define GDN_KERNEL_KINDS 4
+#define GDN_KERNEL_KINDS 5
 int32_t gdn_timing_start(int32_t max_launches);
 int32_t gdn_timing_stop(int32_t *counts, float *total_ms, int32_t n_kinds);
 

@@ -68,6 +68,13 @@ def test_workspace_size(lib):
     assert _ws(d=96) == 0
     assert _ws(c=48) == 0
     assert _ws(n=0) == 0
+    # token by token (chunk 1) needs no workspace; a nonzero size still means
+    # "accepted". Chunk 0 picks it when T <= max(64, 16 N), chunks of 64 above.
+    assert _ws(c=1) == 256 and _ws(c=1, T=1 << 20) == 256
+    assert _ws(c=0, T=64) == 256 and _ws(c=0, n=64, T=1024) == 256
+    assert _ws(c=0, T=65) == _ws(c=64, T=65) > 256
+    assert _ws(c=0) == w
+    assert _ws(c=2) == 0 and _ws(c=-1) == 0
 
 
 FAKE = 0x7F0000000000
@@ -103,6 +110,8 @@ def test_prefill_argument_checks(lib):
     assert _prefill(lib, dk=96, dv=96) == UNSUPPORTED
     assert _prefill(lib, dk=64, dv=128) == UNSUPPORTED
     assert _prefill(lib, chunk=128) == UNSUPPORTED
+    assert _prefill(lib, chunk=8) == UNSUPPORTED
+    assert _prefill(lib, chunk=-1) == UNSUPPORTED
     assert _prefill(lib, io=7) == UNSUPPORTED
     assert _prefill(lib, gate=2) == UNSUPPORTED
     assert _prefill(lib, ws=None) == WORKSPACE
