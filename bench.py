@@ -88,7 +88,7 @@ def measured_traffic(kernel: str):
 
 
 KERNELS = {"schedule": "gdn_schedule_kernel", "prep": "gdn_prep_kernel", "scan": "gdn_scan_kernel",
-           "decode": "gdn_decode_kernel"}
+           "decode": "gdn_decode_kernel", "token_scan": "gdn_token_scan_kernel"}
 
 
 def _short_kernel(name: str) -> str:
@@ -196,6 +196,50 @@ def summarize_profiles(stats_dir: str, fetch_dir: str, write_dir: str, probe_mib
     with open(os.path.join(ROOT, "profiles", "gdn_kernels_prefill4096_decode64.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     return traffic, rows
+
+
+def summarize_short(stats_dir: str, results_jsonl: str):
+    """Write profiles/gdn_token_scan_short_prefill.md from a rocprofv3 kernel
+    trace of `bench.py --short-prefill` and the JSON lines that run printed."""
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(stats_dir, "run_kernel_stats.csv"))))
+    lines = [
+        "# Short prefills: token by token (chunk 1) vs chunked (chunk 64); HK=16, HV=32, d=128, bf16",
+        "",
+        "Made by (from the repository root; OUT is any scratch directory):",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp",
+        "rocprofv3 --kernel-trace --stats -d OUT/stats -o run --output-format csv -- "
+        "python3 REPO/bench.py --short-prefill > OUT/short.jsonl",
+        "cd REPO && python3 bench.py --summarize-short OUT/stats OUT/short.jsonl",
+        "```",
+        "",
+        f"Kernel sources hash: `{kernel_source_hash()}`.",
+        "",
+        "## Kernel durations over all shapes of the run (rocprofv3 --kernel-trace --stats)",
+        "",
+        "| kernel | calls | mean us | min us | max us |",
+        "|---|---|---|---|---|",
+    ]
+    for r in rows:
+        short = _short_kernel(r["Name"])
+        if short in KERNELS:
+            lines.append(f"| {KERNELS[short]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", "## Per shape (HIP events in the same run; 4 rotated buffer sets)", "",
+              "| sequences x tokens | token scan us | chunked us | token-scan kernel us | GB/s | chunk 0 picks |",
+              "|---|---|---|---|---|---|"]
+    for line in open(results_jsonl):
+        line = line.strip()
+        if not line.startswith("{"):
+            continue
+        d = json.loads(line)
+        lines.append(f"| {d['num_seqs']} x {d['tokens_per_seq']} | {d['token_scan_ms'] * 1e3:.1f} | "
+                     f"{d['chunked_ms'] * 1e3:.1f} | {d['token_scan_kernel_ms'] * 1e3:.1f} | "
+                     f"{d['token_scan_gbs']:.0f} | {d['chunk0_picks']} |")
+    with open(os.path.join(ROOT, "profiles", "gdn_token_scan_short_prefill.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def to_device(x: np.ndarray, dtype: str, dev):
@@ -318,10 +362,16 @@ def main():
     ap.add_argument("--summarize", nargs=4, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR", "PROBE_MIB"),
                     help="host only: turn rocprofv3 output directories into the summaries under "
                          "profiles/ and exit")
+    ap.add_argument("--summarize-short", nargs=2, metavar=("STATS_DIR", "RESULTS_JSONL"),
+                    help="host only: turn a kernel trace of --short-prefill into "
+                         "profiles/gdn_token_scan_short_prefill.md and exit")
     args = ap.parse_args()
 
     if args.summarize:
         summarize_profiles(*args.summarize[:3], int(args.summarize[3]))
+        return
+    if args.summarize_short:
+        summarize_short(*args.summarize_short)
         return
 
     if args.gpus != 1:
