@@ -228,8 +228,8 @@ def summarize_short(stats_dir: str, results_jsonl: str):
             lines.append(f"| {KERNELS[short]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     lines += ["", "## Per shape (HIP events in the same run; 4 rotated buffer sets)", "",
-              "Call times (token scan, chunked) were taken under the profiler, which adds launch "
-              "overhead that shows on the smallest shapes; the kernel column is the kernel alone.", "",
+              "Taken under the profiler, which adds a per-launch overhead that shows in every column "
+              "on the smallest shapes; `python3 bench.py --short-prefill` measures the same without it.", "",
               "| sequences x tokens | token scan us | chunked us | token-scan kernel us | GB/s | chunk 0 picks |",
               "|---|---|---|---|---|---|"]
     for line in open(results_jsonl):
