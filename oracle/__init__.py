@@ -21,6 +21,13 @@ What is here:
                        travail distinctes"), written from its derivation in
                        numpy float64; used only to brute-force "scan ==
                        chunked" on tiny inputs.
+* ``rms_norm``      -- the output normalisation that follows the recurrent
+                       update (section "Reduire le trafic intermediaire et
+                       d'etat" names the update "with its normalisation"
+                       without giving its form): per (token, value head),
+                       the dv outputs divided by their root mean square,
+                       with eps inside the root, times one weight per value
+                       channel shared by all heads.
 
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_pins.py`` (closed forms, invariants, scalar cases worked
@@ -238,3 +245,21 @@ def chunked(q, k, v, g, beta, cu_seqlens, *, chunk: int, scale: float = 1.0,
                 S = gam[-1] * S + U.T @ (tail[:, None] * K)
             fin[n, h] = S
     return out, fin
+
+
+def rms_norm(o, weight, eps: float) -> np.ndarray:
+    """Output normalisation over the last axis, float64:
+    y[..., i] = o[..., i] * weight[i] / sqrt(mean_j o[..., j]^2 + eps).
+
+    ``o`` is [..., dv] (the layer outputs, one row per token and value head),
+    ``weight`` [dv]. With eps = 0 an all-zero row gives NaN (0/0), as the
+    definition does."""
+    o = np.asarray(o, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    if w.shape != (o.shape[-1],):
+        raise ValueError("weight must have one entry per value channel")
+    if not (eps >= 0.0):
+        raise ValueError("eps must be >= 0")
+    mean_sq = np.mean(o * o, axis=-1, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return o / np.sqrt(mean_sq + float(eps)) * w

@@ -306,3 +306,60 @@ def test_rejects_bad_arguments():
         oracle.scan(q, k, v, g, b, np.array([0, 9, 8]))
     with pytest.raises(ValueError):  # offsets do not end at T
         oracle.scan(q, k, v, g, b, np.array([0, 4, 7]))
+
+
+# ------------------------------------------------- output normalisation pins
+#
+# rms_norm: y_i = o_i w_i / sqrt(mean_j o_j^2 + eps) over each row's dv values.
+# A sum in place of the mean, eps outside the root, a missing root, the
+# weight applied per head or reversed, or a reduction over the wrong axis
+# each fails one of these.
+
+def test_rms_norm_hand_worked():
+    # o = (3, 4), w = (1, 2), eps = 0.5: mean square 12.5, + eps = 13
+    y = oracle.rms_norm(np.array([3.0, 4.0]), np.array([1.0, 2.0]), 0.5)
+    r = np.sqrt(13.0)
+    assert np.allclose(y, [3.0 / r, 8.0 / r], rtol=0, atol=1e-15)
+
+
+def test_rms_norm_eps_inside_the_root():
+    # a constant row of ones with eps = 3 over d = 4: 1 / sqrt(1 + 3) = 1/2
+    # exactly (eps outside the root, 1 / (1 + 3), would give 1/4)
+    w = np.array([0.5, -1.0, 2.0, 4.0])
+    y = oracle.rms_norm(np.ones(4), w, 3.0)
+    assert np.array_equal(y, w / 2)
+
+
+def test_rms_norm_unit_rms_per_row():
+    # eps = 0, unit weights: every (token, head) row comes out with mean
+    # square 1, whatever the magnitudes of the rows around it
+    rng = np.random.default_rng(5)
+    o = rng.standard_normal((5, 3, 8)) * (10.0 ** rng.integers(-3, 4, (5, 3, 1)))
+    y = oracle.rms_norm(o, np.ones(8), 0.0)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=0, atol=1e-13)
+    # and each row keeps its direction
+    assert np.allclose(y * np.sqrt(np.mean(o * o, axis=-1, keepdims=True)), o, rtol=1e-13, atol=0)
+
+
+def test_rms_norm_one_hot_picks_its_weight():
+    # a single nonzero x at channel j, eps = 0: y_j = sign(x) sqrt(d) w_j
+    d = 16
+    w = np.arange(1.0, d + 1.0)
+    for j, x in ((0, 2.5), (7, -0.25), (15, 1e3)):
+        o = np.zeros(d)
+        o[j] = x
+        y = oracle.rms_norm(o, w, 0.0)
+        want = np.zeros(d)
+        want[j] = np.sign(x) * np.sqrt(d) * w[j]
+        assert np.allclose(y, want, rtol=1e-15, atol=0)
+
+
+def test_rms_norm_scale_invariant_and_zero_rows():
+    rng = np.random.default_rng(6)
+    o = rng.standard_normal((4, 32))
+    w = rng.standard_normal(32)
+    assert np.allclose(oracle.rms_norm(-3.7 * o, w, 0.0), -oracle.rms_norm(o, w, 0.0), rtol=1e-14, atol=0)
+    assert np.array_equal(oracle.rms_norm(np.zeros(32), w, 1e-6), np.zeros(32))
+    assert np.isnan(oracle.rms_norm(np.zeros(32), w, 0.0)).all()
+    with pytest.raises(ValueError):
+        oracle.rms_norm(o, w[:31], 1e-6)
