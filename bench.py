@@ -88,7 +88,8 @@ def measured_traffic(kernel: str):
 
 
 KERNELS = {"schedule": "gdn_schedule_kernel", "prep": "gdn_prep_kernel", "scan": "gdn_scan_kernel",
-           "decode": "gdn_decode_kernel", "token_scan": "gdn_token_scan_kernel"}
+           "decode": "gdn_decode_kernel", "token_scan": "gdn_token_scan_kernel",
+           "decode_norm": "gdn_decode_norm_kernel", "norm_apply": "gdn_norm_apply_kernel"}
 
 
 def _short_kernel(name: str) -> str:
@@ -348,6 +349,93 @@ def short_prefill_sweep(dev, copies, steps):
         }), flush=True)
 
 
+def norm_apply_bytes(tokens, hv=HV, dv=D, elem=2):
+    """Algorithmic HBM bytes of the prefill's output-normalisation pass: every
+    output row read and written once (the weight and cu_seqlens are a few
+    hundred bytes)."""
+    return 2 * tokens * hv * dv * elem
+
+
+def output_norm_bench(dev, copies, steps):
+    """Output normalisation: decode B=64 with the fused kernel against the
+    plain one, and the prefill (T=4096, chunk 64) with its normalisation pass
+    against the plain prefill. One JSON line each; kernel times from the
+    library's dispatch-stamped events."""
+    import torch
+    import gdn_synth as gs
+    import gated_deltanet_linear_02_amd as gdn
+    w = torch.from_numpy(gs.norm_weight(D, seed=gs.SEED_BASE + 505)).to(dev)
+    eps = 1e-6
+
+    def measure(run, sets, kinds):
+        for i in range(3):
+            run(sets[i % copies])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            run(sets[i % copies])
+        e1.record()
+        torch.cuda.synchronize()
+        call_ms = e0.elapsed_time(e1) / steps
+        gdn.timing_start(8 * steps)
+        for i in range(steps):
+            run(sets[i % copies])
+        kt = gdn.timing_stop()
+        return call_ms, {k: kt[k]["mean_ms"] for k in kinds}
+
+    dec = gs.workload("decode", batch=B_DECODE)
+    s_dec = gs.decode_state(B_DECODE, HV, D, D, seed=gs.SEED_BASE + 101)
+    dsets = []
+    for _ in range(copies):
+        d = device_inputs(dec, dev)
+        d["state"] = torch.from_numpy(s_dec).to(dev)
+        d["out"] = torch.empty((B_DECODE, HV, D), dtype=torch.bfloat16, device=dev)
+        dsets.append(d)
+    plain_ms, plain_k = measure(lambda d: gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"],
+                                                          out=d["out"]), dsets, ("decode",))
+    norm_ms, norm_k = measure(lambda d: gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"],
+                                                        out=d["out"], norm_weight=w, norm_eps=eps),
+                              dsets, ("decode_norm",))
+    by = decode_bytes_per_step() + 4 * D
+    gbs = by / (norm_k["decode_norm"] * 1e-3) / 1e9
+    print(json.dumps({
+        "mode": "output-norm", "part": "decode", "plain_ms": plain_ms, "norm_ms": norm_ms,
+        "plain_kernel_ms": plain_k["decode"], "norm_kernel_ms": norm_k["decode_norm"],
+        "norm_kernel_gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": by,
+        "dtype": "bf16", "data": "synthetic", "buffer_copies": copies,
+        "config": {"workload": f"decode batch {B_DECODE}, HK={HK}, HV={HV}, d={D}, fp32 state; "
+                               f"RMS output norm, eps {eps}"},
+    }), flush=True)
+    del dsets
+
+    pre = gs.workload("prefill")
+    ws_bytes = gdn.prefill_workspace_size(1, T_PREFILL, HK, HV, D, D, CHUNK, torch.bfloat16)
+    psets = []
+    for _ in range(copies):
+        d = device_inputs(pre, dev)
+        d["out"] = torch.empty((T_PREFILL, HV, D), dtype=torch.bfloat16, device=dev)
+        d["fin"] = torch.empty((1, HV, D, D), dtype=torch.float32, device=dev)
+        d["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        psets.append(d)
+
+    def pre_run(d, norm):
+        gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=CHUNK,
+                    final_state=d["fin"], out=d["out"], workspace=d["ws"],
+                    norm_weight=w if norm else None, norm_eps=eps)
+    plain_ms, _ = measure(lambda d: pre_run(d, False), psets, ())
+    norm_ms, nk = measure(lambda d: pre_run(d, True), psets, ("norm_apply", "scan"))
+    by = norm_apply_bytes(T_PREFILL)
+    gbs = by / (nk["norm_apply"] * 1e-3) / 1e9
+    print(json.dumps({
+        "mode": "output-norm", "part": "prefill", "plain_ms": plain_ms, "norm_ms": norm_ms,
+        "norm_apply_kernel_ms": nk["norm_apply"], "norm_apply_gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+        "algorithmic_bytes": by, "dtype": "bf16", "data": "synthetic", "buffer_copies": copies,
+        "config": {"workload": f"prefill 1x{T_PREFILL} tokens, HK={HK}, HV={HV}, d={D}, chunk {CHUNK}; "
+                               f"RMS output norm, eps {eps}"},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -358,6 +446,9 @@ def main():
     ap.add_argument("--short-prefill", action="store_true",
                     help="instead of the main line: token-by-token vs chunked prefill on short prompts "
                          "and multi-token steps, one JSON line per shape")
+    ap.add_argument("--norm", action="store_true",
+                    help="instead of the main line: decode and prefill with the output normalisation "
+                         "against the plain calls, one JSON line each")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, run 3 device-to-device copies of this many MiB "
                          "(the known-size reference for HBM byte counters)")
@@ -392,6 +483,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.short_prefill:
         short_prefill_sweep(dev, args.copies, min(args.steps, 30))
+        return
+    if args.norm:
+        output_norm_bench(dev, args.copies, min(args.steps, 30))
         return
     print("[bench] generating inputs", file=sys.stderr, flush=True)
 

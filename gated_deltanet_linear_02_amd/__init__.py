@@ -9,6 +9,8 @@ been built, importing works but every call raises.
 Entry points (same names as the C ABI, without the ``gdn_`` prefix):
     prefill(q, k, v, g, beta, cu_seqlens, ...)  -> (out, final_state)
     decode_step(q, k, v, g, beta, state, ...)   -> out
+    (with ``norm_weight=`` they call gdn_prefill_norm / gdn_decode_step_norm:
+    the output rows RMS-normalised, times one weight per value channel)
     prefill_workspace_size(...)
     timing_start(max_launches) / timing_stop()  -> per-kernel launch times
 """
@@ -33,11 +35,11 @@ _lib = None
 _lock = threading.Lock()
 
 GDN_BF16, GDN_F32 = 0, 1
-KERNEL_KINDS = ("schedule", "prep", "scan", "decode", "token_scan")
+KERNEL_KINDS = ("schedule", "prep", "scan", "decode", "token_scan", "decode_norm", "norm_apply")
 
 STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
-    4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP", 6: "GDN_ERR_ALIAS",
+    4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP", 6: "GDN_ERR_ALIAS", 7: "GDN_ERR_BAD_VALUE",
 }
 
 
@@ -72,9 +74,15 @@ def load():
         L.gdn_prefill.restype = i32
         L.gdn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
                                   f32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.gdn_prefill_norm.restype = i32
+        L.gdn_prefill_norm.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
+                                       f32, i32, i32, vp, vp, vp, f32, vp, vp, sz, vp]
         L.gdn_decode_step.restype = i32
         L.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32,
                                       vp, vp, i32, vp, vp]
+        L.gdn_decode_step_norm.restype = i32
+        L.gdn_decode_step_norm.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32,
+                                           vp, vp, i32, vp, f32, vp, vp]
         L.gdn_timing_start.restype = i32
         L.gdn_timing_start.argtypes = [i32]
         L.gdn_timing_stop.restype = i32
@@ -115,6 +123,19 @@ def _stream(device: torch.device, stream) -> Optional[int]:
     return stream.cuda_stream or None
 
 
+def _check_norm_weight(w: torch.Tensor, dv: int) -> None:
+    if w.dtype != torch.float32 or w.numel() != dv:
+        raise TypeError(f"norm_weight must be float32 with {dv} entries")
+
+
+def _on_device(dev: torch.device, **tensors) -> None:
+    """Every tensor handed to the library must live on the GPU the call runs
+    on: a host pointer would be dereferenced by a kernel."""
+    for name, t in tensors.items():
+        if t is not None and (t.device.type != "cuda" or t.device != dev):
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
 def prefill_workspace_size(num_seqs: int, total_tokens: int, hk: int, hv: int, dk: int, dv: int,
                            chunk: int, io_dtype: torch.dtype) -> int:
     return int(load().gdn_prefill_workspace_size(num_seqs, total_tokens, hk, hv, dk, dv, chunk,
@@ -125,7 +146,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
             cu_seqlens: torch.Tensor, *, chunk: int = 0, scale: float = 1.0,
             initial_state: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-            write_final_state: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            write_final_state: bool = True, norm_weight: Optional[torch.Tensor] = None,
+            norm_eps: float = 1e-6, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Prefill over packed sequences (``gdn_prefill``).
 
     q, k [T, hk, dk]; v [T, hv, dv] (bf16 or fp32, one dtype); g, beta [T, hv]
@@ -133,6 +155,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     [N, hv, dv, dk]. ``final_state`` may be ``initial_state`` (in place).
     ``chunk``: 16, 32 or 64 (chunked), 1 (token by token) or 0 (token by
     token when T <= max(64, 16 N), else chunks of 64).
+    ``norm_weight`` (fp32 [dv], or None): RMS-normalise every output row,
+    y = o * w / sqrt(mean(o^2) + norm_eps) (``gdn_prefill_norm``).
     Missing out / final_state / workspace are allocated with torch.
     """
     T, hk, dk = q.shape
@@ -150,21 +174,35 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     need = prefill_workspace_size(N, T, hk, hv, dk, dv, chunk, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    status = load().gdn_prefill(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
-        hk, hv, dk, dv, chunk, float(scale), io, gate,
-        _ptr(initial_state), _ptr(final_state), _ptr(out),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    _on_device(dev, k=k, v=v, g=g, beta=beta, cu_seqlens=cu_seqlens, initial_state=initial_state,
+               final_state=final_state, out=out, workspace=workspace, norm_weight=norm_weight)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if norm_weight is None:
+        status = load().gdn_prefill(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
+            hk, hv, dk, dv, chunk, float(scale), io, gate,
+            _ptr(initial_state), _ptr(final_state), _ptr(out),
+            _ptr(workspace), ws_bytes, _stream(dev, stream))
+    else:
+        _check_norm_weight(norm_weight, dv)
+        status = load().gdn_prefill_norm(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
+            hk, hv, dk, dv, chunk, float(scale), io, gate,
+            _ptr(initial_state), _ptr(final_state), _ptr(norm_weight), float(norm_eps), _ptr(out),
+            _ptr(workspace), ws_bytes, _stream(dev, stream))
     _check(status)
     return out, final_state
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
                 state: torch.Tensor, *, scale: float = 1.0, state_slots: Optional[torch.Tensor] = None,
-                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
+                norm_eps: float = 1e-6, stream=None) -> torch.Tensor:
     """One token per sequence against resident fp32 states, updated in place
     (``gdn_decode_step``). q, k [B, hk, dk]; v [B, hv, dv]; g, beta [B, hv];
-    state [slots, hv, dv, dk]; state_slots int32 [B] on the device or None."""
+    state [slots, hv, dv, dk]; state_slots int32 [B] on the device or None.
+    ``norm_weight`` (fp32 [dv], or None): the output rows RMS-normalised in
+    the same kernel (``gdn_decode_step_norm``)."""
     B, hk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
     if state.dtype != torch.float32:
@@ -173,10 +211,19 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
         raise TypeError("state_slots must be int32")
     if out is None:
         out = torch.empty((B, hv, dv), dtype=q.dtype, device=q.device)
-    status = load().gdn_decode_step(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), B, hk, hv, dk, dv, float(scale),
-        _dtype_code(q.dtype), _dtype_code(g.dtype), _ptr(state), _ptr(state_slots),
-        state.shape[0], _ptr(out), _stream(q.device, stream))
+    _on_device(q.device, k=k, v=v, g=g, beta=beta, state=state, state_slots=state_slots, out=out,
+               norm_weight=norm_weight)
+    if norm_weight is None:
+        status = load().gdn_decode_step(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), B, hk, hv, dk, dv, float(scale),
+            _dtype_code(q.dtype), _dtype_code(g.dtype), _ptr(state), _ptr(state_slots),
+            state.shape[0], _ptr(out), _stream(q.device, stream))
+    else:
+        _check_norm_weight(norm_weight, dv)
+        status = load().gdn_decode_step_norm(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), B, hk, hv, dk, dv, float(scale),
+            _dtype_code(q.dtype), _dtype_code(g.dtype), _ptr(state), _ptr(state_slots),
+            state.shape[0], _ptr(norm_weight), float(norm_eps), _ptr(out), _stream(q.device, stream))
     _check(status)
     return out
 

@@ -6,6 +6,7 @@
 #include "gdn.h"
 #include "gdn_launch.hpp"
 
+#include <cmath>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -83,6 +84,7 @@ const char *gdn_status_string(int32_t status) {
     case GDN_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than gdn_prefill_workspace_size()";
     case GDN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case GDN_ERR_ALIAS: return "output buffer overlaps an input buffer";
+    case GDN_ERR_BAD_VALUE: return "a scalar argument is out of range (norm eps must be finite and >= 0)";
     default: return "unknown status";
     }
 }
@@ -122,12 +124,17 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_
     return prefill_workspace_bytes(num_seqs, total_tokens, hk, hv, dk, chunk, io_dtype);
 }
 
-int32_t gdn_prefill(const void *q, const void *k, const void *v, const void *g, const void *beta,
-                    const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
-                    int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
-                    float scale, int32_t io_dtype, int32_t gate_dtype,
-                    const float *initial_state, float *final_state, void *out,
-                    void *workspace, size_t workspace_bytes, void *stream) {
+// eps of the output normalisation: finite and not negative.
+static bool valid_eps(float eps) { return std::isfinite(eps) && eps >= 0.f; }
+
+// gdn_prefill, and gdn_prefill_norm when norm_w is not NULL.
+static int32_t prefill_impl(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                            const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                            int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
+                            float scale, int32_t io_dtype, int32_t gate_dtype,
+                            const float *initial_state, float *final_state,
+                            const float *norm_w, float norm_eps, void *out,
+                            void *workspace, size_t workspace_bytes, void *stream) {
     const int32_t sc = check_prefill_shape(num_seqs, total_tokens, hk, hv, dk, dv, chunk, io_dtype, gate_dtype);
     if (sc != GDN_OK) return sc;
     if (!cu_seqlens) return GDN_ERR_NULL_ARG;
@@ -146,6 +153,7 @@ int32_t gdn_prefill(const void *q, const void *k, const void *v, const void *g, 
     const Range inputs[] = {span(q, T * hk * dk * eb), span(k, T * hk * dk * eb), span(v, T * hv * dv * eb),
                             span(g, T * hv * gb), span(beta, T * hv * gb),
                             span(cu_seqlens, sizeof(int32_t) * (num_seqs + 1)),
+                            span(norm_w, sizeof(float) * (size_t)dv),
                             span(initial_state, state_bytes), span(final_state, state_bytes),
                             span(workspace, L.total)};
     for (const Range &r : inputs)
@@ -153,7 +161,7 @@ int32_t gdn_prefill(const void *q, const void *k, const void *v, const void *g, 
     // The final state may be the initial state, but must not overlap any
     // other buffer.
     const Range r_fin = span(final_state, state_bytes);
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < 7; ++i)
         if (overlaps(r_fin, inputs[i])) return GDN_ERR_ALIAS;
     if (overlaps(r_fin, span(workspace, L.total))) return GDN_ERR_ALIAS;
     if (final_state && initial_state && final_state != initial_state &&
@@ -169,16 +177,49 @@ int32_t gdn_prefill(const void *q, const void *k, const void *v, const void *g, 
     A.ws = static_cast<char *>(workspace); A.lay = L;
     try {
         const hipStream_t st = static_cast<hipStream_t>(stream);
-        return (c == 1 ? launch_token_scan(A, st) : launch_prefill(A, st)) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+        if ((c == 1 ? launch_token_scan(A, st) : launch_prefill(A, st)) != hipSuccess) return GDN_ERR_HIP;
+        if (norm_w) {
+            NormArgs N;
+            N.out = out; N.norm_w = norm_w; N.eps = norm_eps; N.cu = cu_seqlens; N.num_seqs = num_seqs;
+            N.total_tokens = total_tokens; N.hv = hv; N.dv = dv; N.io_bf16 = A.io_bf16;
+            if (launch_norm_apply(N, st) != hipSuccess) return GDN_ERR_HIP;
+        }
+        return GDN_OK;
     } catch (...) {
         return GDN_ERR_HIP;
     }
 }
 
-int32_t gdn_decode_step(const void *q, const void *k, const void *v, const void *g, const void *beta,
-                        int32_t batch, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float scale,
-                        int32_t io_dtype, int32_t gate_dtype, float *state, const int32_t *state_slots,
-                        int32_t num_slots, void *out, void *stream) {
+int32_t gdn_prefill(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                    const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                    int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
+                    float scale, int32_t io_dtype, int32_t gate_dtype,
+                    const float *initial_state, float *final_state, void *out,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_impl(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, hk, hv, dk, dv, chunk, scale,
+                        io_dtype, gate_dtype, initial_state, final_state, nullptr, 0.f, out, workspace,
+                        workspace_bytes, stream);
+}
+
+int32_t gdn_prefill_norm(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                         const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                         int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
+                         float scale, int32_t io_dtype, int32_t gate_dtype,
+                         const float *initial_state, float *final_state,
+                         const float *norm_weight, float norm_eps, void *out,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    if (!norm_weight) return GDN_ERR_NULL_ARG;
+    if (!valid_eps(norm_eps)) return GDN_ERR_BAD_VALUE;
+    return prefill_impl(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, hk, hv, dk, dv, chunk, scale,
+                        io_dtype, gate_dtype, initial_state, final_state, norm_weight, norm_eps, out, workspace,
+                        workspace_bytes, stream);
+}
+
+// gdn_decode_step, and gdn_decode_step_norm when norm_w is not NULL.
+static int32_t decode_impl(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                           int32_t batch, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float scale,
+                           int32_t io_dtype, int32_t gate_dtype, float *state, const int32_t *state_slots,
+                           int32_t num_slots, const float *norm_w, float norm_eps, void *out, void *stream) {
     if (batch < 0 || hk < 1 || hv < 1 || hv % hk != 0 || num_slots < 0) return GDN_ERR_BAD_SHAPE;
     if (!valid_head(dk) || dv != dk || !valid_dtype(io_dtype) || !valid_dtype(gate_dtype))
         return GDN_ERR_UNSUPPORTED;
@@ -192,10 +233,11 @@ int32_t gdn_decode_step(const void *q, const void *k, const void *v, const void 
     const Range r_state = span(state, (size_t)num_slots * hv * dv * dk * sizeof(float));
     const Range inputs[] = {span(q, B * hk * dk * eb), span(k, B * hk * dk * eb), span(v, B * hv * dv * eb),
                             span(g, B * hv * gb), span(beta, B * hv * gb),
-                            span(state_slots, B * sizeof(int32_t)), r_state};
+                            span(state_slots, B * sizeof(int32_t)), span(norm_w, sizeof(float) * (size_t)dv),
+                            r_state};
     for (const Range &r : inputs)
         if (overlaps(r_out, r)) return GDN_ERR_ALIAS;
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < 7; ++i)
         if (overlaps(r_state, inputs[i])) return GDN_ERR_ALIAS;
 
     DecodeArgs A;
@@ -203,6 +245,7 @@ int32_t gdn_decode_step(const void *q, const void *k, const void *v, const void 
     A.state = state; A.slots = state_slots; A.num_slots = num_slots; A.out = out;
     A.batch = batch; A.hk = hk; A.hv = hv; A.d = dk; A.scale = scale;
     A.io_bf16 = io_dtype == GDN_BF16; A.gate_bf16 = gate_dtype == GDN_BF16;
+    A.norm_w = norm_w; A.norm_eps = norm_eps;
     try {
         const hipStream_t st = static_cast<hipStream_t>(stream);
         const hipError_t e = launch_decode(A, st);
@@ -210,6 +253,25 @@ int32_t gdn_decode_step(const void *q, const void *k, const void *v, const void 
     } catch (...) {
         return GDN_ERR_HIP;
     }
+}
+
+int32_t gdn_decode_step(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                        int32_t batch, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float scale,
+                        int32_t io_dtype, int32_t gate_dtype, float *state, const int32_t *state_slots,
+                        int32_t num_slots, void *out, void *stream) {
+    return decode_impl(q, k, v, g, beta, batch, hk, hv, dk, dv, scale, io_dtype, gate_dtype, state, state_slots,
+                       num_slots, nullptr, 0.f, out, stream);
+}
+
+int32_t gdn_decode_step_norm(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                             int32_t batch, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float scale,
+                             int32_t io_dtype, int32_t gate_dtype, float *state, const int32_t *state_slots,
+                             int32_t num_slots, const float *norm_weight, float norm_eps, void *out,
+                             void *stream) {
+    if (!norm_weight) return GDN_ERR_NULL_ARG;
+    if (!valid_eps(norm_eps)) return GDN_ERR_BAD_VALUE;
+    return decode_impl(q, k, v, g, beta, batch, hk, hv, dk, dv, scale, io_dtype, gate_dtype, state, state_slots,
+                       num_slots, norm_weight, norm_eps, out, stream);
 }
 
 int32_t gdn_timing_start(int32_t max_launches) {

@@ -47,6 +47,58 @@ template <int DK, int DV> struct DecodeShape {
     static constexpr int SLICES = (DV + ROWS - 1) / ROWS;  // workgroups per (b, h)
 };
 
+// A lane's share of one state row: the 16-byte pieces at columns 4*lr and
+// 4*lr + 4*LPR. The arithmetic below is shared by both decode kernels (with
+// explicit fused multiply-adds, so that the compiler cannot contract it
+// differently in each): they leave bit-identical states.
+template <int LPR> __device__ __forceinline__ float lane_group_sum(float x) {
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) x += __shfl_xor(x, off);
+    return x;
+}
+template <int LPR>
+__device__ __forceinline__ float row_dot(const f32x4 (&s)[2], const float (&x)[8]) {
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(s[m][e], x[4 * m + e], acc);
+    return lane_group_sum<LPR>(acc);
+}
+template <int LPR>
+__device__ __forceinline__ float key_query_dot(const float (&kk)[8], const float (&qq)[8]) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = __builtin_fmaf(kk[j], qq[j], acc);
+    return lane_group_sum<LPR>(acc);
+}
+// u = b (v - a sk);  o = scale (a sq + kq u);  S_new = a S + u k^T (stored).
+__device__ __forceinline__ float write_strength(float beta, float a, float vv, float sk) {
+    return beta * __builtin_fmaf(-a, sk, vv);
+}
+__device__ __forceinline__ float row_output(float scale, float a, float sq, float kq, float u) {
+    return scale * __builtin_fmaf(a, sq, kq * u);
+}
+__device__ __forceinline__ void store_row(float *p, int lr, int lpr, const f32x4 (&s)[2], const float (&kk)[8],
+                                          float a, float u) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = __builtin_fmaf(a, s[m][e], u * kk[4 * m + e]);
+        __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(p + 4 * lr + 4 * lpr * m));
+    }
+}
+
+template <typename E, int LPR>
+__device__ __forceinline__ void load_kq(const E *kp, const E *qp, int lr, float (&kk)[8], float (&qq)[8]) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        load4<E>(kp + 4 * lr + 4 * LPR * m, kk + 4 * m);
+        load4<E>(qp + 4 * lr + 4 * LPR * m, qq + 4 * m);
+    }
+}
+
 template <typename E, typename G, int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_decode_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
@@ -84,43 +136,122 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(
                     : f32x4{0.f, 0.f, 0.f, 0.f};
 
     float kk[8], qq[8];
-    const E *kp = k + ((size_t)b * hk + kh) * DK;
-    const E *qp = q + ((size_t)b * hk + kh) * DK;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        load4<E>(kp + 4 * lr + 4 * LPR * m, kk + 4 * m);
-        load4<E>(qp + 4 * lr + 4 * LPR * m, qq + 4 * m);
-    }
+    load_kq<E, LPR>(k + ((size_t)b * hk + kh) * DK, q + ((size_t)b * hk + kh) * DK, lr, kk, qq);
     const float a = expf(static_cast<float>(gate_g[(size_t)b * hv + h]));
     const float beta = static_cast<float>(gate_b[(size_t)b * hv + h]);
     const float vv = live ? static_cast<float>(v[((size_t)b * hv + h) * DV + row]) : 0.f;
 
-    float kq = 0.f, sk = 0.f, sq = 0.f;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            kq += kk[4 * m + e] * qq[4 * m + e];
-            sk += s[m][e] * kk[4 * m + e];
-            sq += s[m][e] * qq[4 * m + e];
-        }
-    }
-#pragma unroll
-    for (int off = 1; off < LPR; off <<= 1) {
-        kq += __shfl_xor(kq, off);
-        sk += __shfl_xor(sk, off);
-        sq += __shfl_xor(sq, off);
-    }
+    const float kq = key_query_dot<LPR>(kk, qq);
+    const float sk = row_dot<LPR>(s, kk);
+    const float sq = row_dot<LPR>(s, qq);
     if (live) {
-        const float u = beta * (vv - a * sk);
-        if (lr == 0) o_row[row] = from_f32<E>(scale * (a * sq + kq * u));
+        const float u = write_strength(beta, a, vv, sk);
+        if (lr == 0) o_row[row] = from_f32<E>(row_output(scale, a, sq, kq, u));
+        store_row(S + (size_t)row * DK, lr, LPR, s, kk, a, u);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode with the output normalisation fused in
+// ---------------------------------------------------------------------------
+//
+// The recurrent update "with its normalisation" in one launch (section
+// "Reduire le trafic intermediaire et d'etat"): per (sequence, value head)
+// the output row o (dv values) becomes
+//     y_i = o_i w_i / sqrt(mean_j o_j^2 + eps),
+// which needs every row of that head's state. So one workgroup owns a whole
+// (b, h) state: its lanes form groups of LPR lanes as in the plain kernel,
+// and each group holds NRL rows, RPP rows apart (d = 128: 512 threads, four
+// rows per group). The row work and the memory pattern are the plain
+// kernel's; the row outputs stay in registers while the workgroup sums
+// their squares (wave butterflies, then LDS across waves, one barrier), and
+// only the normalised row is written. The unnormalised output never goes to
+// memory.
+template <int DK, int DV> struct DecodeNormShape {
+    static constexpr int LPR = DK / 8;                                  // lanes per state row
+    static constexpr int NRL = DV * LPR > 512 ? DV * LPR / 512 : 1;     // rows per lane group
+    static constexpr int THREADS = DV * LPR / NRL < 64 ? 64 : DV * LPR / NRL;
+    static constexpr int RPP = THREADS / LPR;                           // rows per pass
+    static constexpr int WAVES = THREADS / 64;
+    static_assert(RPP * NRL >= DV, "every row has a lane group");
+};
+
+template <typename E, typename G, int DK, int DV>
+__global__ __launch_bounds__((DecodeNormShape<DK, DV>::THREADS)) void gdn_decode_norm_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
+    const G *__restrict__ gate_g, const G *__restrict__ gate_b,
+    float *__restrict__ state, const int32_t *__restrict__ slots, int32_t num_slots,
+    E *__restrict__ out, int32_t hk, int32_t hv, float scale,
+    const float *__restrict__ norm_w, float eps)
+{
+    typedef DecodeNormShape<DK, DV> SH;
+    constexpr int LPR = SH::LPR, NRL = SH::NRL, RPP = SH::RPP, WAVES = SH::WAVES;
+    __shared__ float s_part[WAVES];
+
+    const int bh = blockIdx.x;
+    const int b = bh / hv;
+    const int h = bh - b * hv;
+    const int kh = h / (hv / hk);
+    const int tid = threadIdx.x;
+    const int lr = tid % LPR;
+    const int r0 = tid / LPR;
+
+    const int slot = slots ? slots[b] : b;
+    E *o_row = out + ((size_t)b * hv + h) * DV;
+    if (slot < 0 || slot >= num_slots) {  // the same for the whole workgroup
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            f32x4 w;
+        for (int p = 0; p < NRL; ++p)
+            if (r0 + p * RPP < DV && lr == 0) o_row[r0 + p * RPP] = from_f32<E>(0.0f);
+        return;
+    }
+    float *S = state + ((size_t)slot * hv + h) * (size_t)(DV * DK);
+
+    f32x4 s[NRL][2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = a * s[m][e] + u * kk[4 * m + e];
-            __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(S + (size_t)row * DK + 4 * lr + 4 * LPR * m));
+    for (int p = 0; p < NRL; ++p) {
+        const int row = r0 + p * RPP;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            s[p][m] = row < DV ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)row * DK + 4 * lr + 4 * LPR * m))
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    float kk[8], qq[8];
+    load_kq<E, LPR>(k + ((size_t)b * hk + kh) * DK, q + ((size_t)b * hk + kh) * DK, lr, kk, qq);
+    const float a = expf(static_cast<float>(gate_g[(size_t)b * hv + h]));
+    const float beta = static_cast<float>(gate_b[(size_t)b * hv + h]);
+    float vv[NRL];
+#pragma unroll
+    for (int p = 0; p < NRL; ++p)
+        vv[p] = r0 + p * RPP < DV ? static_cast<float>(v[((size_t)b * hv + h) * DV + r0 + p * RPP]) : 0.f;
+
+    const float kq = key_query_dot<LPR>(kk, qq);
+    float o[NRL];
+    float part = 0.f;  // sum of squares of this lane group's outputs (lane lr == 0 only)
+#pragma unroll
+    for (int p = 0; p < NRL; ++p) {
+        const int row = r0 + p * RPP;
+        const float sk = row_dot<LPR>(s[p], kk);
+        const float sq = row_dot<LPR>(s[p], qq);
+        const float u = write_strength(beta, a, vv[p], sk);
+        o[p] = row_output(scale, a, sq, kq, u);
+        if (row < DV) {
+            store_row(S + (size_t)row * DK, lr, LPR, s[p], kk, a, u);
+            if (lr == 0) part = __builtin_fmaf(o[p], o[p], part);
         }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) part += __shfl_xor(part, off);
+    if ((tid & 63) == 0) s_part[tid >> 6] = part;
+    __syncthreads();
+    float total = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) total += s_part[w];
+    const float r = 1.0f / sqrtf(total * (1.0f / DV) + eps);
+#pragma unroll
+    for (int p = 0; p < NRL; ++p) {
+        const int row = r0 + p * RPP;
+        if (row < DV && lr == 0) o_row[row] = from_f32<E>(o[p] * r * norm_w[row]);
     }
 }
 
@@ -133,8 +264,27 @@ static hipError_t launch_decode_t(const DecodeArgs &A, hipStream_t st) {
                          (E *)A.out, A.hk, A.hv, A.scale);
 }
 
+template <typename E, typename G, int D>
+static hipError_t launch_decode_norm_t(const DecodeArgs &A, hipStream_t st) {
+    typedef DecodeNormShape<D, D> SH;
+    const dim3 grid((unsigned)A.batch * (unsigned)A.hv), block(SH::THREADS);
+    return launch_kernel(kDecodeNorm, gdn_decode_norm_kernel<E, G, D, D>, grid, block, 0, st,
+                         (const E *)A.q, (const E *)A.k, (const E *)A.v,
+                         (const G *)A.g, (const G *)A.beta, A.state, A.slots, A.num_slots,
+                         (E *)A.out, A.hk, A.hv, A.scale, A.norm_w, A.norm_eps);
+}
+
 template <typename E, typename G>
 static hipError_t launch_decode_d(const DecodeArgs &A, hipStream_t st) {
+    if (A.norm_w) {
+        switch (A.d) {
+        case 16: return launch_decode_norm_t<E, G, 16>(A, st);
+        case 32: return launch_decode_norm_t<E, G, 32>(A, st);
+        case 64: return launch_decode_norm_t<E, G, 64>(A, st);
+        case 128: return launch_decode_norm_t<E, G, 128>(A, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (A.d) {
     case 16: return launch_decode_t<E, G, 16>(A, st);
     case 32: return launch_decode_t<E, G, 32>(A, st);

@@ -9,7 +9,10 @@
 
 namespace gdn {
 
-enum KernelKind { kSchedule = 0, kPrep = 1, kScan = 2, kDecode = 3, kTokenScan = 4, kKinds = 5 };
+enum KernelKind {
+    kSchedule = 0, kPrep = 1, kScan = 2, kDecode = 3, kTokenScan = 4, kDecodeNorm = 5, kNormApply = 6,
+    kKinds = 7
+};
 
 // Per-kernel timing (see gdn_timing_start in gdn.h): while it is active,
 // each launch claims a pair of events that the dispatch itself stamps with
@@ -38,6 +41,8 @@ struct DecodeArgs {
     int32_t batch, hk, hv, d;
     float scale;
     bool io_bf16, gate_bf16;
+    const float *norm_w = nullptr;  // non-null: output normalisation fused in
+    float norm_eps = 0.f;
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
@@ -107,6 +112,20 @@ struct PrefillArgs {
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st);
 // Token-by-token prefill (chunk 1): one kernel, no workspace.
 hipError_t launch_token_scan(const PrefillArgs &a, hipStream_t st);
+
+// Output normalisation of the prefill, in place on `out` after the prefill's
+// kernels: rows of tokens in [cu[0], cu[num_seqs]) (clamped into [0, T]).
+struct NormArgs {
+    void *out;
+    const float *norm_w;
+    float eps;
+    const int32_t *cu;
+    int32_t num_seqs;
+    int64_t total_tokens;
+    int32_t hv, dv;
+    bool io_bf16;
+};
+hipError_t launch_norm_apply(const NormArgs &a, hipStream_t st);
 
 // gdn_prefill with chunk 0 evaluates token by token when
 // total_tokens <= max(kTokenScanTokens, kTokenScanPerSeq * num_seqs), else in

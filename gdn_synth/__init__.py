@@ -14,7 +14,9 @@ head dimension 128. The value distributions are:
 * v ~ N(0, 1);
 * log-decay g = log a = -softplus(x), x ~ N(-1, 1);
 * write strength b = sigmoid(x), x ~ N(0, 1);
-* initial states ~ N(0, 0.02**2) (standard deviation 0.02).
+* initial states ~ N(0, 0.02**2) (standard deviation 0.02);
+* output-normalisation weights (one per value channel) ~ U(0.5, 1.5), the
+  pages giving no trained values.
 
 Storage rounding: values are made in float64, rounded to float32 with
 round-to-nearest-even (numpy's cast) and, for bf16 storage, rounded again
@@ -194,6 +196,12 @@ def decode_state(batch: int, hv: int, dv: int, dk: int, *, seed: int, std: float
     """Resident fp32 states [batch, HV, dv, dk] ~ N(0, std**2)."""
     rng = np.random.default_rng(seed)
     return (rng.standard_normal(size=(batch, hv, dv, dk)) * std).astype(np.float32)
+
+
+def norm_weight(dv: int, *, seed: int) -> np.ndarray:
+    """Synthetic output-normalisation weights, fp32 [dv] ~ U(0.5, 1.5)."""
+    rng = np.random.default_rng(seed)
+    return rng.uniform(0.5, 1.5, size=dv).astype(np.float32)
 
 
 # --------------------------------------------------------------------------

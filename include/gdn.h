@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
     GDN_OK = 0,
@@ -62,7 +62,8 @@ typedef enum {
     GDN_ERR_UNSUPPORTED = 3, /* head size, chunk or dtype outside the built set */
     GDN_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
     GDN_ERR_HIP = 5,         /* a HIP runtime call or launch failed */
-    GDN_ERR_ALIAS = 6        /* out overlaps an input */
+    GDN_ERR_ALIAS = 6,       /* out overlaps an input */
+    GDN_ERR_BAD_VALUE = 7    /* a scalar argument out of range (norm eps) */
 } gdn_status;
 
 typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
@@ -142,6 +143,47 @@ int32_t gdn_decode_step(const void *q, const void *k, const void *v,
                         void *out, void *stream);
 
 /*
+ * The same two calls with the layer's output normalisation applied to every
+ * output row. The recurrent update comes "with its normalisation" ("Optimiser
+ * l'inference sur appareil pour Apple Silicon", section "Reduire le trafic
+ * intermediaire et d'etat"); the pages do not give its form, and this is the
+ * RMS normalisation of each (token or sequence, value head) row of dv outputs:
+ *
+ *     y_i = o_i * norm_weight[i] / sqrt(mean_j o_j^2 + norm_eps)
+ *
+ * norm_weight  fp32 [dv] DEVICE array, one weight per value channel, shared
+ *              by all heads; NULL gives GDN_ERR_NULL_ARG. It must not
+ *              overlap out or the states (GDN_ERR_ALIAS).
+ * norm_eps     finite and >= 0, else GDN_ERR_BAD_VALUE. With 0, an all-zero
+ *              row gives NaN, as the definition does.
+ * Everything else (arguments, layouts, workspace, states, errors) is as in
+ * gdn_prefill and gdn_decode_step, and the states they leave are the same.
+ *
+ * gdn_decode_step_norm is one kernel: a workgroup owns a whole (sequence,
+ * value head) state, so the unnormalised row never goes to memory.
+ * gdn_prefill_norm runs gdn_prefill's kernels, then one pass that rewrites
+ * the rows of out in place (the prefill splits a head's rows over
+ * workgroups that never wait for one another); rows of tokens outside
+ * [cu_seqlens[0], cu_seqlens[N]) are left untouched. In bf16 the row is thus
+ * rounded twice (before and after the normalisation).
+ */
+int32_t gdn_prefill_norm(const void *q, const void *k, const void *v,
+                         const void *g, const void *beta,
+                         const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                         int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
+                         float scale, int32_t io_dtype, int32_t gate_dtype,
+                         const float *initial_state, float *final_state,
+                         const float *norm_weight, float norm_eps, void *out,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+int32_t gdn_decode_step_norm(const void *q, const void *k, const void *v,
+                             const void *g, const void *beta,
+                             int32_t batch, int32_t hk, int32_t hv, int32_t dk, int32_t dv,
+                             float scale, int32_t io_dtype, int32_t gate_dtype,
+                             float *state, const int32_t *state_slots, int32_t num_slots,
+                             const float *norm_weight, float norm_eps, void *out, void *stream);
+
+/*
  * Per-kernel timing (a profiling aid, not needed for computation).
  *
  * gdn_timing_start(max_launches) makes the library time each of its next
@@ -153,10 +195,11 @@ int32_t gdn_decode_step(const void *q, const void *k, const void *v,
  * timed (counts[k]) and their summed duration in milliseconds (total_ms[k]),
  * releases the events and stops timing. Kinds: 0 = varlen schedule,
  * 1 = chunk preparation, 2 = chunk-recurrent scan, 3 = decode step,
- * 4 = token-by-token prefill.
+ * 4 = token-by-token prefill, 5 = decode step with output normalisation,
+ * 6 = output normalisation pass of the prefill.
  * Not thread-safe with concurrent gdn_* calls from other host threads.
  */
-#define GDN_KERNEL_KINDS 5
+#define GDN_KERNEL_KINDS 7
 int32_t gdn_timing_start(int32_t max_launches);
 int32_t gdn_timing_stop(int32_t *counts, float *total_ms, int32_t n_kinds);
 

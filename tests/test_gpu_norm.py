@@ -1,0 +1,195 @@
+"""Output normalisation on the GPU against the fp64 oracle.
+
+gdn_decode_step_norm and gdn_prefill_norm are compared with oracle.decode_step
+or oracle.scan followed by oracle.rms_norm (per (token, value head) row:
+y = o w / sqrt(mean(o^2) + eps)), with synthetic weights from gdn_synth. The
+bars are those of the plain calls, max |gpu - ref| / max |ref| per tensor:
+bf16 I/O <= 2e-2, fp32 I/O <= 1e-4. The states must be those of the plain
+calls: bit for bit in decode (shared arithmetic), and the same kernels in
+prefill.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gdn_synth as gs
+import gated_deltanet_linear_02_amd as gdn
+import oracle
+from gpu_util import TOL_F32, device_inputs, note, oracle_ref, rel_err, requires_gpu, to_f64, tol
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _weight(dv, seed=5):
+    return gs.norm_weight(dv, seed=gs.SEED_BASE + 500 + seed)
+
+
+def _decode_case(batch, io, *, d=128, hk=16, hv=32, seed_off=0):
+    inp = gs.make_inputs([1] * batch, hk, hv, d, d, seed=gs.SEED_BASE + 1 + seed_off,
+                         io_dtype=io, gate_dtype=io)
+    s0 = gs.decode_state(batch, hv, d, d, seed=gs.SEED_BASE + 101 + seed_off)
+    return inp, s0
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.05])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("batch", [1, 64])
+def test_decode_norm_matches_oracle(batch, io, eps):
+    """The decode workload (HK = 16, HV = 32, d = 128, up to 64 sequences)."""
+    inp, s0 = _decode_case(batch, io)
+    w = _weight(128)
+    note(f"decode norm batch={batch} io={io} eps={eps}")
+    d = device_inputs(inp)
+    state = torch.from_numpy(s0).cuda()
+    plain_state = torch.from_numpy(s0).cuda()
+    out = torch.full((batch, 32, 128), float("nan"), dtype=d["q"].dtype, device="cuda")
+    gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, out=out,
+                    norm_weight=torch.from_numpy(w).cuda(), norm_eps=eps)
+    gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], plain_state)
+    torch.cuda.synchronize()
+    wd = inp.widened()
+    o_ref, s_ref = oracle.decode_step(wd["q"], wd["k"], wd["v"], wd["g"], wd["beta"], s0.astype(np.float64))
+    y_ref = oracle.rms_norm(o_ref, w, eps)
+    y = to_f64(out)
+    err = rel_err(y, y_ref)
+    print(f"[parity] decode norm B={batch} io={io} eps={eps} out_err={err:.3e}", flush=True)
+    assert np.isfinite(y).all()
+    assert err <= tol(io)
+    assert rel_err(to_f64(state), s_ref) <= TOL_F32
+    assert torch.equal(state, plain_state), "the fused kernel must leave the plain kernel's state bits"
+
+
+@pytest.mark.parametrize("d", [16, 32, 64])
+def test_decode_norm_other_head_sizes(d):
+    inp, s0 = _decode_case(5, "f32", d=d, hk=2, hv=4, seed_off=3)
+    w = _weight(d, seed=d)
+    note(f"decode norm d={d}")
+    dd = device_inputs(inp)
+    state = torch.from_numpy(s0).cuda()
+    out = gdn.decode_step(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], state, scale=0.5,
+                          norm_weight=torch.from_numpy(w).cuda(), norm_eps=0.01)
+    torch.cuda.synchronize()
+    wd = inp.widened()
+    o_ref, s_ref = oracle.decode_step(wd["q"], wd["k"], wd["v"], wd["g"], wd["beta"],
+                                      s0.astype(np.float64), scale=0.5)
+    assert rel_err(to_f64(out), oracle.rms_norm(o_ref, w, 0.01)) <= TOL_F32
+    assert rel_err(to_f64(state), s_ref) <= TOL_F32
+
+
+def test_decode_norm_state_slots_and_zero_rows():
+    """Slot -1: output row of zeros, state untouched. A sequence whose output
+    is exactly zero (zero state, b = 0) normalises to zeros, not NaN."""
+    batch, slots_n = 6, 10
+    inp, _ = _decode_case(batch, "bf16", seed_off=5)
+    inp.beta[1] = gs.to_storage(np.zeros(inp.hv), "bf16")  # sequence 1 writes nothing
+    pool = gs.decode_state(slots_n, 32, 128, 128, seed=gs.SEED_BASE + 77)
+    slots = np.array([7, 2, -1, 0, 9, 4], dtype=np.int32)
+    pool[2] = 0.0  # sequence 1's slot: zero state
+    w = _weight(128)
+    note("decode norm state_slots")
+    d = device_inputs(inp)
+    state = torch.from_numpy(pool).cuda()
+    out = gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state,
+                          state_slots=torch.from_numpy(slots).cuda(),
+                          norm_weight=torch.from_numpy(w).cuda(), norm_eps=1e-6)
+    torch.cuda.synchronize()
+    wd = inp.widened()
+    o_ref, s_ref = oracle.decode_step(wd["q"], wd["k"], wd["v"], wd["g"], wd["beta"],
+                                      pool[np.maximum(slots, 0)].astype(np.float64))
+    y_ref = oracle.rms_norm(o_ref, w, 1e-6)
+    got = to_f64(state)
+    y = to_f64(out)
+    assert np.all(y[1] == 0) and np.all(y_ref[1] == 0)
+    for b, s in enumerate(slots):
+        if s < 0:
+            assert np.all(y[b] == 0)
+            continue
+        assert rel_err(y[b], y_ref[b]) <= 2e-2
+        assert rel_err(got[s], s_ref[b]) <= TOL_F32
+    for s in set(range(slots_n)) - set(int(x) for x in slots):
+        assert np.array_equal(got[s], pool[s].astype(np.float64))
+
+
+def _prefill_norm(inp, *, chunk, w, eps, scale=1.0, cu=None, s0=None):
+    d = device_inputs(inp)
+    T, hv, dv = inp.total_tokens, inp.hv, inp.dv
+    out_dtype = torch.bfloat16 if inp.io_dtype == "bf16" else torch.float32
+    out = torch.full((T, hv, dv), float("nan"), dtype=out_dtype, device="cuda")
+    n = inp.num_seqs if cu is None else cu.numel() - 1
+    fin = torch.full((n, hv, dv, inp.dk), float("nan"), dtype=torch.float32, device="cuda")
+    o, f = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"] if cu is None else cu,
+                       chunk=chunk, scale=scale,
+                       initial_state=d["initial_state"] if s0 is None else s0, final_state=fin, out=out,
+                       norm_weight=torch.from_numpy(w).cuda(), norm_eps=eps)
+    torch.cuda.synchronize()
+    return o, f
+
+
+@pytest.mark.parametrize("chunk", [64, 16, 1])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_prefill_norm_ragged(chunk, io):
+    """Ragged sequences with an empty one, initial states, scale; chunked and
+    token by token."""
+    inp = gs.make_inputs([1, 70, 0, 130, 33], 2, 4, 64, 64, seed=81, io_dtype=io, gate_dtype="f32",
+                         init_state=True)
+    w = _weight(64)
+    note(f"prefill norm ragged chunk={chunk} io={io}")
+    o, f = _prefill_norm(inp, chunk=chunk, w=w, eps=0.05, scale=0.75)
+    o_ref, f_ref = oracle_ref(inp, scale=0.75)
+    y_ref = oracle.rms_norm(o_ref, w, 0.05)
+    y = to_f64(o)
+    eo, ef = rel_err(y, y_ref), rel_err(to_f64(f), f_ref)
+    print(f"[parity] prefill norm ragged chunk={chunk} io={io} out_err={eo:.3e} state_err={ef:.3e}",
+          flush=True)
+    assert np.isfinite(y).all()
+    assert eo <= tol(io) and ef <= tol(io)
+
+
+@pytest.mark.parametrize("d", [16, 32, 128])
+def test_prefill_norm_head_sizes(d):
+    inp = gs.make_inputs([45, 100], 2, 4, d, d, seed=83 + d, io_dtype="f32", gate_dtype="f32",
+                         init_state=True)
+    w = _weight(d, seed=d)
+    note(f"prefill norm d={d}")
+    o, f = _prefill_norm(inp, chunk=32, w=w, eps=1e-6)
+    o_ref, f_ref = oracle_ref(inp)
+    assert rel_err(to_f64(o), oracle.rms_norm(o_ref, w, 1e-6)) <= TOL_F32
+    assert rel_err(to_f64(f), f_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("chunk", [64, 1])
+def test_prefill_norm_4k(chunk):
+    """The prefill workload (T = 4096, HK = 16, HV = 32, d = 128, bf16), on
+    sampled value heads; the final state is the plain call's, bit for bit."""
+    inp = gs.workload("prefill", io_dtype="bf16")
+    w = _weight(128)
+    note(f"prefill norm T=4096 chunk={chunk}")
+    o, f = _prefill_norm(inp, chunk=chunk, w=w, eps=1e-6)
+    heads = [0, 7, 31]
+    o_ref, f_ref = oracle_ref(inp, heads=heads)
+    y_ref = oracle.rms_norm(o_ref[:, heads], w, 1e-6)
+    eo = rel_err(to_f64(o)[:, heads], y_ref)
+    print(f"[parity] prefill norm T=4096 chunk={chunk} out_err={eo:.3e}", flush=True)
+    assert eo <= tol("bf16")
+    d = device_inputs(inp)
+    note(f"plain prefill T=4096 chunk={chunk}")
+    _, f_plain = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(f, f_plain)
+
+
+def test_prefill_norm_leaves_rows_outside_sequences():
+    """cu_seqlens[0] > 0: rows of the tokens before the first sequence are not
+    written by the normalisation pass either."""
+    inp = gs.make_inputs([5, 70, 33], 2, 4, 32, 32, seed=43, io_dtype="bf16", gate_dtype="f32",
+                         init_state=True)
+    w = _weight(32)
+    d = device_inputs(inp)
+    cu = d["cu_seqlens"][1:].contiguous()
+    note("prefill norm with cu_seqlens[0] = 5")
+    o, f = _prefill_norm(inp, chunk=16, w=w, eps=1e-6, cu=cu, s0=d["initial_state"][1:].contiguous())
+    o_ref, f_ref = oracle_ref(inp)
+    assert rel_err(to_f64(o)[5:], oracle.rms_norm(o_ref[5:], w, 1e-6)) <= tol("bf16")
+    assert rel_err(to_f64(f), f_ref[1:]) <= tol("bf16")
+    assert torch.isnan(o[:5].float()).all()
