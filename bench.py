@@ -349,6 +349,100 @@ def short_prefill_sweep(dev, copies, steps):
         }), flush=True)
 
 
+def probe_copies(dev, mib):
+    """Three device-to-device copies of `mib` MiB: the known-size reference
+    that scales the HBM byte counters of a --pmc run."""
+    if mib <= 0:
+        return
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def summarize_norm(stats_dir: str, fetch_dir: str, write_dir: str, results_jsonl: str, probe_mib: int):
+    """Write profiles/gdn_output_norm.md from runs of `bench.py --norm`: a
+    kernel trace with --stats (whose JSON lines are results_jsonl) and one
+    --pmc FETCH_SIZE and one --pmc WRITE_SIZE pass with --copy-probe-mib."""
+    import csv
+    probe_bytes = probe_mib << 20
+    fetch, ffac, fkib = _counter_means(fetch_dir, "FETCH_SIZE", probe_bytes)
+    write, wfac, wkib = _counter_means(write_dir, "WRITE_SIZE", probe_bytes)
+    rows = list(csv.DictReader(open(os.path.join(stats_dir, "run_kernel_stats.csv"))))
+    res = {}
+    for line in open(results_jsonl):
+        line = line.strip()
+        if line.startswith("{"):
+            d = json.loads(line)
+            res[d["part"]] = d
+    algo = {"decode": decode_bytes_per_step(), "decode_norm": decode_bytes_per_step() + 4 * D,
+            "norm_apply": norm_apply_bytes(T_PREFILL)}
+    lines = [
+        "# Output normalisation: decode batch 64 (fused) and prefill 1x4096 (pass); HK=16, HV=32, d=128, bf16",
+        "",
+        "Made by (from the repository root; OUT is any scratch directory):",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp",
+        "rocprofv3 --kernel-trace --stats -d OUT/stats -o run --output-format csv -- "
+        "python3 REPO/bench.py --norm > OUT/norm.jsonl",
+        "rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run --output-format csv -- "
+        f"python3 REPO/bench.py --norm --steps 5 --copy-probe-mib {probe_mib}",
+        "rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run --output-format csv -- "
+        f"python3 REPO/bench.py --norm --steps 5 --copy-probe-mib {probe_mib}",
+        f"cd REPO && python3 bench.py --summarize-norm OUT/stats OUT/fetch OUT/write OUT/norm.jsonl {probe_mib}",
+        "```",
+        "",
+        f"Kernel sources hash: `{kernel_source_hash()}`.",
+        "",
+        "## Kernel durations (rocprofv3 --kernel-trace --stats)",
+        "",
+        "The run also launches the plain decode and prefill kernels, for comparison.",
+        "",
+        "| kernel | calls | mean us | min us | max us |",
+        "|---|---|---|---|---|",
+    ]
+    for r in rows:
+        short = _short_kernel(r["Name"])
+        if short in KERNELS:
+            lines.append(f"| {KERNELS[short]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += [
+        "",
+        "## HBM bytes per launch (FETCH_SIZE, WRITE_SIZE; scaled by a plain copy)",
+        "",
+        f"A {probe_mib} MiB device-to-device copy in the same runs reads {fkib:.0f} FETCH_SIZE units and "
+        f"{wkib:.0f} WRITE_SIZE units: {ffac:.1f} and {wfac:.1f} bytes per unit.",
+        "",
+        "| kernel | algorithmic MB | fetched MB | written MB | total MB |",
+        "|---|---|---|---|---|",
+    ]
+    for short in ("decode", "decode_norm", "norm_apply"):
+        if short in fetch and short in write:
+            fb, wb = fetch[short] * ffac, write[short] * wfac
+            lines.append(f"| {KERNELS[short]} | {algo[short] / 1e6:.1f} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
+                         f"{(fb + wb) / 1e6:.1f} |")
+    if res:
+        dd, pp = res.get("decode"), res.get("prefill")
+        lines += ["", "## Rates (HIP events in the traced run)", "",
+                  "Taken under the profiler, which adds a per-launch overhead to these event times (compare "
+                  "the kernel durations above); `python3 bench.py --norm` measures the same without it.", ""]
+        if dd:
+            lines.append(f"- decode step, kernel: plain {dd['plain_kernel_ms'] * 1e3:.1f} us, with the norm fused "
+                         f"{dd['norm_kernel_ms'] * 1e3:.1f} us ({dd['norm_kernel_gbs']:.0f} GB/s, "
+                         f"{100 * dd['hbm_frac']:.1f}% of 8 TB/s).")
+        if pp:
+            lines.append(f"- prefill call: plain {pp['plain_ms'] * 1e3:.1f} us, with the norm pass "
+                         f"{pp['norm_ms'] * 1e3:.1f} us; the pass itself {pp['norm_apply_kernel_ms'] * 1e3:.1f} us "
+                         f"({pp['norm_apply_gbs']:.0f} GB/s, {100 * pp['hbm_frac']:.1f}% of 8 TB/s).")
+    with open(os.path.join(ROOT, "profiles", "gdn_output_norm.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def norm_apply_bytes(tokens, hv=HV, dv=D, elem=2):
     """Algorithmic HBM bytes of the prefill's output-normalisation pass: every
     output row read and written once (the weight and cu_seqlens are a few
@@ -458,8 +552,14 @@ def main():
     ap.add_argument("--summarize-short", nargs=2, metavar=("STATS_DIR", "RESULTS_JSONL"),
                     help="host only: turn a kernel trace of --short-prefill into "
                          "profiles/gdn_token_scan_short_prefill.md and exit")
+    ap.add_argument("--summarize-norm", nargs=5,
+                    metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR", "RESULTS_JSONL", "PROBE_MIB"),
+                    help="host only: turn rocprofv3 runs of --norm into profiles/gdn_output_norm.md and exit")
     args = ap.parse_args()
 
+    if args.summarize_norm:
+        summarize_norm(*args.summarize_norm[:4], int(args.summarize_norm[4]))
+        return
     if args.summarize:
         summarize_profiles(*args.summarize[:3], int(args.summarize[3]))
         return
@@ -485,6 +585,7 @@ def main():
         short_prefill_sweep(dev, args.copies, min(args.steps, 30))
         return
     if args.norm:
+        probe_copies(dev, args.copy_probe_mib)
         output_norm_bench(dev, args.copies, min(args.steps, 30))
         return
     print("[bench] generating inputs", file=sys.stderr, flush=True)
@@ -524,14 +625,7 @@ def main():
         sys.exit(1)
 
     stream = torch.cuda.current_stream(dev)
-    if args.copy_probe_mib > 0:
-        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    probe_copies(dev, args.copy_probe_mib)
     for i in range(args.warmup):
         step(sets[i % args.copies])
     torch.cuda.synchronize()

@@ -161,15 +161,17 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(
 //     y_i = o_i w_i / sqrt(mean_j o_j^2 + eps),
 // which needs every row of that head's state. So one workgroup owns a whole
 // (b, h) state: its lanes form groups of LPR lanes as in the plain kernel,
-// and each group holds NRL rows, RPP rows apart (d = 128: 512 threads, four
-// rows per group). The row work and the memory pattern are the plain
-// kernel's; the row outputs stay in registers while the workgroup sums
-// their squares (wave butterflies, then LDS across waves, one barrier), and
-// only the normalised row is written. The unnormalised output never goes to
-// memory.
+// and each group holds NRL rows, RPP rows apart (d = 128: 1024 threads, two
+// rows per group; measured at B = 64 as fast as the plain kernel, where 512
+// threads with four rows each, or 256 with eight, hold more registers per
+// lane, fewer waves per CU, and run 10 to 17% slower). The row work and the
+// memory pattern are the plain kernel's; the row outputs stay in registers
+// while the workgroup sums their squares (wave butterflies, then LDS across
+// waves, one barrier), and only the normalised row is written. The
+// unnormalised output never goes to memory.
 template <int DK, int DV> struct DecodeNormShape {
     static constexpr int LPR = DK / 8;                                  // lanes per state row
-    static constexpr int NRL = DV * LPR > 512 ? DV * LPR / 512 : 1;     // rows per lane group
+    static constexpr int NRL = DV * LPR > 1024 ? DV * LPR / 1024 : 1;     // rows per lane group
     static constexpr int THREADS = DV * LPR / NRL < 64 ? 64 : DV * LPR / NRL;
     static constexpr int RPP = THREADS / LPR;                           // rows per pass
     static constexpr int WAVES = THREADS / 64;
