@@ -29,6 +29,13 @@ What is here:
                        with eps inside the root, times one weight per value
                        channel shared by all heads.
 
+* ``round_to_bf16`` -- rounding of float64 values to the nearest bfloat16
+                       (ties to even), for states stored in bf16 between
+                       calls: the storage variant whose accuracy the pages
+                       argue about (fp32 states in "Maintenir l'etat
+                       recurrent sur la puce" of page 1, bf16 recurrence
+                       states in the engine of page 3).
+
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_pins.py`` (closed forms, invariants, scalar cases worked
 by hand and cross-form brute force).
@@ -263,3 +270,27 @@ def rms_norm(o, weight, eps: float) -> np.ndarray:
     mean_sq = np.mean(o * o, axis=-1, keepdims=True)
     with np.errstate(invalid="ignore", divide="ignore"):
         return o / np.sqrt(mean_sq + float(eps)) * w
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (8 significant
+    bits, the exponent range of float32), ties to even; returned as float64.
+    Overflow goes to +-inf, NaN stays NaN. Written from the definition:
+    scale by a power of two so that the representable neighbours are
+    consecutive integers, then round half to even (numpy's rint)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, dtype=np.float64, copy=True)
+    fin = np.isfinite(x) & (x != 0.0)
+    ax = np.abs(x[fin])
+    # exponent e with 2^e <= |x| < 2^(e+1); below 2^-126 the spacing stays
+    # that of the smallest normal exponent (subnormals)
+    e = np.maximum(np.floor(np.log2(ax)), -126.0)
+    # guard the floor of log2 against rounding at exact powers of two
+    e = np.where(np.ldexp(1.0, e.astype(np.int64)) > ax, e - 1, e)
+    e = np.where(np.ldexp(1.0, (e + 1).astype(np.int64)) <= ax, e + 1, e)
+    e = np.maximum(e, -126.0)
+    ulp_exp = (e - 7).astype(np.int64)  # 7 fraction bits
+    r = np.ldexp(np.rint(np.ldexp(ax, -ulp_exp)), ulp_exp)
+    r = np.where(r >= 2.0 ** 128, np.inf, r)  # past the largest finite bf16 (rounded up into 2^128)
+    out[fin] = np.sign(x[fin]) * r
+    return out

@@ -363,3 +363,39 @@ def test_rms_norm_scale_invariant_and_zero_rows():
     assert np.isnan(oracle.rms_norm(np.zeros(32), w, 0.0)).all()
     with pytest.raises(ValueError):
         oracle.rms_norm(o, w[:31], 1e-6)
+
+
+# ------------------------------------------------------ bf16 rounding pins
+#
+# round_to_bf16 rounds float64 to the nearest bfloat16 (8 significant bits),
+# ties to even. Hand-worked values fix the tie rule and the scale; the
+# storage generator's independent float32 -> bf16 bit routine fixes every
+# exponent range it covers.
+
+def test_round_to_bf16_hand_worked():
+    r = oracle.round_to_bf16
+    # spacing at 1 is 2^-7: 1 + 2^-8 is a tie (to the even 1.0); 1 + 3 2^-8
+    # lies between 1 + 2^-7 (odd) and 1 + 2^-6 (even) on a tie too
+    assert r(1 + 2.0 ** -8) == 1.0
+    assert r(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6
+    assert r(-(1 + 3 * 2.0 ** -8)) == -(1 + 2.0 ** -6)
+    assert r(1 + 2.0 ** -8 + 2.0 ** -20) == 1 + 2.0 ** -7  # just past the tie
+    assert r(0.1) == 0.10009765625  # 0x3DCD
+    assert r(2.0 ** -130) == 2.0 ** -130  # subnormal, exact
+    big = (2 - 2.0 ** -7) * 2.0 ** 127  # largest finite bf16
+    assert r(big) == big
+    assert r(big + 2.0 ** 119 - 2.0 ** 100) == big  # below the tie with 2^128
+    assert r(big + 2.0 ** 119) == np.inf  # the tie rounds to even: 2^128 overflows
+    assert r(0.0) == 0.0 and np.isnan(r(np.nan))
+
+
+def test_round_to_bf16_matches_bit_rounding_of_float32():
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000)).astype(np.float32)
+    want = gs.bf16_bits_to_f32(gs.f32_to_bf16_bits(x)).astype(np.float64)
+    got = oracle.round_to_bf16(x.astype(np.float64))
+    assert np.array_equal(got, want)
+    # idempotent and monotone
+    assert np.array_equal(oracle.round_to_bf16(got), got)
+    xs = np.sort(x.astype(np.float64))
+    assert np.all(np.diff(oracle.round_to_bf16(xs)) >= 0)
