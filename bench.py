@@ -57,10 +57,12 @@ def prep_flops_per_token(hk=HK, dk=D, c=CHUNK):
     return hk * 4 * c * dk
 
 
-def decode_bytes_per_step(b=B_DECODE, hk=HK, hv=HV, dk=D, dv=D):
-    """Algorithmic HBM bytes of one decode step: the fp32 state read and
-    written once, bf16 q, k (per q/k head), v, gates and output."""
-    return b * hv * dv * dk * 4 * 2 + b * (2 * hk * dk + hv * dv) * 2 + b * hv * 2 * 2 + b * hv * dv * 2
+def decode_bytes_per_step(b=B_DECODE, hk=HK, hv=HV, dk=D, dv=D, state_bytes=4):
+    """Algorithmic HBM bytes of one decode step: the state (fp32, or bf16 with
+    state_bytes=2) read and written once, bf16 q, k (per q/k head), v, gates
+    and output."""
+    return (b * hv * dv * dk * state_bytes * 2 + b * (2 * hk * dk + hv * dv) * 2 + b * hv * 2 * 2
+            + b * hv * dv * 2)
 
 
 def kernel_source_hash() -> str:
@@ -99,11 +101,21 @@ def _short_kernel(name: str) -> str:
     return "copy" if "copy" in name.lower() else "other"
 
 
-def _counter_means(directory: str, counter: str, probe_bytes: int):
+def _state_key(name: str) -> str:
+    """Short kernel name, with "/bf16" appended for decode kernels built for
+    bf16 state storage (their third template argument)."""
+    import re
+    short = _short_kernel(name)
+    m = re.search(r"gdn_decode(?:_norm)?_kernelI(?:DF16b|f)(?:DF16b|f)(DF16b|f)Li", name)
+    return short + "/bf16" if m and m.group(1) == "DF16b" else short
+
+
+def _counter_means(directory: str, counter: str, probe_bytes: int, key=None):
     """Mean counter value (KiB) per dispatch of each library kernel, and the
     factor that maps the counter to bytes, taken from the probe copies (the
     dispatches of a copy kernel within 10% of the largest one)."""
     import csv
+    key = key or _short_kernel
     path = os.path.join(directory, "run_counter_collection.csv")
     per = {}
     copies = []
@@ -111,7 +123,7 @@ def _counter_means(directory: str, counter: str, probe_bytes: int):
         for r in csv.DictReader(f):
             if r["Counter_Name"] != counter:
                 continue
-            short = _short_kernel(r["Kernel_Name"])
+            short = key(r["Kernel_Name"])
             val = float(r["Counter_Value"])
             if short == "copy":
                 copies.append(val)
@@ -443,6 +455,77 @@ def summarize_norm(stats_dir: str, fetch_dir: str, write_dir: str, results_jsonl
         f.write("\n".join(lines) + "\n")
 
 
+def summarize_state(stats_dir: str, fetch_dir: str, write_dir: str, results_jsonl: str, probe_mib: int):
+    """Write profiles/gdn_decode_state_storage.md from runs of `bench.py
+    --bf16-state`: a kernel trace with --stats (whose JSON lines are
+    results_jsonl) and one --pmc FETCH_SIZE and one --pmc WRITE_SIZE pass
+    with --copy-probe-mib."""
+    import csv
+    probe_bytes = probe_mib << 20
+    fetch, ffac, fkib = _counter_means(fetch_dir, "FETCH_SIZE", probe_bytes, key=_state_key)
+    write, wfac, wkib = _counter_means(write_dir, "WRITE_SIZE", probe_bytes, key=_state_key)
+    rows = list(csv.DictReader(open(os.path.join(stats_dir, "run_kernel_stats.csv"))))
+    lines = [
+        f"# Decode batch {B_DECODE} with fp32 and bf16 state storage (HK={HK}, HV={HV}, d={D}, bf16 I/O)",
+        "",
+        "Made by (from the repository root; OUT is any scratch directory):",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp",
+        "rocprofv3 --kernel-trace --stats -d OUT/stats -o run --output-format csv -- "
+        "python3 REPO/bench.py --bf16-state > OUT/state.jsonl",
+        "rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run --output-format csv -- "
+        f"python3 REPO/bench.py --bf16-state --steps 5 --copy-probe-mib {probe_mib}",
+        "rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run --output-format csv -- "
+        f"python3 REPO/bench.py --bf16-state --steps 5 --copy-probe-mib {probe_mib}",
+        f"cd REPO && python3 bench.py --summarize-state OUT/stats OUT/fetch OUT/write OUT/state.jsonl {probe_mib}",
+        "```",
+        "",
+        f"Kernel sources hash: `{kernel_source_hash()}`.",
+        "",
+        "## Kernel durations (rocprofv3 --kernel-trace --stats)",
+        "",
+        "| kernel | state | calls | mean us | min us | max us |",
+        "|---|---|---|---|---|---|",
+    ]
+    for r in rows:
+        k = _state_key(r["Name"])
+        short = k.split("/")[0]
+        if short in ("decode", "decode_norm"):
+            lines.append(f"| {KERNELS[short]} | {'bf16' if k.endswith('/bf16') else 'fp32'} | {r['Calls']} | "
+                         f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                         f"{float(r['MaxNs']) / 1e3:.2f} |")
+    lines += [
+        "",
+        "## HBM bytes per launch (FETCH_SIZE, WRITE_SIZE; scaled by a plain copy)",
+        "",
+        f"A {probe_mib} MiB device-to-device copy in the same runs reads {fkib:.0f} FETCH_SIZE units and "
+        f"{wkib:.0f} WRITE_SIZE units: {ffac:.1f} and {wfac:.1f} bytes per unit.",
+        "",
+        "| kernel | state | algorithmic MB | fetched MB | written MB | total MB |",
+        "|---|---|---|---|---|---|",
+    ]
+    for k in ("decode", "decode/bf16", "decode_norm", "decode_norm/bf16"):
+        if k in fetch and k in write:
+            short, bf = k.split("/")[0], k.endswith("/bf16")
+            algo = decode_bytes_per_step(state_bytes=2 if bf else 4) + (4 * D if short == "decode_norm" else 0)
+            fb, wb = fetch[k] * ffac, write[k] * wfac
+            lines.append(f"| {KERNELS[short]} | {'bf16' if bf else 'fp32'} | {algo / 1e6:.1f} | {fb / 1e6:.1f} | "
+                         f"{wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} |")
+    lines += ["", "## Rates (HIP events in the traced run)", "",
+              "Taken under the profiler, which adds a per-launch overhead to these event times; "
+              "`python3 bench.py --bf16-state` measures the same without it.", "",
+              "| state | norm | kernel us | tokens/s | GB/s | of 8 TB/s |", "|---|---|---|---|---|---|"]
+    for line in open(results_jsonl):
+        line = line.strip()
+        if line.startswith("{"):
+            d = json.loads(line)
+            lines.append(f"| {d['state_dtype']} | {'fused' if d['norm'] else 'no'} | {d['kernel_ms'] * 1e3:.1f} | "
+                         f"{d['tokens_per_s'] / 1e6:.2f} M | {d['kernel_gbs']:.0f} | {100 * d['hbm_frac']:.1f}% |")
+    with open(os.path.join(ROOT, "profiles", "gdn_decode_state_storage.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def norm_apply_bytes(tokens, hv=HV, dv=D, elem=2):
     """Algorithmic HBM bytes of the prefill's output-normalisation pass: every
     output row read and written once (the weight and cu_seqlens are a few
@@ -530,6 +613,56 @@ def output_norm_bench(dev, copies, steps):
     }), flush=True)
 
 
+def state_storage_bench(dev, copies, steps):
+    """Decode batch 64 with the state pool stored in fp32 and in bf16 (fp32
+    arithmetic either way), without and with the fused output norm. One JSON
+    line per case; kernel times from the library's dispatch-stamped events,
+    HBM rate from the algorithmic bytes (state read and written once, plus
+    q, k, v, gates and output)."""
+    import torch
+    import gdn_synth as gs
+    import gated_deltanet_linear_02_amd as gdn
+    w = torch.from_numpy(gs.norm_weight(D, seed=gs.SEED_BASE + 505)).to(dev)
+    dec = gs.workload("decode", batch=B_DECODE)
+    s_dec = gs.decode_state(B_DECODE, HV, D, D, seed=gs.SEED_BASE + 101)
+    for sdt in (torch.float32, torch.bfloat16):
+        sets = []
+        for _ in range(copies):
+            d = device_inputs(dec, dev)
+            d["state"] = torch.from_numpy(s_dec).to(dev).to(sdt)
+            d["out"] = torch.empty((B_DECODE, HV, D), dtype=torch.bfloat16, device=dev)
+            sets.append(d)
+        for norm in (False, True):
+            def run(d):
+                gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], out=d["out"],
+                                norm_weight=w if norm else None)
+            for i in range(3):
+                run(sets[i % copies])
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(steps):
+                run(sets[i % copies])
+            e1.record()
+            torch.cuda.synchronize()
+            call_ms = e0.elapsed_time(e1) / steps
+            gdn.timing_start(steps)
+            for i in range(steps):
+                run(sets[i % copies])
+            kind = "decode_norm" if norm else "decode"
+            kms = gdn.timing_stop()[kind]["mean_ms"]
+            sb = 2 if sdt == torch.bfloat16 else 4
+            by = decode_bytes_per_step(state_bytes=sb) + (4 * D if norm else 0)
+            gbs = by / (kms * 1e-3) / 1e9
+            print(json.dumps({
+                "mode": "state-storage", "state_dtype": "bf16" if sb == 2 else "f32", "norm": norm,
+                "call_ms": call_ms, "kernel_ms": kms, "tokens_per_s": B_DECODE / (kms * 1e-3),
+                "kernel_gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": by,
+                "dtype": "bf16", "data": "synthetic", "buffer_copies": copies,
+                "config": {"workload": f"decode batch {B_DECODE}, HK={HK}, HV={HV}, d={D}"},
+            }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -543,6 +676,9 @@ def main():
     ap.add_argument("--norm", action="store_true",
                     help="instead of the main line: decode and prefill with the output normalisation "
                          "against the plain calls, one JSON line each")
+    ap.add_argument("--bf16-state", action="store_true",
+                    help="instead of the main line: decode with fp32 and with bf16 state storage, "
+                         "one JSON line per case")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, run 3 device-to-device copies of this many MiB "
                          "(the known-size reference for HBM byte counters)")
@@ -555,8 +691,15 @@ def main():
     ap.add_argument("--summarize-norm", nargs=5,
                     metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR", "RESULTS_JSONL", "PROBE_MIB"),
                     help="host only: turn rocprofv3 runs of --norm into profiles/gdn_output_norm.md and exit")
+    ap.add_argument("--summarize-state", nargs=5,
+                    metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR", "RESULTS_JSONL", "PROBE_MIB"),
+                    help="host only: turn rocprofv3 runs of --bf16-state into "
+                         "profiles/gdn_decode_state_storage.md and exit")
     args = ap.parse_args()
 
+    if args.summarize_state:
+        summarize_state(*args.summarize_state[:4], int(args.summarize_state[4]))
+        return
     if args.summarize_norm:
         summarize_norm(*args.summarize_norm[:4], int(args.summarize_norm[4]))
         return
@@ -583,6 +726,10 @@ def main():
     torch.cuda.set_device(dev)
     if args.short_prefill:
         short_prefill_sweep(dev, args.copies, min(args.steps, 30))
+        return
+    if args.bf16_state:
+        probe_copies(dev, args.copy_probe_mib)
+        state_storage_bench(dev, args.copies, min(args.steps, 30))
         return
     if args.norm:
         probe_copies(dev, args.copy_probe_mib)

@@ -9,8 +9,9 @@ been built, importing works but every call raises.
 Entry points (same names as the C ABI, without the ``gdn_`` prefix):
     prefill(q, k, v, g, beta, cu_seqlens, ...)  -> (out, final_state)
     decode_step(q, k, v, g, beta, state, ...)   -> out
-    (with ``norm_weight=`` they call gdn_prefill_norm / gdn_decode_step_norm:
-    the output rows RMS-normalised, times one weight per value channel)
+    (bf16 state tensors, or ``norm_weight=``, call gdn_prefill_ex /
+    gdn_decode_step_ex: states stored in bf16 with fp32 arithmetic, and the
+    output rows RMS-normalised, times one weight per value channel)
     prefill_workspace_size(...)
     timing_start(max_launches) / timing_stop()  -> per-kernel launch times
 """
@@ -74,15 +75,15 @@ def load():
         L.gdn_prefill.restype = i32
         L.gdn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
                                   f32, i32, i32, vp, vp, vp, vp, sz, vp]
-        L.gdn_prefill_norm.restype = i32
-        L.gdn_prefill_norm.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
-                                       f32, i32, i32, vp, vp, vp, f32, vp, vp, sz, vp]
+        L.gdn_prefill_ex.restype = i32
+        L.gdn_prefill_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
+                                     f32, i32, i32, vp, vp, i32, vp, f32, vp, vp, sz, vp]
         L.gdn_decode_step.restype = i32
         L.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32,
                                       vp, vp, i32, vp, vp]
-        L.gdn_decode_step_norm.restype = i32
-        L.gdn_decode_step_norm.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32,
-                                           vp, vp, i32, vp, f32, vp, vp]
+        L.gdn_decode_step_ex.restype = i32
+        L.gdn_decode_step_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32,
+                                         vp, i32, vp, i32, vp, f32, vp, vp]
         L.gdn_timing_start.restype = i32
         L.gdn_timing_start.argtypes = [i32]
         L.gdn_timing_stop.restype = i32
@@ -147,7 +148,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
             initial_state: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
             write_final_state: bool = True, norm_weight: Optional[torch.Tensor] = None,
-            norm_eps: float = 1e-6, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            norm_eps: float = 1e-6, state_dtype: Optional[torch.dtype] = None,
+            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Prefill over packed sequences (``gdn_prefill``).
 
     q, k [T, hk, dk]; v [T, hv, dv] (bf16 or fp32, one dtype); g, beta [T, hv]
@@ -156,7 +158,9 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     ``chunk``: 16, 32 or 64 (chunked), 1 (token by token) or 0 (token by
     token when T <= max(64, 16 N), else chunks of 64).
     ``norm_weight`` (fp32 [dv], or None): RMS-normalise every output row,
-    y = o * w / sqrt(mean(o^2) + norm_eps) (``gdn_prefill_norm``).
+    y = o * w / sqrt(mean(o^2) + norm_eps).
+    States are fp32 or bf16 (``gdn_prefill_ex``): the dtype of the state
+    tensors given, else ``state_dtype`` (default fp32).
     Missing out / final_state / workspace are allocated with torch.
     """
     T, hk, dk = q.shape
@@ -169,27 +173,34 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     dev = q.device
     if out is None:
         out = torch.empty((T, hv, dv), dtype=q.dtype, device=dev)
+    given = {t.dtype for t in (initial_state, final_state) if t is not None}
+    if len(given) > 1:
+        raise TypeError("initial_state and final_state must have one dtype")
+    sdt = given.pop() if given else (state_dtype or torch.float32)
+    if state_dtype is not None and sdt != state_dtype:
+        raise TypeError(f"state tensors are {sdt}, state_dtype says {state_dtype}")
     if final_state is None and write_final_state:
-        final_state = torch.empty((N, hv, dv, dk), dtype=torch.float32, device=dev)
+        final_state = torch.empty((N, hv, dv, dk), dtype=sdt, device=dev)
     need = prefill_workspace_size(N, T, hk, hv, dk, dv, chunk, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _on_device(dev, k=k, v=v, g=g, beta=beta, cu_seqlens=cu_seqlens, initial_state=initial_state,
                final_state=final_state, out=out, workspace=workspace, norm_weight=norm_weight)
     ws_bytes = workspace.numel() * workspace.element_size()
-    if norm_weight is None:
+    if norm_weight is None and sdt == torch.float32:
         status = load().gdn_prefill(
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
             hk, hv, dk, dv, chunk, float(scale), io, gate,
             _ptr(initial_state), _ptr(final_state), _ptr(out),
             _ptr(workspace), ws_bytes, _stream(dev, stream))
     else:
-        _check_norm_weight(norm_weight, dv)
-        status = load().gdn_prefill_norm(
+        if norm_weight is not None:
+            _check_norm_weight(norm_weight, dv)
+        status = load().gdn_prefill_ex(
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
             hk, hv, dk, dv, chunk, float(scale), io, gate,
-            _ptr(initial_state), _ptr(final_state), _ptr(norm_weight), float(norm_eps), _ptr(out),
-            _ptr(workspace), ws_bytes, _stream(dev, stream))
+            _ptr(initial_state), _ptr(final_state), _dtype_code(sdt), _ptr(norm_weight), float(norm_eps),
+            _ptr(out), _ptr(workspace), ws_bytes, _stream(dev, stream))
     _check(status)
     return out, final_state
 
@@ -202,28 +213,31 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     (``gdn_decode_step``). q, k [B, hk, dk]; v [B, hv, dv]; g, beta [B, hv];
     state [slots, hv, dv, dk]; state_slots int32 [B] on the device or None.
     ``norm_weight`` (fp32 [dv], or None): the output rows RMS-normalised in
-    the same kernel (``gdn_decode_step_norm``)."""
+    the same kernel. A bf16 ``state`` is stored in bf16 between steps, with
+    fp32 arithmetic (``gdn_decode_step_ex``)."""
     B, hk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
-    if state.dtype != torch.float32:
-        raise TypeError("state must be float32")
+    if state.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("state must be float32 or bfloat16")
     if state_slots is not None and state_slots.dtype != torch.int32:
         raise TypeError("state_slots must be int32")
     if out is None:
         out = torch.empty((B, hv, dv), dtype=q.dtype, device=q.device)
     _on_device(q.device, k=k, v=v, g=g, beta=beta, state=state, state_slots=state_slots, out=out,
                norm_weight=norm_weight)
-    if norm_weight is None:
+    if norm_weight is None and state.dtype == torch.float32:
         status = load().gdn_decode_step(
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), B, hk, hv, dk, dv, float(scale),
             _dtype_code(q.dtype), _dtype_code(g.dtype), _ptr(state), _ptr(state_slots),
             state.shape[0], _ptr(out), _stream(q.device, stream))
     else:
-        _check_norm_weight(norm_weight, dv)
-        status = load().gdn_decode_step_norm(
+        if norm_weight is not None:
+            _check_norm_weight(norm_weight, dv)
+        status = load().gdn_decode_step_ex(
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), B, hk, hv, dk, dv, float(scale),
-            _dtype_code(q.dtype), _dtype_code(g.dtype), _ptr(state), _ptr(state_slots),
-            state.shape[0], _ptr(norm_weight), float(norm_eps), _ptr(out), _stream(q.device, stream))
+            _dtype_code(q.dtype), _dtype_code(g.dtype), _ptr(state), _dtype_code(state.dtype),
+            _ptr(state_slots), state.shape[0], _ptr(norm_weight), float(norm_eps), _ptr(out),
+            _stream(q.device, stream))
     _check(status)
     return out
 

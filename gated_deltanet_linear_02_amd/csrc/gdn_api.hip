@@ -127,16 +127,28 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_
 // eps of the output normalisation: finite and not negative.
 static bool valid_eps(float eps) { return std::isfinite(eps) && eps >= 0.f; }
 
-// gdn_prefill, and gdn_prefill_norm when norm_w is not NULL.
+// The state storage type and output normalisation of a call, checked
+// before anything else of the call: bf16 states need bf16 I/O, a weight
+// needs a finite eps >= 0.
+static int32_t check_options(int32_t io_dtype, int32_t state_dtype, const float *norm_w, float norm_eps) {
+    if (!valid_dtype(state_dtype)) return GDN_ERR_UNSUPPORTED;
+    if (state_dtype == GDN_BF16 && io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (norm_w && !valid_eps(norm_eps)) return GDN_ERR_BAD_VALUE;
+    return GDN_OK;
+}
+
+// gdn_prefill and gdn_prefill_ex.
 static int32_t prefill_impl(const void *q, const void *k, const void *v, const void *g, const void *beta,
                             const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                             int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
                             float scale, int32_t io_dtype, int32_t gate_dtype,
-                            const float *initial_state, float *final_state,
+                            const void *initial_state, void *final_state, int32_t state_dtype,
                             const float *norm_w, float norm_eps, void *out,
                             void *workspace, size_t workspace_bytes, void *stream) {
     const int32_t sc = check_prefill_shape(num_seqs, total_tokens, hk, hv, dk, dv, chunk, io_dtype, gate_dtype);
     if (sc != GDN_OK) return sc;
+    const int32_t so = check_options(io_dtype, state_dtype, norm_w, norm_eps);
+    if (so != GDN_OK) return so;
     if (!cu_seqlens) return GDN_ERR_NULL_ARG;
     if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL_ARG;
 
@@ -148,7 +160,7 @@ static int32_t prefill_impl(const void *q, const void *k, const void *v, const v
         return GDN_ERR_WORKSPACE;
 
     const size_t T = (size_t)total_tokens;
-    const size_t state_bytes = (size_t)num_seqs * hv * dv * dk * sizeof(float);
+    const size_t state_bytes = (size_t)num_seqs * hv * dv * dk * dtype_bytes(state_dtype);
     const Range r_out = span(out, T * hv * dv * eb);
     const Range inputs[] = {span(q, T * hk * dk * eb), span(k, T * hk * dk * eb), span(v, T * hv * dv * eb),
                             span(g, T * hv * gb), span(beta, T * hv * gb),
@@ -173,6 +185,7 @@ static int32_t prefill_impl(const void *q, const void *k, const void *v, const v
     A.cu = cu_seqlens; A.num_seqs = num_seqs; A.total_tokens = total_tokens;
     A.hk = hk; A.hv = hv; A.d = dk; A.chunk = c; A.scale = scale;
     A.io_bf16 = io_dtype == GDN_BF16; A.gate_bf16 = gate_dtype == GDN_BF16;
+    A.state_bf16 = state_dtype == GDN_BF16;
     A.s0 = initial_state; A.s_final = final_state; A.out = out;
     A.ws = static_cast<char *>(workspace); A.lay = L;
     try {
@@ -197,32 +210,33 @@ int32_t gdn_prefill(const void *q, const void *k, const void *v, const void *g, 
                     const float *initial_state, float *final_state, void *out,
                     void *workspace, size_t workspace_bytes, void *stream) {
     return prefill_impl(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, hk, hv, dk, dv, chunk, scale,
-                        io_dtype, gate_dtype, initial_state, final_state, nullptr, 0.f, out, workspace,
+                        io_dtype, gate_dtype, initial_state, final_state, GDN_F32, nullptr, 0.f, out, workspace,
                         workspace_bytes, stream);
 }
 
-int32_t gdn_prefill_norm(const void *q, const void *k, const void *v, const void *g, const void *beta,
-                         const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
-                         int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
-                         float scale, int32_t io_dtype, int32_t gate_dtype,
-                         const float *initial_state, float *final_state,
-                         const float *norm_weight, float norm_eps, void *out,
-                         void *workspace, size_t workspace_bytes, void *stream) {
-    if (!norm_weight) return GDN_ERR_NULL_ARG;
-    if (!valid_eps(norm_eps)) return GDN_ERR_BAD_VALUE;
+int32_t gdn_prefill_ex(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                       const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                       int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
+                       float scale, int32_t io_dtype, int32_t gate_dtype,
+                       const void *initial_state, void *final_state, int32_t state_dtype,
+                       const float *norm_weight, float norm_eps, void *out,
+                       void *workspace, size_t workspace_bytes, void *stream) {
     return prefill_impl(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, hk, hv, dk, dv, chunk, scale,
-                        io_dtype, gate_dtype, initial_state, final_state, norm_weight, norm_eps, out, workspace,
-                        workspace_bytes, stream);
+                        io_dtype, gate_dtype, initial_state, final_state, state_dtype, norm_weight, norm_eps, out,
+                        workspace, workspace_bytes, stream);
 }
 
-// gdn_decode_step, and gdn_decode_step_norm when norm_w is not NULL.
+// gdn_decode_step and gdn_decode_step_ex.
 static int32_t decode_impl(const void *q, const void *k, const void *v, const void *g, const void *beta,
                            int32_t batch, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float scale,
-                           int32_t io_dtype, int32_t gate_dtype, float *state, const int32_t *state_slots,
-                           int32_t num_slots, const float *norm_w, float norm_eps, void *out, void *stream) {
+                           int32_t io_dtype, int32_t gate_dtype, void *state, int32_t state_dtype,
+                           const int32_t *state_slots, int32_t num_slots, const float *norm_w, float norm_eps,
+                           void *out, void *stream) {
     if (batch < 0 || hk < 1 || hv < 1 || hv % hk != 0 || num_slots < 0) return GDN_ERR_BAD_SHAPE;
     if (!valid_head(dk) || dv != dk || !valid_dtype(io_dtype) || !valid_dtype(gate_dtype))
         return GDN_ERR_UNSUPPORTED;
+    const int32_t so = check_options(io_dtype, state_dtype, norm_w, norm_eps);
+    if (so != GDN_OK) return so;
     if (batch == 0) return GDN_OK;
     if ((int64_t)batch * hv > INT32_MAX) return GDN_ERR_UNSUPPORTED;
     if (!state_slots && num_slots < batch) return GDN_ERR_BAD_SHAPE;
@@ -230,7 +244,7 @@ static int32_t decode_impl(const void *q, const void *k, const void *v, const vo
 
     const size_t eb = dtype_bytes(io_dtype), gb = dtype_bytes(gate_dtype), B = (size_t)batch;
     const Range r_out = span(out, B * hv * dv * eb);
-    const Range r_state = span(state, (size_t)num_slots * hv * dv * dk * sizeof(float));
+    const Range r_state = span(state, (size_t)num_slots * hv * dv * dk * dtype_bytes(state_dtype));
     const Range inputs[] = {span(q, B * hk * dk * eb), span(k, B * hk * dk * eb), span(v, B * hv * dv * eb),
                             span(g, B * hv * gb), span(beta, B * hv * gb),
                             span(state_slots, B * sizeof(int32_t)), span(norm_w, sizeof(float) * (size_t)dv),
@@ -245,6 +259,7 @@ static int32_t decode_impl(const void *q, const void *k, const void *v, const vo
     A.state = state; A.slots = state_slots; A.num_slots = num_slots; A.out = out;
     A.batch = batch; A.hk = hk; A.hv = hv; A.d = dk; A.scale = scale;
     A.io_bf16 = io_dtype == GDN_BF16; A.gate_bf16 = gate_dtype == GDN_BF16;
+    A.state_bf16 = state_dtype == GDN_BF16;
     A.norm_w = norm_w; A.norm_eps = norm_eps;
     try {
         const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -259,19 +274,17 @@ int32_t gdn_decode_step(const void *q, const void *k, const void *v, const void 
                         int32_t batch, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float scale,
                         int32_t io_dtype, int32_t gate_dtype, float *state, const int32_t *state_slots,
                         int32_t num_slots, void *out, void *stream) {
-    return decode_impl(q, k, v, g, beta, batch, hk, hv, dk, dv, scale, io_dtype, gate_dtype, state, state_slots,
-                       num_slots, nullptr, 0.f, out, stream);
+    return decode_impl(q, k, v, g, beta, batch, hk, hv, dk, dv, scale, io_dtype, gate_dtype, state, GDN_F32,
+                       state_slots, num_slots, nullptr, 0.f, out, stream);
 }
 
-int32_t gdn_decode_step_norm(const void *q, const void *k, const void *v, const void *g, const void *beta,
-                             int32_t batch, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float scale,
-                             int32_t io_dtype, int32_t gate_dtype, float *state, const int32_t *state_slots,
-                             int32_t num_slots, const float *norm_weight, float norm_eps, void *out,
-                             void *stream) {
-    if (!norm_weight) return GDN_ERR_NULL_ARG;
-    if (!valid_eps(norm_eps)) return GDN_ERR_BAD_VALUE;
-    return decode_impl(q, k, v, g, beta, batch, hk, hv, dk, dv, scale, io_dtype, gate_dtype, state, state_slots,
-                       num_slots, norm_weight, norm_eps, out, stream);
+int32_t gdn_decode_step_ex(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                           int32_t batch, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float scale,
+                           int32_t io_dtype, int32_t gate_dtype, void *state, int32_t state_dtype,
+                           const int32_t *state_slots, int32_t num_slots, const float *norm_weight,
+                           float norm_eps, void *out, void *stream) {
+    return decode_impl(q, k, v, g, beta, batch, hk, hv, dk, dv, scale, io_dtype, gate_dtype, state, state_dtype,
+                       state_slots, num_slots, norm_weight, norm_eps, out, stream);
 }
 
 int32_t gdn_timing_start(int32_t max_launches) {

@@ -18,12 +18,16 @@
 // Mapping: the rows of one (b, h) state are independent, so they are split
 // over several 256-thread workgroups of ROWS rows each: small workgroups keep
 // more of them in flight, which is what an in-place read-then-write stream
-// needs to approach the HBM rate. A state row (dk fp32) is split over
-// LPR = dk/8 consecutive lanes; lane lr holds 8 elements of the row as two
-// 16-byte pieces at columns 4*lr + 4*LPR*m (m = 0, 1), so that for each load
-// the LPR lanes of a row read 16*LPR contiguous bytes. Row dot products finish
-// with log2(LPR) butterfly shuffles. Each workgroup recomputes k.q (dk
-// products), which is negligible.
+// needs to approach the HBM rate. A state row (dk elements) is split over
+// LPR = dk/8 consecutive lanes, 8 elements per lane (StateLane below gives
+// their columns: two 16-byte pieces of fp32, or one of bf16), and each group
+// of LPR lanes holds NRL rows. Row dot products finish with log2(LPR)
+// butterfly shuffles. Each workgroup recomputes k.q (dk products), which is
+// negligible.
+//
+// States are fp32, or bf16 with fp32 arithmetic (widened on load, rounded to
+// nearest even on store): the storage variant that halves the bytes per
+// token, whose accuracy the pages argue about.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -40,29 +44,78 @@ template <> __device__ __forceinline__ void load4<bf16>(const bf16 *p, float *ds
     dst[2] = static_cast<float>(x[2]); dst[3] = static_cast<float>(x[3]);
 }
 
-template <int DK, int DV> struct DecodeShape {
+// Rows a lane group holds in the plain decode kernel, by storage type. A bf16
+// state row is half the bytes, so each lane takes four rows to keep as many
+// bytes in flight (measured at batch 64, d = 128: 26.0 us with four, 26.6
+// with two, 31.2 with one); fp32 rows stay at one per group (two or more
+// change nothing there).
+template <typename SE> constexpr int kDecodeRowsPerLane = 1;
+template <> constexpr int kDecodeRowsPerLane<bf16> = 4;
+
+template <typename SE, int DK, int DV> struct DecodeShape {
     static constexpr int EPL = 8;                  // state elements per lane
     static constexpr int LPR = DK / EPL;           // lanes per state row
-    static constexpr int ROWS = 256 / LPR;         // rows per workgroup
+    static constexpr int RPP = 256 / LPR;          // rows per pass of the workgroup
+    // rows per lane group
+    static constexpr int NRL = RPP >= DV ? 1 : (kDecodeRowsPerLane<SE> < DV / RPP ? kDecodeRowsPerLane<SE> : DV / RPP);
+    static constexpr int ROWS = RPP * NRL;         // rows per workgroup
     static constexpr int SLICES = (DV + ROWS - 1) / ROWS;  // workgroups per (b, h)
 };
 
-// A lane's share of one state row: the 16-byte pieces at columns 4*lr and
-// 4*lr + 4*LPR. The arithmetic below is shared by both decode kernels (with
-// explicit fused multiply-adds, so that the compiler cannot contract it
-// differently in each): they leave bit-identical states.
+// A lane's share of one state row: 8 elements, held as floats whatever the
+// storage type SE. fp32 storage: two 16-byte pieces at columns 4 lr and
+// 4 lr + 4 LPR, so that the LPR lanes of a row read 16 LPR contiguous bytes
+// per load; bf16 storage: one 16-byte piece at columns 8 lr .. 8 lr + 7.
+// Element j of the lane sits at column col(lr, j); columns 4m .. 4m + 3 of
+// the lane are consecutive in both layouts. States are read and written
+// once per step, so the accesses are nontemporal.
+template <typename SE, int LPR> struct StateLane;
+template <int LPR> struct StateLane<float, LPR> {
+    static __device__ __forceinline__ int col(int lr, int j) { return 4 * lr + 4 * LPR * (j >> 2) + (j & 3); }
+    static __device__ __forceinline__ void load(const float *row, int lr, float (&s)[8]) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + col(lr, 4 * m)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[4 * m + e] = x[e];
+        }
+    }
+    static __device__ __forceinline__ void store(float *row, int lr, const float (&w)[8]) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const f32x4 x = {w[4 * m], w[4 * m + 1], w[4 * m + 2], w[4 * m + 3]};
+            __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(row + col(lr, 4 * m)));
+        }
+    }
+};
+template <int LPR> struct StateLane<bf16, LPR> {
+    static __device__ __forceinline__ int col(int lr, int j) { return 8 * lr + j; }
+    static __device__ __forceinline__ void load(const bf16 *row, int lr, float (&s)[8]) {
+        const bf16x8 x = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(row + 8 * lr));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s[j] = static_cast<float>(x[j]);
+    }
+    static __device__ __forceinline__ void store(bf16 *row, int lr, const float (&w)[8]) {
+        bf16x8 x;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = static_cast<bf16>(w[j]);  // round to nearest even
+        __builtin_nontemporal_store(x, reinterpret_cast<bf16x8 *>(row + 8 * lr));
+    }
+};
+
+// The arithmetic below is shared by both decode kernels (with explicit fused
+// multiply-adds, so that the compiler cannot contract it differently in
+// each): they leave bit-identical states.
 template <int LPR> __device__ __forceinline__ float lane_group_sum(float x) {
 #pragma unroll
     for (int off = 1; off < LPR; off <<= 1) x += __shfl_xor(x, off);
     return x;
 }
 template <int LPR>
-__device__ __forceinline__ float row_dot(const f32x4 (&s)[2], const float (&x)[8]) {
+__device__ __forceinline__ float row_dot(const float (&s)[8], const float (&x)[8]) {
     float acc = 0.f;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(s[m][e], x[4 * m + e], acc);
+    for (int j = 0; j < 8; ++j) acc = __builtin_fmaf(s[j], x[j], acc);
     return lane_group_sum<LPR>(acc);
 }
 template <int LPR>
@@ -79,35 +132,36 @@ __device__ __forceinline__ float write_strength(float beta, float a, float vv, f
 __device__ __forceinline__ float row_output(float scale, float a, float sq, float kq, float u) {
     return scale * __builtin_fmaf(a, sq, kq * u);
 }
-__device__ __forceinline__ void store_row(float *p, int lr, int lpr, const f32x4 (&s)[2], const float (&kk)[8],
-                                          float a, float u) {
+template <typename SE, int LPR>
+__device__ __forceinline__ void store_row(SE *row, int lr, const float (&s)[8], const float (&kk)[8], float a,
+                                          float u) {
+    float w[8];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        f32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = __builtin_fmaf(a, s[m][e], u * kk[4 * m + e]);
-        __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(p + 4 * lr + 4 * lpr * m));
-    }
+    for (int j = 0; j < 8; ++j) w[j] = __builtin_fmaf(a, s[j], u * kk[j]);
+    StateLane<SE, LPR>::store(row, lr, w);
 }
 
-template <typename E, int LPR>
+// k and q at the lane's state columns.
+template <typename E, typename SE, int LPR>
 __device__ __forceinline__ void load_kq(const E *kp, const E *qp, int lr, float (&kk)[8], float (&qq)[8]) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-        load4<E>(kp + 4 * lr + 4 * LPR * m, kk + 4 * m);
-        load4<E>(qp + 4 * lr + 4 * LPR * m, qq + 4 * m);
+        const int c = StateLane<SE, LPR>::col(lr, 4 * m);
+        load4<E>(kp + c, kk + 4 * m);
+        load4<E>(qp + c, qq + 4 * m);
     }
 }
 
-template <typename E, typename G, int DK, int DV>
+template <typename E, typename G, typename SE, int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_decode_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const G *__restrict__ gate_g, const G *__restrict__ gate_b,
-    float *__restrict__ state, const int32_t *__restrict__ slots, int32_t num_slots,
+    SE *__restrict__ state, const int32_t *__restrict__ slots, int32_t num_slots,
     E *__restrict__ out, int32_t hk, int32_t hv, float scale)
 {
-    typedef DecodeShape<DK, DV> SH;
-    constexpr int LPR = SH::LPR, ROWS = SH::ROWS, SLICES = SH::SLICES;
+    typedef DecodeShape<SE, DK, DV> SH;
+    typedef StateLane<SE, SH::LPR> SL;
+    constexpr int LPR = SH::LPR, RPP = SH::RPP, NRL = SH::NRL, ROWS = SH::ROWS, SLICES = SH::SLICES;
 
     const int bhs = blockIdx.x;
     const int bh = bhs / SLICES;
@@ -117,37 +171,47 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(
     const int kh = h / (hv / hk);
     const int tid = threadIdx.x;
     const int lr = tid % LPR;
-    const int row = row0 + tid / LPR;
-    const bool live = row < DV;
+    const int r0 = row0 + tid / LPR;  // this lane group's rows: r0 + p RPP, p < NRL
 
     const int slot = slots ? slots[b] : b;
     E *o_row = out + ((size_t)b * hv + h) * DV;
     if (slot < 0 || slot >= num_slots) {
-        if (live && lr == 0) o_row[row] = from_f32<E>(0.0f);
+#pragma unroll
+        for (int p = 0; p < NRL; ++p)
+            if (r0 + p * RPP < DV && lr == 0) o_row[r0 + p * RPP] = from_f32<E>(0.0f);
         return;
     }
-    float *S = state + ((size_t)slot * hv + h) * (size_t)(DV * DK);
+    SE *S = state + ((size_t)slot * hv + h) * (size_t)(DV * DK);
 
     // State row pieces first: the bulk of the bytes, all loads in flight.
-    f32x4 s[2];
+    float s[NRL][8];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-        s[m] = live ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)row * DK + 4 * lr + 4 * LPR * m))
-                    : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < NRL; ++p) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s[p][j] = 0.f;
+        if (r0 + p * RPP < DV) SL::load(S + (size_t)(r0 + p * RPP) * DK, lr, s[p]);
+    }
 
     float kk[8], qq[8];
-    load_kq<E, LPR>(k + ((size_t)b * hk + kh) * DK, q + ((size_t)b * hk + kh) * DK, lr, kk, qq);
+    load_kq<E, SE, LPR>(k + ((size_t)b * hk + kh) * DK, q + ((size_t)b * hk + kh) * DK, lr, kk, qq);
     const float a = expf(static_cast<float>(gate_g[(size_t)b * hv + h]));
     const float beta = static_cast<float>(gate_b[(size_t)b * hv + h]);
-    const float vv = live ? static_cast<float>(v[((size_t)b * hv + h) * DV + row]) : 0.f;
+    float vv[NRL];
+#pragma unroll
+    for (int p = 0; p < NRL; ++p)
+        vv[p] = r0 + p * RPP < DV ? static_cast<float>(v[((size_t)b * hv + h) * DV + r0 + p * RPP]) : 0.f;
 
     const float kq = key_query_dot<LPR>(kk, qq);
-    const float sk = row_dot<LPR>(s, kk);
-    const float sq = row_dot<LPR>(s, qq);
-    if (live) {
-        const float u = write_strength(beta, a, vv, sk);
-        if (lr == 0) o_row[row] = from_f32<E>(row_output(scale, a, sq, kq, u));
-        store_row(S + (size_t)row * DK, lr, LPR, s, kk, a, u);
+#pragma unroll
+    for (int p = 0; p < NRL; ++p) {
+        const int row = r0 + p * RPP;
+        const float sk = row_dot<LPR>(s[p], kk);
+        const float sq = row_dot<LPR>(s[p], qq);
+        if (row < DV) {
+            const float u = write_strength(beta, a, vv[p], sk);
+            if (lr == 0) o_row[row] = from_f32<E>(row_output(scale, a, sq, kq, u));
+            store_row<SE, LPR>(S + (size_t)row * DK, lr, s[p], kk, a, u);
+        }
     }
 }
 
@@ -171,22 +235,23 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(
 // unnormalised output never goes to memory.
 template <int DK, int DV> struct DecodeNormShape {
     static constexpr int LPR = DK / 8;                                  // lanes per state row
-    static constexpr int NRL = DV * LPR > 1024 ? DV * LPR / 1024 : 1;     // rows per lane group
+    static constexpr int NRL = DV * LPR > 1024 ? DV * LPR / 1024 : 1;   // rows per lane group
     static constexpr int THREADS = DV * LPR / NRL < 64 ? 64 : DV * LPR / NRL;
     static constexpr int RPP = THREADS / LPR;                           // rows per pass
     static constexpr int WAVES = THREADS / 64;
     static_assert(RPP * NRL >= DV, "every row has a lane group");
 };
 
-template <typename E, typename G, int DK, int DV>
+template <typename E, typename G, typename SE, int DK, int DV>
 __global__ __launch_bounds__((DecodeNormShape<DK, DV>::THREADS)) void gdn_decode_norm_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const G *__restrict__ gate_g, const G *__restrict__ gate_b,
-    float *__restrict__ state, const int32_t *__restrict__ slots, int32_t num_slots,
+    SE *__restrict__ state, const int32_t *__restrict__ slots, int32_t num_slots,
     E *__restrict__ out, int32_t hk, int32_t hv, float scale,
     const float *__restrict__ norm_w, float eps)
 {
     typedef DecodeNormShape<DK, DV> SH;
+    typedef StateLane<SE, SH::LPR> SL;
     constexpr int LPR = SH::LPR, NRL = SH::NRL, RPP = SH::RPP, WAVES = SH::WAVES;
     __shared__ float s_part[WAVES];
 
@@ -206,20 +271,19 @@ __global__ __launch_bounds__((DecodeNormShape<DK, DV>::THREADS)) void gdn_decode
             if (r0 + p * RPP < DV && lr == 0) o_row[r0 + p * RPP] = from_f32<E>(0.0f);
         return;
     }
-    float *S = state + ((size_t)slot * hv + h) * (size_t)(DV * DK);
+    SE *S = state + ((size_t)slot * hv + h) * (size_t)(DV * DK);
 
-    f32x4 s[NRL][2];
+    float s[NRL][8];
 #pragma unroll
     for (int p = 0; p < NRL; ++p) {
         const int row = r0 + p * RPP;
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-            s[p][m] = row < DV ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)row * DK + 4 * lr + 4 * LPR * m))
-                               : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 8; ++j) s[p][j] = 0.f;
+        if (row < DV) SL::load(S + (size_t)row * DK, lr, s[p]);
     }
 
     float kk[8], qq[8];
-    load_kq<E, LPR>(k + ((size_t)b * hk + kh) * DK, q + ((size_t)b * hk + kh) * DK, lr, kk, qq);
+    load_kq<E, SE, LPR>(k + ((size_t)b * hk + kh) * DK, q + ((size_t)b * hk + kh) * DK, lr, kk, qq);
     const float a = expf(static_cast<float>(gate_g[(size_t)b * hv + h]));
     const float beta = static_cast<float>(gate_b[(size_t)b * hv + h]);
     float vv[NRL];
@@ -238,7 +302,7 @@ __global__ __launch_bounds__((DecodeNormShape<DK, DV>::THREADS)) void gdn_decode
         const float u = write_strength(beta, a, vv[p], sk);
         o[p] = row_output(scale, a, sq, kq, u);
         if (row < DV) {
-            store_row(S + (size_t)row * DK, lr, LPR, s[p], kk, a, u);
+            store_row<SE, LPR>(S + (size_t)row * DK, lr, s[p], kk, a, u);
             if (lr == 0) part = __builtin_fmaf(o[p], o[p], part);
         }
     }
@@ -257,50 +321,45 @@ __global__ __launch_bounds__((DecodeNormShape<DK, DV>::THREADS)) void gdn_decode
     }
 }
 
-template <typename E, typename G, int D>
+template <typename E, typename G, typename SE, int D>
 static hipError_t launch_decode_t(const DecodeArgs &A, hipStream_t st) {
-    const dim3 grid((unsigned)A.batch * (unsigned)A.hv * (unsigned)DecodeShape<D, D>::SLICES), block(256);
-    return launch_kernel(kDecode, gdn_decode_kernel<E, G, D, D>, grid, block, 0, st,
+    SE *state = static_cast<SE *>(A.state);
+    if (A.norm_w) {
+        typedef DecodeNormShape<D, D> SH;
+        const dim3 grid((unsigned)A.batch * (unsigned)A.hv), block(SH::THREADS);
+        return launch_kernel(kDecodeNorm, gdn_decode_norm_kernel<E, G, SE, D, D>, grid, block, 0, st,
+                             (const E *)A.q, (const E *)A.k, (const E *)A.v,
+                             (const G *)A.g, (const G *)A.beta, state, A.slots, A.num_slots,
+                             (E *)A.out, A.hk, A.hv, A.scale, A.norm_w, A.norm_eps);
+    }
+    const dim3 grid((unsigned)A.batch * (unsigned)A.hv * (unsigned)DecodeShape<SE, D, D>::SLICES), block(256);
+    return launch_kernel(kDecode, gdn_decode_kernel<E, G, SE, D, D>, grid, block, 0, st,
                          (const E *)A.q, (const E *)A.k, (const E *)A.v,
-                         (const G *)A.g, (const G *)A.beta, A.state, A.slots, A.num_slots,
+                         (const G *)A.g, (const G *)A.beta, state, A.slots, A.num_slots,
                          (E *)A.out, A.hk, A.hv, A.scale);
 }
 
-template <typename E, typename G, int D>
-static hipError_t launch_decode_norm_t(const DecodeArgs &A, hipStream_t st) {
-    typedef DecodeNormShape<D, D> SH;
-    const dim3 grid((unsigned)A.batch * (unsigned)A.hv), block(SH::THREADS);
-    return launch_kernel(kDecodeNorm, gdn_decode_norm_kernel<E, G, D, D>, grid, block, 0, st,
-                         (const E *)A.q, (const E *)A.k, (const E *)A.v,
-                         (const G *)A.g, (const G *)A.beta, A.state, A.slots, A.num_slots,
-                         (E *)A.out, A.hk, A.hv, A.scale, A.norm_w, A.norm_eps);
-}
-
-template <typename E, typename G>
+template <typename E, typename G, typename SE>
 static hipError_t launch_decode_d(const DecodeArgs &A, hipStream_t st) {
-    if (A.norm_w) {
-        switch (A.d) {
-        case 16: return launch_decode_norm_t<E, G, 16>(A, st);
-        case 32: return launch_decode_norm_t<E, G, 32>(A, st);
-        case 64: return launch_decode_norm_t<E, G, 64>(A, st);
-        case 128: return launch_decode_norm_t<E, G, 128>(A, st);
-        default: return hipErrorInvalidValue;
-        }
-    }
     switch (A.d) {
-    case 16: return launch_decode_t<E, G, 16>(A, st);
-    case 32: return launch_decode_t<E, G, 32>(A, st);
-    case 64: return launch_decode_t<E, G, 64>(A, st);
-    case 128: return launch_decode_t<E, G, 128>(A, st);
+    case 16: return launch_decode_t<E, G, SE, 16>(A, st);
+    case 32: return launch_decode_t<E, G, SE, 32>(A, st);
+    case 64: return launch_decode_t<E, G, SE, 64>(A, st);
+    case 128: return launch_decode_t<E, G, SE, 128>(A, st);
     default: return hipErrorInvalidValue;
     }
 }
 
+// bf16 state storage is built for bf16 I/O only (fp32 I/O is the accuracy
+// mode, where a rounded state would defeat its purpose).
 hipError_t launch_decode(const DecodeArgs &A, hipStream_t st) {
     if (A.io_bf16) {
-        return A.gate_bf16 ? launch_decode_d<bf16, bf16>(A, st) : launch_decode_d<bf16, float>(A, st);
+        if (A.state_bf16)
+            return A.gate_bf16 ? launch_decode_d<bf16, bf16, bf16>(A, st) : launch_decode_d<bf16, float, bf16>(A, st);
+        return A.gate_bf16 ? launch_decode_d<bf16, bf16, float>(A, st) : launch_decode_d<bf16, float, float>(A, st);
     }
-    return A.gate_bf16 ? launch_decode_d<float, bf16>(A, st) : launch_decode_d<float, float>(A, st);
+    if (A.state_bf16) return hipErrorInvalidValue;
+    return A.gate_bf16 ? launch_decode_d<float, bf16, float>(A, st) : launch_decode_d<float, float, float>(A, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -362,12 +421,12 @@ template <int DK, int DV> struct TokenScanShape {
     static constexpr int SLICES = (DV + ROWS - 1) / ROWS;
 };
 
-template <typename E, typename G, int DK, int DV>
+template <typename E, typename G, typename SE, int DK, int DV>
 __global__ __launch_bounds__(256) void gdn_token_scan_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const G *__restrict__ gate_g, const G *__restrict__ gate_b,
     const int32_t *__restrict__ cu, int32_t num_seqs, int32_t total_tokens,
-    const float *__restrict__ s0, float *__restrict__ sfin, E *__restrict__ out,
+    const SE *__restrict__ s0, SE *__restrict__ sfin, E *__restrict__ out,
     int32_t hk, int32_t hv, float scale)
 {
     typedef TokenScanShape<DK, DV> SH;
@@ -391,8 +450,8 @@ __global__ __launch_bounds__(256) void gdn_token_scan_kernel(
     const size_t state0 = ((size_t)n * hv + h) * (size_t)(DV * DK) + (size_t)row * DK + 8 * lr;
     f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     if (s0 && live) {
-        s[0] = *reinterpret_cast<const f32x4 *>(s0 + state0);
-        s[1] = *reinterpret_cast<const f32x4 *>(s0 + state0 + 4);
+        s[0] = load4f<SE>(s0 + state0);
+        s[1] = load4f<SE>(s0 + state0 + 4);
     }
 
     // Sequence n's tokens [lo, hi): offsets clamped into [0, T] and made
@@ -534,35 +593,41 @@ __global__ __launch_bounds__(256) void gdn_token_scan_kernel(
     }
 
     if (sfin && live) {
-        *reinterpret_cast<f32x4 *>(sfin + state0) = s[0];
-        *reinterpret_cast<f32x4 *>(sfin + state0 + 4) = s[1];
+        store4<SE>(sfin + state0, s[0]);
+        store4<SE>(sfin + state0 + 4, s[1]);
     }
 }
 
-template <typename E, typename G, int D>
+template <typename E, typename G, typename SE, int D>
 static hipError_t launch_token_scan_t(const PrefillArgs &A, hipStream_t st) {
     const dim3 grid((unsigned)A.num_seqs * (unsigned)A.hv * (unsigned)TokenScanShape<D, D>::SLICES), block(256);
-    return launch_kernel(kTokenScan, gdn_token_scan_kernel<E, G, D, D>, grid, block, 0, st,
+    return launch_kernel(kTokenScan, gdn_token_scan_kernel<E, G, SE, D, D>, grid, block, 0, st,
                          (const E *)A.q, (const E *)A.k, (const E *)A.v, (const G *)A.g, (const G *)A.beta,
-                         A.cu, A.num_seqs, (int32_t)A.total_tokens, A.s0, A.s_final, (E *)A.out,
-                         A.hk, A.hv, A.scale);
+                         A.cu, A.num_seqs, (int32_t)A.total_tokens, (const SE *)A.s0, (SE *)A.s_final,
+                         (E *)A.out, A.hk, A.hv, A.scale);
 }
 
-template <typename E, typename G>
+template <typename E, typename G, typename SE>
 static hipError_t launch_token_scan_d(const PrefillArgs &A, hipStream_t st) {
     switch (A.d) {
-    case 16: return launch_token_scan_t<E, G, 16>(A, st);
-    case 32: return launch_token_scan_t<E, G, 32>(A, st);
-    case 64: return launch_token_scan_t<E, G, 64>(A, st);
-    case 128: return launch_token_scan_t<E, G, 128>(A, st);
+    case 16: return launch_token_scan_t<E, G, SE, 16>(A, st);
+    case 32: return launch_token_scan_t<E, G, SE, 32>(A, st);
+    case 64: return launch_token_scan_t<E, G, SE, 64>(A, st);
+    case 128: return launch_token_scan_t<E, G, SE, 128>(A, st);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_token_scan(const PrefillArgs &A, hipStream_t st) {
-    if (A.io_bf16)
-        return A.gate_bf16 ? launch_token_scan_d<bf16, bf16>(A, st) : launch_token_scan_d<bf16, float>(A, st);
-    return A.gate_bf16 ? launch_token_scan_d<float, bf16>(A, st) : launch_token_scan_d<float, float>(A, st);
+    if (A.io_bf16) {
+        if (A.state_bf16)
+            return A.gate_bf16 ? launch_token_scan_d<bf16, bf16, bf16>(A, st)
+                               : launch_token_scan_d<bf16, float, bf16>(A, st);
+        return A.gate_bf16 ? launch_token_scan_d<bf16, bf16, float>(A, st)
+                           : launch_token_scan_d<bf16, float, float>(A, st);
+    }
+    if (A.state_bf16) return hipErrorInvalidValue;
+    return A.gate_bf16 ? launch_token_scan_d<float, bf16, float>(A, st) : launch_token_scan_d<float, float, float>(A, st);
 }
 
 }  // namespace gdn

@@ -132,6 +132,14 @@ template <> __device__ __forceinline__ void store4<bf16>(bf16 *p, f32x4 v) {
 }
 template <> __device__ __forceinline__ void store4<float>(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
 
+// Four consecutive elements read as floats.
+template <typename E> __device__ __forceinline__ f32x4 load4f(const E *p);
+template <> __device__ __forceinline__ f32x4 load4f<float>(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+template <> __device__ __forceinline__ f32x4 load4f<bf16>(const bf16 *p) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
+    return f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]), static_cast<float>(x[3])};
+}
+
 // Write an accumulator tile transposed: element D[m0 + 4g + i][n0 + n] goes to
 // dst[(n0 + n) * ld + m0 + 4g + i] (4 contiguous elements per lane).
 template <typename E> __device__ __forceinline__ void store_acc_t(E *dst, int ld, int m0, int n0, int lane, f32x4 v) {

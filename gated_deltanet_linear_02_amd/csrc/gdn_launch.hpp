@@ -34,13 +34,14 @@ hipError_t launch_kernel(KernelKind kind, F kernel, dim3 grid, dim3 block, size_
 
 struct DecodeArgs {
     const void *q, *k, *v, *g, *beta;
-    float *state;
+    void *state;  // fp32, or bf16 when state_bf16
     const int32_t *slots;
     int32_t num_slots;
     void *out;
     int32_t batch, hk, hv, d;
     float scale;
     bool io_bf16, gate_bf16;
+    bool state_bf16 = false;
     const float *norm_w = nullptr;  // non-null: output normalisation fused in
     float norm_eps = 0.f;
 };
@@ -101,8 +102,9 @@ struct PrefillArgs {
     int32_t hk, hv, d, chunk;
     float scale;
     bool io_bf16, gate_bf16;
-    const float *s0;
-    float *s_final;
+    bool state_bf16 = false;  // states stored in bf16 (fp32 arithmetic)
+    const void *s0;           // fp32, or bf16 when state_bf16
+    void *s_final;
     void *out;
     char *ws;
     PrefillLayout lay;

@@ -805,7 +805,7 @@ __device__ __forceinline__ void keep_alive(float x) { asm volatile("" ::"v"(x));
 // Chunks ahead of the scan at which its operands are pulled into L2.
 constexpr int kTouchAhead = 8;
 
-template <typename E, int C, int DK>
+template <typename E, int C, int DK, typename SE>
 __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdn_scan_kernel(
     const E *__restrict__ v,
     const int32_t *__restrict__ bounds, const int32_t *__restrict__ seq_chunk0,
@@ -813,7 +813,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
     const E *__restrict__ tbmat, const E *__restrict__ pmat, const E *__restrict__ wmat,
     const E *__restrict__ qmat, const E *__restrict__ ktmat,
     const float *__restrict__ gates,
-    const float *__restrict__ s0, float *__restrict__ sfin, E *__restrict__ out,
+    const SE *__restrict__ s0, SE *__restrict__ sfin, E *__restrict__ out,
     int32_t num_seqs, int32_t hk, int32_t hv)
 {
     typedef ScanSmem<E, C, DK> L;
@@ -901,8 +901,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             const int mt = q + 4 * j;
             sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (mt < MT) {
-                if (s0)
-                    sacc[j] = *reinterpret_cast<const f32x4 *>(s0 + state0 + (size_t)(col0 + ln) * DK + 16 * mt + 4 * g4);
+                if (s0) sacc[j] = load4f<SE>(s0 + state0 + (size_t)(col0 + ln) * DK + 16 * mt + 4 * g4);
                 store_acc_p<MD>(sS, LDK, 16 * mt, 0, lane, sacc[j]);
             }
         }
@@ -982,8 +981,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
             for (int j = 0; j < NMW; ++j) {
                 const int mt = q + 4 * j;
-                if (mt < MT)
-                    *reinterpret_cast<f32x4 *>(sfin + state0 + (size_t)(col0 + ln) * DK + 16 * mt + 4 * g4) = sacc[j];
+                if (mt < MT) store4<SE>(sfin + state0 + (size_t)(col0 + ln) * DK + 16 * mt + 4 * g4, sacc[j]);
             }
         }
     });
@@ -1167,6 +1165,25 @@ static hipError_t allow_smem(KernelT kernel, size_t bytes, std::atomic<bool> &do
     return e;
 }
 
+// The scan, with states stored as SE (fp32, or bf16 with fp32 arithmetic).
+template <typename E, int C, int D, typename SE>
+static hipError_t launch_scan(const PrefillArgs &A, hipStream_t st, int32_t *bounds, int32_t *seq_chunk0,
+                              int32_t *order, E *tbmat, E *pmat, E *wmat, E *qmat, E *ktmat, float *gates) {
+    typedef ScanSmem<E, C, D> SL;
+    static std::atomic<bool> scan_ok{false};
+    auto scan = gdn_scan_kernel<E, C, D, SE>;
+    hipError_t e;
+    if ((e = allow_smem(scan, SL::bytes, scan_ok)) != hipSuccess) return e;
+    const int64_t per_kh = (int64_t)(A.hv / A.hk) * (D / kSliceRows);
+    const int64_t groups = (int64_t)A.num_seqs * A.hk;
+    const int64_t grid = ((groups + 7) / 8) * per_kh * 8;
+    return launch_kernel(kScan, scan, dim3((unsigned)grid), dim3(kScanThreads), SL::bytes, st,
+                         (const E *)A.v, (const int32_t *)bounds, (const int32_t *)seq_chunk0,
+                         (const int32_t *)order, (const E *)tbmat, (const E *)pmat, (const E *)wmat,
+                         (const E *)qmat, (const E *)ktmat, (const float *)gates, (const SE *)A.s0,
+                         (SE *)A.s_final, (E *)A.out, A.num_seqs, A.hk, A.hv);
+}
+
 template <typename E, typename G, int C, int D>
 static hipError_t launch_prefill_t(const PrefillArgs &A, hipStream_t st) {
     const PrefillLayout &Y = A.lay;
@@ -1205,18 +1222,13 @@ static hipError_t launch_prefill_t(const PrefillArgs &A, hipStream_t st) {
                       tbmat, pmat, wmat, qmat, ktmat, gates, A.hk, A.hv, A.scale);
     if (e != hipSuccess) return e;
 
-    typedef ScanSmem<E, C, D> SL;
-    static std::atomic<bool> scan_ok{false};
-    auto scan = gdn_scan_kernel<E, C, D>;
-    if ((e = allow_smem(scan, SL::bytes, scan_ok)) != hipSuccess) return e;
-    const int64_t per_kh = (int64_t)(A.hv / A.hk) * (D / kSliceRows);
-    const int64_t groups = (int64_t)A.num_seqs * A.hk;
-    const int64_t grid = ((groups + 7) / 8) * per_kh * 8;
-    return launch_kernel(kScan, scan, dim3((unsigned)grid), dim3(kScanThreads), SL::bytes, st,
-                         (const E *)A.v, (const int32_t *)bounds, (const int32_t *)seq_chunk0,
-                         (const int32_t *)order, (const E *)tbmat, (const E *)pmat, (const E *)wmat,
-                         (const E *)qmat, (const E *)ktmat, (const float *)gates, A.s0, A.s_final,
-                         (E *)A.out, A.num_seqs, A.hk, A.hv);
+    if constexpr (IsBf16<E>::value) {
+        if (A.state_bf16)
+            return launch_scan<E, C, D, bf16>(A, st, bounds, seq_chunk0, order, tbmat, pmat, wmat, qmat, ktmat, gates);
+    } else if (A.state_bf16) {
+        return hipErrorInvalidValue;  // bf16 states are built for bf16 I/O only
+    }
+    return launch_scan<E, C, D, float>(A, st, bounds, seq_chunk0, order, tbmat, pmat, wmat, qmat, ktmat, gates);
 }
 
 template <typename E, typename G, int C>

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
     GDN_OK = 0,
@@ -143,45 +143,62 @@ int32_t gdn_decode_step(const void *q, const void *k, const void *v,
                         void *out, void *stream);
 
 /*
- * The same two calls with the layer's output normalisation applied to every
- * output row. The recurrent update comes "with its normalisation" ("Optimiser
- * l'inference sur appareil pour Apple Silicon", section "Reduire le trafic
- * intermediaire et d'etat"); the pages do not give its form, and this is the
- * RMS normalisation of each (token or sequence, value head) row of dv outputs:
+ * The same two calls with two options: how states are stored, and the
+ * layer's output normalisation. With state_dtype GDN_F32 and norm_weight NULL
+ * they are gdn_prefill and gdn_decode_step.
  *
- *     y_i = o_i * norm_weight[i] / sqrt(mean_j o_j^2 + norm_eps)
+ * state_dtype  GDN_F32 or GDN_BF16: the element type of initial_state,
+ *              final_state (prefill) and state (decode), whose layouts are
+ *              unchanged. The pages disagree on it: fp32 because rounding
+ *              accumulates over sequential updates ("Maintenir l'etat
+ *              recurrent sur la puce" of "Optimiser l'inference sur appareil
+ *              pour Apple Silicon"), bf16 recurrence states in the engine of
+ *              "On descend d'un cran : #004 le meme compilateur sur les puces
+ *              d'Apple". With GDN_BF16 all
+ *              arithmetic stays fp32: a decode step widens the stored state
+ *              and rounds the new one to bf16 (nearest, ties to even); a
+ *              prefill widens the initial state, keeps fp32 on chip, and
+ *              rounds the final state once. It halves the state traffic of
+ *              decode. Built for io_dtype GDN_BF16 only (else
+ *              GDN_ERR_UNSUPPORTED); any other value is GDN_ERR_UNSUPPORTED.
  *
- * norm_weight  fp32 [dv] DEVICE array, one weight per value channel, shared
- *              by all heads; NULL gives GDN_ERR_NULL_ARG. It must not
- *              overlap out or the states (GDN_ERR_ALIAS).
- * norm_eps     finite and >= 0, else GDN_ERR_BAD_VALUE. With 0, an all-zero
- *              row gives NaN, as the definition does.
- * Everything else (arguments, layouts, workspace, states, errors) is as in
- * gdn_prefill and gdn_decode_step, and the states they leave are the same.
+ * norm_weight  NULL, or an fp32 [dv] DEVICE array: every output row is then
+ *              RMS-normalised. The recurrent update comes "with its
+ *              normalisation" (section "Reduire le trafic intermediaire et
+ *              d'etat" of the same page), whose form the pages do not give;
+ *              here, per (token or sequence, value head) row of dv outputs,
+ *                  y_i = o_i * norm_weight[i] / sqrt(mean_j o_j^2 + norm_eps)
+ *              with one weight per value channel shared by all heads. It must
+ *              not overlap out or the states (GDN_ERR_ALIAS).
+ * norm_eps     finite and >= 0 when norm_weight is given, else
+ *              GDN_ERR_BAD_VALUE. With 0, an all-zero row gives NaN, as the
+ *              definition does.
  *
- * gdn_decode_step_norm is one kernel: a workgroup owns a whole (sequence,
- * value head) state, so the unnormalised row never goes to memory.
- * gdn_prefill_norm runs gdn_prefill's kernels, then one pass that rewrites
- * the rows of out in place (the prefill splits a head's rows over
- * workgroups that never wait for one another); rows of tokens outside
- * [cu_seqlens[0], cu_seqlens[N]) are left untouched. In bf16 the row is thus
- * rounded twice (before and after the normalisation).
+ * Decode with a weight is one kernel: a workgroup owns a whole (sequence,
+ * value head) state, so the unnormalised row never goes to memory. Prefill
+ * with a weight runs its kernels, then one pass that rewrites the rows of
+ * out in place (the prefill splits a head's rows over workgroups that never
+ * wait for one another); rows of tokens outside [cu_seqlens[0],
+ * cu_seqlens[N]) are left untouched, and in bf16 a row is rounded twice
+ * (before and after the normalisation). The states are those of the call
+ * without a weight.
  */
-int32_t gdn_prefill_norm(const void *q, const void *k, const void *v,
-                         const void *g, const void *beta,
-                         const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
-                         int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
-                         float scale, int32_t io_dtype, int32_t gate_dtype,
-                         const float *initial_state, float *final_state,
-                         const float *norm_weight, float norm_eps, void *out,
-                         void *workspace, size_t workspace_bytes, void *stream);
+int32_t gdn_prefill_ex(const void *q, const void *k, const void *v,
+                       const void *g, const void *beta,
+                       const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                       int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
+                       float scale, int32_t io_dtype, int32_t gate_dtype,
+                       const void *initial_state, void *final_state, int32_t state_dtype,
+                       const float *norm_weight, float norm_eps, void *out,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
-int32_t gdn_decode_step_norm(const void *q, const void *k, const void *v,
-                             const void *g, const void *beta,
-                             int32_t batch, int32_t hk, int32_t hv, int32_t dk, int32_t dv,
-                             float scale, int32_t io_dtype, int32_t gate_dtype,
-                             float *state, const int32_t *state_slots, int32_t num_slots,
-                             const float *norm_weight, float norm_eps, void *out, void *stream);
+int32_t gdn_decode_step_ex(const void *q, const void *k, const void *v,
+                           const void *g, const void *beta,
+                           int32_t batch, int32_t hk, int32_t hv, int32_t dk, int32_t dv,
+                           float scale, int32_t io_dtype, int32_t gate_dtype,
+                           void *state, int32_t state_dtype,
+                           const int32_t *state_slots, int32_t num_slots,
+                           const float *norm_weight, float norm_eps, void *out, void *stream);
 
 /*
  * Per-kernel timing (a profiling aid, not needed for computation).

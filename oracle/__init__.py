@@ -33,8 +33,10 @@ What is here:
                        (ties to even), for states stored in bf16 between
                        calls: the storage variant whose accuracy the pages
                        argue about (fp32 states in "Maintenir l'etat
-                       recurrent sur la puce" of page 1, bf16 recurrence
-                       states in the engine of page 3).
+                       recurrent sur la puce" of "Optimiser l'inference
+                       sur appareil pour Apple Silicon", bf16 recurrence
+                       states in the engine of "On descend d'un cran : #004
+                       le meme compilateur sur les puces d'Apple").
 
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_pins.py`` (closed forms, invariants, scalar cases worked

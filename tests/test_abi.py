@@ -37,14 +37,14 @@ def declared_functions():
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert {"gdn_prefill", "gdn_decode_step", "gdn_prefill_workspace_size",
-            "gdn_prefill_norm", "gdn_decode_step_norm",
+            "gdn_prefill_ex", "gdn_decode_step_ex",
             "gdn_status_string", "gdn_abi_version"} <= set(names)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in gdn.h but not exported"
 
 
 def test_version_and_status_strings(lib):
-    assert gdn.abi_version() == 2
+    assert gdn.abi_version() == 3
     for s in range(8):
         assert lib.gdn_status_string(s)
     assert b"unknown" in lib.gdn_status_string(99)
@@ -172,46 +172,53 @@ def test_binding_raises_on_missing_library(tmp_path, monkeypatch):
 NORM_W = FAKE + (10 << 30)
 
 
-def _prefill_norm(lib, w=NORM_W, eps=1e-6, **kw):
+def _prefill_ex(lib, w=NORM_W, eps=1e-6, sdt=F32, **kw):
     a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30),
              beta=FAKE + (4 << 30), cu=FAKE + (5 << 30), n=1, T=128, hk=2, hv=4, dk=64, dv=64,
              chunk=64, scale=1.0, io=BF16, gate=F32, s0=None, sf=None, out=FAKE + (6 << 30),
              ws=FAKE + (7 << 30), ws_bytes=1 << 30, stream=None)
     a.update(kw)
-    return lib.gdn_prefill_norm(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["n"], a["T"],
-                                a["hk"], a["hv"], a["dk"], a["dv"], a["chunk"], a["scale"], a["io"],
-                                a["gate"], a["s0"], a["sf"], w, eps, a["out"], a["ws"], a["ws_bytes"],
-                                a["stream"])
+    return lib.gdn_prefill_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["n"], a["T"],
+                              a["hk"], a["hv"], a["dk"], a["dv"], a["chunk"], a["scale"], a["io"],
+                              a["gate"], a["s0"], a["sf"], sdt, w, eps, a["out"], a["ws"], a["ws_bytes"],
+                              a["stream"])
 
 
-def _decode_norm(lib, w=NORM_W, eps=1e-6, **kw):
+def _decode_ex(lib, w=NORM_W, eps=1e-6, sdt=F32, **kw):
     a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30),
              beta=FAKE + (4 << 30), B=64, hk=16, hv=32, dk=128, dv=128, scale=1.0, io=BF16,
              gate=BF16, state=FAKE + (5 << 30), slots=None, num_slots=64,
              out=FAKE + (9 << 30), stream=None)
     a.update(kw)
-    return lib.gdn_decode_step_norm(a["q"], a["k"], a["v"], a["g"], a["beta"], a["B"], a["hk"],
-                                    a["hv"], a["dk"], a["dv"], a["scale"], a["io"], a["gate"],
-                                    a["state"], a["slots"], a["num_slots"], w, eps, a["out"],
-                                    a["stream"])
+    return lib.gdn_decode_step_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], a["B"], a["hk"],
+                                  a["hv"], a["dk"], a["dv"], a["scale"], a["io"], a["gate"],
+                                  a["state"], sdt, a["slots"], a["num_slots"], w, eps, a["out"],
+                                  a["stream"])
 
 
 @no_gpu
-def test_norm_argument_checks(lib):
+def test_ex_argument_checks(lib):
     inf, nan = float("inf"), float("nan")
-    for call in (_prefill_norm, _decode_norm):
-        assert call(lib, w=None) == NULL_ARG
+    for call in (_prefill_ex, _decode_ex):
         assert call(lib, eps=-1e-6) == BAD_VALUE
         assert call(lib, eps=inf) == BAD_VALUE
         assert call(lib, eps=nan) == BAD_VALUE
         # the weight is an input: out must not overlap it
-        assert call(lib, w=FAKE + (6 << 30) + 64 if call is _prefill_norm else FAKE + (9 << 30) + 64) == ALIAS
+        assert call(lib, w=FAKE + (6 << 30) + 64 if call is _prefill_ex else FAKE + (9 << 30) + 64) == ALIAS
         # the other checks are those of the plain entry points
         assert call(lib, hk=3) == BAD_SHAPE
         assert call(lib, dk=96, dv=96) == UNSUPPORTED
+        # state storage: fp32 or bf16, and bf16 only with bf16 I/O
+        assert call(lib, sdt=2) == UNSUPPORTED
+        assert call(lib, sdt=BF16, io=F32) == UNSUPPORTED
+        assert call(lib, sdt=BF16, w=None, io=F32) == UNSUPPORTED
     # decode: the state is written, so it must not overlap the weight
-    assert _decode_norm(lib, w=FAKE + (5 << 30) + 4096) == ALIAS
+    assert _decode_ex(lib, w=FAKE + (5 << 30) + 4096) == ALIAS
+    # the state's extent follows its dtype: a bf16 pool of 64 slots is half
+    # as long, so an output just past it is fine for bf16 and overlaps fp32
+    past_bf16 = FAKE + (5 << 30) + 64 * 32 * 128 * 128 * 2
+    assert _decode_ex(lib, out=past_bf16, sdt=F32) == ALIAS
     # prefill: the final state must not overlap the weight either
-    assert _prefill_norm(lib, sf=NORM_W - 64) == ALIAS
-    assert _prefill_norm(lib, ws=None) == WORKSPACE
-    assert _decode_norm(lib, B=0) == OK
+    assert _prefill_ex(lib, sf=NORM_W - 64) == ALIAS
+    assert _prefill_ex(lib, ws=None) == WORKSPACE
+    assert _decode_ex(lib, B=0) == OK
