@@ -526,6 +526,64 @@ def summarize_state(stats_dir: str, fetch_dir: str, write_dir: str, results_json
         f.write("\n".join(lines) + "\n")
 
 
+def summarize_tune(stats_dir: str, results_jsonl: str):
+    """Write profiles/gdn_prefill_tuning.md from a rocprofv3 kernel trace of
+    `bench.py --tune` and the JSON lines that run printed."""
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(stats_dir, "run_kernel_stats.csv"))))
+    lines = [
+        f"# Prefill method chosen by measurement vs the fixed rule; HK={HK}, HV={HV}, d={D}, bf16",
+        "",
+        "Made by (from the repository root; OUT is any scratch directory):",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp",
+        "rocprofv3 --kernel-trace --stats -d OUT/stats -o run --output-format csv -- "
+        "python3 REPO/bench.py --tune > OUT/tune.jsonl",
+        "cd REPO && python3 bench.py --summarize-tune OUT/stats OUT/tune.jsonl",
+        "```",
+        "",
+        f"Kernel sources hash: `{kernel_source_hash()}`.",
+        "",
+        "## Kernel durations over the whole run (rocprofv3 --kernel-trace --stats)",
+        "",
+        "| kernel | calls | mean us | min us | max us |",
+        "|---|---|---|---|---|",
+    ]
+    import re
+    for r in rows:
+        short = _short_kernel(r["Name"])
+        if short in KERNELS or "gate_kernel" in r["Name"]:
+            name = KERNELS.get(short, "gdn_gate_kernel")
+            m = (re.search(r"kernelI(?:DF16b|f)+Li(\d+)ELi\d+", r["Name"])
+                 or re.search(r"_kernel<[^,<>]*, (\d+), \d+>", r["Name"]))
+            if short in ("prep", "scan") and m:
+                name += f" (C={m.group(1)})"
+            elif "gate_kernel" in r["Name"]:
+                name += " (bf16)" if "IDF16b" in r["Name"] else " (fp32)"
+            lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", "## Per shape (HIP events in the same run)", "",
+              "chunk 0 timed on rotated buffer sets under the fixed rule (empty cache; the better of a run "
+              "before and one after) and under the tuned choice; the candidates' own times are the tuner's "
+              "(warm, same inputs). Taken under "
+              "the profiler, which adds a per-launch overhead; `python3 bench.py --tune` measures the same "
+              "without it.", "",
+              "| sequences x tokens | rule | rule us | tuned | tuned us | speedup | tuner's warm us (64/32/16/1) |",
+              "|---|---|---|---|---|---|---|"]
+    for line in open(results_jsonl):
+        line = line.strip()
+        if not line.startswith("{"):
+            continue
+        d = json.loads(line)
+        warm = "/".join(f"{d['candidate_ms_warm'][c] * 1e3:.1f}" if d['candidate_ms_warm'][c] >= 0 else "-"
+                        for c in ("64", "32", "16", "1"))
+        lines.append(f"| {d['num_seqs']} x {d['tokens_per_seq']} | {d['rule_chunk']} | {d['rule_ms'] * 1e3:.1f} | "
+                     f"{d['tuned_chunk']} | {d['tuned_ms'] * 1e3:.1f} | {d['speedup']:.2f} | {warm} |")
+    with open(os.path.join(ROOT, "profiles", "gdn_prefill_tuning.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def norm_apply_bytes(tokens, hv=HV, dv=D, elem=2):
     """Algorithmic HBM bytes of the prefill's output-normalisation pass: every
     output row read and written once (the weight and cu_seqlens are a few
@@ -663,6 +721,68 @@ def state_storage_bench(dev, copies, steps):
             }), flush=True)
 
 
+# Shapes for the tuning sweep: (sequences, tokens each).
+TUNE_SHAPES = ((1, 16), (1, 48), (1, 128), (1, 512), (8, 4), (64, 1), (64, 4), (64, 16), (8, 300), (1, 4096))
+
+
+def tuning_sweep(dev, copies, steps):
+    """gdn_tune_prefill on each shape, then prefill with chunk 0 timed under
+    the fixed rule (empty cache) and under the tuned choice, on rotated buffer
+    sets (cold caches). HK=16, HV=32, d=128, bf16, fp32 gates, nonzero initial
+    states; one JSON line per shape."""
+    import torch
+    import gdn_synth as gs
+    import gated_deltanet_linear_02_amd as gdn
+    for N, k in TUNE_SHAPES:
+        T = N * k
+        inp = gs.make_inputs([k] * N, HK, HV, D, D, seed=gs.SEED_BASE + 900 + T, io_dtype="bf16",
+                             gate_dtype="f32", init_state=True)
+        sets = []
+        for _ in range(copies):
+            d = device_inputs(inp, dev)
+            d["s0"] = torch.from_numpy(inp.initial_state).to(dev)
+            d["out"] = torch.empty((T, HV, D), dtype=torch.bfloat16, device=dev)
+            d["fin"] = torch.empty((N, HV, D, D), dtype=torch.float32, device=dev)
+            d["ws"] = torch.empty(gdn.prefill_workspace_size(N, T, HK, HV, D, D, 0, torch.bfloat16),
+                                  dtype=torch.uint8, device=dev)
+            sets.append(d)
+
+        def run(d):
+            gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=0,
+                        initial_state=d["s0"], final_state=d["fin"], out=d["out"], workspace=d["ws"])
+
+        def timed():
+            for i in range(3):
+                run(sets[i % copies])
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(steps):
+                run(sets[i % copies])
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps
+
+        # the rule is timed before and after the tuned choice (the better of
+        # the two counts), so that warm-up order favours neither
+        gdn.tune_cache_clear()
+        rule_ms = timed()
+        rule = 1 if (T <= 64 or T <= 16 * N) else 64
+        d0 = sets[0]
+        r = gdn.tune_prefill(d0["q"], d0["k"], d0["v"], d0["g"], d0["beta"], d0["cu_seqlens"], initial_state=d0["s0"])
+        tuned_ms = timed()
+        gdn.tune_cache_clear()
+        rule_ms = min(rule_ms, timed())
+        print(json.dumps({
+            "mode": "tuning", "num_seqs": N, "tokens_per_seq": k, "total_tokens": T,
+            "rule_chunk": rule, "tuned_chunk": r["chunk"], "rule_ms": rule_ms, "tuned_ms": tuned_ms,
+            "speedup": rule_ms / tuned_ms, "candidate_ms_warm": {str(c): t for c, t in r["ms"].items()},
+            "candidate_gate_err": {str(c): e for c, e in r["err"].items()},
+            "dtype": "bf16", "data": "synthetic", "buffer_copies": copies,
+            "config": {"workload": f"{N} sequence(s) x {k} tokens, HK={HK}, HV={HV}, d={D}"},
+        }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -679,6 +799,9 @@ def main():
     ap.add_argument("--bf16-state", action="store_true",
                     help="instead of the main line: decode with fp32 and with bf16 state storage, "
                          "one JSON line per case")
+    ap.add_argument("--tune", action="store_true",
+                    help="instead of the main line: tune the prefill method per shape and time chunk 0 "
+                         "under the fixed rule and under the tuned choice, one JSON line per shape")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, run 3 device-to-device copies of this many MiB "
                          "(the known-size reference for HBM byte counters)")
@@ -695,8 +818,13 @@ def main():
                     metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR", "RESULTS_JSONL", "PROBE_MIB"),
                     help="host only: turn rocprofv3 runs of --bf16-state into "
                          "profiles/gdn_decode_state_storage.md and exit")
+    ap.add_argument("--summarize-tune", nargs=2, metavar=("STATS_DIR", "RESULTS_JSONL"),
+                    help="host only: turn a kernel trace of --tune into profiles/gdn_prefill_tuning.md and exit")
     args = ap.parse_args()
 
+    if args.summarize_tune:
+        summarize_tune(*args.summarize_tune)
+        return
     if args.summarize_state:
         summarize_state(*args.summarize_state[:4], int(args.summarize_state[4]))
         return
@@ -726,6 +854,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.short_prefill:
         short_prefill_sweep(dev, args.copies, min(args.steps, 30))
+        return
+    if args.tune:
+        tuning_sweep(dev, args.copies, min(args.steps, 30))
         return
     if args.bf16_state:
         probe_copies(dev, args.copy_probe_mib)

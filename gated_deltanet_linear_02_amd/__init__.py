@@ -13,6 +13,9 @@ Entry points (same names as the C ABI, without the ``gdn_`` prefix):
     gdn_decode_step_ex: states stored in bf16 with fp32 arithmetic, and the
     output rows RMS-normalised, times one weight per value channel)
     prefill_workspace_size(...)
+    tune_prefill(q, k, v, g, beta, cu_seqlens, ...) -> chosen method, per-candidate
+        times and gate errors (cached for prefill's chunk 0);
+    tune_cache_clear / tune_cache_size / tune_cache_save / tune_cache_load
     timing_start(max_launches) / timing_stop()  -> per-kernel launch times
 """
 
@@ -27,6 +30,7 @@ import torch
 
 __all__ = [
     "GdnError", "lib_path", "load", "prefill", "decode_step", "prefill_workspace_size",
+    "tune_prefill", "tune_cache_clear", "tune_cache_size", "tune_cache_save", "tune_cache_load",
     "timing_start", "timing_stop", "abi_version", "KERNEL_KINDS",
 ]
 
@@ -84,6 +88,20 @@ def load():
         L.gdn_decode_step_ex.restype = i32
         L.gdn_decode_step_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32,
                                          vp, i32, vp, i32, vp, f32, vp, vp]
+        L.gdn_tune_prefill_scratch_size.restype = sz
+        L.gdn_tune_prefill_scratch_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]
+        L.gdn_tune_prefill.restype = i32
+        L.gdn_tune_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, f32, i32, i32,
+                                       vp, f32, vp, sz, vp, ctypes.POINTER(i32), ctypes.POINTER(f32),
+                                       ctypes.POINTER(f32)]
+        L.gdn_tune_cache_clear.restype = None
+        L.gdn_tune_cache_clear.argtypes = []
+        L.gdn_tune_cache_size.restype = i32
+        L.gdn_tune_cache_size.argtypes = []
+        L.gdn_tune_cache_save.restype = i32
+        L.gdn_tune_cache_save.argtypes = [ctypes.c_char_p]
+        L.gdn_tune_cache_load.restype = i32
+        L.gdn_tune_cache_load.argtypes = [ctypes.c_char_p, ctypes.POINTER(i32)]
         L.gdn_timing_start.restype = i32
         L.gdn_timing_start.argtypes = [i32]
         L.gdn_timing_stop.restype = i32
@@ -240,6 +258,60 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
             _stream(q.device, stream))
     _check(status)
     return out
+
+
+TUNE_CANDIDATES = (64, 32, 16, 1)
+
+
+def tune_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                 cu_seqlens: torch.Tensor, *, scale: float = 1.0, initial_state: Optional[torch.Tensor] = None,
+                 gate_tol: float = 1.0 / 64, scratch: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Measure every prefill method on these inputs (``gdn_tune_prefill``):
+    methods whose output or final state differs from chunk 64's by more than
+    gate_tol of the largest magnitude are rejected, the fastest of the rest is
+    returned and cached for ``prefill(chunk=0)`` on this device and shape
+    bucket. Returns {"chunk": c, "ms": {c: t}, "err": {c: e}} (t = -1 when
+    rejected). Synchronises the stream."""
+    T, hk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    N = cu_seqlens.numel() - 1
+    dev = q.device
+    need = int(load().gdn_tune_prefill_scratch_size(N, T, hk, hv, dk, dv, _dtype_code(q.dtype)))
+    if need == 0:
+        raise GdnError(2, "shape rejected")
+    if scratch is None:
+        scratch = torch.empty(need, dtype=torch.uint8, device=dev)
+    _on_device(dev, k=k, v=v, g=g, beta=beta, cu_seqlens=cu_seqlens, initial_state=initial_state,
+               scratch=scratch)
+    if initial_state is not None and initial_state.dtype != torch.float32:
+        raise TypeError("tuning takes an fp32 initial state")
+    chosen = ctypes.c_int32(0)
+    ms = (ctypes.c_float * 4)()
+    err = (ctypes.c_float * 4)()
+    _check(load().gdn_tune_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, hk, hv, dk, dv, float(scale),
+        _dtype_code(q.dtype), _dtype_code(g.dtype), _ptr(initial_state), float(gate_tol), _ptr(scratch),
+        scratch.numel(), _stream(dev, stream), ctypes.byref(chosen), ms, err))
+    return {"chunk": int(chosen.value), "ms": {c: float(ms[i]) for i, c in enumerate(TUNE_CANDIDATES)},
+            "err": {c: float(err[i]) for i, c in enumerate(TUNE_CANDIDATES)}}
+
+
+def tune_cache_clear() -> None:
+    load().gdn_tune_cache_clear()
+
+
+def tune_cache_size() -> int:
+    return int(load().gdn_tune_cache_size())
+
+
+def tune_cache_save(path: str) -> None:
+    _check(load().gdn_tune_cache_save(os.fsencode(path)))
+
+
+def tune_cache_load(path: str) -> int:
+    n = ctypes.c_int32(0)
+    _check(load().gdn_tune_cache_load(os.fsencode(path), ctypes.byref(n)))
+    return int(n.value)
 
 
 def timing_start(max_launches: int) -> None:

@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 ARCH = "gfx950"
 
-SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_norm.hip", "gdn_prefill.hip"]
+SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_norm.hip", "gdn_prefill.hip", "gdn_tune.hip"]
 
 # Packed-fp32 VALU forms are disabled; hipcc's host pass warns that it does
 # not know the feature, which is harmless.

@@ -6,6 +6,7 @@
 #include "gdn.h"
 #include "gdn_launch.hpp"
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <new>
@@ -47,9 +48,8 @@ TimingEvents timing_claim(KernelKind kind) {
 static bool valid_head(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 static bool valid_chunk(int32_t c) { return c == 0 || c == 1 || c == 16 || c == 32 || c == 64; }
 
-// The chunk size gdn_prefill uses: 1 (token by token) or 16, 32, 64.
-static int32_t effective_chunk(int32_t chunk, int32_t num_seqs, int64_t total_tokens) {
-    if (chunk != 0) return chunk;
+// The method chunk 0 takes without a tuned choice: 1 (token by token) or 64.
+static int32_t rule_chunk(int32_t num_seqs, int64_t total_tokens) {
     return prefer_token_scan(num_seqs, total_tokens) ? 1 : 64;
 }
 static bool valid_dtype(int32_t t) { return t == GDN_BF16 || t == GDN_F32; }
@@ -89,6 +89,16 @@ const char *gdn_status_string(int32_t status) {
     }
 }
 
+// Whether method c (1, 16, 32 or 64) fits the launch limits for this shape.
+static bool method_fits(int32_t c, int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv, int32_t dk,
+                        int32_t dv, int32_t io_dtype) {
+    if (c == 1)  // token scan: one workgroup per (sequence, value head, row slice)
+        return (int64_t)num_seqs * hv * dv <= INT32_MAX;
+    const PrefillLayout L = prefill_layout(num_seqs, total_tokens, hk, hv, dk, c, dtype_bytes(io_dtype));
+    const int64_t scan_grid = (((int64_t)num_seqs * hk + 7) / 8) * (hv / hk) * (dv / 16) * 8;
+    return scan_grid <= INT32_MAX && L.max_chunks <= INT32_MAX;
+}
+
 static int32_t check_prefill_shape(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
                                    int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype,
                                    int32_t gate_dtype) {
@@ -97,24 +107,31 @@ static int32_t check_prefill_shape(int32_t num_seqs, int64_t total_tokens, int32
     if (!valid_head(dk) || dv != dk || !valid_chunk(chunk) || !valid_dtype(io_dtype) ||
         !valid_dtype(gate_dtype) || hk > 65535)
         return GDN_ERR_UNSUPPORTED;
-    if (effective_chunk(chunk, num_seqs, total_tokens) == 1) {
-        // token scan: one workgroup per (sequence, value head, row slice)
-        return (int64_t)num_seqs * hv * dv > INT32_MAX ? GDN_ERR_UNSUPPORTED : GDN_OK;
-    }
-    const PrefillLayout L = prefill_layout(num_seqs, total_tokens, hk, hv, dk,
-                                           effective_chunk(chunk, num_seqs, total_tokens), dtype_bytes(io_dtype));
-    const int64_t scan_grid = (((int64_t)num_seqs * hk + 7) / 8) * (hv / hk) * (dv / 16) * 8;
-    if (scan_grid > INT32_MAX || L.max_chunks > INT32_MAX) return GDN_ERR_UNSUPPORTED;
-    return GDN_OK;
+    const int32_t c = chunk != 0 ? chunk : rule_chunk(num_seqs, total_tokens);
+    return method_fits(c, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype) ? GDN_OK : GDN_ERR_UNSUPPORTED;
 }
 
-// Workspace bytes of the method gdn_prefill uses (the token scan needs none;
-// 256 are reported so that a size of 0 keeps meaning "rejected").
+// The method a call uses: the chunk asked for, or for chunk 0 the choice
+// cached by gdn_tune_prefill for this device and shape, else the rule.
+static int32_t method_for(int32_t chunk, int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
+                          int32_t dk, int32_t dv, int32_t io_dtype, int32_t gate_dtype) {
+    if (chunk != 0) return chunk;
+    const int32_t t = tuned_chunk(num_seqs, total_tokens, hk, hv, dk, io_dtype, gate_dtype);
+    if (t != 0 && method_fits(t, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype)) return t;
+    return rule_chunk(num_seqs, total_tokens);
+}
+
+// Workspace bytes for chunk c (the token scan needs none; 256 are reported so
+// that a size of 0 keeps meaning "rejected"). Chunk 0 may take any method
+// (a tuned choice), so it reports the largest chunked need.
 static size_t prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
                                       int32_t dk, int32_t chunk, int32_t io_dtype) {
-    const int32_t c = effective_chunk(chunk, num_seqs, total_tokens);
-    if (c == 1) return 256;
-    return prefill_layout(num_seqs, total_tokens, hk, hv, dk, c, dtype_bytes(io_dtype)).total;
+    if (chunk == 1) return 256;
+    if (chunk != 0) return prefill_layout(num_seqs, total_tokens, hk, hv, dk, chunk, dtype_bytes(io_dtype)).total;
+    size_t m = 256;
+    for (int32_t c : {16, 32, 64})
+        m = std::max(m, prefill_layout(num_seqs, total_tokens, hk, hv, dk, c, dtype_bytes(io_dtype)).total);
+    return m;
 }
 
 size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
@@ -153,7 +170,7 @@ static int32_t prefill_impl(const void *q, const void *k, const void *v, const v
     if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL_ARG;
 
     const size_t eb = dtype_bytes(io_dtype), gb = dtype_bytes(gate_dtype);
-    const int32_t c = effective_chunk(chunk, num_seqs, total_tokens);
+    const int32_t c = method_for(chunk, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype, gate_dtype);
     // The token scan uses no workspace: its buffer is not checked or touched.
     const PrefillLayout L = c == 1 ? PrefillLayout{} : prefill_layout(num_seqs, total_tokens, hk, hv, dk, c, eb);
     if (c != 1 && (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255)))

@@ -129,7 +129,12 @@ struct NormArgs {
 };
 hipError_t launch_norm_apply(const NormArgs &a, hipStream_t st);
 
-// gdn_prefill with chunk 0 evaluates token by token when
+// The chunk gdn_tune_prefill cached for this shape on the current device, or
+// 0 (nothing cached, or no device to ask).
+int32_t tuned_chunk(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv, int32_t d, int32_t io,
+                    int32_t gate);
+
+// gdn_prefill with chunk 0 (when nothing is tuned) evaluates token by token when
 // total_tokens <= max(kTokenScanTokens, kTokenScanPerSeq * num_seqs), else in
 // chunks of 64. Measured at HK=16, HV=32, d=128: one sequence breaks even at
 // about 56 tokens, while 64 sequences of 1 to 8 tokens run 2.3 to 4 times

@@ -97,9 +97,11 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
  *              many tokens (the WY form: a preparation kernel, then the
  *              chunk-recurrent scan). 1: token by token, the state rows held
  *              in registers (one kernel, no workspace), which is faster for
- *              short prompts and multi-token steps. 0: 1 when total_tokens
- *              <= max(64, 16 * num_seqs), else 64. The result does not depend
- *              on it beyond rounding.
+ *              short prompts and multi-token steps. 0: the method that
+ *              gdn_tune_prefill cached for this device and shape bucket if
+ *              there is one, else 1 when total_tokens <= max(64, 16 *
+ *              num_seqs), else 64. The result does not depend on it beyond
+ *              rounding.
  * dk, dv       16, 32, 64 or 128 each.
  * scale        multiplies every output (1.0 for the plain rule).
  * initial_state  fp32 [N][hv][dv][dk], or NULL for zero states.
@@ -111,7 +113,8 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
  *              bytes, 256-byte aligned; contents need not be initialised and
  *              are meaningless afterwards. Calls on different streams need
  *              different workspaces. Token by token (chunk 1, or chunk 0
- *              choosing it) uses none; it may then be NULL.
+ *              choosing it) uses none; it may then be NULL. The size for
+ *              chunk 0 covers whichever method it picks.
  */
 int32_t gdn_prefill(const void *q, const void *k, const void *v,
                     const void *g, const void *beta,
@@ -199,6 +202,56 @@ int32_t gdn_decode_step_ex(const void *q, const void *k, const void *v,
                            void *state, int32_t state_dtype,
                            const int32_t *state_slots, int32_t num_slots,
                            const float *norm_weight, float norm_eps, void *out, void *stream);
+
+/*
+ * Choice of the prefill method by measurement, with a correctness gate.
+ *
+ * The fastest evaluation (token by token, or chunks of 16, 32 or 64) depends
+ * on the shape and the hardware ("Qwen cree trois formes de charges de
+ * travail distinctes" of "Optimiser l'inference sur appareil pour Apple
+ * Silicon"); the engine of "On descend d'un cran : #004 le meme compilateur
+ * sur les puces d'Apple" measures its options at load time and checks each
+ * against a reference, with 1/64 of the largest value as its bar.
+ *
+ * gdn_tune_prefill runs every method on the caller's inputs (same arguments
+ * as gdn_prefill, fp32 initial state or NULL). It compares each method's
+ * output and final state with those of chunk 64 and rejects it when
+ * max |x - ref| / max |ref| exceeds gate_tol, in [0, 1] (1/64 is the pages'
+ * bar). It times the rest, each one warm-up plus the mean of five runs on
+ * the same inputs, and returns the fastest in *chosen_chunk. It also caches
+ * the choice for (device, driver version, library version, shape bucket).
+ * The bucket is num_seqs and total_tokens each rounded up to a power of two,
+ * with hk, hv, d and both dtypes exact. gdn_prefill with chunk 0 then uses
+ * the cached choice.
+ * candidate_ms and candidate_err (may be NULL) receive, for chunks 64, 32,
+ * 16 and 1 in that order, the mean time in ms (-1 when rejected or not
+ * applicable) and the gate error (-1 when not run).
+ * scratch      device memory of gdn_tune_prefill_scratch_size(...) bytes,
+ *              256-byte aligned: outputs, final states and a workspace for
+ *              the candidates. The caller's buffers are read, never written.
+ * The call synchronises `stream`. Errors: as gdn_prefill, plus
+ * GDN_ERR_BAD_VALUE for gate_tol outside [0, 1].
+ *
+ * The cache lives in the process, shared by all threads, and may be saved
+ * to a text file and loaded back, one choice per line. Entries made on
+ * another device, driver or library version are kept but never match.
+ * gdn_tune_cache_load returns GDN_ERR_BAD_VALUE when the file cannot be
+ * opened, and skips lines it cannot parse; *entries (may be NULL) receives
+ * the number loaded.
+ */
+size_t gdn_tune_prefill_scratch_size(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
+                                     int32_t dk, int32_t dv, int32_t io_dtype);
+int32_t gdn_tune_prefill(const void *q, const void *k, const void *v,
+                         const void *g, const void *beta,
+                         const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                         int32_t hk, int32_t hv, int32_t dk, int32_t dv, float scale,
+                         int32_t io_dtype, int32_t gate_dtype, const float *initial_state,
+                         float gate_tol, void *scratch, size_t scratch_bytes, void *stream,
+                         int32_t *chosen_chunk, float *candidate_ms, float *candidate_err);
+void gdn_tune_cache_clear(void);
+int32_t gdn_tune_cache_size(void);
+int32_t gdn_tune_cache_save(const char *path);
+int32_t gdn_tune_cache_load(const char *path, int32_t *entries);
 
 /*
  * Per-kernel timing (a profiling aid, not needed for computation).

@@ -37,7 +37,7 @@ def declared_functions():
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert {"gdn_prefill", "gdn_decode_step", "gdn_prefill_workspace_size",
-            "gdn_prefill_ex", "gdn_decode_step_ex",
+            "gdn_prefill_ex", "gdn_decode_step_ex", "gdn_tune_prefill", "gdn_tune_cache_load",
             "gdn_status_string", "gdn_abi_version"} <= set(names)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in gdn.h but not exported"
@@ -72,9 +72,9 @@ def test_workspace_size(lib):
     # token by token (chunk 1) needs no workspace; a nonzero size still means
     # "accepted". Chunk 0 picks it when T <= max(64, 16 N), chunks of 64 above.
     assert _ws(c=1) == 256 and _ws(c=1, T=1 << 20) == 256
-    assert _ws(c=0, T=64) == 256 and _ws(c=0, n=64, T=1024) == 256
-    assert _ws(c=0, T=65) == _ws(c=64, T=65) > 256
-    assert _ws(c=0) == w
+    # chunk 0 may take a tuned choice, so it covers every chunked method
+    for n, T in ((1, 64), (64, 1024), (1, 65), (1, 4096)):
+        assert _ws(c=0, n=n, T=T) == max(_ws(c=c, n=n, T=T) for c in (16, 32, 64)) > 256
     assert _ws(c=2) == 0 and _ws(c=-1) == 0
 
 
@@ -222,3 +222,51 @@ def test_ex_argument_checks(lib):
     assert _prefill_ex(lib, sf=NORM_W - 64) == ALIAS
     assert _prefill_ex(lib, ws=None) == WORKSPACE
     assert _decode_ex(lib, B=0) == OK
+
+
+def test_tune_cache_file_round_trip(tmp_path):
+    """The tuning cache's text file: well-formed lines load, malformed ones
+    and unknown methods are skipped, and a save writes what was loaded."""
+    lib = gdn.load()
+    gdn.tune_cache_clear()
+    src = tmp_path / "tune.txt"
+    src.write_text(
+        "gdn-tune-v1 gfx950/256cu 70000 3001 1 4096 16 32 128 0 1 64\n"
+        "gdn-tune-v1 gfx950/256cu 70000 3001 64 1024 16 32 128 0 0 1\n"
+        "gdn-tune-v1 gfx950/256cu 70000 3001 8 512 2 4 64 1 1 48\n"  # not a method
+        "gdn-tune-v2 gfx950/256cu 70000 3001 8 512 2 4 64 1 1 16\n"  # other format
+        "garbage\n")
+    assert gdn.tune_cache_load(str(src)) == 2
+    assert gdn.tune_cache_size() == 2
+    out = tmp_path / "saved.txt"
+    gdn.tune_cache_save(str(out))
+    lines = sorted(out.read_text().splitlines())
+    assert lines == sorted(src.read_text().splitlines()[:2])
+    gdn.tune_cache_clear()
+    assert gdn.tune_cache_size() == 0
+    with pytest.raises(gdn.GdnError):
+        gdn.tune_cache_load(str(tmp_path / "missing.txt"))
+    assert lib.gdn_tune_cache_save(None) == NULL_ARG
+
+
+def test_tune_scratch_size(lib):
+    size = lib.gdn_tune_prefill_scratch_size(1, 4096, 16, 32, 128, 128, BF16)
+    out_b = 4096 * 32 * 128 * 2
+    fin_b = 32 * 128 * 128 * 4
+    assert size >= 2 * out_b + 2 * fin_b + _ws(c=0)
+    assert lib.gdn_tune_prefill_scratch_size(1, 4096, 3, 32, 128, 128, BF16) == 0
+
+
+@no_gpu
+def test_tune_argument_checks(lib):
+    chosen = ctypes.c_int32(0)
+    # host-side rejections (nothing is launched)
+    args = [FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30), FAKE + (5 << 30),
+            1, 128, 2, 4, 64, 64, 1.0, BF16, F32, None]
+    need = lib.gdn_tune_prefill_scratch_size(1, 128, 2, 4, 64, 64, BF16)
+    assert lib.gdn_tune_prefill(*args, 1.0 / 64, FAKE + (6 << 30), need, None, None, None, None) == NULL_ARG
+    assert lib.gdn_tune_prefill(*args, -0.1, FAKE + (6 << 30), need, None, ctypes.byref(chosen), None,
+                                None) == BAD_VALUE
+    assert lib.gdn_tune_prefill(*args, 1.0 / 64, FAKE + (6 << 30), need - 1, None, ctypes.byref(chosen), None,
+                                None) == WORKSPACE
+    assert lib.gdn_tune_prefill(*args, 1.0 / 64, None, need, None, ctypes.byref(chosen), None, None) == WORKSPACE
