@@ -45,6 +45,7 @@ KERNEL_KINDS = ("schedule", "prep", "scan", "decode", "token_scan", "decode_norm
 STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
     4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP", 6: "GDN_ERR_ALIAS", 7: "GDN_ERR_BAD_VALUE",
+    8: "GDN_ERR_MISALIGNED",
 }
 
 

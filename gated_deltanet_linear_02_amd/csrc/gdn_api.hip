@@ -62,6 +62,10 @@ static Range span(const void *p, size_t bytes) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p);
     return Range{a, a + bytes};
 }
+// Tensors the kernels read or write in 16-byte pieces must start on a
+// 16-byte boundary (their rows are then aligned too: d >= 16).
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 static bool overlaps(Range a, Range b) {
     if (a.lo == a.hi || b.lo == b.hi || a.lo == 0 || b.lo == 0) return false;
     return a.lo < b.hi && b.lo < a.hi;
@@ -85,6 +89,7 @@ const char *gdn_status_string(int32_t status) {
     case GDN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case GDN_ERR_ALIAS: return "output buffer overlaps an input buffer";
     case GDN_ERR_BAD_VALUE: return "a scalar argument is out of range (norm eps must be finite and >= 0)";
+    case GDN_ERR_MISALIGNED: return "q, k, v, out or a state tensor does not start on a 16-byte boundary";
     default: return "unknown status";
     }
 }
@@ -168,6 +173,9 @@ static int32_t prefill_impl(const void *q, const void *k, const void *v, const v
     if (so != GDN_OK) return so;
     if (!cu_seqlens) return GDN_ERR_NULL_ARG;
     if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(initial_state) ||
+        !aligned16(final_state))
+        return GDN_ERR_MISALIGNED;
 
     const size_t eb = dtype_bytes(io_dtype), gb = dtype_bytes(gate_dtype);
     const int32_t c = method_for(chunk, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype, gate_dtype);
@@ -258,6 +266,8 @@ static int32_t decode_impl(const void *q, const void *k, const void *v, const vo
     if ((int64_t)batch * hv > INT32_MAX) return GDN_ERR_UNSUPPORTED;
     if (!state_slots && num_slots < batch) return GDN_ERR_BAD_SHAPE;
     if (!q || !k || !v || !g || !beta || !state || !out) return GDN_ERR_NULL_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(state))
+        return GDN_ERR_MISALIGNED;
 
     const size_t eb = dtype_bytes(io_dtype), gb = dtype_bytes(gate_dtype), B = (size_t)batch;
     const Range r_out = span(out, B * hv * dv * eb);

@@ -24,7 +24,9 @@
  * ---------------------------------------
  * - Every tensor pointer is a DEVICE pointer to row-major, contiguous memory
  *   that the caller owns. The library allocates no device memory per call and
- *   keeps no pointer after a call returns.
+ *   keeps no pointer after a call returns. q, k, v, out and the states are
+ *   read and written in 16-byte pieces and must start on a 16-byte boundary
+ *   (GDN_ERR_MISALIGNED); device allocations always do.
  * - Layouts, with T = total tokens, N = sequences, B = decode batch:
  *       q, k            [T][hk][dk]         (decode: [B][hk][dk])
  *       v, out          [T][hv][dv]         (decode: [B][hv][dv])
@@ -63,7 +65,8 @@ typedef enum {
     GDN_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
     GDN_ERR_HIP = 5,         /* a HIP runtime call or launch failed */
     GDN_ERR_ALIAS = 6,       /* out overlaps an input */
-    GDN_ERR_BAD_VALUE = 7    /* a scalar argument out of range (norm eps) */
+    GDN_ERR_BAD_VALUE = 7,   /* a scalar argument out of range (norm eps) */
+    GDN_ERR_MISALIGNED = 8   /* q, k, v, out or a state not 16-byte aligned */
 } gdn_status;
 
 typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;

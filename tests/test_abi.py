@@ -16,7 +16,7 @@ import gated_deltanet_linear_02_amd as gdn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn.h")
 
-OK, NULL_ARG, BAD_SHAPE, UNSUPPORTED, WORKSPACE, HIP, ALIAS, BAD_VALUE = range(8)
+OK, NULL_ARG, BAD_SHAPE, UNSUPPORTED, WORKSPACE, HIP, ALIAS, BAD_VALUE, MISALIGNED = range(9)
 BF16, F32 = 0, 1
 
 
@@ -45,7 +45,7 @@ def test_exports_every_declared_function(lib):
 
 def test_version_and_status_strings(lib):
     assert gdn.abi_version() == 3
-    for s in range(8):
+    for s in range(9):
         assert lib.gdn_status_string(s)
     assert b"unknown" in lib.gdn_status_string(99)
 
@@ -120,12 +120,17 @@ def test_prefill_argument_checks(lib):
     assert _prefill(lib, ws=FAKE + (7 << 30) + 16) == WORKSPACE  # misaligned
     # out overlapping an input
     assert _prefill(lib, out=FAKE + 64) == ALIAS
-    assert _prefill(lib, out=FAKE + (4 << 30) + 8) == ALIAS
+    assert _prefill(lib, out=FAKE + (4 << 30) + 16) == ALIAS
     # final state overlapping q
     assert _prefill(lib, sf=FAKE + 128) == ALIAS
+    # tensors read in 16-byte pieces must be 16-byte aligned (gates need not)
+    assert _prefill(lib, q=FAKE + 8) == MISALIGNED
+    assert _prefill(lib, out=FAKE + (6 << 30) + 2) == MISALIGNED
+    assert _prefill(lib, s0=FAKE + (8 << 30) + 4) == MISALIGNED
+    assert _prefill(lib, g=FAKE + (3 << 30) + 4, beta=FAKE + (4 << 30) + 4) != MISALIGNED
     # in-place final == initial state is allowed by validation (it would launch
     # next, so it is not called here); overlapping but different is not
-    assert _prefill(lib, s0=FAKE + (8 << 30), sf=FAKE + (8 << 30) + 4) == ALIAS
+    assert _prefill(lib, s0=FAKE + (8 << 30), sf=FAKE + (8 << 30) + 16) == ALIAS
 
 
 def _decode(lib, **kw):
@@ -149,9 +154,11 @@ def test_decode_argument_checks(lib):
     assert _decode(lib, num_slots=10) == BAD_SHAPE  # identity slots need num_slots >= batch
     assert _decode(lib, dk=48, dv=48) == UNSUPPORTED
     assert _decode(lib, io=3) == UNSUPPORTED
-    assert _decode(lib, out=FAKE + 100) == ALIAS
+    assert _decode(lib, out=FAKE + 96) == ALIAS
     assert _decode(lib, out=FAKE + (5 << 30) + 4096) == ALIAS  # out inside the state
     assert _decode(lib, state=FAKE + (2 << 30) + 64) == ALIAS  # state over v
+    assert _decode(lib, v=FAKE + (2 << 30) + 2) == MISALIGNED
+    assert _decode(lib, state=FAKE + (5 << 30) + 4) == MISALIGNED
 
 
 def test_timing_stop_without_start(lib):
