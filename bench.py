@@ -721,6 +721,54 @@ def state_storage_bench(dev, copies, steps):
             }), flush=True)
 
 
+def graph_bench(dev, steps):
+    """One decode step per token, launched eagerly (Python, ctypes, one HIP
+    launch) against the same step captured once in a HIP graph and replayed,
+    at batch 1, 8 and 64 (HK=16, HV=32, d=128, bf16, fp32 states). One JSON
+    line per batch; times from events around `steps` back-to-back steps."""
+    import torch
+    import gdn_synth as gs
+    import gated_deltanet_linear_02_amd as gdn
+    for B in (1, 8, 64):
+        d = device_inputs(gs.make_inputs([1] * B, HK, HV, D, D, seed=gs.SEED_BASE + 1, io_dtype="bf16",
+                                         gate_dtype="bf16"), dev)
+        state = torch.from_numpy(gs.decode_state(B, HV, D, D, seed=gs.SEED_BASE + 101)).to(dev)
+        out = torch.empty((B, HV, D), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, out=out)
+
+        step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+
+        def timed(fn):
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps
+
+        eager_ms, graph_ms = timed(step), timed(graph.replay)
+        gdn.timing_start(steps)
+        for _ in range(steps):
+            step()
+        kms = gdn.timing_stop()["decode"]["mean_ms"]
+        print(json.dumps({
+            "mode": "graph", "batch": B, "eager_ms": eager_ms, "graph_ms": graph_ms, "kernel_ms": kms,
+            "eager_tokens_per_s": B / (eager_ms * 1e-3), "graph_tokens_per_s": B / (graph_ms * 1e-3),
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"decode batch {B}, HK={HK}, HV={HV}, d={D}, fp32 state"},
+        }), flush=True)
+
+
 # Shapes for the tuning sweep: (sequences, tokens each).
 TUNE_SHAPES = ((1, 16), (1, 48), (1, 128), (1, 512), (8, 4), (64, 1), (64, 4), (64, 16), (8, 300), (1, 4096))
 
@@ -802,6 +850,8 @@ def main():
     ap.add_argument("--tune", action="store_true",
                     help="instead of the main line: tune the prefill method per shape and time chunk 0 "
                          "under the fixed rule and under the tuned choice, one JSON line per shape")
+    ap.add_argument("--graph", action="store_true",
+                    help="instead of the main line: decode steps launched eagerly vs replayed from a HIP graph")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before warm-up, run 3 device-to-device copies of this many MiB "
                          "(the known-size reference for HBM byte counters)")
@@ -857,6 +907,9 @@ def main():
         return
     if args.tune:
         tuning_sweep(dev, args.copies, min(args.steps, 30))
+        return
+    if args.graph:
+        graph_bench(dev, max(args.steps, 100))
         return
     if args.bf16_state:
         probe_copies(dev, args.copy_probe_mib)
