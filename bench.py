@@ -51,10 +51,11 @@ def scan_flops_per_token(hv=HV, dk=D, dv=D, c=CHUNK):
     return hv * (6 * dk * dv + 4 * c * dv)
 
 
-def prep_flops_per_token(hk=HK, dk=D, c=CHUNK):
+def prep_flops_per_token(hk=HK, hv=HV, dk=D, c=CHUNK):
     """Algorithmic MFMA flops of the chunk-preparation kernel per token:
-    K K^T and Q K^T per query/key head (2*C*dk each)."""
-    return hk * 4 * c * dk
+    K K^T and Q K^T per query/key head (2*C*dk each), and W = T diag(b gamma) K
+    per value head (2*C*dk)."""
+    return hk * 4 * c * dk + hv * 2 * c * dk
 
 
 def decode_bytes_per_step(b=B_DECODE, hk=HK, hv=HV, dk=D, dv=D, state_bytes=4):
@@ -274,9 +275,21 @@ def device_inputs(inp, dev):
                 cu_seqlens=torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev))
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(threads: int):
     """The fp64 oracle on the host cores: the full 4096-token prefill (all 32
-    value heads) plus one decode step at batch 64."""
+    value heads) plus one decode step at batch 64, with `threads` threads and
+    (the prefill only) with one."""
     import gdn_synth as gs
     import oracle
     inp = gs.workload("prefill")
@@ -284,6 +297,9 @@ def cpu_baseline(threads: int):
     t0 = time.perf_counter()
     oracle.scan(w["q"], w["k"], w["v"], w["g"], w["beta"], w["cu_seqlens"], threads=threads)
     t_pre = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.scan(w["q"], w["k"], w["v"], w["g"], w["beta"], w["cu_seqlens"], threads=1)
+    t_pre1 = time.perf_counter() - t0
     dec = gs.workload("decode", batch=B_DECODE)
     wd = dec.widened()
     s0 = gs.decode_state(B_DECODE, HV, D, D, seed=gs.SEED_BASE + 101).astype(np.float64)
@@ -297,6 +313,9 @@ def cpu_baseline(threads: int):
                   f"fp64 token scan in C; prefill {t_pre:.2f} s, decode {t_dec * 1e3:.1f} ms",
         "prefill_tokens_per_s": T_PREFILL / t_pre,
         "decode_tokens_per_s": B_DECODE / t_dec,
+        "prefill_tokens_per_s_one_thread": T_PREFILL / t_pre1,
+        "cpu_model": _cpu_model(),
+        "host_cpus": os.cpu_count(),
     }
 
 
@@ -581,6 +600,65 @@ def summarize_tune(stats_dir: str, results_jsonl: str):
         lines.append(f"| {d['num_seqs']} x {d['tokens_per_seq']} | {d['rule_chunk']} | {d['rule_ms'] * 1e3:.1f} | "
                      f"{d['tuned_chunk']} | {d['tuned_ms'] * 1e3:.1f} | {d['speedup']:.2f} | {warm} |")
     with open(os.path.join(ROOT, "profiles", "gdn_prefill_tuning.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def summarize_mfma(pmc_dir: str, stats_dir: str):
+    """Write profiles/gdn_mfma_counters.md: MFMA work counted by the hardware
+    (SQ_INSTS_VALU_MFMA_MOPS_*, 512 flops per unit) per launch of the
+    preparation and scan kernels, beside their algorithmic flops, and the
+    rates both give over the kernels' mean durations (kernel trace)."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(os.path.join(pmc_dir, "run_counter_collection.csv"))):
+        short = _short_kernel(r["Kernel_Name"])
+        if short in ("prep", "scan"):
+            per.setdefault(short, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    dur = {}
+    for r in csv.DictReader(open(os.path.join(stats_dir, "run_kernel_stats.csv"))):
+        short = _short_kernel(r["Name"])
+        if short in ("prep", "scan"):
+            dur[short] = float(r["AverageNs"]) * 1e-9
+    algo = {"scan": scan_flops_per_token() * T_PREFILL, "prep": prep_flops_per_token() * T_PREFILL}
+    lines = [
+        f"# MFMA work counted by the hardware: prefill 1x{T_PREFILL} (HK={HK}, HV={HV}, d={D}, C={CHUNK}, bf16)",
+        "",
+        "Made by (from the repository root; OUT is any scratch directory):",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp",
+        "rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES "
+        "SQ_BUSY_CYCLES GRBM_GUI_ACTIVE -d OUT/mfma -o run --output-format csv -- "
+        "python3 REPO/bench.py --no-cpu-baseline --steps 5 --warmup 2",
+        "rocprofv3 --kernel-trace --stats -d OUT/stats -o run --output-format csv -- "
+        "python3 REPO/bench.py --no-cpu-baseline --steps 20",
+        "cd REPO && python3 bench.py --summarize-mfma OUT/mfma OUT/stats",
+        "```",
+        "",
+        f"Kernel sources hash: `{kernel_source_hash()}`. One MOPS unit is 512 flops.",
+        "",
+        "| kernel | counted bf16 GFLOP | counted fp32 GFLOP | algorithmic GFLOP | counted / algorithmic "
+        "| mean us | counted TFLOP/s | algorithmic TFLOP/s | of 2.5 PFLOP/s bf16 (counted) |",
+        "|---|---|---|---|---|---|---|---|---|",
+    ]
+    for k in ("prep", "scan"):
+        c = per.get(k, {})
+        if not c or k not in dur:
+            continue
+        bf = sum(c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [0])) / max(1, len(c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [0]))) * 512
+        f32 = sum(c.get("SQ_INSTS_VALU_MFMA_MOPS_F32", [0])) / max(1, len(c.get("SQ_INSTS_VALU_MFMA_MOPS_F32", [0]))) * 512
+        t = dur[k]
+        lines.append(f"| {KERNELS[k]} | {bf / 1e9:.2f} | {f32 / 1e9:.3f} | {algo[k] / 1e9:.2f} | {bf / algo[k]:.2f} | "
+                     f"{t * 1e6:.1f} | {bf / t / 1e12:.0f} | {algo[k] / t / 1e12:.0f} | "
+                     f"{100 * bf / t / 1e12 / PEAK_BF16_TFLOPS:.1f}% |")
+    lines += ["", "Counted below algorithmic: the kernels skip the zero blocks of the triangular T and P "
+              "(the algorithmic count takes full C x C tiles); the preparation kernel's fp32 MFMA is the "
+              "blocked triangular inverse. Raw means per launch (sums over the device's XCDs, SEs or SIMDs "
+              "as each counter defines):", ""]
+    for k in ("prep", "scan"):
+        if k in per:
+            lines.append(f"- {KERNELS[k]}: " + ", ".join(f"{n} {sum(v) / len(v):.0f}" for n, v in sorted(per[k].items())))
+    with open(os.path.join(ROOT, "profiles", "gdn_mfma_counters.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
@@ -870,8 +948,14 @@ def main():
                          "profiles/gdn_decode_state_storage.md and exit")
     ap.add_argument("--summarize-tune", nargs=2, metavar=("STATS_DIR", "RESULTS_JSONL"),
                     help="host only: turn a kernel trace of --tune into profiles/gdn_prefill_tuning.md and exit")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "STATS_DIR"),
+                    help="host only: turn an MFMA counter run and a kernel trace into "
+                         "profiles/gdn_mfma_counters.md and exit")
     args = ap.parse_args()
 
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
+        return
     if args.summarize_tune:
         summarize_tune(*args.summarize_tune)
         return
@@ -973,6 +1057,21 @@ def main():
     wall = time.perf_counter() - wall0
     ms_step = e0.elapsed_time(e1) / args.steps
 
+    # ---- spread of the step time (a separate pass: an event pair per step)
+    per_step = []
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(sets[i % args.copies])
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(a.elapsed_time(b) for a, b in evs)
+
+    def pct(p):
+        return per_step[min(len(per_step) - 1, int(round(p / 100 * (len(per_step) - 1))))]
+
     # ---- per-kernel pass (same steps, each launch bracketed by events)
     gdn.timing_start(8 * args.steps)
     for i in range(args.steps):
@@ -1039,6 +1138,7 @@ def main():
         "decode": {"tokens_per_s": B_DECODE / (ms_dec * 1e-3), "ms": ms_dec, "kernel_ms": dec_ms,
                    "hbm_frac": dec_gbs / PEAK_HBM_GBS},
         "wall_ms_per_step": wall * 1e3 / args.steps,
+        "step_ms_percentiles": {"p10": pct(10), "p50": pct(50), "p90": pct(90)},
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -68,12 +68,27 @@ def test_prefill_4k(io):
     _check(inp, o, f, label="prefill T=4096")
 
 
+def _segment_errors(o, o_ref, heads, seg=4096):
+    """max |gpu - ref| per segment of `seg` tokens, over the sampled heads,
+    relative to the largest reference magnitude of the whole sequence."""
+    og, orf = to_f64(o)[:, heads], o_ref[:, heads]
+    den = float(np.abs(orf).max())
+    return [float(np.abs(og[t:t + seg] - orf[t:t + seg]).max()) / den for t in range(0, len(orf), seg)]
+
+
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 def test_long_32k_sampled_heads(io):
+    """T = 32768 with an initial state; the error is also reported per
+    4096-token segment, to show whether it grows along the state carry."""
     inp = gs.workload("long", io_dtype=io)
+    heads = [0, 13, 31]
     note(f"prefill T=32768 io={io}")
     o, f = run_prefill(inp, chunk=64)
-    _check(inp, o, f, heads=[0, 13, 31], label="long T=32768")
+    _check(inp, o, f, heads=heads, label="long T=32768")
+    o_ref, _ = oracle_ref(inp, heads=heads)
+    errs = _segment_errors(o, o_ref, heads)
+    print(f"[segments] long T=32768 io={io} out_err per 4K: " + " ".join(f"{e:.2e}" for e in errs), flush=True)
+    assert max(errs) <= tol(io)
 
 
 def test_long_no_decay_stress():
@@ -84,6 +99,12 @@ def test_long_no_decay_stress():
     note("prefill T=32768 g=0 stress")
     o, f = run_prefill(inp, chunk=64)
     _check(inp, o, f, heads=[5], label="long g=0")
+    o_ref, _ = oracle_ref(inp, heads=[5])
+    errs = _segment_errors(o, o_ref, [5])
+    print("[segments] long g=0 f32 out_err per 4K: " + " ".join(f"{e:.2e}" for e in errs), flush=True)
+    # carried over all 32768 tokens, the error must not grow: the last
+    # segment stays within a few times the first
+    assert errs[-1] <= 4 * errs[0] + 1e-6
 
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
@@ -302,3 +323,27 @@ def test_first_sequence_not_at_token_zero(io):
     print(f"[parity] cu0=5 io={io} out_err={eo:.3e} state_err={ef:.3e}", flush=True)
     assert eo <= tol(io) and ef <= tol(io)
     assert torch.isnan(o[:5].float()).all(), "tokens before the first sequence must not be written"
+
+
+def test_tiny_as_64_decode_steps():
+    """The tiny workload (T = 64, HK = HV = 2, d = 16, fp32) run as 64
+    decode steps, one token each, equals the chunked prefill (C = 16) and
+    the oracle: the two GPU paths evaluate one recurrence."""
+    inp = gs.workload("tiny", io_dtype="f32")
+    note("tiny as 64 decode steps")
+    o_p, f_p = run_prefill(inp, chunk=16)
+    d = device_inputs(inp)
+    state = torch.zeros((1, 2, 16, 16), dtype=torch.float32, device="cuda")
+    outs = []
+    for t in range(64):
+        sl = slice(t, t + 1)
+        outs.append(gdn.decode_step(d["q"][sl], d["k"][sl], d["v"][sl], d["g"][sl], d["beta"][sl], state))
+    torch.cuda.synchronize()
+    o_d = torch.cat(outs, 0)
+    o_ref, f_ref = oracle_ref(inp)
+    e_do, e_ds = rel_err(to_f64(o_d), o_ref), rel_err(to_f64(state), f_ref)
+    e_pd = rel_err(to_f64(o_d), to_f64(o_p))
+    print(f"[parity] tiny as 64 decode steps out_err={e_do:.3e} state_err={e_ds:.3e} vs prefill {e_pd:.3e}",
+          flush=True)
+    assert e_do <= TOL_F32 and e_ds <= TOL_F32 and e_pd <= TOL_F32
+    assert rel_err(to_f64(state), to_f64(f_p)) <= TOL_F32
