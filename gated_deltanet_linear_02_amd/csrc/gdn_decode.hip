@@ -219,8 +219,9 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(
 // Decode with the output normalisation fused in
 // ---------------------------------------------------------------------------
 //
-// The recurrent update "with its normalisation" in one launch (section
-// "Reduire le trafic intermediaire et d'etat"): per (sequence, value head)
+// The recurrent update and the normalisation that follows it, in one launch
+// (the pages fuse the two: section "Reduire le trafic intermediaire et
+// d'etat"): per (sequence, value head)
 // the output row o (dv values) becomes
 //     y_i = o_i w_i / sqrt(mean_j o_j^2 + eps),
 // which needs every row of that head's state. So one workgroup owns a whole

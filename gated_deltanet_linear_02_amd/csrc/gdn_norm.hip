@@ -1,8 +1,9 @@
 // gdn_norm.hip -- output normalisation pass of the prefill (gfx950).
 //
-// The layer's output rows are normalised after the recurrent update (the
-// update "with its normalisation" of "Optimiser l'inference sur appareil pour
-// Apple Silicon", section "Reduire le trafic intermediaire et d'etat"): per
+// The layer's output rows are normalised after the recurrent update, which
+// the pages fuse with that normalisation ("Optimiser l'inference sur
+// appareil pour Apple Silicon", section "Reduire le trafic intermediaire et
+// d'etat"): per
 // (token, value head), with the dv outputs o and one weight per value channel
 //     y_i = o_i w_i / sqrt(mean_j o_j^2 + eps).
 // Decode fuses this into its kernel (gdn_decode.hip). The prefill kernels

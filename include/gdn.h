@@ -169,10 +169,10 @@ int32_t gdn_decode_step(const void *q, const void *k, const void *v,
  *              GDN_ERR_UNSUPPORTED); any other value is GDN_ERR_UNSUPPORTED.
  *
  * norm_weight  NULL, or an fp32 [dv] DEVICE array: every output row is then
- *              RMS-normalised. The recurrent update comes "with its
- *              normalisation" (section "Reduire le trafic intermediaire et
- *              d'etat" of the same page), whose form the pages do not give;
- *              here, per (token or sequence, value head) row of dv outputs,
+ *              RMS-normalised. The pages fuse the recurrent update with a
+ *              normalisation (section "Reduire le trafic intermediaire et
+ *              d'etat" of the same page) but do not give its form; here,
+ *              per (token or sequence, value head) row of dv outputs,
  *                  y_i = o_i * norm_weight[i] / sqrt(mean_j o_j^2 + norm_eps)
  *              with one weight per value channel shared by all heads. It must
  *              not overlap out or the states (GDN_ERR_ALIAS).

@@ -23,7 +23,7 @@ What is here:
                        chunked" on tiny inputs.
 * ``rms_norm``      -- the output normalisation that follows the recurrent
                        update (section "Reduire le trafic intermediaire et
-                       d'etat" names the update "with its normalisation"
+                       d'etat" fuses the update with a normalisation
                        without giving its form): per (token, value head),
                        the dv outputs divided by their root mean square,
                        with eps inside the root, times one weight per value
