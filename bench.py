@@ -67,11 +67,17 @@ def decode_bytes_per_step(b=B_DECODE, hk=HK, hv=HV, dk=D, dv=D, state_bytes=4):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: comments and whitespace are dropped,
+    so that counters taken on the same code stay valid after a comment edit."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_deltanet_linear_02_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8", errors="replace") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(name.encode() + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
