@@ -190,7 +190,7 @@ struct PrepSmem {
     static constexpr size_t off_T = off_A + (size_t)C * LDC * sizeof(float);
     static constexpr size_t at_end = off_T + (size_t)C * LDC * sizeof(float);
     static constexpr size_t off_c = ((kq_end > at_end ? kq_end : at_end) + 15) & ~(size_t)15;
-    static constexpr size_t off_b = off_c + (size_t)C * sizeof(float);
+    static constexpr size_t off_b = off_c + (size_t)C * sizeof(double);
     static constexpr size_t off_bg = off_b + (size_t)C * sizeof(float);
     // Chunk location when the kernel schedules itself: sequence ends and
     // lengths (256 each), 4 wave partials and 4 results.
@@ -239,6 +239,7 @@ template <typename G> __device__ __forceinline__ float gate_load(const G *p, siz
 // gates; results below the fp32 range flush to 0).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLog2eD = 1.4426950408889634;
 
 // acc += X[xr.., xc..] (16x16) * Y[yr.., yc..] (16x16), fp32 LDS operands
 // with row stride ld, on v_mfma_f32_16x16x4_f32.
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
     E *sQ = reinterpret_cast<E *>(smem + L::off_Q);
     float *sA = reinterpret_cast<float *>(smem + L::off_A);
     float *sT = reinterpret_cast<float *>(smem + L::off_T);
-    float *sc = reinterpret_cast<float *>(smem + L::off_c);    // c_t log2(e)
+    double *sc = reinterpret_cast<double *>(smem + L::off_c);  // c_t log2(e), fp64 (see the gate prefix)
     float *sb = reinterpret_cast<float *>(smem + L::off_b);    // b_t
     float *sbg = reinterpret_cast<float *>(smem + L::off_bg);  // b_t gamma_t
 
@@ -493,21 +494,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
                 bv = gate_load(gate_b, (size_t)(t0 + (valid ? lane : 0)) * hv + h);
             }
             if (!valid) x = bv = 0.f;
+            // The prefix sums are kept in fp64: every decay factor below is
+            // exp of a difference c_i - c_j, and where some g are huge (a
+            // decay that underflows to 0, g = -1e4) the sums reach -1e5 and
+            // more, where fp32 spacing (0.01) would wipe out the differences
+            // between nearby tokens.
+            double xd = x;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (lane >= off) x += y;
+                const double y = __shfl_up(xd, off);
+                if (lane >= off) xd += y;
             }
-            const float last = __shfl(x, C - 1);
+            const double last = __shfl(xd, C - 1);
             if (lane < C) {
-                const float gam = exp2_hw(x * kLog2e);
-                sc[lane] = x * kLog2e;
+                const float gam = exp2_hw(static_cast<float>(xd * kLog2eD));
+                sc[lane] = xd * kLog2eD;
                 sb[lane] = bv;
                 sbg[lane] = bv * gam;
                 float *rec = gates + ch * (size_t)gate_record(C);
-                rec[lane] = exp2_hw((last - x) * kLog2e);
+                rec[lane] = exp2_hw(static_cast<float>((last - xd) * kLog2eD));
                 rec[C + lane] = scale * gam;
-                if (lane == C - 1) rec[2 * C] = exp2_hw(last * kLog2e);
+                if (lane == C - 1) rec[2 * C] = exp2_hw(static_cast<float>(last * kLog2eD));
             }
         }
         __syncthreads();
@@ -520,20 +527,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
             for (int r = 0; r < TS::NR; ++r) {
                 const int ti = TS::row(r);
                 const int i = 16 * ti + ln;
-                const float cI = sc[i];
+                const double cI = sc[i];
                 const float mI = score_wave ? scale : sb[i];
                 f32x4 val[NB];
 #pragma unroll
                 for (int tj = 0; tj < NB; ++tj) {
                     val[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
                     if (tj <= TS::row(r)) {
-                        const f32x4 cJ = *reinterpret_cast<const f32x4 *>(sc + 16 * tj + 4 * g4);
                         const f32x4 t = til[TS::first(r) + (tj <= TS::row(r) ? tj : 0)];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int j = 16 * tj + 4 * g4 + e;
                             const bool keep = score_wave ? j <= i : j < i;
-                            val[tj][e] = keep ? mI * exp2_hw(cI - cJ[e]) * t[e] : 0.f;
+                            const float dc = static_cast<float>(cI - sc[j]);  // fp64 difference, then fp32
+                            val[tj][e] = keep ? mI * exp2_hw(dc) * t[e] : 0.f;
                         }
                         if (!score_wave) *reinterpret_cast<f32x4 *>(sA + i * LDC + 16 * tj + 4 * g4) = val[tj];
                     }

@@ -125,3 +125,22 @@ def test_decode_retrieval_exact_in_bf16():
     torch.cuda.synchronize()
     vb = gs.widen(inp.v, "bf16")
     assert np.array_equal(to_f64(out), vb)
+
+
+def test_decode_decay_underflow_resets():
+    """a = exp(-1e4) = 0: the new state is b v k^T, whatever the old one."""
+    inp, s0 = _decode_case(6, "f32", seed_off=11)
+    inp.g[...] = np.float32(-1e4)
+    note("decode with a = 0")
+    d = device_inputs(inp)
+    state = torch.from_numpy(s0).cuda()
+    out = gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state)
+    torch.cuda.synchronize()
+    w = inp.widened()
+    o_ref, s_ref = oracle.decode_step(w["q"], w["k"], w["v"], w["g"], w["beta"], s0.astype(np.float64))
+    # the reset state, written out: S = b v k^T per (sequence, value head)
+    kh = np.arange(32) // 2
+    want = w["beta"][:, :, None, None] * w["v"][:, :, :, None] * w["k"][:, kh][:, :, None, :]
+    assert rel_err(s_ref, want) <= 1e-12
+    assert rel_err(to_f64(state), want) <= TOL_F32
+    assert rel_err(to_f64(out), o_ref) <= TOL_F32

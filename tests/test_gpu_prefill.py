@@ -347,3 +347,39 @@ def test_tiny_as_64_decode_steps():
           flush=True)
     assert e_do <= TOL_F32 and e_ds <= TOL_F32 and e_pd <= TOL_F32
     assert rel_err(to_f64(state), to_f64(f_p)) <= TOL_F32
+
+
+@pytest.mark.parametrize("chunk", [64, 1])
+def test_sequences_beyond_the_ranked_count(chunk):
+    """4,500 sequences of 0 to 3 tokens: past 4,096 sequences the schedule
+    keeps them in index order instead of longest first; results are the
+    same."""
+    rng = np.random.default_rng(77)
+    lens = [int(x) for x in rng.integers(0, 4, 4500)]
+    inp = gs.make_inputs(lens, 1, 2, 32, 32, seed=79, io_dtype="f32", gate_dtype="f32", init_state=True)
+    note(f"prefill with {len(lens)} sequences chunk={chunk}")
+    o, f = run_prefill(inp, chunk=chunk)
+    o_ref, f_ref = oracle_ref(inp)
+    eo, ef = rel_err(to_f64(o), o_ref), rel_err(to_f64(f), f_ref)
+    print(f"[parity] N=4500 chunk={chunk} out_err={eo:.3e} state_err={ef:.3e}", flush=True)
+    assert eo <= TOL_F32 and ef <= TOL_F32
+
+
+@pytest.mark.parametrize("chunk", [64, 16, 1])
+def test_decay_underflow_resets_the_state(chunk):
+    """g = -1e4 makes a = exp(g) exactly 0: the state restarts from
+    b v k^T at those tokens (every token, or a random fifth of them). The
+    chunked form then holds cumulative log-decays near -6e5 and decay
+    factors of exactly 0 or 1; nothing may overflow or turn NaN."""
+    for frac in (1.0, 0.2):
+        inp = gs.make_inputs([150, 64, 9], 2, 4, 64, 64, seed=81, io_dtype="f32", gate_dtype="f32",
+                             init_state=True)
+        mask = np.random.default_rng(83).random(inp.g.shape) < frac
+        inp.g[mask] = np.float32(-1e4)
+        note(f"decay underflow frac={frac} chunk={chunk}")
+        o, f = run_prefill(inp, chunk=chunk)
+        o_ref, f_ref = oracle_ref(inp)
+        assert np.isfinite(to_f64(o)).all() and np.isfinite(to_f64(f)).all()
+        eo, ef = rel_err(to_f64(o), o_ref), rel_err(to_f64(f), f_ref)
+        print(f"[parity] reset frac={frac} chunk={chunk} out_err={eo:.3e} state_err={ef:.3e}", flush=True)
+        assert eo <= TOL_F32 and ef <= TOL_F32
