@@ -1,0 +1,56 @@
+"""Seeded random configurations against the fp64 oracle: sequence counts
+and lengths (empty and ragged ones included), head layouts, head sizes,
+dtypes, methods (chunk 0, 1, 16, 32, 64), scale, initial states or none,
+and gates with occasional extreme decays (g = -1e4, a = 0) and b = 0 or 1.
+Every case is drawn from its own seed, printed before it runs, and held to
+the usual bars (bf16 2e-2, fp32 1e-4 max-rel)."""
+
+import numpy as np
+import pytest
+
+import gdn_synth as gs
+from gpu_util import note, oracle_ref, rel_err, requires_gpu, run_prefill, to_f64, tol
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+LAYOUTS = [(1, 1), (1, 2), (2, 4), (2, 2), (4, 8), (1, 8), (4, 4)]
+
+
+def _case(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 7))
+    lens = [int(x) for x in rng.integers(0, 260, n)]
+    if rng.random() < 0.3:
+        lens[int(rng.integers(0, n))] = 0
+    hk, hv = LAYOUTS[int(rng.integers(0, len(LAYOUTS)))]
+    d = int(rng.choice([16, 32, 64, 128]))
+    io = "bf16" if rng.random() < 0.5 else "f32"
+    gate = "bf16" if (io == "bf16" and rng.random() < 0.5) else "f32"
+    chunk = int(rng.choice([0, 1, 16, 32, 64]))
+    scale = float(rng.choice([1.0, 0.5, 1.0 / np.sqrt(d)]))
+    init = bool(rng.random() < 0.6)
+    inp = gs.make_inputs(lens, hk, hv, d, d, seed=seed, io_dtype=io, gate_dtype=gate, init_state=init)
+    # occasional extreme gates: decays that underflow, no writes, full writes
+    g = gs.widen(inp.g, gate)
+    b = gs.widen(inp.beta, gate)
+    extreme = rng.random(g.shape)
+    g = np.where(extreme < 0.03, -1e4, g)
+    b = np.where(extreme > 0.97, 0.0, np.where((extreme > 0.94) & (extreme <= 0.97), 1.0, b))
+    inp.g = gs.to_storage(g, gate)
+    inp.beta = gs.to_storage(b, gate)
+    desc = f"seed={seed} lens={lens} hk={hk} hv={hv} d={d} io={io} gate={gate} chunk={chunk} scale={scale:.3f} init={init}"
+    return inp, chunk, scale, desc
+
+
+@pytest.mark.parametrize("seed", range(5000, 5024))
+def test_random_configuration(seed):
+    inp, chunk, scale, desc = _case(seed)
+    note(desc)
+    o, f = run_prefill(inp, chunk=chunk, scale=scale)
+    o_ref, f_ref = oracle_ref(inp, scale=scale)
+    og, fg = to_f64(o), to_f64(f)
+    assert np.isfinite(og).all() and np.isfinite(fg).all(), desc
+    eo = rel_err(og, o_ref) if og.size else 0.0
+    ef = rel_err(fg, f_ref)
+    print(f"[parity] random {desc} out_err={eo:.3e} state_err={ef:.3e}", flush=True)
+    assert eo <= tol(inp.io_dtype) and ef <= tol(inp.io_dtype), desc
