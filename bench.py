@@ -668,6 +668,56 @@ def summarize_mfma(pmc_dir: str, stats_dir: str):
         f.write("\n".join(lines) + "\n")
 
 
+def summarize_configs(stats_dir: str, results_jsonl: str):
+    """Write profiles/gdn_long_varlen.md from a rocprofv3 kernel trace of
+    `bench.py --configs` and the JSON lines that run printed."""
+    import csv
+    import re
+    rows = list(csv.DictReader(open(os.path.join(stats_dir, "run_kernel_stats.csv"))))
+    lines = [
+        f"# Long (T = 32768) and varlen (8 sequences, then 64 decode steps at batch 8) workloads; "
+        f"HK={HK}, HV={HV}, d={D}, C={CHUNK}, bf16",
+        "",
+        "Made by (from the repository root; OUT is any scratch directory):",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp",
+        "rocprofv3 --kernel-trace --stats -d OUT/stats -o run --output-format csv -- "
+        "python3 REPO/bench.py --configs > OUT/configs.jsonl",
+        "cd REPO && python3 bench.py --summarize-configs OUT/stats OUT/configs.jsonl",
+        "```",
+        "",
+        f"Kernel sources hash: `{kernel_source_hash()}`.",
+        "",
+        "## Kernel durations over the run (rocprofv3 --kernel-trace --stats)",
+        "",
+        "Both prefills' launches are averaged together; the per-workload kernel means follow below.",
+        "",
+        "| kernel | calls | mean us | min us | max us |",
+        "|---|---|---|---|---|",
+    ]
+    for r in rows:
+        short = _short_kernel(r["Name"])
+        if short in KERNELS:
+            lines.append(f"| {KERNELS[short]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", "## Per workload (HIP events in the same run, under the profiler)", "",
+              "| workload | sequences | tokens | prefill ms | tokens/s | prep ms | scan ms | scan MFMA | "
+              "decode b8 step us |", "|---|---|---|---|---|---|---|---|---|"]
+    for line in open(results_jsonl):
+        line = line.strip()
+        if not line.startswith("{"):
+            continue
+        d = json.loads(line)
+        km = d["kernel_ms"]
+        dec = f"{d['decode_b8_step_ms'] * 1e3:.1f}" if "decode_b8_step_ms" in d else "-"
+        lines.append(f"| {d['workload']} | {d['num_seqs']} | {d['total_tokens']} | {d['prefill_ms']:.3f} | "
+                     f"{d['tokens_per_s'] / 1e6:.1f} M | {km['prep']:.3f} | {km['scan']:.3f} | "
+                     f"{100 * d['scan_mfma_frac']:.1f}% | {dec} |")
+    with open(os.path.join(ROOT, "profiles", "gdn_long_varlen.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def norm_apply_bytes(tokens, hv=HV, dv=D, elem=2):
     """Algorithmic HBM bytes of the prefill's output-normalisation pass: every
     output row read and written once (the weight and cu_seqlens are a few
@@ -805,6 +855,69 @@ def state_storage_bench(dev, copies, steps):
             }), flush=True)
 
 
+def configs_bench(dev, reps):
+    """The long and varlen workloads, timed (they are parity cases in the
+    tests; here only their speed): a 32768-token prefill from an initial
+    state, and 8 packed sequences of 256 to 16384 tokens followed by 64
+    decode steps at batch 8 from their final states. HK=16, HV=32, d=128,
+    bf16 I/O, fp32 gates and states, chunk 64. One JSON line each."""
+    import torch
+    import gdn_synth as gs
+    import gated_deltanet_linear_02_amd as gdn
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for name in ("long", "varlen"):
+        inp = gs.workload(name)
+        d = device_inputs(inp, dev)
+        N, T = inp.num_seqs, inp.total_tokens
+        s0 = torch.from_numpy(inp.initial_state).to(dev)
+        fin = torch.empty_like(s0)
+        out = torch.empty((T, HV, D), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(gdn.prefill_workspace_size(N, T, HK, HV, D, D, CHUNK, torch.bfloat16),
+                         dtype=torch.uint8, device=dev)
+
+        def run():
+            gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=CHUNK,
+                        initial_state=s0, final_state=fin, out=out, workspace=ws)
+
+        ms = timed(run, reps)
+        gdn.timing_start(8 * reps)
+        for _ in range(reps):
+            run()
+        kt = gdn.timing_stop()
+        scan_ms = kt["scan"]["mean_ms"]
+        res = {"mode": "configs", "workload": name, "num_seqs": N, "total_tokens": T, "prefill_ms": ms,
+               "tokens_per_s": T / (ms * 1e-3),
+               "kernel_ms": {k: kt[k]["mean_ms"] for k in ("schedule", "prep", "scan")},
+               "scan_mfma_frac": scan_flops_per_token() * T / (scan_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+               "dtype": "bf16", "data": "synthetic",
+               "config": {"workload": f"{name}: {N} sequence(s), {T} tokens, HK={HK}, HV={HV}, d={D}, chunk {CHUNK}",
+                          "lengths": np.diff(inp.cu_seqlens).tolist()}}
+        if name == "varlen":
+            # 64 decode steps at batch 8 continuing from the final states
+            dec = device_inputs(gs.make_inputs([1] * N, HK, HV, D, D, seed=gs.SEED_BASE + 404, io_dtype="bf16",
+                                               gate_dtype="bf16"), dev)
+            state = fin.clone()
+            dout = torch.empty((N, HV, D), dtype=torch.bfloat16, device=dev)
+            step_ms = timed(lambda: gdn.decode_step(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], state,
+                                                    out=dout), 64)
+            res["decode_b8_step_ms"] = step_ms
+            res["decode_b8_tokens_per_s"] = N / (step_ms * 1e-3)
+        print(json.dumps(res), flush=True)
+        del d, out, ws, s0, fin
+        torch.cuda.empty_cache()
+
+
 def graph_bench(dev, steps):
     """One decode step per token, launched eagerly (Python, ctypes, one HIP
     launch) against the same step captured once in a HIP graph and replayed,
@@ -934,6 +1047,9 @@ def main():
     ap.add_argument("--tune", action="store_true",
                     help="instead of the main line: tune the prefill method per shape and time chunk 0 "
                          "under the fixed rule and under the tuned choice, one JSON line per shape")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the main line: time the long (T=32768) and varlen (8 sequences + 64 "
+                         "decode steps) workloads, one JSON line each")
     ap.add_argument("--graph", action="store_true",
                     help="instead of the main line: decode steps launched eagerly vs replayed from a HIP graph")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -957,8 +1073,13 @@ def main():
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_DIR", "STATS_DIR"),
                     help="host only: turn an MFMA counter run and a kernel trace into "
                          "profiles/gdn_mfma_counters.md and exit")
+    ap.add_argument("--summarize-configs", nargs=2, metavar=("STATS_DIR", "RESULTS_JSONL"),
+                    help="host only: turn a kernel trace of --configs into profiles/gdn_long_varlen.md and exit")
     args = ap.parse_args()
 
+    if args.summarize_configs:
+        summarize_configs(*args.summarize_configs)
+        return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma)
         return
@@ -1000,6 +1121,9 @@ def main():
         return
     if args.graph:
         graph_bench(dev, max(args.steps, 100))
+        return
+    if args.configs:
+        configs_bench(dev, min(args.steps, 10))
         return
     if args.bf16_state:
         probe_copies(dev, args.copy_probe_mib)
