@@ -148,6 +148,18 @@ def _check_norm_weight(w: torch.Tensor, dv: int) -> None:
         raise TypeError(f"norm_weight must be float32 with {dv} entries")
 
 
+def _expect(name: str, t: Optional[torch.Tensor], shape: tuple, dtype: Optional[torch.dtype] = None) -> None:
+    """The library reads and writes tensors by their declared sizes alone, so
+    a smaller tensor than the call implies would be accessed past its end:
+    shapes and dtypes are checked here, before the call."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} is {t.dtype}, expected {dtype}")
+
+
 def _on_device(dev: torch.device, **tensors) -> None:
     """Every tensor handed to the library must live on the GPU the call runs
     on: a host pointer would be dereferenced by a kernel."""
@@ -185,10 +197,17 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     T, hk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
     N = cu_seqlens.numel() - 1
-    if cu_seqlens.dtype != torch.int32:
-        raise TypeError("cu_seqlens must be int32")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise TypeError("cu_seqlens must be a 1-d int32 tensor")
     io = _dtype_code(q.dtype)
     gate = _dtype_code(g.dtype)
+    _expect("k", k, (T, hk, dk), q.dtype)
+    _expect("v", v, (T, hv, dv), q.dtype)
+    _expect("g", g, (T, hv))
+    _expect("beta", beta, (T, hv), g.dtype)
+    _expect("out", out, (T, hv, dv), q.dtype)
+    for name, st in (("initial_state", initial_state), ("final_state", final_state)):
+        _expect(name, st, (N, hv, dv, dk))
     dev = q.device
     if out is None:
         out = torch.empty((T, hv, dv), dtype=q.dtype, device=dev)
@@ -238,6 +257,13 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     hv, dv = v.shape[1], v.shape[2]
     if state.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("state must be float32 or bfloat16")
+    _expect("k", k, (B, hk, dk), q.dtype)
+    _expect("v", v, (B, hv, dv), q.dtype)
+    _expect("g", g, (B, hv))
+    _expect("beta", beta, (B, hv), g.dtype)
+    _expect("out", out, (B, hv, dv), q.dtype)
+    _expect("state", state, (state.shape[0], hv, dv, dk))
+    _expect("state_slots", state_slots, (B,))
     if state_slots is not None and state_slots.dtype != torch.int32:
         raise TypeError("state_slots must be int32")
     if out is None:
@@ -276,6 +302,13 @@ def tune_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Ten
     T, hk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
     N = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise TypeError("cu_seqlens must be a 1-d int32 tensor")
+    _expect("k", k, (T, hk, dk), q.dtype)
+    _expect("v", v, (T, hv, dv), q.dtype)
+    _expect("g", g, (T, hv))
+    _expect("beta", beta, (T, hv), g.dtype)
+    _expect("initial_state", initial_state, (N, hv, dv, dk))
     dev = q.device
     need = int(load().gdn_tune_prefill_scratch_size(N, T, hk, hv, dk, dv, _dtype_code(q.dtype)))
     if need == 0:
@@ -292,7 +325,7 @@ def tune_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Ten
     _check(load().gdn_tune_prefill(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, hk, hv, dk, dv, float(scale),
         _dtype_code(q.dtype), _dtype_code(g.dtype), _ptr(initial_state), float(gate_tol), _ptr(scratch),
-        scratch.numel(), _stream(dev, stream), ctypes.byref(chosen), ms, err))
+        scratch.numel() * scratch.element_size(), _stream(dev, stream), ctypes.byref(chosen), ms, err))
     return {"chunk": int(chosen.value), "ms": {c: float(ms[i]) for i, c in enumerate(TUNE_CANDIDATES)},
             "err": {c: float(err[i]) for i, c in enumerate(TUNE_CANDIDATES)}}
 

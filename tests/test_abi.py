@@ -277,3 +277,28 @@ def test_tune_argument_checks(lib):
     assert lib.gdn_tune_prefill(*args, 1.0 / 64, FAKE + (6 << 30), need - 1, None, ctypes.byref(chosen), None,
                                 None) == WORKSPACE
     assert lib.gdn_tune_prefill(*args, 1.0 / 64, None, need, None, ctypes.byref(chosen), None, None) == WORKSPACE
+
+
+def test_binding_checks_shapes_before_calling():
+    """The binding refuses tensors that do not match the call's sizes (the
+    library would access them past their ends); CPU tensors suffice, since
+    the checks run before anything reaches the library."""
+    import torch
+    T, hk, hv, d = 8, 2, 4, 16
+    q = torch.zeros((T, hk, d), dtype=torch.bfloat16)
+    ok = dict(k=torch.zeros((T, hk, d), dtype=torch.bfloat16), v=torch.zeros((T, hv, d), dtype=torch.bfloat16),
+              g=torch.zeros((T, hv)), beta=torch.zeros((T, hv)))
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    bad = [dict(v=torch.zeros((T - 1, hv, d), dtype=torch.bfloat16)),
+           dict(k=torch.zeros((T, hk, d), dtype=torch.float32)),
+           dict(beta=torch.zeros((T, hv + 1))),
+           dict(beta=torch.zeros((T, hv), dtype=torch.bfloat16))]
+    for b in bad:
+        a = {**ok, **b}
+        with pytest.raises((ValueError, TypeError)):
+            gdn.prefill(q, a["k"], a["v"], a["g"], a["beta"], cu)
+    with pytest.raises(ValueError):
+        gdn.prefill(q, ok["k"], ok["v"], ok["g"], ok["beta"], cu,
+                    initial_state=torch.zeros((2, hv, d, d)))
+    with pytest.raises(ValueError):
+        gdn.decode_step(q, ok["k"], ok["v"][:4], ok["g"], ok["beta"], torch.zeros((T, hv, d, d)))
