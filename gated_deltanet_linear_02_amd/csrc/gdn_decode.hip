@@ -415,14 +415,22 @@ template <> struct Vec8<float> {
 // A workgroup covers ROWS rows of one (sequence, value head) state; a row's
 // DK elements are spread over LPR = DK / 8 consecutive lanes, 8 consecutive
 // elements each, so that a lane's part of k or q is one 16-byte load (bf16).
-template <int DK, int DV> struct TokenScanShape {
+// Rows: each group of LPR lanes holds NRL rows, RPP rows apart. With two,
+// a lane converts its k and q pieces and forms k.q once for both rows, which
+// cuts the VALU work per row and token by about a third; it halves the
+// workgroups, so it pays when there are many (batches of sequences) and not
+// for one sequence, where the per-token latency of one workgroup is the
+// time (launch_token_scan chooses).
+template <int DK, int DV, int NRL_> struct TokenScanShape {
     static constexpr int LPR = DK / 8;
-    static constexpr int ROWS = 256 / LPR;
-    static constexpr int RPW = 64 / LPR;  // rows per wave
+    static constexpr int RPP = 256 / LPR;  // rows per pass of the workgroup
+    static constexpr int NRL = RPP * NRL_ > DV ? (DV + RPP - 1) / RPP : NRL_;  // rows per lane group
+    static constexpr int ROWS = RPP * NRL;  // rows per workgroup
+    static constexpr int RPW = 64 / LPR;    // rows per wave and pass
     static constexpr int SLICES = (DV + ROWS - 1) / ROWS;
 };
 
-template <typename E, typename G, typename SE, int DK, int DV>
+template <typename E, typename G, typename SE, int DK, int DV, int NRL_>
 __global__ __launch_bounds__(256) void gdn_token_scan_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const G *__restrict__ gate_g, const G *__restrict__ gate_b,
@@ -430,8 +438,9 @@ __global__ __launch_bounds__(256) void gdn_token_scan_kernel(
     const SE *__restrict__ s0, SE *__restrict__ sfin, E *__restrict__ out,
     int32_t hk, int32_t hv, float scale)
 {
-    typedef TokenScanShape<DK, DV> SH;
-    constexpr int LPR = SH::LPR, ROWS = SH::ROWS, RPW = SH::RPW, SLICES = SH::SLICES;
+    typedef TokenScanShape<DK, DV, NRL_> SH;
+    constexpr int LPR = SH::LPR, RPP = SH::RPP, NRL = SH::NRL, ROWS = SH::ROWS, RPW = SH::RPW,
+                  SLICES = SH::SLICES;
     constexpr int kNext = 3;  // tokens whose k and q are in flight ahead of the one applied
 
     const int bhs = blockIdx.x;
@@ -442,17 +451,20 @@ __global__ __launch_bounds__(256) void gdn_token_scan_kernel(
     const int kh = h / (hv / hk);
     const int tid = threadIdx.x, lane = tid & 63;
     const int lr = tid % LPR;
-    const int row = row0 + tid / LPR;
-    const int wrow0 = row0 + (tid >> 6) * RPW;  // first row of this wave
-    const bool live = row < DV;
+    const int r1 = row0 + tid / LPR;            // this lane group's rows: r1 + p RPP, p < NRL
+    const int wrow0 = row0 + (tid >> 6) * RPW;  // first row of this wave in pass 0
 
     // The state rows first: they do not depend on the sequence's bounds, so
     // their latency overlaps that of cu_seqlens.
-    const size_t state0 = ((size_t)n * hv + h) * (size_t)(DV * DK) + (size_t)row * DK + 8 * lr;
-    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    if (s0 && live) {
-        s[0] = load4f<SE>(s0 + state0);
-        s[1] = load4f<SE>(s0 + state0 + 4);
+    const size_t sbase = ((size_t)n * hv + h) * (size_t)(DV * DK) + 8 * lr;
+    f32x4 s[NRL][2];
+#pragma unroll
+    for (int p = 0; p < NRL; ++p) {
+        s[p][0] = s[p][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (s0 && r1 + p * RPP < DV) {
+            s[p][0] = load4f<SE>(s0 + sbase + (size_t)(r1 + p * RPP) * DK);
+            s[p][1] = load4f<SE>(s0 + sbase + (size_t)(r1 + p * RPP) * DK + 4);
+        }
     }
 
     // Sequence n's tokens [lo, hi): offsets clamped into [0, T] and made
@@ -476,19 +488,22 @@ __global__ __launch_bounds__(256) void gdn_token_scan_kernel(
     lo = __builtin_amdgcn_readfirstlane(lo);
 
     // Per block of 64 tokens, lane l loads token tb + l's gates and, for each
-    // of the wave's RPW rows, its v; a token's values are then read with
-    // readlane. Loads are unconditional (tokens clamped into [lo, hi)) so that
-    // the compiler counts outstanding loads exactly.
+    // of the wave's RPW rows of every pass, its v; a token's values are then
+    // read with readlane. Loads are unconditional (tokens clamped into
+    // [lo, hi)) so that the compiler counts outstanding loads exactly.
     struct Block {
         G g, b;
-        E vr[RPW];
+        E vr[NRL][RPW];
     };
     auto load_block = [&](Block &bl, int tb) {
         const int t = min(tb + lane, hi - 1);
         bl.g = gate_g[(size_t)t * hv + h];
         bl.b = gate_b[(size_t)t * hv + h];
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) bl.vr[r] = v[((size_t)t * hv + h) * DV + min(wrow0 + r, DV - 1)];
+        for (int p = 0; p < NRL; ++p)
+#pragma unroll
+            for (int r = 0; r < RPW; ++r)
+                bl.vr[p][r] = v[((size_t)t * hv + h) * DV + min(wrow0 + p * RPP + r, DV - 1)];
     };
     auto lane_f = [](float x, int i) {
         return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), i));
@@ -503,27 +518,34 @@ __global__ __launch_bounds__(256) void gdn_token_scan_kernel(
         x.k.load(k + tk);
         x.q.load(q + tk);
     };
-    auto apply = [&](const KQ &x, float a, float beta, float vv, int t) {
+    // One token: k, q converted and k.q formed once for the lane's rows.
+    auto apply = [&](const KQ &x, float a, float beta, const float (&vv)[NRL], int t) {
         float kk[8], qq[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             kk[e] = x.k[e];
             qq[e] = x.q[e];
         }
-        float kq = 0.f, sk = 0.f, sq = 0.f;
+        float kq = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            kq += kk[e] * qq[e];
-            sk += s[e >> 2][e & 3] * kk[e];
-            sq += s[e >> 2][e & 3] * qq[e];
-        }
+        for (int e = 0; e < 8; ++e) kq += kk[e] * qq[e];
         kq = row_sum<LPR>(kq);
-        sk = row_sum<LPR>(sk);
-        sq = row_sum<LPR>(sq);
-        const float u = beta * (vv - a * sk);
-        if (live && lr == 0) out[((size_t)t * hv + h) * DV + row] = from_f32<E>(scale * (a * sq + kq * u));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s[e >> 2][e & 3] = a * s[e >> 2][e & 3] + u * kk[e];
+        for (int p = 0; p < NRL; ++p) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sk += s[p][e >> 2][e & 3] * kk[e];
+                sq += s[p][e >> 2][e & 3] * qq[e];
+            }
+            sk = row_sum<LPR>(sk);
+            sq = row_sum<LPR>(sq);
+            const float u = beta * (vv[p] - a * sk);
+            const int row = r1 + p * RPP;
+            if (row < DV && lr == 0) out[((size_t)t * hv + h) * DV + row] = from_f32<E>(scale * (a * sq + kq * u));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[p][e >> 2][e & 3] = a * s[p][e >> 2][e & 3] + u * kk[e];
+        }
     };
 
     // Sequences of up to kShort tokens (multi-token steps): each token's
@@ -534,14 +556,16 @@ __global__ __launch_bounds__(256) void gdn_token_scan_kernel(
     auto short_run = [&](auto lc) {
         constexpr int L = decltype(lc)::value;
         KQ in[L];
-        float ga[L], gb[L], gv[L];
+        float ga[L], gb[L], gv[L][NRL];
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             const int t = lo + i;
             load_kq(in[i], t);
             ga[i] = static_cast<float>(gate_g[(size_t)t * hv + h]);
             gb[i] = static_cast<float>(gate_b[(size_t)t * hv + h]);
-            gv[i] = static_cast<float>(v[((size_t)t * hv + h) * DV + min(row, DV - 1)]);
+#pragma unroll
+            for (int p = 0; p < NRL; ++p)
+                gv[i][p] = static_cast<float>(v[((size_t)t * hv + h) * DV + min(r1 + p * RPP, DV - 1)]);
         }
 #pragma unroll
         for (int i = 0; i < L; ++i) apply(in[i], expf(ga[i]), gb[i], gv[i], lo + i);
@@ -567,11 +591,13 @@ __global__ __launch_bounds__(256) void gdn_token_scan_kernel(
         for (int tb = lo; tb < hi; tb += 64) {
             load_block(nxt, min(tb + 64, hi - 1));
             // this block's gates and v as floats, per lane
-            float ga = 0.f, gb = 0.f, gv[RPW];
+            float ga = 0.f, gb = 0.f, gv[NRL][RPW];
             ga = expf(static_cast<float>(cur.g));
             gb = static_cast<float>(cur.b);
 #pragma unroll
-            for (int r = 0; r < RPW; ++r) gv[r] = static_cast<float>(cur.vr[r]);
+            for (int p = 0; p < NRL; ++p)
+#pragma unroll
+                for (int r = 0; r < RPW; ++r) gv[p][r] = static_cast<float>(cur.vr[p][r]);
             // 64 tokens (16 groups of R = 4), stage u % R holding token t + u
             for (int t = tb; t < min(tb + 64, hi); t += R) {
 #pragma unroll
@@ -579,11 +605,15 @@ __global__ __launch_bounds__(256) void gdn_token_scan_kernel(
                     load_kq(in[(u + kNext) % R], min(t + u + kNext, hi - 1));
                     if (t + u < hi) {
                         const int i = t + u - tb;
-                        float vv = lane_f(gv[0], i);
+                        float vv[NRL];
 #pragma unroll
-                        for (int r = 1; r < RPW; ++r) {
-                            const float vr = lane_f(gv[r], i);
-                            vv = myr == r ? vr : vv;
+                        for (int p = 0; p < NRL; ++p) {
+                            vv[p] = lane_f(gv[p][0], i);
+#pragma unroll
+                            for (int r = 1; r < RPW; ++r) {
+                                const float vr = lane_f(gv[p][r], i);
+                                vv[p] = myr == r ? vr : vv[p];
+                            }
                         }
                         apply(in[u], lane_f(ga, i), lane_f(gb, i), vv, t + u);
                     }
@@ -593,19 +623,37 @@ __global__ __launch_bounds__(256) void gdn_token_scan_kernel(
         }
     }
 
-    if (sfin && live) {
-        store4<SE>(sfin + state0, s[0]);
-        store4<SE>(sfin + state0 + 4, s[1]);
+    if (sfin) {
+#pragma unroll
+        for (int p = 0; p < NRL; ++p) {
+            if (r1 + p * RPP < DV) {
+                store4<SE>(sfin + sbase + (size_t)(r1 + p * RPP) * DK, s[p][0]);
+                store4<SE>(sfin + sbase + (size_t)(r1 + p * RPP) * DK + 4, s[p][1]);
+            }
+        }
     }
+}
+
+// Rows per lane group of the token scan: two when the call has at least
+// kTokenScanPairedWgs workgroups with one (about two per CU), else one.
+constexpr int64_t kTokenScanPairedWgs = 1024;
+
+template <typename E, typename G, typename SE, int D, int NRL>
+static hipError_t launch_token_scan_n(const PrefillArgs &A, hipStream_t st) {
+    const dim3 grid((unsigned)A.num_seqs * (unsigned)A.hv * (unsigned)TokenScanShape<D, D, NRL>::SLICES), block(256);
+    return launch_kernel(kTokenScan, gdn_token_scan_kernel<E, G, SE, D, D, NRL>, grid, block, 0, st,
+                         (const E *)A.q, (const E *)A.k, (const E *)A.v, (const G *)A.g, (const G *)A.beta,
+                         A.cu, A.num_seqs, (int32_t)A.total_tokens, (const SE *)A.s0, (SE *)A.s_final,
+                         (E *)A.out, A.hk, A.hv, A.scale);
 }
 
 template <typename E, typename G, typename SE, int D>
 static hipError_t launch_token_scan_t(const PrefillArgs &A, hipStream_t st) {
-    const dim3 grid((unsigned)A.num_seqs * (unsigned)A.hv * (unsigned)TokenScanShape<D, D>::SLICES), block(256);
-    return launch_kernel(kTokenScan, gdn_token_scan_kernel<E, G, SE, D, D>, grid, block, 0, st,
-                         (const E *)A.q, (const E *)A.k, (const E *)A.v, (const G *)A.g, (const G *)A.beta,
-                         A.cu, A.num_seqs, (int32_t)A.total_tokens, (const SE *)A.s0, (SE *)A.s_final,
-                         (E *)A.out, A.hk, A.hv, A.scale);
+    if constexpr (TokenScanShape<D, D, 2>::NRL == 2) {
+        const int64_t wgs = (int64_t)A.num_seqs * A.hv * TokenScanShape<D, D, 1>::SLICES;
+        if (wgs >= kTokenScanPairedWgs) return launch_token_scan_n<E, G, SE, D, 2>(A, st);
+    }
+    return launch_token_scan_n<E, G, SE, D, 1>(A, st);
 }
 
 template <typename E, typename G, typename SE>

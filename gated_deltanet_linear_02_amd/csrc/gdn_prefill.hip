@@ -238,7 +238,6 @@ template <typename G> __device__ __forceinline__ float gate_load(const G *p, siz
 // 2^x on the hardware instruction (arguments here are <= 0 for decaying
 // gates; results below the fp32 range flush to 0).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr double kLog2eD = 1.4426950408889634;
 
 // acc += X[xr.., xc..] (16x16) * Y[yr.., yc..] (16x16), fp32 LDS operands

@@ -150,3 +150,18 @@ def test_chunk_zero_picks_by_length(lens, expect):
     assert ("token_scan" in ran) != ("scan" in ran), ran
     o_ref, f_ref = oracle_ref(inp)
     assert rel_err(to_f64(o), o_ref) <= tol("bf16") and rel_err(to_f64(f), f_ref) <= tol("bf16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_token_scan_paired_rows_on_batches(d, io):
+    """64 sequences x 32 value heads is enough workgroups for the kernel to
+    hold two state rows per lane group: ragged lengths (empty, 1-4 tokens on
+    the direct path, 5-70 through the block ring), initial states, every
+    head compared."""
+    rng = np.random.default_rng(90 + d)
+    lens = [int(x) for x in rng.choice([0, 1, 2, 3, 4, 5, 9, 17, 64, 70], size=64)]
+    inp = gs.make_inputs(lens, 16, 32, d, d, seed=91 + d, io_dtype=io, gate_dtype=io, init_state=True)
+    note(f"token scan paired rows d={d} io={io}")
+    o, f = run_prefill(inp, chunk=1, scale=0.5)
+    _check(inp, o, f, scale=0.5, label=f"paired d={d}")
