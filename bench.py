@@ -375,7 +375,7 @@ def short_prefill_sweep(dev, copies, steps):
         state_bytes = N * HV * D * D * 4 * 2
         io_bytes = T * (2 * HK * D + 2 * HV * D) * 2 + T * HV * 2 * 2
         gbs = (state_bytes + io_bytes) / (res["kernel"] * 1e-3) / 1e9
-        auto = "token_scan" if (T <= 64 or T <= 16 * N) else "chunked"
+        auto = {1: "token_scan"}.get(gdn.prefill_method(N, T, HK, HV, D), "chunked")
         print(json.dumps({
             "mode": "short-prefill", "num_seqs": N, "tokens_per_seq": k, "total_tokens": T,
             "token_scan_ms": res[1], "chunked_ms": res[CHUNK], "chunk0_picks": auto,
@@ -1012,7 +1012,7 @@ def tuning_sweep(dev, copies, steps):
         # the two counts), so that warm-up order favours neither
         gdn.tune_cache_clear()
         rule_ms = timed()
-        rule = 1 if (T <= 64 or T <= 16 * N) else 64
+        rule = gdn.prefill_method(N, T, HK, HV, D)
         d0 = sets[0]
         r = gdn.tune_prefill(d0["q"], d0["k"], d0["v"], d0["g"], d0["beta"], d0["cu_seqlens"], initial_state=d0["s0"])
         tuned_ms = timed()

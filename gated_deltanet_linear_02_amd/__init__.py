@@ -29,7 +29,7 @@ from typing import Dict, Optional, Tuple
 import torch
 
 __all__ = [
-    "GdnError", "lib_path", "load", "prefill", "decode_step", "prefill_workspace_size",
+    "GdnError", "lib_path", "load", "prefill", "decode_step", "prefill_workspace_size", "prefill_method",
     "tune_prefill", "tune_cache_clear", "tune_cache_size", "tune_cache_save", "tune_cache_load",
     "timing_start", "timing_stop", "abi_version", "KERNEL_KINDS",
 ]
@@ -77,6 +77,8 @@ def load():
         L.gdn_status_string.argtypes = [i32]
         L.gdn_prefill_workspace_size.restype = sz
         L.gdn_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32]
+        L.gdn_prefill_method.restype = i32
+        L.gdn_prefill_method.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32, i32]
         L.gdn_prefill.restype = i32
         L.gdn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
                                   f32, i32, i32, vp, vp, vp, vp, sz, vp]
@@ -174,6 +176,14 @@ def prefill_workspace_size(num_seqs: int, total_tokens: int, hk: int, hv: int, d
                                                  _dtype_code(io_dtype)))
 
 
+def prefill_method(num_seqs: int, total_tokens: int, hk: int, hv: int, d: int, chunk: int = 0,
+                   io_dtype: torch.dtype = torch.bfloat16, gate_dtype: torch.dtype = torch.float32) -> int:
+    """The method ``prefill`` uses for these sizes (``gdn_prefill_method``):
+    1 (token by token), 16, 32 or 64; 0 if the sizes are rejected."""
+    return int(load().gdn_prefill_method(num_seqs, total_tokens, hk, hv, d, d, chunk, _dtype_code(io_dtype),
+                                         _dtype_code(gate_dtype)))
+
+
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
             cu_seqlens: torch.Tensor, *, chunk: int = 0, scale: float = 1.0,
             initial_state: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
@@ -186,8 +196,9 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     q, k [T, hk, dk]; v [T, hv, dv] (bf16 or fp32, one dtype); g, beta [T, hv]
     (bf16 or fp32); cu_seqlens int32 [N + 1] on the device; states fp32
     [N, hv, dv, dk]. ``final_state`` may be ``initial_state`` (in place).
-    ``chunk``: 16, 32 or 64 (chunked), 1 (token by token) or 0 (token by
-    token when T <= max(64, 16 N), else chunks of 64).
+    ``chunk``: 16, 32 or 64 (chunked), 1 (token by token) or 0 (the tuned
+    choice for the shape, else a rule by mean sequence length; see
+    ``prefill_method``).
     ``norm_weight`` (fp32 [dv], or None): RMS-normalise every output row,
     y = o * w / sqrt(mean(o^2) + norm_eps).
     States are fp32 or bf16 (``gdn_prefill_ex``): the dtype of the state

@@ -48,10 +48,6 @@ TimingEvents timing_claim(KernelKind kind) {
 static bool valid_head(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 static bool valid_chunk(int32_t c) { return c == 0 || c == 1 || c == 16 || c == 32 || c == 64; }
 
-// The method chunk 0 takes without a tuned choice: 1 (token by token) or 64.
-static int32_t rule_chunk(int32_t num_seqs, int64_t total_tokens) {
-    return prefer_token_scan(num_seqs, total_tokens) ? 1 : 64;
-}
 static bool valid_dtype(int32_t t) { return t == GDN_BF16 || t == GDN_F32; }
 static size_t dtype_bytes(int32_t t) { return t == GDN_BF16 ? 2 : 4; }
 
@@ -112,7 +108,7 @@ static int32_t check_prefill_shape(int32_t num_seqs, int64_t total_tokens, int32
     if (!valid_head(dk) || dv != dk || !valid_chunk(chunk) || !valid_dtype(io_dtype) ||
         !valid_dtype(gate_dtype) || hk > 65535)
         return GDN_ERR_UNSUPPORTED;
-    const int32_t c = chunk != 0 ? chunk : rule_chunk(num_seqs, total_tokens);
+    const int32_t c = chunk != 0 ? chunk : rule_chunk(num_seqs, total_tokens, hv, dv);
     return method_fits(c, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype) ? GDN_OK : GDN_ERR_UNSUPPORTED;
 }
 
@@ -123,7 +119,7 @@ static int32_t method_for(int32_t chunk, int32_t num_seqs, int64_t total_tokens,
     if (chunk != 0) return chunk;
     const int32_t t = tuned_chunk(num_seqs, total_tokens, hk, hv, dk, io_dtype, gate_dtype);
     if (t != 0 && method_fits(t, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype)) return t;
-    return rule_chunk(num_seqs, total_tokens);
+    return rule_chunk(num_seqs, total_tokens, hv, dv);
 }
 
 // Workspace bytes for chunk c (the token scan needs none; 256 are reported so
@@ -144,6 +140,13 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_
     if (check_prefill_shape(num_seqs, total_tokens, hk, hv, dk, dv, chunk, io_dtype, GDN_F32) != GDN_OK)
         return 0;
     return prefill_workspace_bytes(num_seqs, total_tokens, hk, hv, dk, chunk, io_dtype);
+}
+
+int32_t gdn_prefill_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv, int32_t dk,
+                           int32_t dv, int32_t chunk, int32_t io_dtype, int32_t gate_dtype) {
+    if (check_prefill_shape(num_seqs, total_tokens, hk, hv, dk, dv, chunk, io_dtype, gate_dtype) != GDN_OK)
+        return 0;
+    return method_for(chunk, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype, gate_dtype);
 }
 
 // eps of the output normalisation: finite and not negative.

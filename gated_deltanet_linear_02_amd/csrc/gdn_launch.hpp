@@ -134,17 +134,31 @@ hipError_t launch_norm_apply(const NormArgs &a, hipStream_t st);
 int32_t tuned_chunk(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv, int32_t d, int32_t io,
                     int32_t gate);
 
-// gdn_prefill with chunk 0 (when nothing is tuned) evaluates token by token when
-// total_tokens <= max(kTokenScanTokens, kTokenScanPerSeq * num_seqs), else in
-// chunks of 64. Measured at HK=16, HV=32, d=128: one sequence breaks even at
-// about 56 tokens, while 64 sequences of 1 to 8 tokens run 2.3 to 4 times
-// faster token by token (the chunked path's fixed cost per sequence
-// dominates). The host does not know the lengths; even one sequence holding
-// all 16 N tokens stays within the chunked path's time.
-constexpr int64_t kTokenScanTokens = 64;
-constexpr int64_t kTokenScanPerSeq = 16;
-inline bool prefer_token_scan(int64_t num_seqs, int64_t total_tokens) {
-    return total_tokens <= kTokenScanTokens || total_tokens <= kTokenScanPerSeq * num_seqs;
+// gdn_prefill with chunk 0, when nothing is tuned for the shape, picks the
+// method from host-known sizes alone (the lengths stay on the device), by
+// the mean sequence length L = T / N. Measured at HK = 16, HV = 32, d = 128:
+//   token by token   T <= 32, or L <= 24: the chunked path's fixed costs
+//                    dominate (one 16-token prompt: 8.5 vs 12.8 us; 64
+//                    sequences of 24 tokens: 226 vs 283 us at best chunked);
+//   chunks of 16     L <= 48: the fewest padded rows (64 x 32: 287 vs 336 us
+//                    with 64);
+//   chunks of 32     the scan's workgroups fit the GPU in one pass (at most
+//                    one per CU) and L <= 1024: a lone sequence is bound by
+//                    its chain's latency, which shorter chunks cut (1 x 512:
+//                    29.8 vs 32.5 us);
+//   chunks of 64     otherwise: with several passes over the GPU the total
+//                    work counts, which the largest chunks minimise (8 x 300:
+//                    87 vs 101 us with 32).
+constexpr int64_t kTokenScanTokens = 32;
+constexpr int64_t kTokenScanPerSeq = 24;
+constexpr int64_t kChunk16PerSeq = 48;
+constexpr int64_t kChunk32PerSeq = 1024;
+constexpr int64_t kScanOnePassWgs = 256;  // gfx950 (MI355X): 256 CUs
+inline int32_t rule_chunk(int64_t num_seqs, int64_t total_tokens, int64_t hv, int64_t dv) {
+    if (total_tokens <= kTokenScanTokens || total_tokens <= kTokenScanPerSeq * num_seqs) return 1;
+    if (total_tokens <= kChunk16PerSeq * num_seqs) return 16;
+    if (num_seqs * hv * (dv / 16) <= kScanOnePassWgs && total_tokens <= kChunk32PerSeq * num_seqs) return 32;
+    return 64;
 }
 
 }  // namespace gdn

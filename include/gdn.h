@@ -87,6 +87,15 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
                                   int32_t chunk, int32_t io_dtype);
 
 /*
+ * The method gdn_prefill uses for these sizes and this chunk argument: 1
+ * (token by token), 16, 32 or 64; for chunk 0, the cached tuned choice or the
+ * rule above. Returns 0 for arguments gdn_prefill would reject.
+ */
+int32_t gdn_prefill_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
+                           int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype,
+                           int32_t gate_dtype);
+
+/*
  * Chunked prefill over N packed variable-length sequences.
  *
  * cu_seqlens   int32 [N + 1] DEVICE array of token offsets: sequence n owns
@@ -102,9 +111,11 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
  *              in registers (one kernel, no workspace), which is faster for
  *              short prompts and multi-token steps. 0: the method that
  *              gdn_tune_prefill cached for this device and shape bucket if
- *              there is one, else 1 when total_tokens <= max(64, 16 *
- *              num_seqs), else 64. The result does not depend on it beyond
- *              rounding.
+ *              there is one, else by the mean sequence length L = T / N:
+ *              1 when T <= 32 or L <= 24, 16 when L <= 48, 32 when the
+ *              chunked scan's N * hv * dv / 16 workgroups fit the GPU's 256
+ *              CUs and L <= 1024, else 64 (gdn_prefill_method tells which).
+ *              The result does not depend on it beyond rounding.
  * dk, dv       16, 32, 64 or 128 each.
  * scale        multiplies every output (1.0 for the plain rule).
  * initial_state  fp32 [N][hv][dv][dk], or NULL for zero states.

@@ -70,10 +70,10 @@ def test_workspace_size(lib):
     assert _ws(c=48) == 0
     assert _ws(n=0) == 0
     # token by token (chunk 1) needs no workspace; a nonzero size still means
-    # "accepted". Chunk 0 picks it when T <= max(64, 16 N), chunks of 64 above.
+    # "accepted".
     assert _ws(c=1) == 256 and _ws(c=1, T=1 << 20) == 256
     # chunk 0 may take a tuned choice, so it covers every chunked method
-    for n, T in ((1, 64), (64, 1024), (1, 65), (1, 4096)):
+    for n, T in ((1, 64), (64, 1024), (1, 65), (1, 4096), (8, 2400)):
         assert _ws(c=0, n=n, T=T) == max(_ws(c=c, n=n, T=T) for c in (16, 32, 64)) > 256
     assert _ws(c=2) == 0 and _ws(c=-1) == 0
 
@@ -277,6 +277,21 @@ def test_tune_argument_checks(lib):
     assert lib.gdn_tune_prefill(*args, 1.0 / 64, FAKE + (6 << 30), need - 1, None, ctypes.byref(chosen), None,
                                 None) == WORKSPACE
     assert lib.gdn_tune_prefill(*args, 1.0 / 64, None, need, None, ctypes.byref(chosen), None, None) == WORKSPACE
+
+
+def test_chunk_zero_rule(lib):
+    """The method chunk 0 takes with nothing tuned, by mean sequence length
+    (HK=16, HV=32, d=128; the scan fills the GPU in one pass up to 1 sequence)."""
+    gdn.tune_cache_clear()
+    m = lambda n, T: gdn.prefill_method(n, T, 16, 32, 128)
+    assert m(1, 16) == 1 and m(1, 32) == 1          # one short prompt
+    assert m(64, 64 * 24) == 1 and m(8, 8 * 4) == 1  # batches, mean <= 24
+    assert m(1, 48) == 16 and m(64, 64 * 32) == 16   # mean <= 48
+    assert m(1, 128) == 32 and m(1, 1024) == 32      # one sequence: one pass
+    assert m(1, 4096) == 64 and m(8, 8 * 300) == 64  # long, or several passes
+    assert m(2, 2 * 600) == 64                       # two sequences: two passes
+    assert gdn.prefill_method(1, 4096, 16, 32, 128, chunk=16) == 16  # explicit chunks as given
+    assert gdn.prefill_method(1, 4096, 3, 32, 128) == 0              # rejected shape
 
 
 def test_binding_checks_shapes_before_calling():

@@ -134,10 +134,12 @@ def test_token_scan_malformed_cu_seqlens_is_clamped():
     assert rel_err(to_f64(f1), to_f64(f16)) <= TOL_F32
 
 
-@pytest.mark.parametrize("lens,expect", [([48], "token_scan"), ([100], "scan"),
-                                         ([12] * 16, "token_scan"), ([17] * 16, "scan")])
+@pytest.mark.parametrize("lens,expect", [([30], "token_scan"), ([48], "scan"), ([100], "scan"),
+                                         ([12] * 16, "token_scan"), ([30] * 16, "scan")])
 def test_chunk_zero_picks_by_length(lens, expect):
-    """chunk 0: token by token when T <= max(64, 16 N), chunks of 64 above."""
+    """chunk 0 with nothing tuned: token by token when T <= 32 or the mean
+    length is at most 24 tokens, chunked above (the method the library
+    reports for the sizes is the one that runs)."""
     inp = gs.make_inputs(lens, 2, 4, 32, 32, seed=65, io_dtype="bf16", gate_dtype="f32")
     d = device_inputs(inp)
     note(f"chunk 0 with lengths {lens}")
@@ -148,6 +150,8 @@ def test_chunk_zero_picks_by_length(lens, expect):
     ran = {k for k, v in kt.items() if v.get("count", 0)}
     assert expect in ran, ran
     assert ("token_scan" in ran) != ("scan" in ran), ran
+    m = gdn.prefill_method(len(lens), sum(lens), 2, 4, 32)
+    assert (m == 1) == (expect == "token_scan"), m
     o_ref, f_ref = oracle_ref(inp)
     assert rel_err(to_f64(o), o_ref) <= tol("bf16") and rel_err(to_f64(f), f_ref) <= tol("bf16")
 

@@ -82,7 +82,7 @@ def test_tune_gate_rejects_what_differs():
 def test_tune_cache_file_steers_chunk_zero(tmp_path):
     """A saved choice, edited to another method and loaded back, is what
     chunk 0 runs for that shape bucket (and only for it)."""
-    _, d = _inputs([40, 20], seed=gs.SEED_BASE + 720)
+    _, d = _inputs([20, 10], seed=gs.SEED_BASE + 720)
     note("tune prefill, save, edit, load")
     r = gdn.tune_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
                          initial_state=d["initial_state"])
@@ -94,7 +94,7 @@ def test_tune_cache_file_steers_chunk_zero(tmp_path):
     path.write_text(" ".join(fields[:-1] + [str(forced)]) + "\n")
     gdn.tune_cache_clear()
     _, _, ran = _run(d, 0)
-    assert ran == {"token_scan"}  # T = 60 <= max(64, 16 N): the rule without a choice
+    assert ran == {"token_scan"}  # T = 30 <= 32: the rule without a choice
     assert gdn.tune_cache_load(str(path)) == 1
     o0, f0, ran = _run(d, 0)
     oc, fc, _ = _run(d, forced)
