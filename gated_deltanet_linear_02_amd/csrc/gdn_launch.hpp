@@ -154,6 +154,12 @@ constexpr int64_t kTokenScanPerSeq = 24;
 constexpr int64_t kChunk16PerSeq = 48;
 constexpr int64_t kChunk32PerSeq = 1024;
 constexpr int64_t kScanOnePassWgs = 256;  // gfx950 (MI355X): 256 CUs
+// State rows per chunked-scan workgroup: 32 when 16-row slices would take
+// more than one pass over the CUs (bf16 I/O, d >= 32), else 16.
+inline int32_t scan_slice_rows(int64_t num_seqs, int64_t hv, int64_t dv, bool io_bf16) {
+    return io_bf16 && dv >= 32 && num_seqs * hv * (dv / 16) > kScanOnePassWgs ? 32 : 16;
+}
+
 inline int32_t rule_chunk(int64_t num_seqs, int64_t total_tokens, int64_t hv, int64_t dv) {
     if (total_tokens <= kTokenScanTokens || total_tokens <= kTokenScanPerSeq * num_seqs) return 1;
     if (total_tokens <= kChunk16PerSeq * num_seqs) return 16;

@@ -681,13 +681,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
 // use one stage). The chunk step is about as long as the CU takes to accept
 // its vector-memory instructions, so their number per chunk is kept small.
 
-constexpr int kSliceRows = 16;
 constexpr int kScanThreads = 512;
 
-template <typename E, int C, int DK>
+// R: value rows of the state per workgroup (16, or 32 on bf16 I/O).
+template <typename E, int C, int DK, int R>
 struct ScanSmem {
     static constexpr int PE = Pad<E>::value;
-    static constexpr int R = kSliceRows;
     static constexpr int LDK = DK + PE;  // rows of length DK
     static constexpr int LDC = C + PE;   // rows of length C
     // Rows in fragment-contiguous order (lds_pos: keys for MD, tokens for MC).
@@ -752,15 +751,19 @@ struct RStage {
     }
 };
 
+struct NoAux {};
+
 // An output wave's operands for one chunk (and that chunk's V rows, which
 // the wave stages one chunk earlier).
-template <typename E, int C, int DK, int NT>
+template <typename E, int C, int DK, int NT, int R>
 struct OStage {
     typedef ScanShape<E, C, DK> S;
     typename S::MD::Frag qf[S::KBD];
     typename S::MC::Frag pf[NT];  // P: the NT blocks read (tri_read_blocks)
     typename S::E4 vr;  // fp32: V[16 q + l/4][4 (l%4) ..]
     f32x4 aux = {0.f, 0.f, 0.f, 0.f};  // auxiliary load (see the output role of the scan)
+    // 32-row slices: the V rows 16 q .. 16 q + 15 of the slice (8 values per lane)
+    typename std::conditional<(R > 16), f32x4, NoAux>::type vaux;
 
     __device__ __forceinline__ void load(const E *__restrict__ v, const E *__restrict__ pmat,
                                          const E *__restrict__ qmat, const ChunkRef &r, int hv, int h,
@@ -811,7 +814,7 @@ __device__ __forceinline__ void keep_alive(float x) { asm volatile("" ::"v"(x));
 // Chunks ahead of the scan at which its operands are pulled into L2.
 constexpr int kTouchAhead = 8;
 
-template <typename E, int C, int DK, typename SE>
+template <typename E, int C, int DK, typename SE, int R>
 __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdn_scan_kernel(
     const E *__restrict__ v,
     const int32_t *__restrict__ bounds, const int32_t *__restrict__ seq_chunk0,
@@ -822,20 +825,21 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
     const SE *__restrict__ s0, SE *__restrict__ sfin, E *__restrict__ out,
     int32_t num_seqs, int32_t hk, int32_t hv)
 {
-    typedef ScanSmem<E, C, DK> L;
+    static_assert(R == 16 || (R == 32 && IsBf16<E>::value && DK >= 32), "32-row slices: bf16, d >= 32");
+    typedef ScanSmem<E, C, DK, R> L;
     typedef ScanShape<E, C, DK> SH;
     typedef typename SH::MD MD;
     typedef typename SH::MC MC;
     typedef typename SH::E4 E4;
-    constexpr int R = kSliceRows;
     constexpr int DV = DK;
     constexpr int NS = DV / R;  // value-row slices per head
+    constexpr int RW = R / 16;  // 16-row tiles per slice
     constexpr int LDK = L::LDK, LDC = L::LDC;
     constexpr int RT = SH::RT, MT = SH::MT, NMW = SH::NMW;
     constexpr int KBD = SH::KBD, KBC = SH::KBC;
     // Register stages per role (bf16); fp32 fragments are 4x larger and use one.
     constexpr bool kPipelined = IsBf16<E>::value;
-    constexpr int kRStages = 4, kOStages = 5;
+    constexpr int kRStages = R == 16 ? 4 : 3, kOStages = R == 16 ? 5 : 4;
 
     extern __shared__ __align__(16) char smem[];
     E *sS = reinterpret_cast<E *>(smem + L::off_S);
@@ -899,16 +903,19 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
     if (recurrence) by_tile([&](auto ntc) {
         constexpr int NT = decltype(ntc)::value;
         typedef RStage<E, C, DK, NT> RS;
-        // fp32 master copy of this wave's S^T tiles (key tiles q + 4 j);
-        // operand copy (S[value][key]) in LDS.
-        f32x4 sacc[NMW];
+        // fp32 master copy of this wave's S^T tiles (key tiles q + 4 j, row
+        // tiles rr); operand copy (S[value][key]) in LDS.
+        f32x4 sacc[NMW][RW];
 #pragma unroll
         for (int j = 0; j < NMW; ++j) {
             const int mt = q + 4 * j;
-            sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (mt < MT) {
-                if (s0) sacc[j] = load4f<SE>(s0 + state0 + (size_t)(col0 + ln) * DK + 16 * mt + 4 * g4);
-                store_acc_p<MD>(sS, LDK, 16 * mt, 0, lane, sacc[j]);
+#pragma unroll
+            for (int rr = 0; rr < RW; ++rr) {
+                sacc[j][rr] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (mt < MT) {
+                    if (s0) sacc[j][rr] = load4f<SE>(s0 + state0 + (size_t)(col0 + 16 * rr + ln) * DK + 16 * mt + 4 * g4);
+                    store_acc_p<MD>(sS, LDK, 16 * mt, 16 * rr, lane, sacc[j][rr]);
+                }
             }
         }
         __syncthreads();  // S0 and chunk 0's V rows staged
@@ -920,27 +927,31 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             // MFMAs of different shapes, which must not be chained through
             // one accumulator; two key chains shorten the dependency.
             if (q < RT) {
-                typename MC::Frag vf[NT];
-                typename MD::Frag sf[KBD];
-#pragma unroll
-                for (int kb = 0; kb < NT; ++kb) vf[kb] = load_frag_p<MC>(sVt + (c & 1) * (R * LDC), LDC, 0, kb, lane);
-#pragma unroll
-                for (int kb = 0; kb < KBD; ++kb) sf[kb] = load_frag_p<MD>(sS, LDK, 0, kb, lane);
-                f32x4 ut = {0.f, 0.f, 0.f, 0.f}, uk0 = {0.f, 0.f, 0.f, 0.f}, uk1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < NT; ++kb) ut = MC::mma(st.tf[kb], vf[kb], ut);
-#pragma unroll
-                for (int kb = 0; kb < KBD; ++kb) {
-                    if (kb & 1) uk1 = MD::mma(st.wf[kb], sf[kb], uk1);
-                    else uk0 = MD::mma(st.wf[kb], sf[kb], uk0);
-                }
-                const f32x4 u = ut + uk0 + uk1;
                 const f32x4 dl = *reinterpret_cast<const f32x4 *>(sDl + (c & 1) * C + 16 * q + 4 * g4);
-                store_acc_p<MC>(sUt, LDC, 16 * q, 0, lane, u);
-                f32x4 du;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) du[i] = dl[i] * u[i];
-                store_acc_p<MC>(sDUt, LDC, 16 * q, 0, lane, du);
+                for (int rr = 0; rr < RW; ++rr) {
+                    typename MC::Frag vf[NT];
+                    typename MD::Frag sf[KBD];
+#pragma unroll
+                    for (int kb = 0; kb < NT; ++kb)
+                        vf[kb] = load_frag_p<MC>(sVt + (c & 1) * (R * LDC), LDC, 16 * rr, kb, lane);
+#pragma unroll
+                    for (int kb = 0; kb < KBD; ++kb) sf[kb] = load_frag_p<MD>(sS, LDK, 16 * rr, kb, lane);
+                    f32x4 ut = {0.f, 0.f, 0.f, 0.f}, uk0 = {0.f, 0.f, 0.f, 0.f}, uk1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < NT; ++kb) ut = MC::mma(st.tf[kb], vf[kb], ut);
+#pragma unroll
+                    for (int kb = 0; kb < KBD; ++kb) {
+                        if (kb & 1) uk1 = MD::mma(st.wf[kb], sf[kb], uk1);
+                        else uk0 = MD::mma(st.wf[kb], sf[kb], uk0);
+                    }
+                    const f32x4 u = ut + uk0 + uk1;
+                    store_acc_p<MC>(sUt, LDC, 16 * q, 16 * rr, lane, u);
+                    f32x4 du;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) du[i] = dl[i] * u[i];
+                    store_acc_p<MC>(sDUt, LDC, 16 * q, 16 * rr, lane, du);
+                }
             }
             __syncthreads();
             // ---- phase 2: S^T <- gamma_C S^T + K^T (diag(delta) U)
@@ -948,21 +959,24 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             // bounds the chunk through these waves, phase 2 through the output
             // waves, so a load queue that is full costs less here.
             if constexpr (kThree) fut.load(tbmat, wmat, ktmat, chunk(min(c + kRStages - 1, nch - 1)), q, lane);
-            typename MC::Frag duf[KBC];
-#pragma unroll
-            for (int kb = 0; kb < KBC; ++kb) duf[kb] = load_frag_p<MC>(sDUt, LDC, 0, kb, lane);
             const float gc = sGc[4 * (c & 1)];
 #pragma unroll
-            for (int j = 0; j < NMW; ++j) {
-                const int mt = q + 4 * j;
-                if (mt < MT) {
-                    f32x4 acc = sacc[j];
+            for (int rr = 0; rr < RW; ++rr) {
+                typename MC::Frag duf[KBC];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[i] *= gc;
+                for (int kb = 0; kb < KBC; ++kb) duf[kb] = load_frag_p<MC>(sDUt, LDC, 16 * rr, kb, lane);
 #pragma unroll
-                    for (int kb = 0; kb < KBC; ++kb) acc = MC::mma(st.ktf[j][kb], duf[kb], acc);
-                    sacc[j] = acc;
-                    store_acc_p<MD>(sS, LDK, 16 * mt, 0, lane, acc);
+                for (int j = 0; j < NMW; ++j) {
+                    const int mt = q + 4 * j;
+                    if (mt < MT) {
+                        f32x4 acc = sacc[j][rr];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[i] *= gc;
+#pragma unroll
+                        for (int kb = 0; kb < KBC; ++kb) acc = MC::mma(st.ktf[j][kb], duf[kb], acc);
+                        sacc[j][rr] = acc;
+                        store_acc_p<MD>(sS, LDK, 16 * mt, 16 * rr, lane, acc);
+                    }
                 }
             }
             __syncthreads();
@@ -987,13 +1001,16 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
             for (int j = 0; j < NMW; ++j) {
                 const int mt = q + 4 * j;
-                if (mt < MT) store4<SE>(sfin + state0 + (size_t)(col0 + ln) * DK + 16 * mt + 4 * g4, sacc[j]);
+#pragma unroll
+                for (int rr = 0; rr < RW; ++rr)
+                    if (mt < MT)
+                        store4<SE>(sfin + state0 + (size_t)(col0 + 16 * rr + ln) * DK + 16 * mt + 4 * g4, sacc[j][rr]);
             }
         }
     });
     else by_tile([&](auto ntc) {
         constexpr int NT = decltype(ntc)::value;
-        typedef OStage<E, C, DK, NT> OS;
+        typedef OStage<E, C, DK, NT, R> OS;
         // Besides its Q and P fragments, each output wave issues one auxiliary
         // 16-byte-per-lane load per chunk (bf16):
         //   wave 0     the chunk's gate record (delta and gamma_C for the
@@ -1006,8 +1023,10 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         //              lane, so that the workgroups' own loads later hit L2;
         //              the value is only kept alive until the stage is
         //              refilled;
-        //   waves 2-3  the chunk's V rows 32 (q - 2) .. + 31 (8 values per
-        //              lane), staged in LDS.
+        //   waves 2-3  16-row slices: the chunk's V rows 32 (q - 2) .. + 31
+        //              (8 values per lane), staged in LDS; 32-row slices:
+        //              another L2 touch, and every output wave loads the V
+        //              rows 16 q .. 16 q + 15 of its 32 columns besides.
         // Memory instructions, not bytes, bound the scan, so these small
         // loads are folded into as few instructions as possible. The fp32
         // path (one stage) loads V per wave and the gate record in every wave.
@@ -1025,7 +1044,10 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             const size_t ch0 = (size_t)(c0 + cc) * hv + (size_t)kh * group;
             const int per_head = 2 * kRunM + kRunQ;
             const int nlines = 8 * (2 * kRunQ + group * per_head);
-            const int line = (within * 64 + lane) % nlines;
+            // 32-row slices: half the workgroups per query/key head, touching
+            // from waves 1-3
+            const int part = R == 16 ? within : within * 3 + (q - 1);
+            const int line = (part * 64 + lane) % nlines;
             int r = line >> 3;
             const size_t off = (size_t)(line & 7) * (128 / sizeof(E));
             const E *run;
@@ -1047,7 +1069,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         auto aux_ptr = [&](int c_aux, int c_touch) {
             const ChunkRef r = chunk(c_aux);
             if (!kPipelined || q == 0) return gate_ptr(r);
-            if (q == 1) return kTouch ? touch_ptr(c_touch) : gate_ptr(r);
+            if (q == 1 || R > 16) return kTouch ? touch_ptr(c_touch) : gate_ptr(r);
             const int vrow = min(32 * (q - 2) + (lane >> 1), r.clen - 1);
             return reinterpret_cast<const f32x4 *>(v + ((size_t)(r.tok0 + vrow) * hv + h) * DK + col0 + 8 * (lane & 1));
         };
@@ -1055,6 +1077,11 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         auto load_aux = [&](OS &st, int c_aux, int c_touch) {
             keep_alive(st.aux[0]);  // wave 1: the touch issued when this stage was last filled
             st.aux = *aux_ptr(c_aux, c_touch);
+            if constexpr (R > 16) {
+                const ChunkRef r = chunk(c_aux);
+                const int vrow = min(16 * q + (lane >> 2), r.clen - 1);
+                st.vaux = *reinterpret_cast<const f32x4 *>(v + ((size_t)(r.tok0 + vrow) * hv + h) * DK + col0 + 8 * (lane & 3));
+            }
         };
         // A chunk's staged inputs into LDS buffer `buf`: the gate vectors
         // (wave 0) and, bf16, the V rows (waves 2, 3) from the auxiliary load;
@@ -1068,7 +1095,15 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                     sGc[4 * buf] = st.aux[0];
                 }
             }
-            if constexpr (kPipelined) {
+            if constexpr (R > 16) {
+                const int t = 16 * q + (lane >> 2);
+                if (t < C) {
+                    const bf16x8 x = __builtin_bit_cast(bf16x8, st.vaux);
+                    E *dst = sVt + buf * (R * LDC) + lds_pos<MC>(t);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) dst[(8 * (lane & 3) + i) * LDC] = x[i];
+                }
+            } else if constexpr (kPipelined) {
                 if (q >= 2) {
                     const int t = 32 * (q - 2) + (lane >> 1);
                     if (t < C) {
@@ -1116,10 +1151,15 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             if constexpr (kThree) put_chunk(nxt, nxt.vr, (c + 1) & 1);
             else put_chunk(gn, vn, (c + 1) & 1);
             // ---- phase 1: O1^T = S0 Q^T
-            f32x4 o1 = {0.f, 0.f, 0.f, 0.f};
-            if (q < RT) {
+            f32x4 o1[RW];
 #pragma unroll
-                for (int kb = 0; kb < KBD; ++kb) o1 = MD::mma(load_frag_p<MD>(sS, LDK, 0, kb, lane), st.qf[kb], o1);
+            for (int rr = 0; rr < RW; ++rr) {
+                o1[rr] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (q < RT) {
+#pragma unroll
+                    for (int kb = 0; kb < KBD; ++kb)
+                        o1[rr] = MD::mma(load_frag_p<MD>(sS, LDK, 16 * rr, kb, lane), st.qf[kb], o1[rr]);
+                }
             }
             __syncthreads();
             // ---- phase 2: O^T = O1^T diag(scale gamma) + U^T P^T; lane: token
@@ -1127,16 +1167,19 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             const int tok0 = start + c * C;
             const int clen = min(C, len - c * C);
             if (q < RT) {
-                f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < NT; ++kb) o = MC::mma(load_frag_p<MC>(sUt, LDC, 0, kb, lane), st.pf[kb], o);
                 const int row = 16 * q + ln;
                 const float sg = sSg[(c & 1) * C + row];
-                if (row < clen) {
-                    E4 w;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(sg * o1[i] + o[i]);
-                    *reinterpret_cast<E4 *>(out + ((size_t)(tok0 + row) * hv + h) * DV + col0 + 4 * g4) = w;
+                for (int rr = 0; rr < RW; ++rr) {
+                    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < NT; ++kb) o = MC::mma(load_frag_p<MC>(sUt, LDC, 16 * rr, kb, lane), st.pf[kb], o);
+                    if (row < clen) {
+                        E4 w;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(sg * o1[rr][i] + o[i]);
+                        *reinterpret_cast<E4 *>(out + ((size_t)(tok0 + row) * hv + h) * DV + col0 + 16 * rr + 4 * g4) = w;
+                    }
                 }
             }
             __syncthreads();
@@ -1171,16 +1214,17 @@ static hipError_t allow_smem(KernelT kernel, size_t bytes, std::atomic<bool> &do
     return e;
 }
 
-// The scan, with states stored as SE (fp32, or bf16 with fp32 arithmetic).
-template <typename E, int C, int D, typename SE>
-static hipError_t launch_scan(const PrefillArgs &A, hipStream_t st, int32_t *bounds, int32_t *seq_chunk0,
-                              int32_t *order, E *tbmat, E *pmat, E *wmat, E *qmat, E *ktmat, float *gates) {
-    typedef ScanSmem<E, C, D> SL;
+// The scan, with states stored as SE (fp32, or bf16 with fp32 arithmetic)
+// and R state rows per workgroup.
+template <typename E, int C, int D, typename SE, int R>
+static hipError_t launch_scan_r(const PrefillArgs &A, hipStream_t st, int32_t *bounds, int32_t *seq_chunk0,
+                                int32_t *order, E *tbmat, E *pmat, E *wmat, E *qmat, E *ktmat, float *gates) {
+    typedef ScanSmem<E, C, D, R> SL;
     static std::atomic<bool> scan_ok{false};
-    auto scan = gdn_scan_kernel<E, C, D, SE>;
+    auto scan = gdn_scan_kernel<E, C, D, SE, R>;
     hipError_t e;
     if ((e = allow_smem(scan, SL::bytes, scan_ok)) != hipSuccess) return e;
-    const int64_t per_kh = (int64_t)(A.hv / A.hk) * (D / kSliceRows);
+    const int64_t per_kh = (int64_t)(A.hv / A.hk) * (D / R);
     const int64_t groups = (int64_t)A.num_seqs * A.hk;
     const int64_t grid = ((groups + 7) / 8) * per_kh * 8;
     return launch_kernel(kScan, scan, dim3((unsigned)grid), dim3(kScanThreads), SL::bytes, st,
@@ -1188,6 +1232,20 @@ static hipError_t launch_scan(const PrefillArgs &A, hipStream_t st, int32_t *bou
                          (const int32_t *)order, (const E *)tbmat, (const E *)pmat, (const E *)wmat,
                          (const E *)qmat, (const E *)ktmat, (const float *)gates, (const SE *)A.s0,
                          (SE *)A.s_final, (E *)A.out, A.num_seqs, A.hk, A.hv);
+}
+
+// Every 16-row slice loads the head's whole chunk operands, so 32-row slices
+// halve those loads per state row at the cost of a longer chunk step. That
+// pays once 16-row slices take more than one pass over the CUs (several
+// sequences, or many heads); a single pass keeps the shorter step.
+template <typename E, int C, int D, typename SE>
+static hipError_t launch_scan(const PrefillArgs &A, hipStream_t st, int32_t *bounds, int32_t *seq_chunk0,
+                              int32_t *order, E *tbmat, E *pmat, E *wmat, E *qmat, E *ktmat, float *gates) {
+    if constexpr (IsBf16<E>::value && D >= 32) {
+        if (scan_slice_rows(A.num_seqs, A.hv, D, true) == 32)
+            return launch_scan_r<E, C, D, SE, 32>(A, st, bounds, seq_chunk0, order, tbmat, pmat, wmat, qmat, ktmat, gates);
+    }
+    return launch_scan_r<E, C, D, SE, 16>(A, st, bounds, seq_chunk0, order, tbmat, pmat, wmat, qmat, ktmat, gates);
 }
 
 template <typename E, typename G, int C, int D>

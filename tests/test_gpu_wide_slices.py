@@ -1,0 +1,92 @@
+"""The chunked scan with 32 state rows per workgroup.
+
+On bf16 I/O with d >= 32, the scan gives each workgroup 32 value rows of a
+state instead of 16 once 16-row slices would take more than one pass over
+the GPU's 256 CUs (N * HV * DV / 16 > 256). Every output and state element
+goes through the same MFMA sequence either way, so a batched call must give
+the same bits as calls on each sequence alone, which fit one pass and keep
+16-row slices (1 * HV * DV / 16 <= 256). Both are held to the bf16 bar
+against the fp64 oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gdn_synth as gs
+import gated_deltanet_linear_02_amd as gdn
+from gpu_util import TOL_BF16, device_inputs, note, oracle_ref, rel_err, requires_gpu, to_f64
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+CUS = 256
+
+
+def _wide(n, hv, d):
+    return n * hv * (d // 16) > CUS
+
+
+def _lengths(n, seed):
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in rng.integers(1, 150, size=n)]
+    lens[1] = 0      # an empty sequence
+    lens[2] = 64     # exactly one chunk of 64
+    return lens
+
+
+def _call(q, k, v, g, b, cu, s0, chunk, state_dtype):
+    return gdn.prefill(q, k, v, g, b, cu, chunk=chunk, scale=0.8, initial_state=s0, state_dtype=state_dtype)
+
+
+@pytest.mark.parametrize("d,chunk,state", [(32, 16, "f32"), (32, 32, "f32"), (32, 64, "f32"),
+                                           (64, 16, "f32"), (64, 32, "f32"), (64, 64, "f32"),
+                                           (128, 16, "f32"), (128, 32, "f32"), (128, 64, "f32"),
+                                           (128, 64, "bf16")])
+def test_wide_slices_match_single_sequence_calls(d, chunk, state):
+    hk, hv = 4, 8
+    n = CUS // (hv * d // 16) + 2
+    assert _wide(n, hv, d) and not _wide(1, hv, d)
+    lens = _lengths(n, seed=1200 + d + chunk)
+    inp = gs.make_inputs(lens, hk, hv, d, d, seed=1300 + d + chunk, io_dtype="bf16", gate_dtype="f32",
+                         init_state=True)
+    sd = torch.bfloat16 if state == "bf16" else torch.float32
+    note(f"wide slices d={d} chunk={chunk} state={state} N={n}")
+    t = device_inputs(inp)
+    s0 = t["initial_state"] if state == "f32" else t["initial_state"].to(torch.bfloat16)
+    o, f = _call(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"], s0, chunk, sd)
+    torch.cuda.synchronize()
+    cu = inp.cu_seqlens
+    for i in range(n):
+        a, e = int(cu[i]), int(cu[i + 1])
+        if a == e:
+            assert torch.equal(f[i], s0[i])
+            continue
+        one = torch.tensor([0, e - a], dtype=torch.int32, device="cuda")
+        oi, fi = _call(t["q"][a:e].contiguous(), t["k"][a:e].contiguous(), t["v"][a:e].contiguous(),
+                       t["g"][a:e].contiguous(), t["beta"][a:e].contiguous(), one, s0[i:i + 1].contiguous(),
+                       chunk, sd)
+        torch.cuda.synchronize()
+        assert torch.equal(o[a:e], oi), f"sequence {i}: outputs differ from its own call"
+        assert torch.equal(f[i], fi[0]), f"sequence {i}: final state differs from its own call"
+    # bf16 states: the oracle starts from the rounded initial state
+    o_ref, f_ref = oracle_ref(inp, scale=0.8, initial_state=None if state == "f32" else to_f64(s0))
+    eo, ef = rel_err(to_f64(o), o_ref), rel_err(to_f64(f), f_ref)
+    print(f"[parity] wide slices d={d} chunk={chunk} state={state} N={n} out_err={eo:.3e} state_err={ef:.3e}",
+          flush=True)
+    assert eo <= TOL_BF16 and ef <= TOL_BF16
+
+
+def test_wide_slices_many_heads_one_sequence():
+    """48 value heads of d = 128 (384 16-row slices): one sequence alone
+    takes 32-row slices; every head against the oracle."""
+    inp = gs.make_inputs([300], 16, 48, 128, 128, seed=1401, io_dtype="bf16", gate_dtype="f32", init_state=True)
+    assert _wide(1, 48, 128)
+    note("wide slices 48 heads")
+    t = device_inputs(inp)
+    o, f = gdn.prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"], chunk=64,
+                       initial_state=t["initial_state"])
+    torch.cuda.synchronize()
+    o_ref, f_ref = oracle_ref(inp)
+    eo, ef = rel_err(to_f64(o), o_ref), rel_err(to_f64(f), f_ref)
+    print(f"[parity] wide slices 48 heads out_err={eo:.3e} state_err={ef:.3e}", flush=True)
+    assert eo <= TOL_BF16 and ef <= TOL_BF16
