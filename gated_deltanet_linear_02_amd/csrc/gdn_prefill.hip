@@ -302,7 +302,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
 
     const int ci = blockIdx.x, kh = blockIdx.y;
     const int group = hv / hk;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // readfirstlane: the wave index is uniform, and saying so makes the
+    // role branches, wave-strided loops and their addresses scalar.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4, ln = lane & 15;
     const size_t ld = (size_t)hk * DK;
 
@@ -447,9 +449,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
     const int par = wave & 1;
     constexpr int NTS = TileSet<NB, 0>::N > TileSet<NB, 1>::N ? TileSet<NB, 0>::N : TileSet<NB, 1>::N;
     f32x4 til[NTS > 0 ? NTS : 1];
-    auto gram = [&](auto parc) {
+    // Each role and tile set is its own instantiation (ROLE: 0 Gram, 1 scores).
+    auto by_role = [&](auto &&fn) {
+        if (score_wave) {
+            if (par) fn(std::integral_constant<int, 1>(), std::true_type());
+            else fn(std::integral_constant<int, 0>(), std::true_type());
+        } else {
+            if (par) fn(std::integral_constant<int, 1>(), std::false_type());
+            else fn(std::integral_constant<int, 0>(), std::false_type());
+        }
+    };
+    auto gram = [&](auto parc, auto scorec) {
         typedef TileSet<NB, decltype(parc)::value> TS;
-        const E *Bm = score_wave ? sQ : sK;
+        constexpr bool kScore = decltype(scorec)::value;
+        const E *Bm = kScore ? sQ : sK;
 #pragma unroll
         for (int r = 0; r < TS::NR; ++r) {
             const int ti = TS::row(r);
@@ -464,8 +477,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
             }
         }
     };
-    if (par) gram(std::integral_constant<int, 1>());
-    else gram(std::integral_constant<int, 0>());
+    by_role(gram);
     __syncthreads();  // the K / Q region becomes A / T
 
     // ---- 5. Per value head of the group
@@ -520,8 +532,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
 
         // A = strict_lower(b_i exp(c_i - c_j) (K K^T)_ij) into LDS (waves 0, 1);
         // P = lower(scale exp(c_i - c_j) (Q K^T)_ij) to fragments (waves 2, 3)
-        auto decay = [&](auto parc) {
+        auto decay = [&](auto parc, auto scorec) {
             typedef TileSet<NB, decltype(parc)::value> TS;
+            constexpr bool score_wave = decltype(scorec)::value;
 #pragma unroll
             for (int r = 0; r < TS::NR; ++r) {
                 const int ti = TS::row(r);
@@ -541,10 +554,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
                             const float dc = static_cast<float>(cI - sc[j]);  // fp64 difference, then fp32
                             val[tj][e] = keep ? mI * exp2_hw(dc) * t[e] : 0.f;
                         }
-                        if (!score_wave) *reinterpret_cast<f32x4 *>(sA + i * LDC + 16 * tj + 4 * g4) = val[tj];
+                        if constexpr (!score_wave) *reinterpret_cast<f32x4 *>(sA + i * LDC + 16 * tj + 4 * g4) = val[tj];
                     }
                 }
-                if (score_wave) {
+                if constexpr (score_wave) {
 #pragma unroll
                     for (int kb = 0; kb < KBC; ++kb) {
                         if (kb >= tri_read_blocks<MC, C>(ti)) continue;  // zero, never read
@@ -557,8 +570,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
                 }
             }
         };
-        if (par) decay(std::integral_constant<int, 1>());
-        else decay(std::integral_constant<int, 0>());
+        by_role(decay);
         __syncthreads();
 
         // diagonal blocks: wave b inverts (I + A_bb) by right-looking forward
@@ -659,7 +671,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
 }
 
 // ---------------------------------------------------------------------------
-// 3. Chunk-recurrent scan over one (sequence, value head, 16 value rows)
+// 3. Chunk-recurrent scan over one (sequence, value head, 16 or 32 value rows)
 // ---------------------------------------------------------------------------
 //
 // Eight waves per workgroup, two per SIMD, in two roles. With S0 the slice at
