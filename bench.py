@@ -108,6 +108,35 @@ def _short_kernel(name: str) -> str:
     return "copy" if "copy" in name.lower() else "other"
 
 
+def _template_ints(name: str) -> list:
+    """The integer template arguments of a kernel name as rocprofv3 prints it
+    (mangled, or demangled with the arguments between < and >)."""
+    import re
+    m = re.search(r"_kernelI(.*?)EEv", name)
+    if m:
+        return [int(x) for x in re.findall(r"Li(\d+)E", m.group(1) + "E")]
+    m = re.search(r"_kernel<([^()]*)>\(", name)
+    if m:
+        return [int(x) for x in (a.strip() for a in m.group(1).split(",")) if x.isdigit()]
+    return []
+
+
+def _kernel_label(name: str) -> str:
+    """Kernel name for the summaries, with the variant where a kernel has
+    several: chunk size and state rows per workgroup (scan), chunk size
+    (prep), state rows per lane group (token scan)."""
+    short = _short_kernel(name)
+    label = KERNELS.get(short, name)
+    ints = _template_ints(name)
+    if short == "scan" and len(ints) >= 3:
+        label += f" (C={ints[0]}, {ints[-1]}-row slices)"
+    elif short == "prep" and ints:
+        label += f" (C={ints[0]})"
+    elif short == "token_scan" and len(ints) >= 3 and ints[-1] > 1:
+        label += f" ({ints[-1]} rows per lane group)"
+    return label
+
+
 def _state_key(name: str) -> str:
     """Short kernel name, with "/bf16" appended for decode kernels built for
     bf16 state storage (their third template argument)."""
@@ -196,7 +225,7 @@ def summarize_profiles(stats_dir: str, fetch_dir: str, write_dir: str, probe_mib
     for r in rows:
         short = _short_kernel(r["Name"])
         if short in KERNELS:
-            lines.append(f"| {KERNELS[short]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+            lines.append(f"| {_kernel_label(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     lines += [
         "",
@@ -245,7 +274,7 @@ def summarize_short(stats_dir: str, results_jsonl: str):
     for r in rows:
         short = _short_kernel(r["Name"])
         if short in KERNELS:
-            lines.append(f"| {KERNELS[short]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+            lines.append(f"| {_kernel_label(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     lines += ["", "## Per shape (HIP events in the same run; 4 rotated buffer sets)", "",
               "Taken under the profiler, which adds a per-launch overhead that shows in every column "
@@ -446,7 +475,7 @@ def summarize_norm(stats_dir: str, fetch_dir: str, write_dir: str, results_jsonl
     for r in rows:
         short = _short_kernel(r["Name"])
         if short in KERNELS:
-            lines.append(f"| {KERNELS[short]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+            lines.append(f"| {_kernel_label(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     lines += [
         "",
@@ -517,7 +546,7 @@ def summarize_state(stats_dir: str, fetch_dir: str, write_dir: str, results_json
         k = _state_key(r["Name"])
         short = k.split("/")[0]
         if short in ("decode", "decode_norm"):
-            lines.append(f"| {KERNELS[short]} | {'bf16' if k.endswith('/bf16') else 'fp32'} | {r['Calls']} | "
+            lines.append(f"| {_kernel_label(r['Name'])} | {'bf16' if k.endswith('/bf16') else 'fp32'} | {r['Calls']} | "
                          f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                          f"{float(r['MaxNs']) / 1e3:.2f} |")
     lines += [
@@ -579,13 +608,9 @@ def summarize_tune(stats_dir: str, results_jsonl: str):
     for r in rows:
         short = _short_kernel(r["Name"])
         if short in KERNELS or "gate_kernel" in r["Name"]:
-            name = KERNELS.get(short, "gdn_gate_kernel")
-            m = (re.search(r"kernelI(?:DF16b|f)+Li(\d+)ELi\d+", r["Name"])
-                 or re.search(r"_kernel<[^,<>]*, (\d+), \d+>", r["Name"]))
-            if short in ("prep", "scan") and m:
-                name += f" (C={m.group(1)})"
-            elif "gate_kernel" in r["Name"]:
-                name += " (bf16)" if "IDF16b" in r["Name"] else " (fp32)"
+            name = _kernel_label(r["Name"]) if short in KERNELS else "gdn_gate_kernel"
+            if "gate_kernel" in r["Name"]:
+                name += " (bf16)" if ("IDF16b" in r["Name"] or "_Accum" in r["Name"]) else " (fp32)"
             lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     lines += ["", "## Per shape (HIP events in the same run)", "",
@@ -699,7 +724,7 @@ def summarize_configs(stats_dir: str, results_jsonl: str):
     for r in rows:
         short = _short_kernel(r["Name"])
         if short in KERNELS:
-            lines.append(f"| {KERNELS[short]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+            lines.append(f"| {_kernel_label(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     lines += ["", "## Per workload (HIP events in the same run, under the profiler)", "",
               "| workload | sequences | tokens | prefill ms | tokens/s | prep ms | scan ms | scan MFMA | "
