@@ -240,18 +240,6 @@ template <typename G> __device__ __forceinline__ float gate_load(const G *p, siz
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr double kLog2eD = 1.4426950408889634;
 
-// acc += X[xr.., xc..] (16x16) * Y[yr.., yc..] (16x16), fp32 LDS operands
-// with row stride ld, on v_mfma_f32_16x16x4_f32.
-__device__ __forceinline__ f32x4 mm16_f32(f32x4 acc, const float *X, int xr, int xc, const float *Y, int yr,
-                                          int yc, int ld, int lane) {
-    const int ln = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[(xr + ln) * ld + xc + 4 * kb + g],
-                                                   Y[(yr + 4 * kb + g) * ld + yc + ln], acc, 0, 0, 0);
-    return acc;
-}
-
 template <typename MM> __device__ __forceinline__ void frag_set(typename MM::Frag &f, int e, float x) {
     if constexpr (MM::KPL == 1) f = x; else f[e] = static_cast<bf16>(x);
 }
@@ -595,41 +583,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
 
         // blocks below the diagonal, one wave per block column j:
         //   Z = sum_{m=j}^{i-1} A_im T_mj,  T_ij = -T_ii Z   for i = j+1, ...
-        // Z stays in registers: its accumulator layout is used directly as the
-        // B operand by pairing contraction index 4g + r with k-step r.
+        // The column stays in registers. An accumulator tile (lane: column
+        // l%16, rows 4 (l/16) + r) is the B operand of the next product when
+        // k-step r takes contraction index 4 (l/16) + r, so Z and each new
+        // T_mj feed the following MFMAs directly; A_im and T_ii are read
+        // from LDS once, as the matching 4 contiguous values per lane.
         if (wave < NB - 1) {
             const int j = wave;
-            for (int i = j + 1; i < NB; ++i) {
+            f32x4 tcol[NB];  // T_mj, m >= j, in accumulator layout
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+                tcol[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (m == j) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) tcol[m][r] = sT[(16 * j + 4 * g4 + r) * LDC + 16 * j + ln];
+                }
+            }
+#pragma unroll
+            for (int i = 1; i < NB; ++i) {
+                if (i <= j) continue;
                 f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                for (int m = j; m < i; ++m) z = mm16_f32(z, sA, 16 * i, 16 * m, sT, 16 * m, 16 * j, LDC, lane);
+#pragma unroll
+                for (int m = 0; m < i; ++m) {
+                    if (m < j) continue;
+                    const f32x4 a = *reinterpret_cast<const f32x4 *>(sA + (16 * i + ln) * LDC + 16 * m + 4 * g4);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) z = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], tcol[m][r], z, 0, 0, 0);
+                }
+                const f32x4 d = *reinterpret_cast<const f32x4 *>(sT + (16 * i + ln) * LDC + 16 * i + 4 * g4);
                 f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    t = __builtin_amdgcn_mfma_f32_16x16x4f32(-sT[(16 * i + ln) * LDC + 16 * i + 4 * g4 + r], z[r],
-                                                             t, 0, 0, 0);
+                for (int r = 0; r < 4; ++r) t = __builtin_amdgcn_mfma_f32_16x16x4f32(-d[r], z[r], t, 0, 0, 0);
+                tcol[i] = t;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sT[(16 * i + 4 * g4 + r) * LDC + 16 * j + ln] = t[r];
             }
         }
         __syncthreads();
 
-        // Tb = T diag(b) in fragments (blocks above the diagonal are zero;
-        // those the scan does not read are not written)
+        // Tb = T diag(b) in fragments to the workspace, and the B operand of W,
+        // T diag(b gamma), in the same fragment order to LDS (over A, which is
+        // not read after the inverse), both from one read of T. Blocks above the
+        // diagonal are zero; those the scan does not read are not written, and
+        // the product for W skips them too.
+        typename MC::Frag *sBW = reinterpret_cast<typename MC::Frag *>(sA);
         for (int f = wave; f < NB * KBC; f += 4) {
             const int rt = f / KBC, kb = f - rt * KBC;
             if (kb >= tri_read_blocks<MC, C>(rt)) continue;
             const int i = 16 * rt + ln;
-            typename MC::Frag fr;
+            typename MC::Frag fr, fw;
 #pragma unroll
             for (int e = 0; e < MC::KPL; ++e) {
                 const int j = acc_k<MC>(kb, g4, e);
-                frag_set<MC>(fr, e, (j >> 4) <= rt ? sT[i * LDC + j] * sb[j] : 0.f);
+                const float t = (j >> 4) <= rt ? sT[i * LDC + j] : 0.f;
+                frag_set<MC>(fr, e, t * sb[j]);
+                frag_set<MC>(fw, e, t * sbg[j]);
             }
             *reinterpret_cast<typename MC::Frag *>(tbmat + mat0 + frag_off<MC>(f, lane)) = fr;
+            sBW[f * 64 + lane] = fw;
         }
+        __syncthreads();
 
         // -W = -T diag(b gamma) K: per key group and token tile, K^T (registers)
-        // times (T diag(b gamma))^T read from LDS; the accumulators (lane: token
+        // times (T diag(b gamma))^T from LDS; the accumulators (lane: token
         // 16 ti + l%16, keys 16 mt + 4 (l/16) + r) are W's fragments with keys
         // in accumulator order.
 #pragma unroll
@@ -637,22 +653,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
             const int dg = wave + 4 * gi;
             if (dg >= NDG) continue;
             for (int ti = 0; ti < NB; ++ti) {
-                const int i = 16 * ti + ln;
+                const int nkb = tri_read_blocks<MC, C>(ti);
                 typename MC::Frag bfr[KBC];
 #pragma unroll
-                for (int kb = 0; kb < KBC; ++kb) {
-#pragma unroll
-                    for (int e = 0; e < MC::KPL; ++e) {
-                        const int j = acc_k<MC>(kb, g4, e);
-                        frag_set<MC>(bfr[kb], e, (j >> 4) <= ti ? sT[i * LDC + j] * sbg[j] : 0.f);
-                    }
-                }
+                for (int kb = 0; kb < KBC; ++kb) bfr[kb] = kb < nkb ? sBW[(ti * KBC + kb) * 64 + lane] : zero_frag<MC>();
                 f32x4 w[DG];
 #pragma unroll
                 for (int t = 0; t < DG; ++t) {
                     w[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kb = 0; kb < KBC; ++kb) w[t] = MC::mma(ktr[gi][t][kb], bfr[kb], w[t]);
+                    for (int kb = 0; kb < KBC; ++kb)
+                        if (kb < nkb) w[t] = MC::mma(ktr[gi][t][kb], bfr[kb], w[t]);
                 }
                 if constexpr (MD::KPL == 1) {
 #pragma unroll
