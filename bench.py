@@ -619,17 +619,18 @@ def summarize_tune(stats_dir: str, results_jsonl: str):
               "(warm, same inputs). Taken under "
               "the profiler, which adds a per-launch overhead; `python3 bench.py --tune` measures the same "
               "without it.", "",
-              "| sequences x tokens | rule | rule us | tuned | tuned us | speedup | tuner's warm us (64/32/16/1) |",
+              "Methods are named chunk/rows: chunk size, then state rows per scan workgroup; 1 is token by "
+              "token.", "",
+              "| sequences x tokens | rule | rule us | tuned | tuned us | speedup | tuner's warm us per method |",
               "|---|---|---|---|---|---|---|"]
     for line in open(results_jsonl):
         line = line.strip()
         if not line.startswith("{"):
             continue
         d = json.loads(line)
-        warm = "/".join(f"{d['candidate_ms_warm'][c] * 1e3:.1f}" if d['candidate_ms_warm'][c] >= 0 else "-"
-                        for c in ("64", "32", "16", "1"))
-        lines.append(f"| {d['num_seqs']} x {d['tokens_per_seq']} | {d['rule_chunk']} | {d['rule_ms'] * 1e3:.1f} | "
-                     f"{d['tuned_chunk']} | {d['tuned_ms'] * 1e3:.1f} | {d['speedup']:.2f} | {warm} |")
+        warm = ", ".join(f"{c}: {t * 1e3:.1f}" if t >= 0 else f"{c}: -" for c, t in d["candidate_ms_warm"].items())
+        lines.append(f"| {d['num_seqs']} x {d['tokens_per_seq']} | {d['rule_method']} | {d['rule_ms'] * 1e3:.1f} | "
+                     f"{d['tuned_method']} | {d['tuned_ms'] * 1e3:.1f} | {d['speedup']:.2f} | {warm} |")
     with open(os.path.join(ROOT, "profiles", "gdn_prefill_tuning.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -992,7 +993,8 @@ def graph_bench(dev, steps):
 
 
 # Shapes for the tuning sweep: (sequences, tokens each).
-TUNE_SHAPES = ((1, 16), (1, 48), (1, 128), (1, 512), (8, 4), (64, 1), (64, 4), (64, 16), (8, 300), (1, 4096))
+TUNE_SHAPES = ((1, 16), (1, 48), (1, 128), (1, 512), (8, 4), (64, 1), (64, 4), (64, 16), (8, 300), (2, 600),
+               (2, 2048), (1, 4096))
 
 
 def tuning_sweep(dev, copies, steps):
@@ -1037,7 +1039,7 @@ def tuning_sweep(dev, copies, steps):
         # the two counts), so that warm-up order favours neither
         gdn.tune_cache_clear()
         rule_ms = timed()
-        rule = gdn.prefill_method(N, T, HK, HV, D)
+        rule = gdn.method_name(*gdn.prefill_plan(N, T, HK, HV, D))
         d0 = sets[0]
         r = gdn.tune_prefill(d0["q"], d0["k"], d0["v"], d0["g"], d0["beta"], d0["cu_seqlens"], initial_state=d0["s0"])
         tuned_ms = timed()
@@ -1045,9 +1047,8 @@ def tuning_sweep(dev, copies, steps):
         rule_ms = min(rule_ms, timed())
         print(json.dumps({
             "mode": "tuning", "num_seqs": N, "tokens_per_seq": k, "total_tokens": T,
-            "rule_chunk": rule, "tuned_chunk": r["chunk"], "rule_ms": rule_ms, "tuned_ms": tuned_ms,
-            "speedup": rule_ms / tuned_ms, "candidate_ms_warm": {str(c): t for c, t in r["ms"].items()},
-            "candidate_gate_err": {str(c): e for c, e in r["err"].items()},
+            "rule_method": rule, "tuned_method": r["method"], "rule_ms": rule_ms, "tuned_ms": tuned_ms,
+            "speedup": rule_ms / tuned_ms, "candidate_ms_warm": r["ms"], "candidate_gate_err": r["err"],
             "dtype": "bf16", "data": "synthetic", "buffer_copies": copies,
             "config": {"workload": f"{N} sequence(s) x {k} tokens, HK={HK}, HV={HV}, d={D}"},
         }), flush=True)

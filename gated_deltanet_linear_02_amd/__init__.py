@@ -30,8 +30,8 @@ import torch
 
 __all__ = [
     "GdnError", "lib_path", "load", "prefill", "decode_step", "prefill_workspace_size", "prefill_method",
-    "tune_prefill", "tune_cache_clear", "tune_cache_size", "tune_cache_save", "tune_cache_load",
-    "timing_start", "timing_stop", "abi_version", "KERNEL_KINDS",
+    "prefill_plan", "tune_prefill", "method_name", "TUNE_CANDIDATES", "tune_cache_clear", "tune_cache_size",
+    "tune_cache_save", "tune_cache_load", "timing_start", "timing_stop", "abi_version", "KERNEL_KINDS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -78,7 +78,7 @@ def load():
         L.gdn_prefill_workspace_size.restype = sz
         L.gdn_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32]
         L.gdn_prefill_method.restype = i32
-        L.gdn_prefill_method.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32, i32]
+        L.gdn_prefill_method.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32)]
         L.gdn_prefill.restype = i32
         L.gdn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
                                   f32, i32, i32, vp, vp, vp, vp, sz, vp]
@@ -95,8 +95,8 @@ def load():
         L.gdn_tune_prefill_scratch_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]
         L.gdn_tune_prefill.restype = i32
         L.gdn_tune_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, f32, i32, i32,
-                                       vp, f32, vp, sz, vp, ctypes.POINTER(i32), ctypes.POINTER(f32),
-                                       ctypes.POINTER(f32)]
+                                       vp, f32, vp, sz, vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                       ctypes.POINTER(f32), ctypes.POINTER(f32)]
         L.gdn_tune_cache_clear.restype = None
         L.gdn_tune_cache_clear.argtypes = []
         L.gdn_tune_cache_size.restype = i32
@@ -176,12 +176,23 @@ def prefill_workspace_size(num_seqs: int, total_tokens: int, hk: int, hv: int, d
                                                  _dtype_code(io_dtype)))
 
 
+def prefill_plan(num_seqs: int, total_tokens: int, hk: int, hv: int, d: int, chunk: int = 0,
+                 io_dtype: torch.dtype = torch.bfloat16, gate_dtype: torch.dtype = torch.float32) -> Tuple[int, int]:
+    """The method ``prefill`` uses for these sizes (``gdn_prefill_method``):
+    (chunk, rows) with chunk 1 (token by token), 16, 32 or 64 and rows the
+    chunked scan's state rows per workgroup (16 or 32; 0 token by token);
+    (0, 0) if the sizes are rejected."""
+    rows = ctypes.c_int32(0)
+    c = load().gdn_prefill_method(num_seqs, total_tokens, hk, hv, d, d, chunk, _dtype_code(io_dtype),
+                                  _dtype_code(gate_dtype), ctypes.byref(rows))
+    return int(c), int(rows.value)
+
+
 def prefill_method(num_seqs: int, total_tokens: int, hk: int, hv: int, d: int, chunk: int = 0,
                    io_dtype: torch.dtype = torch.bfloat16, gate_dtype: torch.dtype = torch.float32) -> int:
-    """The method ``prefill`` uses for these sizes (``gdn_prefill_method``):
-    1 (token by token), 16, 32 or 64; 0 if the sizes are rejected."""
-    return int(load().gdn_prefill_method(num_seqs, total_tokens, hk, hv, d, d, chunk, _dtype_code(io_dtype),
-                                         _dtype_code(gate_dtype)))
+    """The chunk of ``prefill_plan``: 1 (token by token), 16, 32 or 64; 0 if
+    the sizes are rejected."""
+    return prefill_plan(num_seqs, total_tokens, hk, hv, d, chunk, io_dtype, gate_dtype)[0]
 
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
@@ -298,18 +309,26 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     return out
 
 
-TUNE_CANDIDATES = (64, 32, 16, 1)
+# gdn_tune_prefill's candidates in its order: (chunk, state rows per scan
+# workgroup), named "chunk/rows" ("1" token by token).
+TUNE_CANDIDATES = ((64, 16), (64, 32), (32, 16), (32, 32), (16, 16), (16, 32), (1, 0))
+
+
+def method_name(chunk: int, rows: int) -> str:
+    return "1" if chunk == 1 else f"{chunk}/{rows}"
 
 
 def tune_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
                  cu_seqlens: torch.Tensor, *, scale: float = 1.0, initial_state: Optional[torch.Tensor] = None,
                  gate_tol: float = 1.0 / 64, scratch: Optional[torch.Tensor] = None, stream=None) -> dict:
     """Measure every prefill method on these inputs (``gdn_tune_prefill``):
-    methods whose output or final state differs from chunk 64's by more than
-    gate_tol of the largest magnitude are rejected, the fastest of the rest is
-    returned and cached for ``prefill(chunk=0)`` on this device and shape
-    bucket. Returns {"chunk": c, "ms": {c: t}, "err": {c: e}} (t = -1 when
-    rejected). Synchronises the stream."""
+    methods whose output or final state differs from chunk 64's (16 rows) by
+    more than gate_tol of the largest magnitude are rejected, the fastest of
+    the rest is returned and cached for ``prefill(chunk=0)`` on this device
+    and shape bucket. Returns {"chunk": c, "rows": r, "method": name,
+    "ms": {name: t}, "err": {name: e}}, names as ``method_name`` (t = -1 when
+    rejected or not applicable, e = -1 when not run). Synchronises the
+    stream."""
     T, hk, dk = q.shape
     hv, dv = v.shape[1], v.shape[2]
     N = cu_seqlens.numel() - 1
@@ -331,14 +350,20 @@ def tune_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Ten
     if initial_state is not None and initial_state.dtype != torch.float32:
         raise TypeError("tuning takes an fp32 initial state")
     chosen = ctypes.c_int32(0)
-    ms = (ctypes.c_float * 4)()
-    err = (ctypes.c_float * 4)()
+    rows = ctypes.c_int32(0)
+    n = len(TUNE_CANDIDATES)
+    ms = (ctypes.c_float * n)()
+    err = (ctypes.c_float * n)()
     _check(load().gdn_tune_prefill(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, hk, hv, dk, dv, float(scale),
         _dtype_code(q.dtype), _dtype_code(g.dtype), _ptr(initial_state), float(gate_tol), _ptr(scratch),
-        scratch.numel() * scratch.element_size(), _stream(dev, stream), ctypes.byref(chosen), ms, err))
-    return {"chunk": int(chosen.value), "ms": {c: float(ms[i]) for i, c in enumerate(TUNE_CANDIDATES)},
-            "err": {c: float(err[i]) for i, c in enumerate(TUNE_CANDIDATES)}}
+        scratch.numel() * scratch.element_size(), _stream(dev, stream), ctypes.byref(chosen), ctypes.byref(rows),
+        ms, err))
+    names = [method_name(c, r) for c, r in TUNE_CANDIDATES]
+    return {"chunk": int(chosen.value), "rows": int(rows.value),
+            "method": method_name(int(chosen.value), int(rows.value)),
+            "ms": {nm: float(ms[i]) for i, nm in enumerate(names)},
+            "err": {nm: float(err[i]) for i, nm in enumerate(names)}}
 
 
 def tune_cache_clear() -> None:

@@ -113,13 +113,25 @@ static int32_t check_prefill_shape(int32_t num_seqs, int64_t total_tokens, int32
 }
 
 // The method a call uses: the chunk asked for, or for chunk 0 the choice
-// cached by gdn_tune_prefill for this device and shape, else the rule.
-static int32_t method_for(int32_t chunk, int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
-                          int32_t dk, int32_t dv, int32_t io_dtype, int32_t gate_dtype) {
-    if (chunk != 0) return chunk;
-    const int32_t t = tuned_chunk(num_seqs, total_tokens, hk, hv, dk, io_dtype, gate_dtype);
-    if (t != 0 && method_fits(t, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype)) return t;
-    return rule_chunk(num_seqs, total_tokens, hv, dv);
+// cached by gdn_tune_prefill for this device and shape, else the rule; and
+// for a chunked method the scan's state rows per workgroup: `rows` when it is
+// given and fits, the tuned rows for chunk 0, else the rule's.
+static Method method_for(int32_t chunk, int32_t rows, int32_t num_seqs, int64_t total_tokens, int32_t hk,
+                         int32_t hv, int32_t dk, int32_t dv, int32_t io_dtype, int32_t gate_dtype) {
+    Method m;
+    m.chunk = chunk;
+    m.rows = rows;
+    if (chunk == 0) {
+        m = tuned_method(num_seqs, total_tokens, hk, hv, dk, io_dtype, gate_dtype);
+        if (m.chunk == 0 || !method_fits(m.chunk, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype)) {
+            m.chunk = rule_chunk(num_seqs, total_tokens, hv, dv);
+            m.rows = 0;
+        }
+    }
+    const bool bf = io_dtype == GDN_BF16;
+    if (m.chunk == 1) m.rows = 0;
+    else if (!slice_rows_fit(m.rows, dv, bf)) m.rows = scan_slice_rows(num_seqs, hv, dv, bf);
+    return m;
 }
 
 // Workspace bytes for chunk c (the token scan needs none; 256 are reported so
@@ -143,10 +155,13 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_
 }
 
 int32_t gdn_prefill_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv, int32_t dk,
-                           int32_t dv, int32_t chunk, int32_t io_dtype, int32_t gate_dtype) {
+                           int32_t dv, int32_t chunk, int32_t io_dtype, int32_t gate_dtype, int32_t *slice_rows) {
+    if (slice_rows) *slice_rows = 0;
     if (check_prefill_shape(num_seqs, total_tokens, hk, hv, dk, dv, chunk, io_dtype, gate_dtype) != GDN_OK)
         return 0;
-    return method_for(chunk, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype, gate_dtype);
+    const Method m = method_for(chunk, 0, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype, gate_dtype);
+    if (slice_rows) *slice_rows = m.rows;
+    return m.chunk;
 }
 
 // eps of the output normalisation: finite and not negative.
@@ -169,7 +184,7 @@ static int32_t prefill_impl(const void *q, const void *k, const void *v, const v
                             float scale, int32_t io_dtype, int32_t gate_dtype,
                             const void *initial_state, void *final_state, int32_t state_dtype,
                             const float *norm_w, float norm_eps, void *out,
-                            void *workspace, size_t workspace_bytes, void *stream) {
+                            void *workspace, size_t workspace_bytes, void *stream, int32_t rows = 0) {
     const int32_t sc = check_prefill_shape(num_seqs, total_tokens, hk, hv, dk, dv, chunk, io_dtype, gate_dtype);
     if (sc != GDN_OK) return sc;
     const int32_t so = check_options(io_dtype, state_dtype, norm_w, norm_eps);
@@ -181,7 +196,8 @@ static int32_t prefill_impl(const void *q, const void *k, const void *v, const v
         return GDN_ERR_MISALIGNED;
 
     const size_t eb = dtype_bytes(io_dtype), gb = dtype_bytes(gate_dtype);
-    const int32_t c = method_for(chunk, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype, gate_dtype);
+    const Method m = method_for(chunk, rows, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype, gate_dtype);
+    const int32_t c = m.chunk;
     // The token scan uses no workspace: its buffer is not checked or touched.
     const PrefillLayout L = c == 1 ? PrefillLayout{} : prefill_layout(num_seqs, total_tokens, hk, hv, dk, c, eb);
     if (c != 1 && (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255)))
@@ -214,6 +230,7 @@ static int32_t prefill_impl(const void *q, const void *k, const void *v, const v
     A.hk = hk; A.hv = hv; A.d = dk; A.chunk = c; A.scale = scale;
     A.io_bf16 = io_dtype == GDN_BF16; A.gate_bf16 = gate_dtype == GDN_BF16;
     A.state_bf16 = state_dtype == GDN_BF16;
+    A.slice_rows = m.rows;
     A.s0 = initial_state; A.s_final = final_state; A.out = out;
     A.ws = static_cast<char *>(workspace); A.lay = L;
     try {
@@ -374,3 +391,19 @@ int32_t gdn_timing_stop(int32_t *counts, float *total_ms, int32_t n_kinds) {
 }
 
 }  // extern "C"
+
+namespace gdn {
+
+int32_t prefill_with_method(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                            const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t hk,
+                            int32_t hv, int32_t dk, int32_t dv, Method m, float scale, int32_t io_dtype,
+                            int32_t gate_dtype, const float *initial_state, float *final_state, void *out,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    if (m.chunk == 0) return GDN_ERR_UNSUPPORTED;
+    if (m.chunk != 1 && !slice_rows_fit(m.rows, dv, io_dtype == GDN_BF16)) return GDN_ERR_UNSUPPORTED;
+    return prefill_impl(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, hk, hv, dk, dv, m.chunk, scale,
+                        io_dtype, gate_dtype, initial_state, final_state, GDN_F32, nullptr, 0.f, out, workspace,
+                        workspace_bytes, stream, m.rows);
+}
+
+}  // namespace gdn

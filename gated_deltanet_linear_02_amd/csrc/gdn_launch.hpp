@@ -103,6 +103,7 @@ struct PrefillArgs {
     float scale;
     bool io_bf16, gate_bf16;
     bool state_bf16 = false;  // states stored in bf16 (fp32 arithmetic)
+    int32_t slice_rows = 16;  // state rows per scan workgroup: 16, or 32 (bf16 I/O, d >= 32)
     const void *s0;           // fp32, or bf16 when state_bf16
     void *s_final;
     void *out;
@@ -131,8 +132,25 @@ hipError_t launch_norm_apply(const NormArgs &a, hipStream_t st);
 
 // The chunk gdn_tune_prefill cached for this shape on the current device, or
 // 0 (nothing cached, or no device to ask).
-int32_t tuned_chunk(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv, int32_t d, int32_t io,
+// A prefill method: chunk size (1 = token by token) and, for the chunked
+// scan, state rows per workgroup (0 = not applicable or not chosen).
+struct Method {
+    int32_t chunk = 0, rows = 0;
+};
+
+// The (chunk, rows) that gdn_tune_prefill cached for this device and shape
+// bucket, or chunk 0 when there is none.
+Method tuned_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv, int32_t d, int32_t io,
                     int32_t gate);
+
+// gdn_prefill with the method given (chunk 1, 16, 32 or 64 and, chunked, 16
+// or 32 state rows per scan workgroup); GDN_ERR_UNSUPPORTED for rows that do
+// not fit the call.
+int32_t prefill_with_method(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                            const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t hk,
+                            int32_t hv, int32_t dk, int32_t dv, Method m, float scale, int32_t io_dtype,
+                            int32_t gate_dtype, const float *initial_state, float *final_state, void *out,
+                            void *workspace, size_t workspace_bytes, void *stream);
 
 // gdn_prefill with chunk 0, when nothing is tuned for the shape, picks the
 // method from host-known sizes alone (the lengths stay on the device), by
@@ -156,6 +174,9 @@ constexpr int64_t kChunk32PerSeq = 1024;
 constexpr int64_t kScanOnePassWgs = 256;  // gfx950 (MI355X): 256 CUs
 // State rows per chunked-scan workgroup: 32 when 16-row slices would take
 // more than one pass over the CUs (bf16 I/O, d >= 32), else 16.
+inline bool slice_rows_fit(int32_t rows, int64_t dv, bool io_bf16) {
+    return rows == 16 || (rows == 32 && io_bf16 && dv >= 32);
+}
 inline int32_t scan_slice_rows(int64_t num_seqs, int64_t hv, int64_t dv, bool io_bf16) {
     return io_bf16 && dv >= 32 && num_seqs * hv * (dv / 16) > kScanOnePassWgs ? 32 : 16;
 }

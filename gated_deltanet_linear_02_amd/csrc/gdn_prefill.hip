@@ -1260,12 +1260,13 @@ static hipError_t launch_scan_r(const PrefillArgs &A, hipStream_t st, int32_t *b
 // Every 16-row slice loads the head's whole chunk operands, so 32-row slices
 // halve those loads per state row at the cost of a longer chunk step. That
 // pays once 16-row slices take more than one pass over the CUs (several
-// sequences, or many heads); a single pass keeps the shorter step.
+// sequences, or many heads); a single pass keeps the shorter step. The caller
+// picks (scan_slice_rows, or a tuned choice).
 template <typename E, int C, int D, typename SE>
 static hipError_t launch_scan(const PrefillArgs &A, hipStream_t st, int32_t *bounds, int32_t *seq_chunk0,
                               int32_t *order, E *tbmat, E *pmat, E *wmat, E *qmat, E *ktmat, float *gates) {
     if constexpr (IsBf16<E>::value && D >= 32) {
-        if (scan_slice_rows(A.num_seqs, A.hv, D, true) == 32)
+        if (A.slice_rows == 32)
             return launch_scan_r<E, C, D, SE, 32>(A, st, bounds, seq_chunk0, order, tbmat, pmat, wmat, qmat, ktmat, gates);
     }
     return launch_scan_r<E, C, D, SE, 16>(A, st, bounds, seq_chunk0, order, tbmat, pmat, wmat, qmat, ktmat, gates);

@@ -2,7 +2,8 @@
 // correctness gate (gfx950).
 //
 // Which evaluation of the recurrence is fastest, token by token or chunked
-// with C = 16, 32 or 64, depends on the shape and the hardware ("Optimiser
+// with C = 16, 32 or 64 and 16 or 32 state rows per scan workgroup, depends
+// on the shape and the hardware ("Optimiser
 // l'inference sur appareil pour Apple Silicon", section "Qwen cree trois
 // formes de charges de travail distinctes"). The engine of "On descend d'un
 // cran : #004 le meme compilateur sur les puces d'Apple" measures its options
@@ -10,9 +11,9 @@
 // reference, where a wrong result counts when it differs by more than 1/64
 // of the largest value. Here, gdn_tune_prefill runs every method on the
 // caller's inputs, rejects any whose output or final state differs from the
-// chunk-64 result by more than gate_tol of the largest magnitude, times the
-// others, and caches the fastest per (device, driver, library version,
-// shape bucket). gdn_prefill with chunk 0 then takes the cached choice for
+// (chunk 64, 16 rows) result by more than gate_tol of the largest magnitude,
+// times the others, and caches the fastest per (device, driver, library
+// version, shape bucket). gdn_prefill with chunk 0 then takes the cached choice for
 // its shape when there is one, else its fixed rule.
 #include "gdn.h"
 #include "gdn_device.hpp"
@@ -89,15 +90,15 @@ struct TuneKey {
     }
 };
 
-constexpr int kTuneRevision = 1;  // bump when the candidate set or the kernels' speeds change
+constexpr int kTuneRevision = 2;  // bump when the candidate set or the kernels' speeds change
 
 namespace {
 std::mutex &tune_mu() {
     static std::mutex m;
     return m;
 }
-std::map<TuneKey, int32_t> &tune_cache() {
-    static std::map<TuneKey, int32_t> c;
+std::map<TuneKey, Method> &tune_cache() {
+    static std::map<TuneKey, Method> c;
     return c;
 }
 }  // namespace
@@ -140,17 +141,17 @@ static bool shape_key(TuneKey &k, int32_t num_seqs, int64_t total_tokens, int32_
     return true;
 }
 
-int32_t tuned_chunk(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv, int32_t d, int32_t io,
+Method tuned_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv, int32_t d, int32_t io,
                     int32_t gate) {
     {
         std::lock_guard<std::mutex> lk(tune_mu());
-        if (tune_cache().empty()) return 0;  // nothing tuned: no device query
+        if (tune_cache().empty()) return Method{};  // nothing tuned: no device query
     }
     TuneKey k;
-    if (!shape_key(k, num_seqs, total_tokens, hk, hv, d, io, gate)) return 0;
+    if (!shape_key(k, num_seqs, total_tokens, hk, hv, d, io, gate)) return Method{};
     std::lock_guard<std::mutex> lk(tune_mu());
     auto it = tune_cache().find(k);
-    return it == tune_cache().end() ? 0 : it->second;
+    return it == tune_cache().end() ? Method{} : it->second;
 }
 
 // ----------------------------------------------------------------- scratch
@@ -196,8 +197,12 @@ int32_t gdn_tune_prefill(const void *q, const void *k, const void *v, const void
                          int32_t hk, int32_t hv, int32_t dk, int32_t dv, float scale,
                          int32_t io_dtype, int32_t gate_dtype, const float *initial_state, float gate_tol,
                          void *scratch, size_t scratch_bytes, void *stream,
-                         int32_t *chosen_chunk, float *candidate_ms, float *candidate_err) {
-    static const int32_t kCandidates[4] = {64, 32, 16, 1};  // the reference first
+                         int32_t *chosen_chunk, int32_t *chosen_rows, float *candidate_ms,
+                         float *candidate_err) {
+    // (chunk, state rows per scan workgroup), the reference first
+    static const Method kCandidates[GDN_TUNE_CANDIDATES] = {{64, 16}, {64, 32}, {32, 16}, {32, 32},
+                                                            {16, 16}, {16, 32}, {1, 0}};
+    constexpr int NC = GDN_TUNE_CANDIDATES;
     if (!chosen_chunk) return GDN_ERR_NULL_ARG;
     if (!(gate_tol >= 0.f) || !(gate_tol <= 1.f)) return GDN_ERR_BAD_VALUE;
     const size_t need = gdn_tune_prefill_scratch_size(num_seqs, total_tokens, hk, hv, dk, dv, io_dtype);
@@ -212,13 +217,15 @@ int32_t gdn_tune_prefill(const void *q, const void *k, const void *v, const void
     const int64_t n_out = total_tokens * hv * dv, n_fin = (int64_t)num_seqs * hv * dv * dk;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     int32_t status = GDN_OK;
-    float ms[4] = {-1.f, -1.f, -1.f, -1.f}, err[4] = {-1.f, -1.f, -1.f, -1.f};
+    float ms[NC], err[NC];
+    for (int i = 0; i < NC; ++i) ms[i] = err[i] = -1.f;
 
-    auto run = [&](int32_t c, bool ref) -> int32_t {
+    auto run = [&](Method c, bool ref) -> int32_t {
         void *out = base + (ref ? L.off_ref_out : L.off_out);
         float *fin = reinterpret_cast<float *>(base + (ref ? L.off_ref_fin : L.off_fin));
-        return gdn_prefill(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, hk, hv, dk, dv, c, scale,
-                           io_dtype, gate_dtype, initial_state, fin, out, base + L.off_ws, L.ws_bytes, stream);
+        return prefill_with_method(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, hk, hv, dk, dv, c, scale,
+                                   io_dtype, gate_dtype, initial_state, fin, out, base + L.off_ws, L.ws_bytes,
+                                   stream);
     };
     if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
         status = GDN_ERR_HIP;
@@ -227,9 +234,11 @@ int32_t gdn_tune_prefill(const void *q, const void *k, const void *v, const void
         // outputs so that they compare equal there.
         if (hipMemsetAsync(base + L.off_ref_out, 0, (size_t)n_out * eb, st) != hipSuccess) status = GDN_ERR_HIP;
         if (status == GDN_OK) status = run(kCandidates[0], true);
-        for (int i = 0; i < 4 && status == GDN_OK; ++i) {
-            const int32_t c = kCandidates[i];
-            // correctness gate against the chunk-64 result
+        for (int i = 0; i < NC && status == GDN_OK; ++i) {
+            const Method c = kCandidates[i];
+            // 32 state rows per workgroup exist for bf16 I/O with d >= 32 only
+            if (c.chunk != 1 && !slice_rows_fit(c.rows, dv, io_dtype == GDN_BF16)) continue;
+            // correctness gate against the (64, 16) result
             if (hipMemsetAsync(base + L.off_out, 0, (size_t)n_out * eb, st) != hipSuccess ||
                 hipMemsetAsync(res, 0, 8 * sizeof(unsigned), st) != hipSuccess) {
                 status = GDN_ERR_HIP;
@@ -280,10 +289,11 @@ int32_t gdn_tune_prefill(const void *q, const void *k, const void *v, const void
     if (status != GDN_OK) return status;
 
     int best = 0;  // the reference always passes its own gate
-    for (int i = 1; i < 4; ++i)
+    for (int i = 1; i < NC; ++i)
         if (ms[i] >= 0.f && ms[i] < ms[best]) best = i;
-    *chosen_chunk = kCandidates[best];
-    for (int i = 0; i < 4; ++i) {
+    *chosen_chunk = kCandidates[best].chunk;
+    if (chosen_rows) *chosen_rows = kCandidates[best].rows;
+    for (int i = 0; i < NC; ++i) {
         if (candidate_ms) candidate_ms[i] = ms[i];
         if (candidate_err) candidate_err[i] = err[i];
     }
@@ -312,8 +322,8 @@ int32_t gdn_tune_cache_save(const char *path) {
     if (!f) return GDN_ERR_BAD_VALUE;
     for (const auto &kv : tune_cache()) {
         const TuneKey &k = kv.first;
-        fprintf(f, "gdn-tune-v1 %s %d %d %d %d %d %d %d %d %d %d\n", k.device.c_str(), k.driver, k.version, k.n2,
-                k.t2, k.hk, k.hv, k.d, k.io, k.gate, kv.second);
+        fprintf(f, "gdn-tune-v2 %s %d %d %d %d %d %d %d %d %d %d %d\n", k.device.c_str(), k.driver, k.version,
+                k.n2, k.t2, k.hk, k.hv, k.d, k.io, k.gate, kv.second.chunk, kv.second.rows);
     }
     return fclose(f) == 0 ? GDN_OK : GDN_ERR_BAD_VALUE;
 }
@@ -328,13 +338,16 @@ int32_t gdn_tune_cache_load(const char *path, int32_t *entries) {
     while (fgets(line, sizeof(line), f)) {
         char tag[16], dev[256];
         TuneKey k;
-        int chunk = 0;
-        if (sscanf(line, "%15s %255s %d %d %d %d %d %d %d %d %d %d", tag, dev, &k.driver, &k.version, &k.n2, &k.t2,
-                   &k.hk, &k.hv, &k.d, &k.io, &k.gate, &chunk) != 12)
+        Method m;
+        if (sscanf(line, "%15s %255s %d %d %d %d %d %d %d %d %d %d %d", tag, dev, &k.driver, &k.version, &k.n2,
+                   &k.t2, &k.hk, &k.hv, &k.d, &k.io, &k.gate, &m.chunk, &m.rows) != 13)
             continue;
-        if (strcmp(tag, "gdn-tune-v1") != 0 || !(chunk == 1 || chunk == 16 || chunk == 32 || chunk == 64)) continue;
+        if (strcmp(tag, "gdn-tune-v2") != 0) continue;
+        const bool ok = m.chunk == 1 ? m.rows == 0
+                                     : (m.chunk == 16 || m.chunk == 32 || m.chunk == 64) && (m.rows == 16 || m.rows == 32);
+        if (!ok) continue;
         k.device = dev;
-        tune_cache()[k] = chunk;
+        tune_cache()[k] = m;
         ++n;
     }
     fclose(f);

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum {
     GDN_OK = 0,
@@ -90,10 +90,14 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
  * The method gdn_prefill uses for these sizes and this chunk argument: 1
  * (token by token), 16, 32 or 64; for chunk 0, the cached tuned choice or the
  * rule above. Returns 0 for arguments gdn_prefill would reject.
+ * slice_rows (may be NULL) receives the chunked scan's state rows per
+ * workgroup: 16, or 32 (bf16 I/O with d >= 32), taken from the tuned choice
+ * for chunk 0 and otherwise 32 exactly when N * hv * dv / 16 exceeds the
+ * GPU's 256 CUs; 0 for the token-by-token method or a rejected call.
  */
 int32_t gdn_prefill_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
                            int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype,
-                           int32_t gate_dtype);
+                           int32_t gate_dtype, int32_t *slice_rows);
 
 /*
  * Chunked prefill over N packed variable-length sequences.
@@ -220,26 +224,30 @@ int32_t gdn_decode_step_ex(const void *q, const void *k, const void *v,
 /*
  * Choice of the prefill method by measurement, with a correctness gate.
  *
- * The fastest evaluation (token by token, or chunks of 16, 32 or 64) depends
- * on the shape and the hardware ("Qwen cree trois formes de charges de
+ * The fastest evaluation (token by token, or chunks of 16, 32 or 64 with 16
+ * or 32 state rows per scan workgroup) depends on the shape and the hardware ("Qwen cree trois formes de charges de
  * travail distinctes" of "Optimiser l'inference sur appareil pour Apple
  * Silicon"); the engine of "On descend d'un cran : #004 le meme compilateur
  * sur les puces d'Apple" measures its options at load time and checks each
  * against a reference, with 1/64 of the largest value as its bar.
  *
  * gdn_tune_prefill runs every method on the caller's inputs (same arguments
- * as gdn_prefill, fp32 initial state or NULL). It compares each method's
- * output and final state with those of chunk 64 and rejects it when
+ * as gdn_prefill, fp32 initial state or NULL). The GDN_TUNE_CANDIDATES
+ * methods, in this order, are (chunk, rows): (64, 16), (64, 32), (32, 16),
+ * (32, 32), (16, 16), (16, 32) and (1, -); 32 rows only for bf16 I/O with
+ * d >= 32. It compares each method's output and final state with those of
+ * (64, 16) and rejects it when
  * max |x - ref| / max |ref| exceeds gate_tol, in [0, 1] (1/64 is the pages'
  * bar). It times the rest, each one warm-up plus the mean of five runs on
- * the same inputs, and returns the fastest in *chosen_chunk. It also caches
+ * the same inputs, and returns the fastest in *chosen_chunk and *chosen_rows
+ * (may be NULL; 0 for the token-by-token method). It also caches
  * the choice for (device, driver version, library version, shape bucket).
  * The bucket is num_seqs and total_tokens each rounded up to a power of two,
  * with hk, hv, d and both dtypes exact. gdn_prefill with chunk 0 then uses
  * the cached choice.
- * candidate_ms and candidate_err (may be NULL) receive, for chunks 64, 32,
- * 16 and 1 in that order, the mean time in ms (-1 when rejected or not
- * applicable) and the gate error (-1 when not run).
+ * candidate_ms and candidate_err (may be NULL; GDN_TUNE_CANDIDATES floats
+ * each) receive, in the order above, the mean time in ms (-1 when rejected or
+ * not applicable) and the gate error (-1 when not run).
  * scratch      device memory of gdn_tune_prefill_scratch_size(...) bytes,
  *              256-byte aligned: outputs, final states and a workspace for
  *              the candidates. The caller's buffers are read, never written.
@@ -247,12 +255,15 @@ int32_t gdn_decode_step_ex(const void *q, const void *k, const void *v,
  * GDN_ERR_BAD_VALUE for gate_tol outside [0, 1].
  *
  * The cache lives in the process, shared by all threads, and may be saved
- * to a text file and loaded back, one choice per line. Entries made on
+ * to a text file and loaded back, one choice per line: "gdn-tune-v2", the
+ * device, driver and library versions, the bucket's sequences, tokens, hk,
+ * hv, d, io and gate dtypes, then the chunk and rows. Entries made on
  * another device, driver or library version are kept but never match.
  * gdn_tune_cache_load returns GDN_ERR_BAD_VALUE when the file cannot be
  * opened, and skips lines it cannot parse; *entries (may be NULL) receives
  * the number loaded.
  */
+#define GDN_TUNE_CANDIDATES 7
 size_t gdn_tune_prefill_scratch_size(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
                                      int32_t dk, int32_t dv, int32_t io_dtype);
 int32_t gdn_tune_prefill(const void *q, const void *k, const void *v,
@@ -261,7 +272,8 @@ int32_t gdn_tune_prefill(const void *q, const void *k, const void *v,
                          int32_t hk, int32_t hv, int32_t dk, int32_t dv, float scale,
                          int32_t io_dtype, int32_t gate_dtype, const float *initial_state,
                          float gate_tol, void *scratch, size_t scratch_bytes, void *stream,
-                         int32_t *chosen_chunk, float *candidate_ms, float *candidate_err);
+                         int32_t *chosen_chunk, int32_t *chosen_rows, float *candidate_ms,
+                         float *candidate_err);
 void gdn_tune_cache_clear(void);
 int32_t gdn_tune_cache_size(void);
 int32_t gdn_tune_cache_save(const char *path);

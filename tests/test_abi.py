@@ -10,6 +10,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import gated_deltanet_linear_02_amd as gdn
 
@@ -44,7 +45,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gdn.abi_version() == 3
+    assert gdn.abi_version() == 4
     for s in range(9):
         assert lib.gdn_status_string(s)
     assert b"unknown" in lib.gdn_status_string(99)
@@ -232,23 +233,27 @@ def test_ex_argument_checks(lib):
 
 
 def test_tune_cache_file_round_trip(tmp_path):
-    """The tuning cache's text file: well-formed lines load, malformed ones
-    and unknown methods are skipped, and a save writes what was loaded."""
+    """The tuning cache's text file: well-formed lines (chunk, then state rows
+    per scan workgroup) load; malformed ones, unknown methods and other
+    formats are skipped; and a save writes what was loaded."""
     lib = gdn.load()
     gdn.tune_cache_clear()
     src = tmp_path / "tune.txt"
     src.write_text(
-        "gdn-tune-v1 gfx950/256cu 70000 3001 1 4096 16 32 128 0 1 64\n"
-        "gdn-tune-v1 gfx950/256cu 70000 3001 64 1024 16 32 128 0 0 1\n"
-        "gdn-tune-v1 gfx950/256cu 70000 3001 8 512 2 4 64 1 1 48\n"  # not a method
-        "gdn-tune-v2 gfx950/256cu 70000 3001 8 512 2 4 64 1 1 16\n"  # other format
+        "gdn-tune-v2 gfx950/256cu 70000 4002 1 4096 16 32 128 0 1 64 16\n"
+        "gdn-tune-v2 gfx950/256cu 70000 4002 8 65536 16 32 128 0 1 64 32\n"
+        "gdn-tune-v2 gfx950/256cu 70000 4002 64 1024 16 32 128 0 0 1 0\n"
+        "gdn-tune-v2 gfx950/256cu 70000 4002 8 512 2 4 64 1 1 48 16\n"  # not a chunk
+        "gdn-tune-v2 gfx950/256cu 70000 4002 8 512 2 4 64 1 1 64 8\n"   # not a row count
+        "gdn-tune-v2 gfx950/256cu 70000 4002 8 512 2 4 64 1 1 1 16\n"   # token by token has no rows
+        "gdn-tune-v1 gfx950/256cu 70000 3001 8 512 2 4 64 1 1 16\n"     # older format
         "garbage\n")
-    assert gdn.tune_cache_load(str(src)) == 2
-    assert gdn.tune_cache_size() == 2
+    assert gdn.tune_cache_load(str(src)) == 3
+    assert gdn.tune_cache_size() == 3
     out = tmp_path / "saved.txt"
     gdn.tune_cache_save(str(out))
     lines = sorted(out.read_text().splitlines())
-    assert lines == sorted(src.read_text().splitlines()[:2])
+    assert lines == sorted(src.read_text().splitlines()[:3])
     gdn.tune_cache_clear()
     assert gdn.tune_cache_size() == 0
     with pytest.raises(gdn.GdnError):
@@ -271,12 +276,13 @@ def test_tune_argument_checks(lib):
     args = [FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30), FAKE + (5 << 30),
             1, 128, 2, 4, 64, 64, 1.0, BF16, F32, None]
     need = lib.gdn_tune_prefill_scratch_size(1, 128, 2, 4, 64, 64, BF16)
-    assert lib.gdn_tune_prefill(*args, 1.0 / 64, FAKE + (6 << 30), need, None, None, None, None) == NULL_ARG
-    assert lib.gdn_tune_prefill(*args, -0.1, FAKE + (6 << 30), need, None, ctypes.byref(chosen), None,
+    assert lib.gdn_tune_prefill(*args, 1.0 / 64, FAKE + (6 << 30), need, None, None, None, None, None) == NULL_ARG
+    assert lib.gdn_tune_prefill(*args, -0.1, FAKE + (6 << 30), need, None, ctypes.byref(chosen), None, None,
                                 None) == BAD_VALUE
     assert lib.gdn_tune_prefill(*args, 1.0 / 64, FAKE + (6 << 30), need - 1, None, ctypes.byref(chosen), None,
+                                None, None) == WORKSPACE
+    assert lib.gdn_tune_prefill(*args, 1.0 / 64, None, need, None, ctypes.byref(chosen), None, None,
                                 None) == WORKSPACE
-    assert lib.gdn_tune_prefill(*args, 1.0 / 64, None, need, None, ctypes.byref(chosen), None, None) == WORKSPACE
 
 
 def test_chunk_zero_rule(lib):
@@ -292,6 +298,15 @@ def test_chunk_zero_rule(lib):
     assert m(2, 2 * 600) == 64                       # two sequences: two passes
     assert gdn.prefill_method(1, 4096, 16, 32, 128, chunk=16) == 16  # explicit chunks as given
     assert gdn.prefill_method(1, 4096, 3, 32, 128) == 0              # rejected shape
+    # state rows per scan workgroup: 32 once 16-row slices need more than one
+    # pass over 256 CUs (N * HV * DV / 16 > 256), bf16 I/O with d >= 32 only
+    p = lambda n, T, hv=32, d=128, io=torch.bfloat16, c=0: gdn.prefill_plan(n, T, 16, hv, d, c, io)
+    assert p(1, 4096) == (64, 16) and p(2, 2 * 4096) == (64, 32)
+    assert p(1, 4096, hv=48) == (64, 32)                             # 384 slices of 16 rows
+    assert p(2, 2 * 4096, io=torch.float32) == (64, 16)              # fp32 I/O: 16 rows
+    assert p(64, 64 * 4, c=1) == (1, 0) and p(64, 64 * 4) == (1, 0)  # token by token: no scan
+    assert p(40, 40 * 100, d=16, hv=16) == (64, 16)                  # d = 16: 16 rows
+    assert p(1, 4096, hv=3) == (0, 0)                                 # rejected
 
 
 def test_binding_checks_shapes_before_calling():

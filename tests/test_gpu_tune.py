@@ -49,14 +49,17 @@ def test_tune_picks_fastest_passing_method(lens):
     note(f"tune prefill lens={lens[:2]}... n={len(lens)}")
     r = gdn.tune_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
                          initial_state=d["initial_state"])
-    print(f"[tune] n={len(lens)} T={sum(lens)}: chose {r['chunk']}; ms {r['ms']}; err {r['err']}", flush=True)
+    print(f"[tune] n={len(lens)} T={sum(lens)}: chose {r['method']}; ms {r['ms']}; err {r['err']}", flush=True)
     passing = {c: t for c, t in r["ms"].items() if t >= 0}
-    assert r["chunk"] in passing
+    assert r["method"] in passing
     assert all(0 <= r["err"][c] <= 1 / 64 for c in passing)
-    assert passing[r["chunk"]] == min(passing.values())
-    assert r["err"][64] == 0.0  # the reference against itself
+    assert passing[r["method"]] == min(passing.values())
+    assert r["err"]["64/16"] == 0.0  # the reference against itself
+    # 32 state rows per workgroup: the same MFMA sequence per element, the same bits
+    assert r["err"]["64/32"] == 0.0 and r["err"]["32/32"] == r["err"]["32/16"]
     assert gdn.tune_cache_size() == 1
     # chunk 0 now runs the chosen method: its kernels, its bits
+    assert gdn.prefill_plan(len(lens), sum(lens), 16, 32, 128) == (r["chunk"], r["rows"])
     o0, f0, ran = _run(d, 0)
     oc, fc, _ = _run(d, r["chunk"])
     assert KERNEL_OF[r["chunk"]] in ran and len({"token_scan", "scan"} & ran) == 1
@@ -67,15 +70,17 @@ def test_tune_picks_fastest_passing_method(lens):
 
 
 def test_tune_gate_rejects_what_differs():
-    """With a zero tolerance only the reference (chunk 64) can pass: every
-    other method rounds differently, so it is rejected and never timed."""
+    """With a zero tolerance only chunk 64 can pass: the reference (16 rows
+    per scan workgroup) and 32 rows, which computes the same bits. Every other
+    chunk rounds differently, so it is rejected and never timed."""
     _, d = _inputs([200, 37], seed=gs.SEED_BASE + 710)
     note("tune prefill with gate_tol = 0")
     r = gdn.tune_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
                          initial_state=d["initial_state"], gate_tol=0.0)
-    print(f"[tune] gate 0: chose {r['chunk']}; ms {r['ms']}; err {r['err']}", flush=True)
+    print(f"[tune] gate 0: chose {r['method']}; ms {r['ms']}; err {r['err']}", flush=True)
     assert r["chunk"] == 64
-    for c in (32, 16, 1):
+    assert r["err"]["64/32"] == 0 and r["ms"]["64/32"] > 0
+    for c in ("32/16", "32/32", "16/16", "16/32", "1"):
         assert r["err"][c] > 0 and r["ms"][c] == -1
 
 
@@ -89,13 +94,15 @@ def test_tune_cache_file_steers_chunk_zero(tmp_path):
     path = tmp_path / "tune.txt"
     gdn.tune_cache_save(str(path))
     fields = path.read_text().split()
-    assert len(fields) == 12 and fields[0] == "gdn-tune-v1" and int(fields[-1]) == r["chunk"]
+    assert len(fields) == 13 and fields[0] == "gdn-tune-v2"
+    assert (int(fields[-2]), int(fields[-1])) == (r["chunk"], r["rows"])
     forced = 16 if r["chunk"] != 16 else 32
-    path.write_text(" ".join(fields[:-1] + [str(forced)]) + "\n")
+    path.write_text(" ".join(fields[:-2] + [str(forced), "32"]) + "\n")
     gdn.tune_cache_clear()
     _, _, ran = _run(d, 0)
     assert ran == {"token_scan"}  # T = 30 <= 32: the rule without a choice
     assert gdn.tune_cache_load(str(path)) == 1
+    assert gdn.prefill_plan(2, 30, 16, 32, 128) == (forced, 32)
     o0, f0, ran = _run(d, 0)
     oc, fc, _ = _run(d, forced)
     assert "scan" in ran and "token_scan" not in ran
