@@ -27,8 +27,10 @@ def _decode_case(batch, io_dtype, seed_off=0, d=128, hk=16, hv=32, scale=1.0):
 
 
 @pytest.mark.parametrize("io_dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("batch", [1, 2, 7, 64])
+@pytest.mark.parametrize("batch", [1, 2, 4, 7, 8, 16, 32, 64])
 def test_decode_matches_oracle(batch, io_dtype):
+    """The decode workload's batch sizes (1 to 64, and 7), HK = 16, HV = 32,
+    d = 128: every output and state element against the oracle."""
     inp, s0 = _decode_case(batch, io_dtype)
     note(f"decode batch={batch} io={io_dtype}")
     d = device_inputs(inp)
