@@ -189,12 +189,14 @@ struct PrepSmem {
     static constexpr size_t off_A = 0;
     static constexpr size_t off_T = off_A + (size_t)C * LDC * sizeof(float);
     static constexpr size_t at_end = off_T + (size_t)C * LDC * sizeof(float);
+    // Gate prefixes c, b and b gamma of two value heads ([2][C] each): the
+    // first two heads' are computed while K and Q load.
     static constexpr size_t off_c = ((kq_end > at_end ? kq_end : at_end) + 15) & ~(size_t)15;
-    static constexpr size_t off_b = off_c + (size_t)C * sizeof(double);
-    static constexpr size_t off_bg = off_b + (size_t)C * sizeof(float);
+    static constexpr size_t off_b = off_c + 2 * (size_t)C * sizeof(double);
+    static constexpr size_t off_bg = off_b + 2 * (size_t)C * sizeof(float);
     // Chunk location when the kernel schedules itself: sequence ends and
     // lengths (256 each), 4 wave partials and 4 results.
-    static constexpr size_t off_loc = off_bg + (size_t)C * sizeof(float);
+    static constexpr size_t off_loc = off_bg + 2 * (size_t)C * sizeof(float);
     static constexpr size_t bytes = off_loc + (2 * 256 + 8) * sizeof(int);
 };
 
@@ -296,16 +298,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
     const int g4 = lane >> 4, ln = lane & 15;
     const size_t ld = (size_t)hk * DK;
 
-    // The inputs of a chunk starting at token tb: its K and Q rows (16 bytes
-    // per thread and pass) and, wave 0, the gate inputs of its tokens for up
-    // to kGatePrefetch value heads of the group. Rows are clamped into
-    // [0, T); rows past the chunk are masked where they are used. All loads
-    // are issued before any is waited for.
+    // The inputs of a chunk starting at token tb: waves 0 and 1 first load
+    // the gate inputs of its tokens for value head `wave` of the group (their
+    // prefix sums are formed while the rest arrives), then every thread its
+    // K and Q rows (16 bytes per pass). Rows are clamped into [0, T); rows
+    // past the chunk are masked where they are used. All loads are issued
+    // before any is waited for.
     constexpr int NIT = (C * VPR + 255) / 256;
-    constexpr int kGatePrefetch = 2;
+    constexpr int kGatePrefetch = 2;  // value heads whose prefix is formed early, one per wave
     Vec16 kr[NIT], qr[NIT];
-    float gx_pre[kGatePrefetch], gb_pre[kGatePrefetch];
+    float gx_pre = 0.f, gb_pre = 0.f;
     auto load_inputs = [&](int tb) {
+        if (wave < kGatePrefetch) {
+            const size_t gi = (size_t)min(tb + lane, total_tokens - 1) * hv + kh * group + min(wave, group - 1);
+            gx_pre = gate_load(gate_g, gi);
+            gb_pre = gate_load(gate_b, gi);
+        }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int i = min(tid + 256 * it, C * VPR - 1);
@@ -313,15 +321,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
             const size_t src = (size_t)min(tb + r, total_tokens - 1) * ld + (size_t)kh * DK + cv * EPV;
             kr[it] = ld16(k + src);
             qr[it] = ld16(q + src);
-        }
-        if (wave == 0) {
-            const size_t t = (size_t)min(tb + lane, total_tokens - 1);
-#pragma unroll
-            for (int hh = 0; hh < kGatePrefetch; ++hh) {
-                const size_t gi = t * hv + kh * group + min(hh, group - 1);
-                gx_pre[hh] = gate_load(gate_g, gi);
-                gb_pre[hh] = gate_load(gate_b, gi);
-            }
         }
     };
     // Most prefills are one sequence from token 0, where chunk ci starts at
@@ -386,6 +385,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
     }
     const size_t kq0 = ((size_t)ci * hk + kh) * (size_t)(C * DK);
     if (!guessed || t0 != t_guess) load_inputs(t0);
+
+    // Gate prefix sums c_t = g_1 + ... + g_t of value head hh (one wave;
+    // C <= 64) into prefix buffer hh % 2, and the chunk's gate record for the
+    // scan. Rows past the end of the sequence act as a = 1, b = 0. The sums
+    // are kept in fp64: every decay factor below is exp of a difference
+    // c_i - c_j, and where some g are huge (a decay that underflows to 0,
+    // g = -1e4) the sums reach -1e5 and more, where fp32 spacing (0.01) would
+    // wipe out the differences between nearby tokens.
+    auto gate_prefix = [&](int hh, float x, float bv) {
+        const bool valid = lane < len;
+        if (!valid) x = bv = 0.f;
+        double xd = x;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const double y = __shfl_up(xd, off);
+            if (lane >= off) xd += y;
+        }
+        const double last = __shfl(xd, C - 1);
+        if (lane < C) {
+            const int buf = hh & 1;
+            const float gam = exp2_hw(static_cast<float>(xd * kLog2eD));
+            sc[buf * C + lane] = xd * kLog2eD;
+            sb[buf * C + lane] = bv;
+            sbg[buf * C + lane] = bv * gam;
+            float *rec = gates + ((size_t)ci * hv + kh * group + hh) * (size_t)gate_record(C);
+            rec[lane] = exp2_hw(static_cast<float>((last - xd) * kLog2eD));
+            rec[C + lane] = scale * gam;
+            if (lane == C - 1) rec[2 * C] = exp2_hw(static_cast<float>(last * kLog2eD));
+        }
+    };
+    // the first value heads' prefixes, while K and Q are still arriving
+    if (wave < kGatePrefetch && wave < group) gate_prefix(wave, gx_pre, gb_pre);
 
     // ---- 1. K and Q rows into LDS (zero past the end of the sequence)
 #pragma unroll
@@ -475,48 +506,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
         const size_t mat0 = ch * (size_t)(C * C);
         const size_t w0 = ch * (size_t)(C * DK);
 
-        // gate prefix sums c_t = g_1 + ... + g_t (C <= 64: one wave); rows past
-        // the end of the sequence act as a = 1, b = 0
-        if (wave == 0) {
-            const bool valid = lane < len;
-            float x = 0.f, bv = 0.f;
-            if (hh < kGatePrefetch) {
-#pragma unroll
-                for (int i = 0; i < kGatePrefetch; ++i) {
-                    if (i == hh) {
-                        x = gx_pre[i];
-                        bv = gb_pre[i];
-                    }
-                }
-            } else {
-                x = gate_load(gate_g, (size_t)(t0 + (valid ? lane : 0)) * hv + h);
-                bv = gate_load(gate_b, (size_t)(t0 + (valid ? lane : 0)) * hv + h);
+        // the gate prefix of the heads beyond the first two (one wave)
+        if (hh >= kGatePrefetch) {
+            if (wave == 0) {
+                const int row = t0 + (lane < len ? lane : 0);
+                gate_prefix(hh, gate_load(gate_g, (size_t)row * hv + h), gate_load(gate_b, (size_t)row * hv + h));
             }
-            if (!valid) x = bv = 0.f;
-            // The prefix sums are kept in fp64: every decay factor below is
-            // exp of a difference c_i - c_j, and where some g are huge (a
-            // decay that underflows to 0, g = -1e4) the sums reach -1e5 and
-            // more, where fp32 spacing (0.01) would wipe out the differences
-            // between nearby tokens.
-            double xd = x;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const double y = __shfl_up(xd, off);
-                if (lane >= off) xd += y;
-            }
-            const double last = __shfl(xd, C - 1);
-            if (lane < C) {
-                const float gam = exp2_hw(static_cast<float>(xd * kLog2eD));
-                sc[lane] = xd * kLog2eD;
-                sb[lane] = bv;
-                sbg[lane] = bv * gam;
-                float *rec = gates + ch * (size_t)gate_record(C);
-                rec[lane] = exp2_hw(static_cast<float>((last - xd) * kLog2eD));
-                rec[C + lane] = scale * gam;
-                if (lane == C - 1) rec[2 * C] = exp2_hw(static_cast<float>(last * kLog2eD));
-            }
+            __syncthreads();
         }
-        __syncthreads();
+        const double *sc_h = sc + (hh & 1) * C;
+        const float *sb_h = sb + (hh & 1) * C;
+        const float *sbg_h = sbg + (hh & 1) * C;
 
         // A = strict_lower(b_i exp(c_i - c_j) (K K^T)_ij) into LDS (waves 0, 1);
         // P = lower(scale exp(c_i - c_j) (Q K^T)_ij) to fragments (waves 2, 3)
@@ -527,8 +527,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
             for (int r = 0; r < TS::NR; ++r) {
                 const int ti = TS::row(r);
                 const int i = 16 * ti + ln;
-                const double cI = sc[i];
-                const float mI = score_wave ? scale : sb[i];
+                const double cI = sc_h[i];
+                const float mI = score_wave ? scale : sb_h[i];
                 f32x4 val[NB];
 #pragma unroll
                 for (int tj = 0; tj < NB; ++tj) {
@@ -539,7 +539,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
                         for (int e = 0; e < 4; ++e) {
                             const int j = 16 * tj + 4 * g4 + e;
                             const bool keep = score_wave ? j <= i : j < i;
-                            const float dc = static_cast<float>(cI - sc[j]);  // fp64 difference, then fp32
+                            const float dc = static_cast<float>(cI - sc_h[j]);  // fp64 difference, then fp32
                             val[tj][e] = keep ? mI * exp2_hw(dc) * t[e] : 0.f;
                         }
                         if constexpr (!score_wave) *reinterpret_cast<f32x4 *>(sA + i * LDC + 16 * tj + 4 * g4) = val[tj];
@@ -636,8 +636,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
             for (int e = 0; e < MC::KPL; ++e) {
                 const int j = acc_k<MC>(kb, g4, e);
                 const float t = (j >> 4) <= rt ? sT[i * LDC + j] : 0.f;
-                frag_set<MC>(fr, e, t * sb[j]);
-                frag_set<MC>(fw, e, t * sbg[j]);
+                frag_set<MC>(fr, e, t * sb_h[j]);
+                frag_set<MC>(fw, e, t * sbg_h[j]);
             }
             *reinterpret_cast<typename MC::Frag *>(tbmat + mat0 + frag_off<MC>(f, lane)) = fr;
             sBW[f * 64 + lane] = fw;
