@@ -3,7 +3,9 @@ and lengths (empty and ragged ones included), head layouts, head sizes,
 dtypes, methods (chunk 0, 1, 16, 32, 64), scale, initial states or none,
 and gates with occasional extreme decays (g = -1e4, a = 0) and b = 0 or 1.
 Every case is drawn from its own seed, printed before it runs, and held to
-the usual bars (bf16 2e-2, fp32 1e-4 max-rel)."""
+the usual bars (bf16 2e-2, fp32 1e-4 max-rel). A second set draws batches
+large enough that the chunked scan takes 32 state rows per workgroup
+(N * HV * DV / 16 > 256, bf16 I/O)."""
 
 import numpy as np
 import pytest
@@ -54,3 +56,28 @@ def test_random_configuration(seed):
     ef = rel_err(fg, f_ref)
     print(f"[parity] random {desc} out_err={eo:.3e} state_err={ef:.3e}", flush=True)
     assert eo <= tol(inp.io_dtype) and ef <= tol(inp.io_dtype), desc
+
+
+def _wide_case(seed):
+    rng = np.random.default_rng(seed)
+    hk, hv = [(2, 8), (4, 16), (8, 32), (16, 48)][int(rng.integers(0, 4))]
+    d = int(rng.choice([32, 64, 128]))
+    one_pass = 256 // (hv * d // 16)
+    n = int(rng.integers(one_pass + 1, one_pass + 12))
+    lens = [int(x) for x in rng.integers(0, 200, n)]
+    chunk = int(rng.choice([0, 16, 32, 64]))
+    init = bool(rng.random() < 0.7)
+    inp = gs.make_inputs(lens, hk, hv, d, d, seed=seed, io_dtype="bf16", gate_dtype="f32", init_state=init)
+    desc = f"seed={seed} n={n} hk={hk} hv={hv} d={d} chunk={chunk} init={init} T={sum(lens)}"
+    return inp, chunk, desc
+
+
+@pytest.mark.parametrize("seed", range(7000, 7012))
+def test_random_wide_batch(seed):
+    inp, chunk, desc = _wide_case(seed)
+    note(f"wide {desc}")
+    o, f = run_prefill(inp, chunk=chunk)
+    o_ref, f_ref = oracle_ref(inp)
+    eo, ef = rel_err(to_f64(o), o_ref), rel_err(to_f64(f), f_ref)
+    print(f"[parity] random wide {desc} out_err={eo:.3e} state_err={ef:.3e}", flush=True)
+    assert eo <= tol("bf16") and ef <= tol("bf16"), desc
