@@ -80,7 +80,7 @@ const char *gdn_status_string(int32_t status) {
     case GDN_OK: return "ok";
     case GDN_ERR_NULL_ARG: return "a required pointer argument is NULL";
     case GDN_ERR_BAD_SHAPE: return "invalid sizes (negative, zero where not allowed, or hv not a multiple of hk)";
-    case GDN_ERR_UNSUPPORTED: return "head size, chunk size or dtype not supported by this build";
+    case GDN_ERR_UNSUPPORTED: return "head size, chunk size or dtype not supported by the library";
     case GDN_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than gdn_prefill_workspace_size()";
     case GDN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case GDN_ERR_ALIAS: return "output buffer overlaps an input buffer";
