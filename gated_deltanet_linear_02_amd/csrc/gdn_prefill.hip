@@ -1042,8 +1042,9 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         //   wave 1     an L2 touch of the chunk kTouchAhead ahead: the 16
         //              workgroups of the query/key head split that chunk's
         //              operands (Q, K^T, and Tb, P, W of each value head of
-        //              the group; 128-byte lines) 64 lines each, one line per
-        //              lane, so that the workgroups' own loads later hit L2;
+        //              the group) and its V rows (128-byte lines) 64 lines
+        //              each, one line per lane, so that the workgroups' own
+        //              loads later hit L2;
         //              the value is only kept alive until the stage is
         //              refilled;
         //   waves 2-3  16-row slices: the chunk's V rows 32 (q - 2) .. + 31
@@ -1066,11 +1067,24 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             const size_t kq = (size_t)(c0 + cc) * hk + kh;
             const size_t ch0 = (size_t)(c0 + cc) * hv + (size_t)kh * group;
             const int per_head = 2 * kRunM + kRunQ;
-            const int nlines = 8 * (2 * kRunQ + group * per_head);
+            const int nops = 8 * (2 * kRunQ + group * per_head);
+            // then the chunk's V rows of each value head of the group, from
+            // the caller's tensor (cold in HBM, unlike the workspace the
+            // preparation kernel has just written)
+            constexpr int kLinesPerRow = DK * (int)sizeof(E) >= 128 ? DK * (int)sizeof(E) / 128 : 1;
+            const int nlines = nops + C * group * kLinesPerRow;
             // 32-row slices: half the workgroups per query/key head, touching
             // from waves 1-3
             const int part = R == 16 ? within : within * 3 + (q - 1);
             const int line = (part * 64 + lane) % nlines;
+            if (line >= nops) {
+                const int vl = line - nops, per_tok = group * kLinesPerRow;
+                const ChunkRef rc = chunk(cc);
+                const int t = min(vl / per_tok, rc.clen - 1), rem = vl % per_tok;
+                const int hh = rem / kLinesPerRow, hf = rem - hh * kLinesPerRow;
+                return reinterpret_cast<const f32x4 *>(v + ((size_t)(rc.tok0 + t) * hv + (size_t)kh * group + hh) * DK +
+                                                       (size_t)hf * (128 / sizeof(E)));
+            }
             int r = line >> 3;
             const size_t off = (size_t)(line & 7) * (128 / sizeof(E));
             const E *run;
