@@ -321,37 +321,56 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(threads: int):
-    """The fp64 oracle on the host cores: the full 4096-token prefill (all 32
-    value heads) plus one decode step at batch 64, with `threads` threads and
-    (the prefill only) with one."""
-    import gdn_synth as gs
+def cpu_baseline(pre, dec, s_dec, threads: int, one_thread: bool = True):
+    """The fp64 oracle on the host cores on the very inputs the GPU step uses:
+    the full 4096-token prefill (all 32 value heads) plus one decode step at
+    batch 64 from the initial decode states, with `threads` threads and (the
+    prefill only, when `one_thread`) with one. Returns the baseline record and
+    the oracle's results, which are the bench's parity reference."""
     import oracle
-    inp = gs.workload("prefill")
-    w = inp.widened()
+    w = pre.widened()
     t0 = time.perf_counter()
-    oracle.scan(w["q"], w["k"], w["v"], w["g"], w["beta"], w["cu_seqlens"], threads=threads)
+    o_ref, f_ref = oracle.scan(w["q"], w["k"], w["v"], w["g"], w["beta"], w["cu_seqlens"], threads=threads)
     t_pre = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.scan(w["q"], w["k"], w["v"], w["g"], w["beta"], w["cu_seqlens"], threads=1)
-    t_pre1 = time.perf_counter() - t0
-    dec = gs.workload("decode", batch=B_DECODE)
+    t_pre1 = None
+    if one_thread:
+        t0 = time.perf_counter()
+        oracle.scan(w["q"], w["k"], w["v"], w["g"], w["beta"], w["cu_seqlens"], threads=1)
+        t_pre1 = time.perf_counter() - t0
     wd = dec.widened()
-    s0 = gs.decode_state(B_DECODE, HV, D, D, seed=gs.SEED_BASE + 101).astype(np.float64)
     t0 = time.perf_counter()
-    oracle.decode_step(wd["q"], wd["k"], wd["v"], wd["g"], wd["beta"], s0, threads=threads)
+    od_ref, sd_ref = oracle.decode_step(wd["q"], wd["k"], wd["v"], wd["g"], wd["beta"],
+                                        s_dec.astype(np.float64), threads=threads)
     t_dec = time.perf_counter() - t0
-    return {
+    rec = {
         "value": (T_PREFILL + B_DECODE) / (t_pre + t_dec), "unit": "tokens/s", "cores": threads,
         "kind": "oracle",
         "sample": f"one full step: prefill T={T_PREFILL} (all {HV} value heads) + decode B={B_DECODE}, "
                   f"fp64 token scan in C; prefill {t_pre:.2f} s, decode {t_dec * 1e3:.1f} ms",
         "prefill_tokens_per_s": T_PREFILL / t_pre,
         "decode_tokens_per_s": B_DECODE / t_dec,
-        "prefill_tokens_per_s_one_thread": T_PREFILL / t_pre1,
+        "prefill_tokens_per_s_one_thread": None if t_pre1 is None else T_PREFILL / t_pre1,
         "cpu_model": _cpu_model(),
         "host_cpus": os.cpu_count(),
     }
+    return rec, dict(prefill_out=o_ref, prefill_state=f_ref, decode_out=od_ref, decode_state=sd_ref)
+
+
+# Parity bars of the bench's gate, as max |gpu - ref| / max |ref| over each
+# tensor: bf16 outputs 2e-2; the prefill's final state 2e-2 (bf16 MFMA
+# operands in bf16 I/O); the fp32 decode states 1e-4.
+PARITY_BARS = {"prefill_out": 2e-2, "prefill_state": 2e-2, "decode_out": 2e-2, "decode_state": 1e-4}
+
+
+def parity_errors(gpu: dict, ref: dict) -> dict:
+    errs = {}
+    for key, r in ref.items():
+        x = gpu[key]
+        den = float(np.abs(r).max())
+        diff = np.abs(x - r)
+        e = float(diff.max()) / den if den > 0 else float(np.abs(x).max())
+        errs[key] = e if np.isfinite(x).all() else float("inf")
+    return errs
 
 
 # Short prefills: (sequences, tokens each). One sequence around the crossover,
@@ -1186,13 +1205,34 @@ def main():
                     final_state=s["fin"], out=s["out"], workspace=s["ws"])
         gdn.decode_step(s["dq"], s["dk"], s["dv"], s["dg"], s["db"], s["state"], out=s["dout"])
 
-    # Sanity check only (parity against the oracle is the tests' job): one
-    # step must write finite outputs and states.
-    step(sets[0])
-    torch.cuda.synchronize()
+    # ---- verify before timing: the oracle on the same inputs (this is also
+    # the CPU baseline), against one untimed GPU step from fresh decode states.
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    threads = max(1, min(16, ncpu))
+    print("[bench] oracle reference (and CPU baseline)", file=sys.stderr, flush=True)
+    cpu_rec, ref = cpu_baseline(pre, dec, s_dec, threads, one_thread=not args.no_cpu_baseline)
     s0 = sets[0]
-    if not all(bool(torch.isfinite(s0[x]).all()) for x in ("out", "fin", "dout", "state")):
-        print(json.dumps({"metric": METRIC, "error": "non-finite output"}))
+    chk_state = torch.from_numpy(s_dec).to(dev)
+    gdn.prefill(s0["q"], s0["k"], s0["v"], s0["g"], s0["beta"], s0["cu"], chunk=CHUNK,
+                final_state=s0["fin"], out=s0["out"], workspace=s0["ws"])
+    gdn.decode_step(s0["dq"], s0["dk"], s0["dv"], s0["dg"], s0["db"], chk_state, out=s0["dout"])
+    torch.cuda.synchronize()
+
+    def f64(t):
+        return t.detach().to("cpu", torch.float64).numpy()
+
+    errs = parity_errors({"prefill_out": f64(s0["out"]), "prefill_state": f64(s0["fin"]),
+                          "decode_out": f64(s0["dout"]), "decode_state": f64(chk_state)}, ref)
+    parity = {"max_rel_err": errs, "bars": PARITY_BARS,
+              "pass": all(errs[k] <= PARITY_BARS[k] for k in PARITY_BARS),
+              "reference": "fp64 oracle, every token and value head of the timed step's inputs"}
+    del chk_state
+    if not parity["pass"]:
+        print(json.dumps({"metric": METRIC, "error": "parity gate failed: the GPU step does not match "
+                          "the oracle; no throughput is reported", "parity": parity}), flush=True)
         sys.exit(1)
 
     stream = torch.cuda.current_stream(dev)
@@ -1260,15 +1300,27 @@ def main():
     dec_bytes = decode_bytes_per_step()
     dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
 
-    roof = {"bound": "mfma", "kernel": "gdn_scan_kernel", "achieved": scan_tflops,
-            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": scan_tflops / PEAK_BF16_TFLOPS,
-            "traffic": measured_traffic("gdn_scan_kernel"),
-            "algorithmic_per_launch": scan_flops, "mean_launch_ms": scan_ms}
+    sched_ms = kt["schedule"]["mean_ms"] if kt["schedule"]["count"] else 0.0
+    prefill_kernel_ms = sched_ms + prep_ms + scan_ms
+    prefill_all_flops = scan_flops + prep_flops
+    pre_tflops = prefill_all_flops / (prefill_kernel_ms * 1e-3) / 1e12
+    t_prep, t_scan = measured_traffic("gdn_prep_kernel"), measured_traffic("gdn_scan_kernel")
+    # The headline is the whole prefill (its kernels, launched back to back on
+    # one stream, as one launch of the layer): the chunked form's algorithmic
+    # MFMA flops per prefill over the summed mean durations of its kernels.
+    roof = {"bound": "mfma", "kernel": "prefill (gdn_prep_kernel + gdn_scan_kernel)", "achieved": pre_tflops,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": pre_tflops / PEAK_BF16_TFLOPS,
+            "traffic": None if t_prep is None or t_scan is None else t_prep + t_scan,
+            "algorithmic_per_launch": prefill_all_flops, "mean_launch_ms": prefill_kernel_ms,
+            "kernel_mean_ms": {"schedule": sched_ms, "prep": prep_ms, "scan": scan_ms},
+            "target_frac": 0.40}
+    roof_scan = {"bound": "mfma", "kernel": "gdn_scan_kernel", "achieved": scan_tflops,
+                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": scan_tflops / PEAK_BF16_TFLOPS,
+                 "traffic": t_scan, "algorithmic_per_launch": scan_flops, "mean_launch_ms": scan_ms}
     roof_dec = {"bound": "hbm", "kernel": "gdn_decode_kernel", "achieved": dec_gbs, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": dec_gbs / PEAK_HBM_GBS,
                 "traffic": measured_traffic("gdn_decode_kernel"),
                 "algorithmic_per_launch": dec_bytes, "mean_launch_ms": dec_ms}
-    prefill_all_flops = scan_flops + prep_flops
     res = {
         "metric": METRIC,
         "value": (T_PREFILL + B_DECODE) / (ms_step * 1e-3),
@@ -1287,6 +1339,7 @@ def main():
                    "prefill_tokens": T_PREFILL, "decode_batch": B_DECODE, "parallelism": "single GPU",
                    "buffer_copies": args.copies},
         "roofline": roof,
+        "roofline_scan": roof_scan,
         "roofline_decode": roof_dec,
         "prefill": {"tokens_per_s": T_PREFILL / (ms_pre * 1e-3), "ms": ms_pre,
                     "mfma_frac_all_kernels": prefill_all_flops / (ms_pre * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -1297,13 +1350,9 @@ def main():
         "step_ms_percentiles": {"p10": pct(10), "p50": pct(50), "p90": pct(90)},
         "kernel_source_hash": kernel_source_hash(),
     }
+    res["parity"] = parity
     if not args.no_cpu_baseline:
-        try:
-            ncpu = len(os.sched_getaffinity(0))
-        except AttributeError:
-            ncpu = os.cpu_count() or 1
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(max(1, min(16, ncpu)))
+        res["cpu_baseline"] = cpu_rec
     print(json.dumps(res), flush=True)
 
 

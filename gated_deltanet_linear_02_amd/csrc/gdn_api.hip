@@ -83,7 +83,7 @@ const char *gdn_status_string(int32_t status) {
     case GDN_ERR_UNSUPPORTED: return "head size, chunk size or dtype not supported by the library";
     case GDN_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than gdn_prefill_workspace_size()";
     case GDN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
-    case GDN_ERR_ALIAS: return "output buffer overlaps an input buffer";
+    case GDN_ERR_ALIAS: return "an output buffer or the workspace overlaps another buffer";
     case GDN_ERR_BAD_VALUE: return "a scalar argument is out of range (norm eps must be finite and >= 0)";
     case GDN_ERR_MISALIGNED: return "q, k, v, out or a state tensor does not start on a 16-byte boundary";
     default: return "unknown status";
@@ -220,6 +220,11 @@ static int32_t prefill_impl(const void *q, const void *k, const void *v, const v
     for (int i = 0; i < 7; ++i)
         if (overlaps(r_fin, inputs[i])) return GDN_ERR_ALIAS;
     if (overlaps(r_fin, span(workspace, L.total))) return GDN_ERR_ALIAS;
+    // The preparation kernel writes the workspace while other workgroups
+    // still read the inputs, so the workspace must not overlap any of them.
+    const Range r_ws = span(workspace, L.total);
+    for (int i = 0; i < 8; ++i)
+        if (overlaps(r_ws, inputs[i])) return GDN_ERR_ALIAS;
     if (final_state && initial_state && final_state != initial_state &&
         overlaps(r_fin, span(initial_state, state_bytes)))
         return GDN_ERR_ALIAS;

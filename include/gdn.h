@@ -64,7 +64,7 @@ typedef enum {
     GDN_ERR_UNSUPPORTED = 3, /* head size, chunk or dtype outside the built set */
     GDN_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
     GDN_ERR_HIP = 5,         /* a HIP runtime call or launch failed */
-    GDN_ERR_ALIAS = 6,       /* out overlaps an input */
+    GDN_ERR_ALIAS = 6,       /* an output or the workspace overlaps another buffer */
     GDN_ERR_BAD_VALUE = 7,   /* a scalar argument out of range (norm eps) */
     GDN_ERR_MISALIGNED = 8   /* q, k, v, out or a state not 16-byte aligned */
 } gdn_status;
@@ -102,6 +102,19 @@ int32_t gdn_prefill_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, i
 /*
  * Chunked prefill over N packed variable-length sequences.
  *
+ * What it computes: the gated delta rule above over every token of every
+ * sequence, writing o_t for each token and each sequence's state after its
+ * last token. The evaluation is the block form that the first page sets
+ * beside the token-by-token one: the same computation reorganised into
+ * chunks so that matrix products and token-level parallelism appear
+ * ("Optimiser l'inference sur appareil pour Apple Silicon", section "Qwen
+ * cree trois formes de charges de travail distinctes"). The state is carried
+ * across chunks on chip and handed between calls through initial_state and
+ * final_state, so that a long prompt can be fed as fragments whose final
+ * state seeds the next (same page, section "Limiter la memoire temporaire
+ * grace au decoupage des prompts"); the state stays fp32 (section "Maintenir
+ * l'etat recurrent sur la puce").
+ *
  * cu_seqlens   int32 [N + 1] DEVICE array of token offsets: sequence n owns
  *              tokens [cu_seqlens[n], cu_seqlens[n+1]). It is read only on the
  *              device. Offsets are clamped into [0, total_tokens] and made
@@ -129,7 +142,9 @@ int32_t gdn_prefill_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, i
  *              cu_seqlens or the states (GDN_ERR_ALIAS).
  * workspace    device scratch of at least gdn_prefill_workspace_size(...)
  *              bytes, 256-byte aligned; contents need not be initialised and
- *              are meaningless afterwards. Calls on different streams need
+ *              are meaningless afterwards. It must not overlap q, k, v, g,
+ *              beta, cu_seqlens, the norm weight or the states
+ *              (GDN_ERR_ALIAS). Calls on different streams need
  *              different workspaces. Token by token (chunk 1, or chunk 0
  *              choosing it) uses none; it may then be NULL. The size for
  *              chunk 0 covers whichever method it picks.
@@ -145,6 +160,15 @@ int32_t gdn_prefill(const void *q, const void *k, const void *v,
 /*
  * One decode step: one new token for each of `batch` sequences, updating
  * their resident fp32 states in place.
+ *
+ * What it computes: one application of the gated delta rule above per
+ * (sequence, value head), S <- a S (I - b k k^T) + b v k^T and o = scale S q,
+ * with the new state written over the old one. Decode produces one new row
+ * per step, and its throughput is set by the bytes moved per token
+ * ("Optimiser l'inference sur appareil pour Apple Silicon", section
+ * "Decodage : minimiser les octets deplaces par token"): each state is read
+ * once and written once, and the recurrent update is one fused step (section
+ * "Reduire le trafic intermediaire et d'etat").
  *
  * state        fp32 [num_slots][hv][dv][dk], read and written in place.
  * state_slots  int32 [batch] DEVICE array: sequence b uses state slot
@@ -166,7 +190,11 @@ int32_t gdn_decode_step(const void *q, const void *k, const void *v,
 /*
  * The same two calls with two options: how states are stored, and the
  * layer's output normalisation. With state_dtype GDN_F32 and norm_weight NULL
- * they are gdn_prefill and gdn_decode_step.
+ * they are gdn_prefill and gdn_decode_step, and compute what those compute
+ * (prefill: "Qwen cree trois formes de charges de travail distinctes" and
+ * "Limiter la memoire temporaire grace au decoupage des prompts"; decode:
+ * "Decodage : minimiser les octets deplaces par token", all on "Optimiser
+ * l'inference sur appareil pour Apple Silicon").
  *
  * state_dtype  GDN_F32 or GDN_BF16: the element type of initial_state,
  *              final_state (prefill) and state (decode), whose layouts are

@@ -124,6 +124,11 @@ def test_prefill_argument_checks(lib):
     assert _prefill(lib, out=FAKE + (4 << 30) + 16) == ALIAS
     # final state overlapping q
     assert _prefill(lib, sf=FAKE + 128) == ALIAS
+    # the workspace overlapping an input: q, v, cu_seqlens, the initial state
+    assert _prefill(lib, ws=FAKE + 256) == ALIAS
+    assert _prefill(lib, ws=FAKE + (2 << 30) - 256) == ALIAS
+    assert _prefill(lib, ws=FAKE + (5 << 30)) == ALIAS
+    assert _prefill(lib, s0=FAKE + (8 << 30), ws=FAKE + (8 << 30) + 4096) == ALIAS
     # tensors read in 16-byte pieces must be 16-byte aligned (gates need not)
     assert _prefill(lib, q=FAKE + 8) == MISALIGNED
     assert _prefill(lib, out=FAKE + (6 << 30) + 2) == MISALIGNED

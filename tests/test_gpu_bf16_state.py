@@ -140,7 +140,7 @@ def test_prefill_bf16_state(chunk):
 
 def test_prefill_bf16_state_4k():
     """The prefill workload (T = 4096, HK = 16, HV = 32, d = 128) with a bf16
-    final state, on sampled heads; output identical to the fp32-state call
+    final state, every value head; output identical to the fp32-state call
     (the state is rounded only once it is stored)."""
     inp = gs.workload("prefill", io_dtype="bf16")
     note("prefill bf16 state T=4096")
@@ -152,10 +152,9 @@ def test_prefill_bf16_state_4k():
     assert f16.dtype == torch.bfloat16
     assert torch.equal(o16, o32)
     assert torch.equal(f16, f32.to(torch.bfloat16))
-    heads = [0, 31]
     w = inp.widened()
-    _, f_ref = oracle.scan(w["q"], w["k"], w["v"], w["g"], w["beta"], w["cu_seqlens"], heads=heads)
-    ef = rel_err(to_f64(f16[:, heads]), f_ref[:, heads])
+    _, f_ref = oracle.scan(w["q"], w["k"], w["v"], w["g"], w["beta"], w["cu_seqlens"])
+    ef = rel_err(to_f64(f16), f_ref)
     print(f"[parity] prefill bf16 state T=4096 state_err={ef:.3e}", flush=True)
     assert ef <= TOL_BF16
 

@@ -2,8 +2,8 @@
 prompts) on the GPU against the fp64 oracle.
 
 The same bars as the chunked path, max |gpu - ref| / max |ref| per tensor:
-bf16 I/O <= 2e-2, fp32 I/O <= 1e-4. Large workloads are compared on sampled
-value heads, each computed by the oracle in full.
+bf16 I/O <= 2e-2, fp32 I/O <= 1e-4. Every workload is compared over all of
+its value heads and tokens.
 """
 
 import numpy as np
@@ -72,7 +72,7 @@ def test_token_scan_prefill_4k(io):
     inp = gs.workload("prefill", io_dtype=io)
     note(f"token scan T=4096 io={io}")
     o, f = run_prefill(inp, chunk=1)
-    _check(inp, o, f, heads=[0, 7, 31], label="T=4096")
+    _check(inp, o, f, label="T=4096")
 
 
 def test_token_scan_varlen_f32():
@@ -80,7 +80,7 @@ def test_token_scan_varlen_f32():
     inp = gs.workload("varlen", io_dtype="f32")
     note(f"token scan varlen lens={np.diff(inp.cu_seqlens).tolist()}")
     o, f = run_prefill(inp, chunk=1)
-    _check(inp, o, f, heads=[3, 30], label="varlen")
+    _check(inp, o, f, label="varlen")
 
 
 def test_token_scan_equals_chunked_fp32():
