@@ -13,6 +13,9 @@ Entry points (same names as the C ABI, without the ``gdn_`` prefix):
     gdn_decode_step_ex: states stored in bf16 with fp32 arithmetic, and the
     output rows RMS-normalised, times one weight per value channel)
     prefill_workspace_size(...)
+    prefill_noalloc(q, k, v, g, beta, cu_seqlens, out=, final_state=, ...)
+        -> gdn_prefill_noalloc: the workspace is the library's own fixed
+        device array (nothing is allocated; out and states must be given)
     tune_prefill(q, k, v, g, beta, cu_seqlens, ...) -> chosen method, per-candidate
         times and gate errors (cached for prefill's chunk 0);
     tune_cache_clear / tune_cache_size / tune_cache_save / tune_cache_load
@@ -29,7 +32,7 @@ from typing import Dict, Optional, Tuple
 import torch
 
 __all__ = [
-    "GdnError", "lib_path", "load", "prefill", "decode_step", "prefill_workspace_size", "prefill_method",
+    "GdnError", "lib_path", "load", "prefill", "prefill_noalloc", "decode_step", "prefill_workspace_size", "prefill_method",
     "prefill_plan", "tune_prefill", "method_name", "TUNE_CANDIDATES", "tune_cache_clear", "tune_cache_size",
     "tune_cache_save", "tune_cache_load", "timing_start", "timing_stop", "abi_version", "KERNEL_KINDS",
 ]
@@ -82,6 +85,9 @@ def load():
         L.gdn_prefill.restype = i32
         L.gdn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
                                   f32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.gdn_prefill_noalloc.restype = i32
+        L.gdn_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
+                                          f32, i32, i32, vp, vp, vp, vp]
         L.gdn_prefill_ex.restype = i32
         L.gdn_prefill_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
                                      f32, i32, i32, vp, vp, i32, vp, f32, vp, vp, sz, vp]
@@ -263,6 +269,37 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
             _ptr(out), _ptr(workspace), ws_bytes, _stream(dev, stream))
     _check(status)
     return out, final_state
+
+
+def prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                    cu_seqlens: torch.Tensor, *, out: torch.Tensor, final_state: Optional[torch.Tensor] = None,
+                    initial_state: Optional[torch.Tensor] = None, chunk: int = 0, scale: float = 1.0,
+                    stream=None) -> None:
+    """``gdn_prefill_noalloc``: ``prefill`` with fp32 states and no
+    normalisation, using the library's fixed device workspace
+    (GDN_NOALLOC_SCRATCH_BYTES per GPU) instead of one from the caller.
+    Nothing is allocated here either: ``out`` must be given, and the final
+    state is written only if ``final_state`` is. Calls that may overlap on one
+    GPU share that workspace and must be serialised by the caller."""
+    T, hk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    N = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise TypeError("cu_seqlens must be a 1-d int32 tensor")
+    _expect("k", k, (T, hk, dk), q.dtype)
+    _expect("v", v, (T, hv, dv), q.dtype)
+    _expect("g", g, (T, hv))
+    _expect("beta", beta, (T, hv), g.dtype)
+    _expect("out", out, (T, hv, dv), q.dtype)
+    for name, st in (("initial_state", initial_state), ("final_state", final_state)):
+        _expect(name, st, (N, hv, dv, dk), torch.float32)
+    dev = q.device
+    _on_device(dev, k=k, v=v, g=g, beta=beta, cu_seqlens=cu_seqlens, initial_state=initial_state,
+               final_state=final_state, out=out)
+    _check(load().gdn_prefill_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
+        hk, hv, dk, dv, chunk, float(scale), _dtype_code(q.dtype), _dtype_code(g.dtype),
+        _ptr(initial_state), _ptr(final_state), _ptr(out), _stream(dev, stream)))
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,

@@ -276,6 +276,79 @@ int32_t gdn_prefill_ex(const void *q, const void *k, const void *v, const void *
                         workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+// ------------------------------------------------- gdn_prefill_noalloc
+
+// The workspace of gdn_prefill_noalloc: one copy on every GPU the library
+// runs on, held until the process ends. In host code `scratch` names a
+// host-side stand-in, not the device array: only the address that
+// hipGetSymbolAddress returns for the current device is ever used.
+static __device__ __align__(256) char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+struct ScratchPtrs {
+    std::mutex mu;
+    void *ptr[kMaxDevices] = {};
+};
+ScratchPtrs &scratch_ptrs() {
+    static ScratchPtrs s;
+    return s;
+}
+}  // namespace
+
+// The device address of `scratch` on the device of `stream` (the current
+// device for the null stream), looked up once per device with that device
+// current.
+static int32_t scratch_address(hipStream_t stream, void **out) {
+    int dev = -1, cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return GDN_ERR_HIP;
+    if (stream) {
+        hipDevice_t d;
+        if (hipStreamGetDevice(stream, &d) != hipSuccess) return GDN_ERR_HIP;
+        dev = (int)d;
+    } else {
+        dev = cur;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return GDN_ERR_UNSUPPORTED;
+    ScratchPtrs &S = scratch_ptrs();
+    std::lock_guard<std::mutex> lk(S.mu);
+    if (!S.ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return GDN_ERR_HIP;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p) return GDN_ERR_HIP;
+        S.ptr[dev] = p;
+    }
+    *out = S.ptr[dev];
+    return GDN_OK;
+}
+
+extern "C" {
+
+int32_t gdn_prefill_noalloc(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                            const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                            int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
+                            float scale, int32_t io_dtype, int32_t gate_dtype,
+                            const float *initial_state, float *final_state, void *out, void *stream) {
+    const int32_t sc = check_prefill_shape(num_seqs, total_tokens, hk, hv, dk, dv, chunk, io_dtype, gate_dtype);
+    if (sc != GDN_OK) return sc;
+    // What this call needs (the token scan needs nothing), checked against
+    // the fixed maximum before any HIP call.
+    const Method m = method_for(chunk, 0, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype, gate_dtype);
+    const size_t need = m.chunk == 1 ? 0
+        : prefill_layout(num_seqs, total_tokens, hk, hv, dk, m.chunk, dtype_bytes(io_dtype)).total;
+    if (need > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_WORKSPACE;
+    void *ws = nullptr;
+    const int32_t sa = scratch_address(static_cast<hipStream_t>(stream), &ws);
+    if (sa != GDN_OK) return sa;
+    return prefill_impl(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, hk, hv, dk, dv, m.chunk, scale,
+                        io_dtype, gate_dtype, initial_state, final_state, GDN_F32, nullptr, 0.f, out, ws,
+                        GDN_NOALLOC_SCRATCH_BYTES, stream, m.rows);
+}
+
 // gdn_decode_step and gdn_decode_step_ex.
 static int32_t decode_impl(const void *q, const void *k, const void *v, const void *g, const void *beta,
                            int32_t batch, int32_t hk, int32_t hv, int32_t dk, int32_t dv, float scale,

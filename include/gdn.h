@@ -158,6 +158,33 @@ int32_t gdn_prefill(const void *q, const void *k, const void *v,
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gdn_prefill for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. The
+ * arguments are gdn_prefill's without the workspace; the workspace is a
+ * fixed array of GDN_NOALLOC_SCRATCH_BYTES in the library's device memory,
+ * one per GPU, which the library keeps from the first such call on a GPU
+ * until the process ends. The call itself allocates nothing.
+ *
+ * The array is found on the device of `stream` (the current device for the
+ * null stream). A call whose method needs more workspace than the array holds
+ * (gdn_prefill_workspace_size of the method gdn_prefill_method reports; the
+ * token-by-token method needs none) returns GDN_ERR_WORKSPACE before
+ * anything is enqueued; at HK = 16, HV = 32, d = 128 and chunk 64 the array
+ * holds one sequence of up to 5,312 bf16 tokens. Every call on a GPU
+ * shares that GPU's array, and the array keeps what the last call left in it
+ * (each call writes what it reads): calls that may overlap on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ * Results are those of gdn_prefill with the same method, bit for bit.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int32_t gdn_prefill_noalloc(const void *q, const void *k, const void *v,
+                            const void *g, const void *beta,
+                            const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                            int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
+                            float scale, int32_t io_dtype, int32_t gate_dtype,
+                            const float *initial_state, float *final_state, void *out, void *stream);
+
+/*
  * One decode step: one new token for each of `batch` sequences, updating
  * their resident fp32 states in place.
  *

@@ -337,3 +337,29 @@ def test_binding_checks_shapes_before_calling():
                     initial_state=torch.zeros((2, hv, d, d)))
     with pytest.raises(ValueError):
         gdn.decode_step(q, ok["k"], ok["v"][:4], ok["g"], ok["beta"], torch.zeros((T, hv, d, d)))
+
+
+@no_gpu
+def test_prefill_noalloc_host_checks(lib):
+    """The fixed-workspace entry point rejects, before any HIP call, shapes
+    the other entry points reject and a method whose workspace exceeds the
+    array (T = 32768 at chunk 64)."""
+    vp = ctypes.c_void_p
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30),
+                 beta=FAKE + (4 << 30), cu=FAKE + (5 << 30), n=1, T=32768, hk=16, hv=32, dk=128, dv=128,
+                 chunk=64, scale=1.0, io=BF16, gate=F32, s0=None, sf=None, out=FAKE + (6 << 30), stream=None)
+        a.update(kw)
+        return lib.gdn_prefill_noalloc(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["n"], a["T"],
+                                       a["hk"], a["hv"], a["dk"], a["dv"], a["chunk"], a["scale"], a["io"],
+                                       a["gate"], a["s0"], a["sf"], a["out"], a["stream"])
+    assert call() == WORKSPACE
+    assert call(hk=3, hv=4) == BAD_SHAPE
+    assert call(dk=96, dv=96) == UNSUPPORTED
+    assert call(chunk=8) == UNSUPPORTED
+    # the largest single bf16 sequence that fits at chunk 64 (5,312 tokens)
+    # and the next one
+    assert lib.gdn_prefill_workspace_size(1, 5312, 16, 32, 128, 128, 64, BF16) <= 128 << 20
+    assert lib.gdn_prefill_workspace_size(1, 5313, 16, 32, 128, 128, 64, BF16) > 128 << 20
+    assert call(T=5313) == WORKSPACE
