@@ -44,18 +44,32 @@ template <> __device__ __forceinline__ void load4<bf16>(const bf16 *p, float *ds
     dst[2] = static_cast<float>(x[2]); dst[3] = static_cast<float>(x[3]);
 }
 
-// Rows a lane group holds in the plain decode kernel, by storage type. A bf16
-// state row is half the bytes, so each lane takes four rows to keep as many
-// bytes in flight (measured at batch 64, d = 128: 26.0 us with four, 26.6
-// with two, 31.2 with one); fp32 rows stay at one per group (two or more
-// change nothing there).
+// Workgroup shape of the plain decode kernel, by storage type, measured at
+// batch 64, d = 128 (kernel us):
+//   fp32 states: 256 threads, one row per lane group (16 rows per
+//     workgroup), nontemporal loads and stores: 43.2-43.9 us. Two rows per
+//     group, or 512 and 1024 threads, are no faster; plain loads are slower
+//     (46.6-48.7 us).
+//   bf16 states: a whole (sequence, value head) state per workgroup, 1024
+//     threads with two rows per lane group, plain loads and nontemporal
+//     stores: 22.8-23.0 us. The same shape with nontemporal loads takes
+//     24.6 us; 512 threads with four rows per group 23.1 us; 256 threads with
+//     four rows per group (64 rows per workgroup) 26.0-26.4 us.
+// Half the bytes per row make a bf16 row's pieces small, so a lane takes
+// more rows and a workgroup more of the state to keep the bytes in flight.
+template <typename SE> constexpr int kDecodeThreads = 256;
+template <> constexpr int kDecodeThreads<bf16> = 1024;
 template <typename SE> constexpr int kDecodeRowsPerLane = 1;
-template <> constexpr int kDecodeRowsPerLane<bf16> = 4;
+template <> constexpr int kDecodeRowsPerLane<bf16> = 2;
 
 template <typename SE, int DK, int DV> struct DecodeShape {
     static constexpr int EPL = 8;                  // state elements per lane
     static constexpr int LPR = DK / EPL;           // lanes per state row
-    static constexpr int RPP = 256 / LPR;          // rows per pass of the workgroup
+    // threads per workgroup: at most what NRL rows per lane group of one
+    // state need (small d), at least one wave
+    static constexpr int TMAX = DV * LPR / kDecodeRowsPerLane<SE>;
+    static constexpr int THREADS = kDecodeThreads<SE> < TMAX ? kDecodeThreads<SE> : (TMAX < 64 ? 64 : TMAX);
+    static constexpr int RPP = THREADS / LPR;      // rows per pass of the workgroup
     // rows per lane group
     static constexpr int NRL = RPP >= DV ? 1 : (kDecodeRowsPerLane<SE> < DV / RPP ? kDecodeRowsPerLane<SE> : DV / RPP);
     static constexpr int ROWS = RPP * NRL;         // rows per workgroup
@@ -68,7 +82,8 @@ template <typename SE, int DK, int DV> struct DecodeShape {
 // per load; bf16 storage: one 16-byte piece at columns 8 lr .. 8 lr + 7.
 // Element j of the lane sits at column col(lr, j); columns 4m .. 4m + 3 of
 // the lane are consecutive in both layouts. States are read and written
-// once per step, so the accesses are nontemporal.
+// once per step, so the stores are nontemporal, and so are the fp32 loads;
+// bf16 rows load faster with the default policy (see kDecodeThreads).
 template <typename SE, int LPR> struct StateLane;
 template <int LPR> struct StateLane<float, LPR> {
     static __device__ __forceinline__ int col(int lr, int j) { return 4 * lr + 4 * LPR * (j >> 2) + (j & 3); }
@@ -91,7 +106,7 @@ template <int LPR> struct StateLane<float, LPR> {
 template <int LPR> struct StateLane<bf16, LPR> {
     static __device__ __forceinline__ int col(int lr, int j) { return 8 * lr + j; }
     static __device__ __forceinline__ void load(const bf16 *row, int lr, float (&s)[8]) {
-        const bf16x8 x = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(row + 8 * lr));
+        const bf16x8 x = *reinterpret_cast<const bf16x8 *>(row + 8 * lr);
 #pragma unroll
         for (int j = 0; j < 8; ++j) s[j] = static_cast<float>(x[j]);
     }
@@ -103,14 +118,27 @@ template <int LPR> struct StateLane<bf16, LPR> {
     }
 };
 
+// Sum of x over the LPR consecutive lanes of a row (LPR = 2, 4, 8 or 16; rows
+// aligned to LPR), on DPP lane moves (no trip through the LDS crossbar, as
+// a shuffle takes). Each step adds the value of a partner lane from a group
+// whose lanes all hold the same partial sum: quads by xor 1 and xor 2, then
+// half-rows by mirroring within 8 lanes, then rows by mirroring within 16.
+template <int Ctrl> __device__ __forceinline__ float dpp_mov(float y) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, y), Ctrl, 0xf, 0xf, false));
+}
+template <int LPR> __device__ __forceinline__ float row_sum(float x) {
+    static_assert(LPR == 2 || LPR == 4 || LPR == 8 || LPR == 16, "row width");
+    x += dpp_mov<0xB1>(x);                         // quad_perm [1, 0, 3, 2]: lane ^ 1
+    if constexpr (LPR >= 4) x += dpp_mov<0x4E>(x);   // quad_perm [2, 3, 0, 1]: lane ^ 2
+    if constexpr (LPR >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror: lane i <- 7 - i
+    if constexpr (LPR >= 16) x += dpp_mov<0x140>(x); // row_mirror: lane i <- 15 - i
+    return x;
+}
+
 // The arithmetic below is shared by both decode kernels (with explicit fused
 // multiply-adds, so that the compiler cannot contract it differently in
 // each): they leave bit-identical states.
-template <int LPR> __device__ __forceinline__ float lane_group_sum(float x) {
-#pragma unroll
-    for (int off = 1; off < LPR; off <<= 1) x += __shfl_xor(x, off);
-    return x;
-}
+template <int LPR> __device__ __forceinline__ float lane_group_sum(float x) { return row_sum<LPR>(x); }
 template <int LPR>
 __device__ __forceinline__ float row_dot(const float (&s)[8], const float (&x)[8]) {
     float acc = 0.f;
@@ -152,8 +180,11 @@ __device__ __forceinline__ void load_kq(const E *kp, const E *qp, int lr, float 
     }
 }
 
-template <typename E, typename G, typename SE, int DK, int DV>
-__global__ __launch_bounds__(256) void gdn_decode_kernel(
+// kSlots: state_slots given. Without them sequence b uses slot b (the host
+// has checked num_slots >= batch), so the kernel neither reads a slot nor
+// branches on one before its state loads.
+template <typename E, typename G, typename SE, int DK, int DV, bool kSlots>
+__global__ __launch_bounds__((DecodeShape<SE, DK, DV>::THREADS)) void gdn_decode_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const G *__restrict__ gate_g, const G *__restrict__ gate_b,
     SE *__restrict__ state, const int32_t *__restrict__ slots, int32_t num_slots,
@@ -173,9 +204,9 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(
     const int lr = tid % LPR;
     const int r0 = row0 + tid / LPR;  // this lane group's rows: r0 + p RPP, p < NRL
 
-    const int slot = slots ? slots[b] : b;
+    const int slot = kSlots ? slots[b] : b;
     E *o_row = out + ((size_t)b * hv + h) * DV;
-    if (slot < 0 || slot >= num_slots) {
+    if (kSlots && (slot < 0 || slot >= num_slots)) {
 #pragma unroll
         for (int p = 0; p < NRL; ++p)
             if (r0 + p * RPP < DV && lr == 0) o_row[r0 + p * RPP] = from_f32<E>(0.0f);
@@ -243,7 +274,7 @@ template <int DK, int DV> struct DecodeNormShape {
     static_assert(RPP * NRL >= DV, "every row has a lane group");
 };
 
-template <typename E, typename G, typename SE, int DK, int DV>
+template <typename E, typename G, typename SE, int DK, int DV, bool kSlots>
 __global__ __launch_bounds__((DecodeNormShape<DK, DV>::THREADS)) void gdn_decode_norm_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const G *__restrict__ gate_g, const G *__restrict__ gate_b,
@@ -264,9 +295,9 @@ __global__ __launch_bounds__((DecodeNormShape<DK, DV>::THREADS)) void gdn_decode
     const int lr = tid % LPR;
     const int r0 = tid / LPR;
 
-    const int slot = slots ? slots[b] : b;
+    const int slot = kSlots ? slots[b] : b;
     E *o_row = out + ((size_t)b * hv + h) * DV;
-    if (slot < 0 || slot >= num_slots) {  // the same for the whole workgroup
+    if (kSlots && (slot < 0 || slot >= num_slots)) {  // the same for the whole workgroup
 #pragma unroll
         for (int p = 0; p < NRL; ++p)
             if (r0 + p * RPP < DV && lr == 0) o_row[r0 + p * RPP] = from_f32<E>(0.0f);
@@ -322,22 +353,28 @@ __global__ __launch_bounds__((DecodeNormShape<DK, DV>::THREADS)) void gdn_decode
     }
 }
 
-template <typename E, typename G, typename SE, int D>
-static hipError_t launch_decode_t(const DecodeArgs &A, hipStream_t st) {
+template <typename E, typename G, typename SE, int D, bool kSlots>
+static hipError_t launch_decode_s(const DecodeArgs &A, hipStream_t st) {
     SE *state = static_cast<SE *>(A.state);
     if (A.norm_w) {
         typedef DecodeNormShape<D, D> SH;
         const dim3 grid((unsigned)A.batch * (unsigned)A.hv), block(SH::THREADS);
-        return launch_kernel(kDecodeNorm, gdn_decode_norm_kernel<E, G, SE, D, D>, grid, block, 0, st,
+        return launch_kernel(kDecodeNorm, gdn_decode_norm_kernel<E, G, SE, D, D, kSlots>, grid, block, 0, st,
                              (const E *)A.q, (const E *)A.k, (const E *)A.v,
                              (const G *)A.g, (const G *)A.beta, state, A.slots, A.num_slots,
                              (E *)A.out, A.hk, A.hv, A.scale, A.norm_w, A.norm_eps);
     }
-    const dim3 grid((unsigned)A.batch * (unsigned)A.hv * (unsigned)DecodeShape<SE, D, D>::SLICES), block(256);
-    return launch_kernel(kDecode, gdn_decode_kernel<E, G, SE, D, D>, grid, block, 0, st,
+    typedef DecodeShape<SE, D, D> SH;
+    const dim3 grid((unsigned)A.batch * (unsigned)A.hv * (unsigned)SH::SLICES), block(SH::THREADS);
+    return launch_kernel(kDecode, gdn_decode_kernel<E, G, SE, D, D, kSlots>, grid, block, 0, st,
                          (const E *)A.q, (const E *)A.k, (const E *)A.v,
                          (const G *)A.g, (const G *)A.beta, state, A.slots, A.num_slots,
                          (E *)A.out, A.hk, A.hv, A.scale);
+}
+
+template <typename E, typename G, typename SE, int D>
+static hipError_t launch_decode_t(const DecodeArgs &A, hipStream_t st) {
+    return A.slots ? launch_decode_s<E, G, SE, D, true>(A, st) : launch_decode_s<E, G, SE, D, false>(A, st);
 }
 
 template <typename E, typename G, typename SE>
@@ -380,21 +417,6 @@ hipError_t launch_decode(const DecodeArgs &A, hipStream_t st) {
 // of k and q (kNext tokens ahead); gates and v come in one load per lane for
 // 64 tokens at a time and are broadcast with readlane.
 
-// Sum of x over the LPR consecutive lanes of a row (LPR = 2, 4, 8 or 16; rows
-// aligned to LPR). Each step adds the value of a partner lane from a group
-// whose lanes all hold the same partial sum: quads by xor 1 and xor 2, then
-// half-rows by mirroring within 8 lanes, then rows by mirroring within 16.
-template <int Ctrl> __device__ __forceinline__ float dpp_mov(float y) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, y), Ctrl, 0xf, 0xf, false));
-}
-template <int LPR> __device__ __forceinline__ float row_sum(float x) {
-    static_assert(LPR == 2 || LPR == 4 || LPR == 8 || LPR == 16, "row width");
-    x += dpp_mov<0xB1>(x);                         // quad_perm [1, 0, 3, 2]: lane ^ 1
-    if constexpr (LPR >= 4) x += dpp_mov<0x4E>(x);   // quad_perm [2, 3, 0, 1]: lane ^ 2
-    if constexpr (LPR >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror: lane i <- 7 - i
-    if constexpr (LPR >= 16) x += dpp_mov<0x140>(x); // row_mirror: lane i <- 15 - i
-    return x;
-}
 
 // A lane's 8 consecutive elements of one token's k or q, as loaded.
 template <typename E> struct Vec8;
