@@ -780,9 +780,10 @@ def norm_apply_bytes(tokens, hv=HV, dv=D, elem=2):
 
 def output_norm_bench(dev, copies, steps):
     """Output normalisation: decode B=64 with the fused kernel against the
-    plain one, and the prefill (T=4096, chunk 64) with its normalisation pass
-    against the plain prefill. One JSON line each; kernel times from the
-    library's dispatch-stamped events."""
+    plain one, and two prefills (one 4096-token sequence, whose scan takes
+    the normalisation; eight 512-token sequences, normalised by a pass after
+    the scan) against the plain prefill. One JSON line each; kernel times
+    from the library's dispatch-stamped events."""
     import torch
     import gdn_synth as gs
     import gated_deltanet_linear_02_amd as gdn
@@ -831,31 +832,47 @@ def output_norm_bench(dev, copies, steps):
     }), flush=True)
     del dsets
 
-    pre = gs.workload("prefill")
-    ws_bytes = gdn.prefill_workspace_size(1, T_PREFILL, HK, HV, D, D, CHUNK, torch.bfloat16)
-    psets = []
-    for _ in range(copies):
-        d = device_inputs(pre, dev)
-        d["out"] = torch.empty((T_PREFILL, HV, D), dtype=torch.bfloat16, device=dev)
-        d["fin"] = torch.empty((1, HV, D, D), dtype=torch.float32, device=dev)
-        d["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-        psets.append(d)
+    # prefill: the headline shape (one pass of scan workgroups: the
+    # normalisation fused into the scan) and eight sequences (several passes:
+    # the normalisation pass after the scan)
+    for lens in ([T_PREFILL], [512] * 8):
+        n, tt = len(lens), sum(lens)
+        pre = gs.make_inputs(lens, HK, HV, D, D, seed=gs.SEED_BASE + 2, io_dtype="bf16", gate_dtype="f32") \
+            if n > 1 else gs.workload("prefill")
+        ws_bytes = gdn.prefill_workspace_size(n, tt, HK, HV, D, D, CHUNK, torch.bfloat16)
+        psets = []
+        for _ in range(copies):
+            d = device_inputs(pre, dev)
+            d["out"] = torch.empty((tt, HV, D), dtype=torch.bfloat16, device=dev)
+            d["fin"] = torch.empty((n, HV, D, D), dtype=torch.float32, device=dev)
+            d["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            psets.append(d)
 
-    def pre_run(d, norm):
-        gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=CHUNK,
-                    final_state=d["fin"], out=d["out"], workspace=d["ws"],
-                    norm_weight=w if norm else None, norm_eps=eps)
-    plain_ms, _ = measure(lambda d: pre_run(d, False), psets, ())
-    norm_ms, nk = measure(lambda d: pre_run(d, True), psets, ("norm_apply", "scan"))
-    by = norm_apply_bytes(T_PREFILL)
-    gbs = by / (nk["norm_apply"] * 1e-3) / 1e9
-    print(json.dumps({
-        "mode": "output-norm", "part": "prefill", "plain_ms": plain_ms, "norm_ms": norm_ms,
-        "norm_apply_kernel_ms": nk["norm_apply"], "norm_apply_gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
-        "algorithmic_bytes": by, "dtype": "bf16", "data": "synthetic", "buffer_copies": copies,
-        "config": {"workload": f"prefill 1x{T_PREFILL} tokens, HK={HK}, HV={HV}, d={D}, chunk {CHUNK}; "
-                               f"RMS output norm, eps {eps}"},
-    }), flush=True)
+        def pre_run(d, norm):
+            gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=CHUNK,
+                        final_state=d["fin"], out=d["out"], workspace=d["ws"],
+                        norm_weight=w if norm else None, norm_eps=eps)
+        kinds = ("schedule", "prep", "scan", "norm_apply")
+        plain_ms, pk = measure(lambda d: pre_run(d, False), psets, kinds)
+        norm_ms, nk = measure(lambda d: pre_run(d, True), psets, kinds)
+        fused = nk["norm_apply"] == 0.0
+        rec = {
+            "mode": "output-norm", "part": "prefill", "sequences": n, "tokens": tt,
+            "normalisation": "fused into the scan" if fused else "pass after the scan",
+            "plain_ms": plain_ms, "norm_ms": norm_ms,
+            "plain_kernel_ms": {k: pk[k] for k in kinds if pk[k] > 0},
+            "norm_kernel_ms": {k: nk[k] for k in kinds if nk[k] > 0},
+            "norm_cost_kernel_us": 1e3 * (sum(nk.values()) - sum(pk.values())),
+            "dtype": "bf16", "data": "synthetic", "buffer_copies": copies,
+            "config": {"workload": f"prefill {n}x{tt // n} tokens, HK={HK}, HV={HV}, d={D}, chunk {CHUNK}; "
+                                   f"RMS output norm, eps {eps}"},
+        }
+        if not fused:
+            by = norm_apply_bytes(tt)
+            gbs = by / (nk["norm_apply"] * 1e-3) / 1e9
+            rec.update({"norm_apply_gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": by})
+        print(json.dumps(rec), flush=True)
+        del psets
 
 
 def state_storage_bench(dev, copies, steps):

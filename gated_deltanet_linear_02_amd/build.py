@@ -22,6 +22,10 @@ LIB = os.path.join(PKG, "libgdn.so")
 ARCH = "gfx950"
 
 SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_norm.hip", "gdn_prefill.hip", "gdn_tune.hip"]
+# gdn_prefill_inst.hip is compiled once per (bf16 I/O, chunk size): the
+# chunked prefill's kernels, six objects built in parallel.
+INSTANCES = [("gdn_prefill_inst.hip", f"gdn_prefill_inst_b{b}_c{c}", [f"-DGDN_INST_BF16={b}", f"-DGDN_INST_CHUNK={c}"])
+             for b in (1, 0) for c in (64, 32, 16)]
 
 # Packed-fp32 VALU forms are disabled; hipcc's host pass warns that it does
 # not know the feature, which is harmless.
@@ -40,9 +44,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libgdn.so)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, stem, defs = job
+    obj = os.path.join(BUILD, stem + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, *defs, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -54,9 +59,10 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
+    work = INSTANCES + [(s, os.path.splitext(s)[0], []) for s in SOURCES]
+    jobs = min(len(work), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, work))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -60,6 +60,10 @@ struct PrefillLayout {
     size_t off_tbmat, off_pmat, off_wmat;  // E, per (chunk, value head)
     size_t off_qmat, off_ktmat;            // E, per (chunk, query/key head)
     size_t off_gates;                      // float [max_chunks][hv][gate_record(C)]
+    // Output normalisation fused into the scan: per (chunk, value head, scan
+    // workgroup of that head (at most dv/16)), one partial sum of squares per
+    // token of the chunk.
+    size_t off_norm_part;                  // float [max_chunks][hv][dv / 16][C]
     size_t total;
 };
 
@@ -90,6 +94,7 @@ inline PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int6
     L.off_qmat = take(per_kq);
     L.off_ktmat = take(per_kq);
     L.off_gates = take((size_t)L.max_chunks * (size_t)hv * (size_t)gate_record(chunk) * sizeof(float));
+    L.off_norm_part = take((size_t)L.max_chunks * (size_t)hv * (size_t)(dk / 16) * (size_t)chunk * sizeof(float));
     L.total = o;
     return L;
 }
@@ -109,7 +114,28 @@ struct PrefillArgs {
     void *out;
     char *ws;
     PrefillLayout lay;
+    // Output normalisation fused into the chunked scan (norm_w non-null):
+    // y = o w / sqrt(mean(o^2) + eps) per (token, value head) row.
+    const float *norm_w = nullptr;
+    float norm_eps = 0.f;
 };
+
+// Workgroups of the chunked scan: per (sequence, query/key head) group of
+// hv/hk value heads, dv/rows slices each, the groups padded to a multiple of
+// 8 (the XCD-aware placement).
+inline int64_t scan_grid(int64_t num_seqs, int64_t hk, int64_t hv, int64_t dv, int64_t rows) {
+    return ((num_seqs * hk + 7) / 8) * (hv / hk) * (dv / rows) * 8;
+}
+
+// Whether a chunked prefill with an output normalisation takes it in the
+// scan: when the scan's workgroups fit the GPU in one pass. The row slices
+// of a head then exchange their partial sums of squares while all of them
+// run; with more workgroups than CUs, slices of one head could wait on one
+// another across passes, so those calls normalise in a pass after the scan.
+constexpr int64_t kFusedNormMaxWgs = 256;  // gfx950 (MI355X): 256 CUs
+inline bool fused_norm_fits(int64_t num_seqs, int64_t hk, int64_t hv, int64_t dv, int64_t rows) {
+    return scan_grid(num_seqs, hk, hv, dv, rows) <= kFusedNormMaxWgs;
+}
 
 // Chunked prefill (chunk 16, 32 or 64): preparation and scan kernels.
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st);

@@ -170,7 +170,7 @@ int32_t gdn_prefill(const void *q, const void *k, const void *v,
  * (gdn_prefill_workspace_size of the method gdn_prefill_method reports; the
  * token-by-token method needs none) returns GDN_ERR_WORKSPACE before
  * anything is enqueued; at HK = 16, HV = 32, d = 128 and chunk 64 the array
- * holds one sequence of up to 5,312 bf16 tokens. Every call on a GPU
+ * holds one sequence of up to 5,120 bf16 tokens. Every call on a GPU
  * shares that GPU's array, and the array keeps what the last call left in it
  * (each call writes what it reads): calls that may overlap on one GPU (other
  * streams, other host threads) race and must be serialised by the caller.
@@ -251,13 +251,16 @@ int32_t gdn_decode_step(const void *q, const void *k, const void *v,
  *              definition does.
  *
  * Decode with a weight is one kernel: a workgroup owns a whole (sequence,
- * value head) state, so the unnormalised row never goes to memory. Prefill
- * with a weight runs its kernels, then one pass that rewrites the rows of
- * out in place (the prefill splits a head's rows over workgroups that never
- * wait for one another); rows of tokens outside [cu_seqlens[0],
- * cu_seqlens[N]) are left untouched, and in bf16 a row is rounded twice
- * (before and after the normalisation). The states are those of the call
- * without a weight.
+ * value head) state, so the unnormalised row never goes to memory. A chunked
+ * prefill with bf16 I/O whose scan workgroups fit the GPU in one pass (one
+ * sequence at HK = 16, HV = 32, d = 128, for instance) normalises inside the
+ * scan: the workgroups holding the parts of a row exchange partial sums of
+ * squares through the workspace, and each output is rounded once. Otherwise
+ * (fp32 I/O, token by token, or more scan workgroups than one pass holds)
+ * the prefill's kernels are followed by one pass that rewrites the rows of
+ * out in place; rows of tokens outside [cu_seqlens[0], cu_seqlens[N]) are
+ * left untouched, and in bf16 a row is then rounded twice (before and after
+ * the normalisation). The states are those of the call without a weight.
  */
 int32_t gdn_prefill_ex(const void *q, const void *k, const void *v,
                        const void *g, const void *beta,

@@ -60,8 +60,10 @@ def test_workspace_size(lib):
     # per chunk: Tb and P (bf16 C x C) and W (bf16 C x d) per value head, Q
     # and K^T per query/key head (bf16 C x d), and per value head a gate
     # record of 2C + 4 fp32 (delta and scale*gamma per token, gamma_C, padding)
+    # and d/16 slots of C fp32 for the fused normalisation's partial sums
     chunks = (4096 + 63) // 64 + 1
-    need = chunks * (32 * (2 * 64 * 64 * 2 + 64 * 128 * 2 + (2 * 64 + 4) * 4) + 16 * 2 * 64 * 128 * 2)
+    need = chunks * (32 * (2 * 64 * 64 * 2 + 64 * 128 * 2 + (2 * 64 + 4) * 4 + (128 // 16) * 64 * 4)
+                     + 16 * 2 * 64 * 128 * 2)
     assert need <= w < need + 64 * 1024
     assert _ws(io=F32) > w
     assert _ws(T=0) > 0
@@ -358,8 +360,8 @@ def test_prefill_noalloc_host_checks(lib):
     assert call(hk=3, hv=4) == BAD_SHAPE
     assert call(dk=96, dv=96) == UNSUPPORTED
     assert call(chunk=8) == UNSUPPORTED
-    # the largest single bf16 sequence that fits at chunk 64 (5,312 tokens)
+    # the largest single bf16 sequence that fits at chunk 64 (5,120 tokens)
     # and the next one
-    assert lib.gdn_prefill_workspace_size(1, 5312, 16, 32, 128, 128, 64, BF16) <= 128 << 20
-    assert lib.gdn_prefill_workspace_size(1, 5313, 16, 32, 128, 128, 64, BF16) > 128 << 20
-    assert call(T=5313) == WORKSPACE
+    assert lib.gdn_prefill_workspace_size(1, 5120, 16, 32, 128, 128, 64, BF16) <= 128 << 20
+    assert lib.gdn_prefill_workspace_size(1, 5121, 16, 32, 128, 128, 64, BF16) > 128 << 20
+    assert call(T=5121) == WORKSPACE

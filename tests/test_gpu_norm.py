@@ -192,3 +192,49 @@ def test_prefill_norm_leaves_rows_outside_sequences():
     assert rel_err(to_f64(o)[5:], oracle.rms_norm(o_ref[5:], w, 1e-6)) <= tol("bf16")
     assert rel_err(to_f64(f), f_ref[1:]) <= tol("bf16")
     assert torch.isnan(o[:5].float()).all()
+
+
+@pytest.mark.parametrize("lens", [[700, 333], [200] * 8])
+def test_prefill_norm_slices_and_passes(lens):
+    """HK = 16, HV = 32, d = 128, bf16. Two sequences: 32-row scan slices
+    (4 per head), one pass over the GPU, so the normalisation is fused into
+    the scan. Eight sequences: more scan workgroups than one pass holds, so
+    a pass over out normalises after the scan. Both against the oracle, with
+    the plain call's final states bit for bit."""
+    inp = gs.make_inputs(lens, 16, 32, 128, 128, seed=gs.SEED_BASE + 520 + len(lens), io_dtype="bf16",
+                         gate_dtype="f32", init_state=True)
+    w = _weight(128, seed=9)
+    note(f"prefill norm lens={lens}")
+    o, f = _prefill_norm(inp, chunk=64, w=w, eps=1e-6)
+    o_ref, f_ref = oracle_ref(inp)
+    eo = rel_err(to_f64(o), oracle.rms_norm(o_ref, w, 1e-6))
+    print(f"[parity] prefill norm lens={lens} out_err={eo:.3e}", flush=True)
+    assert np.isfinite(to_f64(o)).all() and eo <= tol("bf16")
+    d = device_inputs(inp)
+    _, f_plain = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=64,
+                             initial_state=d["initial_state"])
+    torch.cuda.synchronize()
+    assert torch.equal(f, f_plain)
+
+
+def test_prefill_norm_repeated_calls_are_identical():
+    """The fused normalisation sums the row slices' partials in a fixed
+    order, so repeated calls give the same bits; a call after one with other
+    inputs (the partial slots then hold old values until the preparation
+    kernel resets them) too."""
+    inp = gs.workload("prefill", io_dtype="bf16")
+    other = gs.make_inputs([4096], 16, 32, 128, 128, seed=gs.SEED_BASE + 531, io_dtype="bf16",
+                           gate_dtype="f32")
+    w = torch.from_numpy(_weight(128)).cuda()
+    d, e = device_inputs(inp), device_inputs(other)
+    ws = torch.empty(gdn.prefill_workspace_size(1, 4096, 16, 32, 128, 128, 64, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    note("prefill norm repeated")
+    outs = []
+    for x in (d, d, e, d):
+        o, _ = gdn.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"], chunk=64,
+                           norm_weight=w, norm_eps=1e-6, workspace=ws)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[3])
+    assert not torch.equal(outs[0], outs[2])
