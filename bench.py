@@ -129,7 +129,8 @@ def _kernel_label(name: str) -> str:
     label = KERNELS.get(short, name)
     ints = _template_ints(name)
     if short == "scan" and len(ints) >= 3:
-        label += f" (C={ints[0]}, {ints[-1]}-row slices)"
+        norm = "Lb1E" in name or ", true>" in name
+        label += f" (C={ints[0]}, {ints[-1]}-row slices{', norm fused' if norm else ''})"
     elif short == "prep" and ints:
         label += f" (C={ints[0]})"
     elif short == "token_scan" and len(ints) >= 3 and ints[-1] > 1:
@@ -458,16 +459,20 @@ def summarize_norm(stats_dir: str, fetch_dir: str, write_dir: str, results_jsonl
     fetch, ffac, fkib = _counter_means(fetch_dir, "FETCH_SIZE", probe_bytes)
     write, wfac, wkib = _counter_means(write_dir, "WRITE_SIZE", probe_bytes)
     rows = list(csv.DictReader(open(os.path.join(stats_dir, "run_kernel_stats.csv"))))
-    res = {}
+    res, pre = {}, []
     for line in open(results_jsonl):
         line = line.strip()
         if line.startswith("{"):
             d = json.loads(line)
-            res[d["part"]] = d
+            if d["part"] == "prefill":
+                pre.append(d)
+            else:
+                res[d["part"]] = d
     algo = {"decode": decode_bytes_per_step(), "decode_norm": decode_bytes_per_step() + 4 * D,
             "norm_apply": norm_apply_bytes(T_PREFILL)}
     lines = [
-        "# Output normalisation: decode batch 64 (fused) and prefill 1x4096 (pass); HK=16, HV=32, d=128, bf16",
+        "# Output normalisation: decode batch 64 (fused), prefill 1x4096 (fused into the scan) and "
+        "8x512 (pass after the scan); HK=16, HV=32, d=128, bf16",
         "",
         "Made by (from the repository root; OUT is any scratch directory):",
         "",
@@ -511,8 +516,8 @@ def summarize_norm(stats_dir: str, fetch_dir: str, write_dir: str, results_jsonl
             fb, wb = fetch[short] * ffac, write[short] * wfac
             lines.append(f"| {KERNELS[short]} | {algo[short] / 1e6:.1f} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
                          f"{(fb + wb) / 1e6:.1f} |")
-    if res:
-        dd, pp = res.get("decode"), res.get("prefill")
+    if res or pre:
+        dd = res.get("decode")
         lines += ["", "## Rates (HIP events in the traced run)", "",
                   "Taken under the profiler, which adds a per-launch overhead to these event times (compare "
                   "the kernel durations above); `python3 bench.py --norm` measures the same without it.", ""]
@@ -520,10 +525,15 @@ def summarize_norm(stats_dir: str, fetch_dir: str, write_dir: str, results_jsonl
             lines.append(f"- decode step, kernel: plain {dd['plain_kernel_ms'] * 1e3:.1f} us, with the norm fused "
                          f"{dd['norm_kernel_ms'] * 1e3:.1f} us ({dd['norm_kernel_gbs']:.0f} GB/s, "
                          f"{100 * dd['hbm_frac']:.1f}% of 8 TB/s).")
-        if pp:
-            lines.append(f"- prefill call: plain {pp['plain_ms'] * 1e3:.1f} us, with the norm pass "
-                         f"{pp['norm_ms'] * 1e3:.1f} us; the pass itself {pp['norm_apply_kernel_ms'] * 1e3:.1f} us "
-                         f"({pp['norm_apply_gbs']:.0f} GB/s, {100 * pp['hbm_frac']:.1f}% of 8 TB/s).")
+        for pp in pre:
+            kp = ", ".join(f"{k} {v * 1e3:.1f}" for k, v in pp["plain_kernel_ms"].items())
+            kn = ", ".join(f"{k} {v * 1e3:.1f}" for k, v in pp["norm_kernel_ms"].items())
+            extra = (f"; the pass at {pp['norm_apply_gbs']:.0f} GB/s, {100 * pp['hbm_frac']:.1f}% of 8 TB/s"
+                     if "norm_apply_gbs" in pp else "")
+            lines.append(f"- prefill {pp['sequences']}x{pp['tokens'] // pp['sequences']} ({pp['normalisation']}): "
+                         f"call plain {pp['plain_ms'] * 1e3:.1f} us, with the norm {pp['norm_ms'] * 1e3:.1f} us; "
+                         f"kernel us plain ({kp}), with the norm ({kn}); the norm adds "
+                         f"{pp['norm_cost_kernel_us']:.1f} us of kernel time{extra}.")
     with open(os.path.join(ROOT, "profiles", "gdn_output_norm.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 

@@ -108,7 +108,7 @@ static int32_t check_prefill_shape(int32_t num_seqs, int64_t total_tokens, int32
     if (!valid_head(dk) || dv != dk || !valid_chunk(chunk) || !valid_dtype(io_dtype) ||
         !valid_dtype(gate_dtype) || hk > 65535)
         return GDN_ERR_UNSUPPORTED;
-    const int32_t c = chunk != 0 ? chunk : rule_chunk(num_seqs, total_tokens, hv, dv);
+    const int32_t c = chunk != 0 ? chunk : rule_chunk(num_seqs, total_tokens, hv, dv, io_dtype == GDN_BF16);
     return method_fits(c, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype) ? GDN_OK : GDN_ERR_UNSUPPORTED;
 }
 
@@ -124,7 +124,7 @@ static Method method_for(int32_t chunk, int32_t rows, int32_t num_seqs, int64_t 
     if (chunk == 0) {
         m = tuned_method(num_seqs, total_tokens, hk, hv, dk, io_dtype, gate_dtype);
         if (m.chunk == 0 || !method_fits(m.chunk, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype)) {
-            m.chunk = rule_chunk(num_seqs, total_tokens, hv, dv);
+            m.chunk = rule_chunk(num_seqs, total_tokens, hv, dv, io_dtype == GDN_BF16);
             m.rows = 0;
         }
     }

@@ -186,7 +186,8 @@ int32_t prefill_with_method(const void *q, const void *k, const void *v, const v
 //                    sequences of 24 tokens: 226 vs 283 us at best chunked);
 //   chunks of 16     L <= 48: the fewest padded rows (64 x 32: 287 vs 336 us
 //                    with 64);
-//   chunks of 32     the scan's workgroups fit the GPU in one pass (at most
+//   chunks of 32     the scan's workgroups, with the state rows per
+//                    workgroup it takes, fit the GPU in one pass (at most
 //                    one per CU) and L <= 1024: a lone sequence is bound by
 //                    its chain's latency, which shorter chunks cut (1 x 512:
 //                    29.8 vs 32.5 us);
@@ -207,10 +208,14 @@ inline int32_t scan_slice_rows(int64_t num_seqs, int64_t hv, int64_t dv, bool io
     return io_bf16 && dv >= 32 && num_seqs * hv * (dv / 16) > kScanOnePassWgs ? 32 : 16;
 }
 
-inline int32_t rule_chunk(int64_t num_seqs, int64_t total_tokens, int64_t hv, int64_t dv) {
+inline int32_t rule_chunk(int64_t num_seqs, int64_t total_tokens, int64_t hv, int64_t dv, bool io_bf16) {
     if (total_tokens <= kTokenScanTokens || total_tokens <= kTokenScanPerSeq * num_seqs) return 1;
     if (total_tokens <= kChunk16PerSeq * num_seqs) return 16;
-    if (num_seqs * hv * (dv / 16) <= kScanOnePassWgs && total_tokens <= kChunk32PerSeq * num_seqs) return 32;
+    // one pass with the slice rows the scan will take (2 x 600: 32-row
+    // slices fill the 256 CUs once, and chunks of 32 measure 40.2 against
+    // 42.7 us)
+    const int64_t rows = scan_slice_rows(num_seqs, hv, dv, io_bf16);
+    if (num_seqs * hv * (dv / rows) <= kScanOnePassWgs && total_tokens <= kChunk32PerSeq * num_seqs) return 32;
     return 64;
 }
 

@@ -130,7 +130,8 @@ int32_t gdn_prefill_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, i
  *              gdn_tune_prefill cached for this device and shape bucket if
  *              there is one, else by the mean sequence length L = T / N:
  *              1 when T <= 32 or L <= 24, 16 when L <= 48, 32 when the
- *              chunked scan's N * hv * dv / 16 workgroups fit the GPU's 256
+ *              chunked scan's N * hv * dv / rows workgroups (rows: its state
+ *              rows per workgroup, see gdn_prefill_method) fit the GPU's 256
  *              CUs and L <= 1024, else 64 (gdn_prefill_method tells which).
  *              The result does not depend on it beyond rounding.
  * dk, dv       16, 32, 64 or 128 each.

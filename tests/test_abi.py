@@ -294,7 +294,8 @@ def test_tune_argument_checks(lib):
 
 def test_chunk_zero_rule(lib):
     """The method chunk 0 takes with nothing tuned, by mean sequence length
-    (HK=16, HV=32, d=128; the scan fills the GPU in one pass up to 1 sequence)."""
+    (HK=16, HV=32, d=128, bf16; the scan fills the GPU in one pass up to one
+    sequence with 16-row slices, two with 32-row slices)."""
     gdn.tune_cache_clear()
     m = lambda n, T: gdn.prefill_method(n, T, 16, 32, 128)
     assert m(1, 16) == 1 and m(1, 32) == 1          # one short prompt
@@ -302,7 +303,9 @@ def test_chunk_zero_rule(lib):
     assert m(1, 48) == 16 and m(64, 64 * 32) == 16   # mean <= 48
     assert m(1, 128) == 32 and m(1, 1024) == 32      # one sequence: one pass
     assert m(1, 4096) == 64 and m(8, 8 * 300) == 64  # long, or several passes
-    assert m(2, 2 * 600) == 64                       # two sequences: two passes
+    assert m(2, 2 * 600) == 32                       # two sequences: one pass of 32-row slices
+    assert m(4, 4 * 600) == 64                       # four: two passes even so
+    assert gdn.prefill_method(2, 2 * 600, 16, 32, 128, io_dtype=torch.float32) == 64  # fp32: 16-row slices
     assert gdn.prefill_method(1, 4096, 16, 32, 128, chunk=16) == 16  # explicit chunks as given
     assert gdn.prefill_method(1, 4096, 3, 32, 128) == 0              # rejected shape
     # state rows per scan workgroup: 32 once 16-row slices need more than one
