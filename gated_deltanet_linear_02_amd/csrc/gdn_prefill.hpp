@@ -656,7 +656,12 @@ struct ScanSmem {
     static constexpr size_t off_Dl = (off_Vt + 2 * (size_t)R * LDC * sizeof(E) + 15) & ~(size_t)15;  // [2][C] delta
     static constexpr size_t off_Sg = off_Dl + 2 * (size_t)C * sizeof(float);  // [2][C] scale gamma
     static constexpr size_t off_Gc = off_Sg + 2 * (size_t)C * sizeof(float);  // [2][4] gamma_C (first of 4)
-    static constexpr size_t bytes = off_Gc + 8 * sizeof(float);
+    // fused output normalisation: this slice's partial sums of squares of a
+    // chunk, the head's block of every slice's partials, their totals
+    static constexpr size_t off_Np = off_Gc + 8 * sizeof(float);                   // [C]
+    static constexpr size_t off_Nb = off_Np + (size_t)C * sizeof(float);           // [DK / R][C]
+    static constexpr size_t off_Nt = off_Nb + (size_t)(DK / R) * C * sizeof(float);  // [C]
+    static constexpr size_t bytes = off_Nt + (size_t)C * sizeof(float);
 };
 
 template <typename E> struct Vec4;
@@ -742,21 +747,23 @@ struct OStage {
     }
 };
 
-// Runs body(st, nxt, fut, c, three) for chunks c = 0 .. nch-1 over N register
+// Runs body(st, nxt, fut, c, three, idx) for chunks c = 0 .. nch-1 over N register
 // stages used round robin: chunk c sits in st[c % N], `nxt` holds chunk c + 1
 // and `fut` (which held chunk c - 1) is refilled with chunk c + N - 1. The
 // loop is unrolled by N so that every stage index is a compile-time
-// constant (the stages stay in registers). st[0 .. N-2] must hold chunks
-// 0 .. N-2 on entry.
+// constant (the stages stay in registers); idx is that index, I (so c + I
+// has I's parity when N is even). st[0 .. N-2] must hold chunks 0 .. N-2 on
+// entry.
 template <int N, int I = 0, typename St, typename Body>
 __device__ __forceinline__ void pipeline_step(St (&st)[N], int c, Body &body) {
-    body(st[I], st[(I + 1) % N], st[(I + N - 1) % N], c + I, std::true_type());
+    body(st[I], st[(I + 1) % N], st[(I + N - 1) % N], c + I, std::true_type(), std::integral_constant<int, I>());
     if constexpr (I + 1 < N) pipeline_step<N, I + 1>(st, c, body);
 }
 template <int N, int I = 0, typename St, typename Body>
 __device__ __forceinline__ void pipeline_tail(St (&st)[N], int c, int nch, Body &body) {
     if constexpr (I + 1 < N) {
-        if (c + I < nch) body(st[I], st[(I + 1) % N], st[(I + N - 1) % N], c + I, std::true_type());
+        if (c + I < nch)
+            body(st[I], st[(I + 1) % N], st[(I + N - 1) % N], c + I, std::true_type(), std::integral_constant<int, I>());
         pipeline_tail<N, I + 1>(st, c, nch, body);
     }
 }
@@ -777,6 +784,14 @@ constexpr int kTouchAhead = 8;
 // partial sums (about 50 ms of s_sleep 2): a wait that long means a slice
 // never ran, and the rows it leaves are written as NaN rather than wrong.
 constexpr int kNormSpinMax = 1 << 20;
+
+// Steps from a chunk's outputs to its normalised rows in the fused
+// normalisation's exchange (and steps after the last chunk in which it
+// writes the last chunks' rows).
+constexpr int kNormLag = 4;
+
+// Word 3 of a raw buffer resource on gfx9-family GPUs (gfx950 included).
+constexpr int kBufferWord3 = 0x00020000;
 
 template <typename E, int C, int DK, typename SE, int R, bool kNorm>
 __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdn_scan_kernel(
@@ -804,7 +819,10 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
     constexpr int KBD = SH::KBD, KBC = SH::KBC;
     // Register stages per role (bf16); fp32 fragments are 4x larger and use one.
     constexpr bool kPipelined = IsBf16<E>::value;
-    constexpr int kRStages = R == 16 ? 4 : 3, kOStages = R == 16 ? 5 : 4;
+    // The fused normalisation's exchange alternates two register slots by
+    // chunk parity, which the unrolled pipeline keeps compile-time when the
+    // output stages are even.
+    constexpr int kRStages = R == 16 ? 4 : 3, kOStages = R == 16 && !kNorm ? 5 : 4;
 
     extern __shared__ __align__(16) char smem[];
     E *sS = reinterpret_cast<E *>(smem + L::off_S);
@@ -885,7 +903,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         }
         __syncthreads();  // S0 and chunk 0's V rows staged
 
-        auto body = [&](RS &st, RS &, RS &fut, int c, auto three) {
+        auto body = [&](RS &st, RS &, RS &fut, int c, auto three, auto) {
             constexpr bool kThree = decltype(three)::value;
             // ---- phase 1: U = Tb V - W S0^T (W is stored negated). Token and
             // key contractions accumulate separately: with d = 16 they use
@@ -958,10 +976,15 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             } else {
                 RS st0;
                 st0.load(tbmat, wmat, ktmat, chunk(0), q, lane);
-                for (int c = 0; c < nch; ++c) body(st0, st0, st0, c, std::false_type());
+                for (int c = 0; c < nch; ++c) body(st0, st0, st0, c, std::false_type(), std::integral_constant<int, -1>());
             }
         }
 
+        if constexpr (kNorm) {
+            if (nch > 0) {  // the output waves' drain
+                for (int st = 0; st < 2 * kNormLag; ++st) __syncthreads();
+            }
+        }
         if (sfin) {
 #pragma unroll
             for (int j = 0; j < NMW; ++j) {
@@ -1100,25 +1123,34 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         };
         // ---- output normalisation fused in (kNorm). A (token, value head)
         // output row spans the NS row slices of the head, each its own
-        // workgroup. Right after computing chunk c's outputs an output wave
-        //   publishes chunk c's partial sum of squares per token (its
-        //     columns, then the token's four lane groups) in the slot
-        //     (chunk, head, slice) with a device-coherent store; every slot
-        //     holds kNormPartEmpty until then (set by the preparation kernel);
-        //   writes chunk c - 2's rows: the NS partials of each token, read
-        //     with device-coherent loads one step earlier, added in a fixed
-        //     order (the same sum in every slice), give o w / sqrt(mean +
-        //     eps), one rounding of the unrounded output kept in registers;
-        //   issues the loads of chunk c - 1's partials.
-        // Each slot is written once per call, so a value other than
-        // kNormPartEmpty is that call's partial; the rare wait for a slice
-        // behind spins with s_sleep, bounded.
+        // workgroup. Per chunk c, in the workgroup's step
+        //   c      every output wave computes its tokens' partial sums of
+        //          squares (its columns, then the token's four lane groups)
+        //          into LDS, after its outputs;
+        //   c + 1  output wave 0 publishes the chunk's C partials in the slot
+        //          block (chunk, head, slice) with one device-coherent store
+        //          (each slot holds kNormPartEmpty until then, set by the
+        //          preparation kernel);
+        //   c + 2  output wave 1 loads the head's block of the chunk, every
+        //          slice's partials, device-coherent: a step and a half after
+        //          the slices published them, if they run together;
+        //   c + 4  output wave 1 adds each token's NS partials in slice order
+        //          (the same sum in every slice) into LDS, and every output
+        //          wave writes its rows o w / sqrt(mean + eps): one rounding
+        //          of the unrounded outputs kept in registers.
+        // Three memory instructions per workgroup and chunk in all. Each slot
+        // is written once per call, so a value other than kNormPartEmpty is
+        // that call's partial; the rare wait for a slice behind spins with
+        // s_sleep, bounded.
         const int slice = within % NS;
-        f32x4 nw[RW], pend1[RW], pend2[RW];  // outputs of chunks c - 1, c - 2
-        float pv[2] = {0.f, 0.f};            // partials of chunk c - 2
+        float *sNp = reinterpret_cast<float *>(smem + L::off_Np);
+        float *sNb = reinterpret_cast<float *>(smem + L::off_Nb);
+        float *sNt = reinterpret_cast<float *>(smem + L::off_Nt);
+        f32x4 nw[RW], pend[kNormLag][RW];  // pend[j]: outputs of chunk c - 1 - j
 #pragma unroll
         for (int rr = 0; rr < RW; ++rr) {
-            pend1[rr] = pend2[rr] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < kNormLag; ++j) pend[j][rr] = f32x4{0.f, 0.f, 0.f, 0.f};
             nw[rr] = f32x4{0.f, 0.f, 0.f, 0.f};
             if constexpr (kNorm) {
 #pragma unroll
@@ -1126,27 +1158,92 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             }
         }
         auto chunk_rows = [&](int cc) { return min(C, len - cc * C); };
-        // this lane's slots of chunk cc: token 16 q + l%16, slices g4, g4 + 4
-        // (the 16 lanes of a slice read one contiguous 64-byte piece)
-        auto part_slot = [&](int cc, int j) {
-            const int row = 16 * min(q, RT - 1) + ln;
-            return norm_part + (((size_t)(c0 + cc) * hv + h) * NS + g4 + 4 * j) * C + row;
+        // The head's block of chunk cc's partials, NS x C floats, through a
+        // buffer resource: 16-byte loads and stores that bypass the CU's
+        // cache (sc1, device coherence), with reads past the block giving 0.
+        constexpr int kBlkPieces = NS * C / 4, kBlkLoads = (kBlkPieces + 63) / 64;
+        constexpr int kCoherent = 16;  // sc1
+        auto part_rsrc = [&](int cc, int first_slice, int slices) {
+            return __builtin_amdgcn_make_buffer_rsrc(
+                norm_part + (((size_t)(c0 + cc) * hv + h) * NS + first_slice) * C, (short)0, slices * C * 4,
+                kBufferWord3);
         };
-        auto part_ready = [&](int cc, int j) { return 16 * q + ln < chunk_rows(cc) && g4 + 4 * j < NS; };
-        auto load_parts = [&](int cc) {
+        // Two register slots for blocks in flight, by chunk step parity: a
+        // block is loaded two steps before it is summed, as device-coherent
+        // loads reach the other slices' stores only through the L2s' backing
+        // (agent scope) and take about a step to return.
+        f32x4 blk0[kBlkLoads], blk1[kBlkLoads];
+        auto load_into = [&](f32x4 (&b)[kBlkLoads], int cc) {
+            const auto rs = part_rsrc(cc, 0, NS);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                pv[j] = part_ready(cc, j) ? __hip_atomic_load(part_slot(cc, j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                          : 0.f;
+            for (int i = 0; i < kBlkLoads; ++i)
+                b[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (64 * i + lane) * 16, 0,
+                                                                                       kCoherent));
         };
-        auto have_parts = [&](int cc) {
-            bool mine = true;
+        auto load_block = [&](int cc, int par) {
+            if (par) load_into(blk1, cc);
+            else load_into(blk0, cc);
+        };
+        // Whether every slot of chunk cc's block holds a partial. Evaluated
+        // without short-circuit branches: a branch here would leave some of
+        // the block's loads possibly outstanding where the paths meet, and
+        // the compiler would then wait for every load in flight, the operand
+        // prefetches included.
+        auto block_ready = [&](const f32x4 (&b)[kBlkLoads], int cc) {
+            const int rows = chunk_rows(cc);
+            int ok = 1;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) mine = mine && (!part_ready(cc, j) || pv[j] != kNormPartEmpty);
-            return __all(mine);
+            for (int i = 0; i < kBlkLoads; ++i) {
+                const int pc = 64 * i + lane, t0 = (pc % (C / 4)) * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ok &= (int)(pc >= kBlkPieces) | (int)(t0 + e >= rows) | (int)(b[i][e] != kNormPartEmpty);
+            }
+            return __all(ok);
         };
-        // Publish chunk cc's partial sums of squares from its outputs po.
-        auto publish = [&](int cc, const f32x4 (&po)[RW]) {
+        // Output wave 1: chunk cc's totals into LDS, from the block in slot
+        // par. The first check is straight-line code, so that waiting for
+        // these loads does not wait for the later operand prefetches; only
+        // the rare retry loop (a slice behind) waits for everything, and
+        // after kNormSpinMax retries the totals are NaN (the rows are written
+        // as NaN rather than wrong).
+        auto sum_from = [&](f32x4 (&b)[kBlkLoads], int cc) {
+            bool ok = true;
+            if (!block_ready(b, cc)) {
+                for (int spin = 0;; ++spin) {
+                    if (spin >= kNormSpinMax) {
+                        ok = false;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                    load_into(b, cc);
+                    if (block_ready(b, cc)) break;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kBlkLoads; ++i)
+                if (64 * i + lane < kBlkPieces) *reinterpret_cast<f32x4 *>(sNb + 4 * (64 * i + lane)) = b[i];
+            if (lane < C) {  // the wave reads back its own LDS writes
+                float tot = 0.f;
+#pragma unroll
+                for (int sl = 0; sl < NS; ++sl) tot += sNb[sl * C + lane];
+                sNt[lane] = ok ? tot : __builtin_nanf("");
+            }
+        };
+        auto sum_block = [&](int cc, int par) {
+            if (par) sum_from(blk1, cc);
+            else sum_from(blk0, cc);
+        };
+        // Output wave 0: chunk cc's partials from LDS to its slots.
+        auto publish_block = [&](int cc) {
+            const auto rs = part_rsrc(cc, slice, 1);
+            if (lane < C / 4)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4 *>(sNp + 4 * lane)), rs, lane * 16, 0,
+                    kCoherent);
+        };
+        // This wave's partial sums of squares of chunk cc's outputs po.
+        auto put_partials = [&](int cc, const f32x4 (&po)[RW]) {
             float sq = 0.f;
 #pragma unroll
             for (int rr = 0; rr < RW; ++rr)
@@ -1154,35 +1251,31 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                 for (int i = 0; i < 4; ++i) sq = __builtin_fmaf(po[rr][i], po[rr][i], sq);
             sq += __shfl_xor(sq, 16);
             sq += __shfl_xor(sq, 32);
-            const int row = 16 * q + ln;
-            if (row < chunk_rows(cc) && g4 == 0)
-                __hip_atomic_store(norm_part + (((size_t)(c0 + cc) * hv + h) * NS + slice) * C + row, sq,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (g4 == 0) sNp[16 * q + ln] = sq;
         };
-        // Normalise and store chunk cc's outputs po (its loads issued).
-        auto finish = [&](int cc, const f32x4 (&po)[RW]) {
-            // The first check is straight-line code, so that waiting for these
-            // loads does not wait for the later operand prefetches; only the
-            // rare retry loop (a slice behind) waits for everything.
-            bool ok = true;
-            if (!have_parts(cc)) {
-                for (int spin = 0;; ++spin) {
-                    if (spin >= kNormSpinMax) {
-                        ok = false;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(2);
-                    load_parts(cc);
-                    if (have_parts(cc)) break;
-                }
+        // The exchange's work in the two phases of step st (par: st's
+        // parity): publish chunk st - 1, sum chunk st - kNormLag (phase 1);
+        // write chunk st - kNormLag's rows and load chunk st + 2 - kNormLag's
+        // block (phase 2, after this step's outputs), into the slot just
+        // summed. The loop's steps load unconditionally (a clamped chunk),
+        // so that its load count is fixed; the drain's steps past the last
+        // chunk skip what does not exist.
+        auto norm_phase1 = [&](int st, int par) {
+            if (q == 0 && st >= 1 && st - 1 < nch) publish_block(st - 1);
+            if (q == 1 && st >= kNormLag && st - kNormLag < nch) sum_block(st - kNormLag, par);
+        };
+        auto rotate = [&](const f32x4 (&oc)[RW]) {
+#pragma unroll
+            for (int rr = 0; rr < RW; ++rr) {
+#pragma unroll
+                for (int j = kNormLag - 1; j > 0; --j) pend[j][rr] = pend[j - 1][rr];
+                pend[0][rr] = oc[rr];
             }
-            // slices g4 and g4 + 4 here; then lanes g4 ^ 1 and g4 ^ 2 (the
-            // same grouping in every lane, so every slice gets the same sum)
-            float tot = pv[0] + pv[1];
-            tot += __shfl_xor(tot, 16);
-            tot += __shfl_xor(tot, 32);
-            const float r = ok ? 1.0f / sqrtf(tot * (1.0f / DV) + norm_eps) : __builtin_nanf("");
+        };
+        // Normalise and store chunk cc's outputs po (its totals in LDS).
+        auto finish = [&](int cc, const f32x4 (&po)[RW]) {
             const int row = 16 * q + ln;
+            const float r = 1.0f / sqrtf(sNt[row] * (1.0f / DV) + norm_eps);
             if (row < chunk_rows(cc)) {
 #pragma unroll
                 for (int rr = 0; rr < RW; ++rr) {
@@ -1207,7 +1300,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         // (pipelined: its V rows are staged here; `fut` is refilled with
         // chunk c + kOStages - 1). One stage: chunk c + 1's V rows are loaded
         // at the start and `st` is refilled with chunk c + 1 at the end.
-        auto body = [&](OS &st, OS &nxt, OS &fut, int c, auto three) {
+        auto body = [&](OS &st, OS &nxt, OS &fut, int c, auto three, auto idx) {
             constexpr bool kThree = decltype(three)::value;
             E4 vn;
             OS gn;  // one stage: chunk c + 1's gate vectors (its aux)
@@ -1226,6 +1319,10 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             // buffers were last read before the previous barrier).
             if constexpr (kThree) put_chunk(nxt, nxt.vr, (c + 1) & 1);
             else put_chunk(gn, vn, (c + 1) & 1);
+            // the step's parity: compile-time in the unrolled pipeline
+            constexpr int kIdx = decltype(idx)::value;
+            const int par = kIdx >= 0 && kOStages % 2 == 0 ? (kIdx & 1) : (c & 1);
+            if constexpr (kNorm) norm_phase1(c, par);
             // ---- phase 1: O1^T = S0 Q^T
             f32x4 o1[RW];
 #pragma unroll
@@ -1263,15 +1360,13 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                     }
                 }
                 if constexpr (kNorm) {
-                    publish(c, oc);
-                    if (c >= 2) finish(c - 2, pend2);
-                    if (c >= 1) load_parts(c - 1);  // waited for in the next step
-#pragma unroll
-                    for (int rr = 0; rr < RW; ++rr) {
-                        pend2[rr] = pend1[rr];
-                        pend1[rr] = oc[rr];
-                    }
+                    put_partials(c, oc);
+                    if (c >= kNormLag) finish(c - kNormLag, pend[kNormLag - 1]);
+                    rotate(oc);
                 }
+            }
+            if constexpr (kNorm) {
+                if (q == 1) load_block(max(c + 2 - kNormLag, 0), par);
             }
             __syncthreads();
             if constexpr (!kThree) st.load(v, pmat, qmat, chunk(min(c + 1, nch - 1)), hv, h, col0, q, lane);
@@ -1286,13 +1381,19 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                 }
                 run_pipeline<kOStages>(st, nch, body);
             } else {
-                for (int c = 0; c < nch; ++c) body(st[0], st[0], st[0], c, std::false_type());
+                for (int c = 0; c < nch; ++c) body(st[0], st[0], st[0], c, std::false_type(), std::integral_constant<int, -1>());
             }
             if constexpr (kNorm) {
-                if (q < RT) {  // the last two chunks' outputs
-                    if (nch >= 2) finish(nch - 2, pend2);
-                    load_parts(nch - 1);
-                    finish(nch - 1, pend1);
+                // the last kNormLag chunks' outputs, in kNormLag more steps
+                // of two barriers (the recurrence waves take part)
+                for (int st = nch; st < nch + kNormLag; ++st) {
+                    norm_phase1(st, st & 1);
+                    __syncthreads();
+                    if (q < RT && st - kNormLag >= 0) finish(st - kNormLag, pend[kNormLag - 1]);
+                    if (q == 1 && st + 2 - kNormLag >= 0 && st + 2 - kNormLag < nch) load_block(st + 2 - kNormLag, st & 1);
+                    const f32x4 none[RW] = {};
+                    rotate(none);
+                    __syncthreads();
                 }
             }
         }
