@@ -16,9 +16,13 @@ than from the 256 MB Infinity Cache left warm by the previous step.
 
 Timing: HIP events on the stream the library launches on (torch's current
 stream), around exactly --steps steps after --warmup untimed steps, with
-torch.cuda.synchronize() on both sides. A second pass of the same steps
-brackets every kernel launch with the library's own event pairs
-(gdn_timing_start/stop) to get each kernel's mean duration for the roofline.
+torch.cuda.synchronize() on both sides. Measurement passes of the same steps
+run just before them: one brackets every step with events (the spread), one
+every kernel launch with the library's own event pairs (gdn_timing_start/
+stop: each kernel's mean duration for the roofline), then prefill-only and
+decode-only rates. The parity check's GPU step runs first; the oracle it is
+compared with (and the CPU baseline) runs after the timed region, so that the
+GPU does not idle for its ~20 s right before the timed steps.
 
 Output: one JSON line (see the "roofline" and "cpu_baseline" objects).
 """
@@ -1240,15 +1244,9 @@ def main():
                     final_state=s["fin"], out=s["out"], workspace=s["ws"])
         gdn.decode_step(s["dq"], s["dk"], s["dv"], s["dg"], s["db"], s["state"], out=s["dout"])
 
-    # ---- verify before timing: the oracle on the same inputs (this is also
-    # the CPU baseline), against one untimed GPU step from fresh decode states.
-    try:
-        ncpu = len(os.sched_getaffinity(0))
-    except AttributeError:
-        ncpu = os.cpu_count() or 1
-    threads = max(1, min(16, ncpu))
-    print("[bench] oracle reference (and CPU baseline)", file=sys.stderr, flush=True)
-    cpu_rec, ref = cpu_baseline(pre, dec, s_dec, threads, one_thread=not args.no_cpu_baseline)
+    # ---- the GPU side of the parity check: one untimed step from fresh
+    # decode states, its results copied to the host. The oracle runs on the
+    # same inputs after the timed region; its comparison gates the output.
     s0 = sets[0]
     chk_state = torch.from_numpy(s_dec).to(dev)
     gdn.prefill(s0["q"], s0["k"], s0["v"], s0["g"], s0["beta"], s0["cu"], chunk=CHUNK,
@@ -1259,37 +1257,18 @@ def main():
     def f64(t):
         return t.detach().to("cpu", torch.float64).numpy()
 
-    errs = parity_errors({"prefill_out": f64(s0["out"]), "prefill_state": f64(s0["fin"]),
-                          "decode_out": f64(s0["dout"]), "decode_state": f64(chk_state)}, ref)
-    parity = {"max_rel_err": errs, "bars": PARITY_BARS,
-              "pass": all(errs[k] <= PARITY_BARS[k] for k in PARITY_BARS),
-              "reference": "fp64 oracle, every token and value head of the timed step's inputs"}
+    gpu_check = {"prefill_out": f64(s0["out"]), "prefill_state": f64(s0["fin"]),
+                 "decode_out": f64(s0["dout"]), "decode_state": f64(chk_state)}
     del chk_state
-    if not parity["pass"]:
-        print(json.dumps({"metric": METRIC, "error": "parity gate failed: the GPU step does not match "
-                          "the oracle; no throughput is reported", "parity": parity}), flush=True)
-        sys.exit(1)
 
     stream = torch.cuda.current_stream(dev)
     probe_copies(dev, args.copy_probe_mib)
-    for i in range(args.warmup):
-        step(sets[i % args.copies])
-    torch.cuda.synchronize()
 
-    # ---- timed region: exactly --steps steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(sets[i % args.copies])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = e0.elapsed_time(e1) / args.steps
-
-    # ---- spread of the step time (a separate pass: an event pair per step)
-    per_step = []
+    # ---- measurement passes, each over --steps steps, before the timed
+    # region: they run right before it, so that the timed steps do not start
+    # on a GPU whose clocks dropped while it idled (measured after an 8 s
+    # pause: 157 us per step after 10 warm-up steps, 149 us after 100).
+    # spread of the step time (an event pair per step)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -1303,7 +1282,7 @@ def main():
     def pct(p):
         return per_step[min(len(per_step) - 1, int(round(p / 100 * (len(per_step) - 1))))]
 
-    # ---- per-kernel pass (same steps, each launch bracketed by events)
+    # each kernel's duration (every launch stamped by its own dispatch)
     gdn.timing_start(8 * args.steps)
     for i in range(args.steps):
         step(sets[i % args.copies])
@@ -1325,6 +1304,40 @@ def main():
                                          final_state=s["fin"], out=s["out"], workspace=s["ws"]), args.steps)
     ms_dec = timed(lambda s: gdn.decode_step(s["dq"], s["dk"], s["dv"], s["dg"], s["db"], s["state"],
                                              out=s["dout"]), args.steps)
+
+    # ---- warm-up, then the timed region: exactly --steps steps
+    for i in range(args.warmup):
+        step(sets[i % args.copies])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(sets[i % args.copies])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # ---- the oracle on the same inputs (this is also the CPU baseline) and
+    # the parity gate: no throughput is reported unless the checked step
+    # matches it.
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    threads = max(1, min(16, ncpu))
+    print("[bench] oracle reference (and CPU baseline)", file=sys.stderr, flush=True)
+    cpu_rec, ref = cpu_baseline(pre, dec, s_dec, threads, one_thread=not args.no_cpu_baseline)
+    errs = parity_errors(gpu_check, ref)
+    parity = {"max_rel_err": errs, "bars": PARITY_BARS,
+              "pass": all(errs[k] <= PARITY_BARS[k] for k in PARITY_BARS),
+              "reference": "fp64 oracle, every token and value head of the timed step's inputs"}
+    if not parity["pass"]:
+        print(json.dumps({"metric": METRIC, "error": "parity gate failed: the GPU step does not match "
+                          "the oracle; no throughput is reported", "parity": parity}), flush=True)
+        sys.exit(1)
 
     scan_ms = kt["scan"]["mean_ms"]
     prep_ms = kt["prep"]["mean_ms"]
