@@ -14,13 +14,8 @@ Inputs are synthetic (gdn_synth). Several copies of every buffer set are
 rotated through so that each step reads its state and inputs from HBM rather
 than from the 256 MB Infinity Cache left warm by the previous step.
 
-The prefill goes on torch's current stream and the decode on a second stream
-of default priority: the two batches are independent, and a serving engine
-issues them so.
-
-Timing: HIP events around exactly --steps steps after --warmup untimed steps
-(the first on the prefill stream, which the decode stream waits for; the last
-on the prefill stream after it waits for the decode stream), with
+Timing: HIP events on the stream the library launches on (torch's current
+stream), around exactly --steps steps after --warmup untimed steps, with
 torch.cuda.synchronize() on both sides. Measurement passes of the same steps
 run just before them: one brackets every step with events (the spread), one
 every kernel launch with the library's own event pairs (gdn_timing_start/
@@ -1244,31 +1239,10 @@ def main():
             dout=torch.empty((B_DECODE, HV, D), dtype=torch.bfloat16, device=dev),
         ))
 
-    # The step's prefill and decode batches are independent (their own
-    # inputs, outputs and states), so they go on two streams of default
-    # priority, as a serving engine would issue them: the prefill on torch's
-    # current stream, the decode on a second one. Work on the two overlaps
-    # where the kernels leave room (the decode fills the launch gaps and the
-    # tails of the prefill's kernels).
-    stream = torch.cuda.current_stream(dev)
-    dec_stream = torch.cuda.Stream(dev)
-
     def step(s):
         gdn.prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu"], chunk=CHUNK,
-                    final_state=s["fin"], out=s["out"], workspace=s["ws"], stream=stream)
-        gdn.decode_step(s["dq"], s["dk"], s["dv"], s["dg"], s["db"], s["state"], out=s["dout"], stream=dec_stream)
-
-    def open_region(ev):
-        """Record ev on the prefill stream and make the decode stream wait for it."""
-        ev.record(stream)
-        dec_stream.wait_event(ev)
-
-    def close_region(ev):
-        """Make the prefill stream wait for the decode stream, then record ev on it."""
-        joined = torch.cuda.Event()
-        joined.record(dec_stream)
-        stream.wait_event(joined)
-        ev.record(stream)
+                    final_state=s["fin"], out=s["out"], workspace=s["ws"])
+        gdn.decode_step(s["dq"], s["dk"], s["dv"], s["dg"], s["db"], s["state"], out=s["dout"])
 
     # ---- the GPU side of the parity check: one untimed step from fresh
     # decode states, its results copied to the host. The oracle runs on the
@@ -1276,9 +1250,8 @@ def main():
     s0 = sets[0]
     chk_state = torch.from_numpy(s_dec).to(dev)
     gdn.prefill(s0["q"], s0["k"], s0["v"], s0["g"], s0["beta"], s0["cu"], chunk=CHUNK,
-                final_state=s0["fin"], out=s0["out"], workspace=s0["ws"], stream=stream)
-    gdn.decode_step(s0["dq"], s0["dk"], s0["dv"], s0["dg"], s0["db"], chk_state, out=s0["dout"],
-                    stream=dec_stream)
+                final_state=s0["fin"], out=s0["out"], workspace=s0["ws"])
+    gdn.decode_step(s0["dq"], s0["dk"], s0["dv"], s0["dg"], s0["db"], chk_state, out=s0["dout"])
     torch.cuda.synchronize()
 
     def f64(t):
@@ -1288,6 +1261,7 @@ def main():
                  "decode_out": f64(s0["dout"]), "decode_state": f64(chk_state)}
     del chk_state
 
+    stream = torch.cuda.current_stream(dev)
     probe_copies(dev, args.copy_probe_mib)
 
     # ---- measurement passes, each over --steps steps, before the timed
@@ -1299,9 +1273,9 @@ def main():
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
-        open_region(evs[i][0])
+        evs[i][0].record(stream)
         step(sets[i % args.copies])
-        close_region(evs[i][1])
+        evs[i][1].record(stream)
     torch.cuda.synchronize()
     per_step = sorted(a.elapsed_time(b) for a, b in evs)
 
@@ -1329,7 +1303,7 @@ def main():
     ms_pre = timed(lambda s: gdn.prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu"], chunk=CHUNK,
                                          final_state=s["fin"], out=s["out"], workspace=s["ws"]), args.steps)
     ms_dec = timed(lambda s: gdn.decode_step(s["dq"], s["dk"], s["dv"], s["dg"], s["db"], s["state"],
-                                             out=s["dout"], stream=stream), args.steps)
+                                             out=s["dout"]), args.steps)
 
     # ---- warm-up, then the timed region: exactly --steps steps
     for i in range(args.warmup):
@@ -1338,10 +1312,10 @@ def main():
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    open_region(e0)
+    e0.record(stream)
     for i in range(args.steps):
         step(sets[i % args.copies])
-    close_region(e1)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = e0.elapsed_time(e1) / args.steps
@@ -1411,7 +1385,6 @@ def main():
         "config": {"workload": f"GDN layer step: prefill 1x{T_PREFILL} tokens + decode batch {B_DECODE}; "
                                f"HK={HK}, HV={HV}, d={D}, chunk {CHUNK}; bf16 q/k/v/out, fp32 gates/state",
                    "prefill_tokens": T_PREFILL, "decode_batch": B_DECODE, "parallelism": "single GPU",
-                   "streams": "prefill and decode batches on two streams of default priority",
                    "buffer_copies": args.copies},
         "roofline": roof,
         "roofline_scan": roof_scan,
