@@ -17,10 +17,10 @@ than from the 256 MB Infinity Cache left warm by the previous step.
 Timing: HIP events on the stream the library launches on (torch's current
 stream), around exactly --steps steps after --warmup untimed steps, with
 torch.cuda.synchronize() on both sides. Measurement passes of the same steps
-run just before them: one brackets every step with events (the spread), one
-every kernel launch with the library's own event pairs (gdn_timing_start/
-stop: each kernel's mean duration for the roofline), then prefill-only and
-decode-only rates. The parity check's GPU step runs first; the oracle it is
+run just before them: one brackets every step with events (the spread), then
+prefill-only and decode-only rates, then one brackets every kernel launch
+with the library's own event pairs (gdn_timing_start/stop: each kernel's
+mean duration for the roofline). The parity check's GPU step runs first; the oracle it is
 compared with (and the CPU baseline) runs after the timed region, so that the
 GPU does not idle for its ~20 s right before the timed steps.
 
@@ -1282,13 +1282,6 @@ def main():
     def pct(p):
         return per_step[min(len(per_step) - 1, int(round(p / 100 * (len(per_step) - 1))))]
 
-    # each kernel's duration (every launch stamped by its own dispatch)
-    gdn.timing_start(8 * args.steps)
-    for i in range(args.steps):
-        step(sets[i % args.copies])
-    kt = gdn.timing_stop()
-    torch.cuda.synchronize()
-
     # prefill-only and decode-only rates
     def timed(fn, n):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -1304,6 +1297,15 @@ def main():
                                          final_state=s["fin"], out=s["out"], workspace=s["ws"]), args.steps)
     ms_dec = timed(lambda s: gdn.decode_step(s["dq"], s["dk"], s["dv"], s["dg"], s["db"], s["state"],
                                              out=s["dout"]), args.steps)
+
+    # each kernel's duration (every launch stamped by its own dispatch), last,
+    # on clocks the passes above have brought up
+    gdn.timing_start(8 * args.steps)
+    for i in range(args.steps):
+        step(sets[i % args.copies])
+    kt = gdn.timing_stop()
+    torch.cuda.synchronize()
+
 
     # ---- warm-up, then the timed region: exactly --steps steps
     for i in range(args.warmup):
