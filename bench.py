@@ -188,8 +188,11 @@ def summarize_profiles(stats_dir: str, fetch_dir: str, write_dir: str, probe_mib
     fetch, ffac, fkib = _counter_means(fetch_dir, "FETCH_SIZE", probe_bytes)
     write, wfac, wkib = _counter_means(write_dir, "WRITE_SIZE", probe_bytes)
     h = kernel_source_hash()
+    rd = _probe_check(fetch_dir, "FETCH_SIZE", ffac, probe_bytes, "reduce_kernel")
+    wr = _probe_check(write_dir, "WRITE_SIZE", wfac, probe_bytes, "FillFunctor")
     traffic = {"source_hash": h, "probe_copy_bytes": probe_bytes,
-               "fetch_bytes_per_kib": ffac, "write_bytes_per_kib": wfac}
+               "fetch_bytes_per_kib": ffac, "write_bytes_per_kib": wfac,
+               "check_read_only_sum_fetch_ratio": rd, "check_write_only_fill_write_ratio": wr}
     for short in ("schedule", "prep", "scan", "decode"):
         if short in fetch and short in write:
             fb, wb = fetch[short] * ffac, write[short] * wfac
@@ -237,7 +240,10 @@ def summarize_profiles(stats_dir: str, fetch_dir: str, write_dir: str, probe_mib
         "## HBM bytes per launch (FETCH_SIZE, WRITE_SIZE; scaled by a plain copy)",
         "",
         f"A {probe_mib} MiB device-to-device copy in the same runs reads {fkib:.0f} FETCH_SIZE units and "
-        f"{wkib:.0f} WRITE_SIZE units: {ffac:.1f} and {wfac:.1f} bytes per unit.",
+        f"{wkib:.0f} WRITE_SIZE units: {ffac:.1f} and {wfac:.1f} bytes per unit."
+        + ("" if rd is None or wr is None else
+           f" Checked on other request mixes of the same size in the same runs: a read-only sum fetches "
+           f"{rd:.3f} of its bytes and a write-only fill writes {wr:.3f} of its bytes by these factors."),
         "",
         "| kernel | fetched MB | written MB | total MB |",
         "|---|---|---|---|",
@@ -440,8 +446,11 @@ def short_prefill_sweep(dev, copies, steps):
 
 
 def probe_copies(dev, mib):
-    """Three device-to-device copies of `mib` MiB: the known-size reference
-    that scales the HBM byte counters of a --pmc run."""
+    """Known-size references for the HBM byte counters of a --pmc run: three
+    device-to-device copies of `mib` MiB (they read and write it; the
+    counters are scaled by them), and, to check that the same scale holds for
+    other request mixes, a fill (writes it only) and three sums (read it only)
+    of the same size."""
     if mib <= 0:
         return
     import torch
@@ -450,8 +459,29 @@ def probe_copies(dev, mib):
     torch.cuda.synchronize()
     for _ in range(3):
         dst.copy_(src)
+    words = src.view(torch.float32)
+    for _ in range(3):
+        torch.sum(words)
     torch.cuda.synchronize()
-    del src, dst
+    del src, dst, words
+
+
+def _probe_check(directory: str, counter: str, factor: float, probe_bytes: int, tag: str):
+    """The bytes a probe of probe_bytes moves by `counter` at the copy-derived
+    factor, as a fraction of probe_bytes: the largest dispatches (within 10%)
+    of torch kernels whose name holds `tag` (FillFunctor: the fill,
+    reduce_kernel: the sums). None when the run has no such dispatch."""
+    import csv
+    vals = []
+    with open(os.path.join(directory, "run_counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and tag in r["Kernel_Name"] and _short_kernel(r["Kernel_Name"]) == "other":
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        return None
+    top = max(vals)
+    pick = [v for v in vals if v >= 0.9 * top]
+    return sum(pick) / len(pick) * factor / probe_bytes
 
 
 def summarize_norm(stats_dir: str, fetch_dir: str, write_dir: str, results_jsonl: str, probe_mib: int):
