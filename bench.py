@@ -1081,8 +1081,8 @@ def graph_bench(dev, steps):
 
 
 # Shapes for the tuning sweep: (sequences, tokens each).
-TUNE_SHAPES = ((1, 16), (1, 48), (1, 128), (1, 512), (8, 4), (64, 1), (64, 4), (64, 16), (8, 300), (2, 600),
-               (2, 2048), (1, 4096))
+TUNE_SHAPES = ((1, 16), (1, 48), (1, 128), (1, 512), (8, 4), (64, 1), (64, 4), (64, 16), (16, 16), (32, 24),
+               (32, 128), (8, 300), (2, 600), (8, 512), (4, 1024), (2, 2048), (1, 4096))
 
 
 def tuning_sweep(dev, copies, steps):

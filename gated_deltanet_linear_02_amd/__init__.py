@@ -186,7 +186,7 @@ def prefill_plan(num_seqs: int, total_tokens: int, hk: int, hv: int, d: int, chu
                  io_dtype: torch.dtype = torch.bfloat16, gate_dtype: torch.dtype = torch.float32) -> Tuple[int, int]:
     """The method ``prefill`` uses for these sizes (``gdn_prefill_method``):
     (chunk, rows) with chunk 1 (token by token), 16, 32 or 64 and rows the
-    chunked scan's state rows per workgroup (16 or 32; 0 token by token);
+    chunked scan's state rows per workgroup (16, 32, 64 or 128; 0 token by token);
     (0, 0) if the sizes are rejected."""
     rows = ctypes.c_int32(0)
     c = load().gdn_prefill_method(num_seqs, total_tokens, hk, hv, d, d, chunk, _dtype_code(io_dtype),
@@ -348,7 +348,8 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
 
 # gdn_tune_prefill's candidates in its order: (chunk, state rows per scan
 # workgroup), named "chunk/rows" ("1" token by token).
-TUNE_CANDIDATES = ((64, 16), (64, 32), (32, 16), (32, 32), (16, 16), (16, 32), (1, 0))
+TUNE_CANDIDATES = ((64, 16), (64, 32), (64, 64), (64, 128), (32, 16), (32, 32), (32, 64), (32, 128),
+                   (16, 16), (16, 32), (16, 64), (16, 128), (1, 0))
 
 
 def method_name(chunk: int, rows: int) -> str:

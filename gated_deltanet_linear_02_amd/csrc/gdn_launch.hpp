@@ -128,13 +128,15 @@ inline int64_t scan_grid(int64_t num_seqs, int64_t hk, int64_t hv, int64_t dv, i
 }
 
 // Whether a chunked prefill with an output normalisation takes it in the
-// scan: when the scan's workgroups fit the GPU in one pass. The row slices
-// of a head then exchange their partial sums of squares while all of them
-// run; with more workgroups than CUs, slices of one head could wait on one
-// another across passes, so those calls normalise in a pass after the scan.
+// scan: when one workgroup holds a head's whole state (rows = dv), which
+// normalises its own rows, or when the scan's workgroups fit the GPU in one
+// pass. The row slices of a head then exchange their partial sums of squares
+// while all of them run; with more workgroups than CUs, slices of one head
+// could wait on one another across passes, so those calls normalise in a
+// pass after the scan.
 constexpr int64_t kFusedNormMaxWgs = 256;  // gfx950 (MI355X): 256 CUs
 inline bool fused_norm_fits(int64_t num_seqs, int64_t hk, int64_t hv, int64_t dv, int64_t rows) {
-    return scan_grid(num_seqs, hk, hv, dv, rows) <= kFusedNormMaxWgs;
+    return rows == dv || scan_grid(num_seqs, hk, hv, dv, rows) <= kFusedNormMaxWgs;
 }
 
 // Chunked prefill (chunk 16, 32 or 64): preparation and scan kernels.
@@ -169,9 +171,9 @@ struct Method {
 Method tuned_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv, int32_t d, int32_t io,
                     int32_t gate);
 
-// gdn_prefill with the method given (chunk 1, 16, 32 or 64 and, chunked, 16
-// or 32 state rows per scan workgroup); GDN_ERR_UNSUPPORTED for rows that do
-// not fit the call.
+// gdn_prefill with the method given (chunk 1, 16, 32 or 64 and, chunked, 16,
+// 32, 64 or 128 state rows per scan workgroup); GDN_ERR_UNSUPPORTED for rows
+// that do not fit the call.
 int32_t prefill_with_method(const void *q, const void *k, const void *v, const void *g, const void *beta,
                             const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t hk,
                             int32_t hv, int32_t dk, int32_t dv, Method m, float scale, int32_t io_dtype,
@@ -180,41 +182,55 @@ int32_t prefill_with_method(const void *q, const void *k, const void *v, const v
 
 // gdn_prefill with chunk 0, when nothing is tuned for the shape, picks the
 // method from host-known sizes alone (the lengths stay on the device), by
-// the mean sequence length L = T / N. Measured at HK = 16, HV = 32, d = 128:
-//   token by token   T <= 32, or L <= 24: the chunked path's fixed costs
-//                    dominate (one 16-token prompt: 8.5 vs 12.8 us; 64
-//                    sequences of 24 tokens: 226 vs 283 us at best chunked);
-//   chunks of 16     L <= 48: the fewest padded rows (64 x 32: 287 vs 336 us
-//                    with 64);
-//   chunks of 32     the scan's workgroups, with the state rows per
-//                    workgroup it takes, fit the GPU in one pass (at most
-//                    one per CU) and L <= 1024: a lone sequence is bound by
-//                    its chain's latency, which shorter chunks cut (1 x 512:
-//                    29.8 vs 32.5 us);
+// the mean sequence length L = T / N and the state rows per scan workgroup
+// (scan_slice_rows). Measured at HK = 16, HV = 32, d = 128 (whole prefill):
+//   token by token   T <= 32, or L <= 10: the chunked path's fixed costs
+//                    dominate (one 16-token prompt: 8 vs 13 us; 64 x 8: 93
+//                    vs 144 us at best chunked; the crossover lies between
+//                    L = 9 and 14 for 8 to 256 sequences);
+//   64 or 128 rows   (several sequences) one chunk step per sequence where
+//                    it takes one: chunks of 16 for L <= 16, of 32 for
+//                    L <= 32 (the step of a wide slice is long, so fewer
+//                    steps count: 32 x 24: 62 us with chunks of 32, 67.5
+//                    with 16), else of 64;
+//   chunks of 16     (16 or 32 rows) L <= 48: the fewest padded rows;
+//   chunks of 32     (16 or 32 rows) the scan's workgroups fit the GPU in one
+//                    pass (at most one per CU) and L <= 1024: a lone sequence
+//                    is bound by its chain's latency, which shorter chunks cut
+//                    (1 x 512: 28 vs 32 us);
 //   chunks of 64     otherwise: with several passes over the GPU the total
-//                    work counts, which the largest chunks minimise (8 x 300:
-//                    87 vs 101 us with 32).
+//                    work counts, which the largest chunks minimise.
 constexpr int64_t kTokenScanTokens = 32;
-constexpr int64_t kTokenScanPerSeq = 24;
+constexpr int64_t kTokenScanPerSeq = 10;
 constexpr int64_t kChunk16PerSeq = 48;
 constexpr int64_t kChunk32PerSeq = 1024;
 constexpr int64_t kScanOnePassWgs = 256;  // gfx950 (MI355X): 256 CUs
-// State rows per chunked-scan workgroup: 32 when 16-row slices would take
-// more than one pass over the CUs (bf16 I/O, d >= 32), else 16.
+// State rows per chunked-scan workgroup: 16, 32, 64 or 128, more than 16
+// for bf16 I/O only and at most dv.
 inline bool slice_rows_fit(int32_t rows, int64_t dv, bool io_bf16) {
-    return rows == 16 || (rows == 32 && io_bf16 && dv >= 32);
+    return rows == 16 || ((rows == 32 || rows == 64 || rows == 128) && io_bf16 && dv >= rows);
 }
+// Every workgroup of a head loads the head's whole chunk operands, so wider
+// slices cut those loads per state row, at the cost of a longer chunk step.
+// The scan takes the narrowest slices whose workgroups fit the CUs in one
+// pass, else the widest. Measured at HK = 16, HV = 32, d = 128 (whole
+// prefill, us, 16 / 32 / 64 / 128 rows): 1 x 4096: 87.5 / 100.8 / 141 / 232;
+// 2 x 2048: 89.7 / 76.8 / 89.9 / 133; 4 x 1024: 95.1 / 76.7 / 66.8 / 84.9;
+// 8 x 512: 109 / 81.6 / 70.4 / 66.9; 32 x 128: 186 / 128 / 105 / 92.9.
 inline int32_t scan_slice_rows(int64_t num_seqs, int64_t hv, int64_t dv, bool io_bf16) {
-    return io_bf16 && dv >= 32 && num_seqs * hv * (dv / 16) > kScanOnePassWgs ? 32 : 16;
+    int32_t rows = 16;
+    while (slice_rows_fit(rows * 2, dv, io_bf16) && num_seqs * hv * (dv / rows) > kScanOnePassWgs) rows *= 2;
+    return rows;
 }
 
 inline int32_t rule_chunk(int64_t num_seqs, int64_t total_tokens, int64_t hv, int64_t dv, bool io_bf16) {
     if (total_tokens <= kTokenScanTokens || total_tokens <= kTokenScanPerSeq * num_seqs) return 1;
+    const int64_t rows = scan_slice_rows(num_seqs, hv, dv, io_bf16);
+    if (rows >= 64) return total_tokens <= 16 * num_seqs ? 16 : total_tokens <= 32 * num_seqs ? 32 : 64;
     if (total_tokens <= kChunk16PerSeq * num_seqs) return 16;
     // one pass with the slice rows the scan will take (2 x 600: 32-row
-    // slices fill the 256 CUs once, and chunks of 32 measure 40.2 against
-    // 42.7 us)
-    const int64_t rows = scan_slice_rows(num_seqs, hv, dv, io_bf16);
+    // slices fill the 256 CUs once, and chunks of 32 measure 38.5 against
+    // 41 us)
     if (num_seqs * hv * (dv / rows) <= kScanOnePassWgs && total_tokens <= kChunk32PerSeq * num_seqs) return 32;
     return 64;
 }

@@ -618,7 +618,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
 }
 
 // ---------------------------------------------------------------------------
-// 3. Chunk-recurrent scan over one (sequence, value head, 16 or 32 value rows)
+// 3. Chunk-recurrent scan over one (sequence, value head, 16, 32, 64 or 128
+//    value rows)
 // ---------------------------------------------------------------------------
 //
 // Eight waves per workgroup, two per SIMD, in two roles. With S0 the slice at
@@ -642,8 +643,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
 
 constexpr int kScanThreads = 512;
 
-// R: value rows of the state per workgroup (16, or 32 on bf16 I/O).
-template <typename E, int C, int DK, int R>
+// Steps from a chunk's outputs to its normalised rows in the fused
+// normalisation's exchange (and steps after the last chunk in which it
+// writes the last chunks' rows).
+constexpr int kNormLag = 4;
+static_assert((kNormLag & (kNormLag - 1)) == 0, "the pending outputs are a ring of kNormLag chunks");
+
+// R: value rows of the state per workgroup (16, or 32, 64, 128 on bf16 I/O).
+// kPend: the fused normalisation exchanges partial sums between the slices
+// of a head, and keeps each output wave's unnormalised outputs of the last
+// kNormLag chunks.
+template <typename E, int C, int DK, int R, bool kPend = false>
 struct ScanSmem {
     static constexpr int PE = Pad<E>::value;
     static constexpr int LDK = DK + PE;  // rows of length DK
@@ -661,7 +671,10 @@ struct ScanSmem {
     static constexpr size_t off_Np = off_Gc + 8 * sizeof(float);                   // [C]
     static constexpr size_t off_Nb = off_Np + (size_t)C * sizeof(float);           // [DK / R][C]
     static constexpr size_t off_Nt = off_Nb + (size_t)(DK / R) * C * sizeof(float);  // [C]
-    static constexpr size_t bytes = off_Nt + (size_t)C * sizeof(float);
+    static constexpr size_t off_Nw = off_Nt + (size_t)C * sizeof(float);              // [R] weights
+    // [kNormLag][4 output waves][R / 16][64 lanes] f32x4: a ring by chunk
+    static constexpr size_t off_Pd = (off_Nw + (size_t)R * sizeof(float) + 15) & ~(size_t)15;
+    static constexpr size_t bytes = off_Pd + (kPend ? (size_t)kNormLag * 4 * (R / 16) * 64 * 16 : 0);
 };
 
 template <typename E> struct Vec4;
@@ -716,6 +729,7 @@ struct RStage {
 };
 
 struct NoAux {};
+template <int N> struct VRows { f32x4 x[N]; };
 
 // An output wave's operands for one chunk (and that chunk's V rows, which
 // the wave stages one chunk earlier).
@@ -726,8 +740,9 @@ struct OStage {
     typename S::MC::Frag pf[NT];  // P: the NT blocks read (tri_read_blocks)
     typename S::E4 vr;  // fp32: V[16 q + l/4][4 (l%4) ..]
     f32x4 aux = {0.f, 0.f, 0.f, 0.f};  // auxiliary load (see the output role of the scan)
-    // 32-row slices: the V rows 16 q .. 16 q + 15 of the slice (8 values per lane)
-    typename std::conditional<(R > 16), f32x4, NoAux>::type vaux;
+    // Slices of 32 rows or more: the V rows 16 q .. 16 q + 15 of the slice,
+    // 8 values per lane and load, R / 32 loads
+    typename std::conditional<(R > 16), VRows<R / 32>, NoAux>::type vaux;
 
     __device__ __forceinline__ void load(const E *__restrict__ v, const E *__restrict__ pmat,
                                          const E *__restrict__ qmat, const ChunkRef &r, int hv, int h,
@@ -785,11 +800,6 @@ constexpr int kTouchAhead = 8;
 // never ran, and the rows it leaves are written as NaN rather than wrong.
 constexpr int kNormSpinMax = 1 << 20;
 
-// Steps from a chunk's outputs to its normalised rows in the fused
-// normalisation's exchange (and steps after the last chunk in which it
-// writes the last chunks' rows).
-constexpr int kNormLag = 4;
-
 // Word 3 of a raw buffer resource on gfx9-family GPUs (gfx950 included).
 constexpr int kBufferWord3 = 0x00020000;
 
@@ -805,8 +815,9 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
     int32_t num_seqs, int32_t hk, int32_t hv,
     const float *__restrict__ norm_w, float norm_eps, float *__restrict__ norm_part)
 {
-    static_assert(R == 16 || (R == 32 && IsBf16<E>::value && DK >= 32), "32-row slices: bf16, d >= 32");
-    typedef ScanSmem<E, C, DK, R> L;
+    static_assert(R == 16 || ((R == 32 || R == 64 || R == 128) && IsBf16<E>::value && DK >= R),
+                  "slices of 32 rows or more: bf16, d >= rows");
+    typedef ScanSmem<E, C, DK, R, kNorm && (DK / R > 1)> L;
     typedef ScanShape<E, C, DK> SH;
     typedef typename SH::MD MD;
     typedef typename SH::MC MC;
@@ -822,7 +833,11 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
     // The fused normalisation's exchange alternates two register slots by
     // chunk parity, which the unrolled pipeline keeps compile-time when the
     // output stages are even.
-    constexpr int kRStages = R == 16 ? 4 : 3, kOStages = R == 16 && !kNorm ? 5 : 4;
+    constexpr int kRStages = R == 16 ? 4 : 3, kOStages = R == 16 && !kNorm ? 5 : R <= 32 ? 4 : 3;
+    // The fused normalisation: with several slices per head they exchange
+    // partial sums (kNormX); a slice that holds the whole head (R = DV)
+    // normalises its rows in the output wave that computes them (kNormW).
+    constexpr bool kNormX = kNorm && NS > 1, kNormW = kNorm && NS == 1;
 
     extern __shared__ __align__(16) char smem[];
     E *sS = reinterpret_cast<E *>(smem + L::off_S);
@@ -980,7 +995,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             }
         }
 
-        if constexpr (kNorm) {
+        if constexpr (kNormX) {
             if (nch > 0) {  // the output waves' drain
                 for (int st = 0; st < 2 * kNormLag; ++st) __syncthreads();
             }
@@ -1013,9 +1028,10 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         //              the value is only kept alive until the stage is
         //              refilled;
         //   waves 2-3  16-row slices: the chunk's V rows 32 (q - 2) .. + 31
-        //              (8 values per lane), staged in LDS; 32-row slices:
+        //              (8 values per lane), staged in LDS; wider slices:
         //              another L2 touch, and every output wave loads the V
-        //              rows 16 q .. 16 q + 15 of its 32 columns besides.
+        //              rows 16 q .. 16 q + 15 of its R columns besides (R / 32
+        //              loads).
         // Memory instructions, not bytes, bound the scan, so these small
         // loads are folded into as few instructions as possible. The fp32
         // path (one stage) loads V per wave and the gate record in every wave.
@@ -1038,7 +1054,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             // preparation kernel has just written)
             constexpr int kLinesPerRow = DK * (int)sizeof(E) >= 128 ? DK * (int)sizeof(E) / 128 : 1;
             const int nlines = nops + C * group * kLinesPerRow;
-            // 32-row slices: half the workgroups per query/key head, touching
+            // wider slices: fewer workgroups per query/key head, touching
             // from waves 1-3
             const int part = R == 16 ? within : within * 3 + (q - 1);
             const int line = (part * 64 + lane) % nlines;
@@ -1082,7 +1098,9 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             if constexpr (R > 16) {
                 const ChunkRef r = chunk(c_aux);
                 const int vrow = min(16 * q + (lane >> 2), r.clen - 1);
-                st.vaux = *reinterpret_cast<const f32x4 *>(v + ((size_t)(r.tok0 + vrow) * hv + h) * DK + col0 + 8 * (lane & 3));
+                const E *src = v + ((size_t)(r.tok0 + vrow) * hv + h) * DK + col0 + 8 * (lane & 3);
+#pragma unroll
+                for (int j = 0; j < R / 32; ++j) st.vaux.x[j] = *reinterpret_cast<const f32x4 *>(src + 32 * j);
             }
         };
         // A chunk's staged inputs into LDS buffer `buf`: the gate vectors
@@ -1100,10 +1118,13 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             if constexpr (R > 16) {
                 const int t = 16 * q + (lane >> 2);
                 if (t < C) {
-                    const bf16x8 x = __builtin_bit_cast(bf16x8, st.vaux);
                     E *dst = sVt + buf * (R * LDC) + lds_pos<MC>(t);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) dst[(8 * (lane & 3) + i) * LDC] = x[i];
+                    for (int j = 0; j < R / 32; ++j) {
+                        const bf16x8 x = __builtin_bit_cast(bf16x8, st.vaux.x[j]);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) dst[(32 * j + 8 * (lane & 3) + i) * LDC] = x[i];
+                    }
                 }
             } else if constexpr (kPipelined) {
                 if (q >= 2) {
@@ -1121,12 +1142,15 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                 for (int i = 0; i < 4; ++i) dst[(4 * (lane & 3) + i) * LDC] = vr[i];
             }
         };
-        // ---- output normalisation fused in (kNorm). A (token, value head)
-        // output row spans the NS row slices of the head, each its own
-        // workgroup. Per chunk c, in the workgroup's step
+        // ---- output normalisation fused in (kNorm). A slice of the whole
+        // head (NS = 1) normalises each row in the output wave that computes
+        // it. Otherwise a (token, value head) output row spans the NS row
+        // slices of the head, each its own workgroup. Per chunk c, in the
+        // workgroup's step
         //   c      every output wave computes its tokens' partial sums of
         //          squares (its columns, then the token's four lane groups)
-        //          into LDS, after its outputs;
+        //          into LDS, after its outputs, which it keeps in an LDS ring
+        //          of kNormLag chunks;
         //   c + 1  output wave 0 publishes the chunk's C partials in the slot
         //          block (chunk, head, slice) with one device-coherent store
         //          (each slot holds kNormPartEmpty until then, set by the
@@ -1137,7 +1161,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         //   c + 4  output wave 1 adds each token's NS partials in slice order
         //          (the same sum in every slice) into LDS, and every output
         //          wave writes its rows o w / sqrt(mean + eps): one rounding
-        //          of the unrounded outputs kept in registers.
+        //          of the unrounded outputs kept in the ring.
         // Three memory instructions per workgroup and chunk in all. Each slot
         // is written once per call, so a value other than kNormPartEmpty is
         // that call's partial; the rare wait for a slice behind spins with
@@ -1146,17 +1170,14 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         float *sNp = reinterpret_cast<float *>(smem + L::off_Np);
         float *sNb = reinterpret_cast<float *>(smem + L::off_Nb);
         float *sNt = reinterpret_cast<float *>(smem + L::off_Nt);
-        f32x4 nw[RW], pend[kNormLag][RW];  // pend[j]: outputs of chunk c - 1 - j
-#pragma unroll
-        for (int rr = 0; rr < RW; ++rr) {
-#pragma unroll
-            for (int j = 0; j < kNormLag; ++j) pend[j][rr] = f32x4{0.f, 0.f, 0.f, 0.f};
-            nw[rr] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if constexpr (kNorm) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) nw[rr][i] = norm_w[col0 + 16 * rr + 4 * g4 + i];
-            }
+        // the slice's normalisation weights, staged in LDS before the first
+        // barrier; weight(rr): this lane's four columns of row tile rr
+        float *sNw = reinterpret_cast<float *>(smem + L::off_Nw);
+        if constexpr (kNorm) {
+            const int ot = tid - 256;  // this output wave's thread
+            if (ot >= 0 && ot < R) sNw[ot] = norm_w[col0 + ot];
         }
+        auto weight = [&](int rr) { return *reinterpret_cast<const f32x4 *>(sNw + 16 * rr + 4 * g4); };
         auto chunk_rows = [&](int cc) { return min(C, len - cc * C); };
         // The head's block of chunk cc's partials, NS x C floats, through a
         // buffer resource: 16-byte loads and stores that bypass the CU's
@@ -1264,24 +1285,27 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             if (q == 0 && st >= 1 && st - 1 < nch) publish_block(st - 1);
             if (q == 1 && st >= kNormLag && st - kNormLag < nch) sum_block(st - kNormLag, par);
         };
-        auto rotate = [&](const f32x4 (&oc)[RW]) {
-#pragma unroll
-            for (int rr = 0; rr < RW; ++rr) {
-#pragma unroll
-                for (int j = kNormLag - 1; j > 0; --j) pend[j][rr] = pend[j - 1][rr];
-                pend[0][rr] = oc[rr];
-            }
+        // The wave's unnormalised outputs of chunk cc, in the LDS ring (each
+        // lane reads back only what it wrote).
+        auto pend_at = [&](int cc, int rr) -> f32x4 * {
+            return reinterpret_cast<f32x4 *>(smem + L::off_Pd) +
+                   ((((cc & (kNormLag - 1)) * 4 + q) * RW + rr) * 64 + lane);
         };
-        // Normalise and store chunk cc's outputs po (its totals in LDS).
-        auto finish = [&](int cc, const f32x4 (&po)[RW]) {
+        auto stash = [&](int cc, const f32x4 (&oc)[RW]) {
+#pragma unroll
+            for (int rr = 0; rr < RW; ++rr) *pend_at(cc, rr) = oc[rr];
+        };
+        // Normalise and store chunk cc's outputs (its totals in LDS).
+        auto finish = [&](int cc) {
             const int row = 16 * q + ln;
             const float r = 1.0f / sqrtf(sNt[row] * (1.0f / DV) + norm_eps);
             if (row < chunk_rows(cc)) {
 #pragma unroll
                 for (int rr = 0; rr < RW; ++rr) {
+                    const f32x4 po = *pend_at(cc, rr), wr = weight(rr);
                     E4 w;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(po[rr][i] * r * nw[rr][i]);
+                    for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(po[i] * r * wr[i]);
                     *reinterpret_cast<E4 *>(out + ((size_t)(start + cc * C + row) * hv + h) * DV + col0 + 16 * rr +
                                             4 * g4) = w;
                 }
@@ -1322,7 +1346,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             // the step's parity: compile-time in the unrolled pipeline
             constexpr int kIdx = decltype(idx)::value;
             const int par = kIdx >= 0 && kOStages % 2 == 0 ? (kIdx & 1) : (c & 1);
-            if constexpr (kNorm) norm_phase1(c, par);
+            if constexpr (kNormX) norm_phase1(c, par);
             // ---- phase 1: O1^T = S0 Q^T
             f32x4 o1[RW];
 #pragma unroll
@@ -1359,13 +1383,35 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                         }
                     }
                 }
-                if constexpr (kNorm) {
+                if constexpr (kNormX) {
                     put_partials(c, oc);
-                    if (c >= kNormLag) finish(c - kNormLag, pend[kNormLag - 1]);
-                    rotate(oc);
+                    if (c >= kNormLag) finish(c - kNormLag);  // its slot, then this chunk's
+                    stash(c, oc);
+                }
+                if constexpr (kNormW) {
+                    // the whole row: this lane's columns, then its 4 lane groups
+                    float sq = 0.f;
+#pragma unroll
+                    for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sq = __builtin_fmaf(oc[rr][i], oc[rr][i], sq);
+                    sq += __shfl_xor(sq, 16);
+                    sq += __shfl_xor(sq, 32);
+                    const float rs = 1.0f / sqrtf(sq * (1.0f / DV) + norm_eps);
+                    if (row < clen) {
+#pragma unroll
+                        for (int rr = 0; rr < RW; ++rr) {
+                            const f32x4 wr = weight(rr);
+                            E4 w;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) w[i] = from_f32<E>(oc[rr][i] * rs * wr[i]);
+                            *reinterpret_cast<E4 *>(out + ((size_t)(tok0 + row) * hv + h) * DV + col0 + 16 * rr +
+                                                    4 * g4) = w;
+                        }
+                    }
                 }
             }
-            if constexpr (kNorm) {
+            if constexpr (kNormX) {
                 if (q == 1) load_block(max(c + 2 - kNormLag, 0), par);
             }
             __syncthreads();
@@ -1383,16 +1429,14 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             } else {
                 for (int c = 0; c < nch; ++c) body(st[0], st[0], st[0], c, std::false_type(), std::integral_constant<int, -1>());
             }
-            if constexpr (kNorm) {
+            if constexpr (kNormX) {
                 // the last kNormLag chunks' outputs, in kNormLag more steps
                 // of two barriers (the recurrence waves take part)
                 for (int st = nch; st < nch + kNormLag; ++st) {
                     norm_phase1(st, st & 1);
                     __syncthreads();
-                    if (q < RT && st - kNormLag >= 0) finish(st - kNormLag, pend[kNormLag - 1]);
+                    if (q < RT && st - kNormLag >= 0) finish(st - kNormLag);
                     if (q == 1 && st + 2 - kNormLag >= 0 && st + 2 - kNormLag < nch) load_block(st + 2 - kNormLag, st & 1);
-                    const f32x4 none[RW] = {};
-                    rotate(none);
                     __syncthreads();
                 }
             }
@@ -1419,7 +1463,7 @@ template <typename E, int C, int D, typename SE, int R, bool kNorm>
 static hipError_t launch_scan_n(const PrefillArgs &A, hipStream_t st, int32_t *bounds, int32_t *seq_chunk0,
                                 int32_t *order, E *tbmat, E *pmat, E *wmat, E *qmat, E *ktmat, float *gates,
                                 float *norm_part) {
-    typedef ScanSmem<E, C, D, R> SL;
+    typedef ScanSmem<E, C, D, R, kNorm && (D / R > 1)> SL;
     static std::atomic<bool> scan_ok{false};
     auto scan = gdn_scan_kernel<E, C, D, SE, R, kNorm>;
     hipError_t e;
@@ -1445,9 +1489,9 @@ static hipError_t launch_scan_r(const PrefillArgs &A, hipStream_t st, int32_t *b
                                                 gates, norm_part);
 }
 
-// Every 16-row slice loads the head's whole chunk operands, so 32-row slices
-// halve those loads per state row at the cost of a longer chunk step. That
-// pays once 16-row slices take more than one pass over the CUs (several
+// Every slice loads the head's whole chunk operands, so wider slices cut
+// those loads per state row at the cost of a longer chunk step. That pays
+// once narrower slices take more than one pass over the CUs (several
 // sequences, or many heads); a single pass keeps the shorter step. The caller
 // picks (scan_slice_rows, or a tuned choice).
 template <typename E, int C, int D, typename SE>
@@ -1458,6 +1502,16 @@ static hipError_t launch_scan(const PrefillArgs &A, hipStream_t st, int32_t *bou
         if (A.slice_rows == 32)
             return launch_scan_r<E, C, D, SE, 32>(A, st, bounds, seq_chunk0, order, tbmat, pmat, wmat, qmat, ktmat,
                                                   gates, norm_part);
+    }
+    if constexpr (IsBf16<E>::value && D >= 64) {
+        if (A.slice_rows == 64)
+            return launch_scan_r<E, C, D, SE, 64>(A, st, bounds, seq_chunk0, order, tbmat, pmat, wmat, qmat, ktmat,
+                                                  gates, norm_part);
+    }
+    if constexpr (IsBf16<E>::value && D >= 128) {
+        if (A.slice_rows == 128)
+            return launch_scan_r<E, C, D, SE, 128>(A, st, bounds, seq_chunk0, order, tbmat, pmat, wmat, qmat, ktmat,
+                                                   gates, norm_part);
     }
     return launch_scan_r<E, C, D, SE, 16>(A, st, bounds, seq_chunk0, order, tbmat, pmat, wmat, qmat, ktmat, gates,
                                           norm_part);
@@ -1481,7 +1535,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &A, hipStream_t st) {
     float *gates = reinterpret_cast<float *>(ws + Y.off_gates);
     float *norm_part = reinterpret_cast<float *>(ws + Y.off_norm_part);
     // state rows per scan workgroup (launch_scan takes 32 only where it fits)
-    const int scan_rows = IsBf16<E>::value && D >= 32 && A.slice_rows == 32 ? 32 : 16;
+    const int scan_rows = IsBf16<E>::value && A.slice_rows > 16 && A.slice_rows <= D ? A.slice_rows : 16;
 
     // Up to kFoldMaxSeqs sequences the preparation kernel schedules itself.
     const bool fold = A.num_seqs <= kFoldMaxSeqs;
@@ -1500,7 +1554,8 @@ static hipError_t launch_prefill_t(const PrefillArgs &A, hipStream_t st) {
                       fold ? A.cu : nullptr, A.num_seqs, (int32_t)A.total_tokens, bounds, seq_chunk0, order,
                       (const int32_t *)chunk_seq, (const int32_t *)chunk_tok0, (const int32_t *)counters,
                       tbmat, pmat, wmat, qmat, ktmat, gates, A.hk, A.hv, A.scale,
-                      A.norm_w ? norm_part : nullptr, A.norm_w ? (int32_t)(D / scan_rows) : 0);
+                      A.norm_w && scan_rows < D ? norm_part : nullptr,
+                      A.norm_w && scan_rows < D ? (int32_t)(D / scan_rows) : 0);
     if (e != hipSuccess) return e;
 
     if constexpr (IsBf16<E>::value) {

@@ -2,7 +2,7 @@
 // correctness gate (gfx950).
 //
 // Which evaluation of the recurrence is fastest, token by token or chunked
-// with C = 16, 32 or 64 and 16 or 32 state rows per scan workgroup, depends
+// with C = 16, 32 or 64 and 16, 32, 64 or 128 state rows per scan workgroup, depends
 // on the shape and the hardware ("Optimiser
 // l'inference sur appareil pour Apple Silicon", section "Qwen cree trois
 // formes de charges de travail distinctes"). The engine of "On descend d'un
@@ -200,8 +200,9 @@ int32_t gdn_tune_prefill(const void *q, const void *k, const void *v, const void
                          int32_t *chosen_chunk, int32_t *chosen_rows, float *candidate_ms,
                          float *candidate_err) {
     // (chunk, state rows per scan workgroup), the reference first
-    static const Method kCandidates[GDN_TUNE_CANDIDATES] = {{64, 16}, {64, 32}, {32, 16}, {32, 32},
-                                                            {16, 16}, {16, 32}, {1, 0}};
+    static const Method kCandidates[GDN_TUNE_CANDIDATES] = {{64, 16}, {64, 32}, {64, 64}, {64, 128}, {32, 16},
+                                                            {32, 32}, {32, 64}, {32, 128}, {16, 16}, {16, 32},
+                                                            {16, 64}, {16, 128}, {1, 0}};
     constexpr int NC = GDN_TUNE_CANDIDATES;
     if (!chosen_chunk) return GDN_ERR_NULL_ARG;
     if (!(gate_tol >= 0.f) || !(gate_tol <= 1.f)) return GDN_ERR_BAD_VALUE;
@@ -236,7 +237,7 @@ int32_t gdn_tune_prefill(const void *q, const void *k, const void *v, const void
         if (status == GDN_OK) status = run(kCandidates[0], true);
         for (int i = 0; i < NC && status == GDN_OK; ++i) {
             const Method c = kCandidates[i];
-            // 32 state rows per workgroup exist for bf16 I/O with d >= 32 only
+            // more than 16 state rows per workgroup: bf16 I/O with d >= rows only
             if (c.chunk != 1 && !slice_rows_fit(c.rows, dv, io_dtype == GDN_BF16)) continue;
             // correctness gate against the (64, 16) result
             if (hipMemsetAsync(base + L.off_out, 0, (size_t)n_out * eb, st) != hipSuccess ||

@@ -91,9 +91,10 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
  * (token by token), 16, 32 or 64; for chunk 0, the cached tuned choice or the
  * rule above. Returns 0 for arguments gdn_prefill would reject.
  * slice_rows (may be NULL) receives the chunked scan's state rows per
- * workgroup: 16, or 32 (bf16 I/O with d >= 32), taken from the tuned choice
- * for chunk 0 and otherwise 32 exactly when N * hv * dv / 16 exceeds the
- * GPU's 256 CUs; 0 for the token-by-token method or a rejected call.
+ * workgroup: 16, 32, 64 or 128 (more than 16 for bf16 I/O only, at most
+ * dv), taken from the tuned choice for chunk 0 and otherwise the fewest whose
+ * N * hv * dv / rows workgroups fit the GPU's 256 CUs, else the most; 0 for
+ * the token-by-token method or a rejected call.
  */
 int32_t gdn_prefill_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
                            int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype,
@@ -128,11 +129,15 @@ int32_t gdn_prefill_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, i
  *              in registers (one kernel, no workspace), which is faster for
  *              short prompts and multi-token steps. 0: the method that
  *              gdn_tune_prefill cached for this device and shape bucket if
- *              there is one, else by the mean sequence length L = T / N:
- *              1 when T <= 32 or L <= 24, 16 when L <= 48, 32 when the
- *              chunked scan's N * hv * dv / rows workgroups (rows: its state
- *              rows per workgroup, see gdn_prefill_method) fit the GPU's 256
- *              CUs and L <= 1024, else 64 (gdn_prefill_method tells which).
+ *              there is one, else by the mean sequence length L = T / N
+ *              and the chunked scan's state rows per workgroup (rows: the
+ *              fewest of 16, 32, 64, 128 whose N * hv * dv / rows
+ *              workgroups fit the GPU's 256 CUs, else the most; more than
+ *              16 for bf16 I/O only, at most dv): 1 when T <= 32 or
+ *              L <= 10; with 64 or 128 rows 16 when L <= 16, 32 when
+ *              L <= 32, else 64; with 16 or 32 rows 16 when L <= 48, 32
+ *              when the workgroups fit the GPU's 256 CUs and L <= 1024,
+ *              else 64 (gdn_prefill_method tells which).
  *              The result does not depend on it beyond rounding.
  * dk, dv       16, 32, 64 or 128 each.
  * scale        multiplies every output (1.0 for the plain rule).
@@ -283,8 +288,8 @@ int32_t gdn_decode_step_ex(const void *q, const void *k, const void *v,
 /*
  * Choice of the prefill method by measurement, with a correctness gate.
  *
- * The fastest evaluation (token by token, or chunks of 16, 32 or 64 with 16
- * or 32 state rows per scan workgroup) depends on the shape and the hardware ("Qwen cree trois formes de charges de
+ * The fastest evaluation (token by token, or chunks of 16, 32 or 64 with 16,
+ * 32, 64 or 128 state rows per scan workgroup) depends on the shape and the hardware ("Qwen cree trois formes de charges de
  * travail distinctes" of "Optimiser l'inference sur appareil pour Apple
  * Silicon"); the engine of "On descend d'un cran : #004 le meme compilateur
  * sur les puces d'Apple" measures its options at load time and checks each
@@ -292,9 +297,10 @@ int32_t gdn_decode_step_ex(const void *q, const void *k, const void *v,
  *
  * gdn_tune_prefill runs every method on the caller's inputs (same arguments
  * as gdn_prefill, fp32 initial state or NULL). The GDN_TUNE_CANDIDATES
- * methods, in this order, are (chunk, rows): (64, 16), (64, 32), (32, 16),
- * (32, 32), (16, 16), (16, 32) and (1, -); 32 rows only for bf16 I/O with
- * d >= 32. It compares each method's output and final state with those of
+ * methods, in this order, are (chunk, rows): (64, 16), (64, 32), (64, 64),
+ * (64, 128), (32, 16), (32, 32), (32, 64), (32, 128), (16, 16), (16, 32),
+ * (16, 64), (16, 128) and (1, -); more than 16 rows only for bf16 I/O with
+ * d >= rows. It compares each method's output and final state with those of
  * (64, 16) and rejects it when
  * max |x - ref| / max |ref| exceeds gate_tol, in [0, 1] (1/64 is the pages'
  * bar). It times the rest, each one warm-up plus the mean of five runs on
@@ -322,7 +328,7 @@ int32_t gdn_decode_step_ex(const void *q, const void *k, const void *v,
  * opened, and skips lines it cannot parse; *entries (may be NULL) receives
  * the number loaded.
  */
-#define GDN_TUNE_CANDIDATES 7
+#define GDN_TUNE_CANDIDATES 13
 size_t gdn_tune_prefill_scratch_size(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
                                      int32_t dk, int32_t dv, int32_t io_dtype);
 int32_t gdn_tune_prefill(const void *q, const void *k, const void *v,

@@ -295,23 +295,30 @@ def test_tune_argument_checks(lib):
 def test_chunk_zero_rule(lib):
     """The method chunk 0 takes with nothing tuned, by mean sequence length
     (HK=16, HV=32, d=128, bf16; the scan fills the GPU in one pass up to one
-    sequence with 16-row slices, two with 32-row slices)."""
+    sequence with 16-row slices, two with 32-row, four with 64-row and eight
+    with 128-row slices)."""
     gdn.tune_cache_clear()
     m = lambda n, T: gdn.prefill_method(n, T, 16, 32, 128)
     assert m(1, 16) == 1 and m(1, 32) == 1          # one short prompt
-    assert m(64, 64 * 24) == 1 and m(8, 8 * 4) == 1  # batches, mean <= 24
-    assert m(1, 48) == 16 and m(64, 64 * 32) == 16   # mean <= 48
+    assert m(64, 64 * 10) == 1 and m(8, 8 * 4) == 1  # batches, mean <= 10
+    assert m(1, 48) == 16 and m(2, 2 * 48) == 16     # 16- or 32-row slices, mean <= 48
+    assert m(64, 64 * 16) == 16 and m(64, 64 * 24) == 32 and m(64, 64 * 33) == 64  # 128-row slices
     assert m(1, 128) == 32 and m(1, 1024) == 32      # one sequence: one pass
     assert m(1, 4096) == 64 and m(8, 8 * 300) == 64  # long, or several passes
     assert m(2, 2 * 600) == 32                       # two sequences: one pass of 32-row slices
-    assert m(4, 4 * 600) == 64                       # four: two passes even so
+    assert m(4, 4 * 600) == 64                       # four: 64-row slices, whose long step wants chunks of 64
     assert gdn.prefill_method(2, 2 * 600, 16, 32, 128, io_dtype=torch.float32) == 64  # fp32: 16-row slices
     assert gdn.prefill_method(1, 4096, 16, 32, 128, chunk=16) == 16  # explicit chunks as given
     assert gdn.prefill_method(1, 4096, 3, 32, 128) == 0              # rejected shape
-    # state rows per scan workgroup: 32 once 16-row slices need more than one
-    # pass over 256 CUs (N * HV * DV / 16 > 256), bf16 I/O with d >= 32 only
+    # state rows per scan workgroup: the fewest of 16, 32, 64, 128 whose
+    # N * HV * DV / rows workgroups fit 256 CUs in one pass, else the most;
+    # more than 16 for bf16 I/O only, and at most d
     p = lambda n, T, hv=32, d=128, io=torch.bfloat16, c=0: gdn.prefill_plan(n, T, 16, hv, d, c, io)
     assert p(1, 4096) == (64, 16) and p(2, 2 * 4096) == (64, 32)
+    assert p(4, 4 * 1024) == (64, 64) and p(8, 8 * 512) == (64, 128)
+    assert p(32, 32 * 128) == (64, 128)                              # 1024 workgroups even so
+    assert p(64, 64 * 16) == (16, 128) and p(64, 64 * 32) == (32, 128)  # one chunk per sequence
+    assert p(8, 8 * 512, d=64) == (64, 64) and p(8, 8 * 512, d=32) == (32, 32)  # at most d
     assert p(1, 4096, hv=48) == (64, 32)                             # 384 slices of 16 rows
     assert p(2, 2 * 4096, io=torch.float32) == (64, 16)              # fp32 I/O: 16 rows
     assert p(64, 64 * 4, c=1) == (1, 0) and p(64, 64 * 4) == (1, 0)  # token by token: no scan

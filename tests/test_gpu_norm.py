@@ -194,22 +194,30 @@ def test_prefill_norm_leaves_rows_outside_sequences():
     assert torch.isnan(o[:5].float()).all()
 
 
-@pytest.mark.parametrize("lens", [[700, 333], [200] * 8])
-def test_prefill_norm_slices_and_passes(lens):
-    """HK = 16, HV = 32, d = 128, bf16. Two sequences: 32-row scan slices
-    (4 per head), one pass over the GPU, so the normalisation is fused into
-    the scan. Eight sequences: more scan workgroups than one pass holds, so
-    a pass over out normalises after the scan. Both against the oracle, with
-    the plain call's final states bit for bit."""
-    inp = gs.make_inputs(lens, 16, 32, 128, 128, seed=gs.SEED_BASE + 520 + len(lens), io_dtype="bf16",
+@pytest.mark.parametrize("lens,io,rows", [([700, 333], "bf16", 32), ([200] * 3, "bf16", 64),
+                                          ([200] * 8, "bf16", 128), ([200] * 40, "bf16", 128),
+                                          ([200] * 3, "f32", 16)])
+def test_prefill_norm_slices_and_passes(lens, io, rows):
+    """HK = 16, HV = 32, d = 128. bf16, two or three sequences: 32- or 64-row
+    scan slices (4 or 2 per head), one pass over the GPU, so the
+    normalisation is fused into the scan, the slices of a head exchanging
+    their partial sums. bf16, eight or forty sequences: 128-row slices, each
+    one head's whole state, which normalise their own rows in the scan (forty:
+    five passes over the GPU). fp32, three sequences: 16-row slices, more
+    scan workgroups than one pass holds, so a pass over out normalises after
+    the scan. All against the oracle, with the plain call's final states bit
+    for bit."""
+    io_dtype = torch.bfloat16 if io == "bf16" else torch.float32
+    assert gdn.prefill_plan(len(lens), sum(lens), 16, 32, 128, 64, io_dtype) == (64, rows)
+    inp = gs.make_inputs(lens, 16, 32, 128, 128, seed=gs.SEED_BASE + 520 + len(lens), io_dtype=io,
                          gate_dtype="f32", init_state=True)
     w = _weight(128, seed=9)
-    note(f"prefill norm lens={lens}")
+    note(f"prefill norm lens={lens} io={io} rows={rows}")
     o, f = _prefill_norm(inp, chunk=64, w=w, eps=1e-6)
     o_ref, f_ref = oracle_ref(inp)
     eo = rel_err(to_f64(o), oracle.rms_norm(o_ref, w, 1e-6))
-    print(f"[parity] prefill norm lens={lens} out_err={eo:.3e}", flush=True)
-    assert np.isfinite(to_f64(o)).all() and eo <= tol("bf16")
+    print(f"[parity] prefill norm lens={lens} io={io} out_err={eo:.3e}", flush=True)
+    assert np.isfinite(to_f64(o)).all() and eo <= tol(io)
     d = device_inputs(inp)
     _, f_plain = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=64,
                              initial_state=d["initial_state"])

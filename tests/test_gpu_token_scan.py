@@ -135,10 +135,10 @@ def test_token_scan_malformed_cu_seqlens_is_clamped():
 
 
 @pytest.mark.parametrize("lens,expect", [([30], "token_scan"), ([48], "scan"), ([100], "scan"),
-                                         ([12] * 16, "token_scan"), ([30] * 16, "scan")])
+                                         ([10] * 16, "token_scan"), ([12] * 16, "scan"), ([30] * 16, "scan")])
 def test_chunk_zero_picks_by_length(lens, expect):
     """chunk 0 with nothing tuned: token by token when T <= 32 or the mean
-    length is at most 24 tokens, chunked above (the method the library
+    length is at most 10 tokens, chunked above (the method the library
     reports for the sizes is the one that runs)."""
     inp = gs.make_inputs(lens, 2, 4, 32, 32, seed=65, io_dtype="bf16", gate_dtype="f32")
     d = device_inputs(inp)

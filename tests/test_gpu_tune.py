@@ -55,8 +55,11 @@ def test_tune_picks_fastest_passing_method(lens):
     assert all(0 <= r["err"][c] <= 1 / 64 for c in passing)
     assert passing[r["method"]] == min(passing.values())
     assert r["err"]["64/16"] == 0.0  # the reference against itself
-    # 32 state rows per workgroup: the same MFMA sequence per element, the same bits
-    assert r["err"]["64/32"] == 0.0 and r["err"]["32/32"] == r["err"]["32/16"]
+    # 32, 64 or 128 state rows per workgroup: the same MFMA sequence per
+    # element, the same bits
+    for rows in (32, 64, 128):
+        assert r["err"][f"64/{rows}"] == 0.0
+        assert r["err"][f"32/{rows}"] == r["err"]["32/16"] and r["err"][f"16/{rows}"] == r["err"]["16/16"]
     assert gdn.tune_cache_size() == 1
     # chunk 0 now runs the chosen method: its kernels, its bits
     assert gdn.prefill_plan(len(lens), sum(lens), 16, 32, 128) == (r["chunk"], r["rows"])
@@ -71,16 +74,17 @@ def test_tune_picks_fastest_passing_method(lens):
 
 def test_tune_gate_rejects_what_differs():
     """With a zero tolerance only chunk 64 can pass: the reference (16 rows
-    per scan workgroup) and 32 rows, which computes the same bits. Every other
-    chunk rounds differently, so it is rejected and never timed."""
+    per scan workgroup) and 32, 64 and 128 rows, which compute the same bits.
+    Every other chunk rounds differently, so it is rejected and never timed."""
     _, d = _inputs([200, 37], seed=gs.SEED_BASE + 710)
     note("tune prefill with gate_tol = 0")
     r = gdn.tune_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
                          initial_state=d["initial_state"], gate_tol=0.0)
     print(f"[tune] gate 0: chose {r['method']}; ms {r['ms']}; err {r['err']}", flush=True)
     assert r["chunk"] == 64
-    assert r["err"]["64/32"] == 0 and r["ms"]["64/32"] > 0
-    for c in ("32/16", "32/32", "16/16", "16/32", "1"):
+    for c in ("64/32", "64/64", "64/128"):
+        assert r["err"][c] == 0 and r["ms"][c] > 0
+    for c in ("32/16", "32/32", "32/64", "32/128", "16/16", "16/32", "16/64", "16/128", "1"):
         assert r["err"][c] > 0 and r["ms"][c] == -1
 
 

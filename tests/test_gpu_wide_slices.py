@@ -1,12 +1,12 @@
-"""The chunked scan with 32 state rows per workgroup.
+"""The chunked scan with 32, 64 or 128 state rows per workgroup.
 
-On bf16 I/O with d >= 32, the scan gives each workgroup 32 value rows of a
-state instead of 16 once 16-row slices would take more than one pass over
-the GPU's 256 CUs (N * HV * DV / 16 > 256). Every output and state element
-goes through the same MFMA sequence either way, so a batched call must give
-the same bits as calls on each sequence alone, which fit one pass and keep
-16-row slices (1 * HV * DV / 16 <= 256). Both are held to the bf16 bar
-against the fp64 oracle.
+On bf16 I/O, the scan gives each workgroup the fewest value rows of a state
+(16, 32, 64 or 128, at most d) whose workgroups fit the GPU's 256 CUs in one
+pass (N * HV * DV / rows <= 256), else the most. Every output and state
+element goes through the same MFMA sequence whatever the rows, so a batched
+call must give the same bits as calls on each sequence alone, which fit one
+pass and keep 16-row slices (1 * HV * DV / 16 <= 256). Both are held to the
+bf16 bar against the fp64 oracle.
 """
 
 import numpy as np
@@ -26,6 +26,11 @@ def _wide(n, hv, d):
     return n * hv * (d // 16) > CUS
 
 
+def _batch_for(rows, hv, d):
+    """The fewest sequences for which the scan takes `rows` state rows."""
+    return CUS // (hv * d // (rows // 2)) + 2
+
+
 def _lengths(n, seed):
     rng = np.random.default_rng(seed)
     lens = [int(x) for x in rng.integers(1, 150, size=n)]
@@ -38,19 +43,24 @@ def _call(q, k, v, g, b, cu, s0, chunk, state_dtype):
     return gdn.prefill(q, k, v, g, b, cu, chunk=chunk, scale=0.8, initial_state=s0, state_dtype=state_dtype)
 
 
-@pytest.mark.parametrize("d,chunk,state", [(32, 16, "f32"), (32, 32, "f32"), (32, 64, "f32"),
-                                           (64, 16, "f32"), (64, 32, "f32"), (64, 64, "f32"),
-                                           (128, 16, "f32"), (128, 32, "f32"), (128, 64, "f32"),
-                                           (128, 64, "bf16")])
-def test_wide_slices_match_single_sequence_calls(d, chunk, state):
+@pytest.mark.parametrize("d,chunk,state,rows", [(32, 16, "f32", 32), (32, 32, "f32", 32), (32, 64, "f32", 32),
+                                                (64, 16, "f32", 32), (64, 32, "f32", 32), (64, 64, "f32", 32),
+                                                (128, 16, "f32", 32), (128, 32, "f32", 32), (128, 64, "f32", 32),
+                                                (128, 64, "bf16", 32),
+                                                (64, 16, "f32", 64), (64, 64, "f32", 64), (64, 64, "bf16", 64),
+                                                (128, 16, "f32", 64), (128, 32, "f32", 64), (128, 64, "f32", 64),
+                                                (128, 16, "f32", 128), (128, 32, "f32", 128),
+                                                (128, 64, "f32", 128), (128, 64, "bf16", 128)])
+def test_wide_slices_match_single_sequence_calls(d, chunk, state, rows):
     hk, hv = 4, 8
-    n = CUS // (hv * d // 16) + 2
+    n = _batch_for(rows, hv, d)
     assert _wide(n, hv, d) and not _wide(1, hv, d)
-    lens = _lengths(n, seed=1200 + d + chunk)
-    inp = gs.make_inputs(lens, hk, hv, d, d, seed=1300 + d + chunk, io_dtype="bf16", gate_dtype="f32",
+    assert gdn.prefill_plan(n, n * 100, hk, hv, d, chunk) == (chunk, rows)
+    lens = _lengths(n, seed=1200 + d + chunk + rows)
+    inp = gs.make_inputs(lens, hk, hv, d, d, seed=1300 + d + chunk + rows, io_dtype="bf16", gate_dtype="f32",
                          init_state=True)
     sd = torch.bfloat16 if state == "bf16" else torch.float32
-    note(f"wide slices d={d} chunk={chunk} state={state} N={n}")
+    note(f"wide slices d={d} chunk={chunk} state={state} rows={rows} N={n}")
     t = device_inputs(inp)
     s0 = t["initial_state"] if state == "f32" else t["initial_state"].to(torch.bfloat16)
     o, f = _call(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"], s0, chunk, sd)
@@ -71,7 +81,8 @@ def test_wide_slices_match_single_sequence_calls(d, chunk, state):
     # bf16 states: the oracle starts from the rounded initial state
     o_ref, f_ref = oracle_ref(inp, scale=0.8, initial_state=None if state == "f32" else to_f64(s0))
     eo, ef = rel_err(to_f64(o), o_ref), rel_err(to_f64(f), f_ref)
-    print(f"[parity] wide slices d={d} chunk={chunk} state={state} N={n} out_err={eo:.3e} state_err={ef:.3e}",
+    print(f"[parity] wide slices d={d} chunk={chunk} state={state} rows={rows} N={n} out_err={eo:.3e} "
+          f"state_err={ef:.3e}",
           flush=True)
     assert eo <= TOL_BF16 and ef <= TOL_BF16
 
