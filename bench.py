@@ -502,11 +502,12 @@ def summarize_norm(stats_dir: str, fetch_dir: str, write_dir: str, results_jsonl
                 pre.append(d)
             else:
                 res[d["part"]] = d
+    passes = [pp for pp in pre if "algorithmic_bytes" in pp]
     algo = {"decode": decode_bytes_per_step(), "decode_norm": decode_bytes_per_step() + 4 * D,
-            "norm_apply": norm_apply_bytes(T_PREFILL)}
+            "norm_apply": passes[0]["algorithmic_bytes"] if passes else norm_apply_bytes(T_PREFILL)}
     lines = [
-        "# Output normalisation: decode batch 64 (fused), prefill 1x4096 (fused into the scan) and "
-        "8x512 (pass after the scan); HK=16, HV=32, d=128, bf16",
+        "# Output normalisation: decode batch 64 (fused), prefill 1x4096 and 8x512 in bf16 (fused into the "
+        "scan) and 8x512 in fp32 (pass after the scan); HK=16, HV=32, d=128",
         "",
         "Made by (from the repository root; OUT is any scratch directory):",
         "",
@@ -564,7 +565,8 @@ def summarize_norm(stats_dir: str, fetch_dir: str, write_dir: str, results_jsonl
             kn = ", ".join(f"{k} {v * 1e3:.1f}" for k, v in pp["norm_kernel_ms"].items())
             extra = (f"; the pass at {pp['norm_apply_gbs']:.0f} GB/s, {100 * pp['hbm_frac']:.1f}% of 8 TB/s"
                      if "norm_apply_gbs" in pp else "")
-            lines.append(f"- prefill {pp['sequences']}x{pp['tokens'] // pp['sequences']} ({pp['normalisation']}): "
+            lines.append(f"- prefill {pp['sequences']}x{pp['tokens'] // pp['sequences']} {pp.get('io', 'bf16')}, "
+                         f"{pp.get('rows', '?')}-row slices ({pp['normalisation']}): "
                          f"call plain {pp['plain_ms'] * 1e3:.1f} us, with the norm {pp['norm_ms'] * 1e3:.1f} us; "
                          f"kernel us plain ({kp}), with the norm ({kn}); the norm adds "
                          f"{pp['norm_cost_kernel_us']:.1f} us of kernel time{extra}.")
@@ -773,7 +775,7 @@ def summarize_configs(stats_dir: str, results_jsonl: str):
     rows = list(csv.DictReader(open(os.path.join(stats_dir, "run_kernel_stats.csv"))))
     lines = [
         f"# Long (T = 32768) and varlen (8 sequences, then 64 decode steps at batch 8) workloads; "
-        f"HK={HK}, HV={HV}, d={D}, C={CHUNK}, bf16",
+        f"HK={HK}, HV={HV}, d={D}, bf16",
         "",
         "Made by (from the repository root; OUT is any scratch directory):",
         "",
@@ -799,8 +801,12 @@ def summarize_configs(stats_dir: str, results_jsonl: str):
             lines.append(f"| {_kernel_label(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     lines += ["", "## Per workload (HIP events in the same run, under the profiler)", "",
-              "| workload | sequences | tokens | prefill ms | tokens/s | prep ms | scan ms | scan MFMA | "
-              "decode b8 step us |", "|---|---|---|---|---|---|---|---|---|"]
+              "Methods are named chunk/rows (chunk size, state rows per scan workgroup). The first is chunk "
+              "64 with the rule's rows, which the kernel columns describe; the tuned method is the one "
+              "gdn_tune_prefill picks for the workload (the host-side rule sees sizes, not the lengths).", "",
+              "| workload | sequences | tokens | method | prefill ms | tokens/s | prep ms | scan ms | scan MFMA | "
+              "tuned method | tuned prefill ms | tuned tokens/s | decode b8 step us |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for line in open(results_jsonl):
         line = line.strip()
         if not line.startswith("{"):
@@ -808,9 +814,10 @@ def summarize_configs(stats_dir: str, results_jsonl: str):
         d = json.loads(line)
         km = d["kernel_ms"]
         dec = f"{d['decode_b8_step_ms'] * 1e3:.1f}" if "decode_b8_step_ms" in d else "-"
-        lines.append(f"| {d['workload']} | {d['num_seqs']} | {d['total_tokens']} | {d['prefill_ms']:.3f} | "
-                     f"{d['tokens_per_s'] / 1e6:.1f} M | {km['prep']:.3f} | {km['scan']:.3f} | "
-                     f"{100 * d['scan_mfma_frac']:.1f}% | {dec} |")
+        lines.append(f"| {d['workload']} | {d['num_seqs']} | {d['total_tokens']} | {d['method']} | "
+                     f"{d['prefill_ms']:.3f} | {d['tokens_per_s'] / 1e6:.1f} M | {km['prep']:.3f} | "
+                     f"{km['scan']:.3f} | {100 * d['scan_mfma_frac']:.1f}% | {d['tuned_method']} | "
+                     f"{d['tuned_prefill_ms']:.3f} | {d['tuned_tokens_per_s'] / 1e6:.1f} M | {dec} |")
     with open(os.path.join(ROOT, "profiles", "gdn_long_varlen.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -824,10 +831,13 @@ def norm_apply_bytes(tokens, hv=HV, dv=D, elem=2):
 
 def output_norm_bench(dev, copies, steps):
     """Output normalisation: decode B=64 with the fused kernel against the
-    plain one, and two prefills (one 4096-token sequence, whose scan takes
-    the normalisation; eight 512-token sequences, normalised by a pass after
-    the scan) against the plain prefill. One JSON line each; kernel times
-    from the library's dispatch-stamped events."""
+    plain one, and three prefills against the plain prefill: one 4096-token
+    sequence (16-row scan slices, which exchange partial sums: the
+    normalisation fused into the scan), eight 512-token sequences (128-row
+    slices, each a whole head: fused, no exchange), and the same eight in
+    fp32 I/O (16-row slices over several passes: a pass after the scan).
+    One JSON line each; kernel times from the library's dispatch-stamped
+    events."""
     import torch
     import gdn_synth as gs
     import gated_deltanet_linear_02_amd as gdn
@@ -876,18 +886,19 @@ def output_norm_bench(dev, copies, steps):
     }), flush=True)
     del dsets
 
-    # prefill: the headline shape (one pass of scan workgroups: the
-    # normalisation fused into the scan) and eight sequences (several passes:
-    # the normalisation pass after the scan)
-    for lens in ([T_PREFILL], [512] * 8):
+    # prefill: the headline shape and eight sequences, bf16 (the
+    # normalisation fused into the scan), and eight in fp32 (a pass after it)
+    for lens, io in (([T_PREFILL], "bf16"), ([512] * 8, "bf16"), ([512] * 8, "f32")):
         n, tt = len(lens), sum(lens)
-        pre = gs.make_inputs(lens, HK, HV, D, D, seed=gs.SEED_BASE + 2, io_dtype="bf16", gate_dtype="f32") \
+        io_dt = torch.bfloat16 if io == "bf16" else torch.float32
+        pre = gs.make_inputs(lens, HK, HV, D, D, seed=gs.SEED_BASE + 2, io_dtype=io, gate_dtype="f32") \
             if n > 1 else gs.workload("prefill")
-        ws_bytes = gdn.prefill_workspace_size(n, tt, HK, HV, D, D, CHUNK, torch.bfloat16)
+        ws_bytes = gdn.prefill_workspace_size(n, tt, HK, HV, D, D, CHUNK, io_dt)
+        rows = gdn.prefill_plan(n, tt, HK, HV, D, CHUNK, io_dt)[1]
         psets = []
         for _ in range(copies):
             d = device_inputs(pre, dev)
-            d["out"] = torch.empty((tt, HV, D), dtype=torch.bfloat16, device=dev)
+            d["out"] = torch.empty((tt, HV, D), dtype=io_dt, device=dev)
             d["fin"] = torch.empty((n, HV, D, D), dtype=torch.float32, device=dev)
             d["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
             psets.append(d)
@@ -901,18 +912,20 @@ def output_norm_bench(dev, copies, steps):
         norm_ms, nk = measure(lambda d: pre_run(d, True), psets, kinds)
         fused = nk["norm_apply"] == 0.0
         rec = {
-            "mode": "output-norm", "part": "prefill", "sequences": n, "tokens": tt,
-            "normalisation": "fused into the scan" if fused else "pass after the scan",
+            "mode": "output-norm", "part": "prefill", "sequences": n, "tokens": tt, "io": io, "rows": rows,
+            "normalisation": ("fused into the scan" + (" (whole-head slices)" if rows == D else
+                                                        " (exchange between slices)")) if fused
+            else "pass after the scan",
             "plain_ms": plain_ms, "norm_ms": norm_ms,
             "plain_kernel_ms": {k: pk[k] for k in kinds if pk[k] > 0},
             "norm_kernel_ms": {k: nk[k] for k in kinds if nk[k] > 0},
             "norm_cost_kernel_us": 1e3 * (sum(nk.values()) - sum(pk.values())),
-            "dtype": "bf16", "data": "synthetic", "buffer_copies": copies,
-            "config": {"workload": f"prefill {n}x{tt // n} tokens, HK={HK}, HV={HV}, d={D}, chunk {CHUNK}; "
-                                   f"RMS output norm, eps {eps}"},
+            "dtype": io, "data": "synthetic", "buffer_copies": copies,
+            "config": {"workload": f"prefill {n}x{tt // n} tokens, HK={HK}, HV={HV}, d={D}, chunk {CHUNK}, "
+                                   f"{rows}-row scan slices; RMS output norm, eps {eps}"},
         }
         if not fused:
-            by = norm_apply_bytes(tt)
+            by = norm_apply_bytes(tt, elem=4 if io == "f32" else 2)
             gbs = by / (nk["norm_apply"] * 1e-3) / 1e9
             rec.update({"norm_apply_gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes": by})
         print(json.dumps(rec), flush=True)
@@ -974,7 +987,9 @@ def configs_bench(dev, reps):
     tests; here only their speed): a 32768-token prefill from an initial
     state, and 8 packed sequences of 256 to 16384 tokens followed by 64
     decode steps at batch 8 from their final states. HK=16, HV=32, d=128,
-    bf16 I/O, fp32 gates and states, chunk 64. One JSON line each."""
+    bf16 I/O, fp32 gates and states, chunk 64 with the state rows per scan
+    workgroup of the rule; then the method gdn_tune_prefill picks for the
+    workload (chunk 0 after tuning). One JSON line each."""
     import torch
     import gdn_synth as gs
     import gated_deltanet_linear_02_amd as gdn
@@ -1000,20 +1015,28 @@ def configs_bench(dev, reps):
         ws = torch.empty(gdn.prefill_workspace_size(N, T, HK, HV, D, D, CHUNK, torch.bfloat16),
                          dtype=torch.uint8, device=dev)
 
-        def run():
-            gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=CHUNK,
+        def run(chunk=CHUNK):
+            gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=chunk,
                         initial_state=s0, final_state=fin, out=out, workspace=ws)
 
+        gdn.tune_cache_clear()
+        method = gdn.method_name(*gdn.prefill_plan(N, T, HK, HV, D, CHUNK))
         ms = timed(run, reps)
         gdn.timing_start(8 * reps)
         for _ in range(reps):
             run()
         kt = gdn.timing_stop()
         scan_ms = kt["scan"]["mean_ms"]
-        res = {"mode": "configs", "workload": name, "num_seqs": N, "total_tokens": T, "prefill_ms": ms,
-               "tokens_per_s": T / (ms * 1e-3),
+        tuned = gdn.tune_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], initial_state=s0)
+        tuned_ms = timed(lambda: run(0), reps)
+        gdn.tune_cache_clear()
+        ms = min(ms, timed(run, reps))  # the rule's method before and after, so that order favours neither
+        res = {"mode": "configs", "workload": name, "num_seqs": N, "total_tokens": T, "method": method,
+               "prefill_ms": ms, "tokens_per_s": T / (ms * 1e-3),
                "kernel_ms": {k: kt[k]["mean_ms"] for k in ("schedule", "prep", "scan")},
                "scan_mfma_frac": scan_flops_per_token() * T / (scan_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+               "tuned_method": tuned["method"], "tuned_prefill_ms": tuned_ms,
+               "tuned_tokens_per_s": T / (tuned_ms * 1e-3),
                "dtype": "bf16", "data": "synthetic",
                "config": {"workload": f"{name}: {N} sequence(s), {T} tokens, HK={HK}, HV={HV}, d={D}, chunk {CHUNK}",
                           "lengths": np.diff(inp.cu_seqlens).tolist()}}
