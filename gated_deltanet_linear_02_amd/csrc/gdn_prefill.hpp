@@ -833,7 +833,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
     // The fused normalisation's exchange alternates two register slots by
     // chunk parity, which the unrolled pipeline keeps compile-time when the
     // output stages are even.
-    constexpr int kRStages = R == 16 ? 4 : 3, kOStages = R == 16 && !kNorm ? 5 : R <= 32 ? 4 : 3;
+    constexpr int kRStages = R == 16 ? 4 : R <= 64 ? 3 : 2, kOStages = R == 16 && !kNorm ? 5 : R <= 32 ? 4 : 3;
     // The fused normalisation: with several slices per head they exchange
     // partial sums (kNormX); a slice that holds the whole head (R = DV)
     // normalises its rows in the output wave that computes them (kNormW).
@@ -1019,26 +1019,30 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         //   wave 0     the chunk's gate record (delta and gamma_C for the
         //              recurrence waves, scale gamma for the outputs),
         //              staged in LDS;
-        //   wave 1     an L2 touch of the chunk kTouchAhead ahead: the 16
-        //              workgroups of the query/key head split that chunk's
-        //              operands (Q, K^T, and Tb, P, W of each value head of
-        //              the group) and its V rows (128-byte lines) 64 lines
-        //              each, one line per lane, so that the workgroups' own
-        //              loads later hit L2;
-        //              the value is only kept alive until the stage is
-        //              refilled;
+        //   wave 1     16-row slices: an L2 touch of the chunk kTouchAhead
+        //              ahead: the 16 workgroups of the query/key head split
+        //              that chunk's operands (Q, K^T, and Tb, P, W of each
+        //              value head of the group) and its V rows (128-byte
+        //              lines) 64 lines each, one line per lane, so that the
+        //              workgroups' own loads later hit L2; the value is only
+        //              kept alive until the stage is refilled;
         //   waves 2-3  16-row slices: the chunk's V rows 32 (q - 2) .. + 31
-        //              (8 values per lane), staged in LDS; wider slices:
-        //              another L2 touch, and every output wave loads the V
-        //              rows 16 q .. 16 q + 15 of its R columns besides (R / 32
-        //              loads).
+        //              (8 values per lane), staged in LDS.
+        // With wider slices waves 1-3 load the gate record again (no touch,
+        // below), and every output wave loads the V rows 16 q .. 16 q + 15
+        // of its R columns besides (R / 32 loads).
         // Memory instructions, not bytes, bound the scan, so these small
         // loads are folded into as few instructions as possible. The fp32
         // path (one stage) loads V per wave and the gate record in every wave.
         constexpr int kRunQ = (int)((size_t)C * DK * sizeof(E) / 1024);
         constexpr int kRunM = (int)((size_t)C * C * sizeof(E) / 1024);
+        // The L2 touch serves 16-row slices only: wider slices share each
+        // line among fewer workgroups, and their touches, which wait on HBM
+        // in the issuing wave's load queue, measured slower than none (scan
+        // at 2 x 2048, 32 rows: 62.5 against 55.3 us; 4 x 1024, 64 rows:
+        // 50.9 against 45.8 us; 4 rotated buffer sets).
         constexpr bool kTouch = kPipelined && (size_t)C * DK * sizeof(E) % 1024 == 0 &&
-                                (size_t)C * C * sizeof(E) % 1024 == 0;
+                                (size_t)C * C * sizeof(E) % 1024 == 0 && R == 16;
         auto gate_ptr = [&](const ChunkRef &r) {
             // the chunk's gate record, 4 floats per lane: lanes [0, C/4)
             // delta, [C/4, C/2) scale gamma, C/2 gamma_C
@@ -1054,10 +1058,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             // preparation kernel has just written)
             constexpr int kLinesPerRow = DK * (int)sizeof(E) >= 128 ? DK * (int)sizeof(E) / 128 : 1;
             const int nlines = nops + C * group * kLinesPerRow;
-            // wider slices: fewer workgroups per query/key head, touching
-            // from waves 1-3
-            const int part = R == 16 ? within : within * 3 + (q - 1);
-            const int line = (part * 64 + lane) % nlines;
+            const int line = (within * 64 + lane) % nlines;
             if (line >= nops) {
                 const int vl = line - nops, per_tok = group * kLinesPerRow;
                 const ChunkRef rc = chunk(cc);
