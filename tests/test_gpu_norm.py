@@ -246,3 +246,30 @@ def test_prefill_norm_repeated_calls_are_identical():
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[3])
     assert not torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("hk,hv,d", [(4, 16, 64), (8, 8, 128)])
+def test_prefill_norm_whole_head_slices(hk, hv, d):
+    """bf16, enough sequences that the scan takes slices of a whole head
+    (rows = d, more than one pass over the GPU): each output wave normalises
+    its rows itself. Against the oracle (an empty sequence among them), with
+    the plain call's final states bit for bit."""
+    n = 40
+    assert gdn.prefill_plan(n, n * 90, hk, hv, d, 64) == (64, d)
+    rng = np.random.default_rng(hk + hv + d)
+    lens = [int(x) for x in rng.integers(1, 180, size=n)]
+    lens[5] = 0
+    inp = gs.make_inputs(lens, hk, hv, d, d, seed=gs.SEED_BASE + 540 + d, io_dtype="bf16", gate_dtype="f32",
+                         init_state=True)
+    w = _weight(d, seed=d + 1)
+    note(f"prefill norm whole-head slices hk={hk} hv={hv} d={d}")
+    o, f = _prefill_norm(inp, chunk=64, w=w, eps=1e-6, scale=0.9)
+    o_ref, f_ref = oracle_ref(inp, scale=0.9)
+    eo = rel_err(to_f64(o), oracle.rms_norm(o_ref, w, 1e-6))
+    print(f"[parity] prefill norm whole-head slices hk={hk} hv={hv} d={d} out_err={eo:.3e}", flush=True)
+    assert np.isfinite(to_f64(o)).all() and eo <= tol("bf16")
+    dd = device_inputs(inp)
+    _, f_plain = gdn.prefill(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["cu_seqlens"], chunk=64,
+                             scale=0.9, initial_state=dd["initial_state"])
+    torch.cuda.synchronize()
+    assert torch.equal(f, f_plain)

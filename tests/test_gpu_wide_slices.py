@@ -101,3 +101,36 @@ def test_wide_slices_many_heads_one_sequence():
     eo, ef = rel_err(to_f64(o), o_ref), rel_err(to_f64(f), f_ref)
     print(f"[parity] wide slices 48 heads out_err={eo:.3e} state_err={ef:.3e}", flush=True)
     assert eo <= TOL_BF16 and ef <= TOL_BF16
+
+
+@pytest.mark.parametrize("hk,hv,d,rows", [(8, 8, 128, 128), (2, 8, 128, 128), (1, 8, 128, 64), (4, 16, 64, 64),
+                                          (3, 12, 128, 32)])
+def test_wide_slices_head_groups(hk, hv, d, rows):
+    """Value heads per query/key head of 1, 4 and 8 (the scan places a q/k
+    head's slices together; the grid pads the groups), d = 64, and a q/k
+    head count that is not a power of two: every head against the oracle,
+    and sequences 0 and 3 bit for bit against their own calls."""
+    n = _batch_for(rows, hv, d)
+    assert gdn.prefill_plan(n, n * 100, hk, hv, d, 64) == (64, rows)
+    lens = _lengths(n, seed=1500 + hk + hv + d + rows)
+    inp = gs.make_inputs(lens, hk, hv, d, d, seed=1600 + hk + hv + d + rows, io_dtype="bf16", gate_dtype="f32",
+                         init_state=True)
+    note(f"wide slices hk={hk} hv={hv} d={d} rows={rows} N={n}")
+    t = device_inputs(inp)
+    s0 = t["initial_state"]
+    o, f = _call(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"], s0, 64, torch.float32)
+    torch.cuda.synchronize()
+    cu = inp.cu_seqlens
+    for i in (0, 3):
+        a, e = int(cu[i]), int(cu[i + 1])
+        one = torch.tensor([0, e - a], dtype=torch.int32, device="cuda")
+        oi, fi = _call(t["q"][a:e].contiguous(), t["k"][a:e].contiguous(), t["v"][a:e].contiguous(),
+                       t["g"][a:e].contiguous(), t["beta"][a:e].contiguous(), one, s0[i:i + 1].contiguous(),
+                       64, torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(o[a:e], oi) and torch.equal(f[i], fi[0]), f"sequence {i} differs from its own call"
+    o_ref, f_ref = oracle_ref(inp, scale=0.8)
+    eo, ef = rel_err(to_f64(o), o_ref), rel_err(to_f64(f), f_ref)
+    print(f"[parity] wide slices hk={hk} hv={hv} d={d} rows={rows} N={n} out_err={eo:.3e} state_err={ef:.3e}",
+          flush=True)
+    assert eo <= TOL_BF16 and ef <= TOL_BF16
