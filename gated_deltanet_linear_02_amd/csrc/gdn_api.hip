@@ -238,12 +238,12 @@ static int32_t prefill_impl(const void *q, const void *k, const void *v, const v
     A.slice_rows = m.rows;
     A.s0 = initial_state; A.s_final = final_state; A.out = out;
     A.ws = static_cast<char *>(workspace); A.lay = L;
-    // With bf16 I/O the chunked scan takes the normalisation itself when its
-    // workgroups fit the GPU in one pass, so that each output is rounded
-    // once; otherwise (fp32 I/O, where the pass reads the same fp32 values,
-    // or more workgroups than one pass) a pass over out follows, which is
-    // the faster of the two (at T = 4096 the pass adds 10.5 us, the fused
-    // form 14.7 us to the scan).
+    // With bf16 I/O the chunked scan takes the normalisation itself when one
+    // workgroup holds whole rows (rows = dv) or its workgroups fit the GPU in
+    // one pass, so that each output is rounded once (at T = 4096 the fused
+    // form adds about 5 us to the scan, the pass 10.5 us); otherwise (fp32
+    // I/O, where the pass reads the same fp32 values, or narrower slices over
+    // more than one pass) a pass over out follows.
     const bool fused_norm = norm_w && c != 1 && io_dtype == GDN_BF16 &&
                             fused_norm_fits(num_seqs, hk, hv, dv, m.rows);
     if (fused_norm) {
