@@ -184,6 +184,10 @@ static TuneLayout tune_layout(int32_t num_seqs, int64_t total_tokens, int32_t hk
 
 using namespace gdn;
 
+// How much faster than the fixed rule's method another must measure to be
+// chosen instead (see gdn_tune_prefill).
+constexpr float kTuneMargin = 0.03f;
+
 extern "C" {
 
 size_t gdn_tune_prefill_scratch_size(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
@@ -292,6 +296,19 @@ int32_t gdn_tune_prefill(const void *q, const void *k, const void *v, const void
     int best = 0;  // the reference always passes its own gate
     for (int i = 1; i < NC; ++i)
         if (ms[i] >= 0.f && ms[i] < ms[best]) best = i;
+    // The fixed rule's method keeps the choice unless another is faster by
+    // more than kTuneMargin: the candidates are timed warm on the caller's
+    // inputs, and differences within the run-to-run scatter would otherwise
+    // decide, and can reverse with cold caches (one 4096-token sequence: 32
+    // rows per scan workgroup 1% faster warm, 11% slower cold).
+    const bool bf = io_dtype == GDN_BF16;
+    Method rule;
+    rule.chunk = rule_chunk(num_seqs, total_tokens, hv, dv, bf);
+    rule.rows = rule.chunk == 1 ? 0 : scan_slice_rows(num_seqs, hv, dv, bf);
+    for (int i = 0; i < NC; ++i)
+        if (kCandidates[i].chunk == rule.chunk && kCandidates[i].rows == rule.rows && ms[i] >= 0.f &&
+            ms[best] >= ms[i] * (1.f - kTuneMargin))
+            best = i;
     *chosen_chunk = kCandidates[best].chunk;
     if (chosen_rows) *chosen_rows = kCandidates[best].rows;
     for (int i = 0; i < NC; ++i) {

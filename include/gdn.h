@@ -308,7 +308,10 @@ int32_t gdn_decode_step_ex(const void *q, const void *k, const void *v,
  * max |x - ref| / max |ref| exceeds gate_tol, in [0, 1] (1/64 is the pages'
  * bar). It times the rest, each one warm-up plus the mean of five runs on
  * the same inputs, and returns the fastest in *chosen_chunk and *chosen_rows
- * (may be NULL; 0 for the token-by-token method). It also caches
+ * (may be NULL; 0 for the token-by-token method), except that the method of
+ * the fixed rule (chunk 0 with nothing cached) is kept unless the fastest
+ * is more than 3% faster than it: warm timings on one input set differ by
+ * about that much from run to run. It also caches
  * the choice for (device, driver version, library version, shape bucket).
  * The bucket is num_seqs and total_tokens each rounded up to a power of two,
  * with hk, hv, d and both dtypes exact. gdn_prefill with chunk 0 then uses

@@ -47,13 +47,21 @@ def _run(d, chunk):
 def test_tune_picks_fastest_passing_method(lens):
     inp, d = _inputs(lens, seed=gs.SEED_BASE + 700 + len(lens))
     note(f"tune prefill lens={lens[:2]}... n={len(lens)}")
+    gdn.tune_cache_clear()
+    rule = gdn.method_name(*gdn.prefill_plan(len(lens), sum(lens), 16, 32, 128))
     r = gdn.tune_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
                          initial_state=d["initial_state"])
-    print(f"[tune] n={len(lens)} T={sum(lens)}: chose {r['method']}; ms {r['ms']}; err {r['err']}", flush=True)
+    print(f"[tune] n={len(lens)} T={sum(lens)}: rule {rule}, chose {r['method']}; ms {r['ms']}; err {r['err']}",
+          flush=True)
     passing = {c: t for c, t in r["ms"].items() if t >= 0}
     assert r["method"] in passing
     assert all(0 <= r["err"][c] <= 1 / 64 for c in passing)
-    assert passing[r["method"]] == min(passing.values())
+    # the fastest, or the rule's method when none is more than 3% faster
+    fastest = min(passing.values())
+    if r["method"] == rule:
+        assert fastest >= passing[rule] * 0.97
+    else:
+        assert passing[r["method"]] == fastest and fastest < passing[rule] * 0.97
     assert r["err"]["64/16"] == 0.0  # the reference against itself
     # 32, 64 or 128 state rows per workgroup: the same MFMA sequence per
     # element, the same bits
