@@ -636,10 +636,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
 // from one chunk's state to the next; the output waves' work fills the other
 // wave slot of each SIMD. Every A operand (Tb, W, K^T; Q, P) is read from the
 // workspace as contiguous 1 KB fragments and the gate record with one load,
-// issued three (recurrence) or four (output) chunks ahead into register
-// stages used round robin (bf16; fp32 fragments are four times larger and
-// use one stage). The chunk step is about as long as the CU takes to accept
-// its vector-memory instructions, so their number per chunk is kept small.
+// issued up to three (recurrence) or four (output) chunks ahead into
+// register stages used round robin (bf16; fewer stages for the wider
+// slices, whose registers hold more rows; fp32 fragments are four times
+// larger and use one stage). At 16 rows the chunk step is about as long as
+// the CU takes to accept its vector-memory instructions, so their number per
+// chunk is kept small.
 
 constexpr int kScanThreads = 512;
 
