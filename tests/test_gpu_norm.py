@@ -277,3 +277,36 @@ def test_prefill_norm_whole_head_slices(hk, hv, d):
                              scale=0.9, initial_state=dd["initial_state"])
     torch.cuda.synchronize()
     assert torch.equal(f, f_plain)
+
+
+@pytest.mark.parametrize("rows_case", ["whole_head", "exchanging"])
+def test_prefill_norm_bf16_states(rows_case):
+    """bf16 state storage with the normalisation fused into the scan: 40
+    sequences (128-row slices, whole rows per output wave) and 3 sequences
+    (64-row slices, two per head exchanging partial sums). Against the oracle
+    started from the bf16-rounded initial state; the final state is the
+    plain call's, bit for bit."""
+    n = 40 if rows_case == "whole_head" else 3
+    rows = 128 if rows_case == "whole_head" else 64
+    hk, hv, d = (8, 8, 128) if rows_case == "whole_head" else (16, 32, 128)
+    assert gdn.prefill_plan(n, n * 120, hk, hv, d, 64) == (64, rows)
+    rng = np.random.default_rng(77 + n)
+    lens = [int(x) for x in rng.integers(1, 240, size=n)]
+    inp = gs.make_inputs(lens, hk, hv, d, d, seed=gs.SEED_BASE + 560 + n, io_dtype="bf16", gate_dtype="f32",
+                         init_state=True)
+    w = _weight(d, seed=3)
+    dd = device_inputs(inp)
+    s0 = dd["initial_state"].to(torch.bfloat16)
+    note(f"prefill norm bf16 states {rows_case} n={n}")
+    wt = torch.from_numpy(w).cuda()
+    o, f = gdn.prefill(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["cu_seqlens"], chunk=64,
+                       initial_state=s0, state_dtype=torch.bfloat16, norm_weight=wt, norm_eps=1e-6)
+    _, f_plain = gdn.prefill(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["cu_seqlens"], chunk=64,
+                             initial_state=s0, state_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    o_ref, f_ref = oracle_ref(inp, initial_state=to_f64(s0))
+    eo = rel_err(to_f64(o), oracle.rms_norm(o_ref, w, 1e-6))
+    ef = rel_err(to_f64(f), f_ref)
+    print(f"[parity] prefill norm bf16 states {rows_case} out_err={eo:.3e} state_err={ef:.3e}", flush=True)
+    assert np.isfinite(to_f64(o)).all() and eo <= tol("bf16") and ef <= tol("bf16")
+    assert torch.equal(f, f_plain)
