@@ -200,6 +200,12 @@ int32_t prefill_with_method(const void *q, const void *k, const void *v, const v
 //                    (1 x 512: 28 vs 32 us);
 //   chunks of 64     otherwise: with several passes over the GPU the total
 //                    work counts, which the largest chunks minimise.
+// fp32 I/O (16-row slices, one register stage, fp32 MFMA) differs: chunks of
+// 64 are never the fastest there, and the token scan wins whenever the
+// chunked scan would need more than one pass over the CUs and L <= 1024
+// (8 x 512: 591 against 674 us at best chunked; 64 x 48: 434 against 628);
+// otherwise chunks of 16 (1 x 4096: 665 against 1,039 us with 64; 2 x 2048:
+// 659 against 780 token by token).
 constexpr int64_t kTokenScanTokens = 32;
 constexpr int64_t kTokenScanPerSeq = 10;
 constexpr int64_t kChunk16PerSeq = 48;
@@ -225,6 +231,10 @@ inline int32_t scan_slice_rows(int64_t num_seqs, int64_t hv, int64_t dv, bool io
 
 inline int32_t rule_chunk(int64_t num_seqs, int64_t total_tokens, int64_t hv, int64_t dv, bool io_bf16) {
     if (total_tokens <= kTokenScanTokens || total_tokens <= kTokenScanPerSeq * num_seqs) return 1;
+    if (!io_bf16) {
+        const bool passes = num_seqs * hv * (dv / 16) > kScanOnePassWgs;
+        return passes && total_tokens <= kChunk32PerSeq * num_seqs ? 1 : 16;
+    }
     const int64_t rows = scan_slice_rows(num_seqs, hv, dv, io_bf16);
     if (rows >= 64) return total_tokens <= 16 * num_seqs ? 16 : total_tokens <= 32 * num_seqs ? 32 : 64;
     if (total_tokens <= kChunk16PerSeq * num_seqs) return 16;
