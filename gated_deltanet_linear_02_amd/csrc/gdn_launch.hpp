@@ -200,16 +200,17 @@ int32_t prefill_with_method(const void *q, const void *k, const void *v, const v
 //                    (1 x 512: 28 vs 32 us);
 //   chunks of 64     otherwise: with several passes over the GPU the total
 //                    work counts, which the largest chunks minimise.
-// fp32 I/O (16-row slices, one register stage, fp32 MFMA) differs: chunks of
-// 64 are never the fastest there, and the token scan wins whenever the
-// chunked scan would need more than one pass over the CUs and L <= 1024
-// (8 x 512: 591 against 674 us at best chunked; 64 x 48: 434 against 628);
-// otherwise chunks of 16 (1 x 4096: 665 against 1,039 us with 64; 2 x 2048:
-// 659 against 780 token by token).
+// fp32 I/O (16-row slices, fp32 MFMA, fewer register stages) crosses over
+// later: token by token up to L = 48 (64 x 48: 426 against 496 us at best
+// chunked; 16 x 64: 155 against 131), chunks of 32 for one pass and
+// L <= 512 (1 x 128: 29 against 40 us with 64), else 64 (1 x 4096: 323
+// against 405 us with 32; 8 x 300: 230 against 273).
 constexpr int64_t kTokenScanTokens = 32;
 constexpr int64_t kTokenScanPerSeq = 10;
 constexpr int64_t kChunk16PerSeq = 48;
 constexpr int64_t kChunk32PerSeq = 1024;
+constexpr int64_t kF32TokenScanPerSeq = 48;
+constexpr int64_t kF32Chunk32PerSeq = 512;
 constexpr int64_t kScanOnePassWgs = 256;  // gfx950 (MI355X): 256 CUs
 // State rows per chunked-scan workgroup: 16, 32, 64 or 128, more than 16
 // for bf16 I/O only and at most dv.
@@ -232,8 +233,9 @@ inline int32_t scan_slice_rows(int64_t num_seqs, int64_t hv, int64_t dv, bool io
 inline int32_t rule_chunk(int64_t num_seqs, int64_t total_tokens, int64_t hv, int64_t dv, bool io_bf16) {
     if (total_tokens <= kTokenScanTokens || total_tokens <= kTokenScanPerSeq * num_seqs) return 1;
     if (!io_bf16) {
-        const bool passes = num_seqs * hv * (dv / 16) > kScanOnePassWgs;
-        return passes && total_tokens <= kChunk32PerSeq * num_seqs ? 1 : 16;
+        if (total_tokens <= kF32TokenScanPerSeq * num_seqs) return 1;
+        const bool one_pass = num_seqs * hv * (dv / 16) <= kScanOnePassWgs;
+        return one_pass && total_tokens <= kF32Chunk32PerSeq * num_seqs ? 32 : 64;
     }
     const int64_t rows = scan_slice_rows(num_seqs, hv, dv, io_bf16);
     if (rows >= 64) return total_tokens <= 16 * num_seqs ? 16 : total_tokens <= 32 * num_seqs ? 32 : 64;

@@ -637,9 +637,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(IsBf16<E>::
 // wave slot of each SIMD. Every A operand (Tb, W, K^T; Q, P) is read from the
 // workspace as contiguous 1 KB fragments and the gate record with one load,
 // issued up to three (recurrence) or four (output) chunks ahead into
-// register stages used round robin (bf16; fewer stages for the wider
-// slices, whose registers hold more rows; fp32 fragments are four times
-// larger and use one stage). At 16 rows the chunk step is about as long as
+// register stages used round robin (fewer stages for the wider slices,
+// whose registers hold more rows, and for fp32 fragments, which are four
+// times larger: two and three). At 16 rows the chunk step is about as long as
 // the CU takes to accept its vector-memory instructions, so their number per
 // chunk is kept small.
 
@@ -764,7 +764,7 @@ struct OStage {
     }
 };
 
-// Runs body(st, nxt, fut, c, three, idx) for chunks c = 0 .. nch-1 over N register
+// Runs body(st, nxt, fut, c, idx) for chunks c = 0 .. nch-1 over N register
 // stages used round robin: chunk c sits in st[c % N], `nxt` holds chunk c + 1
 // and `fut` (which held chunk c - 1) is refilled with chunk c + N - 1. The
 // loop is unrolled by N so that every stage index is a compile-time
@@ -773,14 +773,14 @@ struct OStage {
 // entry.
 template <int N, int I = 0, typename St, typename Body>
 __device__ __forceinline__ void pipeline_step(St (&st)[N], int c, Body &body) {
-    body(st[I], st[(I + 1) % N], st[(I + N - 1) % N], c + I, std::true_type(), std::integral_constant<int, I>());
+    body(st[I], st[(I + 1) % N], st[(I + N - 1) % N], c + I, std::integral_constant<int, I>());
     if constexpr (I + 1 < N) pipeline_step<N, I + 1>(st, c, body);
 }
 template <int N, int I = 0, typename St, typename Body>
 __device__ __forceinline__ void pipeline_tail(St (&st)[N], int c, int nch, Body &body) {
     if constexpr (I + 1 < N) {
         if (c + I < nch)
-            body(st[I], st[(I + 1) % N], st[(I + N - 1) % N], c + I, std::true_type(), std::integral_constant<int, I>());
+            body(st[I], st[(I + 1) % N], st[(I + N - 1) % N], c + I, std::integral_constant<int, I>());
         pipeline_tail<N, I + 1>(st, c, nch, body);
     }
 }
@@ -830,12 +830,12 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
     constexpr int LDK = L::LDK, LDC = L::LDC;
     constexpr int RT = SH::RT, MT = SH::MT, NMW = SH::NMW;
     constexpr int KBD = SH::KBD, KBC = SH::KBC;
-    // Register stages per role (bf16); fp32 fragments are 4x larger and use one.
-    constexpr bool kPipelined = IsBf16<E>::value;
+    // Register stages per role; fp32 fragments are 4x larger and take fewer.
     // The fused normalisation's exchange alternates two register slots by
     // chunk parity, which the unrolled pipeline keeps compile-time when the
     // output stages are even.
-    constexpr int kRStages = R == 16 ? 4 : R <= 64 ? 3 : 2, kOStages = R == 16 && !kNorm ? 5 : R <= 32 ? 4 : 3;
+    constexpr int kRStages = !IsBf16<E>::value ? 2 : R == 16 ? 4 : R <= 64 ? 3 : 2,
+                  kOStages = !IsBf16<E>::value ? (kNorm ? 4 : 3) : R == 16 && !kNorm ? 5 : R <= 32 ? 4 : 3;
     // The fused normalisation: with several slices per head they exchange
     // partial sums (kNormX); a slice that holds the whole head (R = DV)
     // normalises its rows in the output wave that computes them (kNormW).
@@ -920,8 +920,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         }
         __syncthreads();  // S0 and chunk 0's V rows staged
 
-        auto body = [&](RS &st, RS &, RS &fut, int c, auto three, auto) {
-            constexpr bool kThree = decltype(three)::value;
+        auto body = [&](RS &st, RS &, RS &fut, int c, auto) {
             // ---- phase 1: U = Tb V - W S0^T (W is stored negated). Token and
             // key contractions accumulate separately: with d = 16 they use
             // MFMAs of different shapes, which must not be chained through
@@ -958,7 +957,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             // The prefetch is issued here rather than at the chunk start: phase 1
             // bounds the chunk through these waves, phase 2 through the output
             // waves, so a load queue that is full costs less here.
-            if constexpr (kThree) fut.load(tbmat, wmat, ktmat, chunk(min(c + kRStages - 1, nch - 1)), q, lane);
+            fut.load(tbmat, wmat, ktmat, chunk(min(c + kRStages - 1, nch - 1)), q, lane);
             const float gc = sGc[4 * (c & 1)];
 #pragma unroll
             for (int rr = 0; rr < RW; ++rr) {
@@ -980,21 +979,13 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                 }
             }
             __syncthreads();
-            if constexpr (!kThree) st.load(tbmat, wmat, ktmat, chunk(min(c + 1, nch - 1)), q, lane);
         };
 
         if (nch > 0) {
-            if constexpr (kPipelined) {
-                RS st[kRStages];
+            RS st[kRStages];
 #pragma unroll
-                for (int i = 0; i + 1 < kRStages; ++i)
-                    st[i].load(tbmat, wmat, ktmat, chunk(min(i, nch - 1)), q, lane);
-                run_pipeline<kRStages>(st, nch, body);
-            } else {
-                RS st0;
-                st0.load(tbmat, wmat, ktmat, chunk(0), q, lane);
-                for (int c = 0; c < nch; ++c) body(st0, st0, st0, c, std::false_type(), std::integral_constant<int, -1>());
-            }
+            for (int i = 0; i + 1 < kRStages; ++i) st[i].load(tbmat, wmat, ktmat, chunk(min(i, nch - 1)), q, lane);
+            run_pipeline<kRStages>(st, nch, body);
         }
 
         if constexpr (kNormX) {
@@ -1034,8 +1025,9 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         // below), and every output wave loads the V rows 16 q .. 16 q + 15
         // of its R columns besides (R / 32 loads).
         // Memory instructions, not bytes, bound the scan, so these small
-        // loads are folded into as few instructions as possible. The fp32
-        // path (one stage) loads V per wave and the gate record in every wave.
+        // loads are folded into as few instructions as possible. fp32 I/O
+        // loads V in every output wave with its fragments, and waves 1-3
+        // touch (16-row slices) or load the gate record again.
         constexpr int kRunQ = (int)((size_t)C * DK * sizeof(E) / 1024);
         constexpr int kRunM = (int)((size_t)C * C * sizeof(E) / 1024);
         // The L2 touch serves 16-row slices only: wider slices share each
@@ -1043,7 +1035,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         // in the issuing wave's load queue, measured slower than none (scan
         // at 2 x 2048, 32 rows: 62.5 against 55.3 us; 4 x 1024, 64 rows:
         // 50.9 against 45.8 us; 4 rotated buffer sets).
-        constexpr bool kTouch = kPipelined && (size_t)C * DK * sizeof(E) % 1024 == 0 &&
+        constexpr bool kTouch = (size_t)C * DK * sizeof(E) % 1024 == 0 &&
                                 (size_t)C * C * sizeof(E) % 1024 == 0 && R == 16;
         auto gate_ptr = [&](const ChunkRef &r) {
             // the chunk's gate record, 4 floats per lane: lanes [0, C/4)
@@ -1089,8 +1081,8 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         };
         auto aux_ptr = [&](int c_aux, int c_touch) {
             const ChunkRef r = chunk(c_aux);
-            if (!kPipelined || q == 0) return gate_ptr(r);
-            if (q == 1 || R > 16) return kTouch ? touch_ptr(c_touch) : gate_ptr(r);
+            if (q == 0) return gate_ptr(r);
+            if (q == 1 || R > 16 || !IsBf16<E>::value) return kTouch ? touch_ptr(c_touch) : gate_ptr(r);
             const int vrow = min(32 * (q - 2) + (lane >> 1), r.clen - 1);
             return reinterpret_cast<const f32x4 *>(v + ((size_t)(r.tok0 + vrow) * hv + h) * DK + col0 + 8 * (lane & 1));
         };
@@ -1129,7 +1121,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                         for (int i = 0; i < 8; ++i) dst[(32 * j + 8 * (lane & 3) + i) * LDC] = x[i];
                     }
                 }
-            } else if constexpr (kPipelined) {
+            } else if constexpr (IsBf16<E>::value) {
                 if (q >= 2) {
                     const int t = 32 * (q - 2) + (lane >> 1);
                     if (t < C) {
@@ -1315,7 +1307,7 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
             }
         };
 
-        OS st[kPipelined ? kOStages : 1];
+        OS st[kOStages];
         if (nch > 0) {
             st[0].load(v, pmat, qmat, chunk(0), hv, h, col0, q, lane);
             load_aux(st[0], 0, min(kTouchAhead, nch - 1));
@@ -1323,32 +1315,20 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
         }
         __syncthreads();  // S0 and chunk 0's V rows staged
 
-        // One chunk c with its operands in `st`; `nxt` holds chunk c + 1
-        // (pipelined: its V rows are staged here; `fut` is refilled with
-        // chunk c + kOStages - 1). One stage: chunk c + 1's V rows are loaded
-        // at the start and `st` is refilled with chunk c + 1 at the end.
-        auto body = [&](OS &st, OS &nxt, OS &fut, int c, auto three, auto idx) {
-            constexpr bool kThree = decltype(three)::value;
-            E4 vn;
-            OS gn;  // one stage: chunk c + 1's gate vectors (its aux)
-            if constexpr (kThree) {
-                const int cf = min(c + kOStages - 1, nch - 1);
-                load_aux(fut, cf, min(c + kTouchAhead, nch - 1));
-                fut.load(v, pmat, qmat, chunk(cf), hv, h, col0, q, lane);
-            } else {
-                const ChunkRef rn = chunk(min(c + 1, nch - 1));
-                const int vrow = min(16 * min(q, RT - 1) + (lane >> 2), rn.clen - 1);
-                vn = *reinterpret_cast<const E4 *>(v + ((size_t)(rn.tok0 + vrow) * hv + h) * DK + col0 + 4 * (lane & 3));
-                gn.aux = *gate_ptr(rn);
-            }
+        // One chunk c with its operands in `st`; `nxt` holds chunk c + 1,
+        // whose V rows are staged here, and `fut` is refilled with chunk
+        // c + kOStages - 1.
+        auto body = [&](OS &st, OS &nxt, OS &fut, int c, auto idx) {
+            const int cf = min(c + kOStages - 1, nch - 1);
+            load_aux(fut, cf, min(c + kTouchAhead, nch - 1));
+            fut.load(v, pmat, qmat, chunk(cf), hv, h, col0, q, lane);
             // The next chunk's V rows and gate vectors go to LDS now, while
             // this wave would wait for the recurrence waves anyway (their
             // buffers were last read before the previous barrier).
-            if constexpr (kThree) put_chunk(nxt, nxt.vr, (c + 1) & 1);
-            else put_chunk(gn, vn, (c + 1) & 1);
+            put_chunk(nxt, nxt.vr, (c + 1) & 1);
             // the step's parity: compile-time in the unrolled pipeline
             constexpr int kIdx = decltype(idx)::value;
-            const int par = kIdx >= 0 && kOStages % 2 == 0 ? (kIdx & 1) : (c & 1);
+            const int par = kOStages % 2 == 0 ? (kIdx & 1) : (c & 1);
             if constexpr (kNormX) norm_phase1(c, par);
             // ---- phase 1: O1^T = S0 Q^T
             f32x4 o1[RW];
@@ -1418,20 +1398,15 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                 if (q == 1) load_block(max(c + 2 - kNormLag, 0), par);
             }
             __syncthreads();
-            if constexpr (!kThree) st.load(v, pmat, qmat, chunk(min(c + 1, nch - 1)), hv, h, col0, q, lane);
         };
 
         if (nch > 0) {
-            if constexpr (kPipelined) {
 #pragma unroll
-                for (int i = 1; i + 1 < kOStages; ++i) {
-                    st[i].load(v, pmat, qmat, chunk(min(i, nch - 1)), hv, h, col0, q, lane);
-                    load_aux(st[i], min(i, nch - 1), min(i + kTouchAhead, nch - 1));
-                }
-                run_pipeline<kOStages>(st, nch, body);
-            } else {
-                for (int c = 0; c < nch; ++c) body(st[0], st[0], st[0], c, std::false_type(), std::integral_constant<int, -1>());
+            for (int i = 1; i + 1 < kOStages; ++i) {
+                st[i].load(v, pmat, qmat, chunk(min(i, nch - 1)), hv, h, col0, q, lane);
+                load_aux(st[i], min(i, nch - 1), min(i + kTouchAhead, nch - 1));
             }
+            run_pipeline<kOStages>(st, nch, body);
             if constexpr (kNormX) {
                 // the last kNormLag chunks' outputs, in kNormLag more steps
                 // of two barriers (the recurrence waves take part)

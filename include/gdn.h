@@ -137,9 +137,9 @@ int32_t gdn_prefill_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, i
  *              L <= 10; with 64 or 128 rows 16 when L <= 16, 32 when
  *              L <= 32, else 64; with 16 or 32 rows 16 when L <= 48, 32
  *              when the workgroups fit the GPU's 256 CUs and L <= 1024,
- *              else 64. fp32 I/O: 1 also when the 16-row scan would take
- *              more than one pass over the CUs and L <= 1024, else 16
- *              (gdn_prefill_method tells which).
+ *              else 64. fp32 I/O: 1 when T <= 32 or L <= 48, 32 when
+ *              the 16-row scan fits the CUs in one pass and L <= 512, else
+ *              64 (gdn_prefill_method tells which).
  *              The result does not depend on it beyond rounding.
  * dk, dv       16, 32, 64 or 128 each.
  * scale        multiplies every output (1.0 for the plain rule).

@@ -307,10 +307,11 @@ def test_chunk_zero_rule(lib):
     assert m(1, 4096) == 64 and m(8, 8 * 300) == 64  # long, or several passes
     assert m(2, 2 * 600) == 32                       # two sequences: one pass of 32-row slices
     assert m(4, 4 * 600) == 64                       # four: 64-row slices, whose long step wants chunks of 64
-    # fp32 I/O: the token scan once the 16-row scan needs two passes (L <= 1024), else chunks of 16
+    # fp32 I/O: token by token up to L = 48, chunks of 32 for one pass and L <= 512, else 64
     f32 = lambda n, T: gdn.prefill_method(n, T, 16, 32, 128, io_dtype=torch.float32)
-    assert f32(2, 2 * 600) == 1 and f32(8, 8 * 512) == 1 and f32(2, 2 * 2048) == 16
-    assert f32(1, 4096) == 16 and f32(1, 128) == 16 and f32(1, 16) == 1
+    assert f32(1, 16) == 1 and f32(64, 64 * 48) == 1 and f32(64, 64 * 49) == 64
+    assert f32(1, 128) == 32 and f32(1, 512) == 32 and f32(1, 1024) == 64 and f32(1, 4096) == 64
+    assert f32(2, 2 * 600) == 64 and f32(8, 8 * 300) == 64
     assert gdn.prefill_method(1, 4096, 16, 32, 128, chunk=16) == 16  # explicit chunks as given
     assert gdn.prefill_method(1, 4096, 3, 32, 128) == 0              # rejected shape
     # state rows per scan workgroup: the fewest of 16, 32, 64, 128 whose
@@ -323,7 +324,7 @@ def test_chunk_zero_rule(lib):
     assert p(64, 64 * 16) == (16, 128) and p(64, 64 * 32) == (32, 128)  # one chunk per sequence
     assert p(8, 8 * 512, d=64) == (64, 64) and p(8, 8 * 512, d=32) == (32, 32)  # at most d
     assert p(1, 4096, hv=48) == (64, 32)                             # 384 slices of 16 rows
-    assert p(2, 2 * 4096, io=torch.float32) == (16, 16)              # fp32 I/O: 16 rows
+    assert p(2, 2 * 4096, io=torch.float32) == (64, 16)              # fp32 I/O: 16 rows
     assert p(64, 64 * 4, c=1) == (1, 0) and p(64, 64 * 4) == (1, 0)  # token by token: no scan
     assert p(40, 40 * 100, d=16, hv=16) == (64, 16)                  # d = 16: 16 rows
     assert p(1, 4096, hv=3) == (0, 0)                                 # rejected
