@@ -798,9 +798,10 @@ __device__ __forceinline__ void keep_alive(float x) { asm volatile("" ::"v"(x));
 constexpr int kTouchAhead = 8;
 
 // Spin limit of the fused normalisation's wait for the other row slices'
-// partial sums (about 50 ms of s_sleep 2): a wait that long means a slice
+// partial sums (each retry is an s_sleep 2 and a device-coherent load, about
+// a microsecond, so roughly 0.1 s in all): a wait that long means a slice
 // never ran, and the rows it leaves are written as NaN rather than wrong.
-constexpr int kNormSpinMax = 1 << 20;
+constexpr int kNormSpinMax = 1 << 16;
 
 // Word 3 of a raw buffer resource on gfx9-family GPUs (gfx950 included).
 constexpr int kBufferWord3 = 0x00020000;
@@ -1232,6 +1233,11 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2,
                         break;
                     }
                     __builtin_amdgcn_s_sleep(2);
+                    // The loop stores nothing; without this compiler barrier
+                    // its loads are hoisted out of it, and a slice that found
+                    // a slot empty would test the same registers until the
+                    // spin limit.
+                    asm volatile("" ::: "memory");
                     load_into(b, cc);
                     if (block_ready(b, cc)) break;
                 }

@@ -54,12 +54,18 @@ def test_decode_step_graph_replays(norm, state_dtype):
         assert torch.equal(state, ref_state), f"replay {t}: states differ from the eager call"
 
 
-def test_prefill_graph_replays():
-    """Chunked prefill (preparation and scan) of 3 sequences, captured once
-    and replayed on new token data; every replay equals the eager call."""
-    lens = [300, 77, 5]
+@pytest.mark.parametrize("lens,norm,rows", [([300, 77, 5], False, 64), ([300, 77, 5], True, 64),
+                                           ([120, 7, 64, 200] * 3, True, 128)])
+def test_prefill_graph_replays(lens, norm, rows):
+    """Chunked prefill (preparation and scan), captured once and replayed on
+    new token data; every replay equals the eager call. 3 sequences take
+    64-row scan slices (with a normalisation weight their slices exchange
+    partial sums through the workspace, whose slots the preparation kernel
+    resets in every replay); 12 take 128-row slices, normalised in place."""
+    assert gdn.prefill_plan(len(lens), sum(lens), 16, 32, 128, 64) == (64, rows)
     runs = [gs.make_inputs(lens, 16, 32, 128, 128, seed=gs.SEED_BASE + 1600 + t, io_dtype="bf16",
                            gate_dtype="f32", init_state=True) for t in range(4)]
+    w = torch.from_numpy(gs.norm_weight(128, seed=gs.SEED_BASE + 1650)).cuda() if norm else None
     dev = [device_inputs(r) for r in runs]
     T, N = sum(lens), len(lens)
     static = {x: dev[0][x].clone() for x in ("q", "k", "v", "g", "beta", "cu_seqlens", "initial_state")}
@@ -70,9 +76,10 @@ def test_prefill_graph_replays():
 
     def call(src, o, f):
         return gdn.prefill(src["q"], src["k"], src["v"], src["g"], src["beta"], src["cu_seqlens"], chunk=64,
-                           initial_state=src["initial_state"], final_state=f, out=o, workspace=ws)
+                           initial_state=src["initial_state"], final_state=f, out=o, workspace=ws,
+                           norm_weight=w, norm_eps=1e-6)
 
-    note("prefill graph capture")
+    note(f"prefill graph capture lens={lens[:4]} norm={norm}")
     call(static, out, fin)  # warm-up (first launch sets kernel attributes)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()

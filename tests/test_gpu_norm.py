@@ -252,6 +252,46 @@ def test_prefill_norm_repeated_calls_are_identical():
     assert not torch.equal(outs[0], outs[2])
 
 
+def test_prefill_norm_slice_waits_for_partner():
+    """Sequences of 300, 77 and 5 tokens: 64-row slices that exchange
+    partial sums. The 5-token sequence's slices finish their one chunk in a
+    few steps, so one of a head's slices often reaches the sum before its
+    partner has published (most often in the first calls of a process, on
+    fresh memory) and retries its loads until the partials arrive. Four
+    inputs, each called three times with freshly allocated outputs, in the
+    order a serving loop would: every call finite, the same bits on every
+    repeat, and the oracle's values."""
+    lens = [300, 77, 5]
+    assert gdn.prefill_plan(3, sum(lens), 16, 32, 128, 64) == (64, 64)
+    w = _weight(128, seed=11)
+    wt = torch.from_numpy(w).cuda()
+    inps = [gs.make_inputs(lens, 16, 32, 128, 128, seed=gs.SEED_BASE + 540 + i, io_dtype="bf16",
+                           gate_dtype="f32", init_state=True) for i in range(4)]
+    devs = [device_inputs(x) for x in inps]
+    ws = torch.empty(gdn.prefill_workspace_size(3, sum(lens), 16, 32, 128, 128, 64, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    note("prefill norm slice waits: 4 inputs x 3 calls")
+    outs = [[] for _ in inps]
+    for rep in range(3):
+        for i, d in enumerate(devs):
+            o, _ = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=64,
+                               initial_state=d["initial_state"],
+                               final_state=torch.empty((3, 32, 128, 128), dtype=torch.float32, device="cuda"),
+                               out=torch.empty((sum(lens), 32, 128), dtype=torch.bfloat16, device="cuda"),
+                               norm_weight=wt, norm_eps=1e-6, workspace=ws)
+            torch.cuda.synchronize()
+            outs[i].append(o)
+    for i, inp in enumerate(inps):
+        for rep, o in enumerate(outs[i]):
+            nan = int(torch.isnan(o.float()).sum())
+            assert nan == 0, f"input {i} call {rep}: {nan} NaN outputs (a slice gave up waiting)"
+            assert torch.equal(o, outs[i][0]), f"input {i} call {rep} differs from its first call"
+        o_ref, _ = oracle_ref(inp)
+        eo = rel_err(to_f64(outs[i][0]), oracle.rms_norm(o_ref, w, 1e-6))
+        print(f"[parity] prefill norm slice waits input {i} out_err={eo:.3e}", flush=True)
+        assert eo <= tol("bf16")
+
+
 @pytest.mark.parametrize("hk,hv,d", [(4, 16, 64), (8, 8, 128), (2, 8, 32)])
 def test_prefill_norm_whole_head_slices(hk, hv, d):
     """bf16, enough sequences that the scan takes slices of a whole head
