@@ -7,6 +7,7 @@
 #include "gdn_launch.hpp"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <mutex>
 #include <new>
@@ -41,6 +42,22 @@ TimingEvents timing_claim(KernelKind kind) {
     T.kinds[T.used] = kind;
     ++T.used;
     return ev;
+}
+
+int32_t stream_device_cus(hipStream_t stream) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int32_t> cached[kMaxDevices] = {};
+    hipDevice_t dev = 0;
+    const hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices) {
+        const int32_t n = cached[dev].load(std::memory_order_relaxed);
+        if (n > 0) return n;
+    }
+    int32_t n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) return 0;
+    if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 // ----------------------------------------------------------------- checks
@@ -239,13 +256,14 @@ static int32_t prefill_impl(const void *q, const void *k, const void *v, const v
     A.s0 = initial_state; A.s_final = final_state; A.out = out;
     A.ws = static_cast<char *>(workspace); A.lay = L;
     // With bf16 I/O the chunked scan takes the normalisation itself when one
-    // workgroup holds whole rows (rows = dv) or its workgroups fit the GPU in
-    // one pass, so that each output is rounded once (at T = 4096 the fused
-    // form adds about 5 us to the scan, the pass 10.5 us); otherwise (fp32
-    // I/O, where the pass reads the same fp32 values, or narrower slices over
-    // more than one pass) a pass over out follows.
-    const bool fused_norm = norm_w && c != 1 && io_dtype == GDN_BF16 &&
-                            fused_norm_fits(num_seqs, hk, hv, dv, m.rows);
+    // workgroup holds whole rows (rows = dv) or its workgroups fit the
+    // stream's device in one pass, so that each output is rounded once (at
+    // T = 4096 the fused form adds about 5 us to the scan, the pass 10.5 us);
+    // otherwise (fp32 I/O, where the pass reads the same fp32 values, or
+    // narrower slices over more than one pass) a pass over out follows.
+    const bool fused_norm =
+        norm_w && c != 1 && io_dtype == GDN_BF16 &&
+        fused_norm_fits(num_seqs, hk, hv, dv, m.rows, stream_device_cus(static_cast<hipStream_t>(stream)));
     if (fused_norm) {
         A.norm_w = norm_w;
         A.norm_eps = norm_eps;

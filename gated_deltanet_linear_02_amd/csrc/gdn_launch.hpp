@@ -129,15 +129,18 @@ inline int64_t scan_grid(int64_t num_seqs, int64_t hk, int64_t hv, int64_t dv, i
 
 // Whether a chunked prefill with an output normalisation takes it in the
 // scan: when one workgroup holds a head's whole state (rows = dv), which
-// normalises its own rows, or when the scan's workgroups fit the GPU in one
-// pass. The row slices of a head then exchange their partial sums of squares
-// while all of them run; with more workgroups than CUs, slices of one head
-// could wait on one another across passes, so those calls normalise in a
-// pass after the scan.
-constexpr int64_t kFusedNormMaxWgs = 256;  // gfx950 (MI355X): 256 CUs
-inline bool fused_norm_fits(int64_t num_seqs, int64_t hk, int64_t hv, int64_t dv, int64_t rows) {
-    return rows == dv || scan_grid(num_seqs, hk, hv, dv, rows) <= kFusedNormMaxWgs;
+// normalises its own rows, or when the scan's workgroups fit the device in
+// one pass, one per compute unit (`cus`: the device's count, 256 on a whole
+// MI355X, fewer on a partition of one). The row slices of a head then
+// exchange their partial sums of squares while all of them run; with more
+// workgroups than CUs, slices of one head could wait on one another across
+// passes, so those calls normalise in a pass after the scan.
+inline bool fused_norm_fits(int64_t num_seqs, int64_t hk, int64_t hv, int64_t dv, int64_t rows, int64_t cus) {
+    return rows == dv || scan_grid(num_seqs, hk, hv, dv, rows) <= cus;
 }
+// Compute units of the device that owns `stream` (0 if HIP cannot say),
+// looked up once per device.
+int32_t stream_device_cus(hipStream_t stream);
 
 // Chunked prefill (chunk 16, 32 or 64): preparation and scan kernels.
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t st);

@@ -262,12 +262,15 @@ int32_t gdn_decode_step(const void *q, const void *k, const void *v,
  * value head) state, so the unnormalised row never goes to memory. A chunked
  * prefill with bf16 I/O normalises inside the scan when a scan workgroup
  * holds whole rows (state rows per workgroup = dv, the widest slices the scan
- * takes for several sequences at d = 128) or when its workgroups fit the GPU
- * in one pass (one sequence at HK = 16, HV = 32, d = 128, for instance); in
- * the second case the workgroups holding the parts of a row exchange partial
- * sums of squares through the workspace. Either way each output is rounded
- * once. Otherwise (fp32 I/O, token by token, or narrower slices over more
- * than one pass)
+ * takes for several sequences at d = 128) or when its workgroups, one per
+ * compute unit, fit the stream's device in one pass (one sequence at
+ * HK = 16, HV = 32, d = 128 on a whole MI355X, for instance; a partition of
+ * one counts its own CUs); in the second case the workgroups holding the
+ * parts of a row exchange partial sums of squares through the workspace and
+ * wait for one another, so they must all be resident at once: a stream
+ * limited to fewer CUs than its device (a CU mask) should not take such
+ * calls. Either way each output is rounded once. Otherwise (fp32 I/O, token
+ * by token, or narrower slices over more than one pass)
  * the prefill's kernels are followed by one pass that rewrites the rows of
  * out in place; rows of tokens outside [cu_seqlens[0], cu_seqlens[N]) are
  * left untouched, and in bf16 a row is then rounded twice (before and after
