@@ -252,31 +252,32 @@ def test_prefill_norm_repeated_calls_are_identical():
     assert not torch.equal(outs[0], outs[2])
 
 
-def test_prefill_norm_slice_waits_for_partner():
-    """Sequences of 300, 77 and 5 tokens: 64-row slices that exchange
-    partial sums. The 5-token sequence's slices finish their one chunk in a
-    few steps, so one of a head's slices often reaches the sum before its
-    partner has published (most often in the first calls of a process, on
-    fresh memory) and retries its loads until the partials arrive. Four
-    inputs, each called three times with freshly allocated outputs, in the
-    order a serving loop would: every call finite, the same bits on every
-    repeat, and the oracle's values."""
-    lens = [300, 77, 5]
-    assert gdn.prefill_plan(3, sum(lens), 16, 32, 128, 64) == (64, 64)
+@pytest.mark.parametrize("lens,rows", [([300, 77, 5], 64), ([700, 5], 32)])
+def test_prefill_norm_slice_waits_for_partner(lens, rows):
+    """Ragged batches with a 5-token sequence: 64- or 32-row slices (two or
+    four per head) that exchange partial sums. The short sequence's slices
+    finish their one chunk in a few steps, so one of a head's slices often
+    reaches the sum before its partners have published (most often in the
+    first calls of a process, on fresh memory) and retries its loads until
+    the partials arrive. Four inputs, each called three times with freshly
+    allocated outputs, in the order a serving loop would: every call finite,
+    the same bits on every repeat, and the oracle's values."""
+    n = len(lens)
+    assert gdn.prefill_plan(n, sum(lens), 16, 32, 128, 64) == (64, rows)
     w = _weight(128, seed=11)
     wt = torch.from_numpy(w).cuda()
-    inps = [gs.make_inputs(lens, 16, 32, 128, 128, seed=gs.SEED_BASE + 540 + i, io_dtype="bf16",
+    inps = [gs.make_inputs(lens, 16, 32, 128, 128, seed=gs.SEED_BASE + 540 + 10 * n + i, io_dtype="bf16",
                            gate_dtype="f32", init_state=True) for i in range(4)]
     devs = [device_inputs(x) for x in inps]
-    ws = torch.empty(gdn.prefill_workspace_size(3, sum(lens), 16, 32, 128, 128, 64, torch.bfloat16),
+    ws = torch.empty(gdn.prefill_workspace_size(n, sum(lens), 16, 32, 128, 128, 64, torch.bfloat16),
                      dtype=torch.uint8, device="cuda")
-    note("prefill norm slice waits: 4 inputs x 3 calls")
+    note(f"prefill norm slice waits lens={lens}: 4 inputs x 3 calls")
     outs = [[] for _ in inps]
     for rep in range(3):
         for i, d in enumerate(devs):
             o, _ = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=64,
                                initial_state=d["initial_state"],
-                               final_state=torch.empty((3, 32, 128, 128), dtype=torch.float32, device="cuda"),
+                               final_state=torch.empty((n, 32, 128, 128), dtype=torch.float32, device="cuda"),
                                out=torch.empty((sum(lens), 32, 128), dtype=torch.bfloat16, device="cuda"),
                                norm_weight=wt, norm_eps=1e-6, workspace=ws)
             torch.cuda.synchronize()
