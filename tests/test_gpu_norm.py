@@ -293,6 +293,50 @@ def test_prefill_norm_slice_waits_for_partner(lens, rows):
         assert eo <= tol("bf16")
 
 
+def test_prefill_norm_exchange_on_concurrent_streams():
+    """Slices of a head that exchange partial sums must all be resident at
+    once. Two prefills that each fill the GPU (one 4,096-token sequence,
+    16-row slices: 256 workgroups) run on two streams at once, beside a long
+    matrix product on a third; the slices of each head sit next to one
+    another in an XCD's dispatch order, so every call still finishes without
+    exhausting its wait. Every output equals that of the same call made
+    alone, bit for bit."""
+    lens = [4096]
+    assert gdn.prefill_plan(1, 4096, 16, 32, 128, 64) == (64, 16)
+    w = torch.from_numpy(_weight(128, seed=12)).cuda()
+    inps = [device_inputs(gs.make_inputs(lens, 16, 32, 128, 128, seed=gs.SEED_BASE + 560 + i,
+                                         io_dtype="bf16", gate_dtype="f32")) for i in range(2)]
+    size = gdn.prefill_workspace_size(1, 4096, 16, 32, 128, 128, 64, torch.bfloat16)
+    wss = [torch.empty(size, dtype=torch.uint8, device="cuda") for _ in range(2)]
+
+    def call(i, stream=None):
+        d = inps[i]
+        o, _ = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=64,
+                           norm_weight=w, norm_eps=1e-6, workspace=wss[i], stream=stream)
+        return o
+
+    note("prefill norm exchange: alone")
+    alone = [call(0), call(1)]
+    torch.cuda.synchronize()
+    a = torch.randn(4096, 4096, device="cuda")
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    main = torch.cuda.current_stream()
+    for st in streams:
+        st.wait_stream(main)
+    note("prefill norm exchange: two streams and a matrix product")
+    outs = []
+    for rep in range(4):
+        with torch.cuda.stream(streams[2]):
+            a = (a @ a).clamp_(-1.0, 1.0)
+        outs.append((call(0, streams[0]), call(1, streams[1])))
+    for st in streams:
+        main.wait_stream(st)
+    torch.cuda.synchronize()
+    for rep, (o0, o1) in enumerate(outs):
+        assert not torch.isnan(o0.float()).any() and not torch.isnan(o1.float()).any(), f"rep {rep}: NaN rows"
+        assert torch.equal(o0, alone[0]) and torch.equal(o1, alone[1]), f"rep {rep}: differs from the call alone"
+
+
 @pytest.mark.parametrize("hk,hv,d", [(4, 16, 64), (8, 8, 128), (2, 8, 32)])
 def test_prefill_norm_whole_head_slices(hk, hv, d):
     """bf16, enough sequences that the scan takes slices of a whole head
