@@ -5,12 +5,19 @@ and gates with occasional extreme decays (g = -1e4, a = 0) and b = 0 or 1.
 Every case is drawn from its own seed, printed before it runs, and held to
 the usual bars (bf16 2e-2, fp32 1e-4 max-rel). A second set draws batches
 large enough that the chunked scan takes 32 state rows per workgroup
-(N * HV * DV / 16 > 256, bf16 I/O)."""
+(N * HV * DV / 16 > 256, bf16 I/O). A third set adds the output
+normalisation (a weight per value channel and eps) to random ragged
+batches with short and empty sequences, against oracle.rms_norm of the
+oracle's output, whichever form the call takes (in-wave, exchanged between
+row slices, or the pass after the scan)."""
 
 import numpy as np
 import pytest
+import torch
 
 import gdn_synth as gs
+import gated_deltanet_linear_02_amd as gdn
+import oracle
 from gpu_util import note, oracle_ref, rel_err, requires_gpu, run_prefill, to_f64, tol
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -81,3 +88,39 @@ def test_random_wide_batch(seed):
     eo, ef = rel_err(to_f64(o), o_ref), rel_err(to_f64(f), f_ref)
     print(f"[parity] random wide {desc} out_err={eo:.3e} state_err={ef:.3e}", flush=True)
     assert eo <= tol("bf16") and ef <= tol("bf16"), desc
+
+
+def _norm_case(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 5))
+    lens = [int(x) for x in rng.integers(0, 300, n)]
+    for i in range(n):  # short sequences: one partial chunk, done in a few steps
+        if rng.random() < 0.35:
+            lens[i] = int(rng.integers(0, 9))
+    hk, hv = [(16, 32), (8, 16), (4, 8), (2, 4), (1, 2)][int(rng.integers(0, 5))]
+    d = int(rng.choice([16, 32, 64, 128]))
+    io = "bf16" if rng.random() < 0.75 else "f32"
+    chunk = int(rng.choice([0, 0, 1, 16, 32, 64]))
+    eps = float(rng.choice([1e-6, 1e-3, 0.05]))
+    init = bool(rng.random() < 0.6)
+    inp = gs.make_inputs(lens, hk, hv, d, d, seed=seed, io_dtype=io, gate_dtype="f32", init_state=init)
+    w = gs.norm_weight(d, seed=seed + 1)
+    desc = f"seed={seed} lens={lens} hk={hk} hv={hv} d={d} io={io} chunk={chunk} eps={eps} init={init}"
+    return inp, chunk, w, eps, desc
+
+
+@pytest.mark.parametrize("seed", range(9000, 9016))
+def test_random_normalised_configuration(seed):
+    inp, chunk, w, eps, desc = _norm_case(seed)
+    io_dtype = torch.bfloat16 if inp.io_dtype == "bf16" else torch.float32
+    plan = gdn.prefill_plan(inp.num_seqs, max(inp.total_tokens, 1), inp.hk, inp.hv, inp.dk, chunk, io_dtype)
+    note(f"norm {desc} plan={plan}")
+    o, f = run_prefill(inp, chunk=chunk, norm_weight=torch.from_numpy(w).cuda(), norm_eps=eps)
+    o_ref, f_ref = oracle_ref(inp)
+    y_ref = oracle.rms_norm(o_ref, w, eps)
+    og, fg = to_f64(o), to_f64(f)
+    assert np.isfinite(og).all() and np.isfinite(fg).all(), desc
+    eo = rel_err(og, y_ref) if og.size else 0.0
+    ef = rel_err(fg, f_ref)
+    print(f"[parity] random norm {desc} out_err={eo:.3e} state_err={ef:.3e}", flush=True)
+    assert eo <= tol(inp.io_dtype) and ef <= tol(inp.io_dtype), desc
