@@ -9,7 +9,10 @@ large enough that the chunked scan takes 32 state rows per workgroup
 normalisation (a weight per value channel and eps) to random ragged
 batches with short and empty sequences, against oracle.rms_norm of the
 oracle's output, whichever form the call takes (in-wave, exchanged between
-row slices, or the pass after the scan)."""
+row slices, or the pass after the scan). A fourth draws decode steps: batch, head
+layout and size, I/O and gate dtypes, scale, state slots (permuted, some
+skipped with -1), the fused normalisation, and fp32 or (with bf16 I/O) bf16
+state storage; skipped slots must keep their bits and give rows of zeros."""
 
 import numpy as np
 import pytest
@@ -18,7 +21,7 @@ import torch
 import gdn_synth as gs
 import gated_deltanet_linear_02_amd as gdn
 import oracle
-from gpu_util import note, oracle_ref, rel_err, requires_gpu, run_prefill, to_f64, tol
+from gpu_util import TOL_BF16, TOL_F32, device_inputs, note, oracle_ref, rel_err, requires_gpu, run_prefill, to_f64, tol
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -124,3 +127,59 @@ def test_random_normalised_configuration(seed):
     ef = rel_err(fg, f_ref)
     print(f"[parity] random norm {desc} out_err={eo:.3e} state_err={ef:.3e}", flush=True)
     assert eo <= tol(inp.io_dtype) and ef <= tol(inp.io_dtype), desc
+
+
+def _decode_case(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 65))
+    hk, hv = LAYOUTS[int(rng.integers(0, len(LAYOUTS)))]
+    d = int(rng.choice([16, 32, 64, 128]))
+    io = "bf16" if rng.random() < 0.6 else "f32"
+    gate = "bf16" if (io == "bf16" and rng.random() < 0.6) else "f32"
+    state_bf16 = bool(io == "bf16" and rng.random() < 0.4)  # bf16 storage is built for bf16 I/O only
+    norm = bool(rng.random() < 0.4)
+    eps = float(rng.choice([1e-6, 0.05]))
+    scale = float(rng.choice([1.0, 1.0 / np.sqrt(d)]))
+    inp = gs.make_inputs([1] * B, hk, hv, d, d, seed=seed, io_dtype=io, gate_dtype=gate)
+    pool_n = B + int(rng.integers(0, 5))
+    pool = gs.decode_state(pool_n, hv, d, d, seed=seed + 1)
+    if state_bf16:
+        pool = oracle.round_to_bf16(pool).astype(np.float32)
+    slots = None
+    if rng.random() < 0.5:
+        slots = rng.permutation(pool_n)[:B].astype(np.int32)
+        slots[rng.random(B) < 0.15] = -1
+    w = gs.norm_weight(d, seed=seed + 2) if norm else None
+    desc = (f"seed={seed} B={B} hk={hk} hv={hv} d={d} io={io} gate={gate} state={'bf16' if state_bf16 else 'f32'} "
+            f"norm={norm} eps={eps} scale={scale:.3f} slots={'yes' if slots is not None else 'no'}")
+    return inp, pool, slots, state_bf16, w, eps, scale, desc
+
+
+@pytest.mark.parametrize("seed", range(9500, 9516))
+def test_random_decode_step(seed):
+    inp, pool, slots, state_bf16, w, eps, scale, desc = _decode_case(seed)
+    note(f"decode {desc}")
+    d = device_inputs(inp)
+    pool_t = torch.from_numpy(pool).cuda()
+    state = pool_t.to(torch.bfloat16) if state_bf16 else pool_t.clone()
+    out = gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, scale=scale,
+                          state_slots=None if slots is None else torch.from_numpy(slots).cuda(),
+                          norm_weight=None if w is None else torch.from_numpy(w).cuda(), norm_eps=eps)
+    torch.cuda.synchronize()
+    wd = inp.widened()
+    idx = np.arange(inp.num_seqs) if slots is None else np.maximum(slots, 0)
+    o_ref, s_ref = oracle.decode_step(wd["q"], wd["k"], wd["v"], wd["g"], wd["beta"],
+                                      pool[idx].astype(np.float64), scale=scale)
+    if w is not None:
+        o_ref = oracle.rms_norm(o_ref, w, eps)
+    o, got = to_f64(out), to_f64(state)
+    live = np.ones(inp.num_seqs, bool) if slots is None else slots >= 0
+    assert np.isfinite(o).all() and np.isfinite(got).all(), desc
+    assert np.all(o[~live] == 0), desc
+    eo = rel_err(o[live], o_ref[live]) if live.any() else 0.0
+    s_bar = TOL_BF16 if state_bf16 else TOL_F32
+    es = rel_err(got[idx[live]], s_ref[live]) if live.any() else 0.0
+    untouched = sorted(set(range(pool.shape[0])) - set(int(x) for x in idx[live]))
+    print(f"[parity] random decode {desc} out_err={eo:.3e} state_err={es:.3e}", flush=True)
+    assert eo <= tol(inp.io_dtype) and es <= s_bar, desc
+    assert np.array_equal(got[untouched], pool[untouched].astype(np.float64)), desc
