@@ -82,6 +82,12 @@ def load():
         L.gdn_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32]
         L.gdn_prefill_method.restype = i32
         L.gdn_prefill_method.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32)]
+        L.gdn_prefill_method_hint.restype = i32
+        L.gdn_prefill_method_hint.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, i32, i32,
+                                              ctypes.POINTER(i32)]
+        L.gdn_prefill_hint.restype = i32
+        L.gdn_prefill_hint.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, i32,
+                                       f32, i32, i32, vp, vp, i32, vp, f32, vp, vp, sz, vp]
         L.gdn_prefill.restype = i32
         L.gdn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32,
                                   f32, i32, i32, vp, vp, vp, vp, sz, vp]
@@ -183,14 +189,16 @@ def prefill_workspace_size(num_seqs: int, total_tokens: int, hk: int, hv: int, d
 
 
 def prefill_plan(num_seqs: int, total_tokens: int, hk: int, hv: int, d: int, chunk: int = 0,
-                 io_dtype: torch.dtype = torch.bfloat16, gate_dtype: torch.dtype = torch.float32) -> Tuple[int, int]:
-    """The method ``prefill`` uses for these sizes (``gdn_prefill_method``):
-    (chunk, rows) with chunk 1 (token by token), 16, 32 or 64 and rows the
-    chunked scan's state rows per workgroup (16, 32, 64 or 128; 0 token by token);
-    (0, 0) if the sizes are rejected."""
+                 io_dtype: torch.dtype = torch.bfloat16, gate_dtype: torch.dtype = torch.float32,
+                 max_seqlen: Optional[int] = None) -> Tuple[int, int]:
+    """The method ``prefill`` uses for these sizes (``gdn_prefill_method``,
+    or ``gdn_prefill_method_hint`` with ``max_seqlen``, the longest
+    sequence's length): (chunk, rows) with chunk 1 (token by token), 16, 32
+    or 64 and rows the chunked scan's state rows per workgroup (16, 32, 64 or
+    128; 0 token by token); (0, 0) if the sizes are rejected."""
     rows = ctypes.c_int32(0)
-    c = load().gdn_prefill_method(num_seqs, total_tokens, hk, hv, d, d, chunk, _dtype_code(io_dtype),
-                                  _dtype_code(gate_dtype), ctypes.byref(rows))
+    c = load().gdn_prefill_method_hint(num_seqs, total_tokens, int(max_seqlen or 0), hk, hv, d, d, chunk,
+                                       _dtype_code(io_dtype), _dtype_code(gate_dtype), ctypes.byref(rows))
     return int(c), int(rows.value)
 
 
@@ -207,7 +215,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
             write_final_state: bool = True, norm_weight: Optional[torch.Tensor] = None,
             norm_eps: float = 1e-6, state_dtype: Optional[torch.dtype] = None,
-            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            max_seqlen: Optional[int] = None, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Prefill over packed sequences (``gdn_prefill``).
 
     q, k [T, hk, dk]; v [T, hv, dv] (bf16 or fp32, one dtype); g, beta [T, hv]
@@ -220,6 +228,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     y = o * w / sqrt(mean(o^2) + norm_eps).
     States are fp32 or bf16 (``gdn_prefill_ex``): the dtype of the state
     tensors given, else ``state_dtype`` (default fp32).
+    ``max_seqlen`` (host int, or None): the longest sequence's length, a hint
+    for the method rule on uneven batches (``gdn_prefill_hint``).
     Missing out / final_state / workspace are allocated with torch.
     """
     T, hk, dk = q.shape
@@ -253,7 +263,15 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     _on_device(dev, k=k, v=v, g=g, beta=beta, cu_seqlens=cu_seqlens, initial_state=initial_state,
                final_state=final_state, out=out, workspace=workspace, norm_weight=norm_weight)
     ws_bytes = workspace.numel() * workspace.element_size()
-    if norm_weight is None and sdt == torch.float32:
+    if max_seqlen is not None:
+        if norm_weight is not None:
+            _check_norm_weight(norm_weight, dv)
+        status = load().gdn_prefill_hint(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, int(max_seqlen),
+            hk, hv, dk, dv, chunk, float(scale), io, gate,
+            _ptr(initial_state), _ptr(final_state), _dtype_code(sdt), _ptr(norm_weight), float(norm_eps),
+            _ptr(out), _ptr(workspace), ws_bytes, _stream(dev, stream))
+    elif norm_weight is None and sdt == torch.float32:
         status = load().gdn_prefill(
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
             hk, hv, dk, dv, chunk, float(scale), io, gate,

@@ -119,35 +119,38 @@ static bool method_fits(int32_t c, int32_t num_seqs, int64_t total_tokens, int32
 
 static int32_t check_prefill_shape(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
                                    int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype,
-                                   int32_t gate_dtype) {
+                                   int32_t gate_dtype, int64_t max_seqlen = 0) {
     if (num_seqs < 1 || total_tokens < 0 || total_tokens > INT32_MAX || hk < 1 || hv < 1 || hv % hk != 0)
         return GDN_ERR_BAD_SHAPE;
     if (!valid_head(dk) || dv != dk || !valid_chunk(chunk) || !valid_dtype(io_dtype) ||
         !valid_dtype(gate_dtype) || hk > 65535)
         return GDN_ERR_UNSUPPORTED;
-    const int32_t c = chunk != 0 ? chunk : rule_chunk(num_seqs, total_tokens, hv, dv, io_dtype == GDN_BF16);
+    const int32_t c =
+        chunk != 0 ? chunk : rule_chunk(num_seqs, total_tokens, hv, dv, io_dtype == GDN_BF16, max_seqlen);
     return method_fits(c, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype) ? GDN_OK : GDN_ERR_UNSUPPORTED;
 }
 
 // The method a call uses: the chunk asked for, or for chunk 0 the choice
 // cached by gdn_tune_prefill for this device and shape, else the rule; and
 // for a chunked method the scan's state rows per workgroup: `rows` when it is
-// given and fits, the tuned rows for chunk 0, else the rule's.
+// given and fits, the tuned rows for chunk 0, else the rule's (which a
+// max_seqlen hint, if given, informs).
 static Method method_for(int32_t chunk, int32_t rows, int32_t num_seqs, int64_t total_tokens, int32_t hk,
-                         int32_t hv, int32_t dk, int32_t dv, int32_t io_dtype, int32_t gate_dtype) {
+                         int32_t hv, int32_t dk, int32_t dv, int32_t io_dtype, int32_t gate_dtype,
+                         int64_t max_seqlen = 0) {
     Method m;
     m.chunk = chunk;
     m.rows = rows;
     if (chunk == 0) {
         m = tuned_method(num_seqs, total_tokens, hk, hv, dk, io_dtype, gate_dtype);
         if (m.chunk == 0 || !method_fits(m.chunk, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype)) {
-            m.chunk = rule_chunk(num_seqs, total_tokens, hv, dv, io_dtype == GDN_BF16);
+            m.chunk = rule_chunk(num_seqs, total_tokens, hv, dv, io_dtype == GDN_BF16, max_seqlen);
             m.rows = 0;
         }
     }
     const bool bf = io_dtype == GDN_BF16;
     if (m.chunk == 1) m.rows = 0;
-    else if (!slice_rows_fit(m.rows, dv, bf)) m.rows = scan_slice_rows(num_seqs, hv, dv, bf);
+    else if (!slice_rows_fit(m.rows, dv, bf)) m.rows = scan_slice_rows(num_seqs, hv, dv, bf, total_tokens, max_seqlen);
     return m;
 }
 
@@ -171,12 +174,29 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_
     return prefill_workspace_bytes(num_seqs, total_tokens, hk, hv, dk, chunk, io_dtype);
 }
 
+// A max_seqlen hint: 0 (none), or the longest sequence's length, which
+// lies between the mean length and the total.
+static bool valid_max_seqlen(int64_t max_seqlen, int32_t num_seqs, int64_t total_tokens) {
+    return max_seqlen == 0 ||
+           (max_seqlen > 0 && max_seqlen <= total_tokens && max_seqlen * (int64_t)num_seqs >= total_tokens);
+}
+
 int32_t gdn_prefill_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv, int32_t dk,
                            int32_t dv, int32_t chunk, int32_t io_dtype, int32_t gate_dtype, int32_t *slice_rows) {
+    return gdn_prefill_method_hint(num_seqs, total_tokens, 0, hk, hv, dk, dv, chunk, io_dtype, gate_dtype,
+                                   slice_rows);
+}
+
+int32_t gdn_prefill_method_hint(int32_t num_seqs, int64_t total_tokens, int64_t max_seqlen, int32_t hk,
+                                int32_t hv, int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype,
+                                int32_t gate_dtype, int32_t *slice_rows) {
     if (slice_rows) *slice_rows = 0;
-    if (check_prefill_shape(num_seqs, total_tokens, hk, hv, dk, dv, chunk, io_dtype, gate_dtype) != GDN_OK)
+    if (check_prefill_shape(num_seqs, total_tokens, hk, hv, dk, dv, chunk, io_dtype, gate_dtype, max_seqlen) !=
+            GDN_OK ||
+        !valid_max_seqlen(max_seqlen, num_seqs, total_tokens))
         return 0;
-    const Method m = method_for(chunk, 0, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype, gate_dtype);
+    const Method m =
+        method_for(chunk, 0, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype, gate_dtype, max_seqlen);
     if (slice_rows) *slice_rows = m.rows;
     return m.chunk;
 }
@@ -201,9 +221,12 @@ static int32_t prefill_impl(const void *q, const void *k, const void *v, const v
                             float scale, int32_t io_dtype, int32_t gate_dtype,
                             const void *initial_state, void *final_state, int32_t state_dtype,
                             const float *norm_w, float norm_eps, void *out,
-                            void *workspace, size_t workspace_bytes, void *stream, int32_t rows = 0) {
-    const int32_t sc = check_prefill_shape(num_seqs, total_tokens, hk, hv, dk, dv, chunk, io_dtype, gate_dtype);
+                            void *workspace, size_t workspace_bytes, void *stream, int32_t rows = 0,
+                            int64_t max_seqlen = 0) {
+    const int32_t sc =
+        check_prefill_shape(num_seqs, total_tokens, hk, hv, dk, dv, chunk, io_dtype, gate_dtype, max_seqlen);
     if (sc != GDN_OK) return sc;
+    if (!valid_max_seqlen(max_seqlen, num_seqs, total_tokens)) return GDN_ERR_BAD_VALUE;
     const int32_t so = check_options(io_dtype, state_dtype, norm_w, norm_eps);
     if (so != GDN_OK) return so;
     if (!cu_seqlens) return GDN_ERR_NULL_ARG;
@@ -213,7 +236,8 @@ static int32_t prefill_impl(const void *q, const void *k, const void *v, const v
         return GDN_ERR_MISALIGNED;
 
     const size_t eb = dtype_bytes(io_dtype), gb = dtype_bytes(gate_dtype);
-    const Method m = method_for(chunk, rows, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype, gate_dtype);
+    const Method m =
+        method_for(chunk, rows, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype, gate_dtype, max_seqlen);
     const int32_t c = m.chunk;
     // The token scan uses no workspace: its buffer is not checked or touched.
     const PrefillLayout L = c == 1 ? PrefillLayout{} : prefill_layout(num_seqs, total_tokens, hk, hv, dk, c, eb);
@@ -304,6 +328,18 @@ int32_t gdn_prefill_ex(const void *q, const void *k, const void *v, const void *
     return prefill_impl(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, hk, hv, dk, dv, chunk, scale,
                         io_dtype, gate_dtype, initial_state, final_state, state_dtype, norm_weight, norm_eps, out,
                         workspace, workspace_bytes, stream);
+}
+
+int32_t gdn_prefill_hint(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                         const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens, int64_t max_seqlen,
+                         int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
+                         float scale, int32_t io_dtype, int32_t gate_dtype,
+                         const void *initial_state, void *final_state, int32_t state_dtype,
+                         const float *norm_weight, float norm_eps, void *out,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_impl(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, hk, hv, dk, dv, chunk, scale,
+                        io_dtype, gate_dtype, initial_state, final_state, state_dtype, norm_weight, norm_eps, out,
+                        workspace, workspace_bytes, stream, 0, max_seqlen);
 }
 
 }  // extern "C"

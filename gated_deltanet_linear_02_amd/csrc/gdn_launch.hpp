@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace gdn {
 
 enum KernelKind {
@@ -227,26 +229,75 @@ inline bool slice_rows_fit(int32_t rows, int64_t dv, bool io_bf16) {
 // prefill, us, 16 / 32 / 64 / 128 rows): 1 x 4096: 87.5 / 100.8 / 141 / 232;
 // 2 x 2048: 89.7 / 76.8 / 89.9 / 133; 4 x 1024: 95.1 / 76.7 / 66.8 / 84.9;
 // 8 x 512: 109 / 81.6 / 70.4 / 66.9; 32 x 128: 186 / 128 / 105 / 92.9.
-inline int32_t scan_slice_rows(int64_t num_seqs, int64_t hv, int64_t dv, bool io_bf16) {
+//
+// A caller that knows the longest sequence's length on the host may pass it
+// (max_seqlen > 0). When the lengths are far from even (the longest above
+// 1.25 times the mean), the rows are those that minimise an estimate of the
+// scan's time instead: the chunk-step cost of the width times the larger of
+// the longest sequence's chain and the batch's work spread over the CUs,
+// both counted in tokens with a fixed cost of two 64-token chunk steps per
+// workgroup (its state load and store and its launch). Longest sequences
+// are scheduled first, so shorter ones fill the CUs beside the longest
+// chain, and a narrower slice with a faster step can finish sooner over
+// several passes than the one-pass width. Step costs relative to 16 rows,
+// fitted to whole-prefill times of twelve uneven batches at HK = 16,
+// HV = 32, d = 128, chunk 64, less the preparation: 1, 1.4, 1.9 and 2.9 for
+// 16, 32, 64 and 128 rows. The estimate picks the fastest width on eleven of
+// them and one within 4% on the last (16 against 32 rows for 16384 + 3 x
+// 2048 tokens); the one-pass rule loses 1.1 to 2.1 times on all but the
+// even control (4096 + 4 x 512: 259 against 147 us; 8 sequences of 1,541 to
+// 14,620 tokens: 1.35 against 1.10 ms). On even batches both agree.
+inline double scan_step_cost(int32_t rows) {
+    return rows == 16 ? 1.0 : rows == 32 ? 1.4 : rows == 64 ? 1.9 : 2.9;
+}
+// Whether a max_seqlen hint marks the batch as uneven: several sequences,
+// the longest above 1.25 times the mean.
+inline bool uneven(int64_t num_seqs, int64_t total_tokens, int64_t max_seqlen) {
+    return max_seqlen > 0 && num_seqs > 1 && (double)max_seqlen * (double)num_seqs > 1.25 * (double)total_tokens;
+}
+inline int32_t scan_slice_rows(int64_t num_seqs, int64_t hv, int64_t dv, bool io_bf16, int64_t total_tokens = 0,
+                               int64_t max_seqlen = 0) {
+    if (uneven(num_seqs, total_tokens, max_seqlen)) {
+        constexpr double kFixedTokens = 128.0;
+        const double chain = (double)max_seqlen + kFixedTokens;
+        const double work = (double)total_tokens + kFixedTokens * (double)num_seqs;
+        int32_t best = 16;
+        double best_t = 0.0;
+        for (int32_t rows = 16; rows <= 128; rows *= 2) {
+            if (!slice_rows_fit(rows, dv, io_bf16)) continue;
+            const double spread = (double)hv * (double)(dv / rows) * work / (double)kScanOnePassWgs;
+            const double t = scan_step_cost(rows) * std::max(chain, spread);
+            if (rows == 16 || t < best_t) {
+                best = rows;
+                best_t = t;
+            }
+        }
+        return best;
+    }
     int32_t rows = 16;
     while (slice_rows_fit(rows * 2, dv, io_bf16) && num_seqs * hv * (dv / rows) > kScanOnePassWgs) rows *= 2;
     return rows;
 }
 
-inline int32_t rule_chunk(int64_t num_seqs, int64_t total_tokens, int64_t hv, int64_t dv, bool io_bf16) {
+inline int32_t rule_chunk(int64_t num_seqs, int64_t total_tokens, int64_t hv, int64_t dv, bool io_bf16,
+                          int64_t max_seqlen = 0) {
     if (total_tokens <= kTokenScanTokens || total_tokens <= kTokenScanPerSeq * num_seqs) return 1;
     if (!io_bf16) {
         if (total_tokens <= kF32TokenScanPerSeq * num_seqs) return 1;
         const bool one_pass = num_seqs * hv * (dv / 16) <= kScanOnePassWgs;
         return one_pass && total_tokens <= kF32Chunk32PerSeq * num_seqs ? 32 : 64;
     }
-    const int64_t rows = scan_slice_rows(num_seqs, hv, dv, io_bf16);
+    const int64_t rows = scan_slice_rows(num_seqs, hv, dv, io_bf16, total_tokens, max_seqlen);
     if (rows >= 64) return total_tokens <= 16 * num_seqs ? 16 : total_tokens <= 32 * num_seqs ? 32 : 64;
     if (total_tokens <= kChunk16PerSeq * num_seqs) return 16;
     // one pass with the slice rows the scan will take (2 x 600: 32-row
     // slices fill the 256 CUs once, and chunks of 32 measure 38.5 against
     // 41 us)
     if (num_seqs * hv * (dv / rows) <= kScanOnePassWgs && total_tokens <= kChunk32PerSeq * num_seqs) return 32;
+    // an uneven batch under the hint is bound by its longest chain as a
+    // lone sequence is (300 + 77 + 5 tokens: 24.4 us with chunks of 32
+    // against 28.3 with 64)
+    if (uneven(num_seqs, total_tokens, max_seqlen) && max_seqlen <= kChunk32PerSeq) return 32;
     return 64;
 }
 

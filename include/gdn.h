@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum {
     GDN_OK = 0,
@@ -99,6 +99,23 @@ size_t gdn_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
 int32_t gdn_prefill_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv,
                            int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype,
                            int32_t gate_dtype, int32_t *slice_rows);
+
+/*
+ * gdn_prefill_method with a host-side hint: max_seqlen, the length of the
+ * batch's longest sequence when the caller knows it without reading
+ * cu_seqlens back (as varlen attention kernels take it), or 0 for none. A
+ * hint must lie between the mean length and total_tokens (else the call
+ * returns 0). When the longest sequence is above 1.25 times the mean, the
+ * state rows per scan workgroup are those that minimise an estimate of the
+ * scan's time, the larger of the longest sequence's chain and the batch's
+ * work spread over the CUs, each weighted by the chunk-step cost of the
+ * width; otherwise, and without a hint, the rule of gdn_prefill_method.
+ * Uneven batches gain most (a 4,096-token prompt beside four of 512: 32
+ * rows, 147 us, against 259 us with the one-pass rule's 128 rows).
+ */
+int32_t gdn_prefill_method_hint(int32_t num_seqs, int64_t total_tokens, int64_t max_seqlen,
+                                int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
+                                int32_t io_dtype, int32_t gate_dtype, int32_t *slice_rows);
 
 /*
  * Chunked prefill over N packed variable-length sequences.
@@ -284,6 +301,25 @@ int32_t gdn_prefill_ex(const void *q, const void *k, const void *v,
                        const void *initial_state, void *final_state, int32_t state_dtype,
                        const float *norm_weight, float norm_eps, void *out,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_prefill_ex with the max_seqlen hint of gdn_prefill_method_hint (0 for
+ * none), which steers the method that chunk 0 and the scan's state rows
+ * take; the hint is never checked against cu_seqlens, and a wrong one only
+ * costs time. The state rows do not change a result's bits; where the hint
+ * also changes the chunk size, results differ by rounding, as between
+ * chunk sizes. Errors: as gdn_prefill_ex, plus GDN_ERR_BAD_VALUE for a hint
+ * below the mean length or above total_tokens.
+ */
+int32_t gdn_prefill_hint(const void *q, const void *k, const void *v,
+                         const void *g, const void *beta,
+                         const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                         int64_t max_seqlen,
+                         int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,
+                         float scale, int32_t io_dtype, int32_t gate_dtype,
+                         const void *initial_state, void *final_state, int32_t state_dtype,
+                         const float *norm_weight, float norm_eps, void *out,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 int32_t gdn_decode_step_ex(const void *q, const void *k, const void *v,
                            const void *g, const void *beta,

@@ -45,7 +45,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert gdn.abi_version() == 4
+    assert gdn.abi_version() == 5
     for s in range(9):
         assert lib.gdn_status_string(s)
     assert b"unknown" in lib.gdn_status_string(99)
@@ -237,6 +237,51 @@ def test_ex_argument_checks(lib):
     assert _prefill_ex(lib, sf=NORM_W - 64) == ALIAS
     assert _prefill_ex(lib, ws=None) == WORKSPACE
     assert _decode_ex(lib, B=0) == OK
+
+
+def _prefill_hint(lib, hint, w=NORM_W, **kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30),
+             beta=FAKE + (4 << 30), cu=FAKE + (5 << 30), n=3, T=382, hk=2, hv=4, dk=64, dv=64,
+             chunk=0, scale=1.0, io=BF16, gate=F32, s0=None, sf=None, out=FAKE + (6 << 30),
+             ws=FAKE + (7 << 30), ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.gdn_prefill_hint(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["n"], a["T"], hint,
+                                a["hk"], a["hv"], a["dk"], a["dv"], a["chunk"], a["scale"], a["io"],
+                                a["gate"], a["s0"], a["sf"], F32, w, 1e-6, a["out"], a["ws"], a["ws_bytes"],
+                                a["stream"])
+
+
+@no_gpu
+def test_prefill_hint_argument_checks(lib):
+    """A max_seqlen hint lies between the mean length and the total; the
+    other checks are those of gdn_prefill_ex, made before the hint's."""
+    assert _prefill_hint(lib, 127) == BAD_VALUE   # below the mean of 382 / 3
+    assert _prefill_hint(lib, 383) == BAD_VALUE   # above the total
+    assert _prefill_hint(lib, -1) == BAD_VALUE
+    assert _prefill_hint(lib, 300, hk=3) == BAD_SHAPE
+    assert _prefill_hint(lib, 300, w=FAKE + (6 << 30) + 64) == ALIAS
+    assert _prefill_hint(lib, 300, ws=None) == WORKSPACE
+    assert _prefill_hint(lib, 0, ws=None) == WORKSPACE
+
+
+def test_max_seqlen_hint_plans():
+    """With the longest length as a hint, uneven batches take the state rows
+    (and for short ones the chunk) that the tuner measures fastest; even
+    batches, or a hint within 1.25 times the mean, keep the rule's method."""
+    def p(lens, **kw):
+        return gdn.prefill_plan(len(lens), sum(lens), 16, 32, 128, **kw)
+    varlen = [1541, 2796, 5227, 7117, 8976, 10781, 12892, 14620]
+    assert p(varlen) == (64, 128) and p(varlen, max_seqlen=14620) == (64, 64)
+    assert p([4096] + [512] * 4) == (64, 128) and p([4096] + [512] * 4, max_seqlen=4096) == (64, 32)
+    assert p([8192, 1024, 1024], max_seqlen=8192) == (64, 16)
+    assert p([2048, 1024, 512, 256], max_seqlen=2048) == (64, 32)
+    assert p([300, 77, 5], max_seqlen=300) == (32, 32)
+    for lens in ([1024] * 8, [512] * 8, [2048] * 2, [200] * 3, [4096], [600, 500, 400], [128] * 32):
+        assert p(lens, max_seqlen=max(lens)) == p(lens), lens
+    # fp32 I/O: 16-row slices whatever the hint
+    assert p(varlen, io_dtype=torch.float32, max_seqlen=14620) == (64, 16)
+    # hints outside [mean, total] are refused
+    assert p([300, 77, 5], max_seqlen=100) == (0, 0) and p([300, 77, 5], max_seqlen=383) == (0, 0)
 
 
 def test_tune_cache_file_round_trip(tmp_path):

@@ -15,7 +15,7 @@ import torch
 
 import gdn_synth as gs
 import gated_deltanet_linear_02_amd as gdn
-from gpu_util import TOL_BF16, device_inputs, note, oracle_ref, rel_err, requires_gpu, to_f64
+from gpu_util import TOL_BF16, device_inputs, note, oracle_ref, rel_err, requires_gpu, run_prefill, to_f64
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -134,3 +134,27 @@ def test_wide_slices_head_groups(hk, hv, d, rows):
     print(f"[parity] wide slices hk={hk} hv={hv} d={d} rows={rows} N={n} out_err={eo:.3e} state_err={ef:.3e}",
           flush=True)
     assert eo <= TOL_BF16 and ef <= TOL_BF16
+
+
+def test_max_seqlen_hint_changes_rows_not_results():
+    """An uneven batch (one 2,048-token prompt beside four of 256): the
+    one-pass rule takes 128-row slices; with the longest length as a hint
+    the rule takes 32-row slices, which finish sooner. Same chunk size, so
+    outputs and final states are bit for bit those of the call without the
+    hint, and both meet the oracle's bar. A hint below the mean length or
+    above the total is refused."""
+    lens = [2048, 256, 256, 256, 256]
+    N, T = len(lens), sum(lens)
+    assert gdn.prefill_plan(N, T, 16, 32, 128) == (64, 128)
+    assert gdn.prefill_plan(N, T, 16, 32, 128, max_seqlen=2048) == (64, 32)
+    inp = gs.make_inputs(lens, 16, 32, 128, 128, seed=gs.SEED_BASE + 1700, io_dtype="bf16", gate_dtype="f32",
+                         init_state=True)
+    note("prefill max_seqlen hint 2048 + 4 x 256")
+    o0, f0 = run_prefill(inp, chunk=0)
+    o1, f1 = run_prefill(inp, chunk=0, max_seqlen=2048)
+    assert torch.equal(o0, o1) and torch.equal(f0, f1)
+    o_ref, f_ref = oracle_ref(inp)
+    assert rel_err(to_f64(o1), o_ref) <= TOL_BF16 and rel_err(to_f64(f1), f_ref) <= TOL_BF16
+    for bad in (T // N - 1, T + 1):
+        with pytest.raises(gdn.GdnError):
+            run_prefill(inp, chunk=0, max_seqlen=bad)
