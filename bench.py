@@ -692,11 +692,10 @@ def summarize_tune(stats_dir: str, results_jsonl: str):
               "| sequences x tokens | rule | rule us | tuned | tuned us | speedup | tuner's warm us per method "
               "| rule's candidate / fastest |",
               "|---|---|---|---|---|---|---|---|"]
-    for line in open(results_jsonl):
-        line = line.strip()
-        if not line.startswith("{"):
+    results = [json.loads(x) for x in (y.strip() for y in open(results_jsonl)) if x.startswith("{")]
+    for d in results:
+        if d.get("lengths"):
             continue
-        d = json.loads(line)
         cand = d["candidate_ms_warm"]
         warm = ", ".join(f"{c}: {t * 1e3:.1f}" if t >= 0 else f"{c}: -" for c, t in cand.items())
         best = min(t for t in cand.values() if t >= 0)
@@ -704,6 +703,23 @@ def summarize_tune(stats_dir: str, results_jsonl: str):
         lines.append(f"| {d['num_seqs']} x {d['tokens_per_seq']} | {d['rule_method']} | {d['rule_ms'] * 1e3:.1f} | "
                      f"{d['tuned_method']} | {d['tuned_ms'] * 1e3:.1f} | {d['speedup']:.2f} | {warm} | "
                      f"{ratio:.2f} |")
+    uneven = [d for d in results if d.get("lengths")]
+    if uneven:
+        lines += ["", "## Uneven batches: the rule with and without the max_seqlen hint", "",
+                  "The same protocol, on batches of unequal sequences. The hinted method is the rule's choice "
+                  "when the caller passes the longest length (gdn_prefill_hint); without it the rule sees only "
+                  "the sizes.", "",
+                  "| lengths | rule | rule us | hinted | hinted us | rule / hinted | tuned | tuned us | "
+                  "hinted's candidate / fastest |",
+                  "|---|---|---|---|---|---|---|---|---|"]
+        for d in uneven:
+            cand = d["candidate_ms_warm"]
+            best = min(t for t in cand.values() if t >= 0)
+            hc = cand.get(d["hinted_method"], -1)
+            ratio = hc / best if hc > 0 else float("nan")
+            lines.append(f"| {'+'.join(map(str, d['lengths']))} | {d['rule_method']} | {d['rule_ms'] * 1e3:.1f} | "
+                         f"{d['hinted_method']} | {d['hinted_ms'] * 1e3:.1f} | {d['rule_ms'] / d['hinted_ms']:.2f} | "
+                         f"{d['tuned_method']} | {d['tuned_ms'] * 1e3:.1f} | {ratio:.2f} |")
     with open(os.path.join(ROOT, "profiles", "gdn_prefill_tuning.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -802,11 +818,14 @@ def summarize_configs(stats_dir: str, results_jsonl: str):
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     lines += ["", "## Per workload (HIP events in the same run, under the profiler)", "",
               "Methods are named chunk/rows (chunk size, state rows per scan workgroup). The first is chunk "
-              "64 with the rule's rows, which the kernel columns describe; the tuned method is the one "
-              "gdn_tune_prefill picks for the workload (the host-side rule sees sizes, not the lengths).", "",
+              "64 with the rule's rows, which the kernel columns describe. The hinted method is the rule's "
+              "choice when the caller passes the longest length (max_seqlen, gdn_prefill_hint); the tuned "
+              "method is the one gdn_tune_prefill picks for the workload (the host-side rule sees sizes, "
+              "not the lengths).", "",
               "| workload | sequences | tokens | method | prefill ms | tokens/s | prep ms | scan ms | scan MFMA | "
-              "tuned method | tuned prefill ms | tuned tokens/s | decode b8 step us |",
-              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+              "hinted method | hinted prefill ms | tuned method | tuned prefill ms | tuned tokens/s | "
+              "decode b8 step us |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for line in open(results_jsonl):
         line = line.strip()
         if not line.startswith("{"):
@@ -816,7 +835,8 @@ def summarize_configs(stats_dir: str, results_jsonl: str):
         dec = f"{d['decode_b8_step_ms'] * 1e3:.1f}" if "decode_b8_step_ms" in d else "-"
         lines.append(f"| {d['workload']} | {d['num_seqs']} | {d['total_tokens']} | {d['method']} | "
                      f"{d['prefill_ms']:.3f} | {d['tokens_per_s'] / 1e6:.1f} M | {km['prep']:.3f} | "
-                     f"{km['scan']:.3f} | {100 * d['scan_mfma_frac']:.1f}% | {d['tuned_method']} | "
+                     f"{km['scan']:.3f} | {100 * d['scan_mfma_frac']:.1f}% | {d['hinted_method']} | "
+                     f"{d['hinted_prefill_ms']:.3f} | {d['tuned_method']} | "
                      f"{d['tuned_prefill_ms']:.3f} | {d['tuned_tokens_per_s'] / 1e6:.1f} M | {dec} |")
     with open(os.path.join(ROOT, "profiles", "gdn_long_varlen.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -988,7 +1008,8 @@ def configs_bench(dev, reps):
     state, and 8 packed sequences of 256 to 16384 tokens followed by 64
     decode steps at batch 8 from their final states. HK=16, HV=32, d=128,
     bf16 I/O, fp32 gates and states, chunk 64 with the state rows per scan
-    workgroup of the rule; then the method gdn_tune_prefill picks for the
+    workgroup of the rule; the rule given the longest length as a hint
+    (max_seqlen, chunk 0); then the method gdn_tune_prefill picks for the
     workload (chunk 0 after tuning). One JSON line each."""
     import torch
     import gdn_synth as gs
@@ -1012,12 +1033,13 @@ def configs_bench(dev, reps):
         s0 = torch.from_numpy(inp.initial_state).to(dev)
         fin = torch.empty_like(s0)
         out = torch.empty((T, HV, D), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(gdn.prefill_workspace_size(N, T, HK, HV, D, D, CHUNK, torch.bfloat16),
+        ws = torch.empty(gdn.prefill_workspace_size(N, T, HK, HV, D, D, 0, torch.bfloat16),
                          dtype=torch.uint8, device=dev)
+        lmax = int(np.diff(inp.cu_seqlens).max())
 
-        def run(chunk=CHUNK):
+        def run(chunk=CHUNK, hint=None):
             gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=chunk,
-                        initial_state=s0, final_state=fin, out=out, workspace=ws)
+                        initial_state=s0, final_state=fin, out=out, workspace=ws, max_seqlen=hint)
 
         gdn.tune_cache_clear()
         method = gdn.method_name(*gdn.prefill_plan(N, T, HK, HV, D, CHUNK))
@@ -1027,6 +1049,8 @@ def configs_bench(dev, reps):
             run()
         kt = gdn.timing_stop()
         scan_ms = kt["scan"]["mean_ms"]
+        hinted = gdn.method_name(*gdn.prefill_plan(N, T, HK, HV, D, 0, max_seqlen=lmax))
+        hinted_ms = timed(lambda: run(0, lmax), reps)
         tuned = gdn.tune_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], initial_state=s0)
         tuned_ms = timed(lambda: run(0), reps)
         gdn.tune_cache_clear()
@@ -1035,6 +1059,7 @@ def configs_bench(dev, reps):
                "prefill_ms": ms, "tokens_per_s": T / (ms * 1e-3),
                "kernel_ms": {k: kt[k]["mean_ms"] for k in ("schedule", "prep", "scan")},
                "scan_mfma_frac": scan_flops_per_token() * T / (scan_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+               "hinted_method": hinted, "hinted_prefill_ms": hinted_ms, "max_seqlen": lmax,
                "tuned_method": tuned["method"], "tuned_prefill_ms": tuned_ms,
                "tuned_tokens_per_s": T / (tuned_ms * 1e-3),
                "dtype": "bf16", "data": "synthetic",
@@ -1106,20 +1131,28 @@ def graph_bench(dev, steps):
 # Shapes for the tuning sweep: (sequences, tokens each).
 TUNE_SHAPES = ((1, 16), (1, 48), (1, 128), (1, 512), (8, 4), (64, 1), (64, 4), (64, 16), (16, 16), (32, 24),
                (32, 128), (8, 300), (2, 600), (8, 512), (4, 1024), (2, 2048), (1, 4096))
+# Uneven batches (token counts per sequence), where the rule's choice also
+# depends on the longest length when the caller gives it (max_seqlen).
+UNEVEN_SHAPES = ((4096, 512, 512, 512, 512), (8192, 1024, 1024), (2048, 2048, 128, 128, 128, 128),
+                 (3000,) + (100,) * 10, (6000, 3000, 1500, 750), (2048, 1024, 512, 256), (300, 77, 5),
+                 (1000, 100, 100, 100))
 
 
 def tuning_sweep(dev, copies, steps):
     """gdn_tune_prefill on each shape, then prefill with chunk 0 timed under
     the fixed rule (empty cache) and under the tuned choice, on rotated buffer
-    sets (cold caches). HK=16, HV=32, d=128, bf16, fp32 gates, nonzero initial
-    states; one JSON line per shape."""
+    sets (cold caches); uneven batches also under the rule given the longest
+    length (max_seqlen). HK=16, HV=32, d=128, bf16, fp32 gates, nonzero
+    initial states; one JSON line per shape."""
     import torch
     import gdn_synth as gs
     import gated_deltanet_linear_02_amd as gdn
-    for N, k in TUNE_SHAPES:
-        T = N * k
-        inp = gs.make_inputs([k] * N, HK, HV, D, D, seed=gs.SEED_BASE + 900 + T, io_dtype="bf16",
-                             gate_dtype="f32", init_state=True)
+    shapes = [[k] * N for N, k in TUNE_SHAPES] + [list(u) for u in UNEVEN_SHAPES]
+    for lens in shapes:
+        N, T, k = len(lens), sum(lens), lens[0]
+        uneven = len(set(lens)) > 1
+        inp = gs.make_inputs(lens, HK, HV, D, D, seed=gs.SEED_BASE + 900 + T + (N if uneven else 0),
+                             io_dtype="bf16", gate_dtype="f32", init_state=True)
         sets = []
         for _ in range(copies):
             d = device_inputs(inp, dev)
@@ -1130,18 +1163,19 @@ def tuning_sweep(dev, copies, steps):
                                   dtype=torch.uint8, device=dev)
             sets.append(d)
 
-        def run(d):
+        def run(d, hint=None):
             gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=0,
-                        initial_state=d["s0"], final_state=d["fin"], out=d["out"], workspace=d["ws"])
+                        initial_state=d["s0"], final_state=d["fin"], out=d["out"], workspace=d["ws"],
+                        max_seqlen=hint)
 
-        def timed():
+        def timed(hint=None):
             for i in range(3):
-                run(sets[i % copies])
+                run(sets[i % copies], hint)
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for i in range(steps):
-                run(sets[i % copies])
+                run(sets[i % copies], hint)
             e1.record()
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / steps
@@ -1151,17 +1185,23 @@ def tuning_sweep(dev, copies, steps):
         gdn.tune_cache_clear()
         rule_ms = timed()
         rule = gdn.method_name(*gdn.prefill_plan(N, T, HK, HV, D))
+        hinted = gdn.method_name(*gdn.prefill_plan(N, T, HK, HV, D, max_seqlen=max(lens)))
+        hinted_ms = timed(max(lens)) if uneven else rule_ms
         d0 = sets[0]
         r = gdn.tune_prefill(d0["q"], d0["k"], d0["v"], d0["g"], d0["beta"], d0["cu_seqlens"], initial_state=d0["s0"])
         tuned_ms = timed()
         gdn.tune_cache_clear()
         rule_ms = min(rule_ms, timed())
+        if not uneven:
+            hinted_ms = rule_ms
         print(json.dumps({
             "mode": "tuning", "num_seqs": N, "tokens_per_seq": k, "total_tokens": T,
+            "lengths": lens if uneven else None, "hinted_method": hinted, "hinted_ms": hinted_ms,
             "rule_method": rule, "tuned_method": r["method"], "rule_ms": rule_ms, "tuned_ms": tuned_ms,
             "speedup": rule_ms / tuned_ms, "candidate_ms_warm": r["ms"], "candidate_gate_err": r["err"],
             "dtype": "bf16", "data": "synthetic", "buffer_copies": copies,
-            "config": {"workload": f"{N} sequence(s) x {k} tokens, HK={HK}, HV={HV}, d={D}"},
+            "config": {"workload": (f"{N} sequences of {'+'.join(map(str, lens))} tokens" if uneven
+                                    else f"{N} sequence(s) x {k} tokens") + f", HK={HK}, HV={HV}, d={D}"},
         }), flush=True)
 
 
