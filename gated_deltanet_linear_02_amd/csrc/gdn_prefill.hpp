@@ -799,9 +799,11 @@ constexpr int kTouchAhead = 8;
 
 // Spin limit of the fused normalisation's wait for the other row slices'
 // partial sums (each retry is an s_sleep 2 and a device-coherent load, about
-// a microsecond, so roughly 0.1 s in all): a wait that long means a slice
-// never ran, and the rows it leaves are written as NaN rather than wrong.
-constexpr int kNormSpinMax = 1 << 16;
+// a microsecond, so roughly a second in all). Every slice of the grid runs
+// once CUs free up, so a wait ends unless something holds CUs that long (a
+// persistent kernel on another stream, say); past the limit the rows are
+// written as NaN rather than wrong, and the kernel still ends.
+constexpr int kNormSpinMax = 1 << 20;
 
 // Word 3 of a raw buffer resource on gfx9-family GPUs (gfx950 included).
 constexpr int kBufferWord3 = 0x00020000;
