@@ -12,7 +12,9 @@ oracle's output, whichever form the call takes (in-wave, exchanged between
 row slices, or the pass after the scan). A fourth draws decode steps: batch, head
 layout and size, I/O and gate dtypes, scale, state slots (permuted, some
 skipped with -1), the fused normalisation, and fp32 or (with bf16 I/O) bf16
-state storage; skipped slots must keep their bits and give rows of zeros."""
+state storage; skipped slots must keep their bits and give rows of zeros.
+A fifth draws uneven bf16 batches called with the longest length as the
+method rule's hint (max_seqlen), against the oracle."""
 
 import numpy as np
 import pytest
@@ -183,3 +185,32 @@ def test_random_decode_step(seed):
     print(f"[parity] random decode {desc} out_err={eo:.3e} state_err={es:.3e}", flush=True)
     assert eo <= tol(inp.io_dtype) and es <= s_bar, desc
     assert np.array_equal(got[untouched], pool[untouched].astype(np.float64)), desc
+
+
+def _hint_case(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(2, 9))
+    lens = [int(x) for x in rng.integers(1, 400, n)]
+    lens[int(rng.integers(0, n))] = int(rng.integers(400, 1500))  # one long sequence
+    hk, hv = [(16, 32), (8, 16), (4, 8), (2, 4)][int(rng.integers(0, 4))]
+    d = int(rng.choice([32, 64, 128]))
+    init = bool(rng.random() < 0.6)
+    inp = gs.make_inputs(lens, hk, hv, d, d, seed=seed, io_dtype="bf16", gate_dtype="f32", init_state=init)
+    desc = f"seed={seed} lens={lens} hk={hk} hv={hv} d={d} init={init}"
+    return inp, desc
+
+
+@pytest.mark.parametrize("seed", range(9700, 9712))
+def test_random_hinted_configuration(seed):
+    inp, desc = _hint_case(seed)
+    lens = np.diff(inp.cu_seqlens)
+    hint = int(lens.max())
+    plan = gdn.prefill_plan(inp.num_seqs, inp.total_tokens, inp.hk, inp.hv, inp.dk, max_seqlen=hint)
+    note(f"hinted {desc} plan={plan}")
+    o, f = run_prefill(inp, chunk=0, max_seqlen=hint)
+    o_ref, f_ref = oracle_ref(inp)
+    og, fg = to_f64(o), to_f64(f)
+    assert np.isfinite(og).all() and np.isfinite(fg).all(), desc
+    eo, ef = rel_err(og, o_ref), rel_err(fg, f_ref)
+    print(f"[parity] random hinted {desc} plan={plan} out_err={eo:.3e} state_err={ef:.3e}", flush=True)
+    assert eo <= TOL_BF16 and ef <= TOL_BF16, desc
