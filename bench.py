@@ -822,8 +822,9 @@ def summarize_configs(stats_dir: str, results_jsonl: str):
               "choice when the caller passes the longest length (max_seqlen, gdn_prefill_hint); the tuned "
               "method is the one gdn_tune_prefill picks for the workload (the host-side rule sees sizes, "
               "not the lengths). The decode step at batch 8 is timed two ways: back-to-back eager launches "
-              "from Python (bound by the host at this size, and slowed further under the profiler) and the "
-              "kernel's own events.", "",
+              "from Python (bound by the host at this size) and the kernel's own events; under the profiler "
+              "both read several times longer than without it (kernel about 6.4 us, eager step about "
+              "12 us in a plain run of `bench.py --configs`).", "",
               "| workload | sequences | tokens | method | prefill ms | tokens/s | prep ms | scan ms | scan MFMA | "
               "hinted method | hinted prefill ms | tuned method | tuned prefill ms | tuned tokens/s | "
               "decode b8 step us: eager / kernel |",
