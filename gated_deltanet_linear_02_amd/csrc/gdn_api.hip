@@ -142,7 +142,7 @@ static Method method_for(int32_t chunk, int32_t rows, int32_t num_seqs, int64_t 
     m.chunk = chunk;
     m.rows = rows;
     if (chunk == 0) {
-        m = tuned_method(num_seqs, total_tokens, hk, hv, dk, io_dtype, gate_dtype);
+        m = tuned_method(num_seqs, total_tokens, hk, hv, dk, io_dtype, gate_dtype, max_seqlen);
         if (m.chunk == 0 || !method_fits(m.chunk, num_seqs, total_tokens, hk, hv, dk, dv, io_dtype)) {
             m.chunk = rule_chunk(num_seqs, total_tokens, hv, dv, io_dtype == GDN_BF16, max_seqlen);
             m.rows = 0;

@@ -174,7 +174,7 @@ struct Method {
 // The (chunk, rows) that gdn_tune_prefill cached for this device and shape
 // bucket, or chunk 0 when there is none.
 Method tuned_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv, int32_t d, int32_t io,
-                    int32_t gate);
+                    int32_t gate, int64_t max_seqlen);
 
 // gdn_prefill with the method given (chunk 1, 16, 32 or 64 and, chunked, 16,
 // 32, 64 or 128 state rows per scan workgroup); GDN_ERR_UNSUPPORTED for rows

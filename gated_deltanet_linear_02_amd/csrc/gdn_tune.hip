@@ -27,6 +27,7 @@
 #include <mutex>
 #include <string>
 #include <tuple>
+#include <vector>
 
 namespace gdn {
 
@@ -79,14 +80,17 @@ static hipError_t launch_gate(const void *a, const void *ref, int64_t n, unsigne
 
 // Cached choices, keyed by device, driver, library version and shape bucket
 // (sequence count and total tokens rounded up to powers of two; head counts,
-// head size and dtypes exact).
+// head size and dtypes exact), and whether the batch tuned on was uneven (its
+// longest sequence above 1.25 times the mean, the test of the max_seqlen
+// hint): the fastest method differs between even and uneven batches of one
+// bucket by up to 1.8 times.
 struct TuneKey {
     std::string device;
     int driver = 0, version = 0;
-    int n2 = 0, t2 = 0, hk = 0, hv = 0, d = 0, io = 0, gate = 0;
+    int n2 = 0, t2 = 0, hk = 0, hv = 0, d = 0, io = 0, gate = 0, uneven = 0;
     bool operator<(const TuneKey &o) const {
-        return std::tie(device, driver, version, n2, t2, hk, hv, d, io, gate) <
-               std::tie(o.device, o.driver, o.version, o.n2, o.t2, o.hk, o.hv, o.d, o.io, o.gate);
+        return std::tie(device, driver, version, n2, t2, hk, hv, d, io, gate, uneven) <
+               std::tie(o.device, o.driver, o.version, o.n2, o.t2, o.hk, o.hv, o.d, o.io, o.gate, o.uneven);
     }
 };
 
@@ -133,24 +137,33 @@ static bool device_key(TuneKey &k) {
 }
 
 static bool shape_key(TuneKey &k, int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv, int32_t d,
-                      int32_t io, int32_t gate) {
+                      int32_t io, int32_t gate, bool is_uneven) {
     if (!device_key(k)) return false;
     k.n2 = (int)pow2_at_least(num_seqs);
     k.t2 = (int)pow2_at_least(std::max<int64_t>(total_tokens, 1));
     k.hk = hk; k.hv = hv; k.d = d; k.io = io; k.gate = gate;
+    k.uneven = is_uneven ? 1 : 0;
     return true;
 }
 
+// A call with a max_seqlen hint takes the choice tuned on a batch of its own
+// kind (even or uneven); one without takes the even batches' choice, else
+// the uneven ones'.
 Method tuned_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, int32_t hv, int32_t d, int32_t io,
-                    int32_t gate) {
+                    int32_t gate, int64_t max_seqlen) {
     {
         std::lock_guard<std::mutex> lk(tune_mu());
         if (tune_cache().empty()) return Method{};  // nothing tuned: no device query
     }
     TuneKey k;
-    if (!shape_key(k, num_seqs, total_tokens, hk, hv, d, io, gate)) return Method{};
+    if (!shape_key(k, num_seqs, total_tokens, hk, hv, d, io, gate, uneven(num_seqs, total_tokens, max_seqlen)))
+        return Method{};
     std::lock_guard<std::mutex> lk(tune_mu());
     auto it = tune_cache().find(k);
+    if (it == tune_cache().end() && max_seqlen == 0) {
+        k.uneven = 1;
+        it = tune_cache().find(k);
+    }
     return it == tune_cache().end() ? Method{} : it->second;
 }
 
@@ -217,8 +230,28 @@ int32_t gdn_tune_prefill(const void *q, const void *k, const void *v, const void
     const size_t eb = io_dtype == GDN_BF16 ? 2 : 4;
     const TuneLayout L = tune_layout(num_seqs, total_tokens, hk, hv, dk, eb);
     char *base = static_cast<char *>(scratch);
-    unsigned *res = reinterpret_cast<unsigned *>(base + L.off_res);
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    // The batch's longest sequence (bounds clamped into [0, T] and made
+    // non-decreasing, as the kernels read them): whether it is uneven keys
+    // the cached choice, and the rule it is weighed against takes it as the
+    // max_seqlen hint.
+    int64_t longest = 0;
+    {
+        std::vector<int32_t> cu(num_seqs + 1);
+        if (hipMemcpyAsync(cu.data(), cu_seqlens, cu.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+                hipSuccess ||
+            hipStreamSynchronize(st) != hipSuccess)
+            return GDN_ERR_HIP;
+        int64_t lo = std::min<int64_t>(std::max<int64_t>(cu[0], 0), total_tokens);
+        for (int32_t n = 0; n < num_seqs; ++n) {
+            const int64_t hi = std::max(std::min<int64_t>(std::max<int64_t>(cu[n + 1], 0), total_tokens), lo);
+            longest = std::max(longest, hi - lo);
+            lo = hi;
+        }
+    }
+    const bool is_uneven = uneven(num_seqs, total_tokens, longest);
+    const int64_t hint = is_uneven ? longest : 0;
+    unsigned *res = reinterpret_cast<unsigned *>(base + L.off_res);
     const int64_t n_out = total_tokens * hv * dv, n_fin = (int64_t)num_seqs * hv * dv * dk;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     int32_t status = GDN_OK;
@@ -296,15 +329,16 @@ int32_t gdn_tune_prefill(const void *q, const void *k, const void *v, const void
     int best = 0;  // the reference always passes its own gate
     for (int i = 1; i < NC; ++i)
         if (ms[i] >= 0.f && ms[i] < ms[best]) best = i;
-    // The fixed rule's method keeps the choice unless another is faster by
-    // more than kTuneMargin: the candidates are timed warm on the caller's
+    // The fixed rule's method (given the batch's longest length when the
+    // batch is uneven) keeps the choice unless another is faster by more
+    // than kTuneMargin: the candidates are timed warm on the caller's
     // inputs, and differences within the run-to-run scatter would otherwise
     // decide, and can reverse with cold caches (one 4096-token sequence: 32
     // rows per scan workgroup 1% faster warm, 11% slower cold).
     const bool bf = io_dtype == GDN_BF16;
     Method rule;
-    rule.chunk = rule_chunk(num_seqs, total_tokens, hv, dv, bf);
-    rule.rows = rule.chunk == 1 ? 0 : scan_slice_rows(num_seqs, hv, dv, bf);
+    rule.chunk = rule_chunk(num_seqs, total_tokens, hv, dv, bf, hint);
+    rule.rows = rule.chunk == 1 ? 0 : scan_slice_rows(num_seqs, hv, dv, bf, total_tokens, hint);
     for (int i = 0; i < NC; ++i)
         if (kCandidates[i].chunk == rule.chunk && kCandidates[i].rows == rule.rows && ms[i] >= 0.f &&
             ms[best] >= ms[i] * (1.f - kTuneMargin))
@@ -316,7 +350,7 @@ int32_t gdn_tune_prefill(const void *q, const void *k, const void *v, const void
         if (candidate_err) candidate_err[i] = err[i];
     }
     TuneKey key;
-    if (shape_key(key, num_seqs, total_tokens, hk, hv, dk, io_dtype, gate_dtype)) {
+    if (shape_key(key, num_seqs, total_tokens, hk, hv, dk, io_dtype, gate_dtype, is_uneven)) {
         std::lock_guard<std::mutex> lk(tune_mu());
         tune_cache()[key] = kCandidates[best];
     }
@@ -340,8 +374,8 @@ int32_t gdn_tune_cache_save(const char *path) {
     if (!f) return GDN_ERR_BAD_VALUE;
     for (const auto &kv : tune_cache()) {
         const TuneKey &k = kv.first;
-        fprintf(f, "gdn-tune-v2 %s %d %d %d %d %d %d %d %d %d %d %d\n", k.device.c_str(), k.driver, k.version,
-                k.n2, k.t2, k.hk, k.hv, k.d, k.io, k.gate, kv.second.chunk, kv.second.rows);
+        fprintf(f, "gdn-tune-v3 %s %d %d %d %d %d %d %d %d %d %d %d %d\n", k.device.c_str(), k.driver,
+                k.version, k.n2, k.t2, k.hk, k.hv, k.d, k.io, k.gate, k.uneven, kv.second.chunk, kv.second.rows);
     }
     return fclose(f) == 0 ? GDN_OK : GDN_ERR_BAD_VALUE;
 }
@@ -357,12 +391,14 @@ int32_t gdn_tune_cache_load(const char *path, int32_t *entries) {
         char tag[16], dev[256];
         TuneKey k;
         Method m;
-        if (sscanf(line, "%15s %255s %d %d %d %d %d %d %d %d %d %d %d", tag, dev, &k.driver, &k.version, &k.n2,
-                   &k.t2, &k.hk, &k.hv, &k.d, &k.io, &k.gate, &m.chunk, &m.rows) != 13)
+        if (sscanf(line, "%15s %255s %d %d %d %d %d %d %d %d %d %d %d %d", tag, dev, &k.driver, &k.version, &k.n2,
+                   &k.t2, &k.hk, &k.hv, &k.d, &k.io, &k.gate, &k.uneven, &m.chunk, &m.rows) != 14)
             continue;
-        if (strcmp(tag, "gdn-tune-v2") != 0) continue;
-        const bool ok = m.chunk == 1 ? m.rows == 0
-                                     : (m.chunk == 16 || m.chunk == 32 || m.chunk == 64) && (m.rows == 16 || m.rows == 32);
+        if (strcmp(tag, "gdn-tune-v3") != 0) continue;
+        const bool ok = (k.uneven == 0 || k.uneven == 1) &&
+                        (m.chunk == 1 ? m.rows == 0
+                                      : (m.chunk == 16 || m.chunk == 32 || m.chunk == 64) &&
+                                            (m.rows == 16 || m.rows == 32 || m.rows == 64 || m.rows == 128));
         if (!ok) continue;
         k.device = dev;
         tune_cache()[k] = m;

@@ -352,11 +352,16 @@ int32_t gdn_decode_step_ex(const void *q, const void *k, const void *v,
  * (may be NULL; 0 for the token-by-token method), except that the method of
  * the fixed rule (chunk 0 with nothing cached) is kept unless the fastest
  * is more than 3% faster than it: warm timings on one input set differ by
- * about that much from run to run. It also caches
- * the choice for (device, driver version, library version, shape bucket).
- * The bucket is num_seqs and total_tokens each rounded up to a power of two,
- * with hk, hv, d and both dtypes exact. gdn_prefill with chunk 0 then uses
- * the cached choice.
+ * about that much from run to run. For an uneven batch (its longest
+ * sequence, read from cu_seqlens, above 1.25 times the mean) that rule is
+ * the one given the longest length as a max_seqlen hint. It also caches
+ * the choice for (device, driver version, library version, shape bucket,
+ * evenness). The bucket is num_seqs and total_tokens each rounded up to a
+ * power of two, with hk, hv, d and both dtypes exact; evenness is whether
+ * the batch tuned on was uneven. gdn_prefill with chunk 0 then uses the
+ * cached choice: a call with a max_seqlen hint (gdn_prefill_hint) the one
+ * tuned on a batch of its own evenness, else the hinted rule; a call
+ * without the hint the even batches' choice, else the uneven ones'.
  * candidate_ms and candidate_err (may be NULL; GDN_TUNE_CANDIDATES floats
  * each) receive, in the order above, the mean time in ms (-1 when rejected or
  * not applicable) and the gate error (-1 when not run).
@@ -367,9 +372,10 @@ int32_t gdn_decode_step_ex(const void *q, const void *k, const void *v,
  * GDN_ERR_BAD_VALUE for gate_tol outside [0, 1].
  *
  * The cache lives in the process, shared by all threads, and may be saved
- * to a text file and loaded back, one choice per line: "gdn-tune-v2", the
+ * to a text file and loaded back, one choice per line: "gdn-tune-v3", the
  * device, driver and library versions, the bucket's sequences, tokens, hk,
- * hv, d, io and gate dtypes, then the chunk and rows. Entries made on
+ * hv, d, io and gate dtypes, its evenness (0 even, 1 uneven), then the chunk
+ * and rows. Entries made on
  * another device, driver or library version are kept but never match.
  * gdn_tune_cache_load returns GDN_ERR_BAD_VALUE when the file cannot be
  * opened, and skips lines it cannot parse; *entries (may be NULL) receives

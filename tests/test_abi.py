@@ -285,27 +285,31 @@ def test_max_seqlen_hint_plans():
 
 
 def test_tune_cache_file_round_trip(tmp_path):
-    """The tuning cache's text file: well-formed lines (chunk, then state rows
-    per scan workgroup) load; malformed ones, unknown methods and other
-    formats are skipped; and a save writes what was loaded."""
+    """The tuning cache's text file: well-formed lines (evenness, then chunk
+    and state rows per scan workgroup, 16 to 128) load; malformed ones,
+    unknown methods and other formats are skipped; and a save writes what
+    was loaded."""
     lib = gdn.load()
     gdn.tune_cache_clear()
     src = tmp_path / "tune.txt"
     src.write_text(
-        "gdn-tune-v2 gfx950/256cu 70000 4002 1 4096 16 32 128 0 1 64 16\n"
-        "gdn-tune-v2 gfx950/256cu 70000 4002 8 65536 16 32 128 0 1 64 32\n"
-        "gdn-tune-v2 gfx950/256cu 70000 4002 64 1024 16 32 128 0 0 1 0\n"
-        "gdn-tune-v2 gfx950/256cu 70000 4002 8 512 2 4 64 1 1 48 16\n"  # not a chunk
-        "gdn-tune-v2 gfx950/256cu 70000 4002 8 512 2 4 64 1 1 64 8\n"   # not a row count
-        "gdn-tune-v2 gfx950/256cu 70000 4002 8 512 2 4 64 1 1 1 16\n"   # token by token has no rows
-        "gdn-tune-v1 gfx950/256cu 70000 3001 8 512 2 4 64 1 1 16\n"     # older format
+        "gdn-tune-v3 gfx950/256cu 70000 5002 1 4096 16 32 128 0 1 0 64 16\n"
+        "gdn-tune-v3 gfx950/256cu 70000 5002 8 65536 16 32 128 0 1 0 64 128\n"
+        "gdn-tune-v3 gfx950/256cu 70000 5002 8 65536 16 32 128 0 1 1 64 64\n"  # the same bucket, uneven
+        "gdn-tune-v3 gfx950/256cu 70000 5002 4 4096 16 32 128 0 1 0 64 32\n"
+        "gdn-tune-v3 gfx950/256cu 70000 5002 64 1024 16 32 128 0 0 0 1 0\n"
+        "gdn-tune-v3 gfx950/256cu 70000 5002 8 512 2 4 64 1 1 0 48 16\n"  # not a chunk
+        "gdn-tune-v3 gfx950/256cu 70000 5002 8 512 2 4 64 1 1 0 64 8\n"   # not a row count
+        "gdn-tune-v3 gfx950/256cu 70000 5002 8 512 2 4 64 1 1 0 1 16\n"   # token by token has no rows
+        "gdn-tune-v3 gfx950/256cu 70000 5002 8 512 2 4 64 1 1 2 64 16\n"  # evenness is 0 or 1
+        "gdn-tune-v2 gfx950/256cu 70000 4002 8 512 2 4 64 1 1 64 16\n"    # older format
         "garbage\n")
-    assert gdn.tune_cache_load(str(src)) == 3
-    assert gdn.tune_cache_size() == 3
+    assert gdn.tune_cache_load(str(src)) == 5
+    assert gdn.tune_cache_size() == 5
     out = tmp_path / "saved.txt"
     gdn.tune_cache_save(str(out))
     lines = sorted(out.read_text().splitlines())
-    assert lines == sorted(src.read_text().splitlines()[:3])
+    assert lines == sorted(src.read_text().splitlines()[:5])
     gdn.tune_cache_clear()
     assert gdn.tune_cache_size() == 0
     with pytest.raises(gdn.GdnError):

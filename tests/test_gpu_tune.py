@@ -106,7 +106,7 @@ def test_tune_cache_file_steers_chunk_zero(tmp_path):
     path = tmp_path / "tune.txt"
     gdn.tune_cache_save(str(path))
     fields = path.read_text().split()
-    assert len(fields) == 13 and fields[0] == "gdn-tune-v2"
+    assert len(fields) == 14 and fields[0] == "gdn-tune-v3"
     assert (int(fields[-2]), int(fields[-1])) == (r["chunk"], r["rows"])
     forced = 16 if r["chunk"] != 16 else 32
     path.write_text(" ".join(fields[:-2] + [str(forced), "32"]) + "\n")
@@ -123,3 +123,26 @@ def test_tune_cache_file_steers_chunk_zero(tmp_path):
     _, d2 = _inputs([150, 150], seed=gs.SEED_BASE + 721)
     _, _, ran = _run(d2, 0)
     assert ran == {"schedule", "prep", "scan"} or ran == {"prep", "scan"}
+
+
+def test_tuned_choice_keyed_by_evenness():
+    """One 2,048-token prompt beside four of 256 (an uneven batch: its longest
+    is 3.3 times the mean). The tuner reads the lengths and caches its choice
+    as an uneven batch's: a call with the longest length as a hint takes it,
+    and so does a call without a hint (the bucket holds no even batch's
+    choice). A hint near the mean marks an even batch of the same bucket,
+    which has no tuned choice, so that call takes the rule."""
+    lens = [2048, 256, 256, 256, 256]
+    N, T = len(lens), sum(lens)
+    inp = gs.make_inputs(lens, 16, 32, 128, 128, seed=gs.SEED_BASE + 1720, io_dtype="bf16", gate_dtype="f32")
+    d = device_inputs(inp)
+    rule = gdn.prefill_plan(N, T, 16, 32, 128)
+    note("tune an uneven batch")
+    r = gdn.tune_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"])
+    tuned = (r["chunk"], r["rows"])
+    assert gdn.prefill_plan(N, T, 16, 32, 128, max_seqlen=2048) == tuned
+    assert gdn.prefill_plan(N, T, 16, 32, 128) == tuned
+    assert gdn.prefill_plan(N, T, 16, 32, 128, max_seqlen=T // N + 1) == rule
+    # the choice is never slower than the hinted rule's method (64/32 here)
+    assert gdn.prefill_plan(N, T, 16, 32, 128, max_seqlen=2048) == tuned
+    assert r["ms"][gdn.method_name(*tuned)] <= r["ms"]["64/32"]
