@@ -279,16 +279,38 @@ inline int32_t scan_slice_rows(int64_t num_seqs, int64_t hv, int64_t dv, bool io
     return rows;
 }
 
+// Under the max_seqlen hint an uneven batch is chunked even where its mean
+// length would take it token by token, once its longest sequence exceeds
+// kTokenScanLongest + 2 N tokens: that sequence's token chain (about 0.45 us
+// a token) then outlasts a chunked pass (about 15 + 0.85 N us at these
+// sizes). 500 + 63 x 1 tokens: 79 us chunked against 222 token by token;
+// 120 + 20 x 3: 35 against 58; 64 + 63 x 1 stays token by token (36
+// against 71). Its chunk follows the longest sequence too: with 64 or 128
+// rows, chunks of 16 up to 256 tokens, 32 up to 1,024 (300 + 40 x 8: 55
+// against 62 us with 16), else the mean's.
+constexpr int64_t kTokenScanLongest = 16;
+inline int32_t uneven_chunk(int64_t max_seqlen) {
+    return max_seqlen <= 256 ? 16 : max_seqlen <= kChunk32PerSeq ? 32 : 64;
+}
 inline int32_t rule_chunk(int64_t num_seqs, int64_t total_tokens, int64_t hv, int64_t dv, bool io_bf16,
                           int64_t max_seqlen = 0) {
-    if (total_tokens <= kTokenScanTokens || total_tokens <= kTokenScanPerSeq * num_seqs) return 1;
+    const bool skew = uneven(num_seqs, total_tokens, max_seqlen);
+    const bool long_chain = skew && max_seqlen > kTokenScanLongest + 2 * num_seqs;
+    if ((total_tokens <= kTokenScanTokens || total_tokens <= kTokenScanPerSeq * num_seqs) && !long_chain) return 1;
     if (!io_bf16) {
         if (total_tokens <= kF32TokenScanPerSeq * num_seqs) return 1;
         const bool one_pass = num_seqs * hv * (dv / 16) <= kScanOnePassWgs;
-        return one_pass && total_tokens <= kF32Chunk32PerSeq * num_seqs ? 32 : 64;
+        if (one_pass && total_tokens <= kF32Chunk32PerSeq * num_seqs) return 32;
+        // uneven, under the hint: its longest chain, as a lone sequence's
+        // (300 + 77 + 5 tokens: 64 against 69 us with 64; 500 + 8 x 20:
+        // 101 against 113)
+        return skew && max_seqlen <= kF32Chunk32PerSeq ? 32 : 64;
     }
     const int64_t rows = scan_slice_rows(num_seqs, hv, dv, io_bf16, total_tokens, max_seqlen);
-    if (rows >= 64) return total_tokens <= 16 * num_seqs ? 16 : total_tokens <= 32 * num_seqs ? 32 : 64;
+    if (rows >= 64) {
+        const int32_t c = total_tokens <= 16 * num_seqs ? 16 : total_tokens <= 32 * num_seqs ? 32 : 64;
+        return skew ? std::max(c, uneven_chunk(max_seqlen)) : c;
+    }
     if (total_tokens <= kChunk16PerSeq * num_seqs) return 16;
     // one pass with the slice rows the scan will take (2 x 600: 32-row
     // slices fill the 256 CUs once, and chunks of 32 measure 38.5 against

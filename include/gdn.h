@@ -110,8 +110,12 @@ int32_t gdn_prefill_method(int32_t num_seqs, int64_t total_tokens, int32_t hk, i
  * scan's time, the larger of the longest sequence's chain and the batch's
  * work spread over the CUs, each weighted by the chunk-step cost of the
  * width; otherwise, and without a hint, the rule of gdn_prefill_method.
- * Uneven batches gain most (a 4,096-token prompt beside four of 512: 32
- * rows, 147 us, against 259 us with the one-pass rule's 128 rows).
+ * For such batches the chunk size follows the longest sequence too, and a
+ * bf16 batch that its mean length would send token by token is chunked
+ * once the longest exceeds 16 + 2 num_seqs tokens. Uneven batches gain most
+ * (a 4,096-token prompt beside four of 512: 32 rows, 147 us, against 259
+ * us with the one-pass rule's 128 rows; 500 tokens beside 63 single ones:
+ * chunks of 32, 86 us, against 234 us token by token).
  */
 int32_t gdn_prefill_method_hint(int32_t num_seqs, int64_t total_tokens, int64_t max_seqlen,
                                 int32_t hk, int32_t hv, int32_t dk, int32_t dv, int32_t chunk,

@@ -278,8 +278,18 @@ def test_max_seqlen_hint_plans():
     assert p([300, 77, 5], max_seqlen=300) == (32, 32)
     for lens in ([1024] * 8, [512] * 8, [2048] * 2, [200] * 3, [4096], [600, 500, 400], [128] * 32):
         assert p(lens, max_seqlen=max(lens)) == p(lens), lens
-    # fp32 I/O: 16-row slices whatever the hint
-    assert p(varlen, io_dtype=torch.float32, max_seqlen=14620) == (64, 16)
+    # many tiny sequences beside a longer one: chunked once the longest
+    # exceeds 16 + 2 N tokens, with chunks by the longest length
+    assert p([500] + [1] * 63) == (1, 0) and p([500] + [1] * 63, max_seqlen=500) == (32, 128)
+    assert p([120] + [3] * 20, max_seqlen=120) == (16, 128)
+    assert p([64] + [1] * 63, max_seqlen=64) == (1, 0)
+    assert p([1000] + [2] * 100, max_seqlen=1000) == (32, 128)
+    # fp32 I/O: 16-row slices whatever the hint; short uneven batches take
+    # chunks of 32, and tiny means stay token by token
+    f32 = torch.float32
+    assert p(varlen, io_dtype=f32, max_seqlen=14620) == (64, 16)
+    assert p([300, 77, 5], io_dtype=f32) == (64, 16) and p([300, 77, 5], io_dtype=f32, max_seqlen=300) == (32, 16)
+    assert p([500] + [1] * 63, io_dtype=f32, max_seqlen=500) == (1, 0)
     # hints outside [mean, total] are refused
     assert p([300, 77, 5], max_seqlen=100) == (0, 0) and p([300, 77, 5], max_seqlen=383) == (0, 0)
 
