@@ -1149,7 +1149,7 @@ TUNE_SHAPES = ((1, 16), (1, 48), (1, 128), (1, 512), (8, 4), (64, 1), (64, 4), (
 # depends on the longest length when the caller gives it (max_seqlen).
 UNEVEN_SHAPES = ((4096, 512, 512, 512, 512), (8192, 1024, 1024), (2048, 2048, 128, 128, 128, 128),
                  (3000,) + (100,) * 10, (6000, 3000, 1500, 750), (2048, 1024, 512, 256), (300, 77, 5),
-                 (1000, 100, 100, 100))
+                 (1000, 100, 100, 100), (500,) + (1,) * 63, (120,) + (3,) * 20)
 
 
 def tuning_sweep(dev, copies, steps):

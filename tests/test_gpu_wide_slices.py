@@ -158,3 +158,23 @@ def test_max_seqlen_hint_changes_rows_not_results():
     for bad in (T // N - 1, T + 1):
         with pytest.raises(gdn.GdnError):
             run_prefill(inp, chunk=0, max_seqlen=bad)
+
+
+def test_max_seqlen_hint_chunks_tiny_sequences():
+    """300 tokens beside 40 single-token sequences: the mean length (8.3)
+    sends the batch token by token, but the longest sequence sets the token
+    scan's time; with the hint the batch is chunked (chunks of 32, 128 state
+    rows). Both calls meet the oracle's bar."""
+    lens = [300] + [1] * 40
+    N, T = len(lens), sum(lens)
+    assert gdn.prefill_plan(N, T, 16, 32, 128) == (1, 0)
+    assert gdn.prefill_plan(N, T, 16, 32, 128, max_seqlen=300) == (32, 128)
+    inp = gs.make_inputs(lens, 16, 32, 128, 128, seed=gs.SEED_BASE + 1710, io_dtype="bf16", gate_dtype="f32",
+                         init_state=True)
+    note("prefill max_seqlen hint 300 + 40 x 1")
+    o_ref, f_ref = oracle_ref(inp)
+    for hint in (None, 300):
+        o, f = run_prefill(inp, chunk=0, max_seqlen=hint)
+        eo, ef = rel_err(to_f64(o), o_ref), rel_err(to_f64(f), f_ref)
+        print(f"[parity] hint={hint} out_err={eo:.3e} state_err={ef:.3e}", flush=True)
+        assert eo <= TOL_BF16 and ef <= TOL_BF16
