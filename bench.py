@@ -645,6 +645,18 @@ def summarize_state(stats_dir: str, fetch_dir: str, write_dir: str, results_json
         f.write("\n".join(lines) + "\n")
 
 
+def _lengths_label(lens) -> str:
+    """Sequence lengths with runs grouped: 4096 + 4 x 512."""
+    parts, i = [], 0
+    while i < len(lens):
+        j = i
+        while j < len(lens) and lens[j] == lens[i]:
+            j += 1
+        parts.append(str(lens[i]) if j - i == 1 else f"{j - i} x {lens[i]}")
+        i = j
+    return " + ".join(parts)
+
+
 def summarize_tune(stats_dir: str, results_jsonl: str):
     """Write profiles/gdn_prefill_tuning.md from a rocprofv3 kernel trace of
     `bench.py --tune` (kernel durations) and the JSON lines of a second
@@ -717,7 +729,7 @@ def summarize_tune(stats_dir: str, results_jsonl: str):
             best = min(t for t in cand.values() if t >= 0)
             hc = cand.get(d["hinted_method"], -1)
             ratio = hc / best if hc > 0 else float("nan")
-            lines.append(f"| {'+'.join(map(str, d['lengths']))} | {d['rule_method']} | {d['rule_ms'] * 1e3:.1f} | "
+            lines.append(f"| {_lengths_label(d['lengths'])} | {d['rule_method']} | {d['rule_ms'] * 1e3:.1f} | "
                          f"{d['hinted_method']} | {d['hinted_ms'] * 1e3:.1f} | {d['rule_ms'] / d['hinted_ms']:.2f} | "
                          f"{d['tuned_method']} | {d['tuned_ms'] * 1e3:.1f} | {ratio:.2f} |")
     with open(os.path.join(ROOT, "profiles", "gdn_prefill_tuning.md"), "w") as f:
