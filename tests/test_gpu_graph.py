@@ -54,15 +54,18 @@ def test_decode_step_graph_replays(norm, state_dtype):
         assert torch.equal(state, ref_state), f"replay {t}: states differ from the eager call"
 
 
-@pytest.mark.parametrize("lens,norm,rows", [([300, 77, 5], False, 64), ([300, 77, 5], True, 64),
-                                           ([120, 7, 64, 200] * 3, True, 128)])
-def test_prefill_graph_replays(lens, norm, rows):
+@pytest.mark.parametrize("lens,norm,rows,hint", [([300, 77, 5], False, 64, None), ([300, 77, 5], True, 64, None),
+                                                ([120, 7, 64, 200] * 3, True, 128, None),
+                                                ([2048, 256, 256, 256, 256], True, 32, 2048)])
+def test_prefill_graph_replays(lens, norm, rows, hint):
     """Chunked prefill (preparation and scan), captured once and replayed on
     new token data; every replay equals the eager call. 3 sequences take
     64-row scan slices (with a normalisation weight their slices exchange
     partial sums through the workspace, whose slots the preparation kernel
-    resets in every replay); 12 take 128-row slices, normalised in place."""
-    assert gdn.prefill_plan(len(lens), sum(lens), 16, 32, 128, 64) == (64, rows)
+    resets in every replay); 12 take 128-row slices, normalised in place;
+    an uneven batch given its longest length (max_seqlen) takes 32-row
+    slices rather than the rule's 128."""
+    assert gdn.prefill_plan(len(lens), sum(lens), 16, 32, 128, 64, max_seqlen=hint) == (64, rows)
     runs = [gs.make_inputs(lens, 16, 32, 128, 128, seed=gs.SEED_BASE + 1600 + t, io_dtype="bf16",
                            gate_dtype="f32", init_state=True) for t in range(4)]
     w = torch.from_numpy(gs.norm_weight(128, seed=gs.SEED_BASE + 1650)).cuda() if norm else None
@@ -77,9 +80,9 @@ def test_prefill_graph_replays(lens, norm, rows):
     def call(src, o, f):
         return gdn.prefill(src["q"], src["k"], src["v"], src["g"], src["beta"], src["cu_seqlens"], chunk=64,
                            initial_state=src["initial_state"], final_state=f, out=o, workspace=ws,
-                           norm_weight=w, norm_eps=1e-6)
+                           norm_weight=w, norm_eps=1e-6, max_seqlen=hint)
 
-    note(f"prefill graph capture lens={lens[:4]} norm={norm}")
+    note(f"prefill graph capture lens={lens[:4]} norm={norm} hint={hint}")
     call(static, out, fin)  # warm-up (first launch sets kernel attributes)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
