@@ -50,13 +50,21 @@ int32_t stream_device_cus(hipStream_t stream) {
     hipDevice_t dev = 0;
     const hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
     if (e != hipSuccess || dev < 0) return 0;
-    if (dev < kMaxDevices) {
-        const int32_t n = cached[dev].load(std::memory_order_relaxed);
-        if (n > 0) return n;
+    int32_t n = dev < kMaxDevices ? cached[dev].load(std::memory_order_relaxed) : 0;
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+        if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
     }
-    int32_t n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) return 0;
-    if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+    // A stream whose CU mask leaves some of them out: which XCDs keep how
+    // many is not known here, so it is not counted on to hold a whole grid.
+    constexpr int kMaskWords = 32;  // up to 1,024 CUs
+    uint32_t mask[kMaskWords] = {};
+    const int words = std::min(kMaskWords, (n + 31) / 32);
+    if (hipExtStreamGetCUMask(stream, (uint32_t)words, mask) == hipSuccess) {
+        int on = 0;
+        for (int w = 0; w < words; ++w) on += __builtin_popcount(mask[w]);
+        if (on < n) return 0;
+    }
     return n;
 }
 

@@ -140,8 +140,8 @@ inline int64_t scan_grid(int64_t num_seqs, int64_t hk, int64_t hv, int64_t dv, i
 inline bool fused_norm_fits(int64_t num_seqs, int64_t hk, int64_t hv, int64_t dv, int64_t rows, int64_t cus) {
     return rows == dv || scan_grid(num_seqs, hk, hv, dv, rows) <= cus;
 }
-// Compute units of the device that owns `stream` (0 if HIP cannot say),
-// looked up once per device.
+// Compute units of the device that owns `stream` (looked up once per device),
+// or 0 if HIP cannot say or the stream's CU mask leaves some of them out.
 int32_t stream_device_cus(hipStream_t stream);
 
 // Chunked prefill (chunk 16, 32 or 64): preparation and scan kernels.

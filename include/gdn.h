@@ -286,12 +286,12 @@ int32_t gdn_decode_step(const void *q, const void *k, const void *v,
  * takes for several sequences at d = 128) or when its workgroups, one per
  * compute unit, fit the stream's device in one pass (one sequence at
  * HK = 16, HV = 32, d = 128 on a whole MI355X, for instance; a partition of
- * one counts its own CUs); in the second case the workgroups holding the
- * parts of a row exchange partial sums of squares through the workspace and
- * wait for one another, so they must all be resident at once: a stream
- * limited to fewer CUs than its device (a CU mask) should not take such
- * calls. Either way each output is rounded once. Otherwise (fp32 I/O, token
- * by token, or narrower slices over more than one pass)
+ * one counts its own CUs, and a stream whose CU mask leaves some CUs out
+ * counts none); in the second case the workgroups holding the parts of a row
+ * exchange partial sums of squares through the workspace and wait for one
+ * another, so they must all be resident at once. Either way each output is
+ * rounded once. Otherwise (fp32 I/O, token by token, or narrower slices over
+ * more than one pass or on a masked stream)
  * the prefill's kernels are followed by one pass that rewrites the rows of
  * out in place; rows of tokens outside [cu_seqlens[0], cu_seqlens[N]) are
  * left untouched, and in bf16 a row is then rounded twice (before and after

@@ -337,6 +337,55 @@ def test_prefill_norm_exchange_on_concurrent_streams():
         assert torch.equal(o0, alone[0]) and torch.equal(o1, alone[1]), f"rep {rep}: differs from the call alone"
 
 
+def test_prefill_norm_on_a_cu_masked_stream():
+    """A stream whose CU mask leaves out one CU in every 32 cannot be
+    counted on to hold a GPU-filling exchanging scan at once, so a 4,096-token
+    prefill with the norm on it normalises in the pass after the scan (one
+    norm_apply launch), and meets the oracle's bar; on the default stream the
+    same call fuses the norm into the scan."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    words = (ncu + 31) // 32
+    mask = (ctypes.c_uint32 * words)(*([0xFFFFFFFE] * words))
+    inp = gs.workload("prefill", io_dtype="bf16")
+    w = _weight(128, seed=13)
+    d = device_inputs(inp)
+    wt = torch.from_numpy(w).cuda()
+
+    def call(stream):
+        gdn.timing_start(8)
+        o, _ = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], chunk=64,
+                           norm_weight=wt, norm_eps=1e-6, stream=stream)
+        kt = gdn.timing_stop()
+        torch.cuda.synchronize()
+        return o, kt["norm_apply"]["count"]
+
+    note("prefill norm on the default stream")
+    o_fused, passes = call(None)
+    assert passes == 0
+    handle = ctypes.c_void_p()
+    assert hip.hipExtStreamCreateWithCUMask(ctypes.byref(handle), words, mask) == 0
+    try:
+        st = torch.cuda.ExternalStream(handle.value)
+        st.wait_stream(torch.cuda.current_stream())
+        note("prefill norm on a CU-masked stream")
+        o_masked, passes = call(st)
+    finally:
+        torch.cuda.synchronize()
+        hip.hipStreamDestroy(handle)
+    assert passes == 1
+    o_ref, _ = oracle_ref(inp)
+    y_ref = oracle.rms_norm(o_ref, w, 1e-6)
+    for o in (o_fused, o_masked):
+        eo = rel_err(to_f64(o), y_ref)
+        print(f"[parity] prefill norm masked-stream case out_err={eo:.3e}", flush=True)
+        assert np.isfinite(to_f64(o)).all() and eo <= tol("bf16")
+
+
 @pytest.mark.parametrize("hk,hv,d", [(4, 16, 64), (8, 8, 128), (2, 8, 32)])
 def test_prefill_norm_whole_head_slices(hk, hv, d):
     """bf16, enough sequences that the scan takes slices of a whole head
