@@ -300,7 +300,8 @@ inline int32_t rule_chunk(int64_t num_seqs, int64_t total_tokens, int64_t hv, in
     if (!io_bf16) {
         if (total_tokens <= kF32TokenScanPerSeq * num_seqs) return 1;
         const bool one_pass = num_seqs * hv * (dv / 16) <= kScanOnePassWgs;
-        if (one_pass && total_tokens <= kF32Chunk32PerSeq * num_seqs) return 32;
+        if (one_pass && (skew ? max_seqlen <= kF32Chunk32PerSeq : total_tokens <= kF32Chunk32PerSeq * num_seqs))
+            return 32;
         // uneven, under the hint: its longest chain, as a lone sequence's
         // (300 + 77 + 5 tokens: 64 against 69 us with 64; 500 + 8 x 20:
         // 101 against 113)
@@ -311,15 +312,17 @@ inline int32_t rule_chunk(int64_t num_seqs, int64_t total_tokens, int64_t hv, in
         const int32_t c = total_tokens <= 16 * num_seqs ? 16 : total_tokens <= 32 * num_seqs ? 32 : 64;
         return skew ? std::max(c, uneven_chunk(max_seqlen)) : c;
     }
+    // An uneven batch under the hint is bound by its longest chain as a lone
+    // sequence is, so that length decides, over one pass or more (300 + 77 +
+    // 5 tokens: 24.4 us with chunks of 32 against 28.3 with 64; 2048 + 1024
+    // + 512 + 256 at HV = 16, d = 64, one pass: 44.7 us with 64 against 50.0
+    // with 32).
+    if (skew) return uneven_chunk(max_seqlen);
     if (total_tokens <= kChunk16PerSeq * num_seqs) return 16;
     // one pass with the slice rows the scan will take (2 x 600: 32-row
     // slices fill the 256 CUs once, and chunks of 32 measure 38.5 against
     // 41 us)
     if (num_seqs * hv * (dv / rows) <= kScanOnePassWgs && total_tokens <= kChunk32PerSeq * num_seqs) return 32;
-    // an uneven batch under the hint is bound by its longest chain as a
-    // lone sequence is (300 + 77 + 5 tokens: 24.4 us with chunks of 32
-    // against 28.3 with 64)
-    if (uneven(num_seqs, total_tokens, max_seqlen) && max_seqlen <= kChunk32PerSeq) return 32;
     return 64;
 }
 

@@ -278,6 +278,10 @@ def test_max_seqlen_hint_plans():
     assert p([300, 77, 5], max_seqlen=300) == (32, 32)
     for lens in ([1024] * 8, [512] * 8, [2048] * 2, [200] * 3, [4096], [600, 500, 400], [128] * 32):
         assert p(lens, max_seqlen=max(lens)) == p(lens), lens
+    # other head layouts: the longest length decides the chunk (HK 8, HV 16,
+    # d 64: one pass, but a 2,048-token chain)
+    assert gdn.prefill_plan(4, 3840, 8, 16, 64) == (32, 16)
+    assert gdn.prefill_plan(4, 3840, 8, 16, 64, max_seqlen=2048) == (64, 16)
     # many tiny sequences beside a longer one: chunked once the longest
     # exceeds 16 + 2 N tokens, with chunks by the longest length
     assert p([500] + [1] * 63) == (1, 0) and p([500] + [1] * 63, max_seqlen=500) == (32, 128)
