@@ -146,3 +146,20 @@ def test_tuned_choice_keyed_by_evenness():
     # the choice is never slower than the hinted rule's method (64/32 here)
     assert gdn.prefill_plan(N, T, 16, 32, 128, max_seqlen=2048) == tuned
     assert r["ms"][gdn.method_name(*tuned)] <= r["ms"]["64/32"]
+
+
+def test_even_choice_not_applied_to_a_hinted_uneven_batch():
+    """Eight sequences of 512 tokens tuned (an even batch). A hinted uneven
+    batch in the same bucket (8 sequences, 2,048 + 7 x 256 tokens) does not
+    take that choice but the hinted rule's method; without the hint it
+    takes the even batch's choice, as before."""
+    lens = [512] * 8
+    inp = gs.make_inputs(lens, 16, 32, 128, 128, seed=gs.SEED_BASE + 1730, io_dtype="bf16", gate_dtype="f32")
+    d = device_inputs(inp)
+    N, T = 8, 2048 + 7 * 256
+    hinted_rule = gdn.prefill_plan(N, T, 16, 32, 128, max_seqlen=2048)
+    note("tune an even batch")
+    r = gdn.tune_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"])
+    tuned = (r["chunk"], r["rows"])
+    assert gdn.prefill_plan(N, T, 16, 32, 128, max_seqlen=2048) == hinted_rule
+    assert gdn.prefill_plan(N, T, 16, 32, 128) == tuned
