@@ -51,8 +51,10 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
 
 // Workspace of one prefill call, carved from the caller's buffer. Sizes are
-// upper bounds known on the host: a sequence of length L has ceil(L/C)
-// chunks, so N sequences over T tokens have at most ceil(T/C) + N chunks.
+// upper bounds known on the host: a sequence of length L has ceil(L/C) <=
+// (L + C - 1) / C chunks, so N sequences over at most T tokens have at most
+// floor((T + N (C - 1)) / C); for one sequence that is exactly ceil(T/C),
+// so the preparation grid launches no workgroup without a chunk.
 struct PrefillLayout {
     int64_t max_chunks;
     size_t off_bounds, off_seq_chunk0, off_order;   // int32 [N+1], [N+1], [N]
@@ -79,7 +81,7 @@ constexpr int64_t gate_record(int64_t chunk) { return 2 * chunk + 4; }
 inline PrefillLayout prefill_layout(int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
                                     int64_t dk, int64_t chunk, size_t elem_bytes) {
     PrefillLayout L;
-    L.max_chunks = (total_tokens + chunk - 1) / chunk + num_seqs;
+    L.max_chunks = std::max<int64_t>(1, (total_tokens + num_seqs * (chunk - 1)) / chunk);
     size_t o = 0;
     auto take = [&o](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
     L.off_bounds = take(sizeof(int32_t) * (size_t)(num_seqs + 1));

@@ -199,7 +199,7 @@ int32_t gdn_prefill(const void *q, const void *k, const void *v,
  * (gdn_prefill_workspace_size of the method gdn_prefill_method reports; the
  * token-by-token method needs none) returns GDN_ERR_WORKSPACE before
  * anything is enqueued; at HK = 16, HV = 32, d = 128 and chunk 64 the array
- * holds one sequence of up to 5,120 bf16 tokens. Every call on a GPU
+ * holds one sequence of up to 5,184 bf16 tokens. Every call on a GPU
  * shares that GPU's array, and the array keeps what the last call left in it
  * (each call writes what it reads): calls that may overlap on one GPU (other
  * streams, other host threads) race and must be serialised by the caller.

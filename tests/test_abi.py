@@ -61,7 +61,9 @@ def test_workspace_size(lib):
     # and K^T per query/key head (bf16 C x d), and per value head a gate
     # record of 2C + 4 fp32 (delta and scale*gamma per token, gamma_C, padding)
     # and d/16 slots of C fp32 for the fused normalisation's partial sums
-    chunks = (4096 + 63) // 64 + 1
+    # chunks: at most floor((T + N (C - 1)) / C) over N sequences, which
+    # for one sequence is ceil(T / C)
+    chunks = (4096 + 63) // 64
     need = chunks * (32 * (2 * 64 * 64 * 2 + 64 * 128 * 2 + (2 * 64 + 4) * 4 + (128 // 16) * 64 * 4)
                      + 16 * 2 * 64 * 128 * 2)
     assert need <= w < need + 64 * 1024
@@ -437,8 +439,8 @@ def test_prefill_noalloc_host_checks(lib):
     assert call(hk=3, hv=4) == BAD_SHAPE
     assert call(dk=96, dv=96) == UNSUPPORTED
     assert call(chunk=8) == UNSUPPORTED
-    # the largest single bf16 sequence that fits at chunk 64 (5,120 tokens)
-    # and the next one
-    assert lib.gdn_prefill_workspace_size(1, 5120, 16, 32, 128, 128, 64, BF16) <= 128 << 20
-    assert lib.gdn_prefill_workspace_size(1, 5121, 16, 32, 128, 128, 64, BF16) > 128 << 20
-    assert call(T=5121) == WORKSPACE
+    # the largest single bf16 sequence that fits at chunk 64 (5,184 tokens,
+    # 81 chunks) and the next one
+    assert lib.gdn_prefill_workspace_size(1, 5184, 16, 32, 128, 128, 64, BF16) <= 128 << 20
+    assert lib.gdn_prefill_workspace_size(1, 5185, 16, 32, 128, 128, 64, BF16) > 128 << 20
+    assert call(T=5185) == WORKSPACE
